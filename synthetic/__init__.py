@@ -1,0 +1,198 @@
+"""Seeded synthetic inputs for the Titans memory scan (shared by both sides).
+
+This module only draws numbers: it holds none of the scan's arithmetic.  The
+GPU tests, the bench and the oracle-side tests all take their inputs from
+here, so the HIP path and the oracle see exactly the same values.
+
+Recipe (the memory workloads on the Titans pages carry no data of their own;
+these shapes stand in for the 4K training length, the 16K needle-in-a-haystack
+length and the ">2M token" context claim):
+
+* q, k, v ~ N(0, 1) per element, drawn in C order over [B, T, H, d]; q and k
+  are then L2-normalised per (b, t, h) over d in float64.
+* alpha_t = sigmoid(N(mu_alpha, 1)), eta_t = eta_scale * sigmoid(N(0, 1)),
+  beta_t = sigmoid(N(2, 1)), one draw per (b, t, h), computed in float64.
+* theta0: layer by layer, W_l ~ N(0, 1 / n_{l-1}) per head (shared by every
+  batch row); s0 = 0.
+* Storage: gates and theta0 are rounded to float32.  q/k/v are float32 for the
+  fp32 workload; for bf16 workloads they are rounded float64 -> float32 (RNE)
+  -> bfloat16 (RNE) and kept as raw uint16 bit patterns.
+
+Every (tensor, batch row, block of 4096 tokens) has its own PCG64 stream keyed
+by ``SeedSequence(seed, spawn_key=(tensor, b, block))``, so a prefix of T is the
+same whatever the total length, and blocks can be drawn in parallel.
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+BLOCK_TOKENS = 4096
+
+# tensor ids for the stream keys
+_Q, _K, _V, _ALPHA, _ETA, _BETA, _THETA = range(7)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    heads: int
+    seq_len: int
+    widths: tuple        # n_0 .. n_L (n_0 = n_L = d)
+    chunk: int
+    io: str              # "f32" or "bf16"
+    alpha_mu: float = -4.0
+    eta_scale: float = 0.1
+    beta_mu: float = 2.0
+
+    @property
+    def d(self) -> int:
+        return self.widths[0]
+
+    @property
+    def n_layers(self) -> int:
+        return len(self.widths) - 1
+
+    @property
+    def params(self) -> int:
+        w = self.widths
+        return int(sum(w[i] * w[i - 1] for i in range(1, len(w))))
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    # tiny fp32 reference: 1 head, batch 1, T=512, C=16, MLP 16->64->16
+    "tiny_f32_h1_t512": Workload("tiny_f32_h1_t512", 1, 1, 512, (16, 64, 16), 16, "f32"),
+    # 8 heads x d64, batch 4, T=4096, C=64, MLP 64->256->64
+    "h8_d64_b4_t4k": Workload("h8_d64_b4_t4k", 4, 8, 4096, (64, 256, 64), 64, "bf16"),
+    # 16 heads x d64, batch 8, T=16384, C=64, MLP 64->256->64 (the headline workload)
+    "h16_d64_b8_t16k": Workload("h16_d64_b8_t16k", 8, 16, 16384, (64, 256, 64), 64, "bf16"),
+    # deeper memory: 8 heads x d128, batch 2, T=32768, C=128, MLP 128->512->512->512->128
+    "deep_h8_d128_b2_t32k": Workload("deep_h8_d128_b2_t32k", 2, 8, 32768,
+                                     (128, 512, 512, 512, 128), 128, "bf16",
+                                     alpha_mu=-5.0, eta_scale=0.05),
+    # long-context streaming: 16 heads x d64, batch 1, T=2^21, C=256
+    "long_h16_d64_b1_t2m": Workload("long_h16_d64_b1_t2m", 1, 16, 2097152, (64, 256, 64), 256,
+                                    "bf16"),
+}
+
+HEADLINE = "h16_d64_b8_t16k"
+
+
+@dataclasses.dataclass
+class Inputs:
+    workload: Workload
+    q: np.ndarray        # [B,T,H,d]: float32, or uint16 bf16 bits
+    k: np.ndarray
+    v: np.ndarray
+    alpha: np.ndarray    # [B,T,H] float32
+    eta: np.ndarray
+    beta: np.ndarray
+    theta0: np.ndarray   # [H,P] float32
+    s0: np.ndarray       # [H,P] float32
+
+    def qkv_f32(self, name: str) -> np.ndarray:
+        """q/k/v as float32 values (exact for bf16 storage)."""
+        a = getattr(self, name)
+        return bf16_bits_to_f32(a) if a.dtype == np.uint16 else a
+
+
+def _rng(seed: int, *key) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=key)))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round to nearest, ties to even); returns uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (r >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(
+        np.float32)
+
+
+def _sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _draw_vectors(seed, tensor, wl, B, T, normalise, out):
+    """Fill out[b, t0:t1] block by block with N(0,1) rows of length d."""
+    H, d = wl.heads, wl.d
+
+    def one(bi_blk):
+        b, blk = bi_blk
+        t0 = blk * BLOCK_TOKENS
+        t1 = min(T, t0 + BLOCK_TOKENS)
+        x = _rng(seed, tensor, b, blk).standard_normal((BLOCK_TOKENS, H, d))[: t1 - t0]
+        if normalise:
+            x = x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+        x32 = x.astype(np.float32)
+        out[b, t0:t1] = f32_to_bf16_bits(x32) if wl.io == "bf16" else x32
+
+    jobs = [(b, blk) for b in range(B) for blk in range((T + BLOCK_TOKENS - 1) // BLOCK_TOKENS)]
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, jobs))
+
+
+def _draw_gate(seed, tensor, wl, B, T, transform):
+    H = wl.heads
+    out = np.empty((B, T, H), dtype=np.float32)
+    for b in range(B):
+        for blk in range((T + BLOCK_TOKENS - 1) // BLOCK_TOKENS):
+            t0 = blk * BLOCK_TOKENS
+            t1 = min(T, t0 + BLOCK_TOKENS)
+            z = _rng(seed, tensor, b, blk).standard_normal((BLOCK_TOKENS, H))[: t1 - t0]
+            out[b, t0:t1] = transform(z).astype(np.float32)
+    return out
+
+
+def make_theta0(wl: Workload, seed: int) -> np.ndarray:
+    H, w = wl.heads, wl.widths
+    th = np.empty((H, wl.params), dtype=np.float32)
+    for h in range(H):
+        off = 0
+        for l in range(1, len(w)):
+            n = w[l] * w[l - 1]
+            th[h, off:off + n] = (_rng(seed, _THETA, h, l).standard_normal(n)
+                                  / np.sqrt(w[l - 1])).astype(np.float32)
+            off += n
+    return th
+
+
+def make_inputs(wl: Workload | str, seed: int = 0, seq_len: int | None = None,
+                batch: int | None = None) -> Inputs:
+    """Draw the workload's inputs.  seq_len / batch override T / B (prefix-consistent)."""
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    B = wl.batch if batch is None else batch
+    T = wl.seq_len if seq_len is None else seq_len
+    H, d = wl.heads, wl.d
+    qdt = np.uint16 if wl.io == "bf16" else np.float32
+    q = np.empty((B, T, H, d), dtype=qdt)
+    k = np.empty((B, T, H, d), dtype=qdt)
+    v = np.empty((B, T, H, d), dtype=qdt)
+    _draw_vectors(seed, _Q, wl, B, T, True, q)
+    _draw_vectors(seed, _K, wl, B, T, True, k)
+    _draw_vectors(seed, _V, wl, B, T, False, v)
+    alpha = _draw_gate(seed, _ALPHA, wl, B, T, lambda z: _sigmoid(z + wl.alpha_mu))
+    eta = _draw_gate(seed, _ETA, wl, B, T, lambda z: wl.eta_scale * _sigmoid(z))
+    beta = _draw_gate(seed, _BETA, wl, B, T, lambda z: _sigmoid(z + wl.beta_mu))
+    theta0 = make_theta0(wl, seed)
+    s0 = np.zeros_like(theta0)
+    return Inputs(wl.with_(batch=B, seq_len=T), q, k, v, alpha, eta, beta, theta0, s0)
