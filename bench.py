@@ -1,0 +1,165 @@
+"""Throughput of the Titans memory scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one titans_mem_scan call over the whole workload (every batch row
+and head, all T tokens), with inputs already resident in HBM.  Prints ONE JSON
+line.  value = tokens/s = B*T / (seconds per step).
+
+roofline: algorithmic flops per launch of the scan kernel -- per token-head
+    12 P - 2 n_1 n_0 + (C - 1) sum_l (n_{l-1} + n_l)
+(key forward 2P, backward 2(P - n_1 n_0), reads at the in-chunk weights 4P,
+chunk-end carry of theta and s 4P, strictly-lower C x C decay-masked terms)
+-- divided by the kernel's average duration from HIP events recorded on the
+stream the kernel runs on, against the MI355X peak of the unit that executes
+it.
+cpu_baseline: the fp64 oracle on a bounded sample of the same workload (batch
+row 0, every head, a prefix of the tokens) on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "memory-scan tokens/sec at 16 heads×d64, T=16K; % of MFMA/HBM roofline"
+
+PEAKS = {  # MI355X published dense peaks
+    "mfma_bf16": 2500.0,   # TFLOP/s
+    "mfma_f32": 157.3,
+    "valu_f32": 157.3,
+    "hbm": 8000.0,         # GB/s
+}
+
+
+def alg_flops_per_token_head(widths, C):
+    P = sum(widths[l] * widths[l - 1] for l in range(1, len(widths)))
+    lower = (C - 1) * sum(widths[l - 1] + widths[l] for l in range(1, len(widths)))
+    return 12 * P - 2 * widths[1] * widths[0] + lower
+
+
+def alg_bytes(wl):
+    """q, k, v, y once; three fp32 gates; theta0, s0 in and theta_T, s_T out once per memory."""
+    io = 2 if wl.io == "bf16" else 4
+    th = wl.batch * wl.seq_len * wl.heads
+    return th * (4 * wl.d * io + 12) + 4 * 4 * wl.params * wl.batch * wl.heads
+
+
+def cpu_baseline(inp, wl, sample_tokens):
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    T = min(sample_tokens, wl.seq_len)
+    sl = (slice(0, 1), slice(0, T))
+    q, k, v = (inp.qkv_f32(n)[sl] for n in ("q", "k", "v"))
+    g = [getattr(inp, n)[sl] for n in ("alpha", "eta", "beta")]
+    t0 = time.perf_counter()
+    oracle.scan(q, k, v, *g, inp.theta0, inp.s0, wl.chunk, wl.widths, nthreads=threads)
+    dt = time.perf_counter() - t0
+    used = min(threads, wl.heads)
+    return {"value": T / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"fp64 oracle, batch row 0, all {wl.heads} heads, first {T} of {wl.seq_len} "
+                      f"tokens ({dt:.1f} s on {used} threads of {threads} host cores)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the B*H memories are "
+                                   "independent and are not sharded across GPUs; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import sequence_models_amd as tm
+    import synthetic
+
+    name = args.workload or synthetic.HEADLINE
+    wl = synthetic.WORKLOADS[name]
+    inp = synthetic.make_inputs(wl, args.seed)
+    dev = torch.device("cuda:0")
+    t = {}
+    for n in ("q", "k", "v"):
+        a = getattr(inp, n)
+        t[n] = (torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+                if a.dtype == np.uint16 else torch.from_numpy(a).to(dev))
+    for n in ("alpha", "eta", "beta", "theta0", "s0"):
+        t[n] = torch.from_numpy(getattr(inp, n)).to(dev)
+    B, T, H, d = t["q"].shape
+    P = wl.params
+    y = torch.empty_like(t["q"])
+    thT = torch.empty((B, H, P), dtype=torch.float32, device=dev)
+    sT = torch.empty_like(thT)
+    ws_bytes = tm.scan_workspace_size(t["q"], wl.chunk, wl.widths)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        tm.scan(t["q"], t["k"], t["v"], t["alpha"], t["eta"], t["beta"], t["theta0"], t["s0"],
+                wl.chunk, wl.widths, y=y, theta_T=thT, s_T=sT, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+
+    tokens = B * T
+    flops = alg_flops_per_token_head(wl.widths, wl.chunk) * B * T * H
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    # the generic kernel runs its contractions as fp32 FMAs on the vector ALUs
+    bound, peak = "alu", PEAKS["valu_f32"]
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "heads": H, "seq_len": T, "d_head": d,
+                   "mlp_widths": list(wl.widths), "chunk": wl.chunk, "io": wl.io, "state": "fp32",
+                   "parallelism": "one GPU; one workgroup per (batch row, head) memory"},
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None,
+                     "kernel": "scan_generic_kernel", "kernel_ms": kernel_ms,
+                     "alg_flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes(wl)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_sample_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+/*
+ * titans_mem.h -- C ABI of libtitans_mem.so, the MI355X (gfx950) Titans
+ * neural long-term memory scan.
+ *
+ * The method (Titans: Learning to Memorize at Test Time; the lowest.today
+ * summary, sections "Meccanismo di Aggiornamento della Memoria",
+ * "Meccanismo di Dimenticanza", "Funzione Obiettivo", "Addestramento
+ * Parallelizzato"; the 0h-n0.github.io explainer, sections "Surprise機構",
+ * "ニューラル長期メモリモジュール", "モメンタム機構", "適応的重み減衰"):
+ *
+ *   memory   M_theta: bias-free MLP, widths n_0..n_L with n_0 = n_L = d, SiLU
+ *            between layers, no activation after the last layer.
+ *   read     y_t = M_{theta_t}(q_t), theta_t = weights before token t's write.
+ *   loss     l_t = || M_theta(k_t) - v_t ||_2^2   (no 1/2).
+ *   momentum s_t = beta_t s_{t-1} + (1 - beta_t) grad_theta l_t
+ *   write    theta_{t+1} = (1 - alpha_t) theta_t - eta_t s_t
+ *   chunks   the sequence is cut into chunks of C tokens from the call's first
+ *            token (the last may be partial); inside a chunk every gradient is
+ *            taken at the chunk-start weights (tensorized mini-batch descent).
+ *
+ * One memory per (batch row b, head h); all B*H sequences go in one call.
+ *
+ * Layouts (element strides given in titans_scan_desc; the innermost dimension
+ * is always contiguous):
+ *   q, k, v, y      [B, T, H, d]   io_dtype (fp32 or bf16), d contiguous
+ *   alpha, eta, beta [B, T, H]     fp32
+ *   theta, s        [B, H, P]      fp32, P contiguous: layers l = 1..L
+ *                   concatenated, W_l row-major (n_l rows x n_{l-1} cols),
+ *                   so z_l = W_l h_{l-1}.  P = sum_l n_l n_{l-1}.
+ *
+ * Ownership: the caller allocates every device buffer (inputs, outputs and
+ * the workspace) and keeps it alive until the stream has run the call.  The
+ * library never allocates or frees device memory and never synchronizes the
+ * stream; all work is enqueued on the given stream (a hipStream_t passed as
+ * void*, NULL = the null stream).  The only global state is a thread-local
+ * error string.
+ *
+ * Errors: every argument is checked on the host before any device work; on
+ * error nothing is enqueued and nothing is written.  A kernel launch failure
+ * returns TITANS_ERR_HIP with the HIP error text in titans_last_error().  Device
+ * faults surface when the caller synchronizes the stream.  NaN/Inf inputs are
+ * not checked and propagate.
+ */
+#ifndef TITANS_MEM_H
+#define TITANS_MEM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TITANS_MEM_ABI_VERSION 1
+#define TITANS_MAX_LAYERS 4
+
+typedef enum {
+    TITANS_OK = 0,
+    TITANS_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size/stride, overlap, bad dtype */
+    TITANS_ERR_UNSUPPORTED = 2,      /* valid, but outside the compiled shapes */
+    TITANS_ERR_WORKSPACE = 3,        /* workspace smaller than titans_mem_scan_workspace_size */
+    TITANS_ERR_HIP = 4               /* a HIP runtime call failed (see titans_last_error) */
+} titans_status;
+
+typedef enum { TITANS_F32 = 0, TITANS_BF16 = 1 } titans_dtype;
+
+/* The memory MLP: n_layers = L (1..TITANS_MAX_LAYERS), width[0..L] = n_0..n_L,
+ * width[0] = width[L] = d.  Entries past L are ignored. */
+typedef struct {
+    int32_t n_layers;
+    int32_t width[TITANS_MAX_LAYERS + 1];
+} titans_mlp_desc;
+
+/* Problem shape and strides (all strides in elements, not bytes). */
+typedef struct {
+    int64_t batch;            /* B >= 0 */
+    int64_t seq_len;          /* T >= 0 */
+    int64_t heads;            /* H >= 0 */
+    int32_t chunk;            /* C >= 1 (ignored by titans_mem_retrieve) */
+    int32_t io_dtype;         /* titans_dtype of q, k, v and y */
+    int64_t qkv_stride[3];    /* strides of q, k, v over (b, t, h) */
+    int64_t y_stride[3];      /* strides of y over (b, t, h) */
+    int64_t gate_stride[3];   /* strides of alpha, eta, beta over (b, t, h) */
+    int64_t state_stride[2];  /* strides of theta_T, s_T (retrieve: theta) over (b, h) */
+    int64_t state0_stride[2]; /* strides of theta0, s0 over (b, h); a b-stride of 0 shares
+                                 one initial memory per head across the batch */
+} titans_scan_desc;
+
+/* Version of this ABI (TITANS_MEM_ABI_VERSION of the built library). */
+int titans_abi_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char* titans_status_string(int status);
+
+/* Detail of the last failing call on this thread ("" if none).  Valid until the
+ * next call on this thread. */
+const char* titans_last_error(void);
+
+/* P = sum_l n_l n_{l-1} floats per memory, or -1 if mlp is invalid. */
+int64_t titans_mem_param_count(const titans_mlp_desc* mlp);
+
+/* Device workspace bytes titans_mem_scan needs for this problem (0 if none;
+ * SIZE_MAX if the arguments are invalid).  The workspace must be 256-byte aligned. */
+size_t titans_mem_scan_workspace_size(const titans_scan_desc* desc, const titans_mlp_desc* mlp);
+
+/*
+ * The chunked memory scan: for every (b, h), run the write rule over T tokens
+ * starting from (theta0, s0), read y before each token's write, and return the
+ * final memory and momentum.
+ *
+ *   q, k, v   device, io_dtype, desc->qkv_stride
+ *   alpha, eta, beta   device fp32, desc->gate_stride; alpha, eta, beta in [0, 1]
+ *                      by the method's gating (not checked)
+ *   theta0, s0 device fp32 [.., P], desc->state0_stride
+ *   y          device, io_dtype, desc->y_stride (written for every token)
+ *   theta_T, s_T device fp32, desc->state_stride (may be exactly theta0 / s0 for
+ *              in-place streaming when their strides agree; any other overlap between
+ *              an output and any other buffer is TITANS_ERR_INVALID_ARGUMENT)
+ *   workspace  device, >= titans_mem_scan_workspace_size bytes (may be NULL if that is 0)
+ *
+ * Calls chain exactly: scan(T1) then scan(T2) from (theta_T, s_T) equals scan(T1 + T2)
+ * when T1 is a multiple of C.  T = 0 copies theta0 -> theta_T and s0 -> s_T.
+ * Supported shapes (else TITANS_ERR_UNSUPPORTED): d <= 128, every width <= 512,
+ * L <= 4, C <= 256, io_dtype fp32 or bf16.  q, k, v, y rows must be 16-byte aligned
+ * (bf16: d % 8 == 0; fp32: d % 4 == 0).
+ */
+titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
+                              const void* q, const void* k, const void* v,
+                              const float* alpha, const float* eta, const float* beta,
+                              const float* theta0, const float* s0,
+                              void* y, float* theta_T, float* s_T,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Read with fixed weights (the explainer's retrieve formula with theta held
+ * constant): y[b,t,h] = M_{theta[b,h]}(q[b,t,h]).
+ *   q      device, io_dtype, desc->qkv_stride
+ *   theta  device fp32, desc->state_stride (b-stride 0 shares one memory per head)
+ *   y      device, io_dtype, desc->y_stride; must not overlap q or theta
+ * desc->chunk and the gate/state0 strides are ignored.  Same shape limits as the scan.
+ */
+titans_status titans_mem_retrieve(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
+                                  const void* q, const float* theta, void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TITANS_MEM_H */

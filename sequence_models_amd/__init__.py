@@ -1,0 +1,202 @@
+"""Python binding of libtitans_mem.so (the Titans memory scan for MI355X).
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+the library, on torch's current stream.  torch supplies device memory and the
+stream; nothing here computes.  If the library is not built this module raises
+at import time -- there is no fallback.
+
+    scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths) -> (y, theta_T, s_T)
+    retrieve(q, theta, widths) -> y
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["scan", "retrieve", "scan_workspace_size", "param_count", "TitansError", "LIB_PATH",
+           "lib", "ScanDesc", "MlpDesc", "MAX_LAYERS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtitans_mem.so")
+MAX_LAYERS = 4
+F32, BF16 = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+
+
+class MlpDesc(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("width", ctypes.c_int32 * (MAX_LAYERS + 1))]
+
+
+class ScanDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64), ("heads", ctypes.c_int64),
+                ("chunk", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+                ("qkv_stride", ctypes.c_int64 * 3), ("y_stride", ctypes.c_int64 * 3),
+                ("gate_stride", ctypes.c_int64 * 3), ("state_stride", ctypes.c_int64 * 2),
+                ("state0_stride", ctypes.c_int64 * 2)]
+
+
+lib = ctypes.CDLL(LIB_PATH)
+_vp = ctypes.c_void_p
+lib.titans_abi_version.restype = ctypes.c_int
+lib.titans_status_string.restype = ctypes.c_char_p
+lib.titans_status_string.argtypes = [ctypes.c_int]
+lib.titans_last_error.restype = ctypes.c_char_p
+lib.titans_mem_param_count.restype = ctypes.c_int64
+lib.titans_mem_param_count.argtypes = [ctypes.POINTER(MlpDesc)]
+lib.titans_mem_scan_workspace_size.restype = ctypes.c_size_t
+lib.titans_mem_scan_workspace_size.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)]
+lib.titans_mem_scan.restype = ctypes.c_int
+lib.titans_mem_scan.argtypes = ([ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)] + [_vp] * 12
+                                + [ctypes.c_size_t, _vp])
+lib.titans_mem_retrieve.restype = ctypes.c_int
+lib.titans_mem_retrieve.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc), _vp, _vp,
+                                    _vp, _vp]
+
+
+class TitansError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        name = lib.titans_status_string(status).decode()
+        super().__init__(f"{name}: {message}")
+
+
+def _check(status: int):
+    if status != 0:
+        raise TitansError(status, lib.titans_last_error().decode())
+
+
+def mlp_desc(widths) -> MlpDesc:
+    widths = [int(w) for w in widths]
+    m = MlpDesc()
+    m.n_layers = len(widths) - 1
+    for i, w in enumerate(widths[:MAX_LAYERS + 1]):
+        m.width[i] = w
+    return m
+
+
+def param_count(widths) -> int:
+    return int(lib.titans_mem_param_count(ctypes.byref(mlp_desc(widths))))
+
+
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _strides3(t: torch.Tensor, name: str):
+    if t.numel() == 0:  # nothing is accessed; report packed strides
+        return t.shape[1] * t.shape[2] * t.shape[3], t.shape[2] * t.shape[3], t.shape[3]
+    if t.stride(-1) != 1 and t.shape[-1] > 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    return t.stride(0), t.stride(1), t.stride(2)
+
+
+def _state_strides(t: torch.Tensor, batch: int, name: str):
+    """[H,P] (shared over the batch: b-stride 0) or [B,H,P]; P contiguous."""
+    if t.numel() == 0:
+        return (0, t.shape[-1]) if t.dim() == 2 else (t.shape[1] * t.shape[2], t.shape[2])
+    if t.stride(-1) != 1 and t.shape[-1] > 1:
+        raise ValueError(f"{name}: P must be contiguous")
+    if t.dim() == 2:
+        return 0, t.stride(0)
+    if t.dim() == 3 and t.shape[0] == batch:
+        return t.stride(0), t.stride(1)
+    raise ValueError(f"{name}: expected [H,P] or [B,H,P], got {tuple(t.shape)}")
+
+
+def make_desc(q, chunk, y, gates, theta_T, theta0) -> ScanDesc:
+    B, T, H, _ = q.shape
+    d = ScanDesc()
+    d.batch, d.seq_len, d.heads = B, T, H
+    d.chunk = int(chunk)
+    d.io_dtype = _io_dtype(q)
+    d.qkv_stride[:] = _strides3(q, "q")
+    d.y_stride[:] = _strides3(y, "y")
+    if gates is not None:
+        d.gate_stride[:] = gates.stride()
+    if theta_T is not None:
+        d.state_stride[:] = _state_strides(theta_T, B, "theta_T")
+    if theta0 is not None:
+        d.state0_stride[:] = _state_strides(theta0, B, "theta0")
+    return d
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def scan_workspace_size(q, chunk, widths) -> int:
+    """Workspace bytes titans_mem_scan needs for q's shape (raises on invalid arguments)."""
+    d = make_desc(q, chunk, q, None, None, None)
+    n = lib.titans_mem_scan_workspace_size(ctypes.byref(d), ctypes.byref(mlp_desc(widths)))
+    if n == ctypes.c_size_t(-1).value:
+        raise TitansError(1, "invalid scan shape or MLP widths")
+    return int(n)
+
+
+def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, *, y=None, theta_T=None, s_T=None,
+         workspace=None):
+    """Chunked Titans memory scan on the current stream.
+
+    q, k, v: [B,T,H,d] float32/bfloat16 CUDA tensors (d contiguous);
+    alpha, eta, beta: [B,T,H] float32; theta0, s0: [H,P] (shared by the batch) or [B,H,P].
+    Returns (y [B,T,H,d] like q, theta_T [B,H,P], s_T [B,H,P]).  theta_T / s_T may be passed
+    as theta0 / s0 themselves for in-place streaming.
+    """
+    B, T, H, dd = q.shape
+    P = param_count(widths)
+    if y is None:
+        y = torch.empty((B, T, H, dd), dtype=q.dtype, device=q.device)
+    if theta_T is None:
+        theta_T = torch.empty((B, H, P), dtype=torch.float32, device=q.device)
+    if s_T is None:
+        s_T = torch.empty((B, H, P), dtype=torch.float32, device=q.device)
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.stride() != q.stride() or t.dtype != q.dtype:
+            raise ValueError(f"{name} must have q's shape, strides and dtype")
+    for name, g in (("eta", eta), ("beta", beta)):
+        if g.shape != alpha.shape or g.stride() != alpha.stride():
+            raise ValueError(f"{name} must have alpha's shape and strides")
+    for name, t in (("alpha", alpha), ("eta", eta), ("beta", beta), ("theta0", theta0), ("s0", s0),
+                    ("theta_T", theta_T), ("s_T", s_T)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if s0.stride() != theta0.stride() or s0.shape != theta0.shape:
+        raise ValueError("s0 must have theta0's shape and strides")
+    if s_T.stride() != theta_T.stride() or s_T.shape != theta_T.shape:
+        raise ValueError("s_T must have theta_T's shape and strides")
+    desc = make_desc(q, chunk, y, alpha, theta_T, theta0)
+    mlp = mlp_desc(widths)
+    if workspace is None:
+        n = lib.titans_mem_scan_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+        if n == ctypes.c_size_t(-1).value:
+            n = 0  # the scan call below reports the argument error
+        workspace = torch.empty(max(int(n), 1), dtype=torch.uint8, device=q.device) if n else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.titans_mem_scan(ctypes.byref(desc), ctypes.byref(mlp), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(alpha), _ptr(eta), _ptr(beta), _ptr(theta0), _ptr(s0), _ptr(y),
+                               _ptr(theta_T), _ptr(s_T), _ptr(workspace), ws_bytes, _stream()))
+    return y, theta_T, s_T
+
+
+def retrieve(q, theta, widths, *, y=None):
+    """y = M_theta(q) with fixed weights; q [B,T,H,d], theta [H,P] or [B,H,P] float32."""
+    B, T, H, dd = q.shape
+    if y is None:
+        y = torch.empty((B, T, H, dd), dtype=q.dtype, device=q.device)
+    if theta.dtype != torch.float32:
+        raise TypeError("theta must be float32")
+    desc = make_desc(q, 1, y, None, theta, None)
+    _check(lib.titans_mem_retrieve(ctypes.byref(desc), ctypes.byref(mlp_desc(widths)), _ptr(q),
+                                   _ptr(theta), _ptr(y), _stream()))
+    return y

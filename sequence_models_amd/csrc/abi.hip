@@ -1,0 +1,338 @@
+// C-ABI layer of libtitans_mem: host-side validation, workspace sizing and
+// kernel dispatch.  Every check runs before any HIP call, so an invalid call
+// enqueues nothing and writes nothing.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "titans_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+titans_status fail(titans_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+// Byte interval [lo, hi) touched by a strided tensor; empty tensors touch nothing.
+struct Span {
+    uintptr_t lo = 0, hi = 0;
+    bool empty() const { return hi <= lo; }
+};
+
+Span span_of(const void* p, const int64_t* sizes, const int64_t* strides, int nd, size_t elem) {
+    Span s;
+    int64_t last = 0;
+    for (int i = 0; i < nd; ++i) {
+        if (sizes[i] == 0) return s;
+        last += (sizes[i] - 1) * strides[i];
+    }
+    s.lo = reinterpret_cast<uintptr_t>(p);
+    s.hi = s.lo + (uintptr_t)((last + 1) * (int64_t)elem);
+    return s;
+}
+
+bool overlaps(const Span& a, const Span& b) {
+    if (a.empty() || b.empty()) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+// True when distinct indices map to distinct elements (required of outputs).
+bool non_self_overlapping(const int64_t* sizes, const int64_t* strides, int nd) {
+    std::vector<std::pair<int64_t, int64_t>> dims;  // (stride, size)
+    for (int i = 0; i < nd; ++i) {
+        if (sizes[i] == 0) return true;
+        if (sizes[i] > 1) dims.push_back({strides[i], sizes[i]});
+    }
+    std::sort(dims.begin(), dims.end());
+    int64_t extent = 1;  // elements spanned by the inner dims
+    for (auto& ds : dims) {
+        if (ds.first < extent) return false;
+        extent = ds.first * (ds.second - 1) + extent;
+    }
+    return true;
+}
+
+bool strides_nonneg(const int64_t* s, int n) {
+    for (int i = 0; i < n; ++i)
+        if (s[i] < 0) return false;
+    return true;
+}
+
+titans_status check_mlp(const titans_mlp_desc* mlp, titans::ScanArgs& a) {
+    if (!mlp) return fail(TITANS_ERR_INVALID_ARGUMENT, "mlp descriptor is NULL");
+    if (mlp->n_layers < 1 || mlp->n_layers > TITANS_MAX_LAYERS)
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "n_layers=%d outside 1..%d", mlp->n_layers,
+                    TITANS_MAX_LAYERS);
+    a.L = mlp->n_layers;
+    for (int l = 0; l <= a.L; ++l) {
+        if (mlp->width[l] < 1)
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "width[%d]=%d must be >= 1", l, mlp->width[l]);
+        a.n[l] = mlp->width[l];
+    }
+    for (int l = a.L + 1; l <= TITANS_MAX_LAYERS; ++l) a.n[l] = 0;
+    if (a.n[0] != a.n[a.L])
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "width[0]=%d must equal width[L]=%d (d)", a.n[0],
+                    a.n[a.L]);
+    a.P = 0;
+    a.off[0] = 0;
+    for (int l = 1; l <= a.L; ++l) {
+        a.off[l] = a.P;
+        a.P += (int64_t)a.n[l] * a.n[l - 1];
+    }
+    a.off[a.L + 1] = a.P;
+    return TITANS_OK;
+}
+
+titans_status check_shape_support(const titans::ScanArgs& a, bool scan) {
+    if (a.n[0] > 128)
+        return fail(TITANS_ERR_UNSUPPORTED, "d=%d > 128 is not compiled", a.n[0]);
+    for (int l = 1; l < a.L; ++l)
+        if (a.n[l] > 512) return fail(TITANS_ERR_UNSUPPORTED, "width[%d]=%d > 512", l, a.n[l]);
+    if (scan && a.C > 256) return fail(TITANS_ERR_UNSUPPORTED, "chunk=%d > 256", a.C);
+    if (a.B * a.H > 65535)
+        return fail(TITANS_ERR_UNSUPPORTED, "batch*heads=%lld > 65535",
+                    (long long)(a.B * a.H));
+    return TITANS_OK;
+}
+
+titans_status check_desc_common(const titans_scan_desc* desc, titans::ScanArgs& a) {
+    if (!desc) return fail(TITANS_ERR_INVALID_ARGUMENT, "scan descriptor is NULL");
+    if (desc->batch < 0 || desc->seq_len < 0 || desc->heads < 0)
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "negative size (B=%lld T=%lld H=%lld)",
+                    (long long)desc->batch, (long long)desc->seq_len, (long long)desc->heads);
+    if (desc->io_dtype != TITANS_F32 && desc->io_dtype != TITANS_BF16)
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "io_dtype=%d is neither F32 nor BF16",
+                    desc->io_dtype);
+    a.B = desc->batch;
+    a.T = desc->seq_len;
+    a.H = desc->heads;
+    a.C = desc->chunk;
+    a.io = desc->io_dtype;
+    for (int i = 0; i < 3; ++i) {
+        a.qs[i] = desc->qkv_stride[i];
+        a.ys[i] = desc->y_stride[i];
+        a.gs[i] = desc->gate_stride[i];
+    }
+    for (int i = 0; i < 2; ++i) {
+        a.ss[i] = desc->state_stride[i];
+        a.s0s[i] = desc->state0_stride[i];
+    }
+    if (!strides_nonneg(a.qs, 3) || !strides_nonneg(a.ys, 3) || !strides_nonneg(a.gs, 3) ||
+        !strides_nonneg(a.ss, 2) || !strides_nonneg(a.s0s, 2))
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "negative stride");
+    return TITANS_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+titans_status check_io_alignment(const titans::ScanArgs& a, const void* p, const int64_t* st,
+                                 const char* name) {
+    const int64_t vec = a.io == TITANS_BF16 ? 8 : 4;  // elements per 16 bytes
+    if (a.n[0] % vec)
+        return fail(TITANS_ERR_UNSUPPORTED, "d=%d must be a multiple of %lld for this dtype",
+                    a.n[0], (long long)vec);
+    if (!aligned16(p)) return fail(TITANS_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+    for (int i = 0; i < 3; ++i)
+        if (st[i] % vec)
+            return fail(TITANS_ERR_INVALID_ARGUMENT,
+                        "%s stride[%d]=%lld is not a multiple of 16 bytes", name, i,
+                        (long long)st[i]);
+    return TITANS_OK;
+}
+
+titans_status check_state_alignment(const float* p, const int64_t* st, const char* name) {
+    if (!aligned16(p)) return fail(TITANS_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+    for (int i = 0; i < 2; ++i)
+        if (st[i] % 4)
+            return fail(TITANS_ERR_INVALID_ARGUMENT,
+                        "%s stride[%d]=%lld is not a multiple of 16 bytes", name, i,
+                        (long long)st[i]);
+    return TITANS_OK;
+}
+
+titans_status hip_fail(hipError_t e, const char* what) {
+    return fail(TITANS_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int titans_abi_version(void) { return TITANS_MEM_ABI_VERSION; }
+
+const char* titans_status_string(int status) {
+    switch (status) {
+        case TITANS_OK: return "TITANS_OK";
+        case TITANS_ERR_INVALID_ARGUMENT: return "TITANS_ERR_INVALID_ARGUMENT";
+        case TITANS_ERR_UNSUPPORTED: return "TITANS_ERR_UNSUPPORTED";
+        case TITANS_ERR_WORKSPACE: return "TITANS_ERR_WORKSPACE";
+        case TITANS_ERR_HIP: return "TITANS_ERR_HIP";
+        default: return "TITANS_ERR_UNKNOWN";
+    }
+}
+
+const char* titans_last_error(void) { return g_last_error; }
+
+int64_t titans_mem_param_count(const titans_mlp_desc* mlp) {
+    titans::ScanArgs a{};
+    if (check_mlp(mlp, a) != TITANS_OK) return -1;
+    return a.P;
+}
+
+static titans_status prepare_scan(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
+                                  titans::ScanArgs& a) {
+    titans_status st = check_desc_common(desc, a);
+    if (st) return st;
+    if ((st = check_mlp(mlp, a))) return st;
+    if (a.C < 1) return fail(TITANS_ERR_INVALID_ARGUMENT, "chunk=%d must be >= 1", a.C);
+    return check_shape_support(a, true);
+}
+
+size_t titans_mem_scan_workspace_size(const titans_scan_desc* desc, const titans_mlp_desc* mlp) {
+    titans::ScanArgs a{};
+    if (prepare_scan(desc, mlp, a) != TITANS_OK) return SIZE_MAX;
+    if (a.B * a.H == 0 || a.T == 0) return 0;
+    return titans::scan_generic_workspace_bytes(a);
+}
+
+titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
+                              const void* q, const void* k, const void* v, const float* alpha,
+                              const float* eta, const float* beta, const float* theta0,
+                              const float* s0, void* y, float* theta_T, float* s_T,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    titans::ScanArgs a{};
+    titans_status st = prepare_scan(desc, mlp, a);
+    if (st) return st;
+    const int64_t nseq = a.B * a.H;
+    const bool have_tokens = nseq > 0 && a.T > 0;
+    if (nseq > 0) {
+        if (!theta0 || !s0 || !theta_T || !s_T)
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "theta0, s0, theta_T and s_T must be non-NULL");
+        if ((st = check_state_alignment(theta0, a.s0s, "theta0"))) return st;
+        if ((st = check_state_alignment(s0, a.s0s, "s0"))) return st;
+        if ((st = check_state_alignment(theta_T, a.ss, "theta_T"))) return st;
+        if ((st = check_state_alignment(s_T, a.ss, "s_T"))) return st;
+    }
+    if (have_tokens) {
+        if (!q || !k || !v || !alpha || !eta || !beta || !y)
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "q, k, v, alpha, eta, beta and y must be non-NULL");
+        if ((st = check_io_alignment(a, q, a.qs, "q"))) return st;
+        if ((st = check_io_alignment(a, k, a.qs, "k"))) return st;
+        if ((st = check_io_alignment(a, v, a.qs, "v"))) return st;
+        if ((st = check_io_alignment(a, y, a.ys, "y"))) return st;
+    }
+    // ---- aliasing rules
+    const size_t esz = a.io == TITANS_BF16 ? 2 : 4;
+    const int64_t io_sz[4] = {a.B, a.T, a.H, a.n[0]};
+    const int64_t qst[4] = {a.qs[0], a.qs[1], a.qs[2], 1};
+    const int64_t yst[4] = {a.ys[0], a.ys[1], a.ys[2], 1};
+    const int64_t g_sz[3] = {a.B, a.T, a.H};
+    const int64_t st_sz[3] = {a.B, a.H, a.P};
+    const int64_t sst[3] = {a.ss[0], a.ss[1], 1};
+    const int64_t s0st[3] = {a.s0s[0], a.s0s[1], 1};
+    if (!non_self_overlapping(io_sz, yst, 4))
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "y strides make distinct elements alias");
+    if (!non_self_overlapping(st_sz, sst, 3))
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "theta_T/s_T strides make distinct elements alias");
+    Span sy = have_tokens ? span_of(y, io_sz, yst, 4, esz) : Span{};
+    Span sth = span_of(theta_T, st_sz, sst, 3, 4), ssT = span_of(s_T, st_sz, sst, 3, 4);
+    Span ins[8];
+    int nin = 0;
+    if (have_tokens) {
+        ins[nin++] = span_of(q, io_sz, qst, 4, esz);
+        ins[nin++] = span_of(k, io_sz, qst, 4, esz);
+        ins[nin++] = span_of(v, io_sz, qst, 4, esz);
+        ins[nin++] = span_of(alpha, g_sz, a.gs, 3, 4);
+        ins[nin++] = span_of(eta, g_sz, a.gs, 3, 4);
+        ins[nin++] = span_of(beta, g_sz, a.gs, 3, 4);
+    }
+    Span sth0 = span_of(theta0, st_sz, s0st, 3, 4), ss0 = span_of(s0, st_sz, s0st, 3, 4);
+    const bool same_strides = a.ss[0] == a.s0s[0] && a.ss[1] == a.s0s[1];
+    const bool theta_inplace = theta_T == theta0 && same_strides;
+    const bool s_inplace = s_T == s0 && same_strides;
+    for (int i = 0; i < nin; ++i) {
+        if (overlaps(sy, ins[i]) || overlaps(sth, ins[i]) || overlaps(ssT, ins[i]))
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "an output overlaps an input");
+    }
+    if (overlaps(sy, sth) || overlaps(sy, ssT) || overlaps(sth, ssT) || overlaps(sy, sth0) ||
+        overlaps(sy, ss0))
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "outputs y, theta_T and s_T must not overlap");
+    if (!theta_inplace && (overlaps(sth, sth0) || overlaps(sth, ss0)))
+        return fail(TITANS_ERR_INVALID_ARGUMENT,
+                    "theta_T overlaps theta0/s0 without being exactly theta0");
+    if (!s_inplace && (overlaps(ssT, ss0) || overlaps(ssT, sth0)))
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "s_T overlaps theta0/s0 without being exactly s0");
+    if (theta_inplace && overlaps(sth, ss0) && !s_inplace)
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "theta_T overlaps s0");
+    // ---- workspace
+    size_t need = titans_mem_scan_workspace_size(desc, mlp);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(TITANS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+        Span sw{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+        for (int i = 0; i < nin; ++i)
+            if (overlaps(sw, ins[i])) return fail(TITANS_ERR_INVALID_ARGUMENT, "workspace overlaps an input");
+        if (overlaps(sw, sy) || overlaps(sw, sth) || overlaps(sw, ssT) || overlaps(sw, sth0) ||
+            overlaps(sw, ss0))
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "workspace overlaps a state or output buffer");
+    }
+    if (nseq == 0) return TITANS_OK;
+    a.q = q; a.k = k; a.v = v;
+    a.alpha = alpha; a.eta = eta; a.beta = beta;
+    a.theta0 = theta0; a.s0 = s0;
+    a.y = y; a.thetaT = theta_T; a.sT = s_T;
+    a.ws = workspace;
+    hipError_t e = titans::launch_scan_generic(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "scan launch");
+    return TITANS_OK;
+}
+
+titans_status titans_mem_retrieve(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
+                                  const void* q, const float* theta, void* y, void* stream) {
+    g_last_error[0] = '\0';
+    titans::ScanArgs a{};
+    titans_status st = check_desc_common(desc, a);
+    if (st) return st;
+    if ((st = check_mlp(mlp, a))) return st;
+    if ((st = check_shape_support(a, false))) return st;
+    const int64_t nseq = a.B * a.H;
+    if (nseq == 0 || a.T == 0) return TITANS_OK;
+    if (!q || !theta || !y)
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "q, theta and y must be non-NULL");
+    if ((st = check_io_alignment(a, q, a.qs, "q"))) return st;
+    if ((st = check_io_alignment(a, y, a.ys, "y"))) return st;
+    if ((st = check_state_alignment(theta, a.ss, "theta"))) return st;
+    const size_t esz = a.io == TITANS_BF16 ? 2 : 4;
+    const int64_t io_sz[4] = {a.B, a.T, a.H, a.n[0]};
+    const int64_t qst[4] = {a.qs[0], a.qs[1], a.qs[2], 1};
+    const int64_t yst[4] = {a.ys[0], a.ys[1], a.ys[2], 1};
+    const int64_t st_sz[3] = {a.B, a.H, a.P};
+    const int64_t sst[3] = {a.ss[0], a.ss[1], 1};
+    if (!non_self_overlapping(io_sz, yst, 4))
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "y strides make distinct elements alias");
+    Span sy = span_of(y, io_sz, yst, 4, esz);
+    if (overlaps(sy, span_of(q, io_sz, qst, 4, esz)) || overlaps(sy, span_of(theta, st_sz, sst, 3, 4)))
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "y overlaps q or theta");
+    a.q = q;
+    a.thetaT = const_cast<float*>(theta);
+    a.y = y;
+    hipError_t e = titans::launch_retrieve_generic(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "retrieve launch");
+    return TITANS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Internal interface between the C-ABI layer and the HIP kernels of libtitans_mem.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "titans_mem.h"
+
+namespace titans {
+
+// Everything a scan or retrieve launch needs, already validated on the host.
+struct ScanArgs {
+    int64_t B, T, H;
+    int C;
+    int io;                    // titans_dtype
+    int L;
+    int n[TITANS_MAX_LAYERS + 1];
+    int64_t P;
+    int64_t off[TITANS_MAX_LAYERS + 2];  // float offset of W_l inside one memory, l = 1..L
+    int64_t qs[3], ys[3], gs[3], ss[2], s0s[2];
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* eta;
+    const float* beta;
+    const float* theta0;
+    const float* s0;
+    void* y;
+    float* thetaT;
+    float* sT;
+    void* ws;
+};
+
+// Generic chunked scan: fp32 arithmetic, any supported shape, one workgroup per
+// (b, h), per-chunk intermediates in the workspace.
+size_t scan_generic_workspace_bytes(const ScanArgs& a);
+hipError_t launch_scan_generic(const ScanArgs& a, hipStream_t stream);
+
+// Generic retrieve: fp32 arithmetic, any supported shape.
+hipError_t launch_retrieve_generic(const ScanArgs& a, hipStream_t stream);
+
+}  // namespace titans

@@ -1,0 +1,162 @@
+"""The C-ABI library loads, exports every function include/titans_mem.h declares, and
+rejects invalid calls on the host, before any HIP work.
+
+No call here does device work: every scan/retrieve call is built to fail host
+validation (the status is checked to be a validation error, never TITANS_ERR_HIP).
+Calls that pass fake pointers are skipped when a GPU is visible.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "titans_mem.h")
+
+tm = pytest.importorskip("sequence_models_amd")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(titans_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"titans_mem_scan", "titans_mem_retrieve", "titans_mem_scan_workspace_size",
+            "titans_abi_version", "titans_status_string", "titans_last_error",
+            "titans_mem_param_count"} <= set(names)
+    lib = ctypes.CDLL(tm.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in titans_mem.h but not exported"
+
+
+def test_version_status_strings_and_param_count():
+    assert tm.lib.titans_abi_version() == 1
+    assert tm.lib.titans_status_string(0) == b"TITANS_OK"
+    assert tm.lib.titans_status_string(3) == b"TITANS_ERR_WORKSPACE"
+    assert tm.param_count((64, 256, 64)) == 32768
+    assert tm.param_count((128, 512, 512, 512, 128)) == 655360
+    assert tm.param_count((16, 64, 16)) == 2048
+    assert tm.lib.titans_mem_param_count(ctypes.byref(tm.mlp_desc((4,)))) == -1
+    assert tm.lib.titans_mem_param_count(ctypes.byref(tm.mlp_desc((4, 8, 5)))) == -1
+
+
+def _desc(B=2, T=64, H=4, d=64, C=64, io=1):
+    desc = tm.ScanDesc()
+    desc.batch, desc.seq_len, desc.heads, desc.chunk, desc.io_dtype = B, T, H, C, io
+    desc.qkv_stride[:] = (T * H * d, H * d, d)
+    desc.y_stride[:] = (T * H * d, H * d, d)
+    desc.gate_stride[:] = (T * H, H, 1)
+    return desc
+
+
+def test_workspace_size_query():
+    mlp = tm.mlp_desc((64, 256, 64))
+    size = tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc()), ctypes.byref(mlp))
+    assert 0 < size < 1 << 30 and size % 4 == 0
+    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(T=0)), ctypes.byref(mlp)) == 0
+    bad = ctypes.c_size_t(-1).value
+    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(C=0)), ctypes.byref(mlp)) == bad
+    assert tm.lib.titans_mem_scan_workspace_size(None, ctypes.byref(mlp)) == bad
+    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(C=300)),
+                                                 ctypes.byref(mlp)) == bad
+
+
+def _scan(desc, mlp, ptrs=None, ws=None, ws_bytes=0):
+    p = ptrs or {}
+    args = [p.get(n) for n in ("q", "k", "v", "alpha", "eta", "beta", "theta0", "s0", "y",
+                               "theta_T", "s_T")]
+    st = tm.lib.titans_mem_scan(ctypes.byref(desc) if desc is not None else None,
+                                ctypes.byref(mlp) if mlp is not None else None,
+                                *args, ws, ws_bytes, None)
+    assert st != HIP, "validation let the call through to HIP"
+    return st, tm.lib.titans_last_error().decode()
+
+
+def test_validation_of_descriptors():
+    mlp = tm.mlp_desc((64, 256, 64))
+    assert _scan(None, mlp)[0] == INVALID
+    assert _scan(_desc(), None)[0] == INVALID
+    assert _scan(_desc(C=0), mlp)[0] == INVALID
+    assert _scan(_desc(B=-1), mlp)[0] == INVALID
+    assert _scan(_desc(io=7), mlp)[0] == INVALID
+    assert _scan(_desc(), tm.mlp_desc((64, 256, 32)))[0] == INVALID
+    assert _scan(_desc(), tm.mlp_desc((64, 1, 1, 1, 1, 64)))[0] == INVALID   # 5 layers
+    assert _scan(_desc(C=512), mlp)[0] == UNSUPPORTED
+    assert _scan(_desc(d=256), tm.mlp_desc((256, 256, 256)))[0] == UNSUPPORTED
+    assert _scan(_desc(), tm.mlp_desc((64, 1024, 64)))[0] == UNSUPPORTED
+    st, msg = _scan(_desc(), mlp)   # all pointers NULL
+    assert st == INVALID and "non-NULL" in msg
+
+
+no_fake_pointers_on_gpu = pytest.mark.skipif(
+    __import__("torch").cuda.is_available(), reason="fake device pointers are never passed on a GPU box")
+
+
+def _fake_ptrs(B=2, T=64, H=4, d=64, P=32768, esz=2, base=1 << 40):
+    sizes = {"q": B * T * H * d * esz, "k": B * T * H * d * esz, "v": B * T * H * d * esz,
+             "y": B * T * H * d * esz, "alpha": B * T * H * 4, "eta": B * T * H * 4,
+             "beta": B * T * H * 4, "theta0": H * P * 4, "s0": H * P * 4, "theta_T": B * H * P * 4,
+             "s_T": B * H * P * 4}
+    out, cur = {}, base
+    for n, s in sizes.items():
+        out[n] = cur
+        cur += (s + 4095) // 4096 * 4096
+    return out, cur
+
+
+@no_fake_pointers_on_gpu
+def test_validation_of_overlap_alignment_and_workspace():
+    mlp = tm.mlp_desc((64, 256, 64))
+    B, T, H, d, P = 2, 64, 4, 64, 32768
+    desc = _desc(B, T, H, d)
+    desc.state_stride[:] = (H * P, P)
+    desc.state0_stride[:] = (0, P)
+    ptrs, end = _fake_ptrs()
+    need = tm.lib.titans_mem_scan_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+    # y aliasing q
+    bad = dict(ptrs, y=ptrs["q"])
+    assert _scan(desc, mlp, bad, end, need)[0] == INVALID
+    # theta_T overlapping s0 without being theta0
+    bad = dict(ptrs, theta_T=ptrs["s0"])
+    assert _scan(desc, mlp, bad, end, need)[0] == INVALID
+    # misaligned q
+    bad = dict(ptrs, q=ptrs["q"] + 2)
+    assert _scan(desc, mlp, bad, end, need)[0] == INVALID
+    # workspace too small / missing / overlapping / misaligned
+    assert _scan(desc, mlp, ptrs, end, need - 1)[0] == WORKSPACE
+    assert _scan(desc, mlp, ptrs, None, 0)[0] == WORKSPACE
+    assert _scan(desc, mlp, ptrs, ptrs["v"], need)[0] == INVALID
+    assert _scan(desc, mlp, ptrs, end + 16, need)[0] == INVALID
+    # y strides that alias distinct tokens
+    d2 = _desc(B, T, H, d)
+    d2.state_stride[:] = (H * P, P)
+    d2.state0_stride[:] = (0, P)
+    d2.y_stride[:] = (T * H * d, 0, d)
+    assert _scan(d2, mlp, ptrs, end, need)[0] == INVALID
+    # theta_T with batch stride 0 writes one memory from several batch rows
+    d3 = _desc(B, T, H, d)
+    d3.state_stride[:] = (0, P)
+    d3.state0_stride[:] = (0, P)
+    assert _scan(d3, mlp, ptrs, end, need)[0] == INVALID
+
+
+@no_fake_pointers_on_gpu
+def test_retrieve_validation():
+    mlp = tm.mlp_desc((64, 256, 64))
+    desc = _desc()
+    desc.state_stride[:] = (0, 32768)
+    ptrs, _ = _fake_ptrs()
+    st = tm.lib.titans_mem_retrieve(ctypes.byref(desc), ctypes.byref(mlp), ptrs["q"],
+                                    ptrs["theta0"], ptrs["q"], None)
+    assert st == INVALID
+    st = tm.lib.titans_mem_retrieve(ctypes.byref(desc), ctypes.byref(mlp), None, None, None, None)
+    assert st == INVALID
+    st = tm.lib.titans_mem_retrieve(ctypes.byref(desc), ctypes.byref(tm.mlp_desc((64, 999, 64))),
+                                    ptrs["q"], ptrs["theta0"], ptrs["y"], None)
+    assert st == UNSUPPORTED

@@ -1,0 +1,307 @@
+"""Parity of the HIP scan / retrieve (through the C ABI) against the fp64 oracle.
+
+Bars: fp32 I/O -- relative error <= 1e-4 on y and theta_T; bf16 q/k/v with
+fp32 state -- <= 2e-2 on y and <= 1e-2 on theta_T (relative Frobenius error per
+(b, h), maximum over (b, h)).  Full-size workloads run at their full shape on
+the GPU, in the launch configuration the bench times; the oracle then checks
+sampled sequences (whole or a prefix: the scan is causal, so a prefix of y
+depends only on the prefix of the inputs).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+import sequence_models_amd as tm  # noqa: E402
+import synthetic  # noqa: E402
+from tests.helpers import state_rel_err, to_device, to_f64, y_rel_err  # noqa: E402
+
+Y_BAR = {"f32": 1e-4, "bf16": 2e-2}
+TH_BAR = {"f32": 1e-4, "bf16": 1e-2}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(dev, wl, **kw):
+    return tm.scan(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["eta"], dev["beta"],
+                   dev["theta0"], dev["s0"], wl.chunk, wl.widths, **kw)
+
+
+def oracle_seq(inp, pairs, T=None, theta0=None, s0=None):
+    """Oracle on the (b, h) pairs (prefix T), all pairs in one OpenMP-parallel call.
+    Returns a list of (y [T,d], theta_T [P], s_T [P])."""
+    wl = inp.workload
+    T = wl.seq_len if T is None else T
+    bs = [b for b, _ in pairs]
+    hs = [h for _, h in pairs]
+
+    def gather(a):
+        return np.stack([a[b, :T, h] for b, h in pairs], axis=1)[None]  # [1,T,n,...]
+
+    qkv = [gather(inp.qkv_f32(n)) for n in ("q", "k", "v")]
+    gates = [gather(getattr(inp, n)) for n in ("alpha", "eta", "beta")]
+    th0 = (inp.theta0 if theta0 is None else theta0)[hs]
+    sg0 = (inp.s0 if s0 is None else s0)[hs]
+    y, th, s = oracle.scan(*qkv, *gates, th0, sg0, wl.chunk, wl.widths)
+    del bs
+    return [(y[0, :, i], th[0, i], s[0, i]) for i in range(len(pairs))]
+
+
+def check_pairs(wl, y, thT, sT, pairs, refs, T=None, check_state=True):
+    yg = to_f64(y)
+    tg = to_f64(thT)
+    sg = to_f64(sT)
+    for (b, h), (yr, tr, sr) in zip(pairs, refs):
+        Tn = yr.shape[0]
+        ey = y_rel_err(yg[b:b + 1, :Tn, h:h + 1], yr[None, :, None])
+        msg = f"{wl.name} (b={b},h={h}) T={Tn}: y rel err {ey:.2e}"
+        if check_state:
+            et = state_rel_err(tg[b:b + 1, h:h + 1], tr[None, None])
+            es = state_rel_err(sg[b:b + 1, h:h + 1], sr[None, None])
+            msg += f", theta_T {et:.2e}, s_T {es:.2e}"
+        log(msg)
+        assert ey <= Y_BAR[wl.io], msg
+        if check_state:
+            assert et <= TH_BAR[wl.io], msg
+            assert es <= TH_BAR[wl.io], msg
+
+
+# ---------------------------------------------------------------- workloads
+#
+# With the specified gates (alpha ~ 0.028 per token) and i.i.d. random q/k/v the
+# memory decays to its zero fixed point within a few thousand tokens, so at full
+# length theta_T and late y are ~0 in both the oracle and the GPU.  Each full shape is
+# therefore also run with a "sustained" gate mix (alpha_t = sigmoid(N(mu, 1)) with mu = -7,
+# or -8 for the deep memory) where the memory stays O(1) to the end of the sequence.  With
+# C = 256 the frozen-gradient steps of a chunk add up: eta = 0.1 sigmoid(.) then diverges in
+# the oracle itself, so that shape uses mu = -10 and eta = 0.02 sigmoid(.).
+
+SUSTAINED = {"h8_d64_b4_t4k": (-7.0, 0.1), "h16_d64_b8_t16k": (-7.0, 0.1),
+             "deep_h8_d128_b2_t32k": (-8.0, 0.05), "long_h16_d64_b1_t2m": (-10.0, 0.02)}
+
+
+def _workload(name, sustained):
+    wl = synthetic.WORKLOADS[name]
+    if not sustained:
+        return wl
+    mu, es = SUSTAINED[name]
+    return wl.with_(alpha_mu=mu, eta_scale=es, name=wl.name + "_sustained")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_fp32_full(seed):
+    wl = synthetic.WORKLOADS["tiny_f32_h1_t512"]
+    inp = synthetic.make_inputs(wl, seed)
+    log(f"case tiny_f32 seed={seed}")
+    dev = to_device(inp)
+    y, thT, sT = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    yr, tr, sr = oracle.scan(inp.q, inp.k, inp.v, inp.alpha, inp.eta, inp.beta, inp.theta0, inp.s0,
+                             wl.chunk, wl.widths)
+    ey, et, es = y_rel_err(to_f64(y), yr), state_rel_err(to_f64(thT), tr), state_rel_err(to_f64(sT), sr)
+    log(f"tiny_f32 seed={seed}: y {ey:.2e} theta_T {et:.2e} s_T {es:.2e}")
+    assert ey <= 1e-4 and et <= 1e-4 and es <= 1e-4
+
+
+@pytest.mark.parametrize("sustained", [False, True])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_h8_t4k_sampled(seed, sustained):
+    wl = _workload("h8_d64_b4_t4k", sustained)
+    inp = synthetic.make_inputs(wl, seed)
+    log(f"case {wl.name} seed={seed}")
+    y, thT, sT = run_gpu(to_device(inp), wl)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (3, 7), (1, 4)]
+    check_pairs(wl, y, thT, sT, pairs, oracle_seq(inp, pairs))
+
+
+@pytest.mark.parametrize("sustained", [False, True])
+def test_headline_sampled(sustained):
+    wl = _workload(synthetic.HEADLINE, sustained)
+    inp = synthetic.make_inputs(wl, 0)
+    log(f"case {wl.name} seed=0")
+    y, thT, sT = run_gpu(to_device(inp), wl)
+    torch.cuda.synchronize()
+    full = [(0, 0), (7, 15)]
+    check_pairs(wl, y, thT, sT, full, oracle_seq(inp, full))
+    prefix = [(3, 5), (5, 11), (6, 2)]
+    check_pairs(wl, y, thT, sT, prefix, oracle_seq(inp, prefix, T=1024), check_state=False)
+    # the state after 512 tokens, while it is still O(1) for the specified gates
+    pre = synthetic.make_inputs(wl, 0, seq_len=512)
+    yp, tp, sp = run_gpu(to_device(pre), pre.workload)
+    torch.cuda.synchronize()
+    pairs = [(2, 3), (4, 12)]
+    check_pairs(pre.workload, yp, tp, sp, pairs, oracle_seq(pre, pairs))
+
+
+@pytest.mark.parametrize("sustained", [False, True])
+def test_deep_memory_prefix_and_state(sustained):
+    wl = _workload("deep_h8_d128_b2_t32k", sustained)
+    inp = synthetic.make_inputs(wl, 0)
+    log(f"case {wl.name} full size seed=0")
+    dev = to_device(inp)
+    y, thT, sT = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (1, 7)]
+    check_pairs(wl, y, thT, sT, pairs, oracle_seq(inp, pairs, T=512), check_state=False)
+    # theta after a 768-token prefix (6 chunks), on the GPU alone vs the oracle
+    pre = synthetic.make_inputs(wl, 0, seq_len=768)
+    yp, tp, sp = run_gpu(to_device(pre), pre.workload)
+    torch.cuda.synchronize()
+    pairs = [(0, 3), (1, 6)]
+    check_pairs(pre.workload, yp, tp, sp, pairs, oracle_seq(pre, pairs))
+
+
+@pytest.mark.parametrize("sustained", [False, True])
+def test_long_context_prefix_64k(sustained):
+    wl = _workload("long_h16_d64_b1_t2m", sustained)
+    inp = synthetic.make_inputs(wl, 0, seq_len=65536)
+    log(f"case {wl.name} 64K prefix seed=0")
+    y, thT, sT = run_gpu(to_device(inp), inp.workload)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (0, 9)]
+    check_pairs(inp.workload, y, thT, sT, pairs, oracle_seq(inp, pairs))
+
+
+# -------------------------------------------------------------- edge cases
+
+def _small(widths=(16, 32, 16), B=2, T=37, H=3, C=8, io="f32", seed=5):
+    wl = synthetic.Workload("edge", B, H, T, tuple(widths), C, io)
+    return wl, synthetic.make_inputs(wl, seed)
+
+
+@pytest.mark.parametrize("C", [1, 2, 5, 8, 37, 64])
+@pytest.mark.parametrize("widths", [(16, 16), (16, 32, 16), (8, 24, 12, 8), (16, 40, 24, 32, 16)])
+def test_chunk_sizes_and_depths_fp32(C, widths):
+    wl, inp = _small(widths=widths, C=C)
+    log(f"case edge C={C} widths={widths}")
+    rng = np.random.default_rng(3)
+    s0 = (0.05 * rng.standard_normal(inp.theta0.shape)).astype(np.float32)
+    inp.s0 = s0
+    y, thT, sT = run_gpu(to_device(inp), wl)
+    torch.cuda.synchronize()
+    yr, tr, sr = oracle.scan(inp.q, inp.k, inp.v, inp.alpha, inp.eta, inp.beta, inp.theta0, s0,
+                             C, widths)
+    ey, et, es = y_rel_err(to_f64(y), yr), state_rel_err(to_f64(thT), tr), state_rel_err(to_f64(sT), sr)
+    log(f"  y {ey:.2e} theta_T {et:.2e} s_T {es:.2e}")
+    assert ey <= 1e-4 and et <= 1e-4 and es <= 1e-4
+
+
+def test_bf16_small_ragged():
+    wl, inp = _small(widths=(64, 256, 64), B=1, T=200, H=2, C=64, io="bf16")
+    log("case bf16 ragged T=200 C=64")
+    y, thT, sT = run_gpu(to_device(inp), wl)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (0, 1)]
+    check_pairs(wl, y, thT, sT, pairs, oracle_seq(inp, pairs))
+
+
+def test_empty_and_degenerate():
+    wl, inp = _small(T=0)
+    dev = to_device(inp)
+    log("case T=0")
+    y, thT, sT = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    assert y.shape[1] == 0
+    assert torch.equal(thT[0], dev["theta0"]) and torch.equal(thT[1], dev["theta0"])
+    assert torch.equal(sT[1], dev["s0"])
+    wl, inp = _small(B=0)
+    dev = to_device(inp)
+    y, thT, sT = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    assert thT.shape[0] == 0
+
+
+def test_streaming_chain_and_inplace_and_determinism():
+    wl, inp = _small(T=40, C=8)
+    dev = to_device(inp)
+    log("case streaming / in-place / determinism")
+    y, thT, sT = run_gpu(dev, wl)
+    y2, thT2, sT2 = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(thT, thT2) and torch.equal(sT, sT2)
+    # two calls, the second continuing in place from the first's state
+    B, H = wl.batch, wl.heads
+    th = dev["theta0"].expand(B, -1, -1).contiguous()
+    s = dev["s0"].expand(B, -1, -1).contiguous()
+    half = {n: dev[n][:, :24] for n in ("q", "k", "v", "alpha", "eta", "beta")}
+    rest = {n: dev[n][:, 24:] for n in ("q", "k", "v", "alpha", "eta", "beta")}
+    ya, _, _ = tm.scan(half["q"], half["k"], half["v"], half["alpha"], half["eta"], half["beta"],
+                       th, s, wl.chunk, wl.widths, theta_T=th, s_T=s)
+    yb, _, _ = tm.scan(rest["q"], rest["k"], rest["v"], rest["alpha"], rest["eta"], rest["beta"],
+                       th, s, wl.chunk, wl.widths, theta_T=th, s_T=s)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([ya, yb], dim=1), y)
+    assert torch.equal(th, thT) and torch.equal(s, sT)
+
+
+def test_strided_inputs_and_per_batch_state():
+    wl, inp = _small(B=2, T=33, H=3, C=8)
+    dev = to_device(inp)
+    log("case strided q/k/v and [B,H,P] state")
+    B, T, H, d = dev["q"].shape
+    packed = torch.stack([dev["q"], dev["k"], dev["v"]], dim=3)  # [B,T,H,3,d]
+    q, k, v = packed[:, :, :, 0], packed[:, :, :, 1], packed[:, :, :, 2]
+    g = torch.stack([dev["alpha"], dev["eta"], dev["beta"]], dim=-1)  # [B,T,H,3]
+    rng = np.random.default_rng(9)
+    th0 = torch.from_numpy(rng.standard_normal((B, H, wl.params)).astype(np.float32) * 0.2).cuda()
+    s0 = torch.from_numpy(rng.standard_normal((B, H, wl.params)).astype(np.float32) * 0.01).cuda()
+    y, thT, sT = tm.scan(q, k, v, g[..., 0], g[..., 1], g[..., 2], th0, s0, wl.chunk, wl.widths)
+    torch.cuda.synchronize()
+    yr, tr, sr = oracle.scan(inp.q, inp.k, inp.v, inp.alpha, inp.eta, inp.beta, to_f64(th0),
+                             to_f64(s0), wl.chunk, wl.widths)
+    assert y_rel_err(to_f64(y), yr) <= 1e-4
+    assert state_rel_err(to_f64(thT), tr) <= 1e-4
+    assert state_rel_err(to_f64(sT), sr) <= 1e-4
+
+
+def test_invalid_arguments_raise():
+    wl, inp = _small()
+    dev = to_device(inp)
+    with pytest.raises(tm.TitansError, match="INVALID_ARGUMENT"):
+        tm.scan(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["eta"], dev["beta"], dev["theta0"],
+                dev["s0"], 0, wl.widths)
+    with pytest.raises(tm.TitansError, match="UNSUPPORTED"):
+        tm.scan(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["eta"], dev["beta"], dev["theta0"],
+                dev["s0"], 512, wl.widths)
+    with pytest.raises(tm.TitansError, match="INVALID_ARGUMENT"):  # y overlapping q
+        tm.scan(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["eta"], dev["beta"], dev["theta0"],
+                dev["s0"], 8, wl.widths, y=dev["q"])
+
+
+# ----------------------------------------------------------------- retrieve
+
+@pytest.mark.parametrize("io,widths", [("f32", (16, 32, 16)), ("f32", (8, 24, 12, 8)),
+                                       ("bf16", (64, 256, 64))])
+def test_retrieve_matches_oracle(io, widths):
+    wl, inp = _small(widths=widths, B=2, T=45, H=3, io=io)
+    dev = to_device(inp)
+    log(f"case retrieve {io} {widths}")
+    rng = np.random.default_rng(4)
+    theta = (rng.standard_normal((2, 3, wl.params)) / 4).astype(np.float32)
+    y = tm.retrieve(dev["q"], torch.from_numpy(theta).cuda(), widths)
+    torch.cuda.synchronize()
+    yr = oracle.retrieve(inp.qkv_f32("q"), theta, widths)
+    assert y_rel_err(to_f64(y), yr) <= Y_BAR[io]
+
+
+def test_retrieve_headline_shape_sampled():
+    wl = synthetic.WORKLOADS[synthetic.HEADLINE]
+    inp = synthetic.make_inputs(wl, 0)
+    dev = to_device(inp)
+    log("case retrieve headline shape")
+    y = tm.retrieve(dev["q"], dev["theta0"], wl.widths)
+    torch.cuda.synchronize()
+    yr = oracle.retrieve(inp.qkv_f32("q")[:, ::64], inp.theta0, wl.widths)
+    assert y_rel_err(to_f64(y[:, ::64]), yr) <= 2e-2
