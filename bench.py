@@ -13,8 +13,8 @@ chunk-end carry of theta and s 4P, strictly-lower C x C decay-masked terms)
 -- divided by the kernel's average duration from HIP events recorded on the
 stream the kernel runs on, against the MI355X peak of the unit that executes
 it.
-cpu_baseline: the fp64 oracle on a bounded sample of the same workload (batch
-row 0, every head, a prefix of the tokens) on the host cores.
+cpu_baseline: the fp64 oracle on a bounded sample of the same workload (the first
+batch rows, every head, all or a prefix of the tokens) on the host cores.
 """
 from __future__ import annotations
 
@@ -52,21 +52,23 @@ def alg_bytes(wl):
     return th * (4 * wl.d * io + 12) + 4 * 4 * wl.params * wl.batch * wl.heads
 
 
-def cpu_baseline(inp, wl, sample_tokens):
+def cpu_baseline(inp, wl, sample_rows, sample_tokens):
     import oracle
 
     threads = len(os.sched_getaffinity(0))
     T = min(sample_tokens, wl.seq_len)
-    sl = (slice(0, 1), slice(0, T))
+    rows = min(sample_rows, wl.batch)
+    sl = (slice(0, rows), slice(0, T))
     q, k, v = (inp.qkv_f32(n)[sl] for n in ("q", "k", "v"))
     g = [getattr(inp, n)[sl] for n in ("alpha", "eta", "beta")]
     t0 = time.perf_counter()
     oracle.scan(q, k, v, *g, inp.theta0, inp.s0, wl.chunk, wl.widths, nthreads=threads)
     dt = time.perf_counter() - t0
-    used = min(threads, wl.heads)
-    return {"value": T / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": f"fp64 oracle, batch row 0, all {wl.heads} heads, first {T} of {wl.seq_len} "
-                      f"tokens ({dt:.1f} s on {used} threads of {threads} host cores)"}
+    used = min(threads, rows * wl.heads)
+    return {"value": rows * T / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"fp64 oracle, batch rows 0..{rows - 1} x all {wl.heads} heads "
+                      f"({rows * wl.heads} memories), first {T} of {wl.seq_len} tokens "
+                      f"({dt:.1f} s on {used} threads of {threads} host cores)"}
 
 
 def main():
@@ -76,7 +78,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-sample-rows", type=int, default=4)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -157,7 +160,7 @@ def main():
                      "alg_flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes(wl)},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_sample_tokens)
+        result["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_sample_rows, args.cpu_sample_tokens)
     print(json.dumps(result), flush=True)
 
 
