@@ -136,8 +136,11 @@ def main():
     tokens = B * T
     flops = alg_flops_per_token_head(wl.widths, wl.chunk) * B * T * H
     achieved = flops / (kernel_ms * 1e-3) / 1e12
-    # the generic kernel runs its contractions as fp32 FMAs on the vector ALUs
-    bound, peak = "alu", PEAKS["valu_f32"]
+    path = tm.scan_path(t["q"], wl.chunk, wl.widths)
+    if path == "fused_mfma":  # bf16 MFMA contractions with fp32 accumulation
+        bound, peak, kernel, dtype = "mfma", PEAKS["mfma_bf16"], "scan_mfma_kernel", "bf16"
+    else:  # fp32 FMAs on the vector ALUs
+        bound, peak, kernel, dtype = "alu", PEAKS["valu_f32"], "scan_generic_kernel", "f32"
     result = {
         "metric": METRIC,
         "value": tokens / (ms_per_step * 1e-3),
@@ -149,14 +152,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "heads": H, "seq_len": T, "d_head": d,
                    "mlp_widths": list(wl.widths), "chunk": wl.chunk, "io": wl.io, "state": "fp32",
                    "parallelism": "one GPU; one workgroup per (batch row, head) memory"},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": None,
-                     "kernel": "scan_generic_kernel", "kernel_ms": kernel_ms,
+                     "kernel": kernel, "kernel_ms": kernel_ms,
                      "alg_flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes(wl)},
     }
     if not args.no_cpu_baseline:

@@ -99,6 +99,12 @@ const char* titans_last_error(void);
 /* P = sum_l n_l n_{l-1} floats per memory, or -1 if mlp is invalid. */
 int64_t titans_mem_param_count(const titans_mlp_desc* mlp);
 
+/* Which kernel titans_mem_scan runs for this problem: "fused_mfma" (bf16 MFMA, state
+ * resident on chip; the 64 -> 256 -> 64 memory with C = 64 and bf16 I/O) or
+ * "generic_fp32" (every other supported shape).  NULL if the arguments are invalid.
+ * The returned string is static. */
+const char* titans_mem_scan_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp);
+
 /* Device workspace bytes titans_mem_scan needs for this problem (0 if none;
  * SIZE_MAX if the arguments are invalid).  The workspace must be 256-byte aligned. */
 size_t titans_mem_scan_workspace_size(const titans_scan_desc* desc, const titans_mlp_desc* mlp);

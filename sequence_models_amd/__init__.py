@@ -15,7 +15,7 @@ import os
 
 import torch
 
-__all__ = ["scan", "retrieve", "scan_workspace_size", "param_count", "TitansError", "LIB_PATH",
+__all__ = ["scan", "retrieve", "scan_workspace_size", "scan_path", "param_count", "TitansError", "LIB_PATH",
            "lib", "ScanDesc", "MlpDesc", "MAX_LAYERS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtitans_mem.so")
@@ -48,6 +48,8 @@ lib.titans_mem_param_count.restype = ctypes.c_int64
 lib.titans_mem_param_count.argtypes = [ctypes.POINTER(MlpDesc)]
 lib.titans_mem_scan_workspace_size.restype = ctypes.c_size_t
 lib.titans_mem_scan_workspace_size.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)]
+lib.titans_mem_scan_path.restype = ctypes.c_char_p
+lib.titans_mem_scan_path.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)]
 lib.titans_mem_scan.restype = ctypes.c_int
 lib.titans_mem_scan.argtypes = ([ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)] + [_vp] * 12
                                 + [ctypes.c_size_t, _vp])
@@ -142,6 +144,15 @@ def scan_workspace_size(q, chunk, widths) -> int:
     if n == ctypes.c_size_t(-1).value:
         raise TitansError(1, "invalid scan shape or MLP widths")
     return int(n)
+
+
+def scan_path(q, chunk, widths) -> str:
+    """Name of the kernel that serves this shape: "fused_mfma" or "generic_fp32"."""
+    d = make_desc(q, chunk, q, None, None, None)
+    r = lib.titans_mem_scan_path(ctypes.byref(d), ctypes.byref(mlp_desc(widths)))
+    if r is None:
+        raise TitansError(1, "invalid scan shape or MLP widths")
+    return r.decode()
 
 
 def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, *, y=None, theta_T=None, s_T=None,

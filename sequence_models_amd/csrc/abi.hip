@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -198,10 +199,25 @@ static titans_status prepare_scan(const titans_scan_desc* desc, const titans_mlp
     return check_shape_support(a, true);
 }
 
+// The fused MFMA kernel serves its shape unless TITANS_MEM_FORCE_GENERIC=1 (a debugging
+// switch that routes every call through the generic kernel).
+static bool use_mfma(const titans::ScanArgs& a) {
+    const char* env = getenv("TITANS_MEM_FORCE_GENERIC");
+    if (env && env[0] == '1') return false;
+    return titans::scan_mfma_supported(a);
+}
+
+const char* titans_mem_scan_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp) {
+    titans::ScanArgs a{};
+    if (prepare_scan(desc, mlp, a) != TITANS_OK) return nullptr;
+    return use_mfma(a) ? "fused_mfma" : "generic_fp32";
+}
+
 size_t titans_mem_scan_workspace_size(const titans_scan_desc* desc, const titans_mlp_desc* mlp) {
     titans::ScanArgs a{};
     if (prepare_scan(desc, mlp, a) != TITANS_OK) return SIZE_MAX;
     if (a.B * a.H == 0 || a.T == 0) return 0;
+    if (use_mfma(a)) return 0;
     return titans::scan_generic_workspace_bytes(a);
 }
 
@@ -296,7 +312,9 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
     a.theta0 = theta0; a.s0 = s0;
     a.y = y; a.thetaT = theta_T; a.sT = s_T;
     a.ws = workspace;
-    hipError_t e = titans::launch_scan_generic(a, static_cast<hipStream_t>(stream));
+    hipError_t e = (a.T > 0 && use_mfma(a))
+                       ? titans::launch_scan_mfma(a, static_cast<hipStream_t>(stream))
+                       : titans::launch_scan_generic(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "scan launch");
     return TITANS_OK;
 }

@@ -37,6 +37,11 @@ struct ScanArgs {
 size_t scan_generic_workspace_bytes(const ScanArgs& a);
 hipError_t launch_scan_generic(const ScanArgs& a, hipStream_t stream);
 
+// Fused MFMA scan for the 64 -> 256 -> 64 memory, C = 64, bf16 I/O: one workgroup per
+// (b, h), state resident in registers, no workspace.
+bool scan_mfma_supported(const ScanArgs& a);
+hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t stream);
+
 // Generic retrieve: fp32 arithmetic, any supported shape.
 hipError_t launch_retrieve_generic(const ScanArgs& a, hipStream_t stream);
 

@@ -57,8 +57,14 @@ def _desc(B=2, T=64, H=4, d=64, C=64, io=1):
 
 def test_workspace_size_query():
     mlp = tm.mlp_desc((64, 256, 64))
-    size = tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc()), ctypes.byref(mlp))
+    # the fused kernel (64-256-64, C=64, bf16) keeps everything on chip: no workspace
+    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc()), ctypes.byref(mlp)) == 0
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc()), ctypes.byref(mlp)) == b"fused_mfma"
+    size = tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(C=32)), ctypes.byref(mlp))
     assert 0 < size < 1 << 30 and size % 4 == 0
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=32)), ctypes.byref(mlp)) == b"generic_fp32"
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(io=0)), ctypes.byref(mlp)) == b"generic_fp32"
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=0)), ctypes.byref(mlp)) is None
     assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(T=0)), ctypes.byref(mlp)) == 0
     bad = ctypes.c_size_t(-1).value
     assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(C=0)), ctypes.byref(mlp)) == bad
