@@ -120,7 +120,7 @@ def _fake_ptrs(B=2, T=64, H=4, d=64, P=32768, esz=2, base=1 << 40):
 def test_validation_of_overlap_alignment_and_workspace():
     mlp = tm.mlp_desc((64, 256, 64))
     B, T, H, d, P = 2, 64, 4, 64, 32768
-    desc = _desc(B, T, H, d)
+    desc = _desc(B, T, H, d, C=32)  # C=32 runs the generic kernel, which needs a workspace
     desc.state_stride[:] = (H * P, P)
     desc.state0_stride[:] = (0, P)
     ptrs, end = _fake_ptrs()
