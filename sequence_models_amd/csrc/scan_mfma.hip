@@ -109,6 +109,51 @@ __device__ __forceinline__ bf16x8 state_frag(f32x4 x0, f32x4 x1) {
     return acc_frag(opaque(x0), opaque(x1));
 }
 
+// Wave-wide inclusive scans with DPP (row shifts within 16 lanes, then row broadcasts).
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp(float identity, float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(x),
+                                                      kCtrl, kRowMask, 0xf, false));
+}
+__device__ __forceinline__ float wave_scan_mul(float x) {
+    x *= dpp<0x111, 0xf>(1.f, x);
+    x *= dpp<0x112, 0xf>(1.f, x);
+    x *= dpp<0x114, 0xf>(1.f, x);
+    x *= dpp<0x118, 0xf>(1.f, x);
+    x *= dpp<0x142, 0xa>(1.f, x);
+    x *= dpp<0x143, 0xc>(1.f, x);
+    return x;
+}
+__device__ __forceinline__ float wave_scan_add(float x) {
+    x += dpp<0x111, 0xf>(0.f, x);
+    x += dpp<0x112, 0xf>(0.f, x);
+    x += dpp<0x114, 0xf>(0.f, x);
+    x += dpp<0x118, 0xf>(0.f, x);
+    x += dpp<0x142, 0xa>(0.f, x);
+    x += dpp<0x143, 0xc>(0.f, x);
+    return x;
+}
+// Inclusive scan of affine maps x -> k x + c in lane order (earlier lanes applied first).
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ void affine_step(float& k, float& c) {
+    const float ek = dpp<kCtrl, kRowMask>(1.f, k), ec = dpp<kCtrl, kRowMask>(0.f, c);
+    c = k * ec + c;
+    k *= ek;
+}
+__device__ __forceinline__ void wave_scan_affine(float& k, float& c) {
+    affine_step<0x111, 0xf>(k, c);
+    affine_step<0x112, 0xf>(k, c);
+    affine_step<0x114, 0xf>(k, c);
+    affine_step<0x118, 0xf>(k, c);
+    affine_step<0x142, 0xa>(k, c);
+    affine_step<0x143, 0xc>(k, c);
+}
+// Value of lane l - 1 (lane 0 gets `first`).
+__device__ __forceinline__ float lane_prev(float x, float first) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(first), __float_as_int(x), 0x138,
+                                                      0xf, 0xf, false));
+}
+
 // Make this wave's LDS writes visible to its own later LDS reads.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -135,7 +180,10 @@ struct __attribute__((aligned(16))) Smem {
     __bf16 cm[kMat];           // c_{t,j}, t, j < 64 (rows t)
     float a[kC + 4], b[kC + 4];
     float cc[kC], w[kC], inva[kC];
-    float al[kC], et[kC], be[kC];
+    float et[kC], omb[kC];
+    float la2[kC + 4];         // sum_{m<t} log2(1 - alpha_m), t = 0..64
+    float la2i[kC];            // sum_{m<=t} log2(1 - alpha_m)
+    float lb2[kC];             // sum_{m<=t} log2(beta_m)
     float p;
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
@@ -231,10 +279,34 @@ __global__ void __launch_bounds__(kThreads, 1) scan_mfma_kernel(ScanArgs A) {
                 *reinterpret_cast<bf16x4*>(sm.e2l + xb + 4 * q4) = half4(kpre[q4 >> 1], q4 & 1);
                 *reinterpret_cast<bf16x4*>(sm.qa + xb + 4 * q4) = half4(qpre[q4 >> 1], q4 & 1);
             }
-            if (tid < kC) {
-                sm.al[tid] = gpre[0];
-                sm.et[tid] = gpre[1];
-                sm.be[tid] = gpre[2];
+        }
+        if (wv == 0) {
+            // Gate prefixes over the chunk's tokens (lane l = token l), all lane-parallel scans:
+            //   a_t = prod_{m<t} (1 - alpha_m),  p = prod_m beta_m,
+            //   b_{t+1} = (1 - alpha_t) b_t + eta_t prod_{m<=t} beta_m,
+            //   la2 / lb2: log2 prefix sums of (1 - alpha) and beta for the coefficient matrix.
+            const float keep = 1.f - gpre[0], et_l = gpre[1], be_l = gpre[2];
+            const float pa = wave_scan_mul(keep);   // prod_{m<=l} (1 - alpha_m)
+            const float pbl = wave_scan_mul(be_l);  // prod_{m<=l} beta_m
+            // a zero factor stays exactly zero through exp2 of a very negative exponent
+            const float lk = wave_scan_add(keep > 0.f ? __log2f(keep) : -1024.f);
+            const float lb = wave_scan_add(be_l > 0.f ? __log2f(be_l) : -1024.f);
+            float mk = keep, mc = et_l * pbl;  // affine maps x -> keep_t x + eta_t p_t, composed
+            wave_scan_affine(mk, mc);
+            const float a_l = lane_prev(pa, 1.f), b_l = lane_prev(mc, 0.f);
+            sm.a[l] = a_l;
+            sm.b[l] = b_l;
+            sm.inva[l] = 1.f / a_l;
+            sm.la2[l] = lane_prev(lk, 0.f);
+            sm.la2i[l] = lk;
+            sm.lb2[l] = lb;
+            sm.et[l] = et_l;
+            sm.omb[l] = 1.f - be_l;
+            if (l == 63) {
+                sm.a[kC] = pa;
+                sm.b[kC] = mc;
+                sm.la2[kC] = lk;
+                sm.p = pbl;
             }
         }
         bf16x8 vr[2];
@@ -251,32 +323,66 @@ __global__ void __launch_bounds__(kThreads, 1) scan_mfma_kernel(ScanArgs A) {
         __syncthreads();  // B1
 
         // ================= P1: coefficients (wave 0); key forward and O partials (all)
-        if (wv == 0) {
-            float Bj = 0.f, cj = 0.f, at = 1.f, bt = 0.f, pb = 1.f, my_a = 1.f;
-            const float omb = 1.f - sm.be[l];
-            __bf16* cmc = sm.cm + opq(l);
-            for (int t = 0; t < kC; ++t) {
-                const float al_t = sm.al[t], et_t = sm.et[t], be_t = sm.be[t];
-                cmc[t * kLd] = (__bf16)cj;  // c_{t,l}: weights before token t
-                if (t == l) my_a = at;
-                if (l == 0) {
-                    sm.a[t] = at;
-                    sm.b[t] = bt;
+        // Coefficient matrix c_{t,j} = sum_{j<=i<t} L1[t][i] L2[i][j] with
+        //   L1[t][i] = prod_{i<m<t} (1 - alpha_m),  L2[i][j] = eta_i (1 - beta_j) prod_{j<m<=i} beta_m,
+        // every entry an exp2 of a difference of log2 prefix sums (positive terms only),
+        // the sum one bf16 MFMA product.  Row C of L1 gives the chunk-end row c_C.
+        __bf16* l1m = sm.e2t;   // L1 [t][i]
+        __bf16* l2t = sm.e2c;   // L2^T [j][i]
+        __bf16* l1c = sm.e2w;   // row 0: L1[C][i] (rows 1..15 unused)
+        {
+            const int xb = opq(rc * kLd + cl0);
+            const float lat = sm.la2[rc], lbj = sm.lb2[rc], ombj = sm.omb[rc];
+            bf16x8 v1[2], v2[2];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 la = *reinterpret_cast<const f32x4*>(sm.la2i + cl0 + 4 * q4);
+                const f32x4 lbv = *reinterpret_cast<const f32x4*>(sm.lb2 + cl0 + 4 * q4);
+                const f32x4 etv = *reinterpret_cast<const f32x4*>(sm.et + cl0 + 4 * q4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = cl0 + 4 * q4 + e;
+                    // out-of-triangle exponents may be +inf; the select discards them
+                    const float x1 = __builtin_amdgcn_exp2f(lat - la[e]);
+                    const float x2 = etv[e] * __builtin_amdgcn_exp2f(lbv[e] - lbj) * ombj;
+                    v1[q4 >> 1][(q4 & 1) * 4 + e] = (__bf16)(i < rc ? x1 : 0.f);
+                    v2[q4 >> 1][(q4 & 1) * 4 + e] = (__bf16)(i >= rc ? x2 : 0.f);
                 }
-                pb *= be_t;
-                Bj = (l == t) ? 1.f : Bj * be_t;
-                const float keep = 1.f - al_t;
-                at *= keep;
-                bt = keep * bt + et_t * pb;
-                cj = keep * cj + et_t * omb * Bj;
             }
-            sm.cc[l] = cj;
-            sm.w[l] = omb * Bj;
-            sm.inva[l] = 1.f / my_a;
-            if (l == 0) {
-                sm.a[kC] = at;
-                sm.b[kC] = bt;
-                sm.p = pb;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                *reinterpret_cast<bf16x8*>(l1m + xb + 8 * q) = v1[q];
+                *reinterpret_cast<bf16x8*>(l2t + xb + 8 * q) = v2[q];
+            }
+            if (wv == 0) {
+                l1c[l] = (__bf16)__builtin_amdgcn_exp2f(sm.la2[kC] - sm.la2i[l]);
+                sm.w[l] = sm.omb[l] * __builtin_amdgcn_exp2f(sm.lb2[kC - 1] - sm.lb2[l]);
+            }
+        }
+        __syncthreads();  // B1b
+        {
+            // Cm^T[j][t] = sum_i L2^T[j][i] L1^T[i][t]: wave w owns column tile t in 16w..16w+15
+            const int rb = opq(j * kLd + 4 * g);
+            const __bf16* l2r = l2t + rb;
+            const __bf16* l1r = l1m + rb;
+            __bf16* cmw = sm.cm + rb + 16 * wv * kLd;
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) {
+                f32x4 x = zero4();
+                if (jt <= wv) {
+                    x = mfma(frag(l2r, fo(jt, 0)), frag(l1r, fo(wv, 0)), x);
+                    x = mfma(frag(l2r, fo(jt, 1)), frag(l1r, fo(wv, 1)), x);
+                }
+                *reinterpret_cast<bf16x4*>(cmw + 16 * jt) = bf4(x);
+            }
+            if (wv == 0) {
+                const __bf16* l1cr = l1c + rb;
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) {
+                    f32x4 x = mfma(frag(l2r, fo(jt, 0)), frag(l1cr, 0), zero4());
+                    x = mfma(frag(l2r, fo(jt, 1)), frag(l1cr, 32), x);
+                    if (j == 0) *reinterpret_cast<f32x4*>(sm.cc + 16 * jt + 4 * g) = x;
+                }
             }
         }
         // Z = K W1^T (rows c, cols h), one column tile of hidden units at a time
@@ -442,7 +548,6 @@ __global__ void __launch_bounds__(kThreads, 1) scan_mfma_kernel(ScanArgs A) {
                     f32x4 gg = mfma(frag(er, fo(ct, 0)), b0, zero4());
                     gg = mfma(frag(er, fo(ct, 1)), b1, gg);
                     D1[ct][ht] = bf4(gg * f4(Sp[ct][ht]));
-                    tile_fence();
                 }
             }
         }
@@ -473,7 +578,6 @@ __global__ void __launch_bounds__(kThreads, 1) scan_mfma_kernel(ScanArgs A) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) hq[r] = zq[r] * sigmoid(zq[r]);
                     Hq[ht][ct] = bf4(hq);
-                    tile_fence();
                 }
             }
         }
@@ -501,7 +605,6 @@ __global__ void __launch_bounds__(kThreads, 1) scan_mfma_kernel(ScanArgs A) {
                             pt = -(pt * cmv);
                         }
                         pm[ct][ctp] = bf4(pt);
-                        tile_fence();
                     }
                 }
             }
@@ -528,7 +631,6 @@ __global__ void __launch_bounds__(kThreads, 1) scan_mfma_kernel(ScanArgs A) {
                     yt = mfma(e0, cat(pm[ct][0], pm[ct][1]), yt);
                     if (ct >= 2) yt = mfma(e1, cat(pm[ct][2], pm[ct][3]), yt);
                     *reinterpret_cast<f32x4*>(slot + 16 * ct * kLd + 16 * dt) = yt;
-                    tile_fence();
                 }
             }
         }
