@@ -78,7 +78,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample-rows", type=int, default=4)
+    ap.add_argument("--cpu-sample-rows", type=int, default=8)
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
