@@ -52,6 +52,29 @@ def alg_bytes(wl):
     return th * (4 * wl.d * io + 12) + 4 * 4 * wl.params * wl.batch * wl.heads
 
 
+def kernel_source_digest(kernel):
+    """sha256 of the source file that defines the kernel (traffic is void once it changes)."""
+    import hashlib
+
+    src = {"scan_mfma_kernel": "scan_mfma.hip", "scan_generic_kernel": "scan_generic.hip"}[kernel]
+    with open(os.path.join(ROOT, "sequence_models_amd", "csrc", src), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the stored rocprofv3 FETCH_SIZE / WRITE_SIZE runs, each
+    scaled by what the counter read for a plain copy of known size; None if the kernel
+    source changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(f"{kernel}:{workload}")
+    if not rec or rec.get("source_sha256") != kernel_source_digest(kernel):
+        return None
+    return rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"]
+
+
 def cpu_baseline(inp, wl, sample_rows, sample_tokens):
     import oracle
 
@@ -81,6 +104,8 @@ def main():
     ap.add_argument("--cpu-sample-rows", type=int, default=8)
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device-to-device copy of this size first (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -111,6 +136,13 @@ def main():
     sT = torch.empty_like(thT)
     ws_bytes = tm.scan_workspace_size(t["q"], wl.chunk, wl.widths)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    if args.copy_calibration_mib:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         tm.scan(t["q"], t["k"], t["v"], t["alpha"], t["eta"], t["beta"], t["theta0"], t["s0"],
@@ -158,7 +190,7 @@ def main():
                    "mlp_widths": list(wl.widths), "chunk": wl.chunk, "io": wl.io, "state": "fp32",
                    "parallelism": "one GPU; one workgroup per (batch row, head) memory"},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None,
+                     "frac": achieved / peak, "traffic": measured_traffic(kernel, wl.name),
                      "kernel": kernel, "kernel_ms": kernel_ms,
                      "alg_flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes(wl)},
     }
