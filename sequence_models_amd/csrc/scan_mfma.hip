@@ -253,8 +253,8 @@ __global__ void __launch_bounds__(kThreads, 1) scan_mfma_kernel(ScanArgs A) {
         } else {
             kpre[0] = kpre[1] = qpre[0] = qpre[1] = bf16x8{};
         }
-        if (tid < kC) {
-            const int64_t tt = t0 + tid;
+        {
+            const int64_t tt = t0 + l;
             if (tt < A.T) {
                 const int64_t go = gbase + tt * A.gs[1];
                 gpre[0] = A.alpha[go];
@@ -280,33 +280,36 @@ __global__ void __launch_bounds__(kThreads, 1) scan_mfma_kernel(ScanArgs A) {
                 *reinterpret_cast<bf16x4*>(sm.qa + xb + 4 * q4) = half4(qpre[q4 >> 1], q4 & 1);
             }
         }
-        if (wv == 0) {
-            // Gate prefixes over the chunk's tokens (lane l = token l), all lane-parallel scans:
+        {
+            // Gate prefixes over the chunk's tokens (lane l = token l; every wave holds the
+            // gates, each wave runs its share of the lane-parallel DPP scans):
             //   a_t = prod_{m<t} (1 - alpha_m),  p = prod_m beta_m,
             //   b_{t+1} = (1 - alpha_t) b_t + eta_t prod_{m<=t} beta_m,
-            //   la2 / lb2: log2 prefix sums of (1 - alpha) and beta for the coefficient matrix.
+            //   la2 / lb2: log2 prefix sums of (1 - alpha) and beta for the coefficient matrix
+            //   (a zero factor stays exactly zero through exp2 of a very negative exponent).
             const float keep = 1.f - gpre[0], et_l = gpre[1], be_l = gpre[2];
-            const float pa = wave_scan_mul(keep);   // prod_{m<=l} (1 - alpha_m)
-            const float pbl = wave_scan_mul(be_l);  // prod_{m<=l} beta_m
-            // a zero factor stays exactly zero through exp2 of a very negative exponent
-            const float lk = wave_scan_add(keep > 0.f ? __log2f(keep) : -1024.f);
-            const float lb = wave_scan_add(be_l > 0.f ? __log2f(be_l) : -1024.f);
-            float mk = keep, mc = et_l * pbl;  // affine maps x -> keep_t x + eta_t p_t, composed
-            wave_scan_affine(mk, mc);
-            const float a_l = lane_prev(pa, 1.f), b_l = lane_prev(mc, 0.f);
-            sm.a[l] = a_l;
-            sm.b[l] = b_l;
-            sm.inva[l] = 1.f / a_l;
-            sm.la2[l] = lane_prev(lk, 0.f);
-            sm.la2i[l] = lk;
-            sm.lb2[l] = lb;
-            sm.et[l] = et_l;
-            sm.omb[l] = 1.f - be_l;
-            if (l == 63) {
-                sm.a[kC] = pa;
-                sm.b[kC] = mc;
-                sm.la2[kC] = lk;
-                sm.p = pbl;
+            if (wv == 0) {
+                const float pa = wave_scan_mul(keep);
+                const float a_l = lane_prev(pa, 1.f);
+                sm.a[l] = a_l;
+                sm.inva[l] = 1.f / a_l;
+                if (l == 63) sm.a[kC] = pa;
+            } else if (wv == 1) {
+                const float pbl = wave_scan_mul(be_l);
+                sm.lb2[l] = wave_scan_add(be_l > 0.f ? __log2f(be_l) : -1024.f);
+                if (l == 63) sm.p = pbl;
+            } else if (wv == 2) {
+                const float lk = wave_scan_add(keep > 0.f ? __log2f(keep) : -1024.f);
+                sm.la2[l] = lane_prev(lk, 0.f);
+                sm.la2i[l] = lk;
+                if (l == 63) sm.la2[kC] = lk;
+            } else {
+                float mk = keep, mc = et_l * wave_scan_mul(be_l);
+                wave_scan_affine(mk, mc);  // affine maps x -> keep_t x + eta_t p_t, composed
+                sm.b[l] = lane_prev(mc, 0.f);
+                sm.et[l] = et_l;
+                sm.omb[l] = 1.f - be_l;
+                if (l == 63) sm.b[kC] = mc;
             }
         }
         bf16x8 vr[2];
