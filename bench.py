@@ -56,7 +56,8 @@ def kernel_source_digest(kernel):
     """sha256 of the source file that defines the kernel (traffic is void once it changes)."""
     import hashlib
 
-    src = {"scan_mfma_kernel": "scan_mfma.hip", "scan_generic_kernel": "scan_generic.hip"}[kernel]
+    src = {"scan_pair_kernel": "scan_pair.hip", "scan_mfma_kernel": "scan_mfma.hip",
+           "scan_generic_kernel": "scan_generic.hip"}[kernel]
     with open(os.path.join(ROOT, "sequence_models_amd", "csrc", src), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
@@ -169,10 +170,13 @@ def main():
     flops = alg_flops_per_token_head(wl.widths, wl.chunk) * B * T * H
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     path = tm.scan_path(t["q"], wl.chunk, wl.widths)
-    if path == "fused_mfma":  # bf16 MFMA contractions with fp32 accumulation
-        bound, peak, kernel, dtype = "mfma", PEAKS["mfma_bf16"], "scan_mfma_kernel", "bf16"
+    if path in ("fused_pair", "fused_mfma"):  # bf16 MFMA contractions with fp32 accumulation
+        kernel = "scan_pair_kernel" if path == "fused_pair" else "scan_mfma_kernel"
+        bound, peak, dtype = "mfma", PEAKS["mfma_bf16"], "bf16"
     else:  # fp32 FMAs on the vector ALUs
         bound, peak, kernel, dtype = "alu", PEAKS["valu_f32"], "scan_generic_kernel", "f32"
+    parallelism = {"fused_pair": "one GPU; two workgroups (one XCD) per (batch row, head) memory"}.get(
+        path, "one GPU; one workgroup per (batch row, head) memory")
     result = {
         "metric": METRIC,
         "value": tokens / (ms_per_step * 1e-3),
@@ -188,7 +192,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "heads": H, "seq_len": T, "d_head": d,
                    "mlp_widths": list(wl.widths), "chunk": wl.chunk, "io": wl.io, "state": "fp32",
-                   "parallelism": "one GPU; one workgroup per (batch row, head) memory"},
+                   "parallelism": parallelism, "kernel_path": path},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": measured_traffic(kernel, wl.name),
                      "kernel": kernel, "kernel_ms": kernel_ms,

@@ -18,13 +18,14 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-# Per-source extra flags.  The fused scan keeps 256 fp32 state registers per lane
-# live across the chunk loop; MFMA results in VGPRs (AGPRs then serve as spill
+# Per-source extra flags.  The fused scans keep 256 (single workgroup) or 128 (pair)
+# fp32 state registers per lane live across the chunk loop; MFMA results in VGPRs (AGPRs then serve as spill
 # space) keep it out of scratch memory.
 SOURCES = {
     "abi.hip": [],
     "scan_generic.hip": [],
     "scan_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "scan_pair.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -199,26 +199,56 @@ static titans_status prepare_scan(const titans_scan_desc* desc, const titans_mlp
     return check_shape_support(a, true);
 }
 
-// The fused MFMA kernel serves its shape unless TITANS_MEM_FORCE_GENERIC=1 (a debugging
-// switch that routes every call through the generic kernel).
-static bool use_mfma(const titans::ScanArgs& a) {
+// Compute units of the current device; 256 (an MI355X) when no device is visible, so
+// host-only queries answer as they would on that GPU.
+static int64_t device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    return n;
+}
+
+enum class Path { Generic, Fused, Pair };
+
+// Which kernel serves a (validated) problem.  The fused shape runs on pairs of
+// workgroups while the pairs fit the device at one workgroup per compute unit, else one
+// workgroup per memory.  Debugging switches: TITANS_MEM_FORCE_GENERIC=1 routes every call
+// through the generic kernel, TITANS_MEM_FUSED_SINGLE=1 keeps the fused shape on one
+// workgroup per memory.
+static Path choose_path(const titans::ScanArgs& a) {
     const char* env = getenv("TITANS_MEM_FORCE_GENERIC");
-    if (env && env[0] == '1') return false;
-    return titans::scan_mfma_supported(a);
+    if (env && env[0] == '1') return Path::Generic;
+    if (!titans::scan_mfma_supported(a)) return Path::Generic;
+    env = getenv("TITANS_MEM_FUSED_SINGLE");
+    if (env && env[0] == '1') return Path::Fused;
+    if (titans::scan_pair_supported(a) && titans::scan_pair_workgroups(a) <= device_cus())
+        return Path::Pair;
+    return Path::Fused;
 }
 
 const char* titans_mem_scan_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp) {
     titans::ScanArgs a{};
     if (prepare_scan(desc, mlp, a) != TITANS_OK) return nullptr;
-    return use_mfma(a) ? "fused_mfma" : "generic_fp32";
+    switch (choose_path(a)) {
+        case Path::Pair: return "fused_pair";
+        case Path::Fused: return "fused_mfma";
+        default: return "generic_fp32";
+    }
 }
 
 size_t titans_mem_scan_workspace_size(const titans_scan_desc* desc, const titans_mlp_desc* mlp) {
     titans::ScanArgs a{};
     if (prepare_scan(desc, mlp, a) != TITANS_OK) return SIZE_MAX;
     if (a.B * a.H == 0 || a.T == 0) return 0;
-    if (use_mfma(a)) return 0;
-    return titans::scan_generic_workspace_bytes(a);
+    switch (choose_path(a)) {
+        case Path::Pair: return titans::scan_pair_workspace_bytes(a);
+        case Path::Fused: return 0;
+        default: return titans::scan_generic_workspace_bytes(a);
+    }
 }
 
 titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
@@ -312,9 +342,11 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
     a.theta0 = theta0; a.s0 = s0;
     a.y = y; a.thetaT = theta_T; a.sT = s_T;
     a.ws = workspace;
-    hipError_t e = (a.T > 0 && use_mfma(a))
-                       ? titans::launch_scan_mfma(a, static_cast<hipStream_t>(stream))
-                       : titans::launch_scan_generic(a, static_cast<hipStream_t>(stream));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const Path path = a.T > 0 ? choose_path(a) : Path::Generic;
+    hipError_t e = path == Path::Pair    ? titans::launch_scan_pair(a, hs)
+                   : path == Path::Fused ? titans::launch_scan_mfma(a, hs)
+                                         : titans::launch_scan_generic(a, hs);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
     return TITANS_OK;
 }

@@ -1,0 +1,765 @@
+// Fused chunked Titans memory scan with each memory split over a PAIR of workgroups,
+// for the 64 -> 256 -> 64 SiLU memory with chunks of 64 tokens and bf16 q/k/v/y
+// (fp32 gates and state).
+//
+// Why a pair: one (b, h) memory per workgroup leaves half of the GPU's compute units
+// idle when there are fewer memories than compute units, and its 256 KB of fp32 state
+// fills the register file of one CU.  Here side s (0, 1) of a pair owns hidden units
+// 128 s .. 128 s + 127; wave w of a side owns 32 of them (rows of W1 / S1, columns of
+// W2 / S2), held in registers as MFMA accumulators for the whole sequence.
+//
+// Per chunk the algebra is that of the single-workgroup kernel (the unrolled momentum /
+// forget-gated write rule of the Titans pages with gradients frozen at the chunk start,
+// each gradient an outer product delta h^T).  Everything that depends only on the chunk's
+// tokens and gates (coefficients, scaled Q / K copies, Cm o Q K^T, E2 layouts) is computed
+// by both sides; everything that is a sum over hidden units is computed per side:
+//   O = Hk W2^T      both sides need the full O for E2 = 2 (O - V): each side posts its
+//                    partial (64 x 64 fp32) to the partner and adds the partner's;
+//   Y                each side writes y for its half of the chunk's tokens (side s: rows
+//                    32 s .. 32 s + 31) and posts its partial of the other half to the
+//                    partner, which adds it one chunk later (off the critical path).
+// O = O_0 + O_1 and y = Y_0 + Y_1 are formed in that order on both sides (fp32 addition
+// is commutative), so both sides hold bitwise the same E2 and the result is
+// reproducible.
+//
+// Exchange protocol.  The two workgroups of a pair are blockIdx i and i ^ 8, which the
+// dispatcher places on the same XCD (its L2 is then the meeting point).  Every word of
+// the exchange area is written and read only with agent-scope relaxed atomics (per
+// instruction coherent loads / stores, no L2 writeback or invalidate): thread t of wave
+// w writes its own words, the wave waits for its stores to complete (s_waitcnt
+// vmcnt(0)), then lane 0 stores the wave's flag = exchange number e.  The partner's
+// wave w polls that flag (bounded), then thread t reads exactly the words the partner's
+// thread t wrote.  O and Y areas are double-buffered by the parity of e; a wave posts
+// e + 1 only after its reads of exchange e have returned, which is what lets the partner
+// reuse a buffer two exchanges later.  The launch is cooperative, so both workgroups of
+// a pair are resident together.  A wait that exceeds its bound (never expected) stops
+// all further waits of that wave and the memory's theta_T and s_T come out as NaN.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mfma_util.h"
+#include "titans_internal.h"
+
+namespace titans {
+namespace {
+
+using namespace fused;
+
+constexpr int kD = 64;                   // key / value / query width
+constexpr int kHid = 256;                // hidden width of the memory MLP
+constexpr int kC = 64;                   // chunk length
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kHidSide = kHid / 2;       // hidden units per workgroup
+constexpr int kHidW = kHidSide / kWaves; // hidden units per wave (32)
+constexpr int kHt = kHidW / 16;          // 16-wide hidden tiles per wave (2)
+constexpr int kMat = kC * kLd;           // elements of one padded 64 x 64 matrix
+constexpr int kMaxSpin = 1 << 21;        // flag polls before a wait gives up (about 2 s)
+
+// Exchange area of one pair (byte offsets): flags [side][wave] 128 bytes apart, then
+// O words [slot 2][side 2][i 8][thread], then Y words [slot 2][side 2][i 4][thread];
+// a word is two fp32 values.
+constexpr int64_t kFlagBytes = 2 * kWaves * 128;
+constexpr int64_t kOWords = 2 * 2 * 8 * kThreads;
+constexpr int64_t kYWords = 2 * 2 * 4 * kThreads;
+constexpr int64_t kPairBytes = kFlagBytes + 8 * (kOWords + kYWords);
+static_assert(kPairBytes % 256 == 0, "pair areas stay 256-byte aligned");
+
+__device__ __forceinline__ uint64_t pack2(float a, float b) {
+    return (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+}
+__device__ __forceinline__ float lo32(uint64_t u) { return __uint_as_float((uint32_t)u); }
+__device__ __forceinline__ float hi32(uint64_t u) { return __uint_as_float((uint32_t)(u >> 32)); }
+__device__ __forceinline__ void xstore(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t xload(uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// This wave's exchange stores are complete, then lane 0 publishes exchange number e.
+__device__ __forceinline__ void post_flag(int* flag, int e, int lane) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (lane == 0) __hip_atomic_store(flag, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wave-uniform bounded wait for the partner wave's flag to reach e.  `bad` latches a
+// timeout; a wave that has timed out does not wait again.
+__device__ __forceinline__ void wait_flag(int* flag, int e, bool& bad) {
+    if (bad) return;
+    for (int s = 0; s < kMaxSpin; ++s) {
+        const int v = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (v >= e) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // no load moves above
+            return;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    bad = true;
+}
+
+struct __attribute__((aligned(16))) Smem {
+    // Regions are reused within a chunk; the comment gives each region's lives in order.
+    float r[2][kMat];          // O partials (pairwise reduction) -> the waves' bf16 W2 slices
+                               //   -> Y partial slots 0, 1   ([c][dd] fp32)
+    __bf16 qa[kMat];           // raw Q -> diag(a) Q [c][d]     } Y partial slot 2
+    __bf16 qb[kMat];           // -diag(b) Q [c][d]             }
+    __bf16 mq[kMat];           // -(Cm o Q K^T) [c][c']         } Y partial slot 3
+    __bf16 e2l[kMat];          // E2 [c][dd]                    }
+    __bf16 kk[kMat];           // K [c][d]
+    __bf16 e2t[kMat];          // L1 (coefficients) -> E2^T [dd][c]
+    __bf16 e2c[kMat];          // L2^T (coefficients) -> -(diag(c_C) E2)^T [dd][c]
+    __bf16 e2w[kMat];          // L1 row C -> (diag(w) E2)^T [dd][c]
+    __bf16 kc[kMat];           // -(diag(c_C) K)^T [d][c]
+    __bf16 kw[kMat];           // (diag(w) K)^T    [d][c]
+    __bf16 hk[kWaves / 2][kMat];  // Hk slices [c][h]: wave w at hk[w / 2], columns 32 (w % 2)..
+    __bf16 cm[kMat];           // c_{t,j}, t, j < 64 (rows t)
+    float a[kC + 4], b[kC + 4];
+    float cc[kC], w[kC], inva[kC];
+    float et[kC], omb[kC];
+    float la2[kC + 4];         // sum_{m<t} log2(1 - alpha_m), t = 0..64
+    float la2i[kC];            // sum_{m<=t} log2(1 - alpha_m)
+    float lb2[kC];             // sum_{m<=t} log2(beta_m)
+    float p;
+    int fail;
+};
+static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
+
+__device__ __forceinline__ float* yslot(Smem& sm, int w) {
+    switch (w) {
+        case 0: return sm.r[0];
+        case 1: return sm.r[1];
+        case 2: return reinterpret_cast<float*>(sm.qa);
+        default: return reinterpret_cast<float*>(sm.mq);
+    }
+}
+
+__global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
+    __shared__ Smem sm;
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6, l = tid & 63, g = l >> 4, j = l & 15;
+    // workgroups i and i ^ 8 form pair 8 (i / 16) + i % 8
+    const int bid = blockIdx.x;
+    const int side = (bid >> 3) & 1;
+    const int64_t seq = 8 * (int64_t)(bid >> 4) + (bid & 7);
+    if (seq >= A.B * A.H) return;  // both workgroups of a padding pair leave together
+    const int64_t bi = seq / A.H, hi = seq % A.H;
+
+    char* pbase = static_cast<char*>(A.ws) + seq * kPairBytes;
+    int* myflag = reinterpret_cast<int*>(pbase) + (side * kWaves + wv) * 32;
+    int* otflag = reinterpret_cast<int*>(pbase) + ((1 - side) * kWaves + wv) * 32;
+    uint64_t* xo = reinterpret_cast<uint64_t*>(pbase + kFlagBytes);
+    uint64_t* xy = xo + kOWords;
+    auto oslot = [&](int e, int s) { return xo + ((e & 1) * 2 + s) * 8 * kThreads + tid; };
+    auto yxslot = [&](int e, int s) { return xy + ((e & 1) * 2 + s) * 4 * kThreads + tid; };
+    bool bad = false;
+
+    const float* th0 = A.theta0 + bi * A.s0s[0] + hi * A.s0s[1];
+    const float* mo0 = A.s0 + bi * A.s0s[0] + hi * A.s0s[1];
+    float* thT = A.thetaT + bi * A.ss[0] + hi * A.ss[1];
+    float* moT = A.sT + bi * A.ss[0] + hi * A.ss[1];
+    constexpr int kOff2 = kHid * kD;  // W2 follows W1 (256 x 64) in a memory
+    const int hb = kHidSide * side + kHidW * wv;  // this wave's first hidden unit
+
+    // ---- state: W1T[dt][ht] = W1[h][d] (rows d = 16dt+4g+r, cols h = hb+16ht+j),
+    //             W2T[ht][dt] = W2[dd][h] (rows h = hb+16ht+4g+r, cols dd = 16dt+j)
+    f32x4 W1T[4][kHt], S1T[4][kHt], W2T[kHt][4], S2T[kHt][4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int ht = 0; ht < kHt; ++ht) {
+            const int h = hb + 16 * ht + j;
+            const int d = 16 * dt + 4 * g;
+            W1T[dt][ht] = *reinterpret_cast<const f32x4*>(th0 + h * kD + d);
+            S1T[dt][ht] = *reinterpret_cast<const f32x4*>(mo0 + h * kD + d);
+            const int h2 = hb + 16 * ht + 4 * g;
+            const int dd = 16 * dt + j;
+            W2T[ht][dt] = *reinterpret_cast<const f32x4*>(th0 + kOff2 + dd * kHid + h2);
+            S2T[ht][dt] = *reinterpret_cast<const f32x4*>(mo0 + kOff2 + dd * kHid + h2);
+        }
+    if (tid == 0) sm.fail = 0;
+
+    const __bf16* qg = static_cast<const __bf16*>(A.q);
+    const __bf16* kg = static_cast<const __bf16*>(A.k);
+    const __bf16* vg = static_cast<const __bf16*>(A.v);
+    __bf16* yg = static_cast<__bf16*>(A.y);
+    const int64_t qbase = bi * A.qs[0] + hi * A.qs[2];
+    const int64_t ybase = bi * A.ys[0] + hi * A.ys[2];
+    const int64_t gbase = bi * A.gs[0] + hi * A.gs[2];
+    // this thread's slice of a chunk's 64 x 64 token tiles: row rc, columns cl0 .. cl0+15
+    const int rc = tid >> 2, cl0 = 16 * (tid & 3);
+    // this thread's y elements: row yr of this side's half (own) and of the partner's
+    // half, columns yd0 .. yd0+7
+    const int yr = tid >> 3, yd0 = 8 * (tid & 7);
+    const int yrow_own = 32 * side + yr, yrow_oth = 32 * (1 - side) + yr;
+    float yown[8];
+
+    bf16x8 kpre[2], qpre[2];
+    float gpre[3] = {0.f, 0.f, 1.f};
+    auto prefetch = [&](int64_t t0) {
+        const int64_t t = t0 + rc;
+        if (t < A.T) {
+            const int64_t o = qbase + t * A.qs[1] + cl0;
+            kpre[0] = *reinterpret_cast<const bf16x8*>(kg + o);
+            kpre[1] = *reinterpret_cast<const bf16x8*>(kg + o + 8);
+            qpre[0] = *reinterpret_cast<const bf16x8*>(qg + o);
+            qpre[1] = *reinterpret_cast<const bf16x8*>(qg + o + 8);
+        } else {
+            kpre[0] = kpre[1] = qpre[0] = qpre[1] = bf16x8{};
+        }
+        const int64_t tt = t0 + l;
+        if (tt < A.T) {
+            const int64_t go = gbase + tt * A.gs[1];
+            gpre[0] = A.alpha[go];
+            gpre[1] = A.eta[go];
+            gpre[2] = A.beta[go];
+        } else {  // padding tokens: no decay, no write, momentum kept
+            gpre[0] = 0.f;
+            gpre[1] = 0.f;
+            gpre[2] = 1.f;
+        }
+    };
+    // y for this side's rows of the chunk starting at token t0, own partial + partner's
+    auto write_y = [&](int64_t t0, const uint64_t* px) {
+        const int64_t t = t0 + yrow_own;
+        bf16x8 out;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = (__bf16)(yown[2 * i] + lo32(px[i]));
+            out[2 * i + 1] = (__bf16)(yown[2 * i + 1] + hi32(px[i]));
+        }
+        if (t < A.T) *reinterpret_cast<bf16x8*>(yg + ybase + t * A.ys[1] + yd0) = out;
+    };
+    prefetch(0);
+
+    int e = 0;  // exchange number of the current chunk (1, 2, ...)
+    for (int64_t c0 = 0; c0 < A.T; c0 += kC) {
+        ++e;
+        // ================= P0: commit the prefetched chunk; load V
+        {
+            const int xb = opq(rc * kLd + cl0);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                *reinterpret_cast<bf16x4*>(sm.kk + xb + 4 * q4) = half4(kpre[q4 >> 1], q4 & 1);
+                *reinterpret_cast<bf16x4*>(sm.qa + xb + 4 * q4) = half4(qpre[q4 >> 1], q4 & 1);
+            }
+        }
+        {
+            // Gate prefixes over the chunk's tokens (lane l = token l; each wave runs its
+            // share of the lane-parallel DPP scans):
+            //   a_t = prod_{m<t} (1 - alpha_m),  p = prod_m beta_m,
+            //   b_{t+1} = (1 - alpha_t) b_t + eta_t prod_{m<=t} beta_m,
+            //   la2 / lb2: log2 prefix sums of (1 - alpha) and beta for the coefficient matrix
+            //   (a zero factor stays exactly zero through exp2 of a very negative exponent).
+            const float keep = 1.f - gpre[0], et_l = gpre[1], be_l = gpre[2];
+            if (wv == 0) {
+                const float pa = wave_scan_mul(keep);
+                const float a_l = lane_prev(pa, 1.f);
+                sm.a[l] = a_l;
+                sm.inva[l] = 1.f / a_l;
+                if (l == 63) sm.a[kC] = pa;
+            } else if (wv == 1) {
+                const float pbl = wave_scan_mul(be_l);
+                sm.lb2[l] = wave_scan_add(be_l > 0.f ? __log2f(be_l) : -1024.f);
+                if (l == 63) sm.p = pbl;
+            } else if (wv == 2) {
+                const float lk = wave_scan_add(keep > 0.f ? __log2f(keep) : -1024.f);
+                sm.la2[l] = lane_prev(lk, 0.f);
+                sm.la2i[l] = lk;
+                if (l == 63) sm.la2[kC] = lk;
+            } else {
+                float mk = keep, mc = et_l * wave_scan_mul(be_l);
+                wave_scan_affine(mk, mc);  // affine maps x -> keep_t x + eta_t p_t, composed
+                sm.b[l] = lane_prev(mc, 0.f);
+                sm.et[l] = et_l;
+                sm.omb[l] = 1.f - be_l;
+                if (l == 63) sm.b[kC] = mc;
+            }
+        }
+        bf16x8 vr[2];
+        {
+            const int64_t t = c0 + rc;
+            if (t < A.T) {
+                const int64_t o = qbase + t * A.qs[1] + cl0;
+                vr[0] = *reinterpret_cast<const bf16x8*>(vg + o);
+                vr[1] = *reinterpret_cast<const bf16x8*>(vg + o + 8);
+            } else {
+                vr[0] = vr[1] = bf16x8{};
+            }
+        }
+        __syncthreads();  // B1
+
+        // ================= P1: coefficients; key forward and O partials
+        // c_{t,j} = sum_{j<=i<t} L1[t][i] L2[i][j] with
+        //   L1[t][i] = prod_{i<m<t} (1 - alpha_m),  L2[i][j] = eta_i (1 - beta_j) prod_{j<m<=i} beta_m,
+        // every entry an exp2 of a difference of log2 prefix sums, the sum one bf16 MFMA
+        // product; row C of L1 gives the chunk-end row c_C.
+        __bf16* l1m = sm.e2t;   // L1 [t][i]
+        __bf16* l2t = sm.e2c;   // L2^T [j][i]
+        __bf16* l1c = sm.e2w;   // row 0: L1[C][i] (rows 1..15 unused)
+        {
+            const int xb = opq(rc * kLd + cl0);
+            const float lat = sm.la2[rc], lbj = sm.lb2[rc], ombj = sm.omb[rc];
+            bf16x8 v1[2], v2[2];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 la = *reinterpret_cast<const f32x4*>(sm.la2i + cl0 + 4 * q4);
+                const f32x4 lbv = *reinterpret_cast<const f32x4*>(sm.lb2 + cl0 + 4 * q4);
+                const f32x4 etv = *reinterpret_cast<const f32x4*>(sm.et + cl0 + 4 * q4);
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int i = cl0 + 4 * q4 + e4;
+                    // out-of-triangle exponents may be +inf; the select discards them
+                    const float x1 = __builtin_amdgcn_exp2f(lat - la[e4]);
+                    const float x2 = etv[e4] * __builtin_amdgcn_exp2f(lbv[e4] - lbj) * ombj;
+                    v1[q4 >> 1][(q4 & 1) * 4 + e4] = (__bf16)(i < rc ? x1 : 0.f);
+                    v2[q4 >> 1][(q4 & 1) * 4 + e4] = (__bf16)(i >= rc ? x2 : 0.f);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                *reinterpret_cast<bf16x8*>(l1m + xb + 8 * q) = v1[q];
+                *reinterpret_cast<bf16x8*>(l2t + xb + 8 * q) = v2[q];
+            }
+            if (wv == 0) {
+                l1c[l] = (__bf16)__builtin_amdgcn_exp2f(sm.la2[kC] - sm.la2i[l]);
+                sm.w[l] = sm.omb[l] * __builtin_amdgcn_exp2f(sm.lb2[kC - 1] - sm.lb2[l]);
+            }
+        }
+        __syncthreads();  // B1b
+        {
+            // Cm^T[j][t] = sum_i L2^T[j][i] L1^T[i][t]: wave w owns column tile t in 16w..16w+15
+            const int rb = opq(j * kLd + 4 * g);
+            const __bf16* l2r = l2t + rb;
+            const __bf16* l1r = l1m + rb;
+            __bf16* cmw = sm.cm + rb + 16 * wv * kLd;
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) {
+                f32x4 x = zero4();
+                if (jt <= wv) {
+                    x = mfma(frag(l2r, fo(jt, 0)), frag(l1r, fo(wv, 0)), x);
+                    x = mfma(frag(l2r, fo(jt, 1)), frag(l1r, fo(wv, 1)), x);
+                }
+                *reinterpret_cast<bf16x4*>(cmw + 16 * jt) = bf4(x);
+            }
+            if (wv == 0) {
+                const __bf16* l1cr = l1c + rb;
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) {
+                    f32x4 x = mfma(frag(l2r, fo(jt, 0)), frag(l1cr, 0), zero4());
+                    x = mfma(frag(l2r, fo(jt, 1)), frag(l1cr, 32), x);
+                    if (j == 0) *reinterpret_cast<f32x4*>(sm.cc + 16 * jt + 4 * g) = x;
+                }
+            }
+        }
+        // Z = K W1^T (rows c, cols h) for this wave's 32 hidden units
+        __bf16* hkw0 = sm.hk[wv >> 1] + 32 * (wv & 1);  // this wave's Hk slice [c][h]
+        bf16x4 Hk[4][kHt], Sp[4][kHt];
+        {
+            const int rb = opq(j * kLd + 4 * g), wb = opq(4 * g * kLd + j);
+            const __bf16* ks = sm.kk + rb;
+            __bf16* hkw = hkw0 + wb;
+#pragma unroll
+            for (int ht = 0; ht < kHt; ++ht) {
+                const bf16x8 bw0 = state_frag(W1T[0][ht], W1T[1][ht]);
+                const bf16x8 bw1 = state_frag(W1T[2][ht], W1T[3][ht]);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    f32x4 z = mfma(frag(ks, fo(ct, 0)), bw0, zero4());
+                    z = mfma(frag(ks, fo(ct, 1)), bw1, z);
+                    f32x4 hk, sp;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float sg = sigmoid(z[r]);
+                        const float hh = z[r] * sg;
+                        hk[r] = hh;
+                        sp[r] = sg + hh * (1.f - sg);  // SiLU'(z) = s (1 + z (1 - s))
+                    }
+                    Hk[ct][ht] = bf4(hk);
+                    Sp[ct][ht] = bf4(sp);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) hkw[(16 * ct + r) * kLd + 16 * ht] = Hk[ct][ht][r];
+                }
+            }
+        }
+        wave_lds_sync();
+        // O^T partial over this wave's hidden units: O^T[dd][c] = sum_h W2[dd][h] Hk[c][h]
+        f32x4 Ot[4][4];
+        {
+            const int rb = opq(j * kLd + 4 * g);
+            const __bf16* hkr = hkw0 + rb;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const bf16x8 a0 = state_frag(W2T[0][dt], W2T[1][dt]);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) Ot[dt][ct] = mfma(a0, frag(hkr, fo(ct, 0)), zero4());
+            }
+            // deterministic pairwise reduction, stage 1: waves 2, 3 store their partials
+            if (wv >= 2) {
+                float* slot = sm.r[wv - 2] + rb;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+                        *reinterpret_cast<f32x4*>(slot + 16 * ct * kLd + 16 * dt) = Ot[dt][ct];
+            }
+        }
+        __syncthreads();  // B2: coefficients, O stage 1
+
+        // ================= P2: stage 2 of O; scaled Q and K copies
+        if (wv < 2) {
+            float* slot = sm.r[wv] + opq(j * kLd + 4 * g);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    f32x4* p = reinterpret_cast<f32x4*>(slot + 16 * ct * kLd + 16 * dt);
+                    *p = Ot[dt][ct] + *p;
+                }
+        }
+        {
+            const float ar = sm.a[rc], br = -sm.b[rc];
+            const float ccr = -sm.cc[rc], wr = sm.w[rc];
+            const int xb = opq(rc * kLd + cl0), xt = opq(cl0 * kLd + rc);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 qv = f4(*reinterpret_cast<const bf16x4*>(sm.qa + xb + 4 * q4));
+                *reinterpret_cast<bf16x4*>(sm.qa + xb + 4 * q4) = bf4(qv * ar);
+                *reinterpret_cast<bf16x4*>(sm.qb + xb + 4 * q4) = bf4(qv * br);
+                const f32x4 kv = f4(*reinterpret_cast<const bf16x4*>(sm.kk + xb + 4 * q4));
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    sm.kc[xt + (4 * q4 + e4) * kLd] = (__bf16)(kv[e4] * ccr);
+                    sm.kw[xt + (4 * q4 + e4) * kLd] = (__bf16)(kv[e4] * wr);
+                }
+            }
+        }
+        __syncthreads();  // B3: this side's O partial, diag(a) Q, -diag(b) Q
+
+        // ================= P2x: exchange O; Mq and the state terms of Zq meanwhile
+        float oo[16];
+        {
+            const int xb = opq(rc * kLd + cl0);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 o = *reinterpret_cast<const f32x4*>(sm.r[0] + xb + 4 * q4) +
+                                *reinterpret_cast<const f32x4*>(sm.r[1] + xb + 4 * q4);
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) oo[4 * q4 + e4] = o[e4];
+            }
+            uint64_t* dst = oslot(e, side);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xstore(dst + i * kThreads, pack2(oo[2 * i], oo[2 * i + 1]));
+            post_flag(myflag, e, l);
+        }
+        {
+            // Mq[c][c'] = -(c_{c,c'} / a_c) (Qa K^T)[c][c'] for column tile c = 16 wv + j
+            const int rb = opq(j * kLd + 4 * g);
+            const __bf16* ks = sm.kk + rb;
+            const __bf16* qr = sm.qa + rb + 16 * wv * kLd;
+            const __bf16* cmr = sm.cm + rb + 16 * wv * kLd;
+            __bf16* mqw = sm.mq + rb + 16 * wv * kLd;
+            const float ia = sm.inva[16 * wv + j];
+#pragma unroll
+            for (int ctp = 0; ctp < 4; ++ctp) {
+                f32x4 x = zero4();
+                if (ctp <= wv) {
+                    x = mfma(frag(ks, fo(ctp, 0)), frag(qr, 0), x);
+                    x = mfma(frag(ks, fo(ctp, 1)), frag(qr, 32), x);
+                    const f32x4 cmv = f4(*reinterpret_cast<const bf16x4*>(cmr + 16 * ctp));
+                    x = x * cmv * (-ia);
+                }
+                *reinterpret_cast<bf16x4*>(mqw + 16 * ctp) = bf4(x);
+            }
+        }
+        // Zq^T state terms (rows h, cols c): W1 (diag(a) Q)^T + S1 (-diag(b) Q)^T
+        f32x4 zqp[kHt][4];
+        {
+            const int rb = opq(j * kLd + 4 * g);
+            const __bf16* qar = sm.qa + rb;
+            const __bf16* qbr = sm.qb + rb;
+#pragma unroll
+            for (int ht = 0; ht < kHt; ++ht) {
+                const bf16x8 aw0 = state_frag(W1T[0][ht], W1T[1][ht]);
+                const bf16x8 aw1 = state_frag(W1T[2][ht], W1T[3][ht]);
+                const bf16x8 as0 = state_frag(S1T[0][ht], S1T[1][ht]);
+                const bf16x8 as1 = state_frag(S1T[2][ht], S1T[3][ht]);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    f32x4 zq = mfma(aw0, frag(qar, fo(ct, 0)), zero4());
+                    zq = mfma(aw1, frag(qar, fo(ct, 1)), zq);
+                    zq = mfma(as0, frag(qbr, fo(ct, 0)), zq);
+                    zqp[ht][ct] = mfma(as1, frag(qbr, fo(ct, 1)), zq);
+                }
+            }
+        }
+        wait_flag(otflag, e, bad);
+        if (e > 1) {
+            // the partner's partial of this side's y rows of the previous chunk
+            uint64_t px[4];
+            const uint64_t* src = yxslot(e - 1, 1 - side);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) px[i] = xload(const_cast<uint64_t*>(src + i * kThreads));
+            write_y(c0 - kC, px);
+        }
+        {
+            // E2 = 2 (O - V), O = O_side0 + O_side1, in its four layouts
+            uint64_t po[8];
+            const uint64_t* src = oslot(e, 1 - side);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) po[i] = xload(const_cast<uint64_t*>(src + i * kThreads));
+            const int xb = opq(rc * kLd + cl0), xt = opq(cl0 * kLd + rc);
+            const float ccr = -sm.cc[rc], wr = sm.w[rc];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                f32x4 o;
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int k = 4 * q4 + e4;
+                    const float op = (k & 1) ? hi32(po[k >> 1]) : lo32(po[k >> 1]);
+                    o[e4] = side == 0 ? oo[k] + op : op + oo[k];
+                }
+                const f32x4 v4 = f4(half4(vr[q4 >> 1], q4 & 1));
+                const f32x4 e2 = 2.f * (o - v4);
+                *reinterpret_cast<bf16x4*>(sm.e2l + xb + 4 * q4) = bf4(e2);
+#pragma unroll
+                for (int ee = 0; ee < 4; ++ee) {
+                    const int o2 = xt + (4 * q4 + ee) * kLd;
+                    sm.e2t[o2] = (__bf16)e2[ee];
+                    sm.e2c[o2] = (__bf16)(e2[ee] * ccr);
+                    sm.e2w[o2] = (__bf16)(e2[ee] * wr);
+                }
+            }
+        }
+        __syncthreads();  // B4
+
+        // ================= P4: backward, reads at the in-chunk weights
+        // this wave's W2 slice as bf16 [h][dd] (B operand of G = E2 W2)
+        __bf16* w2c = reinterpret_cast<__bf16*>(&sm.r[0][0]) + wv * kMat;
+        {
+            __bf16* w2w = w2c + opq(4 * g * kLd + j);
+#pragma unroll
+            for (int ht = 0; ht < kHt; ++ht)
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const bf16x4 v = bf4(opaque(W2T[ht][dt]));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) w2w[(16 * ht + r) * kLd + 16 * dt] = v[r];
+                }
+        }
+        wave_lds_sync();
+        // G = E2 W2 (rows c, cols h); D1 = G o SiLU'(Z)
+        bf16x4 D1[4][kHt];
+        {
+            const int rb = opq(j * kLd + 4 * g);
+            const __bf16* w2r = w2c + rb;
+            const __bf16* er = sm.e2l + rb;
+#pragma unroll
+            for (int ht = 0; ht < kHt; ++ht) {
+                const bf16x8 b0 = frag(w2r, fo(ht, 0));
+                const bf16x8 b1 = frag(w2r, fo(ht, 1));
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    f32x4 gg = mfma(frag(er, fo(ct, 0)), b0, zero4());
+                    gg = mfma(frag(er, fo(ct, 1)), b1, gg);
+                    D1[ct][ht] = bf4(gg * f4(Sp[ct][ht]));
+                }
+            }
+        }
+        // Zq^T += D1^T Mq^T; Hq = SiLU(Zq)
+        bf16x4 Hq[kHt][4];
+        {
+            const int rb = opq(j * kLd + 4 * g);
+            const __bf16* mqr = sm.mq + rb;
+#pragma unroll
+            for (int ht = 0; ht < kHt; ++ht) {
+                const bf16x8 ad0 = cat(D1[0][ht], D1[1][ht]);
+                const bf16x8 ad1 = cat(D1[2][ht], D1[3][ht]);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    f32x4 zq = mfma(ad0, frag(mqr, fo(ct, 0)), zqp[ht][ct]);
+                    if (ct >= 2) zq = mfma(ad1, frag(mqr, fo(ct, 1)), zq);
+                    f32x4 hq;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) hq[r] = zq[r] * sigmoid(zq[r]);
+                    Hq[ht][ct] = bf4(hq);
+                }
+            }
+        }
+        __syncthreads();  // B5: Q, Mq, E2 [c][dd] and the W2 slices are dead -> Y slots
+        // Y^T (rows dd, cols c) = a_c (W2 Hq^T) - b_c (S2 Hq^T) + E2^T Pm^T over this wave's
+        // hidden units, Pm^T[c'][c] = -c_{c,c'} (Hk Hq^T)[c'][c]; each wave stores its
+        // partial in its slot
+        {
+            const int rb = opq(j * kLd + 4 * g);
+            bf16x4 pm[4][4];  // [ct][ctp]
+            {
+                const __bf16* hkr = hkw0 + rb;
+                const __bf16* cmr = sm.cm + rb;
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const bf16x8 bq = cat(Hq[0][ct], Hq[1][ct]);
+#pragma unroll
+                    for (int ctp = 0; ctp < 4; ++ctp) {
+                        f32x4 pt = zero4();
+                        if (ctp <= ct) {
+                            pt = mfma(frag(hkr, fo(ctp, 0)), bq, pt);
+                            const f32x4 cmv =
+                                f4(*reinterpret_cast<const bf16x4*>(cmr + 16 * ct * kLd + 16 * ctp));
+                            pt = -(pt * cmv);
+                        }
+                        pm[ct][ctp] = bf4(pt);
+                    }
+                }
+            }
+            float* slot = yslot(sm, wv) + rb;
+            const __bf16* etr = sm.e2t + rb;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const bf16x8 aw = state_frag(W2T[0][dt], W2T[1][dt]);
+                const bf16x8 as = state_frag(S2T[0][dt], S2T[1][dt]);
+                const bf16x8 e0 = frag(etr, fo(dt, 0));
+                const bf16x8 e1 = frag(etr, fo(dt, 1));
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const bf16x8 bq = cat(Hq[0][ct], Hq[1][ct]);
+                    const float ac = sm.a[16 * ct + j], bc = sm.b[16 * ct + j];
+                    const f32x4 u1 = mfma(aw, bq, zero4());
+                    const f32x4 u2 = mfma(as, bq, zero4());
+                    f32x4 yt = ac * u1 - bc * u2;
+                    yt = mfma(e0, cat(pm[ct][0], pm[ct][1]), yt);
+                    if (ct >= 2) yt = mfma(e1, cat(pm[ct][2], pm[ct][3]), yt);
+                    *reinterpret_cast<f32x4*>(slot + 16 * ct * kLd + 16 * dt) = yt;
+                }
+            }
+        }
+        __syncthreads();  // B6: all Y partials stored
+
+        // ================= P5: this side's Y; post the partner's rows; carry
+        {
+            float ys[2][8];
+#pragma unroll
+            for (int hlf = 0; hlf < 2; ++hlf) {
+                const int e0 = (hlf == 0 ? yrow_own : yrow_oth) * kLd + yd0;
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int e4 = e0 + 4 * q;
+                    const f32x4 yv = (*reinterpret_cast<const f32x4*>(yslot(sm, 0) + e4) +
+                                      *reinterpret_cast<const f32x4*>(yslot(sm, 1) + e4)) +
+                                     (*reinterpret_cast<const f32x4*>(yslot(sm, 2) + e4) +
+                                      *reinterpret_cast<const f32x4*>(yslot(sm, 3) + e4));
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) ys[hlf][4 * q + k] = yv[k];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) yown[k] = ys[0][k];
+            uint64_t* dst = yxslot(e, side);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xstore(dst + i * kThreads, pack2(ys[1][2 * i], ys[1][2 * i + 1]));
+        }
+        __syncthreads();  // B7: the Y slots are read before the next chunk reuses them
+        if (c0 + kC < A.T) prefetch(c0 + kC);
+        {
+            const float aC = sm.a[kC], bC = sm.b[kC], pC = sm.p;
+            const int rb = opq(j * kLd + 4 * g);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const bf16x8 kc0 = frag(sm.kc + rb, fo(dt, 0));
+                const bf16x8 kc1 = frag(sm.kc + rb, fo(dt, 1));
+                const bf16x8 kw0 = frag(sm.kw + rb, fo(dt, 0));
+                const bf16x8 kw1 = frag(sm.kw + rb, fo(dt, 1));
+                const bf16x8 ec0 = frag(sm.e2c + rb, fo(dt, 0));
+                const bf16x8 ec1 = frag(sm.e2c + rb, fo(dt, 1));
+                const bf16x8 ew0 = frag(sm.e2w + rb, fo(dt, 0));
+                const bf16x8 ew1 = frag(sm.e2w + rb, fo(dt, 1));
+#pragma unroll
+                for (int ht = 0; ht < kHt; ++ht) {
+                    const bf16x8 bd0 = cat(D1[0][ht], D1[1][ht]);  // B: D1 [c][h]
+                    const bf16x8 bd1 = cat(D1[2][ht], D1[3][ht]);
+                    const bf16x8 ah0 = cat(Hk[0][ht], Hk[1][ht]);  // A: Hk^T [h][c]
+                    const bf16x8 ah1 = cat(Hk[2][ht], Hk[3][ht]);
+                    // chunk-end rescale (a_C W - b_C S, p S) fused into the accumulator input
+                    const f32x4 tw1 = aC * W1T[dt][ht] - bC * S1T[dt][ht];
+                    const f32x4 ts1 = pC * S1T[dt][ht];
+                    W1T[dt][ht] = mfma(kc1, bd1, mfma(kc0, bd0, tw1));
+                    S1T[dt][ht] = mfma(kw1, bd1, mfma(kw0, bd0, ts1));
+                    const f32x4 tw2 = aC * W2T[ht][dt] - bC * S2T[ht][dt];
+                    const f32x4 ts2 = pC * S2T[ht][dt];
+                    W2T[ht][dt] = mfma(ah1, ec1, mfma(ah0, ec0, tw2));
+                    S2T[ht][dt] = mfma(ah1, ew1, mfma(ah0, ew0, ts2));
+                }
+            }
+        }
+    }
+
+    // ---- y of the last chunk: one more exchange (no O words)
+    {
+        const int ef = e + 1;
+        post_flag(myflag, ef, l);
+        wait_flag(otflag, ef, bad);
+        uint64_t px[4];
+        const uint64_t* src = yxslot(e, 1 - side);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) px[i] = xload(const_cast<uint64_t*>(src + i * kThreads));
+        write_y((int64_t)(e - 1) * kC, px);
+    }
+    if (bad) sm.fail = 1;
+    __syncthreads();
+    const float nan = __builtin_nanf("");
+    const bool failed = sm.fail != 0;
+
+    // ---- final memory and momentum of this side's hidden units
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int ht = 0; ht < kHt; ++ht) {
+            const int h = hb + 16 * ht + j;
+            const int d = 16 * dt + 4 * g;
+            const f32x4 nn = {nan, nan, nan, nan};
+            *reinterpret_cast<f32x4*>(thT + h * kD + d) = failed ? nn : W1T[dt][ht];
+            *reinterpret_cast<f32x4*>(moT + h * kD + d) = failed ? nn : S1T[dt][ht];
+            const int h2 = hb + 16 * ht + 4 * g;
+            const int dd = 16 * dt + j;
+            *reinterpret_cast<f32x4*>(thT + kOff2 + dd * kHid + h2) = failed ? nn : W2T[ht][dt];
+            *reinterpret_cast<f32x4*>(moT + kOff2 + dd * kHid + h2) = failed ? nn : S2T[ht][dt];
+        }
+}
+
+// Clears the flags of every pair before a launch (exchange numbers restart at 1).
+__global__ void clear_pair_flags(char* ws, int64_t npairs) {
+    const int64_t pair = blockIdx.x;
+    if (pair >= npairs) return;
+    int* f = reinterpret_cast<int*>(ws + pair * kPairBytes);
+    for (int i = threadIdx.x; i < (int)(kFlagBytes / 4); i += blockDim.x) f[i] = 0;
+}
+
+int64_t padded_pairs(const ScanArgs& a) { return (a.B * a.H + 7) / 8 * 8; }
+
+}  // namespace
+
+bool scan_pair_supported(const ScanArgs& a) {
+    return a.L == 2 && a.n[0] == kD && a.n[1] == kHid && a.n[2] == kD && a.C == kC &&
+           a.io == TITANS_BF16;
+}
+
+size_t scan_pair_workspace_bytes(const ScanArgs& a) {
+    return (size_t)padded_pairs(a) * (size_t)kPairBytes;
+}
+
+int64_t scan_pair_workgroups(const ScanArgs& a) { return 2 * padded_pairs(a); }
+
+hipError_t launch_scan_pair(const ScanArgs& a, hipStream_t stream) {
+    const int64_t npairs = padded_pairs(a);
+    if (npairs == 0) return hipSuccess;
+    char* ws = static_cast<char*>(a.ws);
+    clear_pair_flags<<<dim3((unsigned)npairs), 256, 0, stream>>>(ws, npairs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ScanArgs args = a;
+    void* kargs[] = {&args};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&scan_pair_kernel),
+                                      dim3((unsigned)(2 * npairs)), dim3(kThreads), kargs, 0,
+                                      stream);
+}
+
+}  // namespace titans

@@ -42,6 +42,14 @@ hipError_t launch_scan_generic(const ScanArgs& a, hipStream_t stream);
 bool scan_mfma_supported(const ScanArgs& a);
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t stream);
 
+// Fused MFMA scan split over pairs of workgroups (same shape as above): each (b, h)
+// memory is served by two workgroups on one XCD that exchange partial sums through the
+// workspace; cooperative launch of scan_pair_workgroups(a) workgroups.
+bool scan_pair_supported(const ScanArgs& a);
+size_t scan_pair_workspace_bytes(const ScanArgs& a);
+int64_t scan_pair_workgroups(const ScanArgs& a);
+hipError_t launch_scan_pair(const ScanArgs& a, hipStream_t stream);
+
 // Generic retrieve: fp32 arithmetic, any supported shape.
 hipError_t launch_retrieve_generic(const ScanArgs& a, hipStream_t stream);
 

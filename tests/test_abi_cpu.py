@@ -55,11 +55,22 @@ def _desc(B=2, T=64, H=4, d=64, C=64, io=1):
     return desc
 
 
-def test_workspace_size_query():
+def test_workspace_size_query(monkeypatch):
     mlp = tm.mlp_desc((64, 256, 64))
-    # the fused kernel (64-256-64, C=64, bf16) keeps everything on chip: no workspace
-    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc()), ctypes.byref(mlp)) == 0
+    # the fused shape (64-256-64, C=64, bf16) runs on pairs of workgroups that exchange
+    # partial sums through the workspace: one 97 KiB area per pair, pairs padded to 8
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc()), ctypes.byref(mlp)) == b"fused_pair"
+    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc()), ctypes.byref(mlp)) == 8 * 99328
+    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(B=3, H=3)),
+                                                 ctypes.byref(mlp)) == 16 * 99328
+    # more memories than pairs of compute units: one workgroup per memory, no workspace
+    big = _desc(B=64, H=16)
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(big), ctypes.byref(mlp)) == b"fused_mfma"
+    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(big), ctypes.byref(mlp)) == 0
+    monkeypatch.setenv("TITANS_MEM_FUSED_SINGLE", "1")
     assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc()), ctypes.byref(mlp)) == b"fused_mfma"
+    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc()), ctypes.byref(mlp)) == 0
+    monkeypatch.delenv("TITANS_MEM_FUSED_SINGLE")
     size = tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(C=32)), ctypes.byref(mlp))
     assert 0 < size < 1 << 30 and size % 4 == 0
     assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=32)), ctypes.byref(mlp)) == b"generic_fp32"

@@ -311,19 +311,126 @@ def test_retrieve_headline_shape_sampled():
     assert y_rel_err(to_f64(y[:, ::64]), yr) <= 2e-2
 
 
-def test_fused_path_matches_generic_path(monkeypatch):
-    """The fused MFMA kernel (64-256-64, C=64, bf16) against the generic fp32 kernel."""
+# ----------------------------------------------------------- fused kernels
+#
+# The 64-256-64, C=64, bf16 shape runs on the pair kernel (two workgroups per memory)
+# while the pairs fit the GPU, else on the single-workgroup kernel; both are tested.
+
+FUSED = ["pair", "single"]
+
+
+def _use(kernel, monkeypatch):
+    monkeypatch.setenv("TITANS_MEM_FUSED_SINGLE", "1" if kernel == "single" else "0")
+    return "fused_pair" if kernel == "pair" else "fused_mfma"
+
+
+@pytest.mark.parametrize("kernel", FUSED)
+def test_fused_matches_oracle_and_generic(kernel, monkeypatch):
     wl, inp = _small(widths=(64, 256, 64), B=2, T=300, H=3, C=64, io="bf16", seed=11)
     dev = to_device(inp)
-    log("case fused vs generic 64-256-64 T=300")
-    assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == "fused_mfma"
+    log(f"case fused[{kernel}] vs oracle and generic, 64-256-64 T=300")
+    expected = _use(kernel, monkeypatch)
+    assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == expected
     y1, t1, s1 = run_gpu(dev, wl)
     torch.cuda.synchronize()
+    pairs = [(0, 0), (1, 2), (0, 1)]
+    check_pairs(wl, y1, t1, s1, pairs, oracle_seq(inp, pairs))
     monkeypatch.setenv("TITANS_MEM_FORCE_GENERIC", "1")
     assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == "generic_fp32"
     y2, t2, s2 = run_gpu(dev, wl)
     torch.cuda.synchronize()
     ey = y_rel_err(to_f64(y1), to_f64(y2))
     et = state_rel_err(to_f64(t1), to_f64(t2))
-    log(f"  fused vs generic: y {ey:.2e} theta_T {et:.2e}")
+    log(f"  fused[{kernel}] vs generic: y {ey:.2e} theta_T {et:.2e}")
     assert ey <= 2e-2 and et <= 1e-1
+
+
+@pytest.mark.parametrize("T", [1, 37, 64, 65, 130])
+@pytest.mark.parametrize("kernel", FUSED)
+def test_fused_short_and_ragged(kernel, T, monkeypatch):
+    wl, inp = _small(widths=(64, 256, 64), B=1, T=T, H=2, C=64, io="bf16", seed=T)
+    dev = to_device(inp)
+    log(f"case fused[{kernel}] T={T}")
+    expected = _use(kernel, monkeypatch)
+    assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == expected
+    y, thT, sT = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (0, 1)]
+    check_pairs(wl, y, thT, sT, pairs, oracle_seq(inp, pairs))
+
+
+@pytest.mark.parametrize("kernel", FUSED)
+def test_fused_streaming_inplace_determinism(kernel, monkeypatch):
+    wl, inp = _small(widths=(64, 256, 64), B=2, T=200, H=3, C=64, io="bf16", seed=3)
+    dev = to_device(inp)
+    log(f"case fused[{kernel}] streaming / in-place / determinism")
+    _use(kernel, monkeypatch)
+    y, thT, sT = run_gpu(dev, wl)
+    y2, thT2, sT2 = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(thT, thT2) and torch.equal(sT, sT2)
+    B = wl.batch
+    th = dev["theta0"].expand(B, -1, -1).contiguous()
+    s = dev["s0"].expand(B, -1, -1).contiguous()
+    cut = 128  # a multiple of the chunk: the two calls chain exactly
+    half = {n: dev[n][:, :cut] for n in ("q", "k", "v", "alpha", "eta", "beta")}
+    rest = {n: dev[n][:, cut:] for n in ("q", "k", "v", "alpha", "eta", "beta")}
+    ya, _, _ = tm.scan(half["q"], half["k"], half["v"], half["alpha"], half["eta"], half["beta"],
+                       th, s, wl.chunk, wl.widths, theta_T=th, s_T=s)
+    yb, _, _ = tm.scan(rest["q"], rest["k"], rest["v"], rest["alpha"], rest["eta"], rest["beta"],
+                       th, s, wl.chunk, wl.widths, theta_T=th, s_T=s)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([ya, yb], dim=1), y)
+    assert torch.equal(th, thT) and torch.equal(s, sT)
+
+
+@pytest.mark.parametrize("kernel", FUSED)
+def test_fused_strided_inputs_nonzero_momentum(kernel, monkeypatch):
+    wl, inp = _small(widths=(64, 256, 64), B=2, T=150, H=2, C=64, io="bf16", seed=21)
+    dev = to_device(inp)
+    log(f"case fused[{kernel}] strided q/k/v, per-batch theta0 and nonzero s0")
+    _use(kernel, monkeypatch)
+    packed = torch.stack([dev["q"], dev["k"], dev["v"]], dim=3)  # [B,T,H,3,d]
+    q, k, v = packed[:, :, :, 0], packed[:, :, :, 1], packed[:, :, :, 2]
+    g = torch.stack([dev["alpha"], dev["eta"], dev["beta"]], dim=-1)
+    B, H = wl.batch, wl.heads
+    rng = np.random.default_rng(17)
+    th0 = torch.from_numpy((rng.standard_normal((B, H, wl.params)) * 0.1).astype(np.float32)).cuda()
+    s0 = torch.from_numpy((rng.standard_normal((B, H, wl.params)) * 0.01).astype(np.float32)).cuda()
+    y = torch.empty(B, wl.seq_len, H, 2 * wl.d, dtype=torch.bfloat16, device="cuda")[..., : wl.d]
+    y, thT, sT = tm.scan(q, k, v, g[..., 0], g[..., 1], g[..., 2], th0, s0, wl.chunk, wl.widths, y=y)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (1, 1)]
+    refs = []
+    for b, h in pairs:
+        yr, tr, sr = oracle.scan(inp.qkv_f32("q")[b:b + 1, :, h:h + 1], inp.qkv_f32("k")[b:b + 1, :, h:h + 1],
+                                 inp.qkv_f32("v")[b:b + 1, :, h:h + 1], inp.alpha[b:b + 1, :, h:h + 1],
+                                 inp.eta[b:b + 1, :, h:h + 1], inp.beta[b:b + 1, :, h:h + 1],
+                                 to_f64(th0[b, h:h + 1]), to_f64(s0[b, h:h + 1]), wl.chunk, wl.widths)
+        refs.append((yr[0, :, 0], tr[0, 0], sr[0, 0]))
+    check_pairs(wl, y, thT, sT, pairs, refs)
+
+
+def test_pair_kernel_matches_single_kernel(monkeypatch):
+    """The two fused kernels round at the same points and differ only in summation order."""
+    wl = _workload("h8_d64_b4_t4k", True)
+    inp = synthetic.make_inputs(wl, 5)
+    dev = to_device(inp)
+    log("case pair vs single fused kernel, h8 T=4096 sustained")
+    _use("pair", monkeypatch)
+    y1, t1, s1 = run_gpu(dev, wl)
+    _use("single", monkeypatch)
+    y2, t2, s2 = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    ey = y_rel_err(to_f64(y1), to_f64(y2))
+    et = state_rel_err(to_f64(t1), to_f64(t2))
+    es = state_rel_err(to_f64(s1), to_f64(s2))
+    log(f"  pair vs single: y {ey:.2e} theta_T {et:.2e} s_T {es:.2e}")
+    assert ey <= 2e-2 and et <= 1e-1 and es <= 1e-1
+
+
+@pytest.mark.parametrize("sustained", [False, True])
+def test_headline_sampled_single_kernel(sustained, monkeypatch):
+    """The single-workgroup kernel at the full headline shape (the pair kernel runs it by default)."""
+    _use("single", monkeypatch)
+    test_headline_sampled(sustained)
