@@ -101,20 +101,20 @@ struct __attribute__((aligned(16))) Smem {
     // Regions are reused within a chunk; the comment gives each region's lives in order.
     float r[2][kMat];          // O partials (pairwise reduction) -> the waves' bf16 W2 slices
                                //   -> Y partial slots 0, 1   ([c][dd] fp32)
-    __bf16 qa[kMat];           // raw Q -> diag(a) Q [c][d]     } Y partial slot 2
+    __bf16 qa[kMat];           // diag(a) Q [c][d]              } Y partial slot 2
     __bf16 qb[kMat];           // -diag(b) Q [c][d]             }
     __bf16 mq[kMat];           // -(Cm o Q K^T) [c][c']         } Y partial slot 3
     __bf16 e2l[kMat];          // E2 [c][dd]                    }
     __bf16 kk[kMat];           // K [c][d]
+    __bf16 qq[kMat];           // Q [c][d]
     __bf16 e2t[kMat];          // L1 (coefficients) -> E2^T [dd][c]
     __bf16 e2c[kMat];          // L2^T (coefficients) -> -(diag(c_C) E2)^T [dd][c]
     __bf16 e2w[kMat];          // L1 row C -> (diag(w) E2)^T [dd][c]
     __bf16 kc[kMat];           // -(diag(c_C) K)^T [d][c]
     __bf16 kw[kMat];           // (diag(w) K)^T    [d][c]
-    __bf16 hk[kWaves / 2][kMat];  // Hk slices [c][h]: wave w at hk[w / 2], columns 32 (w % 2)..
     __bf16 cm[kMat];           // c_{t,j}, t, j < 64 (rows t)
     float a[kC + 4], b[kC + 4];
-    float cc[kC], w[kC], inva[kC];
+    float cc[kC], w[kC];
     float et[kC], omb[kC];
     float la2[kC + 4];         // sum_{m<t} log2(1 - alpha_m), t = 0..64
     float la2i[kC];            // sum_{m<=t} log2(1 - alpha_m)
@@ -193,6 +193,10 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
     const int yrow_own = 32 * side + yr, yrow_oth = 32 * (1 - side) + yr;
     float yown[8];
 
+    bf16x8 eye;  // B = [I16; 0] in the MFMA k order: lane (g, j) slot v < 4 is row 4g + v
+#pragma unroll
+    for (int v = 0; v < 8; ++v) eye[v] = (__bf16)((v < 4 && 4 * g + v == j) ? 1.f : 0.f);
+
     bf16x8 kpre[2], qpre[2];
     float gpre[3] = {0.f, 0.f, 1.f};
     auto prefetch = [&](int64_t t0) {
@@ -240,7 +244,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 *reinterpret_cast<bf16x4*>(sm.kk + xb + 4 * q4) = half4(kpre[q4 >> 1], q4 & 1);
-                *reinterpret_cast<bf16x4*>(sm.qa + xb + 4 * q4) = half4(qpre[q4 >> 1], q4 & 1);
+                *reinterpret_cast<bf16x4*>(sm.qq + xb + 4 * q4) = half4(qpre[q4 >> 1], q4 & 1);
             }
         }
         {
@@ -255,7 +259,6 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 const float pa = wave_scan_mul(keep);
                 const float a_l = lane_prev(pa, 1.f);
                 sm.a[l] = a_l;
-                sm.inva[l] = 1.f / a_l;
                 if (l == 63) sm.a[kC] = pa;
             } else if (wv == 1) {
                 const float pbl = wave_scan_mul(be_l);
@@ -351,13 +354,13 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 }
             }
         }
-        // Z = K W1^T (rows c, cols h) for this wave's 32 hidden units
-        __bf16* hkw0 = sm.hk[wv >> 1] + 32 * (wv & 1);  // this wave's Hk slice [c][h]
-        bf16x4 Hk[4][kHt], Sp[4][kHt];
+        // Z = K W1^T (rows c, cols h) for this wave's 32 hidden units; Hk^T (rows h, cols c)
+        // by an exact MFMA against the identity (D = A [I; 0] is the transpose of A's first
+        // 16 x 16 tile when A is an accumulator tile in registers)
+        bf16x4 Hk[4][kHt], Sp[4][kHt], HkT[kHt][4];
         {
-            const int rb = opq(j * kLd + 4 * g), wb = opq(4 * g * kLd + j);
+            const int rb = opq(j * kLd + 4 * g);
             const __bf16* ks = sm.kk + rb;
-            __bf16* hkw = hkw0 + wb;
 #pragma unroll
             for (int ht = 0; ht < kHt; ++ht) {
                 const bf16x8 bw0 = state_frag(W1T[0][ht], W1T[1][ht]);
@@ -376,22 +379,20 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                     }
                     Hk[ct][ht] = bf4(hk);
                     Sp[ct][ht] = bf4(sp);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) hkw[(16 * ct + r) * kLd + 16 * ht] = Hk[ct][ht][r];
+                    HkT[ht][ct] = bf4(mfma(cat(Hk[ct][ht], bf16x4{}), eye, zero4()));
                 }
             }
         }
-        wave_lds_sync();
         // O^T partial over this wave's hidden units: O^T[dd][c] = sum_h W2[dd][h] Hk[c][h]
         f32x4 Ot[4][4];
         {
             const int rb = opq(j * kLd + 4 * g);
-            const __bf16* hkr = hkw0 + rb;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
                 const bf16x8 a0 = state_frag(W2T[0][dt], W2T[1][dt]);
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) Ot[dt][ct] = mfma(a0, frag(hkr, fo(ct, 0)), zero4());
+                for (int ct = 0; ct < 4; ++ct)
+                    Ot[dt][ct] = mfma(a0, cat(HkT[0][ct], HkT[1][ct]), zero4());
             }
             // deterministic pairwise reduction, stage 1: waves 2, 3 store their partials
             if (wv >= 2) {
@@ -422,14 +423,15 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             const int xb = opq(rc * kLd + cl0), xt = opq(cl0 * kLd + rc);
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 qv = f4(*reinterpret_cast<const bf16x4*>(sm.qa + xb + 4 * q4));
+                const f32x4 qv = f4(*reinterpret_cast<const bf16x4*>(sm.qq + xb + 4 * q4));
                 *reinterpret_cast<bf16x4*>(sm.qa + xb + 4 * q4) = bf4(qv * ar);
                 *reinterpret_cast<bf16x4*>(sm.qb + xb + 4 * q4) = bf4(qv * br);
                 const f32x4 kv = f4(*reinterpret_cast<const bf16x4*>(sm.kk + xb + 4 * q4));
+                const bf16x4 kc4 = bf4(kv * ccr), kw4 = bf4(kv * wr);
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) {
-                    sm.kc[xt + (4 * q4 + e4) * kLd] = (__bf16)(kv[e4] * ccr);
-                    sm.kw[xt + (4 * q4 + e4) * kLd] = (__bf16)(kv[e4] * wr);
+                    sm.kc[xt + (4 * q4 + e4) * kLd] = kc4[e4];
+                    sm.kw[xt + (4 * q4 + e4) * kLd] = kw4[e4];
                 }
             }
         }
@@ -446,19 +448,18 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) oo[4 * q4 + e4] = o[e4];
             }
+            // the O words go out now; the flag follows once they have landed (below)
             uint64_t* dst = oslot(e, side);
 #pragma unroll
             for (int i = 0; i < 8; ++i) xstore(dst + i * kThreads, pack2(oo[2 * i], oo[2 * i + 1]));
-            post_flag(myflag, e, l);
         }
         {
-            // Mq[c][c'] = -(c_{c,c'} / a_c) (Qa K^T)[c][c'] for column tile c = 16 wv + j
+            // Mq[c][c'] = -c_{c,c'} (Q K^T)[c][c'] for column tile c = 16 wv + j
             const int rb = opq(j * kLd + 4 * g);
             const __bf16* ks = sm.kk + rb;
-            const __bf16* qr = sm.qa + rb + 16 * wv * kLd;
+            const __bf16* qr = sm.qq + rb + 16 * wv * kLd;
             const __bf16* cmr = sm.cm + rb + 16 * wv * kLd;
             __bf16* mqw = sm.mq + rb + 16 * wv * kLd;
-            const float ia = sm.inva[16 * wv + j];
 #pragma unroll
             for (int ctp = 0; ctp < 4; ++ctp) {
                 f32x4 x = zero4();
@@ -466,7 +467,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                     x = mfma(frag(ks, fo(ctp, 0)), frag(qr, 0), x);
                     x = mfma(frag(ks, fo(ctp, 1)), frag(qr, 32), x);
                     const f32x4 cmv = f4(*reinterpret_cast<const bf16x4*>(cmr + 16 * ctp));
-                    x = x * cmv * (-ia);
+                    x = -(x * cmv);
                 }
                 *reinterpret_cast<bf16x4*>(mqw + 16 * ctp) = bf4(x);
             }
@@ -492,6 +493,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 }
             }
         }
+        post_flag(myflag, e, l);
         wait_flag(otflag, e, bad);
         if (e > 1) {
             // the partner's partial of this side's y rows of the previous chunk
@@ -520,13 +522,14 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 }
                 const f32x4 v4 = f4(half4(vr[q4 >> 1], q4 & 1));
                 const f32x4 e2 = 2.f * (o - v4);
-                *reinterpret_cast<bf16x4*>(sm.e2l + xb + 4 * q4) = bf4(e2);
+                const bf16x4 el = bf4(e2), ec = bf4(e2 * ccr), ew = bf4(e2 * wr);
+                *reinterpret_cast<bf16x4*>(sm.e2l + xb + 4 * q4) = el;
 #pragma unroll
                 for (int ee = 0; ee < 4; ++ee) {
                     const int o2 = xt + (4 * q4 + ee) * kLd;
-                    sm.e2t[o2] = (__bf16)e2[ee];
-                    sm.e2c[o2] = (__bf16)(e2[ee] * ccr);
-                    sm.e2w[o2] = (__bf16)(e2[ee] * wr);
+                    sm.e2t[o2] = el[ee];
+                    sm.e2c[o2] = ec[ee];
+                    sm.e2w[o2] = ew[ee];
                 }
             }
         }
@@ -593,7 +596,6 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             const int rb = opq(j * kLd + 4 * g);
             bf16x4 pm[4][4];  // [ct][ctp]
             {
-                const __bf16* hkr = hkw0 + rb;
                 const __bf16* cmr = sm.cm + rb;
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
@@ -602,7 +604,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                     for (int ctp = 0; ctp < 4; ++ctp) {
                         f32x4 pt = zero4();
                         if (ctp <= ct) {
-                            pt = mfma(frag(hkr, fo(ctp, 0)), bq, pt);
+                            pt = mfma(cat(HkT[0][ctp], HkT[1][ctp]), bq, pt);
                             const f32x4 cmv =
                                 f4(*reinterpret_cast<const bf16x4*>(cmr + 16 * ct * kLd + 16 * ctp));
                             pt = -(pt * cmv);
@@ -613,6 +615,12 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             }
             float* slot = yslot(sm, wv) + rb;
             const __bf16* etr = sm.e2t + rb;
+            float ac[4], bc[4];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                ac[ct] = sm.a[16 * ct + j];
+                bc[ct] = sm.b[16 * ct + j];
+            }
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
                 const bf16x8 aw = state_frag(W2T[0][dt], W2T[1][dt]);
@@ -622,10 +630,9 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
                     const bf16x8 bq = cat(Hq[0][ct], Hq[1][ct]);
-                    const float ac = sm.a[16 * ct + j], bc = sm.b[16 * ct + j];
                     const f32x4 u1 = mfma(aw, bq, zero4());
                     const f32x4 u2 = mfma(as, bq, zero4());
-                    f32x4 yt = ac * u1 - bc * u2;
+                    f32x4 yt = ac[ct] * u1 - bc[ct] * u2;
                     yt = mfma(e0, cat(pm[ct][0], pm[ct][1]), yt);
                     if (ct >= 2) yt = mfma(e1, cat(pm[ct][2], pm[ct][3]), yt);
                     *reinterpret_cast<f32x4*>(slot + 16 * ct * kLd + 16 * dt) = yt;
