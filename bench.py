@@ -95,6 +95,33 @@ def cpu_baseline(inp, wl, sample_rows, sample_tokens):
                       f"({dt:.1f} s on {used} threads of {threads} host cores)"}
 
 
+def bench_retrieve(tm, torch, q, theta, wl, steps, warmup):
+    """titans_mem_retrieve (fixed-weight read) over the same q with the scan's final
+    weights [B, H, P]: its own line, not part of the scan step.  Algorithmic bytes: q and y
+    once, theta once per memory; flops 2 P per token-head."""
+    y = torch.empty_like(q)
+    for _ in range(warmup):
+        tm.retrieve(q, theta, wl.widths, y=y)
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        tm.retrieve(q, theta, wl.widths, y=y)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    B, T, H, d = q.shape
+    io = q.element_size()
+    nbytes = 2 * B * T * H * d * io + B * H * wl.params * 4
+    flops = 2 * wl.params * B * T * H
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"path": tm.retrieve_path(q, wl.widths), "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAKS["hbm"], "unit": "GB/s",
+                         "frac": gbs / PEAKS["hbm"], "alg_bytes_per_launch": nbytes},
+            "mfma_tflops": flops / (ms * 1e-3) / 1e12}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,6 +132,7 @@ def main():
     ap.add_argument("--cpu-sample-rows", type=int, default=8)
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-retrieve", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -198,6 +226,8 @@ def main():
                      "kernel": kernel, "kernel_ms": kernel_ms,
                      "alg_flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes(wl)},
     }
+    if not args.no_retrieve:
+        result["retrieve"] = bench_retrieve(tm, torch, t["q"], thT, wl, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_sample_rows, args.cpu_sample_tokens)
     print(json.dumps(result), flush=True)

@@ -99,10 +99,12 @@ const char* titans_last_error(void);
 /* P = sum_l n_l n_{l-1} floats per memory, or -1 if mlp is invalid. */
 int64_t titans_mem_param_count(const titans_mlp_desc* mlp);
 
-/* Which kernel titans_mem_scan runs for this problem: "fused_mfma" (bf16 MFMA, state
- * resident on chip; the 64 -> 256 -> 64 memory with C = 64 and bf16 I/O) or
- * "generic_fp32" (every other supported shape).  NULL if the arguments are invalid.
- * The returned string is static. */
+/* Which kernel titans_mem_scan runs for this problem on the current device (a 256-CU
+ * MI355X is assumed when no device is visible): for the 64 -> 256 -> 64 memory with
+ * C = 64 and bf16 I/O, "fused_pair" (bf16 MFMA, state resident on chip, two workgroups
+ * per memory; chosen while 2 * ceil(B*H / 8) * 8 workgroups fit one per compute unit) or
+ * "fused_mfma" (one workgroup per memory); "generic_fp32" for every other supported
+ * shape.  NULL if the arguments are invalid.  The returned string is static. */
 const char* titans_mem_scan_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp);
 
 /* Device workspace bytes titans_mem_scan needs for this problem (0 if none;
@@ -136,6 +138,11 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
                               const float* theta0, const float* s0,
                               void* y, float* theta_T, float* s_T,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Which kernel titans_mem_retrieve runs for this problem: "fused_mfma" (bf16 MFMA; the
+ * 64 -> 256 -> 64 memory with bf16 q / y) or "generic_fp32".  NULL if the arguments are
+ * invalid.  The returned string is static. */
+const char* titans_mem_retrieve_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp);
 
 /*
  * Read with fixed weights (the explainer's retrieve formula with theta held

@@ -15,7 +15,7 @@ import os
 
 import torch
 
-__all__ = ["scan", "retrieve", "scan_workspace_size", "scan_path", "param_count", "TitansError", "LIB_PATH",
+__all__ = ["scan", "retrieve", "scan_workspace_size", "scan_path", "retrieve_path", "param_count", "TitansError", "LIB_PATH",
            "lib", "ScanDesc", "MlpDesc", "MAX_LAYERS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtitans_mem.so")
@@ -50,6 +50,8 @@ lib.titans_mem_scan_workspace_size.restype = ctypes.c_size_t
 lib.titans_mem_scan_workspace_size.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)]
 lib.titans_mem_scan_path.restype = ctypes.c_char_p
 lib.titans_mem_scan_path.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)]
+lib.titans_mem_retrieve_path.restype = ctypes.c_char_p
+lib.titans_mem_retrieve_path.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)]
 lib.titans_mem_scan.restype = ctypes.c_int
 lib.titans_mem_scan.argtypes = ([ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)] + [_vp] * 12
                                 + [ctypes.c_size_t, _vp])
@@ -147,7 +149,7 @@ def scan_workspace_size(q, chunk, widths) -> int:
 
 
 def scan_path(q, chunk, widths) -> str:
-    """Name of the kernel that serves this shape: "fused_mfma" or "generic_fp32"."""
+    """Name of the kernel that serves this shape: "fused_pair", "fused_mfma" or "generic_fp32"."""
     d = make_desc(q, chunk, q, None, None, None)
     r = lib.titans_mem_scan_path(ctypes.byref(d), ctypes.byref(mlp_desc(widths)))
     if r is None:
@@ -198,6 +200,15 @@ def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, *, y=None, theta_
                                _ptr(alpha), _ptr(eta), _ptr(beta), _ptr(theta0), _ptr(s0), _ptr(y),
                                _ptr(theta_T), _ptr(s_T), _ptr(workspace), ws_bytes, _stream()))
     return y, theta_T, s_T
+
+
+def retrieve_path(q, widths) -> str:
+    """Name of the kernel titans_mem_retrieve runs for q's shape: "fused_mfma" or "generic_fp32"."""
+    d = make_desc(q, 1, q, None, None, None)
+    r = lib.titans_mem_retrieve_path(ctypes.byref(d), ctypes.byref(mlp_desc(widths)))
+    if r is None:
+        raise TitansError(1, "invalid retrieve shape or MLP widths")
+    return r.decode()
 
 
 def retrieve(q, theta, widths, *, y=None):

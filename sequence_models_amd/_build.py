@@ -26,6 +26,7 @@ SOURCES = {
     "scan_generic.hip": [],
     "scan_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "scan_pair.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "retrieve_mfma.hip": [],
 }
 
 

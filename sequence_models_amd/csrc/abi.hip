@@ -351,14 +351,32 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
     return TITANS_OK;
 }
 
+static titans_status prepare_retrieve(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
+                                      titans::ScanArgs& a) {
+    titans_status st = check_desc_common(desc, a);
+    if (st) return st;
+    if ((st = check_mlp(mlp, a))) return st;
+    return check_shape_support(a, false);
+}
+
+static bool retrieve_uses_mfma(const titans::ScanArgs& a) {
+    const char* env = getenv("TITANS_MEM_FORCE_GENERIC");
+    if (env && env[0] == '1') return false;
+    return titans::retrieve_mfma_supported(a);
+}
+
+const char* titans_mem_retrieve_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp) {
+    titans::ScanArgs a{};
+    if (prepare_retrieve(desc, mlp, a) != TITANS_OK) return nullptr;
+    return retrieve_uses_mfma(a) ? "fused_mfma" : "generic_fp32";
+}
+
 titans_status titans_mem_retrieve(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
                                   const void* q, const float* theta, void* y, void* stream) {
     g_last_error[0] = '\0';
     titans::ScanArgs a{};
-    titans_status st = check_desc_common(desc, a);
+    titans_status st = prepare_retrieve(desc, mlp, a);
     if (st) return st;
-    if ((st = check_mlp(mlp, a))) return st;
-    if ((st = check_shape_support(a, false))) return st;
     const int64_t nseq = a.B * a.H;
     if (nseq == 0 || a.T == 0) return TITANS_OK;
     if (!q || !theta || !y)
@@ -380,7 +398,9 @@ titans_status titans_mem_retrieve(const titans_scan_desc* desc, const titans_mlp
     a.q = q;
     a.thetaT = const_cast<float*>(theta);
     a.y = y;
-    hipError_t e = titans::launch_retrieve_generic(a, static_cast<hipStream_t>(stream));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = retrieve_uses_mfma(a) ? titans::launch_retrieve_mfma(a, hs)
+                                         : titans::launch_retrieve_generic(a, hs);
     if (e != hipSuccess) return hip_fail(e, "retrieve launch");
     return TITANS_OK;
 }

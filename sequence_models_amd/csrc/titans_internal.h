@@ -53,4 +53,8 @@ hipError_t launch_scan_pair(const ScanArgs& a, hipStream_t stream);
 // Generic retrieve: fp32 arithmetic, any supported shape.
 hipError_t launch_retrieve_generic(const ScanArgs& a, hipStream_t stream);
 
+// MFMA retrieve for the 64 -> 256 -> 64 memory with bf16 q / y.
+bool retrieve_mfma_supported(const ScanArgs& a);
+hipError_t launch_retrieve_mfma(const ScanArgs& a, hipStream_t stream);
+
 }  // namespace titans

@@ -300,6 +300,33 @@ def test_retrieve_matches_oracle(io, widths):
     assert y_rel_err(to_f64(y), yr) <= Y_BAR[io]
 
 
+@pytest.mark.parametrize("T", [1, 63, 1023, 1025, 2100])
+def test_retrieve_mfma_matches_generic_and_oracle(T, monkeypatch):
+    """The bf16 MFMA retrieve (64-256-64) against the generic fp32 kernel and the oracle,
+    with per-batch weights, strided q and y and a ragged token count."""
+    wl, inp = _small(widths=(64, 256, 64), B=2, T=T, H=3, io="bf16", seed=T)
+    dev = to_device(inp)
+    log(f"case retrieve mfma T={T}")
+    B, H = 2, 3
+    rng = np.random.default_rng(T)
+    theta = torch.from_numpy((rng.standard_normal((B, H, wl.params)) / 8).astype(np.float32)).cuda()
+    packed = torch.stack([dev["q"], dev["k"]], dim=3)  # [B,T,H,2,d]: q rows strided by 2d
+    q = packed[:, :, :, 0]
+    assert tm.retrieve_path(q, wl.widths) == "fused_mfma"
+    y = torch.empty(B, T, H, 2 * wl.d, dtype=torch.bfloat16, device="cuda")[..., : wl.d]
+    y = tm.retrieve(q, theta, wl.widths, y=y)
+    monkeypatch.setenv("TITANS_MEM_FORCE_GENERIC", "1")
+    assert tm.retrieve_path(q, wl.widths) == "generic_fp32"
+    y2 = tm.retrieve(q, theta, wl.widths)
+    torch.cuda.synchronize()
+    sel = slice(0, T, max(1, T // 200))
+    yr = oracle.retrieve(inp.qkv_f32("q")[:, sel], to_f64(theta), wl.widths)
+    e1 = y_rel_err(to_f64(y[:, sel]), yr)
+    e2 = y_rel_err(to_f64(y), to_f64(y2))
+    log(f"  mfma vs oracle {e1:.2e}, mfma vs generic {e2:.2e}")
+    assert e1 <= 2e-2 and e2 <= 2e-2
+
+
 def test_retrieve_headline_shape_sampled():
     wl = synthetic.WORKLOADS[synthetic.HEADLINE]
     inp = synthetic.make_inputs(wl, 0)
