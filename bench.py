@@ -56,8 +56,8 @@ def kernel_source_digest(kernel):
     """sha256 of the source file that defines the kernel (traffic is void once it changes)."""
     import hashlib
 
-    src = {"scan_pair_kernel": "scan_pair.hip", "scan_mfma_kernel": "scan_mfma.hip",
-           "scan_generic_kernel": "scan_generic.hip"}[kernel]
+    src = {"scan_mfma_kernel": "scan_mfma.hip", "scan_generic_kernel": "scan_generic.hip"}.get(
+        kernel, "scan_pair.hip")
     with open(os.path.join(ROOT, "sequence_models_amd", "csrc", src), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
@@ -199,7 +199,10 @@ def main():
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     path = tm.scan_path(t["q"], wl.chunk, wl.widths)
     if path in ("fused_pair", "fused_mfma"):  # bf16 MFMA contractions with fp32 accumulation
-        kernel = "scan_pair_kernel" if path == "fused_pair" else "scan_mfma_kernel"
+        # the pair path is three launches (flag clear, chunk-coefficient pass, scan); the
+        # events bracket the whole call, so kernel_ms is their sum
+        kernel = ("clear_pair_flags + pair_coef_kernel + scan_pair_kernel" if path == "fused_pair"
+                  else "scan_mfma_kernel")
         bound, peak, dtype = "mfma", PEAKS["mfma_bf16"], "bf16"
     else:  # fp32 FMAs on the vector ALUs
         bound, peak, kernel, dtype = "alu", PEAKS["valu_f32"], "scan_generic_kernel", "f32"

@@ -107,19 +107,14 @@ struct __attribute__((aligned(16))) Smem {
     __bf16 e2l[kMat];          // E2 [c][dd]                    }
     __bf16 kk[kMat];           // K [c][d]
     __bf16 qq[kMat];           // Q [c][d]
-    __bf16 e2t[kMat];          // L1 (coefficients) -> E2^T [dd][c]
-    __bf16 e2c[kMat];          // L2^T (coefficients) -> -(diag(c_C) E2)^T [dd][c]
-    __bf16 e2w[kMat];          // L1 row C -> (diag(w) E2)^T [dd][c]
+    __bf16 e2t[kMat];          // E2^T [dd][c]
+    __bf16 e2c[kMat];          // -(diag(c_C) E2)^T [dd][c]
+    __bf16 e2w[kMat];          // (diag(w) E2)^T [dd][c]
     __bf16 kc[kMat];           // -(diag(c_C) K)^T [d][c]
     __bf16 kw[kMat];           // (diag(w) K)^T    [d][c]
     __bf16 cm[kMat];           // c_{t,j}, t, j < 64 (rows t)
-    float a[kC + 4], b[kC + 4];
-    float cc[kC], w[kC];
-    float et[kC], omb[kC];
-    float la2[kC + 4];         // sum_{m<t} log2(1 - alpha_m), t = 0..64
-    float la2i[kC];            // sum_{m<=t} log2(1 - alpha_m)
-    float lb2[kC];             // sum_{m<=t} log2(beta_m)
-    float p;
+    float a[kC], b[kC], cc[kC], w[kC];  // one chunk's coefficient vectors
+    float tail[4];                       // a_C, b_C, p (right after w: one copy fills all)
     int fail;
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
@@ -130,6 +125,128 @@ __device__ __forceinline__ float* yslot(Smem& sm, int w) {
         case 1: return sm.r[1];
         case 2: return reinterpret_cast<float*>(sm.qa);
         default: return reinterpret_cast<float*>(sm.mq);
+    }
+}
+
+// ---------------------------------------------------------------- chunk coefficients
+//
+// Everything the scan needs from the gates alone, per (memory, chunk), computed for all
+// chunks at once before the scan (they do not depend on the memory's state):
+//   a_t = prod_{m<t} (1 - alpha_m), t = 0..C          (a_C: the chunk-end decay)
+//   b_t: b_0 = 0, b_{t+1} = (1 - alpha_t) b_t + eta_t prod_{m<=t} beta_m
+//   p = prod_m beta_m,  w_j = (1 - beta_j) prod_{j<m<C} beta_m
+//   c_{t,j} = sum_{j<=i<t} L1[t][i] L2[i][j]          (strictly lower, t = 0..C)
+//     L1[t][i] = prod_{i<m<t} (1 - alpha_m),  L2[i][j] = eta_i (1 - beta_j) prod_{j<m<=i} beta_m
+// Each L1 / L2 entry is exp2 of a difference of log2 prefix sums (positive factors only;
+// a zero factor enters as log2 = -1024 and comes out as exactly zero); the C x C sum is one
+// bf16 MFMA product, row C of it is c_C.  Tokens past the sequence end are padding: no
+// decay, no write, momentum kept (alpha = eta = 0, beta = 1).
+//
+// Record of one chunk (bytes): Cm [t][j] bf16 64 x 64 | a[0..63] | b[0..63] | c_C[0..63] |
+// w[0..63] (fp32) | a_C, b_C, p, 0.
+constexpr int64_t kCoefCm = kC * kC * 2;
+constexpr int64_t kCoefBytes = kCoefCm + 5 * kC * 4;
+static_assert(kCoefBytes % 256 == 0, "records stay 256-byte aligned");
+
+struct __attribute__((aligned(16))) CoefSmem {  // one wave's scratch
+    __bf16 l1[kMat];        // L1 [t][i]
+    __bf16 l2t[kMat];       // L2^T [j][i]
+    __bf16 l1c[16 * kLd];   // row 0: L1[C][i]; rows 1..15 only keep fragment reads in bounds
+    float la2i[kC], lb2[kC], et[kC];
+};
+
+__global__ void __launch_bounds__(kThreads) pair_coef_kernel(ScanArgs A, char* coef, int64_t nchunks) {
+    __shared__ CoefSmem csm[kWaves];
+    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, j = l & 15;
+    const int64_t task = (int64_t)blockIdx.x * kWaves + wv;  // one chunk per wave
+    if (task >= A.B * A.H * nchunks) return;
+    const int64_t seq = task / nchunks, n = task % nchunks;
+    const int64_t bi = seq / A.H, hi = seq % A.H;
+    CoefSmem& cs = csm[wv];
+    char* rec = coef + task * kCoefBytes;
+    float* rv = reinterpret_cast<float*>(rec + kCoefCm);
+
+    const int64_t t = n * kC + l;
+    float al = 0.f, et_l = 0.f, be_l = 1.f;
+    if (t < A.T) {
+        const int64_t go = bi * A.gs[0] + t * A.gs[1] + hi * A.gs[2];
+        al = A.alpha[go];
+        et_l = A.eta[go];
+        be_l = A.beta[go];
+    }
+    const float keep = 1.f - al;
+    const float pa = wave_scan_mul(keep);    // prod_{m<=l} (1 - alpha_m)
+    const float pbl = wave_scan_mul(be_l);   // prod_{m<=l} beta_m
+    const float lk = wave_scan_add(keep > 0.f ? __log2f(keep) : -1024.f);
+    const float lb = wave_scan_add(be_l > 0.f ? __log2f(be_l) : -1024.f);
+    float mk = keep, mc = et_l * pbl;        // affine maps x -> keep_t x + eta_t p_t, composed
+    wave_scan_affine(mk, mc);
+    const float la2 = lane_prev(lk, 0.f);    // sum_{m<l} log2(1 - alpha_m)
+    const float la2C = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lk), 63));
+    const float lbL = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lb), 63));
+    cs.la2i[l] = lk;
+    cs.lb2[l] = lb;
+    cs.et[l] = et_l;
+    cs.l1c[l] = (__bf16)__builtin_amdgcn_exp2f(la2C - lk);
+    rv[l] = lane_prev(pa, 1.f);                                            // a_l
+    rv[kC + l] = lane_prev(mc, 0.f);                                       // b_l
+    rv[3 * kC + l] = (1.f - be_l) * __builtin_amdgcn_exp2f(lbL - lb);      // w_l
+    if (l == 63) {
+        rv[4 * kC + 0] = pa;
+        rv[4 * kC + 1] = mc;
+        rv[4 * kC + 2] = pbl;
+        rv[4 * kC + 3] = 0.f;
+    }
+    wave_lds_sync();
+    {
+        // lane r writes row r of L1 (t = r) and of L2^T (j = r)
+        const float omb = 1.f - be_l;
+        __bf16* r1 = cs.l1 + l * kLd;
+        __bf16* r2 = cs.l2t + l * kLd;
+#pragma unroll 4
+        for (int i4 = 0; i4 < kC / 4; ++i4) {
+            const f32x4 li = *reinterpret_cast<const f32x4*>(cs.la2i + 4 * i4);
+            const f32x4 bi4 = *reinterpret_cast<const f32x4*>(cs.lb2 + 4 * i4);
+            const f32x4 ei = *reinterpret_cast<const f32x4*>(cs.et + 4 * i4);
+            f32x4 x1, x2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * i4 + e;
+                // out-of-triangle exponents may be +inf; the select discards them
+                const float v1 = __builtin_amdgcn_exp2f(la2 - li[e]);
+                const float v2 = ei[e] * __builtin_amdgcn_exp2f(bi4[e] - lb) * omb;
+                x1[e] = i < l ? v1 : 0.f;
+                x2[e] = i >= l ? v2 : 0.f;
+            }
+            *reinterpret_cast<bf16x4*>(r1 + 4 * i4) = bf4(x1);
+            *reinterpret_cast<bf16x4*>(r2 + 4 * i4) = bf4(x2);
+        }
+    }
+    wave_lds_sync();
+    {
+        // Cm^T[j][t] = sum_i L2^T[j][i] L1^T[i][t], tiles (j-block jt, t-block tb), jt <= tb
+        const int rb = j * kLd + 4 * g;
+        const __bf16* l2r = cs.l2t + rb;
+        const __bf16* l1r = cs.l1 + rb;
+        __bf16* cmg = reinterpret_cast<__bf16*>(rec);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) {
+                f32x4 x = zero4();
+                if (jt <= tb) {
+                    x = mfma(frag(l2r, fo(jt, 0)), frag(l1r, fo(tb, 0)), x);
+                    x = mfma(frag(l2r, fo(jt, 1)), frag(l1r, fo(tb, 1)), x);
+                }
+                *reinterpret_cast<bf16x4*>(cmg + (16 * tb + j) * kC + 16 * jt + 4 * g) = bf4(x);
+            }
+        const __bf16* l1cr = cs.l1c + rb;
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            f32x4 x = mfma(frag(l2r, fo(jt, 0)), frag(l1cr, 0), zero4());
+            x = mfma(frag(l2r, fo(jt, 1)), frag(l1cr, 32), x);
+            if (j == 0) *reinterpret_cast<f32x4*>(rv + 2 * kC + 16 * jt + 4 * g) = x;  // c_C
+        }
     }
 }
 
@@ -150,6 +267,9 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
     uint64_t* xo = reinterpret_cast<uint64_t*>(pbase + kFlagBytes);
     uint64_t* xy = xo + kOWords;
     auto oslot = [&](int e, int s) { return xo + ((e & 1) * 2 + s) * 8 * kThreads + tid; };
+    const int64_t nchunks = (A.T + kC - 1) / kC;
+    const char* coef = static_cast<const char*>(A.ws) + ((A.B * A.H + 7) / 8 * 8) * kPairBytes +
+                       seq * nchunks * kCoefBytes;
     auto yxslot = [&](int e, int s) { return xy + ((e & 1) * 2 + s) * 4 * kThreads + tid; };
     bool bad = false;
 
@@ -184,7 +304,6 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
     __bf16* yg = static_cast<__bf16*>(A.y);
     const int64_t qbase = bi * A.qs[0] + hi * A.qs[2];
     const int64_t ybase = bi * A.ys[0] + hi * A.ys[2];
-    const int64_t gbase = bi * A.gs[0] + hi * A.gs[2];
     // this thread's slice of a chunk's 64 x 64 token tiles: row rc, columns cl0 .. cl0+15
     const int rc = tid >> 2, cl0 = 16 * (tid & 3);
     // this thread's y elements: row yr of this side's half (own) and of the partner's
@@ -197,9 +316,15 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
 #pragma unroll
     for (int v = 0; v < 8; ++v) eye[v] = (__bf16)((v < 4 && 4 * g + v == j) ? 1.f : 0.f);
 
-    bf16x8 kpre[2], qpre[2];
-    float gpre[3] = {0.f, 0.f, 1.f};
+    bf16x8 kpre[2], qpre[2], cpre[2];
+    f32x4 vpre = zero4();
     auto prefetch = [&](int64_t t0) {
+        // the chunk's coefficient record: Cm row rc, columns cl0 .. cl0+15; threads 0..64
+        // also one 16-byte piece of a | b | c_C | w | (a_C, b_C, p)
+        const char* rec = coef + (t0 / kC) * kCoefBytes;
+        cpre[0] = *reinterpret_cast<const bf16x8*>(rec + 32 * tid);
+        cpre[1] = *reinterpret_cast<const bf16x8*>(rec + 32 * tid + 16);
+        if (tid <= kC) vpre = *reinterpret_cast<const f32x4*>(rec + kCoefCm + 16 * tid);
         const int64_t t = t0 + rc;
         if (t < A.T) {
             const int64_t o = qbase + t * A.qs[1] + cl0;
@@ -209,17 +334,6 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             qpre[1] = *reinterpret_cast<const bf16x8*>(qg + o + 8);
         } else {
             kpre[0] = kpre[1] = qpre[0] = qpre[1] = bf16x8{};
-        }
-        const int64_t tt = t0 + l;
-        if (tt < A.T) {
-            const int64_t go = gbase + tt * A.gs[1];
-            gpre[0] = A.alpha[go];
-            gpre[1] = A.eta[go];
-            gpre[2] = A.beta[go];
-        } else {  // padding tokens: no decay, no write, momentum kept
-            gpre[0] = 0.f;
-            gpre[1] = 0.f;
-            gpre[2] = 1.f;
         }
     };
     // y for this side's rows of the chunk starting at token t0, own partial + partner's
@@ -248,35 +362,11 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             }
         }
         {
-            // Gate prefixes over the chunk's tokens (lane l = token l; each wave runs its
-            // share of the lane-parallel DPP scans):
-            //   a_t = prod_{m<t} (1 - alpha_m),  p = prod_m beta_m,
-            //   b_{t+1} = (1 - alpha_t) b_t + eta_t prod_{m<=t} beta_m,
-            //   la2 / lb2: log2 prefix sums of (1 - alpha) and beta for the coefficient matrix
-            //   (a zero factor stays exactly zero through exp2 of a very negative exponent).
-            const float keep = 1.f - gpre[0], et_l = gpre[1], be_l = gpre[2];
-            if (wv == 0) {
-                const float pa = wave_scan_mul(keep);
-                const float a_l = lane_prev(pa, 1.f);
-                sm.a[l] = a_l;
-                if (l == 63) sm.a[kC] = pa;
-            } else if (wv == 1) {
-                const float pbl = wave_scan_mul(be_l);
-                sm.lb2[l] = wave_scan_add(be_l > 0.f ? __log2f(be_l) : -1024.f);
-                if (l == 63) sm.p = pbl;
-            } else if (wv == 2) {
-                const float lk = wave_scan_add(keep > 0.f ? __log2f(keep) : -1024.f);
-                sm.la2[l] = lane_prev(lk, 0.f);
-                sm.la2i[l] = lk;
-                if (l == 63) sm.la2[kC] = lk;
-            } else {
-                float mk = keep, mc = et_l * wave_scan_mul(be_l);
-                wave_scan_affine(mk, mc);  // affine maps x -> keep_t x + eta_t p_t, composed
-                sm.b[l] = lane_prev(mc, 0.f);
-                sm.et[l] = et_l;
-                sm.omb[l] = 1.f - be_l;
-                if (l == 63) sm.b[kC] = mc;
-            }
+            const int xb = opq(rc * kLd + cl0);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                *reinterpret_cast<bf16x4*>(sm.cm + xb + 4 * q4) = half4(cpre[q4 >> 1], q4 & 1);
+            if (tid <= kC) *reinterpret_cast<f32x4*>(sm.a + 4 * tid) = vpre;  // a|b|cc|w|tail
         }
         bf16x8 vr[2];
         {
@@ -291,69 +381,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
         }
         __syncthreads();  // B1
 
-        // ================= P1: coefficients; key forward and O partials
-        // c_{t,j} = sum_{j<=i<t} L1[t][i] L2[i][j] with
-        //   L1[t][i] = prod_{i<m<t} (1 - alpha_m),  L2[i][j] = eta_i (1 - beta_j) prod_{j<m<=i} beta_m,
-        // every entry an exp2 of a difference of log2 prefix sums, the sum one bf16 MFMA
-        // product; row C of L1 gives the chunk-end row c_C.
-        __bf16* l1m = sm.e2t;   // L1 [t][i]
-        __bf16* l2t = sm.e2c;   // L2^T [j][i]
-        __bf16* l1c = sm.e2w;   // row 0: L1[C][i] (rows 1..15 unused)
-        {
-            const int xb = opq(rc * kLd + cl0);
-            const float lat = sm.la2[rc], lbj = sm.lb2[rc], ombj = sm.omb[rc];
-            bf16x8 v1[2], v2[2];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 la = *reinterpret_cast<const f32x4*>(sm.la2i + cl0 + 4 * q4);
-                const f32x4 lbv = *reinterpret_cast<const f32x4*>(sm.lb2 + cl0 + 4 * q4);
-                const f32x4 etv = *reinterpret_cast<const f32x4*>(sm.et + cl0 + 4 * q4);
-#pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const int i = cl0 + 4 * q4 + e4;
-                    // out-of-triangle exponents may be +inf; the select discards them
-                    const float x1 = __builtin_amdgcn_exp2f(lat - la[e4]);
-                    const float x2 = etv[e4] * __builtin_amdgcn_exp2f(lbv[e4] - lbj) * ombj;
-                    v1[q4 >> 1][(q4 & 1) * 4 + e4] = (__bf16)(i < rc ? x1 : 0.f);
-                    v2[q4 >> 1][(q4 & 1) * 4 + e4] = (__bf16)(i >= rc ? x2 : 0.f);
-                }
-            }
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                *reinterpret_cast<bf16x8*>(l1m + xb + 8 * q) = v1[q];
-                *reinterpret_cast<bf16x8*>(l2t + xb + 8 * q) = v2[q];
-            }
-            if (wv == 0) {
-                l1c[l] = (__bf16)__builtin_amdgcn_exp2f(sm.la2[kC] - sm.la2i[l]);
-                sm.w[l] = sm.omb[l] * __builtin_amdgcn_exp2f(sm.lb2[kC - 1] - sm.lb2[l]);
-            }
-        }
-        __syncthreads();  // B1b
-        {
-            // Cm^T[j][t] = sum_i L2^T[j][i] L1^T[i][t]: wave w owns column tile t in 16w..16w+15
-            const int rb = opq(j * kLd + 4 * g);
-            const __bf16* l2r = l2t + rb;
-            const __bf16* l1r = l1m + rb;
-            __bf16* cmw = sm.cm + rb + 16 * wv * kLd;
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
-                f32x4 x = zero4();
-                if (jt <= wv) {
-                    x = mfma(frag(l2r, fo(jt, 0)), frag(l1r, fo(wv, 0)), x);
-                    x = mfma(frag(l2r, fo(jt, 1)), frag(l1r, fo(wv, 1)), x);
-                }
-                *reinterpret_cast<bf16x4*>(cmw + 16 * jt) = bf4(x);
-            }
-            if (wv == 0) {
-                const __bf16* l1cr = l1c + rb;
-#pragma unroll
-                for (int jt = 0; jt < 4; ++jt) {
-                    f32x4 x = mfma(frag(l2r, fo(jt, 0)), frag(l1cr, 0), zero4());
-                    x = mfma(frag(l2r, fo(jt, 1)), frag(l1cr, 32), x);
-                    if (j == 0) *reinterpret_cast<f32x4*>(sm.cc + 16 * jt + 4 * g) = x;
-                }
-            }
-        }
+        // ================= P1: key forward and O partials
         // Z = K W1^T (rows c, cols h) for this wave's 32 hidden units; Hk^T (rows h, cols c)
         // by an exact MFMA against the identity (D = A [I; 0] is the transpose of A's first
         // 16 x 16 tile when A is an accumulator tile in registers)
@@ -667,7 +695,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
         __syncthreads();  // B7: the Y slots are read before the next chunk reuses them
         if (c0 + kC < A.T) prefetch(c0 + kC);
         {
-            const float aC = sm.a[kC], bC = sm.b[kC], pC = sm.p;
+            const float aC = sm.tail[0], bC = sm.tail[1], pC = sm.tail[2];
             const int rb = opq(j * kLd + 4 * g);
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
@@ -741,6 +769,7 @@ __global__ void clear_pair_flags(char* ws, int64_t npairs) {
 }
 
 int64_t padded_pairs(const ScanArgs& a) { return (a.B * a.H + 7) / 8 * 8; }
+int64_t num_chunks(const ScanArgs& a) { return (a.T + kC - 1) / kC; }
 
 }  // namespace
 
@@ -750,7 +779,8 @@ bool scan_pair_supported(const ScanArgs& a) {
 }
 
 size_t scan_pair_workspace_bytes(const ScanArgs& a) {
-    return (size_t)padded_pairs(a) * (size_t)kPairBytes;
+    return (size_t)padded_pairs(a) * (size_t)kPairBytes +
+           (size_t)(a.B * a.H) * (size_t)num_chunks(a) * (size_t)kCoefBytes;
 }
 
 int64_t scan_pair_workgroups(const ScanArgs& a) { return 2 * padded_pairs(a); }
@@ -762,6 +792,16 @@ hipError_t launch_scan_pair(const ScanArgs& a, hipStream_t stream) {
     clear_pair_flags<<<dim3((unsigned)npairs), 256, 0, stream>>>(ws, npairs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const int64_t nchunks = num_chunks(a);
+    const int64_t ntasks = a.B * a.H * nchunks;
+    if (ntasks > 0) {
+        const int64_t blocks = (ntasks + kWaves - 1) / kWaves;
+        if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+        pair_coef_kernel<<<dim3((unsigned)blocks), kThreads, 0, stream>>>(
+            a, ws + npairs * kPairBytes, nchunks);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     ScanArgs args = a;
     void* kargs[] = {&args};
     return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&scan_pair_kernel),

@@ -58,11 +58,13 @@ def _desc(B=2, T=64, H=4, d=64, C=64, io=1):
 def test_workspace_size_query(monkeypatch):
     mlp = tm.mlp_desc((64, 256, 64))
     # the fused shape (64-256-64, C=64, bf16) runs on pairs of workgroups that exchange
-    # partial sums through the workspace: one 97 KiB area per pair, pairs padded to 8
+    # partial sums through the workspace (one 97 KiB area per pair, pairs padded to 8),
+    # after a pass that writes every chunk's gate coefficients (9472 bytes per chunk)
     assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc()), ctypes.byref(mlp)) == b"fused_pair"
-    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc()), ctypes.byref(mlp)) == 8 * 99328
-    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(B=3, H=3)),
-                                                 ctypes.byref(mlp)) == 16 * 99328
+    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc()),
+                                                 ctypes.byref(mlp)) == 8 * 99328 + 8 * 1 * 9472
+    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(B=3, T=130, H=3)),
+                                                 ctypes.byref(mlp)) == 16 * 99328 + 9 * 3 * 9472
     # more memories than pairs of compute units: one workgroup per memory, no workspace
     big = _desc(B=64, H=16)
     assert tm.lib.titans_mem_scan_path(ctypes.byref(big), ctypes.byref(mlp)) == b"fused_mfma"
