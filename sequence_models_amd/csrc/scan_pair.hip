@@ -368,6 +368,8 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 *reinterpret_cast<bf16x4*>(sm.cm + xb + 4 * q4) = half4(cpre[q4 >> 1], q4 & 1);
             if (tid <= kC) *reinterpret_cast<f32x4*>(sm.a + 4 * tid) = vpre;  // a|b|cc|w|tail
         }
+        // the next chunk's K, Q and coefficients load during this whole chunk
+        if (c0 + kC < A.T) prefetch(c0 + kC);
         bf16x8 vr[2];
         {
             const int64_t t = c0 + rc;
@@ -445,21 +447,31 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                     *p = Ot[dt][ct] + *p;
                 }
         }
+        // waves 0, 1 (after their O adds): diag(a) Q and -diag(b) Q; waves 2, 3: the
+        // transposed K copies.  Each of the 128 threads takes row u / 2, columns 32 (u % 2)..
         {
-            const float ar = sm.a[rc], br = -sm.b[rc];
-            const float ccr = -sm.cc[rc], wr = sm.w[rc];
-            const int xb = opq(rc * kLd + cl0), xt = opq(cl0 * kLd + rc);
+            const int u = tid & 127, row = u >> 1, c32 = 32 * (u & 1);
+            if (wv < 2) {
+                const float ar = sm.a[row], br = -sm.b[row];
+                const int xb = opq(row * kLd + c32);
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 qv = f4(*reinterpret_cast<const bf16x4*>(sm.qq + xb + 4 * q4));
-                *reinterpret_cast<bf16x4*>(sm.qa + xb + 4 * q4) = bf4(qv * ar);
-                *reinterpret_cast<bf16x4*>(sm.qb + xb + 4 * q4) = bf4(qv * br);
-                const f32x4 kv = f4(*reinterpret_cast<const bf16x4*>(sm.kk + xb + 4 * q4));
-                const bf16x4 kc4 = bf4(kv * ccr), kw4 = bf4(kv * wr);
+                for (int q4 = 0; q4 < 8; ++q4) {
+                    const f32x4 qv = f4(*reinterpret_cast<const bf16x4*>(sm.qq + xb + 4 * q4));
+                    *reinterpret_cast<bf16x4*>(sm.qa + xb + 4 * q4) = bf4(qv * ar);
+                    *reinterpret_cast<bf16x4*>(sm.qb + xb + 4 * q4) = bf4(qv * br);
+                }
+            } else {
+                const float ccr = -sm.cc[row], wr = sm.w[row];
+                const int xb = opq(row * kLd + c32), xt = opq(c32 * kLd + row);
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    sm.kc[xt + (4 * q4 + e4) * kLd] = kc4[e4];
-                    sm.kw[xt + (4 * q4 + e4) * kLd] = kw4[e4];
+                for (int q4 = 0; q4 < 8; ++q4) {
+                    const f32x4 kv = f4(*reinterpret_cast<const bf16x4*>(sm.kk + xb + 4 * q4));
+                    const bf16x4 kc4 = bf4(kv * ccr), kw4 = bf4(kv * wr);
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4) {
+                        sm.kc[xt + (4 * q4 + e4) * kLd] = kc4[e4];
+                        sm.kw[xt + (4 * q4 + e4) * kLd] = kw4[e4];
+                    }
                 }
             }
         }
@@ -519,9 +531,23 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                     zq = mfma(as0, frag(qbr, fo(ct, 0)), zq);
                     zqp[ht][ct] = mfma(as1, frag(qbr, fo(ct, 1)), zq);
                 }
+                // the O words went out before Mq: they have landed by now; the partner's
+                // flag then travels while this wave finishes its state terms
+                if (ht == 0) post_flag(myflag, e, l);
             }
         }
-        post_flag(myflag, e, l);
+        {
+            // W1 and S1 are not read again before the carry: apply its rescale now
+            // (a_C W1 - b_C S1, p S1; the carry's products add onto these)
+            const float aC = sm.tail[0], bC = sm.tail[1], pC = sm.tail[2];
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int ht = 0; ht < kHt; ++ht) {
+                    W1T[dt][ht] = aC * W1T[dt][ht] - bC * S1T[dt][ht];
+                    S1T[dt][ht] = pC * S1T[dt][ht];
+                }
+        }
         wait_flag(otflag, e, bad);
         if (e > 1) {
             // the partner's partial of this side's y rows of the previous chunk
@@ -693,7 +719,6 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             for (int i = 0; i < 4; ++i) xstore(dst + i * kThreads, pack2(ys[1][2 * i], ys[1][2 * i + 1]));
         }
         __syncthreads();  // B7: the Y slots are read before the next chunk reuses them
-        if (c0 + kC < A.T) prefetch(c0 + kC);
         {
             const float aC = sm.tail[0], bC = sm.tail[1], pC = sm.tail[2];
             const int rb = opq(j * kLd + 4 * g);
@@ -713,11 +738,10 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                     const bf16x8 bd1 = cat(D1[2][ht], D1[3][ht]);
                     const bf16x8 ah0 = cat(Hk[0][ht], Hk[1][ht]);  // A: Hk^T [h][c]
                     const bf16x8 ah1 = cat(Hk[2][ht], Hk[3][ht]);
-                    // chunk-end rescale (a_C W - b_C S, p S) fused into the accumulator input
-                    const f32x4 tw1 = aC * W1T[dt][ht] - bC * S1T[dt][ht];
-                    const f32x4 ts1 = pC * S1T[dt][ht];
-                    W1T[dt][ht] = mfma(kc1, bd1, mfma(kc0, bd0, tw1));
-                    S1T[dt][ht] = mfma(kw1, bd1, mfma(kw0, bd0, ts1));
+                    // W1 and S1 were rescaled before the exchange wait; W2, S2 here
+                    // (a_C W - b_C S, p S fused into the accumulator input)
+                    W1T[dt][ht] = mfma(kc1, bd1, mfma(kc0, bd0, W1T[dt][ht]));
+                    S1T[dt][ht] = mfma(kw1, bd1, mfma(kw0, bd0, S1T[dt][ht]));
                     const f32x4 tw2 = aC * W2T[ht][dt] - bC * S2T[ht][dt];
                     const f32x4 ts2 = pC * S2T[ht][dt];
                     W2T[ht][dt] = mfma(ah1, ec1, mfma(ah0, ec0, tw2));
