@@ -99,8 +99,8 @@ __device__ __forceinline__ void wait_flag(int* flag, int e, bool& bad) {
 
 struct __attribute__((aligned(16))) Smem {
     // Regions are reused within a chunk; the comment gives each region's lives in order.
-    float r[2][kMat];          // O partials (pairwise reduction) -> the waves' bf16 W2 slices
-                               //   -> Y partial slots 0, 1   ([c][dd] fp32)
+    float r[2][kMat];          // O partials (pairwise reduction) -> Y partial slots 0, 1
+                               //   ([c][dd] fp32)
     __bf16 qa[kMat];           // diag(a) Q [c][d]              } Y partial slot 2
     __bf16 qb[kMat];           // -diag(b) Q [c][d]             }
     __bf16 mq[kMat];           // -(Cm o Q K^T) [c][c']         } Y partial slot 3
@@ -590,30 +590,22 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
         __syncthreads();  // B4
 
         // ================= P4: backward, reads at the in-chunk weights
-        // this wave's W2 slice as bf16 [h][dd] (B operand of G = E2 W2)
-        __bf16* w2c = reinterpret_cast<__bf16*>(&sm.r[0][0]) + wv * kMat;
+        // G = E2 W2 (rows c, cols h); D1 = G o SiLU'(Z).  The B operand W2 [dd][h] is the
+        // transpose of the state tiles W2T [h][dd]: one exact identity MFMA per tile.
+        bf16x4 D1[4][kHt];
         {
-            __bf16* w2w = w2c + opq(4 * g * kLd + j);
+            bf16x4 W2n[4][kHt];  // rows dd = 16 dt + 4g + r, cols h = 16 ht + j
 #pragma unroll
             for (int ht = 0; ht < kHt; ++ht)
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const bf16x4 v = bf4(opaque(W2T[ht][dt]));
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) w2w[(16 * ht + r) * kLd + 16 * dt] = v[r];
-                }
-        }
-        wave_lds_sync();
-        // G = E2 W2 (rows c, cols h); D1 = G o SiLU'(Z)
-        bf16x4 D1[4][kHt];
-        {
+                for (int dt = 0; dt < 4; ++dt)
+                    W2n[dt][ht] = bf4(mfma(cat(bf4(W2T[ht][dt]), bf16x4{}), eye, zero4()));
             const int rb = opq(j * kLd + 4 * g);
-            const __bf16* w2r = w2c + rb;
             const __bf16* er = sm.e2l + rb;
 #pragma unroll
             for (int ht = 0; ht < kHt; ++ht) {
-                const bf16x8 b0 = frag(w2r, fo(ht, 0));
-                const bf16x8 b1 = frag(w2r, fo(ht, 1));
+                const bf16x8 b0 = cat(W2n[0][ht], W2n[1][ht]);
+                const bf16x8 b1 = cat(W2n[2][ht], W2n[3][ht]);
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
                     f32x4 gg = mfma(frag(er, fo(ct, 0)), b0, zero4());
@@ -622,11 +614,18 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 }
             }
         }
-        // Zq^T += D1^T Mq^T; Hq = SiLU(Zq)
-        bf16x4 Hq[kHt][4];
+        // Zq^T += D1^T Mq^T; Hq = SiLU(Zq), also scaled by a_c and -b_c (its column c is
+        // token c) for the W2 / S2 terms of Y
+        bf16x4 Hq[kHt][4], Hqa[kHt][4], Hqb[kHt][4];
         {
             const int rb = opq(j * kLd + 4 * g);
             const __bf16* mqr = sm.mq + rb;
+            float ac[4], nbc[4];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                ac[ct] = sm.a[16 * ct + j];
+                nbc[ct] = -sm.b[16 * ct + j];
+            }
 #pragma unroll
             for (int ht = 0; ht < kHt; ++ht) {
                 const bf16x8 ad0 = cat(D1[0][ht], D1[1][ht]);
@@ -639,11 +638,13 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) hq[r] = zq[r] * sigmoid(zq[r]);
                     Hq[ht][ct] = bf4(hq);
+                    Hqa[ht][ct] = bf4(hq * ac[ct]);
+                    Hqb[ht][ct] = bf4(hq * nbc[ct]);
                 }
             }
         }
-        __syncthreads();  // B5: Q, Mq, E2 [c][dd] and the W2 slices are dead -> Y slots
-        // Y^T (rows dd, cols c) = a_c (W2 Hq^T) - b_c (S2 Hq^T) + E2^T Pm^T over this wave's
+        __syncthreads();  // B5: Q, Mq and E2 [c][dd] are dead -> Y slots
+        // Y^T (rows dd, cols c) = W2 (a_c Hq)^T + S2 (-b_c Hq)^T + E2^T Pm^T over this wave's
         // hidden units, Pm^T[c'][c] = -c_{c,c'} (Hk Hq^T)[c'][c]; each wave stores its
         // partial in its slot
         {
@@ -669,12 +670,6 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             }
             float* slot = yslot(sm, wv) + rb;
             const __bf16* etr = sm.e2t + rb;
-            float ac[4], bc[4];
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                ac[ct] = sm.a[16 * ct + j];
-                bc[ct] = sm.b[16 * ct + j];
-            }
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
                 const bf16x8 aw = state_frag(W2T[0][dt], W2T[1][dt]);
@@ -683,10 +678,8 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 const bf16x8 e1 = frag(etr, fo(dt, 1));
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
-                    const bf16x8 bq = cat(Hq[0][ct], Hq[1][ct]);
-                    const f32x4 u1 = mfma(aw, bq, zero4());
-                    const f32x4 u2 = mfma(as, bq, zero4());
-                    f32x4 yt = ac[ct] * u1 - bc[ct] * u2;
+                    f32x4 yt = mfma(aw, cat(Hqa[0][ct], Hqa[1][ct]), zero4());
+                    yt = mfma(as, cat(Hqb[0][ct], Hqb[1][ct]), yt);
                     yt = mfma(e0, cat(pm[ct][0], pm[ct][1]), yt);
                     if (ct >= 2) yt = mfma(e1, cat(pm[ct][2], pm[ct][3]), yt);
                     *reinterpret_cast<f32x4*>(slot + 16 * ct * kLd + 16 * dt) = yt;
