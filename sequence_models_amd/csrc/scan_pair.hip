@@ -347,29 +347,28 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
         }
         if (t < A.T) *reinterpret_cast<bf16x8*>(yg + ybase + t * A.ys[1] + yd0) = out;
     };
+    // the prefetched chunk's K, Q, Cm and coefficient vectors into LDS
+    auto commit = [&]() {
+        const int xb = opq(rc * kLd + cl0);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            *reinterpret_cast<bf16x4*>(sm.kk + xb + 4 * q4) = half4(kpre[q4 >> 1], q4 & 1);
+            *reinterpret_cast<bf16x4*>(sm.qq + xb + 4 * q4) = half4(qpre[q4 >> 1], q4 & 1);
+            *reinterpret_cast<bf16x4*>(sm.cm + xb + 4 * q4) = half4(cpre[q4 >> 1], q4 & 1);
+        }
+        if (tid <= kC) *reinterpret_cast<f32x4*>(sm.a + 4 * tid) = vpre;  // a|b|cc|w|tail
+    };
+    // Chunk n+1's data is committed to LDS at the end of chunk n (after its last reads of
+    // those regions) and chunk n+2's loads are issued right after, so a whole chunk of
+    // work covers them and no wait for them ever lands behind the exchange stores.
     prefetch(0);
+    commit();
+    if (kC < A.T) prefetch(kC);
 
     int e = 0;  // exchange number of the current chunk (1, 2, ...)
     for (int64_t c0 = 0; c0 < A.T; c0 += kC) {
         ++e;
-        // ================= P0: commit the prefetched chunk; load V
-        {
-            const int xb = opq(rc * kLd + cl0);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                *reinterpret_cast<bf16x4*>(sm.kk + xb + 4 * q4) = half4(kpre[q4 >> 1], q4 & 1);
-                *reinterpret_cast<bf16x4*>(sm.qq + xb + 4 * q4) = half4(qpre[q4 >> 1], q4 & 1);
-            }
-        }
-        {
-            const int xb = opq(rc * kLd + cl0);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                *reinterpret_cast<bf16x4*>(sm.cm + xb + 4 * q4) = half4(cpre[q4 >> 1], q4 & 1);
-            if (tid <= kC) *reinterpret_cast<f32x4*>(sm.a + 4 * tid) = vpre;  // a|b|cc|w|tail
-        }
-        // the next chunk's K, Q and coefficients load during this whole chunk
-        if (c0 + kC < A.T) prefetch(c0 + kC);
+        // ================= P0: load V
         bf16x8 vr[2];
         {
             const int64_t t = c0 + rc;
@@ -512,6 +511,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 *reinterpret_cast<bf16x4*>(mqw + 16 * ctp) = bf4(x);
             }
         }
+        const float aC = sm.tail[0], bC = sm.tail[1], pC = sm.tail[2];  // chunk-end factors
         // Zq^T state terms (rows h, cols c): W1 (diag(a) Q)^T + S1 (-diag(b) Q)^T
         f32x4 zqp[kHt][4];
         {
@@ -539,7 +539,6 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
         {
             // W1 and S1 are not read again before the carry: apply its rescale now
             // (a_C W1 - b_C S1, p S1; the carry's products add onto these)
-            const float aC = sm.tail[0], bC = sm.tail[1], pC = sm.tail[2];
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -549,20 +548,19 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 }
         }
         wait_flag(otflag, e, bad);
-        if (e > 1) {
-            // the partner's partial of this side's y rows of the previous chunk
-            uint64_t px[4];
-            const uint64_t* src = yxslot(e - 1, 1 - side);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) px[i] = xload(const_cast<uint64_t*>(src + i * kThreads));
-            write_y(c0 - kC, px);
-        }
         {
-            // E2 = 2 (O - V), O = O_side0 + O_side1, in its four layouts
-            uint64_t po[8];
+            // the partner's O partial of this chunk and its partial of this side's y rows of
+            // the previous chunk, all loads issued together (one round trip)
+            uint64_t po[8], px[4];
             const uint64_t* src = oslot(e, 1 - side);
 #pragma unroll
             for (int i = 0; i < 8; ++i) po[i] = xload(const_cast<uint64_t*>(src + i * kThreads));
+            if (e > 1) {
+                const uint64_t* srcy = yxslot(e - 1, 1 - side);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) px[i] = xload(const_cast<uint64_t*>(srcy + i * kThreads));
+            }
+            // E2 = 2 (O - V), O = O_side0 + O_side1, in its four layouts
             const int xb = opq(rc * kLd + cl0), xt = opq(cl0 * kLd + rc);
             const float ccr = -sm.cc[rc], wr = sm.w[rc];
 #pragma unroll
@@ -586,6 +584,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                     sm.e2w[o2] = ew[ee];
                 }
             }
+            if (e > 1) write_y(c0 - kC, px);
         }
         __syncthreads();  // B4
 
@@ -711,9 +710,12 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) xstore(dst + i * kThreads, pack2(ys[1][2 * i], ys[1][2 * i + 1]));
         }
-        __syncthreads();  // B7: the Y slots are read before the next chunk reuses them
+        __syncthreads();  // B7: the Y slots, K, Q, Cm and the vectors are no longer read
+        if (c0 + kC < A.T) {
+            commit();
+            if (c0 + 2 * kC < A.T) prefetch(c0 + 2 * kC);
+        }
         {
-            const float aC = sm.tail[0], bC = sm.tail[1], pC = sm.tail[2];
             const int rb = opq(j * kLd + 4 * g);
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
