@@ -10,9 +10,11 @@
 //
 // Per chunk the algebra is that of the single-workgroup kernel (the unrolled momentum /
 // forget-gated write rule of the Titans pages with gradients frozen at the chunk start,
-// each gradient an outer product delta h^T).  Everything that depends only on the chunk's
-// tokens and gates (coefficients, scaled Q / K copies, Cm o Q K^T, E2 layouts) is computed
-// by both sides; everything that is a sum over hidden units is computed per side:
+// each gradient an outer product delta h^T).  What depends on the gates only (the
+// coefficient vectors and Cm) comes from a pass over all chunks before the scan
+// (pair_coef_kernel); the rest that does not depend on the hidden units (scaled Q / K
+// copies, Cm o Q K^T, E2 layouts) is formed by both sides; every sum over hidden units
+// is computed per side:
 //   O = Hk W2^T      both sides need the full O for E2 = 2 (O - V): each side posts its
 //                    partial (64 x 64 fp32) to the partner and adds the partner's;
 //   Y                each side writes y for its half of the chunk's tokens (side s: rows
@@ -22,18 +24,20 @@
 // is commutative), so both sides hold bitwise the same E2 and the result is
 // reproducible.
 //
-// Exchange protocol.  The two workgroups of a pair are blockIdx i and i ^ 8, which the
-// dispatcher places on the same XCD (its L2 is then the meeting point).  Every word of
-// the exchange area is written and read only with agent-scope relaxed atomics (per
-// instruction coherent loads / stores, no L2 writeback or invalidate): thread t of wave
-// w writes its own words, the wave waits for its stores to complete (s_waitcnt
-// vmcnt(0)), then lane 0 stores the wave's flag = exchange number e.  The partner's
-// wave w polls that flag (bounded), then thread t reads exactly the words the partner's
-// thread t wrote.  O and Y areas are double-buffered by the parity of e; a wave posts
-// e + 1 only after its reads of exchange e have returned, which is what lets the partner
-// reuse a buffer two exchanges later.  The launch is cooperative, so both workgroups of
-// a pair are resident together.  A wait that exceeds its bound (never expected) stops
-// all further waits of that wave and the memory's theta_T and s_T come out as NaN.
+// Exchange protocol.  The two workgroups of a pair are blockIdx i and i ^ 8 (the
+// dispatcher places both on one XCD).  Every word of the exchange area is written and
+// read only with agent-scope relaxed atomics: per-instruction coherent loads and stores
+// that meet beyond the per-XCD L2s, so no L2 writeback or invalidate is ever issued.
+// Thread t of wave w writes its own words, the wave waits for its stores to complete
+// (s_waitcnt vmcnt(0)), then lane 0 stores the wave's flag = exchange number e.  The
+// partner's wave w polls that flag (bounded), then thread t reads exactly the words the
+// partner's thread t wrote.  Exchange e (one per chunk, plus one after the last) carries
+// chunk e's O partial and chunk e-1's y partial.  O and Y areas are double-buffered by
+// the parity of the chunk; a wave posts e + 1 only after its reads of exchange e have
+// returned, which is what lets the partner reuse a buffer two exchanges later.  The
+// launch is cooperative, so both workgroups of a pair are resident together.  A wait that
+// exceeds its bound (never expected) stops all further waits of that wave and the
+// memory's theta_T and s_T come out as NaN.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
