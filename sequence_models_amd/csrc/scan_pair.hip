@@ -152,12 +152,43 @@ constexpr int64_t kCoefCm = kC * kC * 2;
 constexpr int64_t kCoefBytes = kCoefCm + 5 * kC * 4;
 static_assert(kCoefBytes % 256 == 0, "records stay 256-byte aligned");
 
-struct __attribute__((aligned(16))) CoefSmem {  // one wave's scratch
-    __bf16 l1[kMat];        // L1 [t][i]
-    __bf16 l2t[kMat];       // L2^T [j][i]
-    __bf16 l1c[16 * kLd];   // row 0: L1[C][i]; rows 1..15 only keep fragment reads in bounds
-    float la2i[kC], lb2[kC], et[kC];
+struct __attribute__((aligned(16))) CoefSmem {  // one wave's per-token vectors
+    float la2i[kC];  // sum_{m<=t} log2(1 - alpha_m)
+    float la2x[kC];  // sum_{m<t} log2(1 - alpha_m)
+    float lb2[kC];   // sum_{m<=t} log2(beta_m)
+    float et[kC];    // eta_t
+    float omb[kC];   // 1 - beta_t
 };
+
+// L1 / L2 entries are formed directly in the MFMA operand layout: lane (g, j) holds, for
+// reduction block kb, the eight entries with i = 32 kb + {4g .. 4g+3, 16+4g .. 16+4g+3}.
+__device__ __forceinline__ bf16x8 l1_frag(const CoefSmem& cs, float la2t, int t, int kb, int g) {
+    bf16x8 f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int i0 = 32 * kb + 16 * h + 4 * g;
+        const f32x4 li = *reinterpret_cast<const f32x4*>(cs.la2i + i0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)  // out-of-triangle exponents may be +inf: discarded
+            f[4 * h + v] = (__bf16)(i0 + v < t ? __builtin_amdgcn_exp2f(la2t - li[v]) : 0.f);
+    }
+    return f;
+}
+__device__ __forceinline__ bf16x8 l2_frag(const CoefSmem& cs, float lbj, float ombj, int jr, int kb,
+                                          int g) {
+    bf16x8 f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int i0 = 32 * kb + 16 * h + 4 * g;
+        const f32x4 lb = *reinterpret_cast<const f32x4*>(cs.lb2 + i0);
+        const f32x4 et = *reinterpret_cast<const f32x4*>(cs.et + i0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            f[4 * h + v] =
+                (__bf16)(i0 + v >= jr ? et[v] * __builtin_amdgcn_exp2f(lb[v] - lbj) * ombj : 0.f);
+    }
+    return f;
+}
 
 __global__ void __launch_bounds__(kThreads) pair_coef_kernel(ScanArgs A, char* coef, int64_t nchunks) {
     __shared__ CoefSmem csm[kWaves];
@@ -185,13 +216,13 @@ __global__ void __launch_bounds__(kThreads) pair_coef_kernel(ScanArgs A, char* c
     const float lb = wave_scan_add(be_l > 0.f ? __log2f(be_l) : -1024.f);
     float mk = keep, mc = et_l * pbl;        // affine maps x -> keep_t x + eta_t p_t, composed
     wave_scan_affine(mk, mc);
-    const float la2 = lane_prev(lk, 0.f);    // sum_{m<l} log2(1 - alpha_m)
     const float la2C = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lk), 63));
     const float lbL = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lb), 63));
     cs.la2i[l] = lk;
+    cs.la2x[l] = lane_prev(lk, 0.f);
     cs.lb2[l] = lb;
     cs.et[l] = et_l;
-    cs.l1c[l] = (__bf16)__builtin_amdgcn_exp2f(la2C - lk);
+    cs.omb[l] = 1.f - be_l;
     rv[l] = lane_prev(pa, 1.f);                                            // a_l
     rv[kC + l] = lane_prev(mc, 0.f);                                       // b_l
     rv[3 * kC + l] = (1.f - be_l) * __builtin_amdgcn_exp2f(lbL - lb);      // w_l
@@ -202,53 +233,38 @@ __global__ void __launch_bounds__(kThreads) pair_coef_kernel(ScanArgs A, char* c
         rv[4 * kC + 3] = 0.f;
     }
     wave_lds_sync();
-    {
-        // lane r writes row r of L1 (t = r) and of L2^T (j = r)
-        const float omb = 1.f - be_l;
-        __bf16* r1 = cs.l1 + l * kLd;
-        __bf16* r2 = cs.l2t + l * kLd;
-#pragma unroll 4
-        for (int i4 = 0; i4 < kC / 4; ++i4) {
-            const f32x4 li = *reinterpret_cast<const f32x4*>(cs.la2i + 4 * i4);
-            const f32x4 bi4 = *reinterpret_cast<const f32x4*>(cs.lb2 + 4 * i4);
-            const f32x4 ei = *reinterpret_cast<const f32x4*>(cs.et + 4 * i4);
-            f32x4 x1, x2;
+    // Cm^T[j][t] = sum_i L2^T[j][i] L1^T[i][t], tiles (j-block jt, t-block tb), jt <= tb;
+    // c_C[j] = sum_i L2^T[j][i] L1[C][i] with L1[C][i] broadcast to every column
+    bf16x8 l2f[4][2];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * i4 + e;
-                // out-of-triangle exponents may be +inf; the select discards them
-                const float v1 = __builtin_amdgcn_exp2f(la2 - li[e]);
-                const float v2 = ei[e] * __builtin_amdgcn_exp2f(bi4[e] - lb) * omb;
-                x1[e] = i < l ? v1 : 0.f;
-                x2[e] = i >= l ? v2 : 0.f;
-            }
-            *reinterpret_cast<bf16x4*>(r1 + 4 * i4) = bf4(x1);
-            *reinterpret_cast<bf16x4*>(r2 + 4 * i4) = bf4(x2);
-        }
+    for (int jt = 0; jt < 4; ++jt) {
+        const int jr = 16 * jt + j;
+        const float lbj = cs.lb2[jr], ombj = cs.omb[jr];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) l2f[jt][kb] = l2_frag(cs, lbj, ombj, jr, kb, g);
     }
-    wave_lds_sync();
-    {
-        // Cm^T[j][t] = sum_i L2^T[j][i] L1^T[i][t], tiles (j-block jt, t-block tb), jt <= tb
-        const int rb = j * kLd + 4 * g;
-        const __bf16* l2r = cs.l2t + rb;
-        const __bf16* l1r = cs.l1 + rb;
-        __bf16* cmg = reinterpret_cast<__bf16*>(rec);
+    __bf16* cmg = reinterpret_cast<__bf16*>(rec);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
-                f32x4 x = zero4();
-                if (jt <= tb) {
-                    x = mfma(frag(l2r, fo(jt, 0)), frag(l1r, fo(tb, 0)), x);
-                    x = mfma(frag(l2r, fo(jt, 1)), frag(l1r, fo(tb, 1)), x);
-                }
-                *reinterpret_cast<bf16x4*>(cmg + (16 * tb + j) * kC + 16 * jt + 4 * g) = bf4(x);
-            }
-        const __bf16* l1cr = cs.l1c + rb;
+    for (int tb = 0; tb < 4; ++tb) {
+        const int tr = 16 * tb + j;
+        const float la2t = cs.la2x[tr];
+        const bf16x8 b0 = l1_frag(cs, la2t, tr, 0, g), b1 = l1_frag(cs, la2t, tr, 1, g);
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-            f32x4 x = mfma(frag(l2r, fo(jt, 0)), frag(l1cr, 0), zero4());
-            x = mfma(frag(l2r, fo(jt, 1)), frag(l1cr, 32), x);
+            f32x4 x = zero4();
+            if (jt <= tb) {
+                x = mfma(l2f[jt][0], b0, x);
+                x = mfma(l2f[jt][1], b1, x);
+            }
+            *reinterpret_cast<bf16x4*>(cmg + tr * kC + 16 * jt + 4 * g) = bf4(x);
+        }
+    }
+    {
+        const bf16x8 c0 = l1_frag(cs, la2C, kC, 0, g), c1 = l1_frag(cs, la2C, kC, 1, g);
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            f32x4 x = mfma(l2f[jt][0], c0, zero4());
+            x = mfma(l2f[jt][1], c1, x);
             if (j == 0) *reinterpret_cast<f32x4*>(rv + 2 * kC + 16 * jt + 4 * g) = x;  // c_C
         }
     }
