@@ -78,6 +78,9 @@ def test_workspace_size_query(monkeypatch):
     assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=32)), ctypes.byref(mlp)) == b"generic_fp32"
     assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(io=0)), ctypes.byref(mlp)) == b"generic_fp32"
     assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=0)), ctypes.byref(mlp)) is None
+    assert tm.lib.titans_mem_retrieve_path(ctypes.byref(_desc()), ctypes.byref(mlp)) == b"fused_mfma"
+    assert tm.lib.titans_mem_retrieve_path(ctypes.byref(_desc(io=0)), ctypes.byref(mlp)) == b"generic_fp32"
+    assert tm.lib.titans_mem_retrieve_path(ctypes.byref(_desc()), ctypes.byref(tm.mlp_desc((64, 128, 64)))) == b"generic_fp32"
     assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(T=0)), ctypes.byref(mlp)) == 0
     bad = ctypes.c_size_t(-1).value
     assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(C=0)), ctypes.byref(mlp)) == bad
@@ -163,6 +166,24 @@ def test_validation_of_overlap_alignment_and_workspace():
     d3.state_stride[:] = (0, P)
     d3.state0_stride[:] = (0, P)
     assert _scan(d3, mlp, ptrs, end, need)[0] == INVALID
+
+
+@no_fake_pointers_on_gpu
+def test_pair_path_workspace_validation():
+    """The fused pair path needs its exchange area and coefficient records."""
+    mlp = tm.mlp_desc((64, 256, 64))
+    B, T, H, P = 2, 64, 4, 32768
+    desc = _desc(B, T, H)
+    desc.state_stride[:] = (H * P, P)
+    desc.state0_stride[:] = (0, P)
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(desc), ctypes.byref(mlp)) == b"fused_pair"
+    ptrs, end = _fake_ptrs()
+    need = tm.lib.titans_mem_scan_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+    assert need > 0
+    assert _scan(desc, mlp, ptrs, end, need - 1)[0] == WORKSPACE
+    assert _scan(desc, mlp, ptrs, None, 0)[0] == WORKSPACE
+    assert _scan(desc, mlp, ptrs, end + 128, need)[0] == INVALID  # not 256-byte aligned
+    assert _scan(desc, mlp, ptrs, ptrs["y"], need)[0] == INVALID  # overlaps y
 
 
 @no_fake_pointers_on_gpu

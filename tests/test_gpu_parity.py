@@ -456,6 +456,25 @@ def test_pair_kernel_matches_single_kernel(monkeypatch):
     assert ey <= 2e-2 and et <= 1e-1 and es <= 1e-1
 
 
+def test_fused_path_switch_at_the_compute_unit_limit(monkeypatch):
+    """More memories than pairs of compute units: the fused shape runs one workgroup per
+    memory (and still matches the oracle)."""
+    monkeypatch.delenv("TITANS_MEM_FUSED_SINGLE", raising=False)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    H = 8
+    B = cus // (2 * H) + 1  # 2 * ceil(B*H / 8) * 8 > cus
+    wl, inp = _small(widths=(64, 256, 64), B=B, T=130, H=H, C=64, io="bf16", seed=31)
+    dev = to_device(inp)
+    log(f"case fused path switch: B*H = {B * H} memories on {cus} compute units")
+    assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == "fused_mfma"
+    small = _small(widths=(64, 256, 64), B=B - 1, T=130, H=H, C=64, io="bf16", seed=31)[1]
+    assert tm.scan_path(to_device(small)["q"], wl.chunk, wl.widths) == "fused_pair"
+    y, thT, sT = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (B - 1, H - 1)]
+    check_pairs(wl, y, thT, sT, pairs, oracle_seq(inp, pairs))
+
+
 @pytest.mark.parametrize("sustained", [False, True])
 def test_headline_sampled_single_kernel(sustained, monkeypatch):
     """The single-workgroup kernel at the full headline shape (the pair kernel runs it by default)."""
