@@ -114,8 +114,6 @@ struct __attribute__((aligned(16))) Smem {
     __bf16 e2t[kMat];          // E2^T [dd][c]
     __bf16 e2c[kMat];          // -(diag(c_C) E2)^T [dd][c]
     __bf16 e2w[kMat];          // (diag(w) E2)^T [dd][c]
-    __bf16 kc[kMat];           // -(diag(c_C) K)^T [d][c]
-    __bf16 kw[kMat];           // (diag(w) K)^T    [d][c]
     __bf16 cm[kMat];           // c_{t,j}, t, j < 64 (rows t)
     float a[kC], b[kC], cc[kC], w[kC];  // one chunk's coefficient vectors
     float tail[4];                       // a_C, b_C, p (right after w: one copy fills all)
@@ -332,9 +330,14 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
     const int yrow_own = 32 * side + yr, yrow_oth = 32 * (1 - side) + yr;
     float yown[8];
 
-    bf16x8 eye;  // B = [I16; 0] in the MFMA k order: lane (g, j) slot v < 4 is row 4g + v
+    // B = [I16; 0] and [0; I16] in the MFMA k order (lane (g, j) slot v < 4 is row 4g + v of
+    // the block's first 16 rows, slot v >= 4 row 4g + v - 4 of its second 16)
+    bf16x8 eye, eye1;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) eye[v] = (__bf16)((v < 4 && 4 * g + v == j) ? 1.f : 0.f);
+    for (int v = 0; v < 8; ++v) {
+        eye[v] = (__bf16)((v < 4 && 4 * g + v == j) ? 1.f : 0.f);
+        eye1[v] = (__bf16)((v >= 4 && 4 * g + v - 4 == j) ? 1.f : 0.f);
+    }
 
     bf16x8 kpre[2], qpre[2], cpre[2];
     f32x4 vpre = zero4();
@@ -383,7 +386,6 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
     // work covers them and no wait for them ever lands behind the exchange stores.
     prefetch(0);
     commit();
-    if (kC < A.T) prefetch(kC);
 
     int e = 0;  // exchange number of the current chunk (1, 2, ...)
     for (int64_t c0 = 0; c0 < A.T; c0 += kC) {
@@ -455,43 +457,39 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
         }
         __syncthreads();  // B2: coefficients, O stage 1
 
-        // ================= P2: stage 2 of O; scaled Q and K copies
+        // ================= P2: stage 2 of O; scaled Q copies
         if (wv < 2) {
+            // all reads first, then all writes (the slot never aliases within itself; a
+            // read-add-write per tile would wait out one LDS round trip per tile)
             float* slot = sm.r[wv] + opq(j * kLd + 4 * g);
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
+            for (int half = 0; half < 2; ++half) {
+                f32x4 prev[2][4];
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) {
-                    f32x4* p = reinterpret_cast<f32x4*>(slot + 16 * ct * kLd + 16 * dt);
-                    *p = Ot[dt][ct] + *p;
-                }
+                for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+                        prev[d2][ct] = *reinterpret_cast<const f32x4*>(
+                            slot + 16 * ct * kLd + 16 * (2 * half + d2));
+                reload();
+#pragma unroll
+                for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+                        *reinterpret_cast<f32x4*>(slot + 16 * ct * kLd + 16 * (2 * half + d2)) =
+                            Ot[2 * half + d2][ct] + prev[d2][ct];
+            }
         }
-        // waves 0, 1 (after their O adds): diag(a) Q and -diag(b) Q; waves 2, 3: the
-        // transposed K copies.  Each of the 128 threads takes row u / 2, columns 32 (u % 2)..
-        {
+        // waves 2, 3 meanwhile: diag(a) Q and -diag(b) Q (thread u: row u / 2, 32 columns)
+        if (wv >= 2) {
             const int u = tid & 127, row = u >> 1, c32 = 32 * (u & 1);
-            if (wv < 2) {
-                const float ar = sm.a[row], br = -sm.b[row];
-                const int xb = opq(row * kLd + c32);
+            const float ar = sm.a[row], br = -sm.b[row];
+            const int xb = opq(row * kLd + c32);
 #pragma unroll
-                for (int q4 = 0; q4 < 8; ++q4) {
-                    const f32x4 qv = f4(*reinterpret_cast<const bf16x4*>(sm.qq + xb + 4 * q4));
-                    *reinterpret_cast<bf16x4*>(sm.qa + xb + 4 * q4) = bf4(qv * ar);
-                    *reinterpret_cast<bf16x4*>(sm.qb + xb + 4 * q4) = bf4(qv * br);
-                }
-            } else {
-                const float ccr = -sm.cc[row], wr = sm.w[row];
-                const int xb = opq(row * kLd + c32), xt = opq(c32 * kLd + row);
-#pragma unroll
-                for (int q4 = 0; q4 < 8; ++q4) {
-                    const f32x4 kv = f4(*reinterpret_cast<const bf16x4*>(sm.kk + xb + 4 * q4));
-                    const bf16x4 kc4 = bf4(kv * ccr), kw4 = bf4(kv * wr);
-#pragma unroll
-                    for (int e4 = 0; e4 < 4; ++e4) {
-                        sm.kc[xt + (4 * q4 + e4) * kLd] = kc4[e4];
-                        sm.kw[xt + (4 * q4 + e4) * kLd] = kw4[e4];
-                    }
-                }
+            for (int q4 = 0; q4 < 8; ++q4) {
+                const f32x4 qv = f4(*reinterpret_cast<const bf16x4*>(sm.qq + xb + 4 * q4));
+                *reinterpret_cast<bf16x4*>(sm.qa + xb + 4 * q4) = bf4(qv * ar);
+                *reinterpret_cast<bf16x4*>(sm.qb + xb + 4 * q4) = bf4(qv * br);
             }
         }
         __syncthreads();  // B3: this side's O partial, diag(a) Q, -diag(b) Q
@@ -609,6 +607,9 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
         __syncthreads();  // B4
 
         // ================= P4: backward, reads at the in-chunk weights
+        // The next chunk's K, Q and coefficients load from here to the end of the chunk
+        // (registers stay free through the phases above; about 4 us of cover).
+        if (c0 + kC < A.T) prefetch(c0 + kC);
         // G = E2 W2 (rows c, cols h); D1 = G o SiLU'(Z).  The B operand W2 [dd][h] is the
         // transpose of the state tiles W2T [h][dd]: one exact identity MFMA per tile.
         bf16x4 D1[4][kHt];
@@ -730,19 +731,30 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) xstore(dst + i * kThreads, pack2(ys[1][2 * i], ys[1][2 * i + 1]));
         }
-        __syncthreads();  // B7: the Y slots, K, Q, Cm and the vectors are no longer read
-        if (c0 + kC < A.T) {
-            commit();
-            if (c0 + 2 * kC < A.T) prefetch(c0 + 2 * kC);
-        }
         {
+            // The carry's K operands: A = (-c_C o K)^T and (w o K)^T, rows d, k = tokens c.
+            // An identity MFMA on K's LDS rows gives K tiles in accumulator layout (lane
+            // (g, j): K[16 ct + 4g + r][16 dt + j], exact); as operand A that is K^T, scaled
+            // by c_C / w of its token per element.
             const int rb = opq(j * kLd + 4 * g);
+            f32x4 ncc[4], wv4[4];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                ncc[ct] = -*reinterpret_cast<const f32x4*>(sm.cc + 16 * ct + 4 * g);
+                wv4[ct] = *reinterpret_cast<const f32x4*>(sm.w + 16 * ct + 4 * g);
+            }
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                const bf16x8 kc0 = frag(sm.kc + rb, fo(dt, 0));
-                const bf16x8 kc1 = frag(sm.kc + rb, fo(dt, 1));
-                const bf16x8 kw0 = frag(sm.kw + rb, fo(dt, 0));
-                const bf16x8 kw1 = frag(sm.kw + rb, fo(dt, 1));
+                bf16x4 kc[4], kw[4];
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const f32x4 kd = mfma(frag(sm.kk + rb, fo(ct, dt >> 1)), (dt & 1) ? eye1 : eye,
+                                          zero4());
+                    kc[ct] = bf4(kd * ncc[ct]);
+                    kw[ct] = bf4(kd * wv4[ct]);
+                }
+                const bf16x8 kc0 = cat(kc[0], kc[1]), kc1 = cat(kc[2], kc[3]);
+                const bf16x8 kw0 = cat(kw[0], kw[1]), kw1 = cat(kw[2], kw[3]);
                 const bf16x8 ec0 = frag(sm.e2c + rb, fo(dt, 0));
                 const bf16x8 ec1 = frag(sm.e2c + rb, fo(dt, 1));
                 const bf16x8 ew0 = frag(sm.e2w + rb, fo(dt, 0));
@@ -763,6 +775,10 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                     S2T[ht][dt] = mfma(ah1, ew1, mfma(ah0, ew0, ts2));
                 }
             }
+        }
+        __syncthreads();  // B7: the Y slots, K, Q, Cm and the vectors are no longer read
+        if (c0 + kC < A.T) {
+            commit();
         }
     }
 
