@@ -100,11 +100,11 @@ const char* titans_last_error(void);
 int64_t titans_mem_param_count(const titans_mlp_desc* mlp);
 
 /* Which kernel titans_mem_scan runs for this problem on the current device (a 256-CU
- * MI355X is assumed when no device is visible): for the 64 -> 256 -> 64 memory with
- * C = 64 and bf16 I/O, "fused_pair" (bf16 MFMA, state resident on chip, two workgroups
- * per memory; chosen while 2 * ceil(B*H / 8) * 8 workgroups fit one per compute unit) or
- * "fused_mfma" (one workgroup per memory); "generic_fp32" for every other supported
- * shape.  NULL if the arguments are invalid.  The returned string is static. */
+ * MI355X is assumed when no device is visible).  For the 64 -> 256 -> 64 memory with bf16
+ * I/O: "fused_pair" (bf16 MFMA, state resident on chip, two workgroups per memory; C a
+ * multiple of 64; chosen while 2 * ceil(B*H / 8) * 8 workgroups fit one per compute unit),
+ * else "fused_mfma" (one workgroup per memory; C = 64).  "generic_fp32" for every other
+ * supported shape.  NULL if the arguments are invalid.  The returned string is static. */
 const char* titans_mem_scan_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp);
 
 /* Device workspace bytes titans_mem_scan needs for this problem (0 if none;

@@ -214,20 +214,20 @@ static int64_t device_cus() {
 
 enum class Path { Generic, Fused, Pair };
 
-// Which kernel serves a (validated) problem.  The fused shape runs on pairs of
-// workgroups while the pairs fit the device at one workgroup per compute unit, else one
-// workgroup per memory.  Debugging switches: TITANS_MEM_FORCE_GENERIC=1 routes every call
+// Which kernel serves a (validated) problem.  The 64-256-64 bf16 memory runs on pairs of
+// workgroups (any chunk length that is a multiple of 64) while the pairs fit the device at
+// one workgroup per compute unit, else on one workgroup per memory (C = 64 only).  Debugging switches: TITANS_MEM_FORCE_GENERIC=1 routes every call
 // through the generic kernel, TITANS_MEM_FUSED_SINGLE=1 keeps the fused shape on one
 // workgroup per memory.
 static Path choose_path(const titans::ScanArgs& a) {
     const char* env = getenv("TITANS_MEM_FORCE_GENERIC");
     if (env && env[0] == '1') return Path::Generic;
-    if (!titans::scan_mfma_supported(a)) return Path::Generic;
     env = getenv("TITANS_MEM_FUSED_SINGLE");
-    if (env && env[0] == '1') return Path::Fused;
-    if (titans::scan_pair_supported(a) && titans::scan_pair_workgroups(a) <= device_cus())
+    const bool single = env && env[0] == '1';
+    if (!single && titans::scan_pair_supported(a) &&
+        titans::scan_pair_workgroups(a) <= device_cus())
         return Path::Pair;
-    return Path::Fused;
+    return titans::scan_mfma_supported(a) ? Path::Fused : Path::Generic;
 }
 
 const char* titans_mem_scan_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp) {

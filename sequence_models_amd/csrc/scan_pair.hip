@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mfma_util.h"
 #include "titans_internal.h"
 
@@ -120,6 +122,17 @@ struct __attribute__((aligned(16))) Smem {
     int fail;
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
+
+// Gradient chunks longer than the 64-token sub-chunk (C = 128, 192, 256): the gradients of
+// every sub-chunk are taken at the weights of the chunk start, kept here in bf16 (the
+// precision every product reads them in) and refreshed at each chunk start; the reads and
+// the carry use the running weights in registers as for C = 64.
+constexpr int kLd2 = kHidSide + 8;  // padded row of the frozen W2 slice
+struct __attribute__((aligned(16))) SmemFrozen : Smem {
+    __bf16 w1c[kHidSide * kLd];  // W1 at the chunk start [h][d], this side's 128 rows
+    __bf16 w2c[kD * kLd2];       // W2 at the chunk start [dd][h], this side's 128 columns
+};
+static_assert(sizeof(SmemFrozen) <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ float* yslot(Smem& sm, int w) {
     switch (w) {
@@ -268,8 +281,10 @@ __global__ void __launch_bounds__(kThreads) pair_coef_kernel(ScanArgs A, char* c
     }
 }
 
+template <bool kFrozen>
 __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
-    __shared__ Smem sm;
+    __shared__ std::conditional_t<kFrozen, SmemFrozen, Smem> sm;
+    const int kSub = A.C / kC;  // sub-chunks per gradient chunk
     const int tid = threadIdx.x;
     const int wv = tid >> 6, l = tid & 63, g = l >> 4, j = l & 15;
     // workgroups i and i ^ 8 form pair 8 (i / 16) + i % 8
@@ -387,9 +402,24 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
     prefetch(0);
     commit();
 
-    int e = 0;  // exchange number of the current chunk (1, 2, ...)
+    int e = 0;  // exchange number of the current sub-chunk (1, 2, ...)
     for (int64_t c0 = 0; c0 < A.T; c0 += kC) {
         ++e;
+        if constexpr (kFrozen) {
+            if ((e - 1) % kSub == 0) {
+                // a gradient chunk starts: freeze this wave's W1 rows and W2 columns (each
+                // wave reads back only its own slice; B1 orders the writes before the reads)
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int ht = 0; ht < kHt; ++ht) {
+                        *reinterpret_cast<bf16x4*>(sm.w1c + (32 * wv + 16 * ht + j) * kLd + 16 * dt +
+                                                   4 * g) = bf4(W1T[dt][ht]);
+                        *reinterpret_cast<bf16x4*>(sm.w2c + (16 * dt + j) * kLd2 + 32 * wv + 16 * ht +
+                                                   4 * g) = bf4(W2T[ht][dt]);
+                    }
+            }
+        }
         // ================= P0: load V
         bf16x8 vr[2];
         {
@@ -414,8 +444,15 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             const __bf16* ks = sm.kk + rb;
 #pragma unroll
             for (int ht = 0; ht < kHt; ++ht) {
-                const bf16x8 bw0 = state_frag(W1T[0][ht], W1T[1][ht]);
-                const bf16x8 bw1 = state_frag(W1T[2][ht], W1T[3][ht]);
+                bf16x8 bw0, bw1;
+                if constexpr (kFrozen) {
+                    const __bf16* wr = sm.w1c + (32 * wv + 16 * ht + j) * kLd + 4 * g;
+                    bw0 = frag(wr, 0);
+                    bw1 = frag(wr, 32);
+                } else {
+                    bw0 = state_frag(W1T[0][ht], W1T[1][ht]);
+                    bw1 = state_frag(W1T[2][ht], W1T[3][ht]);
+                }
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
                     f32x4 z = mfma(frag(ks, fo(ct, 0)), bw0, zero4());
@@ -440,7 +477,11 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             const int rb = opq(j * kLd + 4 * g);
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                const bf16x8 a0 = state_frag(W2T[0][dt], W2T[1][dt]);
+                bf16x8 a0;
+                if constexpr (kFrozen)
+                    a0 = frag(sm.w2c + (16 * dt + j) * kLd2 + 32 * wv + 4 * g, 0);
+                else
+                    a0 = state_frag(W2T[0][dt], W2T[1][dt]);
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct)
                     Ot[dt][ct] = mfma(a0, cat(HkT[0][ct], HkT[1][ct]), zero4());
@@ -618,8 +659,17 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
 #pragma unroll
             for (int ht = 0; ht < kHt; ++ht)
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-                    W2n[dt][ht] = bf4(mfma(cat(bf4(W2T[ht][dt]), bf16x4{}), eye, zero4()));
+                for (int dt = 0; dt < 4; ++dt) {
+                    // lane (g, j): W2[16 dt + j][16 ht + 4g + v], v < 4, of the weights the
+                    // gradient is taken at (operand A of the identity product)
+                    bf16x4 tile;
+                    if constexpr (kFrozen)
+                        tile = *reinterpret_cast<const bf16x4*>(sm.w2c + (16 * dt + j) * kLd2 +
+                                                                 32 * wv + 16 * ht + 4 * g);
+                    else
+                        tile = bf4(W2T[ht][dt]);
+                    W2n[dt][ht] = bf4(mfma(cat(tile, bf16x4{}), eye, zero4()));
+                }
             const int rb = opq(j * kLd + 4 * g);
             const __bf16* er = sm.e2l + rb;
 #pragma unroll
@@ -829,8 +879,8 @@ int64_t num_chunks(const ScanArgs& a) { return (a.T + kC - 1) / kC; }
 }  // namespace
 
 bool scan_pair_supported(const ScanArgs& a) {
-    return a.L == 2 && a.n[0] == kD && a.n[1] == kHid && a.n[2] == kD && a.C == kC &&
-           a.io == TITANS_BF16;
+    return a.L == 2 && a.n[0] == kD && a.n[1] == kHid && a.n[2] == kD && a.C >= kC &&
+           a.C % kC == 0 && a.io == TITANS_BF16;
 }
 
 size_t scan_pair_workspace_bytes(const ScanArgs& a) {
@@ -859,7 +909,9 @@ hipError_t launch_scan_pair(const ScanArgs& a, hipStream_t stream) {
     }
     ScanArgs args = a;
     void* kargs[] = {&args};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&scan_pair_kernel),
+    const void* fn = a.C == kC ? reinterpret_cast<const void*>(&scan_pair_kernel<false>)
+                               : reinterpret_cast<const void*>(&scan_pair_kernel<true>);
+    return hipLaunchCooperativeKernel(fn,
                                       dim3((unsigned)(2 * npairs)), dim3(kThreads), kargs, 0,
                                       stream);
 }

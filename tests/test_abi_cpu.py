@@ -65,6 +65,13 @@ def test_workspace_size_query(monkeypatch):
                                                  ctypes.byref(mlp)) == 8 * 99328 + 8 * 1 * 9472
     assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(B=3, T=130, H=3)),
                                                  ctypes.byref(mlp)) == 16 * 99328 + 9 * 3 * 9472
+    # chunks that are multiples of 64 run on the pair path too (64-token sub-chunks whose
+    # gradients share the chunk-start weights); other lengths on the generic kernel
+    for C, path in ((128, b"fused_pair"), (256, b"fused_pair"), (96, b"generic_fp32"),
+                    (32, b"generic_fp32")):
+        assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=C)), ctypes.byref(mlp)) == path
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(B=64, H=16, C=256)),
+                                       ctypes.byref(mlp)) == b"generic_fp32"
     # more memories than pairs of compute units: one workgroup per memory, no workspace
     big = _desc(B=64, H=16)
     assert tm.lib.titans_mem_scan_path(ctypes.byref(big), ctypes.byref(mlp)) == b"fused_mfma"

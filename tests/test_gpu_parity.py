@@ -438,6 +438,29 @@ def test_fused_strided_inputs_nonzero_momentum(kernel, monkeypatch):
     check_pairs(wl, y, thT, sT, pairs, refs)
 
 
+@pytest.mark.parametrize("C,T", [(128, 300), (192, 385), (256, 600), (256, 100)])
+def test_pair_long_chunks_match_oracle(C, T, monkeypatch):
+    """Chunks of 128..256 tokens on the pair path: 64-token sub-chunks whose gradients are
+    all taken at the chunk-start weights."""
+    wl, inp = _small(widths=(64, 256, 64), B=2, T=T, H=3, C=C, io="bf16", seed=C + T)
+    dev = to_device(inp)
+    log(f"case pair path C={C} T={T}")
+    expected = _use("pair", monkeypatch)
+    assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == expected
+    y, thT, sT = run_gpu(dev, wl)
+    y2, thT2, sT2 = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(thT, thT2)
+    pairs = [(0, 0), (1, 2)]
+    check_pairs(wl, y, thT, sT, pairs, oracle_seq(inp, pairs))
+    monkeypatch.setenv("TITANS_MEM_FORCE_GENERIC", "1")
+    yg, tg, _ = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    ey, et = y_rel_err(to_f64(y), to_f64(yg)), state_rel_err(to_f64(thT), to_f64(tg))
+    log(f"  pair vs generic: y {ey:.2e} theta_T {et:.2e}")
+    assert ey <= 2e-2 and et <= 1e-1
+
+
 def test_pair_kernel_matches_single_kernel(monkeypatch):
     """The two fused kernels round at the same points and differ only in summation order."""
     wl = _workload("h8_d64_b4_t4k", True)
