@@ -342,6 +342,11 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
     a.theta0 = theta0; a.s0 = s0;
     a.y = y; a.thetaT = theta_T; a.sT = s_T;
     a.ws = workspace;
+    // Test hook for the pair path's failure handling: side 1 of every pair never posts its
+    // exchange flags and every wait gives up after a few polls, so side 0 times out (its
+    // slice of theta_T / s_T comes out NaN) while every kernel still ends normally.
+    const char* hook = getenv("TITANS_MEM_TEST_PAIR_TIMEOUT");
+    a.debug = (hook && hook[0] == '1') ? 1 : 0;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const Path path = a.T > 0 ? choose_path(a) : Path::Generic;
     hipError_t e = path == Path::Pair    ? titans::launch_scan_pair(a, hs)

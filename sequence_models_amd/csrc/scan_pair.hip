@@ -89,9 +89,9 @@ __device__ __forceinline__ void post_flag(int* flag, int e, int lane) {
 }
 // Wave-uniform bounded wait for the partner wave's flag to reach e.  `bad` latches a
 // timeout; a wave that has timed out does not wait again.
-__device__ __forceinline__ void wait_flag(int* flag, int e, bool& bad) {
+__device__ __forceinline__ void wait_flag(int* flag, int e, bool& bad, int max_spin) {
     if (bad) return;
-    for (int s = 0; s < kMaxSpin; ++s) {
+    for (int s = 0; s < max_spin; ++s) {
         const int v = __builtin_amdgcn_readfirstlane(
             __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         if (v >= e) {
@@ -305,6 +305,9 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                        seq * nchunks * kCoefBytes;
     auto yxslot = [&](int e, int s) { return xy + ((e & 1) * 2 + s) * 4 * kThreads + tid; };
     bool bad = false;
+    // test hook (debug bit 0): side 1 never posts, every wait gives up after 1024 polls
+    const bool mute = (A.debug & 1) && side == 1;
+    const int max_spin = (A.debug & 1) ? 1024 : kMaxSpin;
 
     const float* th0 = A.theta0 + bi * A.s0s[0] + hi * A.s0s[1];
     const float* mo0 = A.s0 + bi * A.s0s[0] + hi * A.s0s[1];
@@ -592,7 +595,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 }
                 // the O words went out before Mq: they have landed by now; the partner's
                 // flag then travels while this wave finishes its state terms
-                if (ht == 0) post_flag(myflag, e, l);
+                if (ht == 0 && !mute) post_flag(myflag, e, l);
             }
         }
         {
@@ -606,7 +609,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                     S1T[dt][ht] = pC * S1T[dt][ht];
                 }
         }
-        wait_flag(otflag, e, bad);
+        wait_flag(otflag, e, bad, max_spin);
         {
             // the partner's O partial of this chunk and its partial of this side's y rows of
             // the previous chunk, all loads issued together (one round trip)
@@ -835,8 +838,8 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
     // ---- y of the last chunk: one more exchange (no O words)
     {
         const int ef = e + 1;
-        post_flag(myflag, ef, l);
-        wait_flag(otflag, ef, bad);
+        if (!mute) post_flag(myflag, ef, l);
+        wait_flag(otflag, ef, bad, max_spin);
         uint64_t px[4];
         const uint64_t* src = yxslot(e, 1 - side);
 #pragma unroll

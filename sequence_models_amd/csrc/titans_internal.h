@@ -30,6 +30,7 @@ struct ScanArgs {
     float* thetaT;
     float* sT;
     void* ws;
+    int debug;                 // test hooks (0 in normal use), see abi.hip
 };
 
 // Generic chunked scan: fp32 arithmetic, any supported shape, one workgroup per

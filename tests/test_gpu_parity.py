@@ -461,6 +461,27 @@ def test_pair_long_chunks_match_oracle(C, T, monkeypatch):
     assert ey <= 2e-2 and et <= 1e-1
 
 
+def test_pair_wait_bound_ends_the_kernel(monkeypatch):
+    """Failure handling of the pair exchange, forced from the host: one side of every pair
+    never posts (test hook) and the waits give up after a few polls. The kernel must end,
+    the side that timed out must return NaN for its half of theta_T, and the next normal
+    call must be exact again."""
+    wl, inp = _small(widths=(64, 256, 64), B=1, T=200, H=2, C=64, io="bf16", seed=41)
+    dev = to_device(inp)
+    log("case pair wait bound (forced timeout)")
+    _use("pair", monkeypatch)
+    y0, t0, s0 = run_gpu(dev, wl)
+    monkeypatch.setenv("TITANS_MEM_TEST_PAIR_TIMEOUT", "1")
+    y1, t1, s1 = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    P1 = 256 * 64  # W1 rows h = 0..127 belong to side 0
+    assert torch.isnan(t1[:, :, : P1 // 2]).all() and torch.isnan(s1[:, :, : P1 // 2]).all()
+    monkeypatch.delenv("TITANS_MEM_TEST_PAIR_TIMEOUT")
+    y2, t2, s2 = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y0) and torch.equal(t2, t0) and torch.equal(s2, s0)
+
+
 def test_pair_kernel_matches_single_kernel(monkeypatch):
     """The two fused kernels round at the same points and differ only in summation order."""
     wl = _workload("h8_d64_b4_t4k", True)
