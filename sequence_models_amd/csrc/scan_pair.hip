@@ -134,6 +134,13 @@ struct __attribute__((aligned(16))) SmemFrozen : Smem {
 };
 static_assert(sizeof(SmemFrozen) <= 160 * 1024, "LDS budget");
 
+// C = 64: the LDS the frozen copy would take holds two more O partial slots instead, so all
+// four waves store their partials at once and the sum needs no second stage or barrier.
+struct __attribute__((aligned(16))) SmemFour : Smem {
+    float o2[2][kMat];  // O partials of waves 2, 3
+};
+static_assert(sizeof(SmemFour) <= 160 * 1024, "LDS budget");
+
 __device__ __forceinline__ float* yslot(Smem& sm, int w) {
     switch (w) {
         case 0: return sm.r[0];
@@ -283,7 +290,7 @@ __global__ void __launch_bounds__(kThreads) pair_coef_kernel(ScanArgs A, char* c
 
 template <bool kFrozen>
 __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
-    __shared__ std::conditional_t<kFrozen, SmemFrozen, Smem> sm;
+    __shared__ std::conditional_t<kFrozen, SmemFrozen, SmemFour> sm;
     const int kSub = A.C / kC;  // sub-chunks per gradient chunk
     const int tid = threadIdx.x;
     const int wv = tid >> 6, l = tid & 63, g = l >> 4, j = l & 15;
@@ -489,8 +496,17 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 for (int ct = 0; ct < 4; ++ct)
                     Ot[dt][ct] = mfma(a0, cat(HkT[0][ct], HkT[1][ct]), zero4());
             }
-            // deterministic pairwise reduction, stage 1: waves 2, 3 store their partials
-            if (wv >= 2) {
+            // deterministic reduction, fixed order (w0 + w2) + (w1 + w3):
+            //   C = 64: every wave stores its partial in its own slot;
+            //   longer chunks (less LDS): waves 2, 3 store, waves 0, 1 add theirs in P2
+            if constexpr (!kFrozen) {
+                float* slot = (wv < 2 ? sm.r[wv] : sm.o2[wv - 2]) + rb;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+                        *reinterpret_cast<f32x4*>(slot + 16 * ct * kLd + 16 * dt) = Ot[dt][ct];
+            } else if (wv >= 2) {
                 float* slot = sm.r[wv - 2] + rb;
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt)
@@ -499,44 +515,57 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                         *reinterpret_cast<f32x4*>(slot + 16 * ct * kLd + 16 * dt) = Ot[dt][ct];
             }
         }
-        __syncthreads();  // B2: coefficients, O stage 1
-
-        // ================= P2: stage 2 of O; scaled Q copies
-        if (wv < 2) {
-            // all reads first, then all writes (the slot never aliases within itself; a
-            // read-add-write per tile would wait out one LDS round trip per tile)
-            float* slot = sm.r[wv] + opq(j * kLd + 4 * g);
+        if constexpr (!kFrozen) {
+            // diag(a) Q and -diag(b) Q
+            const float ar = sm.a[rc], br = -sm.b[rc];
+            const int xb = opq(rc * kLd + cl0);
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                f32x4 prev[2][4];
-#pragma unroll
-                for (int d2 = 0; d2 < 2; ++d2)
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct)
-                        prev[d2][ct] = *reinterpret_cast<const f32x4*>(
-                            slot + 16 * ct * kLd + 16 * (2 * half + d2));
-                reload();
-#pragma unroll
-                for (int d2 = 0; d2 < 2; ++d2)
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct)
-                        *reinterpret_cast<f32x4*>(slot + 16 * ct * kLd + 16 * (2 * half + d2)) =
-                            Ot[2 * half + d2][ct] + prev[d2][ct];
-            }
-        }
-        // waves 2, 3 meanwhile: diag(a) Q and -diag(b) Q (thread u: row u / 2, 32 columns)
-        if (wv >= 2) {
-            const int u = tid & 127, row = u >> 1, c32 = 32 * (u & 1);
-            const float ar = sm.a[row], br = -sm.b[row];
-            const int xb = opq(row * kLd + c32);
-#pragma unroll
-            for (int q4 = 0; q4 < 8; ++q4) {
+            for (int q4 = 0; q4 < 4; ++q4) {
                 const f32x4 qv = f4(*reinterpret_cast<const bf16x4*>(sm.qq + xb + 4 * q4));
                 *reinterpret_cast<bf16x4*>(sm.qa + xb + 4 * q4) = bf4(qv * ar);
                 *reinterpret_cast<bf16x4*>(sm.qb + xb + 4 * q4) = bf4(qv * br);
             }
         }
-        __syncthreads();  // B3: this side's O partial, diag(a) Q, -diag(b) Q
+        __syncthreads();  // B2: O partials (C = 64: and the scaled Q copies)
+
+        if constexpr (kFrozen) {
+            // ================= P2: stage 2 of O; scaled Q copies
+            if (wv < 2) {
+                // all reads first, then all writes (the slot never aliases within itself; a
+                // read-add-write per tile would wait out one LDS round trip per tile)
+                float* slot = sm.r[wv] + opq(j * kLd + 4 * g);
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    f32x4 prev[2][4];
+#pragma unroll
+                    for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+                        for (int ct = 0; ct < 4; ++ct)
+                            prev[d2][ct] = *reinterpret_cast<const f32x4*>(
+                                slot + 16 * ct * kLd + 16 * (2 * half + d2));
+                    reload();
+#pragma unroll
+                    for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+                        for (int ct = 0; ct < 4; ++ct)
+                            *reinterpret_cast<f32x4*>(slot + 16 * ct * kLd + 16 * (2 * half + d2)) =
+                                Ot[2 * half + d2][ct] + prev[d2][ct];
+                }
+            }
+            // waves 2, 3 meanwhile: diag(a) Q and -diag(b) Q (thread u: row u / 2, 32 columns)
+            if (wv >= 2) {
+                const int u = tid & 127, row = u >> 1, c32 = 32 * (u & 1);
+                const float ar = sm.a[row], br = -sm.b[row];
+                const int xb = opq(row * kLd + c32);
+#pragma unroll
+                for (int q4 = 0; q4 < 8; ++q4) {
+                    const f32x4 qv = f4(*reinterpret_cast<const bf16x4*>(sm.qq + xb + 4 * q4));
+                    *reinterpret_cast<bf16x4*>(sm.qa + xb + 4 * q4) = bf4(qv * ar);
+                    *reinterpret_cast<bf16x4*>(sm.qb + xb + 4 * q4) = bf4(qv * br);
+                }
+            }
+            __syncthreads();  // B3: this side's O partial, diag(a) Q, -diag(b) Q
+        }
 
         // ================= P2x: exchange O; Mq and the state terms of Zq meanwhile
         float oo[16];
@@ -544,8 +573,15 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             const int xb = opq(rc * kLd + cl0);
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 o = *reinterpret_cast<const f32x4*>(sm.r[0] + xb + 4 * q4) +
-                                *reinterpret_cast<const f32x4*>(sm.r[1] + xb + 4 * q4);
+                f32x4 o;
+                if constexpr (!kFrozen)
+                    o = (*reinterpret_cast<const f32x4*>(sm.r[0] + xb + 4 * q4) +
+                         *reinterpret_cast<const f32x4*>(sm.o2[0] + xb + 4 * q4)) +
+                        (*reinterpret_cast<const f32x4*>(sm.r[1] + xb + 4 * q4) +
+                         *reinterpret_cast<const f32x4*>(sm.o2[1] + xb + 4 * q4));
+                else
+                    o = *reinterpret_cast<const f32x4*>(sm.r[0] + xb + 4 * q4) +
+                        *reinterpret_cast<const f32x4*>(sm.r[1] + xb + 4 * q4);
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) oo[4 * q4 + e4] = o[e4];
             }
