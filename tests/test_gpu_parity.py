@@ -461,6 +461,25 @@ def test_pair_long_chunks_match_oracle(C, T, monkeypatch):
     assert ey <= 2e-2 and et <= 1e-1
 
 
+def test_scan_and_retrieve_on_a_side_stream():
+    """The library enqueues on the caller's stream: a side stream gives the same bits."""
+    wl, inp = _small(widths=(64, 256, 64), B=2, T=200, H=3, C=64, io="bf16", seed=51)
+    dev = to_device(inp)
+    log("case side stream")
+    y0, t0, s0 = run_gpu(dev, wl)
+    r0 = tm.retrieve(dev["q"], t0, wl.widths)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        y1, t1, s1 = run_gpu(dev, wl)
+        r1 = tm.retrieve(dev["q"], t1, wl.widths)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(t0, t1) and torch.equal(s0, s1)
+    assert torch.equal(r0, r1)
+
+
 def test_pair_wait_bound_ends_the_kernel(monkeypatch):
     """Failure handling of the pair exchange, forced from the host: one side of every pair
     never posts (test hook) and the waits give up after a few polls. The kernel must end,
