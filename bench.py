@@ -204,6 +204,8 @@ def main():
         kernel = ("clear_pair_flags + pair_coef_kernel + scan_pair_kernel" if path == "fused_pair"
                   else "scan_mfma_kernel")
         bound, peak, dtype = "mfma", PEAKS["mfma_bf16"], "bf16"
+    elif path == "generic_mfma":  # bf16 MFMA products, fp32 accumulation
+        bound, peak, kernel, dtype = "mfma", PEAKS["mfma_bf16"], "scan_generic_kernel", "bf16"
     else:  # fp32 FMAs on the vector ALUs
         bound, peak, kernel, dtype = "alu", PEAKS["valu_f32"], "scan_generic_kernel", "f32"
     parallelism = {"fused_pair": "one GPU; two workgroups (one XCD) per (batch row, head) memory"}.get(

@@ -103,8 +103,10 @@ int64_t titans_mem_param_count(const titans_mlp_desc* mlp);
  * MI355X is assumed when no device is visible).  For the 64 -> 256 -> 64 memory with bf16
  * I/O: "fused_pair" (bf16 MFMA, state resident on chip, two workgroups per memory; C a
  * multiple of 64; chosen while 2 * ceil(B*H / 8) * 8 workgroups fit one per compute unit),
- * else "fused_mfma" (one workgroup per memory; C = 64).  "generic_fp32" for every other
- * supported shape.  NULL if the arguments are invalid.  The returned string is static. */
+ * else "fused_mfma" (one workgroup per memory; C = 64).  Every other supported shape runs the
+ * generic kernel: "generic_mfma" (bf16 I/O: bf16 MFMA products, fp32 accumulation and
+ * state) or "generic_fp32" (fp32 I/O: fp32 arithmetic throughout).  NULL if the arguments
+ * are invalid.  The returned string is static. */
 const char* titans_mem_scan_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp);
 
 /* Device workspace bytes titans_mem_scan needs for this problem (0 if none;
@@ -140,7 +142,7 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Which kernel titans_mem_retrieve runs for this problem: "fused_mfma" (bf16 MFMA; the
- * 64 -> 256 -> 64 memory with bf16 q / y) or "generic_fp32".  NULL if the arguments are
+ * 64 -> 256 -> 64 memory with bf16 q / y), else "generic_mfma" (bf16) or "generic_fp32" (fp32 I/O).  NULL if the arguments are
  * invalid.  The returned string is static. */
 const char* titans_mem_retrieve_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp);
 

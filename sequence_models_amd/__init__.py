@@ -149,7 +149,8 @@ def scan_workspace_size(q, chunk, widths) -> int:
 
 
 def scan_path(q, chunk, widths) -> str:
-    """Name of the kernel that serves this shape: "fused_pair", "fused_mfma" or "generic_fp32"."""
+    """Name of the kernel that serves this shape: "fused_pair", "fused_mfma", "generic_mfma"
+    (bf16 I/O) or "generic_fp32" (fp32 I/O)."""
     d = make_desc(q, chunk, q, None, None, None)
     r = lib.titans_mem_scan_path(ctypes.byref(d), ctypes.byref(mlp_desc(widths)))
     if r is None:
@@ -203,7 +204,8 @@ def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, *, y=None, theta_
 
 
 def retrieve_path(q, widths) -> str:
-    """Name of the kernel titans_mem_retrieve runs for q's shape: "fused_mfma" or "generic_fp32"."""
+    """Name of the kernel titans_mem_retrieve runs for q's shape: "fused_mfma", "generic_mfma"
+    or "generic_fp32"."""
     d = make_desc(q, 1, q, None, None, None)
     r = lib.titans_mem_retrieve_path(ctypes.byref(d), ctypes.byref(mlp_desc(widths)))
     if r is None:

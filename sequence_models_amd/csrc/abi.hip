@@ -236,7 +236,7 @@ const char* titans_mem_scan_path(const titans_scan_desc* desc, const titans_mlp_
     switch (choose_path(a)) {
         case Path::Pair: return "fused_pair";
         case Path::Fused: return "fused_mfma";
-        default: return "generic_fp32";
+        default: return a.io == TITANS_BF16 ? "generic_mfma" : "generic_fp32";
     }
 }
 
@@ -373,7 +373,8 @@ static bool retrieve_uses_mfma(const titans::ScanArgs& a) {
 const char* titans_mem_retrieve_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp) {
     titans::ScanArgs a{};
     if (prepare_retrieve(desc, mlp, a) != TITANS_OK) return nullptr;
-    return retrieve_uses_mfma(a) ? "fused_mfma" : "generic_fp32";
+    if (retrieve_uses_mfma(a)) return "fused_mfma";
+    return a.io == TITANS_BF16 ? "generic_mfma" : "generic_fp32";
 }
 
 titans_status titans_mem_retrieve(const titans_scan_desc* desc, const titans_mlp_desc* mlp,

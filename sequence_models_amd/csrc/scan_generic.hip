@@ -1,4 +1,6 @@
-// Generic chunked Titans memory scan and retrieve for gfx950, fp32 arithmetic.
+// Generic chunked Titans memory scan and retrieve for gfx950.  With fp32 I/O every
+// product is fp32 FMAs; with bf16 I/O the products are bf16 MFMA with fp32 accumulation
+// (operands rounded to bf16 as they are staged; state and intermediates stay fp32).
 //
 // This path serves every supported shape (any L <= 4, widths <= 512, C <= 256,
 // fp32 or bf16 I/O).  One 256-thread workgroup owns one (b, h) memory; theta
@@ -31,7 +33,15 @@ constexpr int kThreads = 256;
 constexpr int kTile = 64;   // output tile edge
 constexpr int kKStep = 16;  // reduction step
 constexpr int kPad = 4;
-constexpr int kGemmLds = 2 * kKStep * (kTile + kPad);  // floats
+constexpr int kGemmLdsF32 = 2 * kKStep * (kTile + kPad);  // floats
+constexpr int kMK = 32;                                     // MFMA reduction step
+constexpr int kMLd = kMK + 8;                               // padded bf16 row of a staged tile
+constexpr int kGemmLdsMfma = 2 * kTile * kMLd / 2;          // floats (two bf16 tiles)
+constexpr int kGemmLds = kGemmLdsF32 > kGemmLdsMfma ? kGemmLdsF32 : kGemmLdsMfma;
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -132,6 +142,106 @@ __device__ void block_gemm(int M, int N, int K, MatA A, MatB B, float* lds, Epi 
     __syncthreads();
 }
 
+// The same workgroup GEMM on bf16 MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+// Per 64 x 64 output tile and 32-wide reduction step, A (64 x 32) and B (32 x 64) are staged
+// in LDS as bf16 with the reduction index contiguous ([row i][k], [column j][k]); wave w
+// computes output rows 16w .. 16w+15 against the four 16-column tiles.  Operand layouts of
+// the MFMA: lane l (g = l / 16, j = l % 16) holds A[j][k] and B[k][j] for k in
+// {4g .. 4g+3, 16+4g .. 16+4g+3} and D[4g + r][j], r = 0..3.
+template <class Epi>
+__device__ void block_gemm_mfma(int M, int N, int K, MatA A, MatB B, float* lds, Epi epi) {
+    __bf16* As = reinterpret_cast<__bf16*>(lds);  // [64][kMLd]
+    __bf16* Bs = As + kTile * kMLd;                // [64][kMLd]
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6, g = (tid & 63) >> 4, j = tid & 15;
+    for (int i0 = 0; i0 < M; i0 += kTile) {
+        for (int j0 = 0; j0 < N; j0 += kTile) {
+            f32x4_t acc[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int k0 = 0; k0 < K; k0 += kMK) {
+                // stage: each thread moves two groups of four elements of A and of B
+#pragma unroll
+                for (int rep = 0; rep < 2; ++rep) {
+                    const int e = tid + kThreads * rep;  // 0 .. 511
+                    if (A.sk == 1) {                     // four consecutive k of one row
+                        const int ii = e >> 3, kq = (e & 7) * 4, gi = i0 + ii;
+                        bf16x4_t v;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int gk = k0 + kq + u;
+                            float x = 0.f;
+                            if (gi < M && gk < K) {
+                                x = A.p[gi * A.si + gk];
+                                if (A.kscale) x *= A.kscale[gk];
+                            }
+                            v[u] = (__bf16)x;
+                        }
+                        *reinterpret_cast<bf16x4_t*>(As + ii * kMLd + kq) = v;
+                    } else {                             // four consecutive rows of one k
+                        const int kk = e >> 4, iq = (e & 15) * 4, gk = k0 + kk;
+                        const float sc = (A.kscale && gk < K) ? A.kscale[gk] : 1.f;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int gi = i0 + iq + u;
+                            const float x = (gi < M && gk < K) ? A.p[gi * A.si + gk * A.sk] * sc : 0.f;
+                            As[(iq + u) * kMLd + kk] = (__bf16)x;
+                        }
+                    }
+                    if (B.sk == 1) {                     // four consecutive k of one column
+                        const int jj = e >> 3, kq = (e & 7) * 4, gj = j0 + jj;
+                        bf16x4_t v;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int gk = k0 + kq + u;
+                            v[u] = (__bf16)((gj < N && gk < K) ? B.p[gk + gj * B.sj] : 0.f);
+                        }
+                        *reinterpret_cast<bf16x4_t*>(Bs + jj * kMLd + kq) = v;
+                    } else {                             // four consecutive columns of one k
+                        const int kk = e >> 4, jq = (e & 15) * 4, gk = k0 + kk;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int gj = j0 + jq + u;
+                            const float x = (gj < N && gk < K) ? B.p[gk * B.sk + gj * B.sj] : 0.f;
+                            Bs[(jq + u) * kMLd + kk] = (__bf16)x;
+                        }
+                    }
+                }
+                __syncthreads();
+                const __bf16* ar = As + (16 * wv + j) * kMLd + 4 * g;
+                const bf16x8_t af = __builtin_shufflevector(*reinterpret_cast<const bf16x4_t*>(ar),
+                                                            *reinterpret_cast<const bf16x4_t*>(ar + 16),
+                                                            0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                for (int tn = 0; tn < 4; ++tn) {
+                    const __bf16* br = Bs + (16 * tn + j) * kMLd + 4 * g;
+                    const bf16x8_t bf = __builtin_shufflevector(
+                        *reinterpret_cast<const bf16x4_t*>(br), *reinterpret_cast<const bf16x4_t*>(br + 16),
+                        0, 1, 2, 3, 4, 5, 6, 7);
+                    acc[tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[tn], 0, 0, 0);
+                }
+                __syncthreads();
+            }
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = i0 + 16 * wv + 4 * g + r, jc = j0 + 16 * tn + j;
+                    if (i < M && jc < N) epi(i, jc, acc[tn][r]);
+                }
+        }
+    }
+    __syncthreads();
+}
+
+template <bool kMfma, class Epi>
+__device__ __forceinline__ void gemm(int M, int N, int K, MatA A, MatB B, float* lds, Epi epi) {
+    if constexpr (kMfma)
+        block_gemm_mfma(M, N, K, A, B, lds, epi);
+    else
+        block_gemm(M, N, K, A, B, lds, epi);
+}
+
 __device__ __forceinline__ int64_t round64(int64_t x) { return (x + 63) & ~int64_t(63); }
 
 // Float offsets of the per-sequence workspace regions.
@@ -164,6 +274,7 @@ __host__ __device__ inline WsLayout ws_layout(int C, int L, const int* n) {
     return w;
 }
 
+template <bool kMfma>
 __global__ void __launch_bounds__(kThreads) scan_generic_kernel(ScanArgs a) {
     __shared__ float lds_gemm[kGemmLds];
     __shared__ float s_al[256], s_et[256], s_be[256];
@@ -250,14 +361,14 @@ __global__ void __launch_bounds__(kThreads) scan_generic_kernel(ScanArgs a) {
             if (l < L) {
                 float* Hout = ws + wl.hk[l];
                 float* Sp = ws + wl.sp[l];
-                block_gemm(n, nout, nin, A, Bm, lds_gemm, [&](int i, int jj, float z) {
+                gemm<kMfma>(n, nout, nin, A, Bm, lds_gemm, [&](int i, int jj, float z) {
                     float sg = sigmoidf_(z);
                     Hout[i * nout + jj] = z * sg;
                     Sp[i * nout + jj] = sg * (1.0f + z * (1.0f - sg));
                 });
             } else {
                 float* D = ws + wl.dl[L];
-                block_gemm(n, nout, nin, A, Bm, lds_gemm, [&](int i, int jj, float z) {
+                gemm<kMfma>(n, nout, nin, A, Bm, lds_gemm, [&](int i, int jj, float z) {
                     float vv = load_io(a.v, qbase + (c0 + i) * a.qs[1] + jj, a.io);
                     D[i * nout + jj] = 2.0f * (z - vv);
                 });
@@ -270,7 +381,7 @@ __global__ void __launch_bounds__(kThreads) scan_generic_kernel(ScanArgs a) {
             const float* Dl = ws + wl.dl[l];
             float* Dp = ws + wl.dl[l - 1];
             const float* Sp = ws + wl.sp[l - 1];
-            block_gemm(n, nin, nout, MatA{Dl, nout, 1, nullptr}, MatB{W, nin, 1}, lds_gemm,
+            gemm<kMfma>(n, nin, nout, MatA{Dl, nout, 1, nullptr}, MatB{W, nin, 1}, lds_gemm,
                        [&](int i, int jj, float g) { Dp[i * nin + jj] = g * Sp[i * nin + jj]; });
         }
         // ---- retrieval at the in-chunk weights, layer by layer
@@ -285,22 +396,22 @@ __global__ void __launch_bounds__(kThreads) scan_generic_kernel(ScanArgs a) {
             const float* Dl = ws + wl.dl[l];
             float* Mq = ws + wl.mq;
             // Mq = Cm o (Hq Hk^T), strictly lower triangular
-            block_gemm(n, n, nin, MatA{Hq, nin, 1, nullptr}, MatB{Hk, 1, nin}, lds_gemm,
+            gemm<kMfma>(n, n, nin, MatA{Hq, nin, 1, nullptr}, MatB{Hk, 1, nin}, lds_gemm,
                        [&](int i, int jj, float x) {
                            Mq[i * C + jj] = (jj < i) ? Cm[(int64_t)i * C + jj] * x : 0.0f;
                        });
-            block_gemm(n, nout, nin, MatA{Hq, nin, 1, nullptr}, MatB{W, 1, nin}, lds_gemm,
+            gemm<kMfma>(n, nout, nin, MatA{Hq, nin, 1, nullptr}, MatB{W, 1, nin}, lds_gemm,
                        [&](int i, int jj, float x) { U[i * nout + jj] = coef_a[i] * x; });
-            block_gemm(n, nout, nin, MatA{Hq, nin, 1, nullptr}, MatB{S, 1, nin}, lds_gemm,
+            gemm<kMfma>(n, nout, nin, MatA{Hq, nin, 1, nullptr}, MatB{S, 1, nin}, lds_gemm,
                        [&](int i, int jj, float x) { U[i * nout + jj] -= coef_b[i] * x; });
             if (l < L) {
-                block_gemm(n, nout, n, MatA{Mq, C, 1, nullptr}, MatB{Dl, nout, 1}, lds_gemm,
+                gemm<kMfma>(n, nout, n, MatA{Mq, C, 1, nullptr}, MatB{Dl, nout, 1}, lds_gemm,
                            [&](int i, int jj, float x) {
                                float u = U[i * nout + jj] - x;
                                U[i * nout + jj] = u * sigmoidf_(u);
                            });
             } else {
-                block_gemm(n, nout, n, MatA{Mq, C, 1, nullptr}, MatB{Dl, nout, 1}, lds_gemm,
+                gemm<kMfma>(n, nout, n, MatA{Mq, C, 1, nullptr}, MatB{Dl, nout, 1}, lds_gemm,
                            [&](int i, int jj, float x) {
                                store_io(a.y, ybase + (c0 + i) * a.ys[1] + jj, a.io,
                                         U[i * nout + jj] - x);
@@ -317,12 +428,12 @@ __global__ void __launch_bounds__(kThreads) scan_generic_kernel(ScanArgs a) {
             float* S = mom + a.off[l];
             const float* Dl = ws + wl.dl[l];
             const float* Hk = ws + wl.hk[l - 1];
-            block_gemm(nout, nin, n, MatA{Dl, 1, nout, crow}, MatB{Hk, nin, 1}, lds_gemm,
+            gemm<kMfma>(nout, nin, n, MatA{Dl, 1, nout, crow}, MatB{Hk, nin, 1}, lds_gemm,
                        [&](int i, int jj, float x) {
                            int64_t o = (int64_t)i * nin + jj;
                            W[o] = an * W[o] - bn * S[o] - x;
                        });
-            block_gemm(nout, nin, n, MatA{Dl, 1, nout, coef_w}, MatB{Hk, nin, 1}, lds_gemm,
+            gemm<kMfma>(nout, nin, n, MatA{Dl, 1, nout, coef_w}, MatB{Hk, nin, 1}, lds_gemm,
                        [&](int i, int jj, float x) {
                            int64_t o = (int64_t)i * nin + jj;
                            S[o] = pn * S[o] + x;
@@ -333,6 +444,7 @@ __global__ void __launch_bounds__(kThreads) scan_generic_kernel(ScanArgs a) {
 
 constexpr int kRetrieveTokens = 16;
 
+template <bool kMfma>
 __global__ void __launch_bounds__(kThreads) retrieve_generic_kernel(ScanArgs a) {
     extern __shared__ float smem[];
     const int64_t seq = blockIdx.y;
@@ -359,10 +471,10 @@ __global__ void __launch_bounds__(kThreads) retrieve_generic_kernel(ScanArgs a) 
         float* Yb = buf[cur ^ 1];
         const float* W = theta + a.off[l];
         if (l < a.L) {
-            block_gemm(n, nout, nin, MatA{X, nin, 1, nullptr}, MatB{W, 1, nin}, lds_gemm,
+            gemm<kMfma>(n, nout, nin, MatA{X, nin, 1, nullptr}, MatB{W, 1, nin}, lds_gemm,
                        [&](int i, int jj, float z) { Yb[i * nout + jj] = z * sigmoidf_(z); });
         } else {
-            block_gemm(n, nout, nin, MatA{X, nin, 1, nullptr}, MatB{W, 1, nin}, lds_gemm,
+            gemm<kMfma>(n, nout, nin, MatA{X, nin, 1, nullptr}, MatB{W, 1, nin}, lds_gemm,
                        [&](int i, int jj, float z) {
                            store_io(a.y, ybase + i * a.ys[1] + jj, a.io, z);
                        });
@@ -400,7 +512,10 @@ hipError_t launch_scan_generic(const ScanArgs& a, hipStream_t stream) {
         copy_state_kernel<<<grid, 256, 0, stream>>>(a);
         return hipGetLastError();
     }
-    scan_generic_kernel<<<dim3((unsigned)nseq), kThreads, 0, stream>>>(a);
+    if (a.io == TITANS_BF16)
+        scan_generic_kernel<true><<<dim3((unsigned)nseq), kThreads, 0, stream>>>(a);
+    else
+        scan_generic_kernel<false><<<dim3((unsigned)nseq), kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -411,7 +526,10 @@ hipError_t launch_retrieve_generic(const ScanArgs& a, hipStream_t stream) {
     for (int l = 0; l <= a.L; ++l) maxw = a.n[l] > maxw ? a.n[l] : maxw;
     size_t lds = sizeof(float) * (kGemmLds + 2 * kRetrieveTokens * maxw);
     dim3 grid((unsigned)((a.T + kRetrieveTokens - 1) / kRetrieveTokens), (unsigned)nseq);
-    retrieve_generic_kernel<<<grid, kThreads, lds, stream>>>(a);
+    if (a.io == TITANS_BF16)
+        retrieve_generic_kernel<true><<<grid, kThreads, lds, stream>>>(a);
+    else
+        retrieve_generic_kernel<false><<<grid, kThreads, lds, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -33,8 +33,9 @@ struct ScanArgs {
     int debug;                 // test hooks (0 in normal use), see abi.hip
 };
 
-// Generic chunked scan: fp32 arithmetic, any supported shape, one workgroup per
-// (b, h), per-chunk intermediates in the workspace.
+// Generic chunked scan: any supported shape, one workgroup per (b, h), per-chunk
+// intermediates in the workspace.  Its matrix products run on bf16 MFMA (fp32
+// accumulation) for bf16 I/O and on fp32 FMAs for fp32 I/O; state is fp32 either way.
 size_t scan_generic_workspace_bytes(const ScanArgs& a);
 hipError_t launch_scan_generic(const ScanArgs& a, hipStream_t stream);
 
@@ -51,7 +52,7 @@ size_t scan_pair_workspace_bytes(const ScanArgs& a);
 int64_t scan_pair_workgroups(const ScanArgs& a);
 hipError_t launch_scan_pair(const ScanArgs& a, hipStream_t stream);
 
-// Generic retrieve: fp32 arithmetic, any supported shape.
+// Generic retrieve: any supported shape, products as in the generic scan.
 hipError_t launch_retrieve_generic(const ScanArgs& a, hipStream_t stream);
 
 // MFMA retrieve for the 64 -> 256 -> 64 memory with bf16 q / y.

@@ -67,11 +67,11 @@ def test_workspace_size_query(monkeypatch):
                                                  ctypes.byref(mlp)) == 16 * 99328 + 9 * 3 * 9472
     # chunks that are multiples of 64 run on the pair path too (64-token sub-chunks whose
     # gradients share the chunk-start weights); other lengths on the generic kernel
-    for C, path in ((128, b"fused_pair"), (256, b"fused_pair"), (96, b"generic_fp32"),
-                    (32, b"generic_fp32")):
+    for C, path in ((128, b"fused_pair"), (256, b"fused_pair"), (96, b"generic_mfma"),
+                    (32, b"generic_mfma")):
         assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=C)), ctypes.byref(mlp)) == path
     assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(B=64, H=16, C=256)),
-                                       ctypes.byref(mlp)) == b"generic_fp32"
+                                       ctypes.byref(mlp)) == b"generic_mfma"
     # more memories than pairs of compute units: one workgroup per memory, no workspace
     big = _desc(B=64, H=16)
     assert tm.lib.titans_mem_scan_path(ctypes.byref(big), ctypes.byref(mlp)) == b"fused_mfma"
@@ -82,12 +82,12 @@ def test_workspace_size_query(monkeypatch):
     monkeypatch.delenv("TITANS_MEM_FUSED_SINGLE")
     size = tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(C=32)), ctypes.byref(mlp))
     assert 0 < size < 1 << 30 and size % 4 == 0
-    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=32)), ctypes.byref(mlp)) == b"generic_fp32"
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=32)), ctypes.byref(mlp)) == b"generic_mfma"
     assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(io=0)), ctypes.byref(mlp)) == b"generic_fp32"
     assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=0)), ctypes.byref(mlp)) is None
     assert tm.lib.titans_mem_retrieve_path(ctypes.byref(_desc()), ctypes.byref(mlp)) == b"fused_mfma"
     assert tm.lib.titans_mem_retrieve_path(ctypes.byref(_desc(io=0)), ctypes.byref(mlp)) == b"generic_fp32"
-    assert tm.lib.titans_mem_retrieve_path(ctypes.byref(_desc()), ctypes.byref(tm.mlp_desc((64, 128, 64)))) == b"generic_fp32"
+    assert tm.lib.titans_mem_retrieve_path(ctypes.byref(_desc()), ctypes.byref(tm.mlp_desc((64, 128, 64)))) == b"generic_mfma"
     assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(T=0)), ctypes.byref(mlp)) == 0
     bad = ctypes.c_size_t(-1).value
     assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(C=0)), ctypes.byref(mlp)) == bad

@@ -202,6 +202,20 @@ def test_chunk_sizes_and_depths_fp32(C, widths):
     assert ey <= 1e-4 and et <= 1e-4 and es <= 1e-4
 
 
+@pytest.mark.parametrize("C", [1, 5, 37, 64, 128])
+@pytest.mark.parametrize("widths", [(16, 16), (16, 32, 16), (8, 24, 12, 8), (16, 40, 24, 32, 16)])
+def test_chunk_sizes_and_depths_bf16_generic(C, widths):
+    """Shapes outside the fused kernels with bf16 I/O: the generic kernel on bf16 MFMA."""
+    wl, inp = _small(widths=widths, B=2, T=150, H=3, C=C, io="bf16", seed=C)
+    dev = to_device(inp)
+    log(f"case bf16 generic {widths} C={C}")
+    assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == "generic_mfma"
+    y, thT, sT = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (1, 2)]
+    check_pairs(wl, y, thT, sT, pairs, oracle_seq(inp, pairs))
+
+
 def test_bf16_small_ragged():
     wl, inp = _small(widths=(64, 256, 64), B=1, T=200, H=2, C=64, io="bf16")
     log("case bf16 ragged T=200 C=64")
@@ -287,6 +301,7 @@ def test_invalid_arguments_raise():
 # ----------------------------------------------------------------- retrieve
 
 @pytest.mark.parametrize("io,widths", [("f32", (16, 32, 16)), ("f32", (8, 24, 12, 8)),
+                                       ("bf16", (16, 32, 16)), ("bf16", (8, 24, 12, 8)),
                                        ("bf16", (64, 256, 64))])
 def test_retrieve_matches_oracle(io, widths):
     wl, inp = _small(widths=widths, B=2, T=45, H=3, io=io)
@@ -302,7 +317,7 @@ def test_retrieve_matches_oracle(io, widths):
 
 @pytest.mark.parametrize("T", [1, 63, 1023, 1025, 2100])
 def test_retrieve_mfma_matches_generic_and_oracle(T, monkeypatch):
-    """The bf16 MFMA retrieve (64-256-64) against the generic fp32 kernel and the oracle,
+    """The fused bf16 MFMA retrieve (64-256-64) against the generic kernel and the oracle,
     with per-batch weights, strided q and y and a ragged token count."""
     wl, inp = _small(widths=(64, 256, 64), B=2, T=T, H=3, io="bf16", seed=T)
     dev = to_device(inp)
@@ -316,7 +331,7 @@ def test_retrieve_mfma_matches_generic_and_oracle(T, monkeypatch):
     y = torch.empty(B, T, H, 2 * wl.d, dtype=torch.bfloat16, device="cuda")[..., : wl.d]
     y = tm.retrieve(q, theta, wl.widths, y=y)
     monkeypatch.setenv("TITANS_MEM_FORCE_GENERIC", "1")
-    assert tm.retrieve_path(q, wl.widths) == "generic_fp32"
+    assert tm.retrieve_path(q, wl.widths) == "generic_mfma"
     y2 = tm.retrieve(q, theta, wl.widths)
     torch.cuda.synchronize()
     sel = slice(0, T, max(1, T // 200))
@@ -363,7 +378,7 @@ def test_fused_matches_oracle_and_generic(kernel, monkeypatch):
     pairs = [(0, 0), (1, 2), (0, 1)]
     check_pairs(wl, y1, t1, s1, pairs, oracle_seq(inp, pairs))
     monkeypatch.setenv("TITANS_MEM_FORCE_GENERIC", "1")
-    assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == "generic_fp32"
+    assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == "generic_mfma"
     y2, t2, s2 = run_gpu(dev, wl)
     torch.cuda.synchronize()
     ey = y_rel_err(to_f64(y1), to_f64(y2))
