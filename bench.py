@@ -56,8 +56,8 @@ def kernel_source_digest(kernel):
     """sha256 of the source file that defines the kernel (traffic is void once it changes)."""
     import hashlib
 
-    src = {"scan_mfma_kernel": "scan_mfma.hip", "scan_generic_kernel": "scan_generic.hip"}.get(
-        kernel, "scan_pair.hip")
+    src = {"scan_mfma_kernel": "scan_mfma.hip", "scan_generic_kernel": "scan_generic.hip",
+           "phase_kernel": "scan_phased.hip"}.get(kernel, "scan_pair.hip")
     with open(os.path.join(ROOT, "sequence_models_amd", "csrc", src), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
@@ -204,12 +204,20 @@ def main():
         kernel = ("clear_pair_flags + pair_coef_kernel + scan_pair_kernel" if path == "fused_pair"
                   else "scan_mfma_kernel")
         bound, peak, dtype = "mfma", PEAKS["mfma_bf16"], "bf16"
-    elif path == "generic_mfma":  # bf16 MFMA products, fp32 accumulation
-        bound, peak, kernel, dtype = "mfma", PEAKS["mfma_bf16"], "scan_generic_kernel", "bf16"
+    elif path in ("generic_mfma", "phased_mfma"):  # bf16 MFMA products, fp32 accumulation
+        kernel = "scan_generic_kernel" if path == "generic_mfma" else "phase_kernel"
+        bound, peak, dtype = "mfma", PEAKS["mfma_bf16"], "bf16"
     else:  # fp32 FMAs on the vector ALUs
-        bound, peak, kernel, dtype = "alu", PEAKS["valu_f32"], "scan_generic_kernel", "f32"
-    parallelism = {"fused_pair": "one GPU; two workgroups (one XCD) per (batch row, head) memory"}.get(
-        path, "one GPU; one workgroup per (batch row, head) memory")
+        kernel = "scan_generic_kernel" if path == "generic_fp32" else "phase_kernel"
+        bound, peak, dtype = "alu", PEAKS["valu_f32"], "f32"
+    parallelism = {
+        "fused_pair": "one GPU; two workgroups (one XCD) per (batch row, head) memory",
+        "phased_mfma": "one GPU; every chunk product split into 64x64 tiles of all memories, "
+                       "4L-2 launches per chunk",
+    }.get(path, "one GPU; one workgroup per (batch row, head) memory")
+    if path == "phased_fp32":
+        parallelism = "one GPU; every chunk product split into 64x64 tiles of all memories, " \
+                      "4L-2 launches per chunk"
     result = {
         "metric": METRIC,
         "value": tokens / (ms_per_step * 1e-3),

@@ -149,8 +149,8 @@ def scan_workspace_size(q, chunk, widths) -> int:
 
 
 def scan_path(q, chunk, widths) -> str:
-    """Name of the kernel that serves this shape: "fused_pair", "fused_mfma", "generic_mfma"
-    (bf16 I/O) or "generic_fp32" (fp32 I/O)."""
+    """Name of the kernel that serves this shape: "fused_pair", "fused_mfma", "phased_mfma" /
+    "phased_fp32" (layers of 128+ units; bf16 / fp32 I/O) or "generic_mfma" / "generic_fp32"."""
     d = make_desc(q, chunk, q, None, None, None)
     r = lib.titans_mem_scan_path(ctypes.byref(d), ctypes.byref(mlp_desc(widths)))
     if r is None:

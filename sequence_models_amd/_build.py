@@ -24,6 +24,7 @@ FLAGS = [
 SOURCES = {
     "abi.hip": [],
     "scan_generic.hip": [],
+    "scan_phased.hip": [],
     "scan_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "scan_pair.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "retrieve_mfma.hip": [],

@@ -212,7 +212,19 @@ static int64_t device_cus() {
     return n;
 }
 
-enum class Path { Generic, Fused, Pair };
+enum class Path { Generic, Phased, Fused, Pair };
+
+// Within the generic family: the chain of GPU-wide launches for memories with a layer of
+// 128 or more units (their chunk products span several 64 x 64 tiles), else one workgroup
+// per memory.  TITANS_MEM_GENERIC_MODE=single / phased picks one for testing.
+static Path generic_path(const titans::ScanArgs& a) {
+    const char* env = getenv("TITANS_MEM_GENERIC_MODE");
+    if (env && strcmp(env, "single") == 0) return Path::Generic;
+    if (env && strcmp(env, "phased") == 0) return Path::Phased;
+    int maxw = 0;
+    for (int l = 0; l <= a.L; ++l) maxw = a.n[l] > maxw ? a.n[l] : maxw;
+    return maxw >= 128 ? Path::Phased : Path::Generic;
+}
 
 // Which kernel serves a (validated) problem.  The 64-256-64 bf16 memory runs on pairs of
 // workgroups (any chunk length that is a multiple of 64) while the pairs fit the device at
@@ -221,13 +233,13 @@ enum class Path { Generic, Fused, Pair };
 // workgroup per memory.
 static Path choose_path(const titans::ScanArgs& a) {
     const char* env = getenv("TITANS_MEM_FORCE_GENERIC");
-    if (env && env[0] == '1') return Path::Generic;
+    if (env && env[0] == '1') return generic_path(a);
     env = getenv("TITANS_MEM_FUSED_SINGLE");
     const bool single = env && env[0] == '1';
     if (!single && titans::scan_pair_supported(a) &&
         titans::scan_pair_workgroups(a) <= device_cus())
         return Path::Pair;
-    return titans::scan_mfma_supported(a) ? Path::Fused : Path::Generic;
+    return titans::scan_mfma_supported(a) ? Path::Fused : generic_path(a);
 }
 
 const char* titans_mem_scan_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp) {
@@ -236,6 +248,7 @@ const char* titans_mem_scan_path(const titans_scan_desc* desc, const titans_mlp_
     switch (choose_path(a)) {
         case Path::Pair: return "fused_pair";
         case Path::Fused: return "fused_mfma";
+        case Path::Phased: return a.io == TITANS_BF16 ? "phased_mfma" : "phased_fp32";
         default: return a.io == TITANS_BF16 ? "generic_mfma" : "generic_fp32";
     }
 }
@@ -247,6 +260,7 @@ size_t titans_mem_scan_workspace_size(const titans_scan_desc* desc, const titans
     switch (choose_path(a)) {
         case Path::Pair: return titans::scan_pair_workspace_bytes(a);
         case Path::Fused: return 0;
+        case Path::Phased: return titans::scan_phased_workspace_bytes(a);
         default: return titans::scan_generic_workspace_bytes(a);
     }
 }
@@ -351,7 +365,8 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
     const Path path = a.T > 0 ? choose_path(a) : Path::Generic;
     hipError_t e = path == Path::Pair    ? titans::launch_scan_pair(a, hs)
                    : path == Path::Fused ? titans::launch_scan_mfma(a, hs)
-                                         : titans::launch_scan_generic(a, hs);
+                   : path == Path::Phased ? titans::launch_scan_phased(a, hs)
+                                          : titans::launch_scan_generic(a, hs);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
     return TITANS_OK;
 }

@@ -24,10 +24,13 @@
 //   S_l <- p S_l + Delta_l^T diag(w) Hk_{l-1}.
 #include <hip/hip_runtime.h>
 
+#include "generic_util.h"
 #include "titans_internal.h"
 
 namespace titans {
 namespace {
+
+using namespace generic;
 
 constexpr int kThreads = 256;
 constexpr int kTile = 64;   // output tile edge
@@ -42,32 +45,6 @@ constexpr int kGemmLds = kGemmLdsF32 > kGemmLdsMfma ? kGemmLdsF32 : kGemmLdsMfma
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-    return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
-
-// Round to nearest even; NaN stays NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
-}
-
-__device__ __forceinline__ float load_io(const void* p, int64_t idx, int io) {
-    return io == TITANS_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[idx])
-                             : static_cast<const float*>(p)[idx];
-}
-
-__device__ __forceinline__ void store_io(void* p, int64_t idx, int io, float x) {
-    if (io == TITANS_BF16)
-        static_cast<uint16_t*>(p)[idx] = f32_to_bf16(x);
-    else
-        static_cast<float*>(p)[idx] = x;
-}
-
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 // A(i, k) = p[i*si + k*sk] * (kscale ? kscale[k] : 1)
 struct MatA {

@@ -1,0 +1,726 @@
+// Chunked Titans memory scan as a chain of GPU-wide phases, for memories whose chunk work
+// is too large for one compute unit (the deep 128-512-512-512-128 memory holds 2.6 MB of
+// weights and 2.6 MB of momentum per head, and a few such heads leave most of the GPU
+// idle when each runs on one workgroup).
+//
+// The algebra is the generic kernel's (gradients at the chunk-start weights, the
+// summary page's "tensorized mini-batch" form; the momentum / forget recurrence unrolled
+// into per-chunk coefficients a, b, c, w, p; reads at the in-chunk weights
+//   U_l = diag(a) Hq W_l^T - diag(b) Hq S_l^T - (Cm o Hq Hk^T) Delta_l,
+// chunk-end carry W_l <- a_n W_l - b_n S_l - Delta_l^T diag(c_n) Hk, S_l <- p S_l +
+// Delta_l^T diag(w) Hk).  What changes is how a chunk's work is spread: each matrix
+// product of the chunk is cut into 64 x 64 output tiles, the tiles of every memory form
+// one kernel launch, and consecutive launches on the stream are the barriers between
+// dependent products.  Products that depend on the same inputs share a launch:
+//   launch 1          key forward of layer 1, the layer-1 read products (Cm o Q K^T and
+//                     a Q W1^T - b Q S1^T), and the next chunk's coefficients and staged
+//                     Q, K (double-buffered by chunk parity);
+//   launches 2..L     key forward of layers 2..L (SiLU and SiLU' in the epilogue; the last
+//                     layer's epilogue forms Delta_L = 2 (O - V));
+//   L - 1 launches    backward Delta_{l-1} = (Delta_l W_l) o SiLU'(Z_{l-1});
+//   2L - 1 launches   reads: U_l -= (Cm o Hq Hk^T) Delta_l then SiLU (or y for l = L),
+//                     then the next layer's read products; the last one also carries every
+//                     layer's W_l and S_l to the chunk end (all of their readers are done).
+// That is 4L - 2 launches per chunk.  With bf16 I/O a tile stages its whole reduction
+// extent (<= 512) of both operands in LDS as bf16 (one load latency per tile) and runs
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation; with fp32 I/O it runs 16-wide fp32 FMA
+// steps.  State and intermediates are fp32 in HBM (theta_T / s_T and the workspace).
+#include <hip/hip_runtime.h>
+
+#include "generic_util.h"
+#include "titans_internal.h"
+
+namespace titans {
+namespace {
+
+using namespace generic;
+
+constexpr int kThreads = 256;
+constexpr int kTile = 64;
+constexpr int kKStep = 16;  // fp32 reduction step
+constexpr int kPad = 4;
+constexpr int kMaxSeg = 6;
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+// Operand of a tile product: element (r, k) = p[r * sr + k * sk] * (ks ? ks[k] : 1)
+// * (rs ? rs[r] : 1).  Every operand here has sk == 1 or sr == 1.
+struct Opnd {
+    const float* p;
+    int64_t sr, sk;
+    const float* ks;
+    const float* rs = nullptr;
+};
+
+// 16-byte loads are used when the operand's base and its stride across the vector
+// direction keep every group of four 16-byte aligned.
+__device__ __forceinline__ bool vec_ok(const Opnd& X) {
+    const int64_t s = X.sk == 1 ? X.sr : X.sk;
+    return ((reinterpret_cast<uintptr_t>(X.p) & 15u) == 0) && (s & 3) == 0;
+}
+
+// Four consecutive elements along the contiguous index starting at (r, k): k .. k+3 of
+// row r when sk == 1, rows r .. r+3 of column k otherwise; zero outside R x K.
+__device__ __forceinline__ f32x4_t load4(const Opnd& X, bool vec, int r, int R, int k, int K) {
+    if (X.sk == 1) {
+        const float* q = X.p + (int64_t)r * X.sr + k;
+        if (vec && r < R && k + 3 < K) return *reinterpret_cast<const f32x4_t*>(q);
+        f32x4_t v;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = (r < R && k + u < K) ? q[u] : 0.f;
+        return v;
+    }
+    const float* q = X.p + r + (int64_t)k * X.sk;
+    if (vec && r + 3 < R && k < K) return *reinterpret_cast<const f32x4_t*>(q);
+    f32x4_t v;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = (r + u < R && k < K) ? q[u] : 0.f;
+    return v;
+}
+
+// Where thread tid's two groups of a 32-wide k slice sit in the 64-row tile: with
+// sk == 1, rows (tid >> 3) + 32 p and k = 4 (tid & 7) .. +3 (eight lanes read 128
+// contiguous bytes of a row); with sr == 1, rows 4 (tid & 15) .. +3 and k = (tid >> 4) +
+// 16 p (sixteen lanes read 256 contiguous bytes of a column).
+__device__ __forceinline__ void grp_pos(const Opnd& X, int tid, int p, int& rr, int& kk) {
+    if (X.sk == 1) { rr = (tid >> 3) + 32 * p; kk = 4 * (tid & 7); }
+    else { rr = 4 * (tid & 15); kk = (tid >> 4) + 16 * p; }
+}
+
+__device__ __forceinline__ void store4(__bf16* dst, int ld, const Opnd& X, int rr, int k, int K,
+                                       int gr, int R, f32x4_t v) {
+    if (X.sk == 1) {
+        bf16x4_t o;
+        const float rsc = (X.rs && gr < R) ? X.rs[gr] : 1.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float x = v[u] * rsc;
+            if (X.ks && k + u < K) x *= X.ks[k + u];
+            o[u] = (__bf16)x;
+        }
+        *reinterpret_cast<bf16x4_t*>(dst + rr * ld + k) = o;
+    } else {
+        const float ksc = (X.ks && k < K) ? X.ks[k] : 1.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float x = v[u] * ksc;
+            if (X.rs && gr + u < R) x *= X.rs[gr + u];
+            dst[(rr + u) * ld + k] = (__bf16)x;
+        }
+    }
+}
+
+constexpr int kSlices = 8;  // 32-wide k slices per staging batch (256 k)
+
+// Stage rows r0 .. r0+63 (< R) x k < K of X into dst[r][k] as bf16 (row length ld,
+// zero-filled up to Kp), for up to three operands at once.  Each batch issues every
+// 16-byte load of its 256 k before the first LDS store, so a tile waits for a load
+// latency once per batch.
+template <int kN>
+__device__ __forceinline__ void stage(__bf16* const* dst, const Opnd* X, const int* r0,
+                                      const int* R, int K, int Kp, int ld) {
+    const int tid = threadIdx.x;
+    bool vec[kN];
+#pragma unroll
+    for (int o = 0; o < kN; ++o) vec[o] = vec_ok(X[o]);
+    for (int s0 = 0; s0 < Kp; s0 += 32 * kSlices) {
+        f32x4_t v[kN][kSlices][2];
+#pragma unroll
+        for (int o = 0; o < kN; ++o)
+#pragma unroll
+            for (int sl = 0; sl < kSlices; ++sl)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    int rr, kk;
+                    grp_pos(X[o], tid, p, rr, kk);
+                    const int k = s0 + 32 * sl + kk;
+                    v[o][sl][p] = (s0 + 32 * sl < Kp)
+                                      ? load4(X[o], vec[o], r0[o] + rr, R[o], k, K)
+                                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+        for (int o = 0; o < kN; ++o)
+#pragma unroll
+            for (int sl = 0; sl < kSlices; ++sl)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    if (s0 + 32 * sl >= Kp) continue;
+                    int rr, kk;
+                    grp_pos(X[o], tid, p, rr, kk);
+                    store4(dst[o], ld, X[o], rr, s0 + 32 * sl + kk, K, r0[o] + rr, R[o], v[o][sl][p]);
+                }
+    }
+}
+
+// LDS bytes of a bf16 tile product with reduction extent K and n staged operands.
+__host__ __device__ constexpr int mfma_lds_bytes(int K, int n = 2) {
+    return n * kTile * (((K + 31) & ~31) + 8) * 2;
+}
+
+// acc[tn] += A B^T over the staged k range for wave w's rows 16w .. 16w+15 of the tile.
+// Operand layouts of v_mfma_f32_16x16x32_bf16: lane l (g = l / 16, j = l % 16) holds
+// A[j][k] and B[k][j] for k in {4g .. 4g+3, 16+4g .. 16+4g+3}; the result D[4g + r][j].
+__device__ __forceinline__ void mfma_tile(const __bf16* As, const __bf16* Bs, int Kp, int ld,
+                                          f32x4_t* acc) {
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6, g = (tid & 63) >> 4, j = tid & 15;
+    const __bf16* ar = As + (16 * wv + j) * ld + 4 * g;
+    const __bf16* br = Bs + j * ld + 4 * g;
+#pragma unroll 2
+    for (int k0 = 0; k0 < Kp; k0 += 32) {
+        const bf16x8_t af = __builtin_shufflevector(*reinterpret_cast<const bf16x4_t*>(ar + k0),
+                                                    *reinterpret_cast<const bf16x4_t*>(ar + k0 + 16),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) {
+            const __bf16* b = br + 16 * tn * ld + k0;
+            const bf16x8_t bf = __builtin_shufflevector(*reinterpret_cast<const bf16x4_t*>(b),
+                                                        *reinterpret_cast<const bf16x4_t*>(b + 16),
+                                                        0, 1, 2, 3, 4, 5, 6, 7);
+            acc[tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[tn], 0, 0, 0);
+        }
+    }
+}
+
+// epi(i, j, v) for every in-range element of the tile, each by exactly one thread (the
+// same thread for the same (i, j) in every tile call).
+template <class Epi>
+__device__ __forceinline__ void tile_epilogue(int i0, int j0, int M, int N, const f32x4_t* acc,
+                                              Epi epi) {
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6, g = (tid & 63) >> 4, j = tid & 15;
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 16 * wv + 4 * g + r, jc = j0 + 16 * tn + j;
+            if (i < M && jc < N) epi(i, jc, acc[tn][r]);
+        }
+}
+
+__device__ __forceinline__ void zero_acc(f32x4_t* acc) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+// out(i, j) = sum_{k < K} A(i, k) B(j, k) for the 64 x 64 tile at (i0, j0) of an M x N
+// result (K <= 512), bf16 operands, fp32 accumulation; epi(i, j, out).
+template <class Epi>
+__device__ __forceinline__ void tile_mfma(int i0, int j0, int M, int N, int K, Opnd A, Opnd B, __bf16* lds,
+                          Epi epi) {
+    const int Kp = (K + 31) & ~31, ld = Kp + 8;
+    __bf16* const dst[2] = {lds, lds + kTile * ld};
+    const Opnd X[2] = {A, B};
+    const int r0[2] = {i0, j0}, R[2] = {M, N};
+    stage<2>(dst, X, r0, R, K, Kp, ld);
+    __syncthreads();
+    f32x4_t acc[4];
+    zero_acc(acc);
+    mfma_tile(dst[0], dst[1], Kp, ld, acc);
+    tile_epilogue(i0, j0, M, N, acc, epi);
+    __syncthreads();  // the LDS tiles may be restaged by the next product
+}
+
+// out = A1 B1^T + A2 B2^T (one accumulator, two staging rounds).
+template <class Epi>
+__device__ __forceinline__ void tile_mfma_sum2(int i0, int j0, int M, int N, int K, Opnd A1, Opnd B1, Opnd A2,
+                               Opnd B2, __bf16* lds, Epi epi) {
+    const int Kp = (K + 31) & ~31, ld = Kp + 8;
+    __bf16* const dst[2] = {lds, lds + kTile * ld};
+    const int r0[2] = {i0, j0}, R[2] = {M, N};
+    f32x4_t acc[4];
+    zero_acc(acc);
+    {
+        const Opnd X[2] = {A1, B1};
+        stage<2>(dst, X, r0, R, K, Kp, ld);
+        __syncthreads();
+        mfma_tile(dst[0], dst[1], Kp, ld, acc);
+        __syncthreads();
+    }
+    {
+        const Opnd X[2] = {A2, B2};
+        stage<2>(dst, X, r0, R, K, Kp, ld);
+        __syncthreads();
+        mfma_tile(dst[0], dst[1], Kp, ld, acc);
+    }
+    tile_epilogue(i0, j0, M, N, acc, epi);
+    __syncthreads();
+}
+
+// out1 = A1 B^T and out2 = A2 B^T (three operands staged once); epi(i, j, out1, out2).
+template <class Epi>
+__device__ __forceinline__ void tile_mfma_dual(int i0, int j0, int M, int N, int K, Opnd A1, Opnd A2, Opnd B,
+                               __bf16* lds, Epi epi) {
+    const int Kp = (K + 31) & ~31, ld = Kp + 8;
+    __bf16* const dst[3] = {lds, lds + kTile * ld, lds + 2 * kTile * ld};
+    const Opnd X[3] = {A1, A2, B};
+    const int r0[3] = {i0, i0, j0}, R[3] = {M, M, N};
+    stage<3>(dst, X, r0, R, K, Kp, ld);
+    __syncthreads();
+    f32x4_t acc1[4], acc2[4];
+    zero_acc(acc1);
+    zero_acc(acc2);
+    mfma_tile(dst[0], dst[2], Kp, ld, acc1);
+    mfma_tile(dst[1], dst[2], Kp, ld, acc2);
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6, g = (tid & 63) >> 4, j = tid & 15;
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 16 * wv + 4 * g + r, jc = j0 + 16 * tn + j;
+            if (i < M && jc < N) epi(i, jc, acc1[tn][r], acc2[tn][r]);
+        }
+    __syncthreads();
+}
+
+// The same contract in fp32 FMAs: 16-wide reduction steps staged in LDS, 4 x 4 outputs
+// per thread.
+template <class Epi>
+__device__ __forceinline__ void tile_f32(int i0, int j0, int M, int N, int K, Opnd A, Opnd B, float* lds,
+                         Epi epi) {
+    float* As = lds;  // [kKStep][kTile + kPad]
+    float* Bs = lds + kKStep * (kTile + kPad);
+    const int tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;
+    float acc[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = 0.0f;
+    for (int k0 = 0; k0 < K; k0 += kKStep) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = tid + kThreads * r;
+            int ii, kk;
+            if (A.sk == 1) { kk = e & 15; ii = e >> 4; } else { ii = e & 63; kk = e >> 6; }
+            int gi = i0 + ii, gk = k0 + kk;
+            float val = 0.0f;
+            if (gi < M && gk < K) {
+                val = A.p[(int64_t)gi * A.sr + (int64_t)gk * A.sk];
+                if (A.ks) val *= A.ks[gk];
+            }
+            As[kk * (kTile + kPad) + ii] = val;
+            if (B.sk == 1) { kk = e & 15; ii = e >> 4; } else { ii = e & 63; kk = e >> 6; }
+            gi = j0 + ii;
+            gk = k0 + kk;
+            val = 0.0f;
+            if (gi < N && gk < K) {
+                val = B.p[(int64_t)gi * B.sr + (int64_t)gk * B.sk];
+                if (B.ks) val *= B.ks[gk];
+            }
+            Bs[kk * (kTile + kPad) + ii] = val;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < kKStep; ++kk) {
+            float av[4], bv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) av[r] = As[kk * (kTile + kPad) + ty + 16 * r];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) bv[c] = Bs[kk * (kTile + kPad) + tx + 16 * c];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int i = i0 + ty + 16 * r, j = j0 + tx + 16 * c;
+            if (i < M && j < N) epi(i, j, acc[r][c]);
+        }
+}
+
+constexpr int kF32Lds = 2 * kKStep * (kTile + kPad) * 4;  // bytes
+
+template <bool kMfma, class Epi>
+__device__ __forceinline__ void tile(int i0, int j0, int M, int N, int K, Opnd A, Opnd B,
+                                     void* lds, Epi epi) {
+    if constexpr (kMfma)
+        tile_mfma(i0, j0, M, N, K, A, B, static_cast<__bf16*>(lds), epi);
+    else
+        tile_f32(i0, j0, M, N, K, A, B, static_cast<float*>(lds), epi);
+}
+
+// Float offsets of the per-memory workspace regions.
+struct PhLayout {
+    int64_t coef[2];   // by chunk parity: a[C+1], b[C+1], w[C], p, -b[C+1]
+    int64_t cm[2];     // by chunk parity: (C+1) x C, row t = c_{t, j}
+    int64_t qst[2];    // by chunk parity: Q, C x d
+    int64_t kst[2];    // by chunk parity: K (= Hk_0), C x d
+    int64_t hk[TITANS_MAX_LAYERS];      // l = 1..L-1: C x n_l
+    int64_t sp[TITANS_MAX_LAYERS];      // l = 1..L-1: C x n_l, SiLU'(Z_l)
+    int64_t dl[TITANS_MAX_LAYERS + 1];  // l = 1..L:   C x n_l
+    int64_t hq[2];     // U_l / Hq_l in buffer l & 1: C x maxw
+    int64_t mq;        // C x C
+    int64_t per_seq;
+};
+
+__host__ __device__ inline PhLayout ph_layout(int C, int L, const int* n) {
+    auto r64 = [](int64_t x) { return (x + 63) & ~int64_t(63); };
+    PhLayout w{};
+    int maxw = 0;
+    for (int l = 0; l <= L; ++l) maxw = n[l] > maxw ? n[l] : maxw;
+    int64_t o = 0;
+    for (int p = 0; p < 2; ++p) {
+        w.coef[p] = o; o += r64(4 * (int64_t)C + 4);
+        w.cm[p] = o; o += r64((int64_t)(C + 1) * C);
+        w.qst[p] = o; o += r64((int64_t)C * n[0]);
+        w.kst[p] = o; o += r64((int64_t)C * n[0]);
+    }
+    for (int l = 1; l < L; ++l) { w.hk[l] = o; o += r64((int64_t)C * n[l]); }
+    for (int l = 1; l < L; ++l) { w.sp[l] = o; o += r64((int64_t)C * n[l]); }
+    for (int l = 1; l <= L; ++l) { w.dl[l] = o; o += r64((int64_t)C * n[l]); }
+    w.hq[0] = o; o += r64((int64_t)C * maxw);
+    w.hq[1] = o; o += r64((int64_t)C * maxw);
+    w.mq = o; o += r64((int64_t)C * C);
+    w.per_seq = o;
+    return w;
+}
+
+enum Task : int { kPrep = 0, kFwd, kBwd, kMq, kU, kQb, kCarry };
+
+// One segment of a launch: `count` blocks of one task on layer l; tiles are numbered
+// row-major over ceil(M/64) x tj tiles.
+struct Seg {
+    int task, l, tj, count;
+};
+
+struct Phase {
+    PhLayout wl;  // workspace layout (in the argument block: indexed by layer at run time)
+    int nseg;
+    Seg seg[kMaxSeg];
+    int64_t c0;  // first token of the chunk the products serve
+    int n;       // its length
+    int par;     // its parity buffer
+    int64_t c0p; // chunk a kPrep task stages (into parity buffer ppar)
+    int np;
+    int ppar;
+};
+
+template <bool kMfma>
+__global__ void __launch_bounds__(kThreads) phase_kernel(ScanArgs a, Phase ph) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __shared__ float s_al[256], s_et[256], s_be[256];
+
+    // find this block's segment (unrolled: no dynamic indexing of the argument block)
+    int t = blockIdx.x;
+    Seg sg = ph.seg[0];
+#pragma unroll
+    for (int s = 1; s < kMaxSeg; ++s) {
+        if (s < ph.nseg && t >= sg.count) {
+            t -= sg.count;
+            sg = ph.seg[s];
+        }
+    }
+    const int i0 = (t / sg.tj) * kTile, j0 = (t % sg.tj) * kTile;
+
+    const int64_t seq = blockIdx.y;
+    const int64_t b = seq / a.H, h = seq % a.H;
+    const int tid = threadIdx.x;
+    const int L = a.L, C = a.C, d = a.n[0];
+    const PhLayout& wl = ph.wl;
+    float* ws = static_cast<float*>(a.ws) + seq * wl.per_seq;
+    float* theta = a.thetaT + b * a.ss[0] + h * a.ss[1];
+    float* mom = a.sT + b * a.ss[0] + h * a.ss[1];
+    const int64_t qbase = b * a.qs[0] + h * a.qs[2];
+    const int64_t ybase = b * a.ys[0] + h * a.ys[2];
+    const int64_t gbase = b * a.gs[0] + h * a.gs[2];
+
+    if (sg.task == kPrep) {
+        // gates, Q and K of chunk (c0p, np) -> coefficients and staged Q, K in buffer ppar
+        const int n = ph.np, pp = ph.ppar;
+        const int64_t c0 = ph.c0p;
+        for (int i = tid; i < n; i += kThreads) {
+            const int64_t gi = gbase + (c0 + i) * a.gs[1];
+            s_al[i] = a.alpha[gi];
+            s_et[i] = a.eta[gi];
+            s_be[i] = a.beta[gi];
+        }
+        float* Q = ws + wl.qst[pp];
+        float* K = ws + wl.kst[pp];
+        for (int e = tid; e < n * d; e += kThreads) {
+            const int r = e / d, c = e % d;
+            const int64_t src = qbase + (c0 + r) * a.qs[1] + c;
+            K[e] = load_io(a.k, src, a.io);
+            Q[e] = load_io(a.q, src, a.io);
+        }
+        __syncthreads();
+        // thread j owns column j of Cm: c_{t,j} for t = 0..n (the generic kernel's recurrence)
+        float* ca = ws + wl.coef[pp];
+        float* cb = ca + (C + 1);
+        float* cw = cb + (C + 1);
+        float* cp = cw + C;
+        float* Cm = ws + wl.cm[pp];
+        const int j = tid;
+        float Bj = 0.0f, cj = 0.0f, at = 1.0f, bt = 0.0f, pb = 1.0f;
+        const float omb_j = (j < n) ? 1.0f - s_be[j] : 0.0f;
+        if (j < n) Cm[j] = 0.0f;
+        if (j == 0) { ca[0] = 1.0f; cb[0] = 0.0f; }
+        for (int tt = 0; tt < n; ++tt) {
+            const float al = s_al[tt], et = s_et[tt], be = s_be[tt];
+            pb *= be;
+            if (j < tt) Bj *= be;
+            else if (j == tt) Bj = 1.0f;
+            const float keep = 1.0f - al;
+            at *= keep;
+            bt = keep * bt + et * pb;
+            cj = keep * cj + ((j <= tt) ? et * omb_j * Bj : 0.0f);
+            if (j < n) Cm[(int64_t)(tt + 1) * C + j] = cj;
+            if (j == 0) { ca[tt + 1] = at; cb[tt + 1] = bt; }
+        }
+        if (j < n) cw[j] = omb_j * Bj;
+        if (j == 0) cp[0] = pb;
+        __syncthreads();
+        for (int i = tid; i <= n; i += kThreads) cp[1 + i] = -cb[i];
+        return;
+    }
+
+    const int n = ph.n, par = ph.par, l = sg.l;
+    const int64_t c0 = ph.c0;
+    const float* coef_a = ws + wl.coef[par];
+    const float* coef_b = coef_a + (C + 1);
+    const float* coef_w = coef_b + (C + 1);
+    const float* coef_p = coef_w + C;
+    const float* coef_nb = coef_p + 1;  // -b, written by the coefficient task
+    const float* Cm = ws + wl.cm[par];
+    const float* Kst = ws + wl.kst[par];
+    const float* Qst = ws + wl.qst[par];
+    const int nin = a.n[l - 1], nout = a.n[l];
+    const float* Hk_in = l == 1 ? Kst : ws + wl.hk[l - 1];  // Hk_{l-1}
+    const float* Hq_in = l == 1 ? Qst : ws + wl.hq[(l - 1) & 1];
+    float* U = ws + wl.hq[l & 1];
+    float* Dl = ws + wl.dl[l];
+    float* Mq = ws + wl.mq;
+    float* W = theta + a.off[l];
+    float* S = mom + a.off[l];
+    void* lds = smem;
+
+    switch (sg.task) {
+        case kFwd: {  // Z_l = Hk_{l-1} W_l^T
+            const Opnd A{Hk_in, nin, 1, nullptr}, Bo{W, nin, 1, nullptr};
+            if (l < L) {
+                float* Hout = ws + wl.hk[l];
+                float* Sp = ws + wl.sp[l];
+                tile<kMfma>(i0, j0, n, nout, nin, A, Bo, lds, [&](int i, int jj, float z) {
+                    const float sg_ = sigmoidf_(z);
+                    Hout[i * nout + jj] = z * sg_;
+                    Sp[i * nout + jj] = sg_ * (1.0f + z * (1.0f - sg_));
+                });
+            } else {
+                tile<kMfma>(i0, j0, n, nout, nin, A, Bo, lds, [&](int i, int jj, float z) {
+                    const float vv = load_io(a.v, qbase + (c0 + i) * a.qs[1] + jj, a.io);
+                    Dl[i * nout + jj] = 2.0f * (z - vv);
+                });
+            }
+            break;
+        }
+        case kBwd: {  // Delta_{l-1} = (Delta_l W_l) o SiLU'(Z_{l-1})
+            float* Dp = ws + wl.dl[l - 1];
+            const float* Sp = ws + wl.sp[l - 1];
+            tile<kMfma>(i0, j0, n, nin, nout, Opnd{Dl, nout, 1, nullptr}, Opnd{W, 1, nin, nullptr},
+                        lds, [&](int i, int jj, float x) { Dp[i * nin + jj] = x * Sp[i * nin + jj]; });
+            break;
+        }
+        case kMq: {  // Mq = Cm o (Hq_{l-1} Hk_{l-1}^T), strictly lower triangular
+            tile<kMfma>(i0, j0, n, n, nin, Opnd{Hq_in, nin, 1, nullptr},
+                        Opnd{Hk_in, nin, 1, nullptr}, lds, [&](int i, int jj, float x) {
+                            Mq[i * C + jj] = (jj < i) ? Cm[(int64_t)i * C + jj] * x : 0.0f;
+                        });
+            break;
+        }
+        case kU: {  // U_l = diag(a) Hq W_l^T - diag(b) Hq S_l^T
+            if constexpr (kMfma) {  // one accumulator: rows of Hq scaled by a, then by -b
+                tile_mfma_sum2(i0, j0, n, nout, nin, Opnd{Hq_in, nin, 1, nullptr, coef_a},
+                               Opnd{W, nin, 1, nullptr}, Opnd{Hq_in, nin, 1, nullptr, coef_nb},
+                               Opnd{S, nin, 1, nullptr}, static_cast<__bf16*>(lds),
+                               [&](int i, int jj, float x) { U[i * nout + jj] = x; });
+            } else {
+                const Opnd A{Hq_in, nin, 1, nullptr};
+                tile<kMfma>(i0, j0, n, nout, nin, A, Opnd{W, nin, 1, nullptr}, lds,
+                            [&](int i, int jj, float x) { U[i * nout + jj] = coef_a[i] * x; });
+                tile<kMfma>(i0, j0, n, nout, nin, A, Opnd{S, nin, 1, nullptr}, lds,
+                            [&](int i, int jj, float x) { U[i * nout + jj] -= coef_b[i] * x; });
+            }
+            break;
+        }
+        case kQb: {  // U_l -= Mq Delta_l; then Hq_l = SiLU(U_l) in place, or y
+            const Opnd A{Mq, C, 1, nullptr}, Bo{Dl, 1, nout, nullptr};
+            if (l < L) {
+                tile<kMfma>(i0, j0, n, nout, n, A, Bo, lds, [&](int i, int jj, float x) {
+                    const float u = U[i * nout + jj] - x;
+                    U[i * nout + jj] = u * sigmoidf_(u);
+                });
+            } else {
+                tile<kMfma>(i0, j0, n, nout, n, A, Bo, lds, [&](int i, int jj, float x) {
+                    store_io(a.y, ybase + (c0 + i) * a.ys[1] + jj, a.io, U[i * nout + jj] - x);
+                });
+            }
+            break;
+        }
+        case kCarry: {  // W_l, S_l to the chunk end (W first: it needs the chunk-start S)
+            const float an = coef_a[n], bn = coef_b[n], pn = coef_p[0];
+            const float* crow = Cm + (int64_t)n * C;
+            const Opnd Bo{Hk_in, 1, nin, nullptr};
+            if constexpr (kMfma) {  // both products from one staging of Delta_l and Hk
+                tile_mfma_dual(i0, j0, nout, nin, n, Opnd{Dl, 1, nout, crow},
+                               Opnd{Dl, 1, nout, coef_w}, Bo, static_cast<__bf16*>(lds),
+                               [&](int i, int jj, float x1, float x2) {
+                                   const int64_t o = (int64_t)i * nin + jj;
+                                   const float s_old = S[o];
+                                   W[o] = an * W[o] - bn * s_old - x1;
+                                   S[o] = pn * s_old + x2;
+                               });
+                break;
+            }
+            tile<kMfma>(i0, j0, nout, nin, n, Opnd{Dl, 1, nout, crow}, Bo, lds,
+                        [&](int i, int jj, float x) {
+                            const int64_t o = (int64_t)i * nin + jj;
+                            W[o] = an * W[o] - bn * S[o] - x;
+                        });
+            tile<kMfma>(i0, j0, nout, nin, n, Opnd{Dl, 1, nout, coef_w}, Bo, lds,
+                        [&](int i, int jj, float x) {
+                            const int64_t o = (int64_t)i * nin + jj;
+                            S[o] = pn * S[o] + x;
+                        });
+            break;
+        }
+        default: break;
+    }
+}
+
+__global__ void copy_state_kernel(ScanArgs a) {
+    const int64_t seq = blockIdx.y;
+    const int64_t b = seq / a.H, h = seq % a.H;
+    float* th = a.thetaT + b * a.ss[0] + h * a.ss[1];
+    float* mo = a.sT + b * a.ss[0] + h * a.ss[1];
+    const float* th0 = a.theta0 + b * a.s0s[0] + h * a.s0s[1];
+    const float* mo0 = a.s0 + b * a.s0s[0] + h * a.s0s[1];
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.P;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        if (th != th0) th[i] = th0[i];
+        if (mo != mo0) mo[i] = mo0[i];
+    }
+}
+
+int tiles(int x) { return (x + kTile - 1) / kTile; }
+
+// Host-side builder of one launch.
+struct Launch {
+    Phase ph{};
+    int blocks = 0;
+    int lds = 0;   // bf16 staging bytes its largest product needs
+    void add(int task, int l, int M, int N, int K) {
+        Seg& s = ph.seg[ph.nseg++];
+        s.task = task;
+        s.l = l;
+        s.tj = task == kPrep ? 1 : tiles(N);
+        s.count = task == kPrep ? 1 : tiles(M) * s.tj;
+        blocks += s.count;
+        const int need = task == kPrep ? 0 : mfma_lds_bytes(K, task == kCarry ? 3 : 2);
+        if (need > lds) lds = need;
+    }
+};
+
+template <bool kMfma>
+hipError_t run(const ScanArgs& a, hipStream_t stream) {
+    const int64_t nseq = a.B * a.H;
+    const int L = a.L, C = a.C;
+    const int64_t nchunks = (a.T + C - 1) / C;
+    const PhLayout wl = ph_layout(C, L, a.n);
+    auto chunk_len = [&](int64_t c) { return (int)((a.T - c * C) < C ? (a.T - c * C) : C); };
+
+    if (kMfma) {
+        const hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&phase_kernel<true>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, mfma_lds_bytes(512));
+        if (e != hipSuccess) return e;
+    }
+    auto go = [&](Launch& x) -> hipError_t {
+        const size_t lds = kMfma ? (size_t)(x.lds > 0 ? x.lds : mfma_lds_bytes(32)) : (size_t)kF32Lds;
+        phase_kernel<kMfma><<<dim3((unsigned)x.blocks, (unsigned)nseq), kThreads, lds, stream>>>(a, x.ph);
+        return hipGetLastError();
+    };
+
+    {
+        const dim3 grid((unsigned)((a.P + 255) / 256 < 64 ? (a.P + 255) / 256 : 64), (unsigned)nseq);
+        copy_state_kernel<<<grid, 256, 0, stream>>>(a);
+        Launch p0;
+        p0.ph.wl = wl;
+        p0.ph.c0p = 0;
+        p0.ph.np = chunk_len(0);
+        p0.ph.ppar = 0;
+        p0.add(kPrep, 1, 0, 0, 0);
+        hipError_t e = go(p0);
+        if (e != hipSuccess) return e;
+    }
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int n = chunk_len(c), par = (int)(c & 1);
+        auto base = [&]() {
+            Launch x;
+            x.ph.wl = wl;
+            x.ph.c0 = c * C;
+            x.ph.n = n;
+            x.ph.par = par;
+            return x;
+        };
+        hipError_t e;
+        {  // key forward of layer 1, layer-1 read products, next chunk's coefficients
+            Launch x = base();
+            x.add(kFwd, 1, n, a.n[1], a.n[0]);
+            x.add(kMq, 1, n, n, a.n[0]);
+            x.add(kU, 1, n, a.n[1], a.n[0]);
+            if (c + 1 < nchunks) {
+                x.ph.c0p = (c + 1) * C;
+                x.ph.np = chunk_len(c + 1);
+                x.ph.ppar = par ^ 1;
+                x.add(kPrep, 1, 0, 0, 0);
+            }
+            if ((e = go(x)) != hipSuccess) return e;
+        }
+        for (int l = 2; l <= L; ++l) {
+            Launch x = base();
+            x.add(kFwd, l, n, a.n[l], a.n[l - 1]);
+            if ((e = go(x)) != hipSuccess) return e;
+        }
+        for (int l = L; l >= 2; --l) {
+            Launch x = base();
+            x.add(kBwd, l, n, a.n[l - 1], a.n[l]);
+            if ((e = go(x)) != hipSuccess) return e;
+        }
+        for (int l = 1; l <= L; ++l) {
+            if (l > 1) {
+                Launch x = base();
+                x.add(kMq, l, n, n, a.n[l - 1]);
+                x.add(kU, l, n, a.n[l], a.n[l - 1]);
+                if ((e = go(x)) != hipSuccess) return e;
+            }
+            Launch x = base();
+            x.add(kQb, l, n, a.n[l], n);
+            if (l == L)
+                for (int m = 1; m <= L; ++m) x.add(kCarry, m, a.n[m], a.n[m - 1], n);
+            if ((e = go(x)) != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+size_t scan_phased_workspace_bytes(const ScanArgs& a) {
+    const PhLayout w = ph_layout(a.C, a.L, a.n);
+    return (size_t)(a.B * a.H) * (size_t)w.per_seq * sizeof(float);
+}
+
+hipError_t launch_scan_phased(const ScanArgs& a, hipStream_t stream) {
+    if (a.B * a.H == 0) return hipSuccess;
+    return a.io == TITANS_BF16 ? run<true>(a, stream) : run<false>(a, stream);
+}
+
+}  // namespace titans

@@ -39,6 +39,11 @@ struct ScanArgs {
 size_t scan_generic_workspace_bytes(const ScanArgs& a);
 hipError_t launch_scan_generic(const ScanArgs& a, hipStream_t stream);
 
+// The generic scan as a chain of GPU-wide launches (4L - 2 per chunk), each spreading
+// one step's matrix products over 64 x 64 tiles of every memory; for wide memories.
+size_t scan_phased_workspace_bytes(const ScanArgs& a);
+hipError_t launch_scan_phased(const ScanArgs& a, hipStream_t stream);
+
 // Fused MFMA scan for the 64 -> 256 -> 64 memory, C = 64, bf16 I/O: one workgroup per
 // (b, h), state resident in registers, no workspace.
 bool scan_mfma_supported(const ScanArgs& a);

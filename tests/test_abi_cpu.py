@@ -67,11 +67,11 @@ def test_workspace_size_query(monkeypatch):
                                                  ctypes.byref(mlp)) == 16 * 99328 + 9 * 3 * 9472
     # chunks that are multiples of 64 run on the pair path too (64-token sub-chunks whose
     # gradients share the chunk-start weights); other lengths on the generic kernel
-    for C, path in ((128, b"fused_pair"), (256, b"fused_pair"), (96, b"generic_mfma"),
-                    (32, b"generic_mfma")):
+    for C, path in ((128, b"fused_pair"), (256, b"fused_pair"), (96, b"phased_mfma"),
+                    (32, b"phased_mfma")):
         assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=C)), ctypes.byref(mlp)) == path
     assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(B=64, H=16, C=256)),
-                                       ctypes.byref(mlp)) == b"generic_mfma"
+                                       ctypes.byref(mlp)) == b"phased_mfma"
     # more memories than pairs of compute units: one workgroup per memory, no workspace
     big = _desc(B=64, H=16)
     assert tm.lib.titans_mem_scan_path(ctypes.byref(big), ctypes.byref(mlp)) == b"fused_mfma"
@@ -82,8 +82,27 @@ def test_workspace_size_query(monkeypatch):
     monkeypatch.delenv("TITANS_MEM_FUSED_SINGLE")
     size = tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(C=32)), ctypes.byref(mlp))
     assert 0 < size < 1 << 30 and size % 4 == 0
-    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=32)), ctypes.byref(mlp)) == b"generic_mfma"
-    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(io=0)), ctypes.byref(mlp)) == b"generic_fp32"
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=32)), ctypes.byref(mlp)) == b"phased_mfma"
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(io=0)), ctypes.byref(mlp)) == b"phased_fp32"
+    # the generic family: layers of 128+ units run as a chain of GPU-wide launches, narrower
+    # memories on one workgroup each; TITANS_MEM_GENERIC_MODE forces either
+    narrow = tm.mlp_desc((64, 96, 64))
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=32)), ctypes.byref(narrow)) == b"generic_mfma"
+    deep = tm.mlp_desc((128, 512, 512, 512, 128))
+    ddesc = _desc(B=2, T=32768, H=8, d=128, C=128)
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(ddesc), ctypes.byref(deep)) == b"phased_mfma"
+    # per memory: two parity buffers of coefficients (4C+4), Cm ((C+1) C), Q and K (C d);
+    # Hk and SiLU' of the hidden layers, Delta of every layer, two read buffers (C x 512)
+    # and Cm o Hq Hk^T (C x C), each rounded up to 64 floats
+    r64 = lambda x: (x + 63) // 64 * 64
+    per = (2 * (r64(4 * 128 + 4) + r64(129 * 128) + 2 * r64(128 * 128)) + 2 * 3 * 128 * 512
+           + (3 * 128 * 512 + 128 * 128) + 2 * 128 * 512 + 128 * 128)
+    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(ddesc), ctypes.byref(deep)) == 16 * per * 4
+    monkeypatch.setenv("TITANS_MEM_GENERIC_MODE", "single")
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(ddesc), ctypes.byref(deep)) == b"generic_mfma"
+    monkeypatch.setenv("TITANS_MEM_GENERIC_MODE", "phased")
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=32)), ctypes.byref(narrow)) == b"phased_mfma"
+    monkeypatch.delenv("TITANS_MEM_GENERIC_MODE")
     assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=0)), ctypes.byref(mlp)) is None
     assert tm.lib.titans_mem_retrieve_path(ctypes.byref(_desc()), ctypes.byref(mlp)) == b"fused_mfma"
     assert tm.lib.titans_mem_retrieve_path(ctypes.byref(_desc(io=0)), ctypes.byref(mlp)) == b"generic_fp32"

@@ -185,11 +185,20 @@ def _small(widths=(16, 32, 16), B=2, T=37, H=3, C=8, io="f32", seed=5):
     return wl, synthetic.make_inputs(wl, seed)
 
 
+GENERIC_MODES = ["single", "phased"]
+
+
+@pytest.mark.parametrize("mode", GENERIC_MODES)
 @pytest.mark.parametrize("C", [1, 2, 5, 8, 37, 64])
 @pytest.mark.parametrize("widths", [(16, 16), (16, 32, 16), (8, 24, 12, 8), (16, 40, 24, 32, 16)])
-def test_chunk_sizes_and_depths_fp32(C, widths):
+def test_chunk_sizes_and_depths_fp32(C, widths, mode, monkeypatch):
+    """The generic family with fp32 I/O: one workgroup per memory, and the chain of
+    GPU-wide launches (forced here; it normally serves layers of 128 units or more)."""
+    monkeypatch.setenv("TITANS_MEM_GENERIC_MODE", mode)
     wl, inp = _small(widths=widths, C=C)
-    log(f"case edge C={C} widths={widths}")
+    log(f"case edge {mode} C={C} widths={widths}")
+    assert tm.scan_path(torch.empty(1, 1, 1, widths[0], dtype=torch.float32).cuda(), C, widths) == (
+        "generic_fp32" if mode == "single" else "phased_fp32")
     rng = np.random.default_rng(3)
     s0 = (0.05 * rng.standard_normal(inp.theta0.shape)).astype(np.float32)
     inp.s0 = s0
@@ -202,17 +211,40 @@ def test_chunk_sizes_and_depths_fp32(C, widths):
     assert ey <= 1e-4 and et <= 1e-4 and es <= 1e-4
 
 
+@pytest.mark.parametrize("mode", GENERIC_MODES)
 @pytest.mark.parametrize("C", [1, 5, 37, 64, 128])
 @pytest.mark.parametrize("widths", [(16, 16), (16, 32, 16), (8, 24, 12, 8), (16, 40, 24, 32, 16)])
-def test_chunk_sizes_and_depths_bf16_generic(C, widths):
-    """Shapes outside the fused kernels with bf16 I/O: the generic kernel on bf16 MFMA."""
+def test_chunk_sizes_and_depths_bf16_generic(C, widths, mode, monkeypatch):
+    """Shapes outside the fused kernels with bf16 I/O: the generic family on bf16 MFMA."""
+    monkeypatch.setenv("TITANS_MEM_GENERIC_MODE", mode)
     wl, inp = _small(widths=widths, B=2, T=150, H=3, C=C, io="bf16", seed=C)
     dev = to_device(inp)
-    log(f"case bf16 generic {widths} C={C}")
-    assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == "generic_mfma"
+    log(f"case bf16 generic {mode} {widths} C={C}")
+    assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == (
+        "generic_mfma" if mode == "single" else "phased_mfma")
     y, thT, sT = run_gpu(dev, wl)
     torch.cuda.synchronize()
     pairs = [(0, 0), (1, 2)]
+    check_pairs(wl, y, thT, sT, pairs, oracle_seq(inp, pairs))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("widths,C,T", [((32, 160, 96, 32), 100, 230), ((128, 128), 70, 150),
+                                        ((64, 200, 64), 64, 129),
+                                        ((128, 512, 512, 512, 128), 128, 300)])
+def test_phased_wide_memories(widths, C, T, io):
+    """Layers of 128+ units run as the chain of GPU-wide launches by default: ragged
+    64-wide tiles in every dimension, L = 1, 2, 3, 4, partial last chunks."""
+    wl, inp = _small(widths=widths, B=2, T=T, H=2, C=C, io=io, seed=T)
+    rng = np.random.default_rng(7)
+    inp.s0 = (0.05 * rng.standard_normal(inp.theta0.shape)).astype(np.float32)
+    dev = to_device(inp)
+    log(f"case phased {io} {widths} C={C} T={T}")
+    assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == (
+        "phased_mfma" if io == "bf16" else "phased_fp32")
+    y, thT, sT = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    pairs = [(0, 1), (1, 0)]
     check_pairs(wl, y, thT, sT, pairs, oracle_seq(inp, pairs))
 
 
@@ -378,7 +410,7 @@ def test_fused_matches_oracle_and_generic(kernel, monkeypatch):
     pairs = [(0, 0), (1, 2), (0, 1)]
     check_pairs(wl, y1, t1, s1, pairs, oracle_seq(inp, pairs))
     monkeypatch.setenv("TITANS_MEM_FORCE_GENERIC", "1")
-    assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == "generic_mfma"
+    assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == "phased_mfma"
     y2, t2, s2 = run_gpu(dev, wl)
     torch.cuda.synchronize()
     ey = y_rel_err(to_f64(y1), to_f64(y2))
