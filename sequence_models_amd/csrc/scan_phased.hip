@@ -13,8 +13,8 @@
 // one kernel launch, and consecutive launches on the stream are the barriers between
 // dependent products.  Products that depend on the same inputs share a launch:
 //   launch 1          key forward of layer 1, the layer-1 read products (Cm o Q K^T and
-//                     a Q W1^T - b Q S1^T), and the next chunk's coefficients and staged
-//                     Q, K (double-buffered by chunk parity);
+//                     a Q W1^T - b Q S1^T; q and k are read from the caller's tensors),
+//                     and the next chunk's coefficients (double-buffered by chunk parity);
 //   launches 2..L     key forward of layers 2..L (SiLU and SiLU' in the epilogue; the last
 //                     layer's epilogue forms Delta_L = 2 (O - V));
 //   L - 1 launches    backward Delta_{l-1} = (Delta_l W_l) o SiLU'(Z_{l-1});
@@ -45,25 +45,43 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
-// Operand of a tile product: element (r, k) = p[r * sr + k * sk] * (ks ? ks[k] : 1)
-// * (rs ? rs[r] : 1).  Every operand here has sk == 1 or sr == 1.
+// Operand of a tile product: element (r, k) = p[r * sr + k * sk] * (ks ? ks[k] : 1), read
+// from fp32 p or, when pb is set, from bf16 pb (q and k straight from a bf16 input).
+// Every operand here has sk == 1 or sr == 1.
 struct Opnd {
     const float* p;
     int64_t sr, sk;
     const float* ks;
-    const float* rs = nullptr;
+    const __bf16* pb = nullptr;
 };
 
-// 16-byte loads are used when the operand's base and its stride across the vector
-// direction keep every group of four 16-byte aligned.
+// Vector loads (16 bytes of fp32, 8 of bf16) are used when the operand's base and its
+// stride across the vector direction keep every group of four aligned.
 __device__ __forceinline__ bool vec_ok(const Opnd& X) {
     const int64_t s = X.sk == 1 ? X.sr : X.sk;
-    return ((reinterpret_cast<uintptr_t>(X.p) & 15u) == 0) && (s & 3) == 0;
+    const uintptr_t base = X.pb ? reinterpret_cast<uintptr_t>(X.pb) : reinterpret_cast<uintptr_t>(X.p);
+    return (base & (X.pb ? 7u : 15u)) == 0 && (s & 3) == 0;
+}
+
+__device__ __forceinline__ f32x4_t widen(bf16x4_t t) {
+    return f32x4_t{(float)t[0], (float)t[1], (float)t[2], (float)t[3]};
 }
 
 // Four consecutive elements along the contiguous index starting at (r, k): k .. k+3 of
 // row r when sk == 1, rows r .. r+3 of column k otherwise; zero outside R x K.
 __device__ __forceinline__ f32x4_t load4(const Opnd& X, bool vec, int r, int R, int k, int K) {
+    if (X.pb) {
+        const int64_t o = X.sk == 1 ? (int64_t)r * X.sr + k : r + (int64_t)k * X.sk;
+        const bool in = X.sk == 1 ? (r < R && k + 3 < K) : (r + 3 < R && k < K);
+        if (vec && in) return widen(*reinterpret_cast<const bf16x4_t*>(X.pb + o));
+        f32x4_t v;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool ok = X.sk == 1 ? (r < R && k + u < K) : (r + u < R && k < K);
+            v[u] = ok ? (float)X.pb[o + u] : 0.f;  // the unit-stride index advances
+        }
+        return v;
+    }
     if (X.sk == 1) {
         const float* q = X.p + (int64_t)r * X.sr + k;
         if (vec && r < R && k + 3 < K) return *reinterpret_cast<const f32x4_t*>(q);
@@ -90,68 +108,164 @@ __device__ __forceinline__ void grp_pos(const Opnd& X, int tid, int p, int& rr, 
 }
 
 __device__ __forceinline__ void store4(__bf16* dst, int ld, const Opnd& X, int rr, int k, int K,
-                                       int gr, int R, f32x4_t v) {
+                                       f32x4_t v, int kl) {
+    // k: the operand's column (scale, range); kl: the LDS column
     if (X.sk == 1) {
         bf16x4_t o;
-        const float rsc = (X.rs && gr < R) ? X.rs[gr] : 1.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            float x = v[u] * rsc;
+            float x = v[u];
             if (X.ks && k + u < K) x *= X.ks[k + u];
             o[u] = (__bf16)x;
         }
-        *reinterpret_cast<bf16x4_t*>(dst + rr * ld + k) = o;
+        *reinterpret_cast<bf16x4_t*>(dst + rr * ld + kl) = o;
     } else {
         const float ksc = (X.ks && k < K) ? X.ks[k] : 1.f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            float x = v[u] * ksc;
-            if (X.rs && gr + u < R) x *= X.rs[gr + u];
-            dst[(rr + u) * ld + k] = (__bf16)x;
+        for (int u = 0; u < 4; ++u) dst[(rr + u) * ld + kl] = (__bf16)(v[u] * ksc);
+    }
+}
+
+// Stage rows r0 .. r0+63 (< R) x columns kb .. kb+Kw-1 (< K) of each operand X[o] into
+// dst[o][r][k - kb] as bf16 (row length ld, zero-filled up to Kwp = Kw rounded up to 32).
+// Each batch of kSl 32-wide slices issues every 16-byte load before its first LDS store,
+// so the tile waits for one load latency per batch.  With kShare01, operand 1 is operand
+// 0's data under other scales and reuses its loads.
+// Interior tiles (every row and column of the window in range, vector-aligned, no
+// per-k scale on a k-contiguous operand) take an unchecked copy of the loop with the
+// operand's layout and source type decided once per batch: plain vector loads at
+// r * sr + k * sk, packed conversion to bf16.
+template <int kN, int kSl, bool kShare01>
+__device__ __forceinline__ void stage_fast(__bf16* const* dst, const Opnd* X, const int* r0,
+                                           int kb, int Kwp, int ld) {
+    const int tid = threadIdx.x;
+    for (int s0 = 0; s0 < Kwp; s0 += 32 * kSl) {
+        const int nsl = (Kwp - s0) / 32 < kSl ? (Kwp - s0) / 32 : kSl;
+        f32x4_t v[kN][kSl][2];
+#pragma unroll
+        for (int o = 0; o < kN; ++o) {
+            if (kShare01 && o == 1) continue;
+            const Opnd& Y = X[o];
+            int64_t base[2];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                int rr, kk;
+                grp_pos(Y, tid, p, rr, kk);
+                base[p] = (int64_t)(r0[o] + rr) * Y.sr + (int64_t)(kb + s0 + kk) * Y.sk;
+            }
+            const int64_t step = 32 * Y.sk;
+            if (Y.pb) {
+#pragma unroll
+                for (int sl = 0; sl < kSl; ++sl)
+#pragma unroll
+                    for (int p = 0; p < 2; ++p)
+                        v[o][sl][p] = sl < nsl ? widen(*reinterpret_cast<const bf16x4_t*>(
+                                                     Y.pb + base[p] + sl * step))
+                                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            } else {
+#pragma unroll
+                for (int sl = 0; sl < kSl; ++sl)
+#pragma unroll
+                    for (int p = 0; p < 2; ++p)
+                        v[o][sl][p] = sl < nsl ? *reinterpret_cast<const f32x4_t*>(
+                                                     Y.p + base[p] + sl * step)
+                                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+#pragma unroll
+        for (int o = 0; o < kN; ++o) {
+            const Opnd& Y = X[o];
+            const int ov = (kShare01 && o == 1) ? 0 : o;
+            if (Y.sk == 1) {  // four consecutive k of one row: one 8-byte store
+                const int rr = tid >> 3, kk = 4 * (tid & 7);
+#pragma unroll
+                for (int sl = 0; sl < kSl; ++sl)
+#pragma unroll
+                    for (int p = 0; p < 2; ++p)
+                        if (sl < nsl)
+                            *reinterpret_cast<bf16x4_t*>(dst[o] + (rr + 32 * p) * ld + s0 + 32 * sl + kk) =
+                                __builtin_convertvector(v[ov][sl][p], bf16x4_t);
+            } else {  // four consecutive rows of one k: four 2-byte stores
+                const int rr = 4 * (tid & 15), kk = tid >> 4;
+#pragma unroll
+                for (int sl = 0; sl < kSl; ++sl)
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) {
+                        if (sl >= nsl) continue;
+                        const int kl = s0 + 32 * sl + kk + 16 * p;
+                        f32x4_t x = v[ov][sl][p];
+                        if (Y.ks) x = x * Y.ks[kb + kl];
+                        const bf16x4_t b = __builtin_convertvector(x, bf16x4_t);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) dst[o][(rr + u) * ld + kl] = b[u];
+                    }
+            }
         }
     }
 }
 
-constexpr int kSlices = 8;  // 32-wide k slices per staging batch (256 k)
-
-// Stage rows r0 .. r0+63 (< R) x k < K of X into dst[r][k] as bf16 (row length ld,
-// zero-filled up to Kp), for up to three operands at once.  Each batch issues every
-// 16-byte load of its 256 k before the first LDS store, so a tile waits for a load
-// latency once per batch.
-template <int kN>
-__device__ __forceinline__ void stage(__bf16* const* dst, const Opnd* X, const int* r0,
-                                      const int* R, int K, int Kp, int ld) {
+template <int kN, int kSl, bool kShare01>
+__device__ __forceinline__ void stage_checked(__bf16* const* dst, const Opnd* X, const int* r0,
+                                              const int* R, int kb, int Kwp, int K, int ld,
+                                              const bool* vec) {
     const int tid = threadIdx.x;
-    bool vec[kN];
+    for (int s0 = 0; s0 < Kwp; s0 += 32 * kSl) {
+        f32x4_t v[kN][kSl][2];
 #pragma unroll
-    for (int o = 0; o < kN; ++o) vec[o] = vec_ok(X[o]);
-    for (int s0 = 0; s0 < Kp; s0 += 32 * kSlices) {
-        f32x4_t v[kN][kSlices][2];
+        for (int o = 0; o < kN; ++o) {
+            if (kShare01 && o == 1) continue;
 #pragma unroll
-        for (int o = 0; o < kN; ++o)
-#pragma unroll
-            for (int sl = 0; sl < kSlices; ++sl)
+            for (int sl = 0; sl < kSl; ++sl)
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
                     int rr, kk;
                     grp_pos(X[o], tid, p, rr, kk);
-                    const int k = s0 + 32 * sl + kk;
-                    v[o][sl][p] = (s0 + 32 * sl < Kp)
+                    const int k = kb + s0 + 32 * sl + kk;
+                    v[o][sl][p] = (s0 + 32 * sl < Kwp)
                                       ? load4(X[o], vec[o], r0[o] + rr, R[o], k, K)
                                       : f32x4_t{0.f, 0.f, 0.f, 0.f};
                 }
+        }
 #pragma unroll
         for (int o = 0; o < kN; ++o)
 #pragma unroll
-            for (int sl = 0; sl < kSlices; ++sl)
+            for (int sl = 0; sl < kSl; ++sl)
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
-                    if (s0 + 32 * sl >= Kp) continue;
+                    if (s0 + 32 * sl >= Kwp) continue;
+                    const int ov = (kShare01 && o == 1) ? 0 : o;
                     int rr, kk;
                     grp_pos(X[o], tid, p, rr, kk);
-                    store4(dst[o], ld, X[o], rr, s0 + 32 * sl + kk, K, r0[o] + rr, R[o], v[o][sl][p]);
+                    const int kl = s0 + 32 * sl + kk;
+                    store4(dst[o], ld, X[o], rr, kb + kl, K, v[ov][sl][p], kl);
                 }
     }
+}
+
+template <int kN, int kSl, bool kShare01 = false>
+__device__ __forceinline__ void stage(__bf16* const* dst, const Opnd* X, const int* r0,
+                                      const int* R, int kb, int Kwp, int K, int ld) {
+    bool vec[kN];
+    bool full = kb + Kwp <= K;
+#pragma unroll
+    for (int o = 0; o < kN; ++o) {
+        vec[o] = vec_ok(X[o]);
+        full = full && vec[o] && r0[o] + kTile <= R[o] && !(X[o].sk == 1 && X[o].ks);
+    }
+    if (full)
+        stage_fast<kN, kSl, kShare01>(dst, X, r0, kb, Kwp, ld);
+    else  // edge tiles: one slice per batch keeps this copy of the loop small
+        stage_checked<kN, 1, kShare01>(dst, X, r0, R, kb, Kwp, K, ld, vec);
+}
+
+// Logistic function: on the bf16 MFMA path the hardware exp2 / reciprocal (about one ulp
+// each, far inside bf16 rounding); on the fp32 path the accurate library forms.
+template <bool kFast>
+__device__ __forceinline__ float sigm(float z) {
+    if constexpr (kFast)
+        return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+    else
+        return sigmoidf_(z);
 }
 
 // LDS bytes of a bf16 tile product with reduction extent K and n staged operands.
@@ -168,7 +282,6 @@ __device__ __forceinline__ void mfma_tile(const __bf16* As, const __bf16* Bs, in
     const int wv = tid >> 6, g = (tid & 63) >> 4, j = tid & 15;
     const __bf16* ar = As + (16 * wv + j) * ld + 4 * g;
     const __bf16* br = Bs + j * ld + 4 * g;
-#pragma unroll 2
     for (int k0 = 0; k0 < Kp; k0 += 32) {
         const bf16x8_t af = __builtin_shufflevector(*reinterpret_cast<const bf16x4_t*>(ar + k0),
                                                     *reinterpret_cast<const bf16x4_t*>(ar + k0 + 16),
@@ -206,15 +319,16 @@ __device__ __forceinline__ void zero_acc(f32x4_t* acc) {
 }
 
 // out(i, j) = sum_{k < K} A(i, k) B(j, k) for the 64 x 64 tile at (i0, j0) of an M x N
-// result (K <= 512), bf16 operands, fp32 accumulation; epi(i, j, out).
-template <class Epi>
-__device__ __forceinline__ void tile_mfma(int i0, int j0, int M, int N, int K, Opnd A, Opnd B, __bf16* lds,
-                          Epi epi) {
+// result (K <= 512), bf16 operands, fp32 accumulation; epi(i, j, out).  kSl 32-wide
+// slices per staging batch.
+template <int kSl = 8, class Epi>
+__device__ __forceinline__ void tile_mfma(int i0, int j0, int M, int N, int K, Opnd A, Opnd B,
+                                          __bf16* lds, Epi epi) {
     const int Kp = (K + 31) & ~31, ld = Kp + 8;
     __bf16* const dst[2] = {lds, lds + kTile * ld};
     const Opnd X[2] = {A, B};
     const int r0[2] = {i0, j0}, R[2] = {M, N};
-    stage<2>(dst, X, r0, R, K, Kp, ld);
+    stage<2, kSl>(dst, X, r0, R, 0, Kp, K, ld);
     __syncthreads();
     f32x4_t acc[4];
     zero_acc(acc);
@@ -223,47 +337,30 @@ __device__ __forceinline__ void tile_mfma(int i0, int j0, int M, int N, int K, O
     __syncthreads();  // the LDS tiles may be restaged by the next product
 }
 
-// out = A1 B1^T + A2 B2^T (one accumulator, two staging rounds).
-template <class Epi>
-__device__ __forceinline__ void tile_mfma_sum2(int i0, int j0, int M, int N, int K, Opnd A1, Opnd B1, Opnd A2,
-                               Opnd B2, __bf16* lds, Epi epi) {
-    const int Kp = (K + 31) & ~31, ld = Kp + 8;
-    __bf16* const dst[2] = {lds, lds + kTile * ld};
-    const int r0[2] = {i0, j0}, R[2] = {M, N};
-    f32x4_t acc[4];
-    zero_acc(acc);
-    {
-        const Opnd X[2] = {A1, B1};
-        stage<2>(dst, X, r0, R, K, Kp, ld);
-        __syncthreads();
-        mfma_tile(dst[0], dst[1], Kp, ld, acc);
-        __syncthreads();
-    }
-    {
-        const Opnd X[2] = {A2, B2};
-        stage<2>(dst, X, r0, R, K, Kp, ld);
-        __syncthreads();
-        mfma_tile(dst[0], dst[1], Kp, ld, acc);
-    }
-    tile_epilogue(i0, j0, M, N, acc, epi);
-    __syncthreads();
-}
+constexpr int kWin3 = 128;  // k window of a three-operand staging round (52 KB of LDS)
 
-// out1 = A1 B^T and out2 = A2 B^T (three operands staged once); epi(i, j, out1, out2).
+// out1 = A B1^T and out2 = A B2^T: A, B1, B2 staged together in k windows of 128 (A is
+// loaded once); epi(i, j, out1, out2).
 template <class Epi>
-__device__ __forceinline__ void tile_mfma_dual(int i0, int j0, int M, int N, int K, Opnd A1, Opnd A2, Opnd B,
-                               __bf16* lds, Epi epi) {
-    const int Kp = (K + 31) & ~31, ld = Kp + 8;
+__device__ __forceinline__ void tile_mfma_shared_a(int i0, int j0, int M, int N, int K, Opnd A,
+                                                   Opnd B1, Opnd B2, __bf16* lds, Epi epi) {
+    const int Kw = K < kWin3 ? K : kWin3;
+    const int Kwp = (Kw + 31) & ~31, ld = Kwp + 8;
     __bf16* const dst[3] = {lds, lds + kTile * ld, lds + 2 * kTile * ld};
-    const Opnd X[3] = {A1, A2, B};
-    const int r0[3] = {i0, i0, j0}, R[3] = {M, M, N};
-    stage<3>(dst, X, r0, R, K, Kp, ld);
-    __syncthreads();
+    const Opnd X[3] = {A, B1, B2};
+    const int r0[3] = {i0, j0, j0}, R[3] = {M, N, N};
     f32x4_t acc1[4], acc2[4];
     zero_acc(acc1);
     zero_acc(acc2);
-    mfma_tile(dst[0], dst[2], Kp, ld, acc1);
-    mfma_tile(dst[1], dst[2], Kp, ld, acc2);
+    for (int kb = 0; kb < K; kb += kWin3) {
+        const int kw = (K - kb) < kWin3 ? (K - kb) : kWin3;
+        const int kwp = (kw + 31) & ~31;
+        stage<3, 4>(dst, X, r0, R, kb, kwp, K, ld);
+        __syncthreads();
+        mfma_tile(dst[0], dst[1], kwp, ld, acc1);
+        mfma_tile(dst[0], dst[2], kwp, ld, acc2);
+        __syncthreads();
+    }
     const int tid = threadIdx.x;
     const int wv = tid >> 6, g = (tid & 63) >> 4, j = tid & 15;
 #pragma unroll
@@ -273,7 +370,58 @@ __device__ __forceinline__ void tile_mfma_dual(int i0, int j0, int M, int N, int
             const int i = i0 + 16 * wv + 4 * g + r, jc = j0 + 16 * tn + j;
             if (i < M && jc < N) epi(i, jc, acc1[tn][r], acc2[tn][r]);
         }
-    __syncthreads();
+}
+
+// The chunk-end carry of one 64 x 64 tile of W_l and S_l (M = n_l rows, N = n_{l-1}
+// columns, K = n tokens):
+//   W <- a_n W - b_n S - (c_n o Delta)^T Hk,   S <- p S + (w o Delta)^T Hk,
+// with A1 = c_n-scaled Delta^T and A2 = w-scaled Delta^T sharing their loads and both
+// products sharing B = Hk.  The tile's old W and S values are loaded first, so their
+// latency overlaps the staging.
+__device__ __forceinline__ void tile_carry(int i0, int j0, int M, int N, int K, Opnd A1, Opnd A2,
+                                           Opnd B, float* W, float* S, int64_t ldw, float an,
+                                           float bn, float pn, __bf16* lds) {
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6, g = (tid & 63) >> 4, j = tid & 15;
+    float w_old[4][4], s_old[4][4];
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 16 * wv + 4 * g + r, jc = j0 + 16 * tn + j;
+            const bool in = i < M && jc < N;
+            const int64_t o = (int64_t)i * ldw + jc;
+            w_old[tn][r] = in ? W[o] : 0.f;
+            s_old[tn][r] = in ? S[o] : 0.f;
+        }
+    const int Kw = K < kWin3 ? K : kWin3;
+    const int ld = ((Kw + 31) & ~31) + 8;
+    __bf16* const dst[3] = {lds, lds + kTile * ld, lds + 2 * kTile * ld};
+    const Opnd X[3] = {A1, A2, B};
+    const int r0[3] = {i0, i0, j0}, R[3] = {M, M, N};
+    f32x4_t acc1[4], acc2[4];
+    zero_acc(acc1);
+    zero_acc(acc2);
+    for (int kb = 0; kb < K; kb += kWin3) {
+        const int kw = (K - kb) < kWin3 ? (K - kb) : kWin3;
+        const int kwp = (kw + 31) & ~31;
+        stage<3, 2, true>(dst, X, r0, R, kb, kwp, K, ld);
+        __syncthreads();
+        mfma_tile(dst[0], dst[2], kwp, ld, acc1);
+        mfma_tile(dst[1], dst[2], kwp, ld, acc2);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 16 * wv + 4 * g + r, jc = j0 + 16 * tn + j;
+            if (i < M && jc < N) {
+                const int64_t o = (int64_t)i * ldw + jc;
+                W[o] = an * w_old[tn][r] - bn * s_old[tn][r] - acc1[tn][r];
+                S[o] = pn * s_old[tn][r] + acc2[tn][r];
+            }
+        }
 }
 
 // The same contract in fp32 FMAs: 16-wide reduction steps staged in LDS, 4 x 4 outputs
@@ -339,21 +487,19 @@ __device__ __forceinline__ void tile_f32(int i0, int j0, int M, int N, int K, Op
 
 constexpr int kF32Lds = 2 * kKStep * (kTile + kPad) * 4;  // bytes
 
-template <bool kMfma, class Epi>
+template <bool kMfma, int kSl = 8, class Epi>
 __device__ __forceinline__ void tile(int i0, int j0, int M, int N, int K, Opnd A, Opnd B,
                                      void* lds, Epi epi) {
     if constexpr (kMfma)
-        tile_mfma(i0, j0, M, N, K, A, B, static_cast<__bf16*>(lds), epi);
+        tile_mfma<kSl>(i0, j0, M, N, K, A, B, static_cast<__bf16*>(lds), epi);
     else
         tile_f32(i0, j0, M, N, K, A, B, static_cast<float*>(lds), epi);
 }
 
 // Float offsets of the per-memory workspace regions.
 struct PhLayout {
-    int64_t coef[2];   // by chunk parity: a[C+1], b[C+1], w[C], p, -b[C+1]
+    int64_t coef[2];   // by chunk parity: a[C+1], b[C+1], w[C], p
     int64_t cm[2];     // by chunk parity: (C+1) x C, row t = c_{t, j}
-    int64_t qst[2];    // by chunk parity: Q, C x d
-    int64_t kst[2];    // by chunk parity: K (= Hk_0), C x d
     int64_t hk[TITANS_MAX_LAYERS];      // l = 1..L-1: C x n_l
     int64_t sp[TITANS_MAX_LAYERS];      // l = 1..L-1: C x n_l, SiLU'(Z_l)
     int64_t dl[TITANS_MAX_LAYERS + 1];  // l = 1..L:   C x n_l
@@ -369,10 +515,8 @@ __host__ __device__ inline PhLayout ph_layout(int C, int L, const int* n) {
     for (int l = 0; l <= L; ++l) maxw = n[l] > maxw ? n[l] : maxw;
     int64_t o = 0;
     for (int p = 0; p < 2; ++p) {
-        w.coef[p] = o; o += r64(4 * (int64_t)C + 4);
+        w.coef[p] = o; o += r64(3 * (int64_t)C + 3);
         w.cm[p] = o; o += r64((int64_t)(C + 1) * C);
-        w.qst[p] = o; o += r64((int64_t)C * n[0]);
-        w.kst[p] = o; o += r64((int64_t)C * n[0]);
     }
     for (int l = 1; l < L; ++l) { w.hk[l] = o; o += r64((int64_t)C * n[l]); }
     for (int l = 1; l < L; ++l) { w.sp[l] = o; o += r64((int64_t)C * n[l]); }
@@ -394,6 +538,7 @@ struct Seg {
 
 struct Phase {
     PhLayout wl;  // workspace layout (in the argument block: indexed by layer at run time)
+    int gx;       // blocks per memory
     int nseg;
     Seg seg[kMaxSeg];
     int64_t c0;  // first token of the chunk the products serve
@@ -404,13 +549,30 @@ struct Phase {
     int ppar;
 };
 
-template <bool kMfma>
-__global__ void __launch_bounds__(kThreads) phase_kernel(ScanArgs a, Phase ph) {
+constexpr unsigned bit(int task) { return 1u << task; }
+// The task sets one launch can hold; each is its own kernel instance, so the register
+// allocation of one step's tiles does not pay for another's.
+constexpr unsigned kSetFirst = bit(kFwd) | bit(kMq) | bit(kU) | bit(kPrep);
+constexpr unsigned kSetFwd = bit(kFwd);
+constexpr unsigned kSetBwd = bit(kBwd);
+constexpr unsigned kSetRead = bit(kMq) | bit(kU);
+constexpr unsigned kSetLast = bit(kQb) | bit(kCarry);
+
+template <bool kMfma, unsigned kTasks>
+__global__ void __launch_bounds__(kThreads, kTasks == kSetLast ? 2 : 1) phase_kernel(ScanArgs a, Phase ph) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ float s_al[256], s_et[256], s_be[256];
 
+    // Workgroup w runs on XCD w % 8; renumber so that each XCD holds a contiguous range of
+    // (memory, task) ids -- the tiles of one memory share operands through that XCD's L2.
+    const int64_t nblk = gridDim.x;
+    const int64_t w = blockIdx.x;
+    const int64_t full = nblk & ~int64_t(7);
+    const int64_t lid = w < full ? (w & 7) * (full >> 3) + (w >> 3) : w;
+    const int64_t seq = lid / ph.gx;
+
     // find this block's segment (unrolled: no dynamic indexing of the argument block)
-    int t = blockIdx.x;
+    int t = (int)(lid % ph.gx);
     Seg sg = ph.seg[0];
 #pragma unroll
     for (int s = 1; s < kMaxSeg; ++s) {
@@ -421,10 +583,9 @@ __global__ void __launch_bounds__(kThreads) phase_kernel(ScanArgs a, Phase ph) {
     }
     const int i0 = (t / sg.tj) * kTile, j0 = (t % sg.tj) * kTile;
 
-    const int64_t seq = blockIdx.y;
     const int64_t b = seq / a.H, h = seq % a.H;
     const int tid = threadIdx.x;
-    const int L = a.L, C = a.C, d = a.n[0];
+    const int L = a.L, C = a.C;
     const PhLayout& wl = ph.wl;
     float* ws = static_cast<float*>(a.ws) + seq * wl.per_seq;
     float* theta = a.thetaT + b * a.ss[0] + h * a.ss[1];
@@ -433,8 +594,8 @@ __global__ void __launch_bounds__(kThreads) phase_kernel(ScanArgs a, Phase ph) {
     const int64_t ybase = b * a.ys[0] + h * a.ys[2];
     const int64_t gbase = b * a.gs[0] + h * a.gs[2];
 
-    if (sg.task == kPrep) {
-        // gates, Q and K of chunk (c0p, np) -> coefficients and staged Q, K in buffer ppar
+    if (kTasks & bit(kPrep) && sg.task == kPrep) {
+        // gates of chunk (c0p, np) -> its coefficients in parity buffer ppar
         const int n = ph.np, pp = ph.ppar;
         const int64_t c0 = ph.c0p;
         for (int i = tid; i < n; i += kThreads) {
@@ -442,14 +603,6 @@ __global__ void __launch_bounds__(kThreads) phase_kernel(ScanArgs a, Phase ph) {
             s_al[i] = a.alpha[gi];
             s_et[i] = a.eta[gi];
             s_be[i] = a.beta[gi];
-        }
-        float* Q = ws + wl.qst[pp];
-        float* K = ws + wl.kst[pp];
-        for (int e = tid; e < n * d; e += kThreads) {
-            const int r = e / d, c = e % d;
-            const int64_t src = qbase + (c0 + r) * a.qs[1] + c;
-            K[e] = load_io(a.k, src, a.io);
-            Q[e] = load_io(a.q, src, a.io);
         }
         __syncthreads();
         // thread j owns column j of Cm: c_{t,j} for t = 0..n (the generic kernel's recurrence)
@@ -477,8 +630,7 @@ __global__ void __launch_bounds__(kThreads) phase_kernel(ScanArgs a, Phase ph) {
         }
         if (j < n) cw[j] = omb_j * Bj;
         if (j == 0) cp[0] = pb;
-        __syncthreads();
-        for (int i = tid; i <= n; i += kThreads) cp[1 + i] = -cb[i];
+
         return;
     }
 
@@ -488,13 +640,22 @@ __global__ void __launch_bounds__(kThreads) phase_kernel(ScanArgs a, Phase ph) {
     const float* coef_b = coef_a + (C + 1);
     const float* coef_w = coef_b + (C + 1);
     const float* coef_p = coef_w + C;
-    const float* coef_nb = coef_p + 1;  // -b, written by the coefficient task
     const float* Cm = ws + wl.cm[par];
-    const float* Kst = ws + wl.kst[par];
-    const float* Qst = ws + wl.qst[par];
     const int nin = a.n[l - 1], nout = a.n[l];
-    const float* Hk_in = l == 1 ? Kst : ws + wl.hk[l - 1];  // Hk_{l-1}
-    const float* Hq_in = l == 1 ? Qst : ws + wl.hq[(l - 1) & 1];
+    // Hk_{l-1} and Hq_{l-1} as (token, unit) or (unit, token) operands; for l = 1 these
+    // are k and q themselves, read from the caller's tensors
+    const int64_t in_off = qbase + c0 * a.qs[1];
+    auto input = [&](const void* p, int64_t sr, int64_t sk) {
+        Opnd o{nullptr, sr, sk, nullptr};
+        if (a.io == TITANS_BF16)
+            o.pb = static_cast<const __bf16*>(p) + in_off;
+        else
+            o.p = static_cast<const float*>(p) + in_off;
+        return o;
+    };
+    const Opnd hk_rows = l == 1 ? input(a.k, a.qs[1], 1) : Opnd{ws + wl.hk[l - 1], nin, 1, nullptr};
+    const Opnd hk_cols = l == 1 ? input(a.k, 1, a.qs[1]) : Opnd{ws + wl.hk[l - 1], 1, nin, nullptr};
+    const Opnd hq_rows = l == 1 ? input(a.q, a.qs[1], 1) : Opnd{ws + wl.hq[(l - 1) & 1], nin, 1, nullptr};
     float* U = ws + wl.hq[l & 1];
     float* Dl = ws + wl.dl[l];
     float* Mq = ws + wl.mq;
@@ -504,12 +665,13 @@ __global__ void __launch_bounds__(kThreads) phase_kernel(ScanArgs a, Phase ph) {
 
     switch (sg.task) {
         case kFwd: {  // Z_l = Hk_{l-1} W_l^T
-            const Opnd A{Hk_in, nin, 1, nullptr}, Bo{W, nin, 1, nullptr};
+            if constexpr (!(kTasks & bit(kFwd))) break;
+            const Opnd A = hk_rows, Bo{W, nin, 1, nullptr};
             if (l < L) {
                 float* Hout = ws + wl.hk[l];
                 float* Sp = ws + wl.sp[l];
                 tile<kMfma>(i0, j0, n, nout, nin, A, Bo, lds, [&](int i, int jj, float z) {
-                    const float sg_ = sigmoidf_(z);
+                    const float sg_ = sigm<kMfma>(z);
                     Hout[i * nout + jj] = z * sg_;
                     Sp[i * nout + jj] = sg_ * (1.0f + z * (1.0f - sg_));
                 });
@@ -522,6 +684,7 @@ __global__ void __launch_bounds__(kThreads) phase_kernel(ScanArgs a, Phase ph) {
             break;
         }
         case kBwd: {  // Delta_{l-1} = (Delta_l W_l) o SiLU'(Z_{l-1})
+            if constexpr (!(kTasks & bit(kBwd))) break;
             float* Dp = ws + wl.dl[l - 1];
             const float* Sp = ws + wl.sp[l - 1];
             tile<kMfma>(i0, j0, n, nin, nout, Opnd{Dl, nout, 1, nullptr}, Opnd{W, 1, nin, nullptr},
@@ -529,20 +692,22 @@ __global__ void __launch_bounds__(kThreads) phase_kernel(ScanArgs a, Phase ph) {
             break;
         }
         case kMq: {  // Mq = Cm o (Hq_{l-1} Hk_{l-1}^T), strictly lower triangular
-            tile<kMfma>(i0, j0, n, n, nin, Opnd{Hq_in, nin, 1, nullptr},
-                        Opnd{Hk_in, nin, 1, nullptr}, lds, [&](int i, int jj, float x) {
+            if constexpr (!(kTasks & bit(kMq))) break;
+            tile<kMfma>(i0, j0, n, n, nin, hq_rows, hk_rows, lds, [&](int i, int jj, float x) {
                             Mq[i * C + jj] = (jj < i) ? Cm[(int64_t)i * C + jj] * x : 0.0f;
                         });
             break;
         }
         case kU: {  // U_l = diag(a) Hq W_l^T - diag(b) Hq S_l^T
-            if constexpr (kMfma) {  // one accumulator: rows of Hq scaled by a, then by -b
-                tile_mfma_sum2(i0, j0, n, nout, nin, Opnd{Hq_in, nin, 1, nullptr, coef_a},
-                               Opnd{W, nin, 1, nullptr}, Opnd{Hq_in, nin, 1, nullptr, coef_nb},
-                               Opnd{S, nin, 1, nullptr}, static_cast<__bf16*>(lds),
-                               [&](int i, int jj, float x) { U[i * nout + jj] = x; });
+            if constexpr (!(kTasks & bit(kU))) break;
+            if constexpr (kMfma) {  // both products from one staging of Hq, W, S
+                tile_mfma_shared_a(i0, j0, n, nout, nin, hq_rows,
+                                   Opnd{W, nin, 1, nullptr}, Opnd{S, nin, 1, nullptr},
+                                   static_cast<__bf16*>(lds), [&](int i, int jj, float xw, float xs) {
+                                       U[i * nout + jj] = coef_a[i] * xw - coef_b[i] * xs;
+                                   });
             } else {
-                const Opnd A{Hq_in, nin, 1, nullptr};
+                const Opnd A = hq_rows;
                 tile<kMfma>(i0, j0, n, nout, nin, A, Opnd{W, nin, 1, nullptr}, lds,
                             [&](int i, int jj, float x) { U[i * nout + jj] = coef_a[i] * x; });
                 tile<kMfma>(i0, j0, n, nout, nin, A, Opnd{S, nin, 1, nullptr}, lds,
@@ -551,32 +716,28 @@ __global__ void __launch_bounds__(kThreads) phase_kernel(ScanArgs a, Phase ph) {
             break;
         }
         case kQb: {  // U_l -= Mq Delta_l; then Hq_l = SiLU(U_l) in place, or y
+            if constexpr (!(kTasks & bit(kQb))) break;
             const Opnd A{Mq, C, 1, nullptr}, Bo{Dl, 1, nout, nullptr};
             if (l < L) {
-                tile<kMfma>(i0, j0, n, nout, n, A, Bo, lds, [&](int i, int jj, float x) {
+                tile<kMfma, 4>(i0, j0, n, nout, n, A, Bo, lds, [&](int i, int jj, float x) {
                     const float u = U[i * nout + jj] - x;
-                    U[i * nout + jj] = u * sigmoidf_(u);
+                    U[i * nout + jj] = u * sigm<kMfma>(u);
                 });
             } else {
-                tile<kMfma>(i0, j0, n, nout, n, A, Bo, lds, [&](int i, int jj, float x) {
+                tile<kMfma, 4>(i0, j0, n, nout, n, A, Bo, lds, [&](int i, int jj, float x) {
                     store_io(a.y, ybase + (c0 + i) * a.ys[1] + jj, a.io, U[i * nout + jj] - x);
                 });
             }
             break;
         }
         case kCarry: {  // W_l, S_l to the chunk end (W first: it needs the chunk-start S)
+            if constexpr (!(kTasks & bit(kCarry))) break;
             const float an = coef_a[n], bn = coef_b[n], pn = coef_p[0];
             const float* crow = Cm + (int64_t)n * C;
-            const Opnd Bo{Hk_in, 1, nin, nullptr};
+            const Opnd Bo = hk_cols;
             if constexpr (kMfma) {  // both products from one staging of Delta_l and Hk
-                tile_mfma_dual(i0, j0, nout, nin, n, Opnd{Dl, 1, nout, crow},
-                               Opnd{Dl, 1, nout, coef_w}, Bo, static_cast<__bf16*>(lds),
-                               [&](int i, int jj, float x1, float x2) {
-                                   const int64_t o = (int64_t)i * nin + jj;
-                                   const float s_old = S[o];
-                                   W[o] = an * W[o] - bn * s_old - x1;
-                                   S[o] = pn * s_old + x2;
-                               });
+                tile_carry(i0, j0, nout, nin, n, Opnd{Dl, 1, nout, crow}, Opnd{Dl, 1, nout, coef_w},
+                           Bo, W, S, nin, an, bn, pn, static_cast<__bf16*>(lds));
                 break;
             }
             tile<kMfma>(i0, j0, nout, nin, n, Opnd{Dl, 1, nout, crow}, Bo, lds,
@@ -616,14 +777,18 @@ struct Launch {
     Phase ph{};
     int blocks = 0;
     int lds = 0;   // bf16 staging bytes its largest product needs
+    unsigned tasks = 0;
     void add(int task, int l, int M, int N, int K) {
         Seg& s = ph.seg[ph.nseg++];
         s.task = task;
         s.l = l;
         s.tj = task == kPrep ? 1 : tiles(N);
+        tasks |= bit(task);
         s.count = task == kPrep ? 1 : tiles(M) * s.tj;
         blocks += s.count;
-        const int need = task == kPrep ? 0 : mfma_lds_bytes(K, task == kCarry ? 3 : 2);
+        const int need = task == kPrep ? 0
+                         : (task == kCarry || task == kU) ? mfma_lds_bytes(K < kWin3 ? K : kWin3, 3)
+                                                          : mfma_lds_bytes(K, 2);
         if (need > lds) lds = need;
     }
 };
@@ -637,14 +802,32 @@ hipError_t run(const ScanArgs& a, hipStream_t stream) {
     auto chunk_len = [&](int64_t c) { return (int)((a.T - c * C) < C ? (a.T - c * C) : C); };
 
     if (kMfma) {
-        const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&phase_kernel<true>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, mfma_lds_bytes(512));
-        if (e != hipSuccess) return e;
+        const void* fns[] = {reinterpret_cast<const void*>(&phase_kernel<true, kSetFirst>),
+                             reinterpret_cast<const void*>(&phase_kernel<true, kSetFwd>),
+                             reinterpret_cast<const void*>(&phase_kernel<true, kSetBwd>),
+                             reinterpret_cast<const void*>(&phase_kernel<true, kSetRead>),
+                             reinterpret_cast<const void*>(&phase_kernel<true, kSetLast>)};
+        for (const void* f : fns) {
+            const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     mfma_lds_bytes(512));
+            if (e != hipSuccess) return e;
+        }
     }
     auto go = [&](Launch& x) -> hipError_t {
         const size_t lds = kMfma ? (size_t)(x.lds > 0 ? x.lds : mfma_lds_bytes(32)) : (size_t)kF32Lds;
-        phase_kernel<kMfma><<<dim3((unsigned)x.blocks, (unsigned)nseq), kThreads, lds, stream>>>(a, x.ph);
+        x.ph.gx = x.blocks;
+        const dim3 grid((unsigned)(x.blocks * nseq));
+        auto within = [&](unsigned set) { return (x.tasks & ~set) == 0; };
+        if (within(kSetFwd))
+            phase_kernel<kMfma, kSetFwd><<<grid, kThreads, lds, stream>>>(a, x.ph);
+        else if (within(kSetBwd))
+            phase_kernel<kMfma, kSetBwd><<<grid, kThreads, lds, stream>>>(a, x.ph);
+        else if (within(kSetRead))
+            phase_kernel<kMfma, kSetRead><<<grid, kThreads, lds, stream>>>(a, x.ph);
+        else if (within(kSetLast))
+            phase_kernel<kMfma, kSetLast><<<grid, kThreads, lds, stream>>>(a, x.ph);
+        else
+            phase_kernel<kMfma, kSetFirst><<<grid, kThreads, lds, stream>>>(a, x.ph);
         return hipGetLastError();
     };
 

@@ -91,11 +91,11 @@ def test_workspace_size_query(monkeypatch):
     deep = tm.mlp_desc((128, 512, 512, 512, 128))
     ddesc = _desc(B=2, T=32768, H=8, d=128, C=128)
     assert tm.lib.titans_mem_scan_path(ctypes.byref(ddesc), ctypes.byref(deep)) == b"phased_mfma"
-    # per memory: two parity buffers of coefficients (4C+4), Cm ((C+1) C), Q and K (C d);
+    # per memory: two parity buffers of coefficients (3C+3) and Cm ((C+1) C);
     # Hk and SiLU' of the hidden layers, Delta of every layer, two read buffers (C x 512)
     # and Cm o Hq Hk^T (C x C), each rounded up to 64 floats
     r64 = lambda x: (x + 63) // 64 * 64
-    per = (2 * (r64(4 * 128 + 4) + r64(129 * 128) + 2 * r64(128 * 128)) + 2 * 3 * 128 * 512
+    per = (2 * (r64(3 * 128 + 3) + r64(129 * 128)) + 2 * 3 * 128 * 512
            + (3 * 128 * 512 + 128 * 128) + 2 * 128 * 512 + 128 * 128)
     assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(ddesc), ctypes.byref(deep)) == 16 * per * 4
     monkeypatch.setenv("TITANS_MEM_GENERIC_MODE", "single")
