@@ -54,6 +54,16 @@ def _load():
         lib.oracle_scan.argtypes = [i64, i64, i64, ctypes.c_int, ip, i64,
                                     dp, dp, dp, dp, dp, dp, dp, dp, i64,
                                     dp, dp, dp, ctypes.c_int]
+        lib.oracle_mlp_loss_bias.restype = ctypes.c_double
+        lib.oracle_mlp_loss_bias.argtypes = [ctypes.c_int, ip, dp, dp, dp, ctypes.c_int,
+                                             ctypes.c_double]
+        lib.oracle_mlp_grad_bias.restype = ctypes.c_double
+        lib.oracle_mlp_grad_bias.argtypes = [ctypes.c_int, ip, dp, dp, dp, dp, ctypes.c_int,
+                                             ctypes.c_double]
+        lib.oracle_scan_bias.restype = ctypes.c_int
+        lib.oracle_scan_bias.argtypes = [i64, i64, i64, ctypes.c_int, ip, i64,
+                                         dp, dp, dp, dp, dp, dp, dp, dp, i64,
+                                         dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_double]
         lib.oracle_retrieve.restype = ctypes.c_int
         lib.oracle_retrieve.argtypes = [i64, i64, i64, ctypes.c_int, ip, dp, dp, i64, dp,
                                         ctypes.c_int]
@@ -87,25 +97,39 @@ def mlp_forward(widths, theta, x):
     return out
 
 
-def mlp_loss(widths, theta, k, v) -> float:
+# Attentional bias: None / ("l2",) = the squared loss; ("huber", delta); ("lp", p).
+BIAS_KINDS = {"l2": 0, "huber": 1, "lp": 2}
+
+
+def _bias(bias):
+    if bias is None:
+        return 0, 0.0
+    kind = BIAS_KINDS[bias[0]]
+    return kind, float(bias[1]) if len(bias) > 1 else 0.0
+
+
+def mlp_loss(widths, theta, k, v, bias=None) -> float:
+    """sum_i loss(M_theta(k)_i - v_i); the squared loss unless bias says otherwise."""
     lib = _load()
     L, w = _widths(widths)
     theta, k, v = _f64(theta), _f64(k), _f64(v)
-    return float(lib.oracle_mlp_loss(L, w, _ptr(theta), _ptr(k), _ptr(v)))
+    kind, prm = _bias(bias)
+    return float(lib.oracle_mlp_loss_bias(L, w, _ptr(theta), _ptr(k), _ptr(v), kind, prm))
 
 
-def mlp_grad(widths, theta, k, v):
-    """(loss, gradient) of ||M_theta(k) - v||^2, gradient in theta's layout."""
+def mlp_grad(widths, theta, k, v, bias=None):
+    """(loss, gradient) of sum_i loss(M_theta(k)_i - v_i), gradient in theta's layout."""
     lib = _load()
     L, w = _widths(widths)
     theta, k, v = _f64(theta), _f64(k), _f64(v)
     g = np.empty_like(theta)
-    loss = lib.oracle_mlp_grad(L, w, _ptr(theta), _ptr(k), _ptr(v), _ptr(g))
+    kind, prm = _bias(bias)
+    loss = lib.oracle_mlp_grad_bias(L, w, _ptr(theta), _ptr(k), _ptr(v), _ptr(g), kind, prm)
     return float(loss), g
 
 
-def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, nthreads: int = 0):
-    """Sequential chunked scan in fp64.
+def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, nthreads: int = 0, bias=None):
+    """Sequential chunked scan in fp64 (bias: the attentional bias, see BIAS_KINDS).
 
     q, k, v: [B, T, H, d]; alpha, eta, beta: [B, T, H];
     theta0, s0: [H, P] (shared over the batch) or [B, H, P].
@@ -130,9 +154,10 @@ def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, nthreads: int = 0
     y = np.zeros((B, T, H, d), dtype=np.float64)
     thT = np.zeros((B, H, P), dtype=np.float64)
     sT = np.zeros((B, H, P), dtype=np.float64)
-    rc = lib.oracle_scan(B, T, H, L, w, int(chunk), _ptr(q), _ptr(k), _ptr(v),
-                         _ptr(alpha), _ptr(eta), _ptr(beta), _ptr(theta0), _ptr(s0),
-                         bstride, _ptr(y), _ptr(thT), _ptr(sT), int(nthreads))
+    kind, prm = _bias(bias)
+    rc = lib.oracle_scan_bias(B, T, H, L, w, int(chunk), _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(alpha), _ptr(eta), _ptr(beta), _ptr(theta0), _ptr(s0),
+                              bstride, _ptr(y), _ptr(thT), _ptr(sT), int(nthreads), kind, prm)
     if rc != 0:
         raise ValueError(f"oracle_scan rejected its arguments (rc={rc})")
     return y, thT, sT

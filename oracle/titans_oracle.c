@@ -16,6 +16,14 @@
  *              (same explainer, retrieve formula).
  *   loss       l = || M_theta(k_t) - v_t ||_2^2, no 1/2 factor
  *              (lowest.today Titans summary, "Funzione Obiettivo").
+ *              Alternative attentional biases (the MIRAS variants named on the
+ *              explainer page, "MIRAS" section, and the ITmedia Titans/MIRAS article:
+ *              YAAD uses a Huber loss, MONETA generalized norms), applied to each
+ *              component r of r = M_theta(k_t) - v_t and summed:
+ *                Huber, threshold delta:  r^2 if |r| <= delta, else 2 delta |r| - delta^2
+ *                (the squared loss above with its slope capped at 2 delta);
+ *                l_p, p >= 1:             |r|^p
+ *              (both reduce to the squared loss: delta -> infinity, p = 2).
  *   surprise   g_t = grad_theta l, taken at the chunk-start weights theta_c
  *              (the chunked "mini-batch" form: lowest.today Titans summary,
  *              "Addestramento Parallelizzato").
@@ -46,6 +54,31 @@
 #endif
 
 #define ORACLE_MAX_LAYERS 8
+
+/* attentional bias kinds */
+#define ORACLE_BIAS_L2 0
+#define ORACLE_BIAS_HUBER 1
+#define ORACLE_BIAS_LP 2
+
+/* loss of one residual component r */
+static double bias_loss(int kind, double prm, double r) {
+    double a = fabs(r);
+    if (kind == ORACLE_BIAS_HUBER) return a <= prm ? r * r : 2.0 * prm * a - prm * prm;
+    if (kind == ORACLE_BIAS_LP) return pow(a, prm);
+    return r * r;
+}
+
+/* its derivative d loss / d r (0 at r = 0 for l_1) */
+static double bias_grad(int kind, double prm, double r) {
+    double a = fabs(r);
+    if (kind == ORACLE_BIAS_HUBER) return a <= prm ? 2.0 * r : (r > 0 ? 2.0 * prm : -2.0 * prm);
+    if (kind == ORACLE_BIAS_LP) {
+        if (r == 0.0) return 0.0;
+        double m = prm * pow(a, prm - 1.0);
+        return r > 0 ? m : -m;
+    }
+    return 2.0 * r;
+}
 
 static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 static double silu(double z) { return z * sigmoid(z); }
@@ -88,15 +121,15 @@ static void mlp_forward(int L, const int* n, const double* theta, const double* 
 }
 
 /*
- * grad = d/dtheta || M_theta(k) - v ||^2 by explicit backpropagation.
+ * grad = d/dtheta sum_i loss(M_theta(k)_i - v_i) by explicit backpropagation.
  * Returns the loss.  work must hold (2 * (L + 1) + 2) * max_width doubles.
  *   forward:  h_0 = k, z_l = W_l h_{l-1}, h_l = SiLU(z_l) (l < L), o = z_L
- *   output:   delta_L = 2 (o - v)
+ *   output:   delta_L = loss'(o - v)   (= 2 (o - v) for the squared loss)
  *   backward: delta_{l-1} = (W_l^T delta_l) * SiLU'(z_{l-1})
  *   gradient: dW_l = delta_l h_{l-1}^T
  */
 static double mlp_grad(int L, const int* n, const double* theta, const double* k,
-                       const double* v, double* grad, double* work) {
+                       const double* v, double* grad, double* work, int kind, double prm) {
     int mw = max_width(L, n);
     double* z = work;                    /* z_l at z + l*mw, l = 1..L */
     double* h = work + (int64_t)(L + 1) * mw; /* h_l at h + l*mw, l = 0..L-1 */
@@ -128,8 +161,8 @@ static double mlp_grad(int L, const int* n, const double* theta, const double* k
     double* zL = z + (int64_t)L * mw;
     for (int i = 0; i < n[L]; ++i) {
         double e = zL[i] - v[i];
-        loss += e * e;
-        delta[i] = 2.0 * e;
+        loss += bias_loss(kind, prm, e);
+        delta[i] = bias_grad(kind, prm, e);
     }
     for (int l = L; l >= 1; --l) {
         const double* hin = h + (int64_t)(l - 1) * mw;
@@ -161,21 +194,31 @@ void oracle_mlp_forward(int L, const int* n, const double* theta, const double* 
     free(work);
 }
 
-double oracle_mlp_loss(int L, const int* n, const double* theta, const double* k, const double* v) {
+double oracle_mlp_loss_bias(int L, const int* n, const double* theta, const double* k,
+                            const double* v, int kind, double prm) {
     double* o = (double*)malloc(sizeof(double) * n[L]);
     oracle_mlp_forward(L, n, theta, k, o);
     double loss = 0.0;
-    for (int i = 0; i < n[L]; ++i) loss += (o[i] - v[i]) * (o[i] - v[i]);
+    for (int i = 0; i < n[L]; ++i) loss += bias_loss(kind, prm, o[i] - v[i]);
     free(o);
+    return loss;
+}
+
+double oracle_mlp_loss(int L, const int* n, const double* theta, const double* k, const double* v) {
+    return oracle_mlp_loss_bias(L, n, theta, k, v, ORACLE_BIAS_L2, 0.0);
+}
+
+double oracle_mlp_grad_bias(int L, const int* n, const double* theta, const double* k,
+                            const double* v, double* grad, int kind, double prm) {
+    double* work = (double*)malloc(sizeof(double) * grad_work_len(L, n));
+    double loss = mlp_grad(L, n, theta, k, v, grad, work, kind, prm);
+    free(work);
     return loss;
 }
 
 double oracle_mlp_grad(int L, const int* n, const double* theta, const double* k, const double* v,
                        double* grad) {
-    double* work = (double*)malloc(sizeof(double) * grad_work_len(L, n));
-    double loss = mlp_grad(L, n, theta, k, v, grad, work);
-    free(work);
-    return loss;
+    return oracle_mlp_grad_bias(L, n, theta, k, v, grad, ORACLE_BIAS_L2, 0.0);
 }
 
 /*
@@ -186,7 +229,7 @@ static void scan_one(int L, const int* n, int64_t T, int64_t C,
                      const double* q, const double* k, const double* v, int64_t tok_stride,
                      const double* alpha, const double* eta, const double* beta, int64_t gate_stride,
                      const double* theta0, const double* s0,
-                     double* y, int64_t y_stride, double* theta, double* s) {
+                     double* y, int64_t y_stride, double* theta, double* s, int kind, double prm) {
     int64_t P = oracle_param_count(L, n);
     double* theta_c = (double*)malloc(sizeof(double) * P);
     double* g = (double*)malloc(sizeof(double) * P);
@@ -201,7 +244,7 @@ static void scan_one(int L, const int* n, int64_t T, int64_t C,
             /* read with the weights before this token's write */
             mlp_forward(L, n, theta, q + t * tok_stride, y + t * y_stride, fwork);
             /* surprise at the chunk-start weights */
-            mlp_grad(L, n, theta_c, k + t * tok_stride, v + t * tok_stride, g, gwork);
+            mlp_grad(L, n, theta_c, k + t * tok_stride, v + t * tok_stride, g, gwork, kind, prm);
             double a = alpha[t * gate_stride], e = eta[t * gate_stride], bt = beta[t * gate_stride];
             for (int64_t i = 0; i < P; ++i) {
                 s[i] = bt * s[i] + (1.0 - bt) * g[i];
@@ -220,12 +263,16 @@ static void scan_one(int L, const int* n, int64_t T, int64_t C,
  *   theta_T, s_T : [B, H, P]
  * Returns 0 on success, -1 on bad arguments, -2 on allocation failure.
  */
-int oracle_scan(int64_t B, int64_t T, int64_t H, int L, const int* n, int64_t C,
-                const double* q, const double* k, const double* v,
-                const double* alpha, const double* eta, const double* beta,
-                const double* theta0, const double* s0, int64_t state0_bstride,
-                double* y, double* theta_T, double* s_T, int nthreads) {
+int oracle_scan_bias(int64_t B, int64_t T, int64_t H, int L, const int* n, int64_t C,
+                     const double* q, const double* k, const double* v,
+                     const double* alpha, const double* eta, const double* beta,
+                     const double* theta0, const double* s0, int64_t state0_bstride,
+                     double* y, double* theta_T, double* s_T, int nthreads, int kind,
+                     double prm) {
     if (L < 1 || L > ORACLE_MAX_LAYERS || C < 1 || B < 0 || T < 0 || H < 0) return -1;
+    if (kind < ORACLE_BIAS_L2 || kind > ORACLE_BIAS_LP) return -1;
+    if (kind == ORACLE_BIAS_HUBER && !(prm > 0.0)) return -1;
+    if (kind == ORACLE_BIAS_LP && !(prm >= 1.0)) return -1;
     if (n[0] != n[L]) return -1;
     int64_t d = n[0];
     int64_t P = oracle_param_count(L, n);
@@ -245,9 +292,18 @@ int oracle_scan(int64_t B, int64_t T, int64_t H, int L, const int* n, int64_t C,
         scan_one(L, n, T, C, q + base, k + base, v + base, tok,
                  alpha + gbase, eta + gbase, beta + gbase, H,
                  th0, sg0, y + base, tok,
-                 theta_T + (b * H + h) * P, s_T + (b * H + h) * P);
+                 theta_T + (b * H + h) * P, s_T + (b * H + h) * P, kind, prm);
     }
     return err;
+}
+
+int oracle_scan(int64_t B, int64_t T, int64_t H, int L, const int* n, int64_t C,
+                const double* q, const double* k, const double* v,
+                const double* alpha, const double* eta, const double* beta,
+                const double* theta0, const double* s0, int64_t state0_bstride,
+                double* y, double* theta_T, double* s_T, int nthreads) {
+    return oracle_scan_bias(B, T, H, L, n, C, q, k, v, alpha, eta, beta, theta0, s0,
+                            state0_bstride, y, theta_T, s_T, nthreads, ORACLE_BIAS_L2, 0.0);
 }
 
 /*

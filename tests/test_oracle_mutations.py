@@ -30,7 +30,11 @@ MUTANTS = {
                                       "                theta[i] = (1.0 - a) * theta[i] - e * s[i];\n"
                                       "                s[i] = bt * s[i] + (1.0 - bt) * g[i];\n"
                                       "            }\n")],
-    "loss_without_factor_two": [("delta[i] = 2.0 * e;", "delta[i] = e;")],
+    "loss_without_factor_two": [("    return 2.0 * r;\n}", "    return r;\n}")],
+    "huber_slope_not_capped": [("a <= prm ? 2.0 * r : (r > 0 ? 2.0 * prm : -2.0 * prm)", "2.0 * r")],
+    "huber_loss_not_continuous": [("2.0 * prm * a - prm * prm", "2.0 * prm * a")],
+    "lp_gradient_exponent": [("double m = prm * pow(a, prm - 1.0);", "double m = prm * pow(a, prm);")],
+    "lp_gradient_sign_dropped": [("return r > 0 ? m : -m;", "return m;")],
     "wrong_silu_derivative": [("return s * (1.0 + z * (1.0 - s));", "return s * (1.0 + z * s);")],
     "gradient_step_sign": [("theta[i] = (1.0 - a) * theta[i] - e * s[i];",
                             "theta[i] = (1.0 - a) * theta[i] + e * s[i];")],
@@ -59,6 +63,11 @@ PIN_CASES = [
     (pins.test_eta_zero_is_pure_decay, dict(C=5)),
     (pins.test_alpha_one_beta_zero_keeps_one_token, {}),
     (pins.test_scalar_memory_momentum_and_decay_closed_form, dict(s0_val=0.7)),
+    (pins.test_bias_loss_values_by_hand, {}),
+    (pins.test_bias_grad_matches_central_differences, dict(widths=(4, 8, 4), bias=("huber", 0.3))),
+    (pins.test_bias_grad_matches_central_differences, dict(widths=(4, 8, 4), bias=("lp", 3.0))),
+    (pins.test_linear_memory_biased_delta_rule, dict(bias=("huber", 0.2), C=4)),
+    (pins.test_linear_memory_biased_delta_rule, dict(bias=("lp", 3.0), C=1)),
 ]
 
 
@@ -89,7 +98,8 @@ def test_pins_reject_planted_mistake(name, tmp_path, monkeypatch):
     real = oracle._load()
     mutant = ctypes.CDLL(so)
     for fn in ("oracle_param_count", "oracle_mlp_forward", "oracle_mlp_loss", "oracle_mlp_grad",
-               "oracle_scan", "oracle_retrieve"):
+               "oracle_scan", "oracle_retrieve", "oracle_mlp_loss_bias", "oracle_mlp_grad_bias",
+               "oracle_scan_bias"):
         getattr(mutant, fn).restype = getattr(real, fn).restype
         getattr(mutant, fn).argtypes = getattr(real, fn).argtypes
     monkeypatch.setattr(oracle, "_lib", mutant)

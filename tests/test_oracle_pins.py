@@ -353,3 +353,118 @@ def test_retrieve_is_the_read_with_fixed_weights():
     zeros = np.zeros((2, 5, 3))
     ys, _, _ = oracle.scan(q, q, q, zeros, zeros, zeros, theta, np.zeros_like(theta), 2, widths)
     assert np.array_equal(ys, y)
+
+
+# ------------------------------------------------------- attentional biases
+#
+# The pages name two alternative attentional biases (the MIRAS variants: YAAD with a
+# Huber loss, MONETA with generalized norms) without formulas.  The oracle reads them as
+# per-component losses of the residual r = M(k) - v, summed: Huber with threshold delta,
+# r^2 inside |r| <= delta and 2 delta |r| - delta^2 outside; l_p, |r|^p.  These pins fix
+# each definition by values computed by hand, by its own finite differences, by its
+# reduction to the squared loss and by closed-form updates of a linear memory.
+
+def _identity_residual(r):
+    """A linear memory W = I with k = r and v = 0: the residual is r itself."""
+    d = len(r)
+    return (d, d), np.eye(d).reshape(-1), np.asarray(r, dtype=np.float64), np.zeros(d)
+
+
+def test_bias_loss_values_by_hand():
+    widths, theta, k, v = _identity_residual([0.5, -3.0, 1.0, -0.2])
+    assert oracle.mlp_loss(widths, theta, k, v) == pytest.approx(0.25 + 9 + 1 + 0.04, rel=1e-15)
+    # delta = 1: 0.25 + (2*3 - 1) + 1 + 0.04
+    assert oracle.mlp_loss(widths, theta, k, v, ("huber", 1.0)) == pytest.approx(6.29, rel=1e-14)
+    # delta = 0.4: (0.8*0.5 - 0.16) + (0.8*3 - 0.16) + (0.8 - 0.16) + 0.04
+    assert oracle.mlp_loss(widths, theta, k, v, ("huber", 0.4)) == pytest.approx(
+        0.24 + 2.24 + 0.64 + 0.04, rel=1e-14)
+    assert oracle.mlp_loss(widths, theta, k, v, ("lp", 3.0)) == pytest.approx(
+        0.125 + 27 + 1 + 0.008, rel=1e-14)
+    assert oracle.mlp_loss(widths, theta, k, v, ("lp", 1.0)) == pytest.approx(4.7, rel=1e-14)
+    # the gradient of a linear memory is loss'(r) k^T; with W = I, k = r its diagonal is
+    # loss'(r_i) r_i: Huber delta = 1 clips the slope of -3 at -2
+    _, g = oracle.mlp_grad(widths, theta, k, v, ("huber", 1.0))
+    np.testing.assert_allclose(np.diag(g.reshape(4, 4)), [1.0 * 0.5, -2.0 * -3.0, 2.0, 0.08],
+                               rtol=1e-15)
+    _, g = oracle.mlp_grad(widths, theta, k, v, ("lp", 3.0))
+    np.testing.assert_allclose(np.diag(g.reshape(4, 4)),
+                               [3 * 0.25 * 0.5, -3 * 9 * -3.0, 3.0, -3 * 0.04 * -0.2], rtol=1e-14)
+
+
+BIASES = [("huber", 0.3), ("huber", 2.0), ("lp", 1.5), ("lp", 3.0)]
+
+
+@pytest.mark.parametrize("bias", BIASES)
+@pytest.mark.parametrize("widths", [(4, 8, 4), (5, 7, 3)])
+def test_bias_grad_matches_central_differences(widths, bias):
+    rng = np.random.default_rng(11)
+    theta = _rand_theta(widths, rng)
+    k = rng.standard_normal(widths[0])
+    v = rng.standard_normal(widths[-1])
+    r = oracle.mlp_forward(widths, theta, k) - v
+    if bias[0] == "huber":  # some components on each side of the threshold, none at it
+        assert (np.abs(r) < bias[1]).any() or bias[1] < 0.5
+        assert np.abs(np.abs(r) - bias[1]).min() > 1e-3
+    loss, g = oracle.mlp_grad(widths, theta, k, v, bias)
+    h = 1e-6
+    fd = np.empty_like(theta)
+    for i in range(theta.size):
+        tp, tm = theta.copy(), theta.copy()
+        tp[i] += h
+        tm[i] -= h
+        fd[i] = (oracle.mlp_loss(widths, tp, k, v, bias) - oracle.mlp_loss(widths, tm, k, v, bias)) / (2 * h)
+    assert np.linalg.norm(g - fd) <= 1e-7 * np.linalg.norm(fd)
+    assert loss == pytest.approx(oracle.mlp_loss(widths, theta, k, v, bias), rel=1e-15)
+
+
+def test_bias_reduces_to_the_squared_loss():
+    rng = np.random.default_rng(12)
+    widths, T, C = (4, 8, 4), 30, 7
+    q, k, v, alpha, eta, beta = _seq_inputs(rng, T, 4, H=2, B=2)
+    th0 = np.stack([_rand_theta(widths, rng) for _ in range(2)])
+    s0 = 0.1 * rng.standard_normal(th0.shape)
+    ref = oracle.scan(q, k, v, alpha, eta, beta, th0, s0, C, widths)
+    for bias in (("huber", 1e30), ("lp", 2.0)):
+        out = oracle.scan(q, k, v, alpha, eta, beta, th0, s0, C, widths, bias=bias)
+        for a, b in zip(out, ref):
+            np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+    out = oracle.scan(q, k, v, alpha, eta, beta, th0, s0, C, widths, bias=("huber", 0.05))
+    assert np.abs(out[1] - ref[1]).max() > 1e-3  # a small threshold does change the memory
+
+
+@pytest.mark.parametrize("bias", [("huber", 0.2), ("lp", 1.0), ("lp", 3.0)])
+@pytest.mark.parametrize("C", [1, 4])
+def test_linear_memory_biased_delta_rule(bias, C):
+    """L=1, alpha=beta=0: W <- W - eta loss'(W_c k - v) k^T, loss' written out here:
+    2 clip(r, -delta, delta) for Huber, sign(r) for l_1, 3 |r| r for l_3."""
+    rng = np.random.default_rng(13)
+    d, T = 5, 21
+    q, k, v, _, eta, _ = _seq_inputs(rng, T, d)
+    zeros = np.zeros((1, T, 1))
+    W0 = rng.standard_normal((d, d)) / np.sqrt(d)
+    y, thT, _ = oracle.scan(q, k, v, zeros, eta, zeros, W0.reshape(1, -1), np.zeros((1, d * d)),
+                            C, (d, d), bias=bias)
+    if bias[0] == "huber":
+        dl = lambda r: 2 * np.clip(r, -bias[1], bias[1])  # noqa: E731
+    elif bias[1] == 1.0:
+        dl = np.sign
+    else:
+        dl = lambda r: 3 * np.abs(r) * r  # noqa: E731
+    W = W0.copy()
+    y_ref = np.zeros((T, d))
+    for c0 in range(0, T, C):
+        Wc = W.copy()
+        for t in range(c0, min(T, c0 + C)):
+            y_ref[t] = W @ q[0, t, 0]
+            W = W - eta[0, t, 0] * np.outer(dl(Wc @ k[0, t, 0] - v[0, t, 0]), k[0, t, 0])
+    np.testing.assert_allclose(y[0, :, 0], y_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(thT[0, 0].reshape(d, d), W, rtol=1e-12, atol=1e-12)
+
+
+def test_bias_arguments_are_checked():
+    rng = np.random.default_rng(14)
+    q, k, v, alpha, eta, beta = _seq_inputs(rng, 3, 4)
+    th0 = _rand_theta((4, 4), rng)[None]
+    for bias in (("huber", 0.0), ("huber", -1.0), ("lp", 0.5)):
+        with pytest.raises(ValueError):
+            oracle.scan(q, k, v, alpha, eta, beta, th0, np.zeros_like(th0), 2, (4, 4), bias=bias)
