@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define TITANS_MEM_ABI_VERSION 1
+#define TITANS_MEM_ABI_VERSION 2
 #define TITANS_MAX_LAYERS 4
 
 typedef enum {
@@ -63,6 +63,19 @@ typedef enum {
 } titans_status;
 
 typedef enum { TITANS_F32 = 0, TITANS_BF16 = 1 } titans_dtype;
+
+/* Attentional bias: the per-token loss the memory is written by, a sum over the
+ * components r of r = M_theta(k_t) - v_t.  The Titans pages (the lowest.today summary,
+ * "Funzione Obiettivo") give the squared error; the MIRAS variants they name (explainer
+ * page, "MIRAS" section: YAAD with a Huber loss, MONETA with generalized norms) give no
+ * formula, and the library reads them as:
+ *   TITANS_BIAS_L2     r^2                                   (gradient 2 r)
+ *   TITANS_BIAS_HUBER  r^2 if |r| <= delta, else 2 delta |r| - delta^2
+ *                      (gradient 2 clamp(r, -delta, delta)); delta = bias_param > 0
+ *   TITANS_BIAS_LP     |r|^p  (gradient p sign(r) |r|^(p-1), 0 at r = 0);
+ *                      p = bias_param >= 1, finite
+ * Both reduce to TITANS_BIAS_L2 (delta = infinity, p = 2). */
+typedef enum { TITANS_BIAS_L2 = 0, TITANS_BIAS_HUBER = 1, TITANS_BIAS_LP = 2 } titans_bias;
 
 /* The memory MLP: n_layers = L (1..TITANS_MAX_LAYERS), width[0..L] = n_0..n_L,
  * width[0] = width[L] = d.  Entries past L are ignored. */
@@ -84,6 +97,10 @@ typedef struct {
     int64_t state_stride[2];  /* strides of theta_T, s_T (retrieve: theta) over (b, h) */
     int64_t state0_stride[2]; /* strides of theta0, s0 over (b, h); a b-stride of 0 shares
                                  one initial memory per head across the batch */
+    int32_t bias;             /* titans_bias of the scan's writes (0 = squared error; ignored
+                                 by titans_mem_retrieve) */
+    float bias_param;         /* its parameter: Huber delta or the l_p exponent p (ignored
+                                 for TITANS_BIAS_L2) */
 } titans_scan_desc;
 
 /* Version of this ABI (TITANS_MEM_ABI_VERSION of the built library). */
@@ -104,9 +121,12 @@ int64_t titans_mem_param_count(const titans_mlp_desc* mlp);
  * I/O: "fused_pair" (bf16 MFMA, state resident on chip, two workgroups per memory; C a
  * multiple of 64; chosen while 2 * ceil(B*H / 8) * 8 workgroups fit one per compute unit),
  * else "fused_mfma" (one workgroup per memory; C = 64).  Every other supported shape runs the
- * generic kernel: "generic_mfma" (bf16 I/O: bf16 MFMA products, fp32 accumulation and
- * state) or "generic_fp32" (fp32 I/O: fp32 arithmetic throughout).  NULL if the arguments
- * are invalid.  The returned string is static. */
+ * generic family: "phased_mfma" / "phased_fp32" when a layer has 128 or more units (each
+ * chunk step's products spread as 64 x 64 tiles over the whole GPU, one launch per step),
+ * else "generic_mfma" / "generic_fp32" (one workgroup per memory); the _mfma kernels serve
+ * bf16 I/O (bf16 MFMA products, fp32 accumulation and state), the _fp32 ones fp32 I/O (fp32
+ * arithmetic throughout).  NULL if the arguments are invalid.  The returned string is
+ * static. */
 const char* titans_mem_scan_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp);
 
 /* Device workspace bytes titans_mem_scan needs for this problem (0 if none;

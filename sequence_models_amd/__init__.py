@@ -35,7 +35,11 @@ class ScanDesc(ctypes.Structure):
                 ("chunk", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
                 ("qkv_stride", ctypes.c_int64 * 3), ("y_stride", ctypes.c_int64 * 3),
                 ("gate_stride", ctypes.c_int64 * 3), ("state_stride", ctypes.c_int64 * 2),
-                ("state0_stride", ctypes.c_int64 * 2)]
+                ("state0_stride", ctypes.c_int64 * 2), ("bias", ctypes.c_int32),
+                ("bias_param", ctypes.c_float)]
+
+
+BIASES = {"l2": 0, "huber": 1, "lp": 2}
 
 
 lib = ctypes.CDLL(LIB_PATH)
@@ -159,11 +163,13 @@ def scan_path(q, chunk, widths) -> str:
 
 
 def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, *, y=None, theta_T=None, s_T=None,
-         workspace=None):
+         workspace=None, bias=None):
     """Chunked Titans memory scan on the current stream.
 
     q, k, v: [B,T,H,d] float32/bfloat16 CUDA tensors (d contiguous);
     alpha, eta, beta: [B,T,H] float32; theta0, s0: [H,P] (shared by the batch) or [B,H,P].
+    bias: the attentional bias of the writes, None (squared error), ("huber", delta) or
+    ("lp", p).
     Returns (y [B,T,H,d] like q, theta_T [B,H,P], s_T [B,H,P]).  theta_T / s_T may be passed
     as theta0 / s0 themselves for in-place streaming.
     """
@@ -190,6 +196,9 @@ def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, *, y=None, theta_
     if s_T.stride() != theta_T.stride() or s_T.shape != theta_T.shape:
         raise ValueError("s_T must have theta_T's shape and strides")
     desc = make_desc(q, chunk, y, alpha, theta_T, theta0)
+    if bias is not None:
+        desc.bias = BIASES[bias[0]]
+        desc.bias_param = float(bias[1]) if len(bias) > 1 else 0.0
     mlp = mlp_desc(widths)
     if workspace is None:
         n = lib.titans_mem_scan_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))

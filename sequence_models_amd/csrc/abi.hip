@@ -2,6 +2,7 @@
 // kernel dispatch.  Every check runs before any HIP call, so an invalid call
 // enqueues nothing and writes nothing.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -196,6 +197,15 @@ static titans_status prepare_scan(const titans_scan_desc* desc, const titans_mlp
     if (st) return st;
     if ((st = check_mlp(mlp, a))) return st;
     if (a.C < 1) return fail(TITANS_ERR_INVALID_ARGUMENT, "chunk=%d must be >= 1", a.C);
+    a.bias = desc->bias;
+    a.bias_param = desc->bias_param;
+    if (a.bias == TITANS_BIAS_HUBER && !(a.bias_param > 0.f))
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "Huber delta=%g must be > 0", (double)a.bias_param);
+    if (a.bias == TITANS_BIAS_LP && !(a.bias_param >= 1.f && a.bias_param < INFINITY))
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "l_p exponent p=%g must be finite and >= 1",
+                    (double)a.bias_param);
+    if (a.bias != TITANS_BIAS_L2 && a.bias != TITANS_BIAS_HUBER && a.bias != TITANS_BIAS_LP)
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "bias=%d is not a titans_bias", a.bias);
     return check_shape_support(a, true);
 }
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bias_util.h"
 #include "titans_mem.h"
 
 namespace titans {

@@ -14,6 +14,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "bias_util.h"
+
 namespace titans {
 namespace fused {
 
@@ -129,6 +131,16 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The output-layer error E2 = loss'(O - V) of four components; the squared error (the
+// default) stays one multiply.
+__device__ __forceinline__ f32x4 bias_grad4(f32x4 r, int kind, float prm) {
+    if (kind == TITANS_BIAS_L2) return 2.f * r;
+    f32x4 e;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) e[u] = bias_grad(r[u], kind, prm);
+    return e;
 }
 
 }  // namespace fused

@@ -347,7 +347,7 @@ __global__ void __launch_bounds__(kThreads) scan_generic_kernel(ScanArgs a) {
                 float* D = ws + wl.dl[L];
                 gemm<kMfma>(n, nout, nin, A, Bm, lds_gemm, [&](int i, int jj, float z) {
                     float vv = load_io(a.v, qbase + (c0 + i) * a.qs[1] + jj, a.io);
-                    D[i * nout + jj] = 2.0f * (z - vv);
+                    D[i * nout + jj] = bias_grad(z - vv, a.bias, a.bias_param);
                 });
             }
         }

@@ -388,7 +388,8 @@ __global__ void __launch_bounds__(kThreads, 1) scan_mfma_kernel(ScanArgs A) {
         }
         __syncthreads();  // B3
 
-        // ================= P3: E2 = 2 (O - V) in its four layouts
+        // ================= P3: E2 = loss'(O - V) (2 (O - V) for the squared error) in its
+        // four layouts
         {
             const int xb = opq(rc * kLd + cl0), xt = opq(cl0 * kLd + rc);
             const float ccr = -sm.cc[rc], wr = sm.w[rc];
@@ -397,7 +398,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_mfma_kernel(ScanArgs A) {
                 const f32x4 o = *reinterpret_cast<const f32x4*>(sm.r[0] + xb + 4 * q4) +
                                 *reinterpret_cast<const f32x4*>(sm.r[1] + xb + 4 * q4);
                 const f32x4 v4 = f4(half4(vr[q4 >> 1], q4 & 1));
-                const f32x4 e = 2.f * (o - v4);
+                const f32x4 e = bias_grad4(o - v4, A.bias, A.bias_param);
                 *reinterpret_cast<bf16x4*>(sm.e2l + xb + 4 * q4) = bf4(e);
 #pragma unroll
                 for (int ee = 0; ee < 4; ++ee) {

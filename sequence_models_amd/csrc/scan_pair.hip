@@ -658,7 +658,8 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) px[i] = xload(const_cast<uint64_t*>(srcy + i * kThreads));
             }
-            // E2 = 2 (O - V), O = O_side0 + O_side1, in its four layouts
+            // E2 = loss'(O - V) (2 (O - V) for the squared error), O = O_side0 + O_side1,
+            // in its four layouts
             const int xb = opq(rc * kLd + cl0), xt = opq(cl0 * kLd + rc);
             const float ccr = -sm.cc[rc], wr = sm.w[rc];
 #pragma unroll
@@ -671,7 +672,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                     o[e4] = side == 0 ? oo[k] + op : op + oo[k];
                 }
                 const f32x4 v4 = f4(half4(vr[q4 >> 1], q4 & 1));
-                const f32x4 e2 = 2.f * (o - v4);
+                const f32x4 e2 = bias_grad4(o - v4, A.bias, A.bias_param);
                 const bf16x4 el = bf4(e2), ec = bf4(e2 * ccr), ew = bf4(e2 * wr);
                 *reinterpret_cast<bf16x4*>(sm.e2l + xb + 4 * q4) = el;
 #pragma unroll

@@ -678,7 +678,7 @@ __global__ void __launch_bounds__(kThreads, kTasks == kSetLast ? 2 : 1) phase_ke
             } else {
                 tile<kMfma>(i0, j0, n, nout, nin, A, Bo, lds, [&](int i, int jj, float z) {
                     const float vv = load_io(a.v, qbase + (c0 + i) * a.qs[1] + jj, a.io);
-                    Dl[i * nout + jj] = 2.0f * (z - vv);
+                    Dl[i * nout + jj] = bias_grad(z - vv, a.bias, a.bias_param);
                 });
             }
             break;

@@ -31,6 +31,8 @@ struct ScanArgs {
     float* sT;
     void* ws;
     int debug;                 // test hooks (0 in normal use), see abi.hip
+    int bias;                  // titans_bias of the writes
+    float bias_param;          // Huber delta or l_p exponent
 };
 
 // Generic chunked scan: any supported shape, one workgroup per (b, h), per-chunk

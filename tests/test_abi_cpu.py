@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_status_strings_and_param_count():
-    assert tm.lib.titans_abi_version() == 1
+    assert tm.lib.titans_abi_version() == 2
     assert tm.lib.titans_status_string(0) == b"TITANS_OK"
     assert tm.lib.titans_status_string(3) == b"TITANS_ERR_WORKSPACE"
     assert tm.param_count((64, 256, 64)) == 32768
@@ -140,6 +140,21 @@ def test_validation_of_descriptors():
     assert _scan(_desc(), tm.mlp_desc((64, 1024, 64)))[0] == UNSUPPORTED
     st, msg = _scan(_desc(), mlp)   # all pointers NULL
     assert st == INVALID and "non-NULL" in msg
+    # attentional bias: kind and parameter are checked before anything else runs
+    for bias, prm, text in ((3, 1.0, "titans_bias"), (-1, 1.0, "titans_bias"), (1, 0.0, "Huber"),
+                            (1, -2.0, "Huber"), (1, float("nan"), "Huber"), (2, 0.5, "l_p"),
+                            (2, float("inf"), "l_p"), (2, float("nan"), "l_p")):
+        d = _desc()
+        d.bias, d.bias_param = bias, prm
+        st, msg = _scan(d, mlp)
+        assert st == INVALID and text in msg, (bias, prm, msg)
+    for bias, prm in ((0, -5.0), (1, float("inf")), (1, 1e-6), (2, 1.0), (2, 7.5)):
+        d = _desc()
+        d.bias, d.bias_param = bias, prm
+        st, msg = _scan(d, mlp)   # valid bias: the NULL pointers are what fails
+        assert st == INVALID and "non-NULL" in msg, (bias, prm, msg)
+    # the descriptor's layout matches the header (bias fields after the strides)
+    assert ctypes.sizeof(tm.ScanDesc) == 3 * 8 + 2 * 4 + 13 * 8 + 4 + 4
 
 
 no_fake_pointers_on_gpu = pytest.mark.skipif(

@@ -42,7 +42,7 @@ def run_gpu(dev, wl, **kw):
                    dev["theta0"], dev["s0"], wl.chunk, wl.widths, **kw)
 
 
-def oracle_seq(inp, pairs, T=None, theta0=None, s0=None):
+def oracle_seq(inp, pairs, T=None, theta0=None, s0=None, bias=None):
     """Oracle on the (b, h) pairs (prefix T), all pairs in one OpenMP-parallel call.
     Returns a list of (y [T,d], theta_T [P], s_T [P])."""
     wl = inp.workload
@@ -57,7 +57,7 @@ def oracle_seq(inp, pairs, T=None, theta0=None, s0=None):
     gates = [gather(getattr(inp, n)) for n in ("alpha", "eta", "beta")]
     th0 = (inp.theta0 if theta0 is None else theta0)[hs]
     sg0 = (inp.s0 if s0 is None else s0)[hs]
-    y, th, s = oracle.scan(*qkv, *gates, th0, sg0, wl.chunk, wl.widths)
+    y, th, s = oracle.scan(*qkv, *gates, th0, sg0, wl.chunk, wl.widths, bias=bias)
     del bs
     return [(y[0, :, i], th[0, i], s[0, i]) for i in range(len(pairs))]
 
@@ -590,3 +590,45 @@ def test_headline_sampled_single_kernel(sustained, monkeypatch):
     """The single-workgroup kernel at the full headline shape (the pair kernel runs it by default)."""
     _use("single", monkeypatch)
     test_headline_sampled(sustained)
+
+
+# ------------------------------------------------------ attentional biases
+#
+# The Huber and l_p attentional biases replace the output-layer error 2 (O - V) by the
+# derivative of the per-component loss in every scan kernel.  Each path against the
+# oracle with the same bias (l_1 only with fp32 I/O: its gradient jumps at r = 0, where
+# bf16 rounding of the residual flips signs).
+
+BIAS_PATHS = {
+    # name: (widths, C, io, env, expected path)
+    "generic_f32": ((16, 32, 16), 8, "f32", {"TITANS_MEM_GENERIC_MODE": "single"}, "generic_fp32"),
+    "generic_bf16": ((16, 32, 16), 5, "bf16", {"TITANS_MEM_GENERIC_MODE": "single"}, "generic_mfma"),
+    "phased_f32": ((32, 160, 32), 40, "f32", {}, "phased_fp32"),
+    "phased_bf16": ((32, 160, 32), 40, "bf16", {}, "phased_mfma"),
+    "pair": ((64, 256, 64), 64, "bf16", {}, "fused_pair"),
+    "pair_c128": ((64, 256, 64), 128, "bf16", {}, "fused_pair"),
+    "single": ((64, 256, 64), 64, "bf16", {"TITANS_MEM_FUSED_SINGLE": "1"}, "fused_mfma"),
+}
+
+
+@pytest.mark.parametrize("bias", [("huber", 0.5), ("lp", 1.5), ("lp", 3.0), ("lp", 1.0)])
+@pytest.mark.parametrize("path", sorted(BIAS_PATHS))
+def test_attentional_bias_matches_oracle(path, bias, monkeypatch):
+    widths, C, io, env, expected = BIAS_PATHS[path]
+    if bias == ("lp", 1.0) and io == "bf16":
+        pytest.skip("l_1 flips the sign of near-zero residuals under bf16 rounding")
+    for k_, v_ in env.items():
+        monkeypatch.setenv(k_, v_)
+    wl, inp = _small(widths=widths, B=2, T=200, H=2, C=C, io=io, seed=C + 7)
+    dev = to_device(inp)
+    log(f"case bias {bias} on {path}")
+    assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == expected
+    y, thT, sT = run_gpu(dev, wl, bias=bias)
+    torch.cuda.synchronize()
+    pairs = [(0, 1), (1, 0)]
+    refs = oracle_seq(inp, pairs, bias=bias)
+    check_pairs(wl, y, thT, sT, pairs, refs)
+    # the bias changes the memory (else the test would not see a kernel that ignores it)
+    y0, t0, _ = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    assert state_rel_err(to_f64(t0[:1, 1:2]), refs[0][1][None, None]) > 0.3
