@@ -15,6 +15,8 @@ stream the kernel runs on, against the MI355X peak of the unit that executes
 it.
 cpu_baseline: the fp64 oracle on a bounded sample of the same workload (the first
 batch rows, every head, all or a prefix of the tokens) on the host cores.
+retrieve: titans_mem_retrieve over the same q with the scan's final weights.
+biases: the same scan with the Huber (delta 0.5) and l_p (p 3) attentional biases.
 """
 from __future__ import annotations
 
@@ -122,6 +124,32 @@ def bench_retrieve(tm, torch, q, theta, wl, steps, warmup):
             "mfma_tflops": flops / (ms * 1e-3) / 1e12}
 
 
+def bench_biases(tm, torch, t, wl, out, ws, steps, warmup):
+    """The same scan with the Huber and l_p attentional biases (their own lines, not part of
+    the step): ms per call and tokens/s, to show what the loss derivative costs."""
+    y, thT, sT = out
+    res = {}
+    stream = torch.cuda.current_stream()
+    for bias in (("huber", 0.5), ("lp", 3.0)):
+        def run():
+            tm.scan(t["q"], t["k"], t["v"], t["alpha"], t["eta"], t["beta"], t["theta0"], t["s0"],
+                    wl.chunk, wl.widths, y=y, theta_T=thT, s_T=sT, workspace=ws, bias=bias)
+        for _ in range(warmup):
+            run()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(steps):
+            run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        B, T = t["q"].shape[:2]
+        res[f"{bias[0]}_{bias[1]:g}"] = {"ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+                                         "path": tm.scan_path(t["q"], wl.chunk, wl.widths)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +161,7 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-retrieve", action="store_true")
+    ap.add_argument("--no-biases", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -241,6 +270,9 @@ def main():
     }
     if not args.no_retrieve:
         result["retrieve"] = bench_retrieve(tm, torch, t["q"], thT, wl, args.steps, args.warmup)
+    if not args.no_biases:
+        # after the retrieve: it reads the squared-error scan's final weights
+        result["biases"] = bench_biases(tm, torch, t, wl, (y, thT, sT), ws, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_sample_rows, args.cpu_sample_tokens)
     print(json.dumps(result), flush=True)

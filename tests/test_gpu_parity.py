@@ -231,7 +231,9 @@ def test_chunk_sizes_and_depths_bf16_generic(C, widths, mode, monkeypatch):
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("widths,C,T", [((32, 160, 96, 32), 100, 230), ((128, 128), 70, 150),
                                         ((64, 200, 64), 64, 129),
-                                        ((128, 512, 512, 512, 128), 128, 300)])
+                                        ((128, 512, 512, 512, 128), 128, 300),
+                                        ((128, 512, 128), 256, 600),
+                                        ((64, 384, 136, 64), 193, 420)])
 def test_phased_wide_memories(widths, C, T, io):
     """Layers of 128+ units run as the chain of GPU-wide launches by default: ragged
     64-wide tiles in every dimension, L = 1, 2, 3, 4, partial last chunks."""
