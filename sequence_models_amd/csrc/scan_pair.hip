@@ -395,22 +395,29 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
         }
         if (t < A.T) *reinterpret_cast<bf16x8*>(yg + ybase + t * A.ys[1] + yd0) = out;
     };
-    // the prefetched chunk's K, Q, Cm and coefficient vectors into LDS
-    auto commit = [&]() {
+    // the prefetched chunk's Q and Cm into LDS (both dead once the Y partials are stored)
+    auto commit_qc = [&]() {
         const int xb = opq(rc * kLd + cl0);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            *reinterpret_cast<bf16x4*>(sm.kk + xb + 4 * q4) = half4(kpre[q4 >> 1], q4 & 1);
             *reinterpret_cast<bf16x4*>(sm.qq + xb + 4 * q4) = half4(qpre[q4 >> 1], q4 & 1);
             *reinterpret_cast<bf16x4*>(sm.cm + xb + 4 * q4) = half4(cpre[q4 >> 1], q4 & 1);
         }
+    };
+    // ... and its K and coefficient vectors (read by the carry: after the last barrier)
+    auto commit_kv = [&]() {
+        const int xb = opq(rc * kLd + cl0);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<bf16x4*>(sm.kk + xb + 4 * q4) = half4(kpre[q4 >> 1], q4 & 1);
         if (tid <= kC) *reinterpret_cast<f32x4*>(sm.a + 4 * tid) = vpre;  // a|b|cc|w|tail
     };
-    // Chunk n+1's data is committed to LDS at the end of chunk n (after its last reads of
-    // those regions) and chunk n+2's loads are issued right after, so a whole chunk of
-    // work covers them and no wait for them ever lands behind the exchange stores.
+    // Chunk n+1's loads are issued early in chunk n (after B4) and land in LDS once chunk n
+    // has stopped reading each region: Q and Cm after the Y partials are stored, K and the
+    // coefficient vectors after the last barrier.
     prefetch(0);
-    commit();
+    commit_qc();
+    commit_kv();
 
     int e = 0;  // exchange number of the current sub-chunk (1, 2, ...)
     for (int64_t c0 = 0; c0 < A.T; c0 += kC) {
@@ -821,6 +828,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) xstore(dst + i * kThreads, pack2(ys[1][2 * i], ys[1][2 * i + 1]));
         }
+        if (c0 + kC < A.T) commit_qc();  // every wave is past B6: Q and Cm are no longer read
         {
             // The carry's K operands: A = (-c_C o K)^T and (w o K)^T, rows d, k = tokens c.
             // An identity MFMA on K's LDS rows gives K tiles in accumulator layout (lane
@@ -867,9 +875,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             }
         }
         __syncthreads();  // B7: the Y slots, K, Q, Cm and the vectors are no longer read
-        if (c0 + kC < A.T) {
-            commit();
-        }
+        if (c0 + kC < A.T) commit_kv();
     }
 
     // ---- y of the last chunk: one more exchange (no O words)
