@@ -64,6 +64,11 @@ def _load():
         lib.oracle_scan_bias.argtypes = [i64, i64, i64, ctypes.c_int, ip, i64,
                                          dp, dp, dp, dp, dp, dp, dp, dp, i64,
                                          dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_double]
+        lib.oracle_scan_full.restype = ctypes.c_int
+        lib.oracle_scan_full.argtypes = [i64, i64, i64, ctypes.c_int, ip, i64,
+                                         dp, dp, dp, dp, dp, dp, dp, dp, i64,
+                                         dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                         ctypes.c_void_p]
         lib.oracle_retrieve.restype = ctypes.c_int
         lib.oracle_retrieve.argtypes = [i64, i64, i64, ctypes.c_int, ip, dp, dp, i64, dp,
                                         ctypes.c_int]
@@ -128,8 +133,10 @@ def mlp_grad(widths, theta, k, v, bias=None):
     return float(loss), g
 
 
-def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, nthreads: int = 0, bias=None):
-    """Sequential chunked scan in fp64 (bias: the attentional bias, see BIAS_KINDS).
+def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, nthreads: int = 0, bias=None,
+         surprise=False):
+    """Sequential chunked scan in fp64 (bias: the attentional bias, see BIAS_KINDS; with
+    surprise=True a fourth result [B, T, H] holds each token's gradient norm).
 
     q, k, v: [B, T, H, d]; alpha, eta, beta: [B, T, H];
     theta0, s0: [H, P] (shared over the batch) or [B, H, P].
@@ -155,12 +162,14 @@ def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, nthreads: int = 0
     thT = np.zeros((B, H, P), dtype=np.float64)
     sT = np.zeros((B, H, P), dtype=np.float64)
     kind, prm = _bias(bias)
-    rc = lib.oracle_scan_bias(B, T, H, L, w, int(chunk), _ptr(q), _ptr(k), _ptr(v),
+    sur = np.zeros((B, T, H), dtype=np.float64) if surprise else None
+    rc = lib.oracle_scan_full(B, T, H, L, w, int(chunk), _ptr(q), _ptr(k), _ptr(v),
                               _ptr(alpha), _ptr(eta), _ptr(beta), _ptr(theta0), _ptr(s0),
-                              bstride, _ptr(y), _ptr(thT), _ptr(sT), int(nthreads), kind, prm)
+                              bstride, _ptr(y), _ptr(thT), _ptr(sT), int(nthreads), kind, prm,
+                              None if sur is None else sur.ctypes.data)
     if rc != 0:
         raise ValueError(f"oracle_scan rejected its arguments (rc={rc})")
-    return y, thT, sT
+    return (y, thT, sT, sur) if surprise else (y, thT, sT)
 
 
 def retrieve(q, theta, widths, nthreads: int = 0):

@@ -32,6 +32,10 @@
  *   write      theta_{t+1} = (1 - alpha_t) theta_t - eta_t s_t
  *              (explainer, "適応的重み減衰（忘却ゲート）").
  *
+ *   surprise   (optional output) the norm || g_t ||_2 of each token's gradient, the
+ *              "momentary surprise" of the explainer ("サプライズ（驚き）メトリクス") that the
+ *              momentum accumulates.
+ *
  * Chunks of C tokens start at the call's first token; the last chunk may be
  * partial.  Nothing is blocked, fused or reordered: every token does one MLP
  * forward at the current weights (the read), one forward + backward at the
@@ -229,7 +233,8 @@ static void scan_one(int L, const int* n, int64_t T, int64_t C,
                      const double* q, const double* k, const double* v, int64_t tok_stride,
                      const double* alpha, const double* eta, const double* beta, int64_t gate_stride,
                      const double* theta0, const double* s0,
-                     double* y, int64_t y_stride, double* theta, double* s, int kind, double prm) {
+                     double* y, int64_t y_stride, double* theta, double* s, int kind, double prm,
+                     double* surprise, int64_t surprise_stride) {
     int64_t P = oracle_param_count(L, n);
     double* theta_c = (double*)malloc(sizeof(double) * P);
     double* g = (double*)malloc(sizeof(double) * P);
@@ -245,6 +250,11 @@ static void scan_one(int L, const int* n, int64_t T, int64_t C,
             mlp_forward(L, n, theta, q + t * tok_stride, y + t * y_stride, fwork);
             /* surprise at the chunk-start weights */
             mlp_grad(L, n, theta_c, k + t * tok_stride, v + t * tok_stride, g, gwork, kind, prm);
+            if (surprise) {
+                double gg = 0.0;
+                for (int64_t i = 0; i < P; ++i) gg += g[i] * g[i];
+                surprise[t * surprise_stride] = sqrt(gg);
+            }
             double a = alpha[t * gate_stride], e = eta[t * gate_stride], bt = beta[t * gate_stride];
             for (int64_t i = 0; i < P; ++i) {
                 s[i] = bt * s[i] + (1.0 - bt) * g[i];
@@ -263,12 +273,13 @@ static void scan_one(int L, const int* n, int64_t T, int64_t C,
  *   theta_T, s_T : [B, H, P]
  * Returns 0 on success, -1 on bad arguments, -2 on allocation failure.
  */
-int oracle_scan_bias(int64_t B, int64_t T, int64_t H, int L, const int* n, int64_t C,
+/* surprise: NULL, or [B, T, H] receiving || g_t || of every token */
+int oracle_scan_full(int64_t B, int64_t T, int64_t H, int L, const int* n, int64_t C,
                      const double* q, const double* k, const double* v,
                      const double* alpha, const double* eta, const double* beta,
                      const double* theta0, const double* s0, int64_t state0_bstride,
                      double* y, double* theta_T, double* s_T, int nthreads, int kind,
-                     double prm) {
+                     double prm, double* surprise) {
     if (L < 1 || L > ORACLE_MAX_LAYERS || C < 1 || B < 0 || T < 0 || H < 0) return -1;
     if (kind < ORACLE_BIAS_L2 || kind > ORACLE_BIAS_LP) return -1;
     if (kind == ORACLE_BIAS_HUBER && !(prm > 0.0)) return -1;
@@ -292,9 +303,20 @@ int oracle_scan_bias(int64_t B, int64_t T, int64_t H, int L, const int* n, int64
         scan_one(L, n, T, C, q + base, k + base, v + base, tok,
                  alpha + gbase, eta + gbase, beta + gbase, H,
                  th0, sg0, y + base, tok,
-                 theta_T + (b * H + h) * P, s_T + (b * H + h) * P, kind, prm);
+                 theta_T + (b * H + h) * P, s_T + (b * H + h) * P, kind, prm,
+                 surprise ? surprise + gbase : NULL, H);
     }
     return err;
+}
+
+int oracle_scan_bias(int64_t B, int64_t T, int64_t H, int L, const int* n, int64_t C,
+                     const double* q, const double* k, const double* v,
+                     const double* alpha, const double* eta, const double* beta,
+                     const double* theta0, const double* s0, int64_t state0_bstride,
+                     double* y, double* theta_T, double* s_T, int nthreads, int kind,
+                     double prm) {
+    return oracle_scan_full(B, T, H, L, n, C, q, k, v, alpha, eta, beta, theta0, s0,
+                            state0_bstride, y, theta_T, s_T, nthreads, kind, prm, NULL);
 }
 
 int oracle_scan(int64_t B, int64_t T, int64_t H, int L, const int* n, int64_t C,

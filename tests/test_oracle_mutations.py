@@ -35,6 +35,8 @@ MUTANTS = {
     "huber_loss_not_continuous": [("2.0 * prm * a - prm * prm", "2.0 * prm * a")],
     "lp_gradient_exponent": [("double m = prm * pow(a, prm - 1.0);", "double m = prm * pow(a, prm);")],
     "lp_gradient_sign_dropped": [("return r > 0 ? m : -m;", "return m;")],
+    "surprise_without_root": [("surprise[t * surprise_stride] = sqrt(gg);",
+                               "surprise[t * surprise_stride] = gg;")],
     "wrong_silu_derivative": [("return s * (1.0 + z * (1.0 - s));", "return s * (1.0 + z * s);")],
     "gradient_step_sign": [("theta[i] = (1.0 - a) * theta[i] - e * s[i];",
                             "theta[i] = (1.0 - a) * theta[i] + e * s[i];")],
@@ -68,6 +70,7 @@ PIN_CASES = [
     (pins.test_bias_grad_matches_central_differences, dict(widths=(4, 8, 4), bias=("lp", 3.0))),
     (pins.test_linear_memory_biased_delta_rule, dict(bias=("huber", 0.2), C=4)),
     (pins.test_linear_memory_biased_delta_rule, dict(bias=("lp", 3.0), C=1)),
+    (pins.test_surprise_of_a_linear_memory_closed_form, {}),
 ]
 
 
@@ -99,7 +102,7 @@ def test_pins_reject_planted_mistake(name, tmp_path, monkeypatch):
     mutant = ctypes.CDLL(so)
     for fn in ("oracle_param_count", "oracle_mlp_forward", "oracle_mlp_loss", "oracle_mlp_grad",
                "oracle_scan", "oracle_retrieve", "oracle_mlp_loss_bias", "oracle_mlp_grad_bias",
-               "oracle_scan_bias"):
+               "oracle_scan_bias", "oracle_scan_full"):
         getattr(mutant, fn).restype = getattr(real, fn).restype
         getattr(mutant, fn).argtypes = getattr(real, fn).argtypes
     monkeypatch.setattr(oracle, "_lib", mutant)

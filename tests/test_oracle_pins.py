@@ -468,3 +468,53 @@ def test_bias_arguments_are_checked():
     for bias in (("huber", 0.0), ("huber", -1.0), ("lp", 0.5)):
         with pytest.raises(ValueError):
             oracle.scan(q, k, v, alpha, eta, beta, th0, np.zeros_like(th0), 2, (4, 4), bias=bias)
+
+
+# ------------------------------------------------------------ surprise norm
+#
+# The optional per-token output || g_t ||: the norm of the gradient each token writes
+# with (at the chunk-start weights, under the chosen attentional bias).
+
+@pytest.mark.parametrize("bias", [None, ("huber", 0.3)])
+@pytest.mark.parametrize("C", [1, 3])
+def test_surprise_is_the_norm_of_the_token_gradient(C, bias):
+    """Recomputed here from the (finite-difference pinned) single-token gradient at the
+    chunk-start weights, which the scan's own theta_T sequence supplies."""
+    rng = np.random.default_rng(21)
+    widths, T = (4, 6, 4), 7
+    q, k, v, alpha, eta, beta = _seq_inputs(rng, T, 4)
+    th0 = _rand_theta(widths, rng)[None]
+    s0 = np.zeros_like(th0)
+    y, thT, sT, sur = oracle.scan(q, k, v, alpha, eta, beta, th0, s0, C, widths, bias=bias,
+                                  surprise=True)
+    for t in range(T):
+        c0 = t - t % C  # the chunk's start weights: the state after the first c0 tokens
+        if c0 == 0:
+            thc = th0[0]
+        else:
+            thc = oracle.scan(q[:, :c0], k[:, :c0], v[:, :c0], alpha[:, :c0], eta[:, :c0],
+                              beta[:, :c0], th0, s0, C, widths, bias=bias)[1][0, 0]
+        _, g = oracle.mlp_grad(widths, thc, k[0, t, 0], v[0, t, 0], bias)
+        assert sur[0, t, 0] == pytest.approx(np.linalg.norm(g), rel=1e-12)
+    ref = oracle.scan(q, k, v, alpha, eta, beta, th0, s0, C, widths, bias=bias)
+    for a, b in zip((y, thT, sT), ref):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_surprise_of_a_linear_memory_closed_form():
+    """L = 1: g_t = 2 (W_c k - v) k^T, so || g_t || = 2 || W_c k - v || || k ||."""
+    rng = np.random.default_rng(22)
+    d, T, C = 5, 9, 4
+    q, k, v, _, eta, _ = _seq_inputs(rng, T, d)
+    zeros = np.zeros((1, T, 1))
+    W0 = rng.standard_normal((d, d)) / np.sqrt(d)
+    *_, sur = oracle.scan(q, k, v, zeros, eta, zeros, W0.reshape(1, -1), np.zeros((1, d * d)),
+                          C, (d, d), surprise=True)
+    W = W0.copy()
+    for c0 in range(0, T, C):
+        Wc = W.copy()
+        for t in range(c0, min(T, c0 + C)):
+            r = Wc @ k[0, t, 0] - v[0, t, 0]
+            assert sur[0, t, 0] == pytest.approx(2 * np.linalg.norm(r) * np.linalg.norm(k[0, t, 0]),
+                                                 rel=1e-12)
+            W = W - 2 * eta[0, t, 0] * np.outer(r, k[0, t, 0])
