@@ -17,6 +17,7 @@ cpu_baseline: the fp64 oracle on a bounded sample of the same workload (the firs
 batch rows, every head, all or a prefix of the tokens) on the host cores.
 retrieve: titans_mem_retrieve over the same q with the scan's final weights.
 biases: the same scan with the Huber (delta 0.5) and l_p (p 3) attentional biases.
+surprise: titans_mem_scan_surprise (the scan plus each token's gradient norm).
 """
 from __future__ import annotations
 
@@ -150,6 +151,31 @@ def bench_biases(tm, torch, t, wl, out, ws, steps, warmup):
     return res
 
 
+def bench_surprise(tm, torch, t, wl, out, steps, warmup):
+    """titans_mem_scan_surprise on the same inputs (its own line): the scan plus each
+    token's gradient norm, on the generic family (phased for 128+ unit layers)."""
+    y, thT, sT = out
+    sur = torch.empty_like(t["alpha"])
+
+    def run():  # the binding sizes the workspace for this call's path
+        tm.scan(t["q"], t["k"], t["v"], t["alpha"], t["eta"], t["beta"], t["theta0"], t["s0"],
+                wl.chunk, wl.widths, y=y, theta_T=thT, s_T=sT, surprise=sur)
+    for _ in range(warmup):
+        run()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    B, T = t["q"].shape[:2]
+    return {"ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "path": tm.surprise_path(t["q"], wl.chunk, wl.widths)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +188,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-retrieve", action="store_true")
     ap.add_argument("--no-biases", action="store_true")
+    ap.add_argument("--no-surprise", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -273,6 +300,8 @@ def main():
     if not args.no_biases:
         # after the retrieve: it reads the squared-error scan's final weights
         result["biases"] = bench_biases(tm, torch, t, wl, (y, thT, sT), ws, args.steps, args.warmup)
+    if not args.no_surprise:
+        result["surprise"] = bench_surprise(tm, torch, t, wl, (y, thT, sT), min(args.steps, 5), 1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_sample_rows, args.cpu_sample_tokens)
     print(json.dumps(result), flush=True)

@@ -161,6 +161,35 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
                               void* y, float* theta_T, float* s_T,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The same scan, also writing each token's momentary surprise: surprise[b, t, h] =
+ * || grad_theta loss(M_theta_c(k_t), v_t) ||_2, the norm of the gradient the token writes
+ * with (at its chunk's start weights theta_c, under desc->bias); the explainer's
+ * "サプライズ（驚き）メトリクス" section calls this the momentary surprise.  Per layer the
+ * gradient is the outer product delta_l h_{l-1}^T, so the norm is
+ * sqrt(sum_l ||delta_l||^2 ||h_{l-1}||^2) -- no P-sized work per token.
+ *   surprise   device fp32 with alpha's layout (desc->gate_stride), 4-byte aligned; must
+ *              not overlap any other buffer (TITANS_ERR_INVALID_ARGUMENT)
+ *   workspace  >= titans_mem_scan_surprise_workspace_size bytes
+ * This call always runs the generic family ("phased_*" or "generic_*" by the width rule
+ * of titans_mem_scan_path; the fused kernels do not produce the norms).  Every other
+ * argument and result is as for titans_mem_scan.
+ */
+titans_status titans_mem_scan_surprise(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
+                                       const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* eta, const float* beta,
+                                       const float* theta0, const float* s0,
+                                       void* y, float* theta_T, float* s_T, float* surprise,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Which kernel titans_mem_scan_surprise runs ("phased_*" or "generic_*"; NULL if the
+ * arguments are invalid; static string). */
+const char* titans_mem_scan_surprise_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp);
+
+/* Workspace bytes titans_mem_scan_surprise needs (SIZE_MAX if the arguments are invalid). */
+size_t titans_mem_scan_surprise_workspace_size(const titans_scan_desc* desc,
+                                               const titans_mlp_desc* mlp);
+
 /* Which kernel titans_mem_retrieve runs for this problem: "fused_mfma" (bf16 MFMA; the
  * 64 -> 256 -> 64 memory with bf16 q / y), else "generic_mfma" (bf16) or "generic_fp32" (fp32 I/O).  NULL if the arguments are
  * invalid.  The returned string is static. */

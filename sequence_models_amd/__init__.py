@@ -59,6 +59,14 @@ lib.titans_mem_retrieve_path.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTE
 lib.titans_mem_scan.restype = ctypes.c_int
 lib.titans_mem_scan.argtypes = ([ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)] + [_vp] * 12
                                 + [ctypes.c_size_t, _vp])
+lib.titans_mem_scan_surprise.restype = ctypes.c_int
+lib.titans_mem_scan_surprise.argtypes = ([ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)]
+                                         + [_vp] * 13 + [ctypes.c_size_t, _vp])
+lib.titans_mem_scan_surprise_path.restype = ctypes.c_char_p
+lib.titans_mem_scan_surprise_path.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)]
+lib.titans_mem_scan_surprise_workspace_size.restype = ctypes.c_size_t
+lib.titans_mem_scan_surprise_workspace_size.argtypes = [ctypes.POINTER(ScanDesc),
+                                                        ctypes.POINTER(MlpDesc)]
 lib.titans_mem_retrieve.restype = ctypes.c_int
 lib.titans_mem_retrieve.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc), _vp, _vp,
                                     _vp, _vp]
@@ -162,16 +170,29 @@ def scan_path(q, chunk, widths) -> str:
     return r.decode()
 
 
+def surprise_path(q, chunk, widths) -> str:
+    """Name of the kernel the scan with per-token surprise norms runs: "phased_*" or
+    "generic_*" (the fused kernels do not produce the norms)."""
+    d = make_desc(q, chunk, q, None, None, None)
+    r = lib.titans_mem_scan_surprise_path(ctypes.byref(d), ctypes.byref(mlp_desc(widths)))
+    if r is None:
+        raise TitansError(1, "invalid scan shape or MLP widths")
+    return r.decode()
+
+
 def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, *, y=None, theta_T=None, s_T=None,
-         workspace=None, bias=None):
+         workspace=None, bias=None, surprise=None):
     """Chunked Titans memory scan on the current stream.
 
     q, k, v: [B,T,H,d] float32/bfloat16 CUDA tensors (d contiguous);
     alpha, eta, beta: [B,T,H] float32; theta0, s0: [H,P] (shared by the batch) or [B,H,P].
     bias: the attentional bias of the writes, None (squared error), ("huber", delta) or
     ("lp", p).
-    Returns (y [B,T,H,d] like q, theta_T [B,H,P], s_T [B,H,P]).  theta_T / s_T may be passed
-    as theta0 / s0 themselves for in-place streaming.
+    surprise: None, True (allocate) or a float32 tensor with alpha's shape and strides that
+    receives each token's gradient norm (titans_mem_scan_surprise: the generic kernels).
+    Returns (y [B,T,H,d] like q, theta_T [B,H,P], s_T [B,H,P]) and, when surprise is asked
+    for, the surprise tensor as a fourth result.  theta_T / s_T may be passed as theta0 / s0
+    themselves for in-place streaming.
     """
     B, T, H, dd = q.shape
     P = param_count(widths)
@@ -200,12 +221,26 @@ def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, *, y=None, theta_
         desc.bias = BIASES[bias[0]]
         desc.bias_param = float(bias[1]) if len(bias) > 1 else 0.0
     mlp = mlp_desc(widths)
+    if surprise is True:
+        surprise = torch.empty_like(alpha)
+    if surprise is not None:
+        if surprise.shape != alpha.shape or surprise.stride() != alpha.stride() or \
+                surprise.dtype != torch.float32:
+            raise ValueError("surprise must be float32 with alpha's shape and strides")
+    size_fn = (lib.titans_mem_scan_workspace_size if surprise is None
+               else lib.titans_mem_scan_surprise_workspace_size)
     if workspace is None:
-        n = lib.titans_mem_scan_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+        n = size_fn(ctypes.byref(desc), ctypes.byref(mlp))
         if n == ctypes.c_size_t(-1).value:
             n = 0  # the scan call below reports the argument error
         workspace = torch.empty(max(int(n), 1), dtype=torch.uint8, device=q.device) if n else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if surprise is not None:
+        _check(lib.titans_mem_scan_surprise(
+            ctypes.byref(desc), ctypes.byref(mlp), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+            _ptr(eta), _ptr(beta), _ptr(theta0), _ptr(s0), _ptr(y), _ptr(theta_T), _ptr(s_T),
+            _ptr(surprise), _ptr(workspace), ws_bytes, _stream()))
+        return y, theta_T, s_T, surprise
     _check(lib.titans_mem_scan(ctypes.byref(desc), ctypes.byref(mlp), _ptr(q), _ptr(k), _ptr(v),
                                _ptr(alpha), _ptr(eta), _ptr(beta), _ptr(theta0), _ptr(s0), _ptr(y),
                                _ptr(theta_T), _ptr(s_T), _ptr(workspace), ws_bytes, _stream()))

@@ -252,10 +252,8 @@ static Path choose_path(const titans::ScanArgs& a) {
     return titans::scan_mfma_supported(a) ? Path::Fused : generic_path(a);
 }
 
-const char* titans_mem_scan_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp) {
-    titans::ScanArgs a{};
-    if (prepare_scan(desc, mlp, a) != TITANS_OK) return nullptr;
-    switch (choose_path(a)) {
+static const char* path_name(Path p, const titans::ScanArgs& a) {
+    switch (p) {
         case Path::Pair: return "fused_pair";
         case Path::Fused: return "fused_mfma";
         case Path::Phased: return a.io == TITANS_BF16 ? "phased_mfma" : "phased_fp32";
@@ -263,11 +261,20 @@ const char* titans_mem_scan_path(const titans_scan_desc* desc, const titans_mlp_
     }
 }
 
-size_t titans_mem_scan_workspace_size(const titans_scan_desc* desc, const titans_mlp_desc* mlp) {
+const char* titans_mem_scan_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp) {
     titans::ScanArgs a{};
-    if (prepare_scan(desc, mlp, a) != TITANS_OK) return SIZE_MAX;
+    if (prepare_scan(desc, mlp, a) != TITANS_OK) return nullptr;
+    return path_name(choose_path(a), a);
+}
+
+// The path of a call; the per-token surprise output is computed by the generic family only.
+static Path scan_path_of(const titans::ScanArgs& a, bool surprise) {
+    return surprise ? generic_path(a) : choose_path(a);
+}
+
+static size_t workspace_of(const titans::ScanArgs& a, bool surprise) {
     if (a.B * a.H == 0 || a.T == 0) return 0;
-    switch (choose_path(a)) {
+    switch (scan_path_of(a, surprise)) {
         case Path::Pair: return titans::scan_pair_workspace_bytes(a);
         case Path::Fused: return 0;
         case Path::Phased: return titans::scan_phased_workspace_bytes(a);
@@ -275,11 +282,31 @@ size_t titans_mem_scan_workspace_size(const titans_scan_desc* desc, const titans
     }
 }
 
-titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
-                              const void* q, const void* k, const void* v, const float* alpha,
-                              const float* eta, const float* beta, const float* theta0,
-                              const float* s0, void* y, float* theta_T, float* s_T,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+size_t titans_mem_scan_workspace_size(const titans_scan_desc* desc, const titans_mlp_desc* mlp) {
+    titans::ScanArgs a{};
+    if (prepare_scan(desc, mlp, a) != TITANS_OK) return SIZE_MAX;
+    return workspace_of(a, false);
+}
+
+const char* titans_mem_scan_surprise_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp) {
+    titans::ScanArgs a{};
+    if (prepare_scan(desc, mlp, a) != TITANS_OK) return nullptr;
+    return path_name(scan_path_of(a, true), a);
+}
+
+size_t titans_mem_scan_surprise_workspace_size(const titans_scan_desc* desc,
+                                               const titans_mlp_desc* mlp) {
+    titans::ScanArgs a{};
+    if (prepare_scan(desc, mlp, a) != TITANS_OK) return SIZE_MAX;
+    return workspace_of(a, true);
+}
+
+static titans_status scan_impl(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
+                               const void* q, const void* k, const void* v, const float* alpha,
+                               const float* eta, const float* beta, const float* theta0,
+                               const float* s0, void* y, float* theta_T, float* s_T,
+                               float* surprise, bool want_surprise, void* workspace,
+                               size_t workspace_bytes, void* stream) {
     g_last_error[0] = '\0';
     titans::ScanArgs a{};
     titans_status st = prepare_scan(desc, mlp, a);
@@ -301,6 +328,10 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
         if ((st = check_io_alignment(a, k, a.qs, "k"))) return st;
         if ((st = check_io_alignment(a, v, a.qs, "v"))) return st;
         if ((st = check_io_alignment(a, y, a.ys, "y"))) return st;
+        if (want_surprise && !surprise)
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "surprise must be non-NULL");
+        if (want_surprise && (reinterpret_cast<uintptr_t>(surprise) & 3u) != 0)
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "surprise is not 4-byte aligned");
     }
     // ---- aliasing rules
     const size_t esz = a.io == TITANS_BF16 ? 2 : 4;
@@ -315,6 +346,9 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
         return fail(TITANS_ERR_INVALID_ARGUMENT, "y strides make distinct elements alias");
     if (!non_self_overlapping(st_sz, sst, 3))
         return fail(TITANS_ERR_INVALID_ARGUMENT, "theta_T/s_T strides make distinct elements alias");
+    if (want_surprise && have_tokens && !non_self_overlapping(g_sz, a.gs, 3))
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "gate strides make distinct surprise elements alias");
+    const Span ssur = (want_surprise && have_tokens) ? span_of(surprise, g_sz, a.gs, 3, 4) : Span{};
     Span sy = have_tokens ? span_of(y, io_sz, yst, 4, esz) : Span{};
     Span sth = span_of(theta_T, st_sz, sst, 3, 4), ssT = span_of(s_T, st_sz, sst, 3, 4);
     Span ins[8];
@@ -338,6 +372,11 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
     if (overlaps(sy, sth) || overlaps(sy, ssT) || overlaps(sth, ssT) || overlaps(sy, sth0) ||
         overlaps(sy, ss0))
         return fail(TITANS_ERR_INVALID_ARGUMENT, "outputs y, theta_T and s_T must not overlap");
+    for (int i = 0; i < nin; ++i)
+        if (overlaps(ssur, ins[i])) return fail(TITANS_ERR_INVALID_ARGUMENT, "surprise overlaps an input");
+    if (overlaps(ssur, sy) || overlaps(ssur, sth) || overlaps(ssur, ssT) || overlaps(ssur, sth0) ||
+        overlaps(ssur, ss0))
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "surprise overlaps a state or output buffer");
     if (!theta_inplace && (overlaps(sth, sth0) || overlaps(sth, ss0)))
         return fail(TITANS_ERR_INVALID_ARGUMENT,
                     "theta_T overlaps theta0/s0 without being exactly theta0");
@@ -346,7 +385,7 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
     if (theta_inplace && overlaps(sth, ss0) && !s_inplace)
         return fail(TITANS_ERR_INVALID_ARGUMENT, "theta_T overlaps s0");
     // ---- workspace
-    size_t need = titans_mem_scan_workspace_size(desc, mlp);
+    size_t need = workspace_of(a, want_surprise);
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
             return fail(TITANS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -357,7 +396,7 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
         for (int i = 0; i < nin; ++i)
             if (overlaps(sw, ins[i])) return fail(TITANS_ERR_INVALID_ARGUMENT, "workspace overlaps an input");
         if (overlaps(sw, sy) || overlaps(sw, sth) || overlaps(sw, ssT) || overlaps(sw, sth0) ||
-            overlaps(sw, ss0))
+            overlaps(sw, ss0) || overlaps(sw, ssur))
             return fail(TITANS_ERR_INVALID_ARGUMENT, "workspace overlaps a state or output buffer");
     }
     if (nseq == 0) return TITANS_OK;
@@ -365,6 +404,7 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
     a.alpha = alpha; a.eta = eta; a.beta = beta;
     a.theta0 = theta0; a.s0 = s0;
     a.y = y; a.thetaT = theta_T; a.sT = s_T;
+    a.surprise = want_surprise ? surprise : nullptr;
     a.ws = workspace;
     // Test hook for the pair path's failure handling: side 1 of every pair never posts its
     // exchange flags and every wait gives up after a few polls, so side 0 times out (its
@@ -372,13 +412,32 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
     const char* hook = getenv("TITANS_MEM_TEST_PAIR_TIMEOUT");
     a.debug = (hook && hook[0] == '1') ? 1 : 0;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    const Path path = a.T > 0 ? choose_path(a) : Path::Generic;
+    const Path path = a.T > 0 ? scan_path_of(a, want_surprise) : Path::Generic;
     hipError_t e = path == Path::Pair    ? titans::launch_scan_pair(a, hs)
                    : path == Path::Fused ? titans::launch_scan_mfma(a, hs)
                    : path == Path::Phased ? titans::launch_scan_phased(a, hs)
                                           : titans::launch_scan_generic(a, hs);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
     return TITANS_OK;
+}
+
+titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
+                              const void* q, const void* k, const void* v, const float* alpha,
+                              const float* eta, const float* beta, const float* theta0,
+                              const float* s0, void* y, float* theta_T, float* s_T,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    return scan_impl(desc, mlp, q, k, v, alpha, eta, beta, theta0, s0, y, theta_T, s_T, nullptr,
+                     false, workspace, workspace_bytes, stream);
+}
+
+titans_status titans_mem_scan_surprise(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
+                                       const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* eta, const float* beta,
+                                       const float* theta0, const float* s0, void* y,
+                                       float* theta_T, float* s_T, float* surprise,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+    return scan_impl(desc, mlp, q, k, v, alpha, eta, beta, theta0, s0, y, theta_T, s_T, surprise,
+                     true, workspace, workspace_bytes, stream);
 }
 
 static titans_status prepare_retrieve(const titans_scan_desc* desc, const titans_mlp_desc* mlp,

@@ -251,8 +251,9 @@ __host__ __device__ inline WsLayout ws_layout(int C, int L, const int* n) {
     return w;
 }
 
+// The layout comes in the argument block: it is indexed by layer at run time.
 template <bool kMfma>
-__global__ void __launch_bounds__(kThreads) scan_generic_kernel(ScanArgs a) {
+__global__ void __launch_bounds__(kThreads) scan_generic_kernel(ScanArgs a, WsLayout wl) {
     __shared__ float lds_gemm[kGemmLds];
     __shared__ float s_al[256], s_et[256], s_be[256];
 
@@ -263,7 +264,6 @@ __global__ void __launch_bounds__(kThreads) scan_generic_kernel(ScanArgs a) {
     const int64_t P = a.P;
     const int d = a.n[0];
 
-    const WsLayout wl = ws_layout(C, L, a.n);
     float* ws = static_cast<float*>(a.ws) + seq * wl.per_seq;
     float* coef_a = ws + wl.coef;
     float* coef_b = coef_a + (C + 1);
@@ -360,6 +360,27 @@ __global__ void __launch_bounds__(kThreads) scan_generic_kernel(ScanArgs a) {
             const float* Sp = ws + wl.sp[l - 1];
             gemm<kMfma>(n, nin, nout, MatA{Dl, nout, 1, nullptr}, MatB{W, nin, 1}, lds_gemm,
                        [&](int i, int jj, float g) { Dp[i * nin + jj] = g * Sp[i * nin + jj]; });
+        }
+        // ---- optional: each token's gradient norm; the gradient of layer l is the outer
+        // product Delta_l Hk_{l-1}^T, so its squared norm is |Delta_l|^2 |Hk_{l-1}|^2
+        if (a.surprise) {
+            for (int t = tid; t < n; t += kThreads) {
+                float acc = 0.0f;
+                // the Delta_l and Hk_l regions are consecutive: walk them by pointer
+                const float* Db = ws + wl.dl[1];
+                const float* Hb = ws + wl.hk[0];
+                for (int l = 1; l <= L; ++l) {
+                    const float* Dr = Db + (int64_t)t * a.n[l];
+                    const float* Hr = Hb + (int64_t)t * a.n[l - 1];
+                    float dd = 0.0f, hh = 0.0f;
+                    for (int i = 0; i < a.n[l]; ++i) dd = fmaf(Dr[i], Dr[i], dd);
+                    for (int i = 0; i < a.n[l - 1]; ++i) hh = fmaf(Hr[i], Hr[i], hh);
+                    acc = fmaf(dd, hh, acc);
+                    Db += round64((int64_t)C * a.n[l]);
+                    Hb += round64((int64_t)C * a.n[l - 1]);
+                }
+                a.surprise[gbase + (c0 + t) * a.gs[1]] = sqrtf(acc);
+            }
         }
         // ---- retrieval at the in-chunk weights, layer by layer
         int cur = 0;
@@ -489,10 +510,11 @@ hipError_t launch_scan_generic(const ScanArgs& a, hipStream_t stream) {
         copy_state_kernel<<<grid, 256, 0, stream>>>(a);
         return hipGetLastError();
     }
+    const WsLayout wl = ws_layout(a.C, a.L, a.n);
     if (a.io == TITANS_BF16)
-        scan_generic_kernel<true><<<dim3((unsigned)nseq), kThreads, 0, stream>>>(a);
+        scan_generic_kernel<true><<<dim3((unsigned)nseq), kThreads, 0, stream>>>(a, wl);
     else
-        scan_generic_kernel<false><<<dim3((unsigned)nseq), kThreads, 0, stream>>>(a);
+        scan_generic_kernel<false><<<dim3((unsigned)nseq), kThreads, 0, stream>>>(a, wl);
     return hipGetLastError();
 }
 

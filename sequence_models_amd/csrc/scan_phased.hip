@@ -528,7 +528,7 @@ __host__ __device__ inline PhLayout ph_layout(int C, int L, const int* n) {
     return w;
 }
 
-enum Task : int { kPrep = 0, kFwd, kBwd, kMq, kU, kQb, kCarry };
+enum Task : int { kPrep = 0, kFwd, kBwd, kMq, kU, kQb, kCarry, kNorm };
 
 // One segment of a launch: `count` blocks of one task on layer l; tiles are numbered
 // row-major over ceil(M/64) x tj tiles.
@@ -557,6 +557,7 @@ constexpr unsigned kSetFwd = bit(kFwd);
 constexpr unsigned kSetBwd = bit(kBwd);
 constexpr unsigned kSetRead = bit(kMq) | bit(kU);
 constexpr unsigned kSetLast = bit(kQb) | bit(kCarry);
+constexpr unsigned kSetNorm = bit(kNorm);
 
 template <bool kMfma, unsigned kTasks>
 __global__ void __launch_bounds__(kThreads, kTasks == kSetLast ? 2 : 1) phase_kernel(ScanArgs a, Phase ph) {
@@ -662,6 +663,31 @@ __global__ void __launch_bounds__(kThreads, kTasks == kSetLast ? 2 : 1) phase_ke
     float* W = theta + a.off[l];
     float* S = mom + a.off[l];
     void* lds = smem;
+
+    if (kTasks & bit(kNorm) && sg.task == kNorm) {
+        // each token's gradient norm: the gradient of layer l is Delta_l Hk_{l-1}^T, so its
+        // squared norm is |Delta_l|^2 |Hk_{l-1}|^2 (Hk_0 = k, read from the caller's tensor)
+        for (int t = tid; t < n; t += kThreads) {
+            float acc = 0.0f;
+            for (int m = 1; m <= L; ++m) {
+                const float* Dr = ws + wl.dl[m] + (int64_t)t * a.n[m];
+                float dd = 0.0f, hh = 0.0f;
+                for (int i = 0; i < a.n[m]; ++i) dd = fmaf(Dr[i], Dr[i], dd);
+                if (m == 1) {
+                    for (int i = 0; i < a.n[0]; ++i) {
+                        const float x = load_io(a.k, in_off + (int64_t)t * a.qs[1] + i, a.io);
+                        hh = fmaf(x, x, hh);
+                    }
+                } else {
+                    const float* Hr = ws + wl.hk[m - 1] + (int64_t)t * a.n[m - 1];
+                    for (int i = 0; i < a.n[m - 1]; ++i) hh = fmaf(Hr[i], Hr[i], hh);
+                }
+                acc = fmaf(dd, hh, acc);
+            }
+            a.surprise[gbase + (c0 + t) * a.gs[1]] = sqrtf(acc);
+        }
+        return;
+    }
 
     switch (sg.task) {
         case kFwd: {  // Z_l = Hk_{l-1} W_l^T
@@ -782,11 +808,12 @@ struct Launch {
         Seg& s = ph.seg[ph.nseg++];
         s.task = task;
         s.l = l;
-        s.tj = task == kPrep ? 1 : tiles(N);
+        const bool single = task == kPrep || task == kNorm;  // one block per memory
+        s.tj = single ? 1 : tiles(N);
         tasks |= bit(task);
-        s.count = task == kPrep ? 1 : tiles(M) * s.tj;
+        s.count = single ? 1 : tiles(M) * s.tj;
         blocks += s.count;
-        const int need = task == kPrep ? 0
+        const int need = (task == kPrep || task == kNorm) ? 0
                          : (task == kCarry || task == kU) ? mfma_lds_bytes(K < kWin3 ? K : kWin3, 3)
                                                           : mfma_lds_bytes(K, 2);
         if (need > lds) lds = need;
@@ -826,6 +853,8 @@ hipError_t run(const ScanArgs& a, hipStream_t stream) {
             phase_kernel<kMfma, kSetRead><<<grid, kThreads, lds, stream>>>(a, x.ph);
         else if (within(kSetLast))
             phase_kernel<kMfma, kSetLast><<<grid, kThreads, lds, stream>>>(a, x.ph);
+        else if (within(kSetNorm))
+            phase_kernel<kMfma, kSetNorm><<<grid, kThreads, lds, stream>>>(a, x.ph);
         else
             phase_kernel<kMfma, kSetFirst><<<grid, kThreads, lds, stream>>>(a, x.ph);
         return hipGetLastError();
@@ -882,6 +911,11 @@ hipError_t run(const ScanArgs& a, hipStream_t stream) {
                 Launch x = base();
                 x.add(kMq, l, n, n, a.n[l - 1]);
                 x.add(kU, l, n, a.n[l], a.n[l - 1]);
+                if ((e = go(x)) != hipSuccess) return e;
+            }
+            if (l == 1 && a.surprise) {  // every Delta is written: the token gradient norms
+                Launch x = base();
+                x.add(kNorm, 1, 0, 0, 0);
                 if ((e = go(x)) != hipSuccess) return e;
             }
             Launch x = base();

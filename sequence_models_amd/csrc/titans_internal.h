@@ -27,6 +27,7 @@ struct ScanArgs {
     const float* theta0;
     const float* s0;
     void* y;
+    float* surprise;           // NULL, or [B, T, H] per-token gradient norms (gate strides)
     float* thetaT;
     float* sT;
     void* ws;

@@ -241,3 +241,53 @@ def test_retrieve_validation():
     st = tm.lib.titans_mem_retrieve(ctypes.byref(desc), ctypes.byref(tm.mlp_desc((64, 999, 64))),
                                     ptrs["q"], ptrs["theta0"], ptrs["y"], None)
     assert st == UNSUPPORTED
+
+
+def _scan_surprise(desc, mlp, ptrs, surprise, ws=None, ws_bytes=0):
+    args = [ptrs.get(n) for n in ("q", "k", "v", "alpha", "eta", "beta", "theta0", "s0", "y",
+                                  "theta_T", "s_T")]
+    st = tm.lib.titans_mem_scan_surprise(ctypes.byref(desc), ctypes.byref(mlp), *args, surprise,
+                                         ws, ws_bytes, None)
+    assert st != HIP, "validation let the call through to HIP"
+    return st, tm.lib.titans_last_error().decode()
+
+
+def test_surprise_workspace_follows_the_generic_family(monkeypatch):
+    """The surprise call always runs the generic family: for the fused shape its workspace
+    is the phased path's, which TITANS_MEM_FORCE_GENERIC shows for the plain scan."""
+    mlp = tm.mlp_desc((64, 256, 64))
+    desc = _desc()
+    pair = tm.lib.titans_mem_scan_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+    sur = tm.lib.titans_mem_scan_surprise_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+    monkeypatch.setenv("TITANS_MEM_FORCE_GENERIC", "1")
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(desc), ctypes.byref(mlp)) == b"phased_mfma"
+    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(desc), ctypes.byref(mlp)) == sur
+    assert sur != pair
+    assert tm.lib.titans_mem_scan_surprise_path(ctypes.byref(desc), ctypes.byref(mlp)) == b"phased_mfma"
+    monkeypatch.delenv("TITANS_MEM_FORCE_GENERIC")
+    assert tm.lib.titans_mem_scan_surprise_path(ctypes.byref(desc), ctypes.byref(mlp)) == b"phased_mfma"
+    assert tm.lib.titans_mem_scan_surprise_path(ctypes.byref(_desc(io=0)),
+                                                ctypes.byref(tm.mlp_desc((64, 96, 64)))) == b"generic_fp32"
+    bad = ctypes.c_size_t(-1).value
+    assert tm.lib.titans_mem_scan_surprise_workspace_size(ctypes.byref(_desc(C=0)),
+                                                          ctypes.byref(mlp)) == bad
+
+
+@no_fake_pointers_on_gpu
+def test_surprise_validation():
+    mlp = tm.mlp_desc((64, 256, 64))
+    B, T, H, d, P = 2, 64, 4, 64, 32768
+    desc = _desc(B, T, H, d)
+    desc.state_stride[:] = (H * P, P)
+    desc.state0_stride[:] = (0, P)
+    ptrs, end = _fake_ptrs()
+    sur = end
+    ws = end + 4096 * 4
+    need = tm.lib.titans_mem_scan_surprise_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+    st, msg = _scan_surprise(desc, mlp, ptrs, None, ws, need)
+    assert st == INVALID and "surprise" in msg
+    assert _scan_surprise(desc, mlp, ptrs, sur + 2, ws, need)[0] == INVALID      # misaligned
+    assert _scan_surprise(desc, mlp, ptrs, ptrs["alpha"], ws, need)[0] == INVALID  # an input
+    assert _scan_surprise(desc, mlp, ptrs, ptrs["y"], ws, need)[0] == INVALID    # an output
+    assert _scan_surprise(desc, mlp, ptrs, ws, ws, need)[0] == INVALID          # the workspace
+    assert _scan_surprise(desc, mlp, ptrs, sur, ws, need - 1)[0] == WORKSPACE

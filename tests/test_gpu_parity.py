@@ -634,3 +634,41 @@ def test_attentional_bias_matches_oracle(path, bias, monkeypatch):
     y0, t0, _ = run_gpu(dev, wl)
     torch.cuda.synchronize()
     assert state_rel_err(to_f64(t0[:1, 1:2]), refs[0][1][None, None]) > 0.3
+
+
+# ------------------------------------------------------------ surprise norm
+
+SURPRISE_CASES = {
+    # name: (widths, C, io, env, expected path of the surprise call)
+    "generic_f32": ((16, 32, 16), 8, "f32", {"TITANS_MEM_GENERIC_MODE": "single"}, "generic_fp32"),
+    "generic_bf16": ((8, 24, 12, 8), 5, "bf16", {"TITANS_MEM_GENERIC_MODE": "single"}, "generic_mfma"),
+    "phased_f32": ((32, 160, 32), 40, "f32", {}, "phased_fp32"),
+    "phased_bf16": ((128, 512, 128), 128, "bf16", {}, "phased_mfma"),
+    "fused_shape": ((64, 256, 64), 64, "bf16", {}, "phased_mfma"),
+}
+
+
+@pytest.mark.parametrize("bias", [None, ("huber", 0.5)])
+@pytest.mark.parametrize("case", sorted(SURPRISE_CASES))
+def test_surprise_matches_oracle(case, bias, monkeypatch):
+    """Each token's gradient norm from titans_mem_scan_surprise against the oracle's (same
+    relative-error bars as y), with y and the state as in the plain scan."""
+    widths, C, io, env, expected = SURPRISE_CASES[case]
+    for k_, v_ in env.items():
+        monkeypatch.setenv(k_, v_)
+    wl, inp = _small(widths=widths, B=2, T=150, H=2, C=C, io=io, seed=C + 3)
+    dev = to_device(inp)
+    log(f"case surprise {case} bias={bias}")
+    assert tm.surprise_path(dev["q"], wl.chunk, wl.widths) == expected
+    y, thT, sT, sur = run_gpu(dev, wl, bias=bias, surprise=True)
+    torch.cuda.synchronize()
+    pairs = [(0, 1), (1, 0)]
+    check_pairs(wl, y, thT, sT, pairs, oracle_seq(inp, pairs, bias=bias))
+    q, k, v = [inp.qkv_f32(n) for n in ("q", "k", "v")]
+    *_, sr = oracle.scan(q, k, v, inp.alpha, inp.eta, inp.beta, inp.theta0, inp.s0, C, widths,
+                         bias=bias, surprise=True)
+    sg = to_f64(sur)
+    err = max(np.linalg.norm(sg[b, :, h] - sr[b, :, h]) / np.linalg.norm(sr[b, :, h])
+              for b in range(2) for h in range(2))
+    log(f"  surprise rel err {err:.2e}")
+    assert err <= Y_BAR[io]
