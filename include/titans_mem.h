@@ -190,9 +190,11 @@ const char* titans_mem_scan_surprise_path(const titans_scan_desc* desc, const ti
 size_t titans_mem_scan_surprise_workspace_size(const titans_scan_desc* desc,
                                                const titans_mlp_desc* mlp);
 
-/* Which kernel titans_mem_retrieve runs for this problem: "fused_mfma" (bf16 MFMA; the
- * 64 -> 256 -> 64 memory with bf16 q / y), else "generic_mfma" (bf16) or "generic_fp32" (fp32 I/O).  NULL if the arguments are
- * invalid.  The returned string is static. */
+/* Which kernel titans_mem_retrieve runs for this problem: "fused_mfma" (bf16 MFMA, both
+ * weight matrices in LDS; the 64 -> 256 -> 64 memory with bf16 q / y), "wide_mfma" (bf16
+ * MFMA with the weights streamed through LDS; bf16 memories whose widths are all multiples
+ * of 16), else "generic_mfma" (bf16) or "generic_fp32" (fp32 I/O).  NULL if the arguments
+ * are invalid.  The returned string is static. */
 const char* titans_mem_retrieve_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp);
 
 /*

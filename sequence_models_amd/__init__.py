@@ -248,8 +248,8 @@ def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, *, y=None, theta_
 
 
 def retrieve_path(q, widths) -> str:
-    """Name of the kernel titans_mem_retrieve runs for q's shape: "fused_mfma", "generic_mfma"
-    or "generic_fp32"."""
+    """Name of the kernel titans_mem_retrieve runs for q's shape: "fused_mfma", "wide_mfma",
+    "generic_mfma" or "generic_fp32"."""
     d = make_desc(q, 1, q, None, None, None)
     r = lib.titans_mem_retrieve_path(ctypes.byref(d), ctypes.byref(mlp_desc(widths)))
     if r is None:

@@ -28,6 +28,7 @@ SOURCES = {
     "scan_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "scan_pair.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "retrieve_mfma.hip": [],
+    "retrieve_wide.hip": [],
 }
 
 

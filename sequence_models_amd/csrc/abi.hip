@@ -448,17 +448,26 @@ static titans_status prepare_retrieve(const titans_scan_desc* desc, const titans
     return check_shape_support(a, false);
 }
 
-static bool retrieve_uses_mfma(const titans::ScanArgs& a) {
+enum class RPath { Fused, Wide, Generic };
+
+// The 64-256-64 bf16 memory keeps its weights in LDS ("fused_mfma"); other bf16 memories
+// with widths that are multiples of 16 stream them ("wide_mfma"); the rest, and fp32 I/O,
+// take the generic kernel.  TITANS_MEM_FORCE_GENERIC=1 forces the generic kernel.
+static RPath retrieve_path_of(const titans::ScanArgs& a) {
     const char* env = getenv("TITANS_MEM_FORCE_GENERIC");
-    if (env && env[0] == '1') return false;
-    return titans::retrieve_mfma_supported(a);
+    if (env && env[0] == '1') return RPath::Generic;
+    if (titans::retrieve_mfma_supported(a)) return RPath::Fused;
+    return titans::retrieve_wide_supported(a) ? RPath::Wide : RPath::Generic;
 }
 
 const char* titans_mem_retrieve_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp) {
     titans::ScanArgs a{};
     if (prepare_retrieve(desc, mlp, a) != TITANS_OK) return nullptr;
-    if (retrieve_uses_mfma(a)) return "fused_mfma";
-    return a.io == TITANS_BF16 ? "generic_mfma" : "generic_fp32";
+    switch (retrieve_path_of(a)) {
+        case RPath::Fused: return "fused_mfma";
+        case RPath::Wide: return "wide_mfma";
+        default: return a.io == TITANS_BF16 ? "generic_mfma" : "generic_fp32";
+    }
 }
 
 titans_status titans_mem_retrieve(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
@@ -489,8 +498,10 @@ titans_status titans_mem_retrieve(const titans_scan_desc* desc, const titans_mlp
     a.thetaT = const_cast<float*>(theta);
     a.y = y;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    hipError_t e = retrieve_uses_mfma(a) ? titans::launch_retrieve_mfma(a, hs)
-                                         : titans::launch_retrieve_generic(a, hs);
+    const RPath rp = retrieve_path_of(a);
+    hipError_t e = rp == RPath::Fused  ? titans::launch_retrieve_mfma(a, hs)
+                   : rp == RPath::Wide ? titans::launch_retrieve_wide(a, hs)
+                                       : titans::launch_retrieve_generic(a, hs);
     if (e != hipSuccess) return hip_fail(e, "retrieve launch");
     return TITANS_OK;
 }

@@ -1,0 +1,190 @@
+// Read with fixed weights, y = M_theta(q), on gfx950 MFMA for any memory whose widths are
+// multiples of 16 (up to 512, L <= 4) with bf16 q / y (the explainer's retrieve formula
+// with theta held constant).  The 64 -> 256 -> 64 memory has its own kernel
+// (retrieve_mfma.hip) that keeps both weight matrices in LDS; wider memories (the deep
+// 128-512-512-512-128 one holds 2.6 MB of weights) do not fit, so here the weights stream.
+//
+// A workgroup (four waves) serves one (b, h) memory and 32 tokens.  The tokens'
+// activations stay in LDS as bf16 across all layers (two 32 x 512 buffers, ping-pong);
+// each layer's weights pass through LDS in 64-output x 256-input windows, double-buffered:
+// the next window's 16-byte loads are in flight while the current window's MFMAs run.
+// Per window, wave w computes outputs 16w .. 16w+15 of the window's 64 for all 32 tokens
+// (v_mfma_f32_16x16x32_bf16, A = weight rows, B = activation rows, fp32 accumulation); an
+// output tile's epilogue applies SiLU (hidden layers) and writes bf16 activations, or y.
+// Workgroups are numbered so that each XCD holds whole memories: all token tiles of a
+// memory then read its weights through one L2.
+#include <hip/hip_runtime.h>
+
+#include "mfma_util.h"
+#include "titans_internal.h"
+
+namespace titans {
+namespace {
+
+using namespace fused;
+
+constexpr int kThreads = 256;
+constexpr int kTok = 32;          // tokens per workgroup
+constexpr int kOut = 64;          // outputs per tile
+constexpr int kWin = 256;         // inputs per weight window
+constexpr int kMaxW = 512;
+constexpr int kActLd = kMaxW + 8; // padded activation row (bf16)
+constexpr int kWLd = kWin + 8;    // padded weight row (bf16)
+constexpr int kGroups = kOut * kWin / 4 / kThreads;  // 16-byte groups per thread per window
+
+struct __attribute__((aligned(16))) WSmem {
+    __bf16 act[2][kTok * kActLd];  // [token][feature]
+    __bf16 w[2][kOut * kWLd];      // [output][input - k0]
+};
+
+// One weight window: rows o0 .. o0+63 (< nout) and columns k0 .. k0+255 (< nin) of W
+// (row-major nout x nin, fp32).  Thread t loads columns 4 (t % 64) .. +3 of rows
+// t / 64 + 4 m, m < 16: sixteen 16-byte loads (64 contiguous floats per row and wave).
+struct Window {
+    f32x4 v[kGroups];
+};
+
+__device__ __forceinline__ void load_window(Window& x, const float* W, int nout, int nin, int o0,
+                                            int k0) {
+    const int tid = threadIdx.x;
+    const int k = k0 + 4 * (tid & 63);
+#pragma unroll
+    for (int m = 0; m < kGroups; ++m) {
+        const int r = o0 + (tid >> 6) + 4 * m;
+        x.v[m] = (r < nout && k < nin) ? *reinterpret_cast<const f32x4*>(W + (int64_t)r * nin + k)
+                                       : zero4();
+    }
+}
+
+__device__ __forceinline__ void store_window(const Window& x, __bf16* dst) {
+    const int tid = threadIdx.x;
+    const int kk = 4 * (tid & 63);
+#pragma unroll
+    for (int m = 0; m < kGroups; ++m)
+        *reinterpret_cast<bf16x4*>(dst + ((tid >> 6) + 4 * m) * kWLd + kk) = bf4(x.v[m]);
+}
+
+__global__ void __launch_bounds__(kThreads) retrieve_wide_kernel(ScanArgs A) {
+    __shared__ WSmem sm;
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6, g = (tid & 63) >> 4, j = tid & 15;
+
+    // XCD-contiguous numbering of (memory, token tile)
+    const int64_t ntiles = (A.T + kTok - 1) / kTok;
+    const int64_t nblk = gridDim.x;
+    const int64_t w = blockIdx.x;
+    const int64_t full = nblk & ~int64_t(7);
+    const int64_t lid = w < full ? (w & 7) * (full >> 3) + (w >> 3) : w;
+    const int64_t seq = lid / ntiles;
+    const int64_t t0 = (lid % ntiles) * kTok;
+    const int64_t bi = seq / A.H, hi = seq % A.H;
+    const float* th = A.thetaT + bi * A.ss[0] + hi * A.ss[1];
+    const __bf16* qg = static_cast<const __bf16*>(A.q);
+    __bf16* yg = static_cast<__bf16*>(A.y);
+    const int64_t qbase = bi * A.qs[0] + hi * A.qs[2];
+    const int64_t ybase = bi * A.ys[0] + hi * A.ys[2];
+    const int d = A.n[0];
+
+    // the window sequence: layer l, output tile o0, input window k0
+    int wl = 1, wo = 0, wk = 0;
+    auto advance = [&](int& L_, int& o_, int& k_) {
+        k_ += kWin;
+        if (k_ >= A.n[L_ - 1]) {
+            k_ = 0;
+            o_ += kOut;
+            if (o_ >= A.n[L_]) {
+                o_ = 0;
+                ++L_;
+            }
+        }
+    };
+
+    // first window in flight while q lands in LDS.  Both activation buffers start at zero:
+    // a 32-wide MFMA step over a width that is a multiple of 16 only reads up to 16
+    // columns past it, against zero weights, and those columns must be finite.
+    Window nx;
+    load_window(nx, th + A.off[1], A.n[1], A.n[0], 0, 0);
+    for (int i = tid; i < 2 * kTok * kActLd / 8; i += kThreads)
+        reinterpret_cast<bf16x8*>(&sm.act[0][0])[i] = bf16x8{};
+    __syncthreads();
+    for (int i = tid; i < kTok * (d / 4); i += kThreads) {
+        const int t = i / (d / 4), c = 4 * (i % (d / 4));
+        bf16x4 v{};
+        if (t0 + t < A.T)
+            v = *reinterpret_cast<const bf16x4*>(qg + qbase + (t0 + t) * A.qs[1] + c);
+        *reinterpret_cast<bf16x4*>(sm.act[0] + t * kActLd + c) = v;
+    }
+    store_window(nx, sm.w[0]);
+    __syncthreads();
+
+    int buf = 0, cur = 0;
+    f32x4 acc[2] = {zero4(), zero4()};
+    while (wl <= A.L) {
+        const int nin = A.n[wl - 1], nout = A.n[wl];
+        // the following window's loads go out before this one's MFMAs
+        int L2 = wl, o2 = wo, k2 = wk;
+        advance(L2, o2, k2);
+        const bool more = L2 <= A.L;
+        if (more) load_window(nx, th + A.off[L2], A.n[L2], A.n[L2 - 1], o2, k2);
+
+        const int kw = (nin - wk) < kWin ? (nin - wk) : kWin;  // a multiple of 16
+        const __bf16* ar = sm.w[buf] + (16 * wv + j) * kWLd + 4 * g;
+#pragma unroll 2
+        for (int ks = 0; ks < kw; ks += 32) {
+            const bf16x8 a = frag(ar, ks);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const __bf16* br = sm.act[cur] + (16 * ct + j) * kActLd + wk + ks + 4 * g;
+                acc[ct] = mfma(a, frag(br, 0), acc[ct]);
+            }
+        }
+        if (wk + kWin >= nin) {  // last window of this output tile: epilogue
+            const int f0 = wo + 16 * wv + 4 * g;  // outputs f0 .. f0+3 of token 16 ct + j
+            if (wl < A.L) {
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    f32x4 h;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) h[r] = acc[ct][r] * sigmoid(acc[ct][r]);
+                    if (f0 < nout)
+                        *reinterpret_cast<bf16x4*>(sm.act[cur ^ 1] + (16 * ct + j) * kActLd + f0) =
+                            bf4(h);
+                }
+            } else {
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const int64_t t = t0 + 16 * ct + j;
+                    if (f0 < nout && t < A.T)
+                        *reinterpret_cast<bf16x4*>(yg + ybase + t * A.ys[1] + f0) = bf4(acc[ct]);
+                }
+            }
+            acc[0] = acc[1] = zero4();
+        }
+        if (more) store_window(nx, sm.w[buf ^ 1]);
+        __syncthreads();  // the next window is in LDS; a finished layer's outputs too
+        if (more && L2 != wl) cur ^= 1;
+        buf ^= 1;
+        wl = L2;
+        wo = o2;
+        wk = k2;
+    }
+}
+
+}  // namespace
+
+bool retrieve_wide_supported(const ScanArgs& a) {
+    if (a.io != TITANS_BF16 || a.L < 1 || a.L > TITANS_MAX_LAYERS) return false;
+    for (int l = 0; l <= a.L; ++l)
+        if (a.n[l] % 16 != 0 || a.n[l] > kMaxW) return false;
+    return true;
+}
+
+hipError_t launch_retrieve_wide(const ScanArgs& a, hipStream_t stream) {
+    const int64_t nseq = a.B * a.H;
+    if (nseq == 0 || a.T == 0) return hipSuccess;
+    const int64_t blocks = (a.T + kTok - 1) / kTok * nseq;
+    retrieve_wide_kernel<<<dim3((unsigned)blocks), kThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace titans

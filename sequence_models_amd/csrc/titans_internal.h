@@ -63,6 +63,11 @@ hipError_t launch_scan_pair(const ScanArgs& a, hipStream_t stream);
 // Generic retrieve: any supported shape, products as in the generic scan.
 hipError_t launch_retrieve_generic(const ScanArgs& a, hipStream_t stream);
 
+// MFMA retrieve for any memory with widths multiples of 16 (<= 512) and bf16 q / y:
+// activations in LDS, weights streamed in windows.
+bool retrieve_wide_supported(const ScanArgs& a);
+hipError_t launch_retrieve_wide(const ScanArgs& a, hipStream_t stream);
+
 // MFMA retrieve for the 64 -> 256 -> 64 memory with bf16 q / y.
 bool retrieve_mfma_supported(const ScanArgs& a);
 hipError_t launch_retrieve_mfma(const ScanArgs& a, hipStream_t stream);

@@ -106,7 +106,11 @@ def test_workspace_size_query(monkeypatch):
     assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=0)), ctypes.byref(mlp)) is None
     assert tm.lib.titans_mem_retrieve_path(ctypes.byref(_desc()), ctypes.byref(mlp)) == b"fused_mfma"
     assert tm.lib.titans_mem_retrieve_path(ctypes.byref(_desc(io=0)), ctypes.byref(mlp)) == b"generic_fp32"
-    assert tm.lib.titans_mem_retrieve_path(ctypes.byref(_desc()), ctypes.byref(tm.mlp_desc((64, 128, 64)))) == b"generic_mfma"
+    assert tm.lib.titans_mem_retrieve_path(ctypes.byref(_desc()), ctypes.byref(tm.mlp_desc((64, 128, 64)))) == b"wide_mfma"
+    assert tm.lib.titans_mem_retrieve_path(ctypes.byref(_desc(d=16)),
+                                           ctypes.byref(tm.mlp_desc((16, 24, 16)))) == b"generic_mfma"
+    assert tm.lib.titans_mem_retrieve_path(ctypes.byref(_desc(io=0)),
+                                           ctypes.byref(tm.mlp_desc((64, 128, 64)))) == b"generic_fp32"
     assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(T=0)), ctypes.byref(mlp)) == 0
     bad = ctypes.c_size_t(-1).value
     assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(C=0)), ctypes.byref(mlp)) == bad

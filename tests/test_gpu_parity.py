@@ -376,6 +376,33 @@ def test_retrieve_mfma_matches_generic_and_oracle(T, monkeypatch):
     assert e1 <= 2e-2 and e2 <= 2e-2
 
 
+@pytest.mark.parametrize("T", [1, 31, 33, 700])
+@pytest.mark.parametrize("widths", [(128, 512, 512, 512, 128), (32, 160, 96, 32), (64, 384, 64),
+                                    (16, 32, 16)])
+def test_retrieve_wide_matches_oracle(widths, T):
+    """bf16 memories other than 64-256-64 with widths multiples of 16: weights streamed
+    through LDS; per-batch weights, strided q and y, ragged token counts."""
+    wl, inp = _small(widths=widths, B=2, T=T, H=3, io="bf16", seed=T + len(widths))
+    dev = to_device(inp)
+    log(f"case retrieve wide {widths} T={T}")
+    B, H = 2, 3
+    rng = np.random.default_rng(T)
+    scale = [1.0 / np.sqrt(w) for w in widths[:-1]]
+    theta = np.concatenate([(rng.standard_normal((B, H, widths[l + 1] * widths[l])) * scale[l])
+                            for l in range(len(widths) - 1)], axis=2).astype(np.float32)
+    theta_t = torch.from_numpy(theta).cuda()
+    packed = torch.stack([dev["q"], dev["k"]], dim=3)
+    q = packed[:, :, :, 0]
+    assert tm.retrieve_path(q, wl.widths) == "wide_mfma"
+    y = torch.empty(B, T, H, 2 * wl.d, dtype=torch.bfloat16, device="cuda")[..., : wl.d]
+    y = tm.retrieve(q, theta_t, wl.widths, y=y)
+    torch.cuda.synchronize()
+    yr = oracle.retrieve(inp.qkv_f32("q"), theta, wl.widths)
+    err = y_rel_err(to_f64(y), yr)
+    log(f"  wide vs oracle {err:.2e}")
+    assert err <= 2e-2
+
+
 def test_retrieve_headline_shape_sampled():
     wl = synthetic.WORKLOADS[synthetic.HEADLINE]
     inp = synthetic.make_inputs(wl, 0)
