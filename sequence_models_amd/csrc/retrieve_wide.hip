@@ -129,7 +129,6 @@ __global__ void __launch_bounds__(kThreads) retrieve_wide_kernel(ScanArgs A) {
 
         const int kw = (nin - wk) < kWin ? (nin - wk) : kWin;  // a multiple of 16
         const __bf16* ar = sm.w[buf] + (16 * wv + j) * kWLd + 4 * g;
-#pragma unroll 2
         for (int ks = 0; ks < kw; ks += 32) {
             const bf16x8 a = frag(ar, ks);
 #pragma unroll
