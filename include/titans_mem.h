@@ -123,7 +123,10 @@ int64_t titans_mem_param_count(const titans_mlp_desc* mlp);
  * else "fused_mfma" (one workgroup per memory; C = 64).  Every other supported shape runs the
  * generic family: "phased_mfma" / "phased_fp32" when a layer has 128 or more units (each
  * chunk step's products spread as 64 x 64 tiles over the whole GPU, one launch per step),
- * else "generic_mfma" / "generic_fp32" (one workgroup per memory); the _mfma kernels serve
+ * else "generic_mfma" / "generic_fp32" (one workgroup per memory).  A linear memory (L = 1)
+ * with the squared-error bias and at least 16 chunks per sequence runs "linear_mfma" /
+ * "linear_fp32": its chunk carries are affine maps of (W, S), composed in parallel over
+ * groups of chunks, so the sequence axis is split over the GPU.  The _mfma kernels serve
  * bf16 I/O (bf16 MFMA products, fp32 accumulation and state), the _fp32 ones fp32 I/O (fp32
  * arithmetic throughout).  NULL if the arguments are invalid.  The returned string is
  * static. */

@@ -222,7 +222,7 @@ static int64_t device_cus() {
     return n;
 }
 
-enum class Path { Generic, Phased, Fused, Pair };
+enum class Path { Generic, Phased, Fused, Pair, Linear };
 
 // Within the generic family: the chain of GPU-wide launches for memories with a layer of
 // 128 or more units (their chunk products span several 64 x 64 tiles), else one workgroup
@@ -238,12 +238,16 @@ static Path generic_path(const titans::ScanArgs& a) {
 
 // Which kernel serves a (validated) problem.  The 64-256-64 bf16 memory runs on pairs of
 // workgroups (any chunk length that is a multiple of 64) while the pairs fit the device at
-// one workgroup per compute unit, else on one workgroup per memory (C = 64 only).  Debugging switches: TITANS_MEM_FORCE_GENERIC=1 routes every call
-// through the generic kernel, TITANS_MEM_FUSED_SINGLE=1 keeps the fused shape on one
-// workgroup per memory.
+// one workgroup per compute unit, else on one workgroup per memory (C = 64 only).  A linear
+// memory (L = 1) with the squared-error bias and enough chunks takes the sequence-parallel
+// linear path.  Debugging switches: TITANS_MEM_FORCE_GENERIC=1 routes every call through
+// the generic family, TITANS_MEM_LINEAR=0 keeps linear memories on it too,
+// TITANS_MEM_FUSED_SINGLE=1 keeps the fused shape on one workgroup per memory.
 static Path choose_path(const titans::ScanArgs& a) {
     const char* env = getenv("TITANS_MEM_FORCE_GENERIC");
     if (env && env[0] == '1') return generic_path(a);
+    env = getenv("TITANS_MEM_LINEAR");
+    if (!(env && env[0] == '0') && titans::scan_linear_supported(a)) return Path::Linear;
     env = getenv("TITANS_MEM_FUSED_SINGLE");
     const bool single = env && env[0] == '1';
     if (!single && titans::scan_pair_supported(a) &&
@@ -257,6 +261,7 @@ static const char* path_name(Path p, const titans::ScanArgs& a) {
         case Path::Pair: return "fused_pair";
         case Path::Fused: return "fused_mfma";
         case Path::Phased: return a.io == TITANS_BF16 ? "phased_mfma" : "phased_fp32";
+        case Path::Linear: return a.io == TITANS_BF16 ? "linear_mfma" : "linear_fp32";
         default: return a.io == TITANS_BF16 ? "generic_mfma" : "generic_fp32";
     }
 }
@@ -278,6 +283,7 @@ static size_t workspace_of(const titans::ScanArgs& a, bool surprise) {
         case Path::Pair: return titans::scan_pair_workspace_bytes(a);
         case Path::Fused: return 0;
         case Path::Phased: return titans::scan_phased_workspace_bytes(a);
+        case Path::Linear: return titans::scan_linear_workspace_bytes(a);
         default: return titans::scan_generic_workspace_bytes(a);
     }
 }
@@ -416,6 +422,7 @@ static titans_status scan_impl(const titans_scan_desc* desc, const titans_mlp_de
     hipError_t e = path == Path::Pair    ? titans::launch_scan_pair(a, hs)
                    : path == Path::Fused ? titans::launch_scan_mfma(a, hs)
                    : path == Path::Phased ? titans::launch_scan_phased(a, hs)
+                   : path == Path::Linear ? titans::launch_scan_linear(a, hs)
                                           : titans::launch_scan_generic(a, hs);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
     return TITANS_OK;

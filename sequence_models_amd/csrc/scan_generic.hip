@@ -251,42 +251,64 @@ __host__ __device__ inline WsLayout ws_layout(int C, int L, const int* n) {
     return w;
 }
 
+// Sequence groups of the linear-memory path: group g of a memory runs tokens
+// [g span, (g + 1) span) from the state the combine pass left in states (W then S, P
+// floats each, per (memory, group)); the last group copies its end state to theta_T, s_T.
+struct Groups {
+    int G;          // groups per memory; 0: whole sequences from theta0, s0
+    int64_t span;   // tokens per group (a multiple of C)
+    float* states;  // [B*H][G][2P]
+};
+
 // The layout comes in the argument block: it is indexed by layer at run time.
 template <bool kMfma>
-__global__ void __launch_bounds__(kThreads) scan_generic_kernel(ScanArgs a, WsLayout wl) {
+__global__ void __launch_bounds__(kThreads) scan_generic_kernel(ScanArgs a, WsLayout wl,
+                                                                 Groups grp) {
     __shared__ float lds_gemm[kGemmLds];
     __shared__ float s_al[256], s_et[256], s_be[256];
 
-    const int64_t seq = blockIdx.x;
+    const int64_t wg = blockIdx.x;  // (memory, group) in group mode, else the memory
+    const int64_t seq = grp.G ? wg / grp.G : wg;
+    const int64_t grp_i = grp.G ? wg % grp.G : 0;
     const int64_t b = seq / a.H, h = seq % a.H;
     const int tid = threadIdx.x;
     const int L = a.L, C = a.C;
     const int64_t P = a.P;
     const int d = a.n[0];
 
-    float* ws = static_cast<float*>(a.ws) + seq * wl.per_seq;
+    float* ws = static_cast<float*>(a.ws) + wg * wl.per_seq;
     float* coef_a = ws + wl.coef;
     float* coef_b = coef_a + (C + 1);
     float* coef_w = coef_b + (C + 1);
     float* coef_p = coef_w + C;
     float* Cm = ws + wl.cm;
 
-    float* theta = a.thetaT + b * a.ss[0] + h * a.ss[1];
-    float* mom = a.sT + b * a.ss[0] + h * a.ss[1];
-    const float* theta0 = a.theta0 + b * a.s0s[0] + h * a.s0s[1];
-    const float* mom0 = a.s0 + b * a.s0s[0] + h * a.s0s[1];
-    if (theta != theta0)
-        for (int64_t i = tid; i < P; i += kThreads) theta[i] = theta0[i];
-    if (mom != mom0)
-        for (int64_t i = tid; i < P; i += kThreads) mom[i] = mom0[i];
+    float* thetaT = a.thetaT + b * a.ss[0] + h * a.ss[1];
+    float* momT = a.sT + b * a.ss[0] + h * a.ss[1];
+    float* theta = thetaT;
+    float* mom = momT;
+    int64_t t_begin = 0, t_end = a.T;
+    if (grp.G) {  // the group's start state was written by the combine pass
+        theta = grp.states + wg * 2 * P;
+        mom = theta + P;
+        t_begin = grp_i * grp.span;
+        t_end = t_begin + grp.span < a.T ? t_begin + grp.span : a.T;
+    } else {
+        const float* theta0 = a.theta0 + b * a.s0s[0] + h * a.s0s[1];
+        const float* mom0 = a.s0 + b * a.s0s[0] + h * a.s0s[1];
+        if (theta != theta0)
+            for (int64_t i = tid; i < P; i += kThreads) theta[i] = theta0[i];
+        if (mom != mom0)
+            for (int64_t i = tid; i < P; i += kThreads) mom[i] = mom0[i];
+    }
     __syncthreads();
 
     const int64_t qbase = b * a.qs[0] + h * a.qs[2];
     const int64_t ybase = b * a.ys[0] + h * a.ys[2];
     const int64_t gbase = b * a.gs[0] + h * a.gs[2];
 
-    for (int64_t c0 = 0; c0 < a.T; c0 += C) {
-        const int n = (int)((a.T - c0) < C ? (a.T - c0) : C);
+    for (int64_t c0 = t_begin; c0 < t_end; c0 += C) {
+        const int n = (int)((t_end - c0) < C ? (t_end - c0) : C);
         // ---- stage gates, K (as Hk_0) and Q (as Hq_0) in fp32
         for (int t = tid; t < n; t += kThreads) {
             int64_t gi = gbase + (c0 + t) * a.gs[1];
@@ -438,6 +460,13 @@ __global__ void __launch_bounds__(kThreads) scan_generic_kernel(ScanArgs a, WsLa
                        });
         }
     }
+    if (grp.G && grp_i == grp.G - 1) {  // the sequence's end state
+        __syncthreads();
+        for (int64_t i = tid; i < P; i += kThreads) {
+            thetaT[i] = theta[i];
+            momT[i] = mom[i];
+        }
+    }
 }
 
 constexpr int kRetrieveTokens = 16;
@@ -495,7 +524,234 @@ __global__ void copy_state_kernel(ScanArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- linear memory (L = 1)
+//
+// With one layer and the squared-error bias the chunk-end carry is affine in the state
+// X = [W | S] (d x 2d): with Delta_j = 2 (W k_j - v_j),
+//   W' = a W - b S - sum_j c_j Delta_j k_j^T = W (a I - 2 Gc) - b S + 2 Hc
+//   S' = p S + sum_j w_j Delta_j k_j^T      = W (2 Gw) + p S - 2 Hw
+// Gc = K^T diag(c) K, Gw = K^T diag(w) K, Hc = V^T diag(c) K, Hw = V^T diag(w) K, i.e.
+//   X' = X M + N,  M = [[a I - 2 Gc, 2 Gw], [-b I, p I]],  N = [2 Hc, -2 Hw].
+// Affine maps compose associatively (the explainer's "associative scan" applies exactly
+// here, and only here: a deeper memory's gradient is not linear in W).  A sequence is cut
+// into G groups of chunks: the summary kernel composes each group's maps (P, Q) in
+// parallel (P <- P M, Q <- Q M + N from P = I, Q = 0), the combine kernel runs
+// X_{g+1} = X_g P_g + Q_g over the groups of a memory, and the generic kernel then runs
+// every group's chunks (reads and carry) from its start state in parallel.  fp32
+// throughout the summary and combine.
+
+struct LinLayout {  // floats per (memory, group) summary area
+    int64_t P11, P12, P21, P22, Q1, Q2;  // the composed map, d x d blocks
+    int64_t Gc, Gw, Hc, Hw;             // one chunk's products
+    int64_t T[6];                        // P11 Gc, P11 Gw, P21 Gc, P21 Gw, Q1 Gc, Q1 Gw
+    int64_t K, V;                        // the chunk's K, V (C x d)
+    int64_t c, w;                        // its c_C, w
+    int64_t per_group;
+};
+
+__host__ __device__ inline LinLayout lin_layout(int C, int d) {
+    auto r64 = [](int64_t x) { return (x + 63) & ~int64_t(63); };
+    const int64_t dd = r64((int64_t)d * d);
+    LinLayout l{};
+    int64_t o = 0;
+    int64_t* blocks[16] = {&l.P11, &l.P12, &l.P21, &l.P22, &l.Q1, &l.Q2, &l.Gc, &l.Gw,
+                           &l.Hc, &l.Hw, &l.T[0], &l.T[1], &l.T[2], &l.T[3], &l.T[4], &l.T[5]};
+    for (int i = 0; i < 16; ++i) { *blocks[i] = o; o += dd; }
+    l.K = o; o += r64((int64_t)C * d);
+    l.V = o; o += r64((int64_t)C * d);
+    l.c = o; o += r64(C);
+    l.w = o; o += r64(C);
+    l.per_group = o;
+    return l;
+}
+
+__global__ void __launch_bounds__(kThreads) linear_summary_kernel(ScanArgs a, Groups grp,
+                                                                   LinLayout ll, float* sums) {
+    __shared__ float lds_gemm[kGemmLds];
+    __shared__ float s_al[256], s_et[256], s_be[256];
+    __shared__ float s_tail[3];  // a_n, b_n, p of the chunk
+    const int64_t wg = blockIdx.x;
+    const int64_t seq = wg / grp.G, gi = wg % grp.G;
+    const int64_t b = seq / a.H, h = seq % a.H;
+    const int tid = threadIdx.x, d = a.n[0], C = a.C;
+    const int64_t dd = (int64_t)d * d;
+    float* z = sums + wg * ll.per_group;
+    float *P11 = z + ll.P11, *P12 = z + ll.P12, *P21 = z + ll.P21, *P22 = z + ll.P22;
+    float *Q1 = z + ll.Q1, *Q2 = z + ll.Q2;
+    float *Gc = z + ll.Gc, *Gw = z + ll.Gw, *Hc = z + ll.Hc, *Hw = z + ll.Hw;
+    float* Kst = z + ll.K;
+    float* Vst = z + ll.V;
+    float* cv = z + ll.c;
+    float* wv = z + ll.w;
+    for (int64_t e = tid; e < dd; e += kThreads) {
+        const int i = (int)(e / d), j = (int)(e % d);
+        P11[e] = P22[e] = (i == j) ? 1.0f : 0.0f;
+        P12[e] = P21[e] = Q1[e] = Q2[e] = 0.0f;
+    }
+    const int64_t qbase = b * a.qs[0] + h * a.qs[2];
+    const int64_t gbase = b * a.gs[0] + h * a.gs[2];
+    const int64_t t_begin = gi * grp.span;
+    const int64_t t_end = t_begin + grp.span < a.T ? t_begin + grp.span : a.T;
+    for (int64_t c0 = t_begin; c0 < t_end; c0 += C) {
+        const int n = (int)((t_end - c0) < C ? (t_end - c0) : C);
+        for (int t = tid; t < n; t += kThreads) {
+            const int64_t g = gbase + (c0 + t) * a.gs[1];
+            s_al[t] = a.alpha[g];
+            s_et[t] = a.eta[g];
+            s_be[t] = a.beta[g];
+        }
+        for (int e = tid; e < n * d; e += kThreads) {
+            const int t = e / d, c = e % d;
+            const int64_t src = qbase + (c0 + t) * a.qs[1] + c;
+            Kst[e] = load_io(a.k, src, a.io);
+            Vst[e] = load_io(a.v, src, a.io);
+        }
+        __syncthreads();
+        {  // chunk-end coefficients: thread j follows column j of the coefficient recurrence
+            const int j = tid;
+            float Bj = 0.0f, cj = 0.0f, at = 1.0f, bt = 0.0f, pb = 1.0f;
+            const float omb_j = (j < n) ? 1.0f - s_be[j] : 0.0f;
+            for (int t = 0; t < n; ++t) {
+                const float al = s_al[t], et = s_et[t], be = s_be[t];
+                pb *= be;
+                if (j < t) Bj *= be;
+                else if (j == t) Bj = 1.0f;
+                const float keep = 1.0f - al;
+                at *= keep;
+                bt = keep * bt + et * pb;
+                cj = keep * cj + ((j <= t) ? et * omb_j * Bj : 0.0f);
+            }
+            if (j < n) {
+                cv[j] = cj;
+                wv[j] = omb_j * Bj;
+            }
+            if (j == 0) {
+                s_tail[0] = at;
+                s_tail[1] = bt;
+                s_tail[2] = pb;
+            }
+        }
+        __syncthreads();
+        // Gc, Gw, Hc, Hw: sums over the chunk's tokens of scaled outer products
+        block_gemm(d, d, n, MatA{Kst, 1, d, cv}, MatB{Kst, d, 1}, lds_gemm,
+                   [&](int i, int j, float x) { Gc[i * d + j] = x; });
+        block_gemm(d, d, n, MatA{Kst, 1, d, wv}, MatB{Kst, d, 1}, lds_gemm,
+                   [&](int i, int j, float x) { Gw[i * d + j] = x; });
+        block_gemm(d, d, n, MatA{Vst, 1, d, cv}, MatB{Kst, d, 1}, lds_gemm,
+                   [&](int i, int j, float x) { Hc[i * d + j] = x; });
+        block_gemm(d, d, n, MatA{Vst, 1, d, wv}, MatB{Kst, d, 1}, lds_gemm,
+                   [&](int i, int j, float x) { Hw[i * d + j] = x; });
+        // the products of the composed map with this chunk's M
+        const float* lhs[6] = {P11, P11, P21, P21, Q1, Q1};
+        const float* rhs[6] = {Gc, Gw, Gc, Gw, Gc, Gw};
+        for (int m = 0; m < 6; ++m) {
+            float* Tm = z + ll.T[m];
+            block_gemm(d, d, d, MatA{lhs[m], d, 1, nullptr}, MatB{rhs[m], d, 1}, lds_gemm,
+                       [&](int i, int j, float x) { Tm[i * d + j] = x; });
+        }
+        const float an = s_tail[0], bn = s_tail[1], pn = s_tail[2];
+        const float *Ta = z + ll.T[0], *Tb = z + ll.T[1], *Tc = z + ll.T[2], *Td = z + ll.T[3],
+                    *Te = z + ll.T[4], *Tf = z + ll.T[5];
+        for (int64_t e = tid; e < dd; e += kThreads) {  // (P, Q) <- (P M, Q M + N)
+            const float p11 = P11[e], p12 = P12[e], p21 = P21[e], p22 = P22[e];
+            const float q1 = Q1[e], q2 = Q2[e];
+            P11[e] = an * p11 - 2.0f * Ta[e] - bn * p12;
+            P12[e] = 2.0f * Tb[e] + pn * p12;
+            P21[e] = an * p21 - 2.0f * Tc[e] - bn * p22;
+            P22[e] = 2.0f * Td[e] + pn * p22;
+            Q1[e] = an * q1 - 2.0f * Te[e] - bn * q2 + 2.0f * Hc[e];
+            Q2[e] = 2.0f * Tf[e] + pn * q2 - 2.0f * Hw[e];
+        }
+        __syncthreads();
+    }
+}
+
+// X_0 = [theta0 | s0]; X_{g+1} = X_g P_g + Q_g = [W P11 + S P21 + Q1, W P12 + S P22 + Q2]
+__global__ void __launch_bounds__(kThreads) linear_combine_kernel(ScanArgs a, Groups grp,
+                                                                   LinLayout ll, const float* sums) {
+    __shared__ float lds_gemm[kGemmLds];
+    const int64_t seq = blockIdx.x;
+    const int64_t b = seq / a.H, h = seq % a.H;
+    const int tid = threadIdx.x, d = a.n[0];
+    const int64_t P = a.P;
+    const float* th0 = a.theta0 + b * a.s0s[0] + h * a.s0s[1];
+    const float* mo0 = a.s0 + b * a.s0s[0] + h * a.s0s[1];
+    float* x0 = grp.states + seq * grp.G * 2 * P;
+    for (int64_t i = tid; i < P; i += kThreads) {
+        x0[i] = th0[i];
+        x0[P + i] = mo0[i];
+    }
+    __syncthreads();
+    for (int g = 0; g + 1 < grp.G; ++g) {
+        const float* W = x0 + (int64_t)g * 2 * P;
+        const float* S = W + P;
+        float* Wn = x0 + (int64_t)(g + 1) * 2 * P;
+        float* Sn = Wn + P;
+        const float* z = sums + (seq * grp.G + g) * ll.per_group;
+        const float *P11 = z + ll.P11, *P12 = z + ll.P12, *P21 = z + ll.P21, *P22 = z + ll.P22;
+        const float *Q1 = z + ll.Q1, *Q2 = z + ll.Q2;
+        block_gemm(d, d, d, MatA{W, d, 1, nullptr}, MatB{P11, d, 1}, lds_gemm,
+                   [&](int i, int j, float x) { Wn[i * d + j] = x + Q1[i * d + j]; });
+        block_gemm(d, d, d, MatA{S, d, 1, nullptr}, MatB{P21, d, 1}, lds_gemm,
+                   [&](int i, int j, float x) { Wn[i * d + j] += x; });
+        block_gemm(d, d, d, MatA{W, d, 1, nullptr}, MatB{P12, d, 1}, lds_gemm,
+                   [&](int i, int j, float x) { Sn[i * d + j] = x + Q2[i * d + j]; });
+        block_gemm(d, d, d, MatA{S, d, 1, nullptr}, MatB{P22, d, 1}, lds_gemm,
+                   [&](int i, int j, float x) { Sn[i * d + j] += x; });
+    }
+}
+
+// Groups per memory for the linear path: about 512 workgroups over the GPU, at least 8
+// chunks per group; 0 if that leaves fewer than two groups.
+int64_t linear_groups(const ScanArgs& a, int64_t& span) {
+    const int64_t nseq = a.B * a.H;
+    const int64_t nch = (a.T + a.C - 1) / a.C;
+    if (nseq == 0 || nch < 2) return 0;
+    int64_t G = 512 / nseq;
+    if (G > nch / 8) G = nch / 8;
+    if (G < 2) return 0;
+    const int64_t per = (nch + G - 1) / G;  // chunks per group
+    G = (nch + per - 1) / per;              // every group non-empty
+    span = per * a.C;
+    return G;
+}
+
 }  // namespace
+
+bool scan_linear_supported(const ScanArgs& a) {
+    int64_t span = 0;
+    return a.L == 1 && a.bias == TITANS_BIAS_L2 && linear_groups(a, span) >= 2;
+}
+
+size_t scan_linear_workspace_bytes(const ScanArgs& a) {
+    int64_t span = 0;
+    const int64_t G = linear_groups(a, span);
+    const int64_t nseq = a.B * a.H;
+    const WsLayout w = ws_layout(a.C, a.L, a.n);
+    const LinLayout ll = lin_layout(a.C, a.n[0]);
+    const int64_t floats = nseq * G * (w.per_seq + ll.per_group + 2 * a.P);
+    return (size_t)floats * sizeof(float);
+}
+
+hipError_t launch_scan_linear(const ScanArgs& a, hipStream_t stream) {
+    int64_t span = 0;
+    const int64_t G = linear_groups(a, span);
+    const int64_t nseq = a.B * a.H;
+    if (G < 2) return hipErrorInvalidValue;  // the caller checked scan_linear_supported
+    const WsLayout wl = ws_layout(a.C, a.L, a.n);
+    const LinLayout ll = lin_layout(a.C, a.n[0]);
+    float* base = static_cast<float*>(a.ws);
+    float* sums = base + nseq * G * wl.per_seq;
+    Groups grp{(int)G, span, sums + nseq * G * ll.per_group};
+    const unsigned nwg = (unsigned)(nseq * G);
+    linear_summary_kernel<<<dim3(nwg), kThreads, 0, stream>>>(a, grp, ll, sums);
+    linear_combine_kernel<<<dim3((unsigned)nseq), kThreads, 0, stream>>>(a, grp, ll, sums);
+    if (a.io == TITANS_BF16)
+        scan_generic_kernel<true><<<dim3(nwg), kThreads, 0, stream>>>(a, wl, grp);
+    else
+        scan_generic_kernel<false><<<dim3(nwg), kThreads, 0, stream>>>(a, wl, grp);
+    return hipGetLastError();
+}
 
 size_t scan_generic_workspace_bytes(const ScanArgs& a) {
     WsLayout w = ws_layout(a.C, a.L, a.n);
@@ -511,10 +767,11 @@ hipError_t launch_scan_generic(const ScanArgs& a, hipStream_t stream) {
         return hipGetLastError();
     }
     const WsLayout wl = ws_layout(a.C, a.L, a.n);
+    const Groups whole{0, 0, nullptr};
     if (a.io == TITANS_BF16)
-        scan_generic_kernel<true><<<dim3((unsigned)nseq), kThreads, 0, stream>>>(a, wl);
+        scan_generic_kernel<true><<<dim3((unsigned)nseq), kThreads, 0, stream>>>(a, wl, whole);
     else
-        scan_generic_kernel<false><<<dim3((unsigned)nseq), kThreads, 0, stream>>>(a, wl);
+        scan_generic_kernel<false><<<dim3((unsigned)nseq), kThreads, 0, stream>>>(a, wl, whole);
     return hipGetLastError();
 }
 

@@ -42,6 +42,13 @@ struct ScanArgs {
 size_t scan_generic_workspace_bytes(const ScanArgs& a);
 hipError_t launch_scan_generic(const ScanArgs& a, hipStream_t stream);
 
+// Linear memory (L = 1) with the squared-error bias: the chunk carries are affine maps of
+// [W | S], composed per group of chunks in parallel, chained over the groups, then every
+// group's chunks run from its start state in parallel (three launches).
+bool scan_linear_supported(const ScanArgs& a);
+size_t scan_linear_workspace_bytes(const ScanArgs& a);
+hipError_t launch_scan_linear(const ScanArgs& a, hipStream_t stream);
+
 // The generic scan as a chain of GPU-wide launches (4L - 2 per chunk), each spreading
 // one step's matrix products over 64 x 64 tiles of every memory; for wide memories.
 size_t scan_phased_workspace_bytes(const ScanArgs& a);

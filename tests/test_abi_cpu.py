@@ -295,3 +295,33 @@ def test_surprise_validation():
     assert _scan_surprise(desc, mlp, ptrs, ptrs["y"], ws, need)[0] == INVALID    # an output
     assert _scan_surprise(desc, mlp, ptrs, ws, ws, need)[0] == INVALID          # the workspace
     assert _scan_surprise(desc, mlp, ptrs, sur, ws, need - 1)[0] == WORKSPACE
+
+
+def test_linear_memory_path_selection(monkeypatch):
+    """L = 1 with the squared-error bias and enough chunks: the sequence-parallel path;
+    its workspace holds, per (memory, group), the generic kernel's area, the group's
+    composed map and its start state."""
+    lin = tm.mlp_desc((64, 64))
+    long_ = _desc(B=1, T=4096, H=2, C=16)
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(long_), ctypes.byref(lin)) == b"linear_mfma"
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(B=1, T=4096, H=2, C=16, io=0)),
+                                       ctypes.byref(lin)) == b"linear_fp32"
+    # 4 chunks: no groups of 8 -> the ordinary generic kernel
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(B=1, T=64, H=2, C=16)),
+                                       ctypes.byref(lin)) == b"generic_mfma"
+    # another bias, the surprise call, a deeper memory: not linear
+    d = _desc(B=1, T=4096, H=2, C=16)
+    d.bias, d.bias_param = 1, 0.5
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(d), ctypes.byref(lin)) == b"generic_mfma"
+    assert tm.lib.titans_mem_scan_surprise_path(ctypes.byref(long_), ctypes.byref(lin)) == b"generic_mfma"
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(long_), ctypes.byref(tm.mlp_desc((64, 64, 64)))) \
+        == b"generic_mfma"
+    # 256 chunks, 2 memories: 512 / 2 = 256 groups, capped at 256 / 8 = 32 groups of 8 chunks
+    r64 = lambda x: (x + 63) // 64 * 64
+    C, dd, P = 16, 64, 64 * 64
+    gen = r64(3 * C + 3) + r64((C + 1) * C) + r64(C * dd) + r64(C * dd) + 2 * r64(C * dd) + r64(C * C)
+    summ = 16 * r64(dd * dd) + 2 * r64(C * dd) + 2 * r64(C)
+    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(long_), ctypes.byref(lin)) == \
+        2 * 32 * (gen + summ + 2 * P) * 4
+    monkeypatch.setenv("TITANS_MEM_LINEAR", "0")
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(long_), ctypes.byref(lin)) == b"generic_mfma"

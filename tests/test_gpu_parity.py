@@ -699,3 +699,41 @@ def test_surprise_matches_oracle(case, bias, monkeypatch):
               for b in range(2) for h in range(2))
     log(f"  surprise rel err {err:.2e}")
     assert err <= Y_BAR[io]
+
+
+# ------------------------------------------------- linear memory, sequence-parallel
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("d,C,nch", [(16, 4, 40), (64, 16, 37), (128, 64, 24), (64, 256, 17)])
+def test_linear_memory_parallel_scan(d, C, nch, io, monkeypatch):
+    """L = 1: chunk carries composed per group of chunks in parallel, chained over the
+    groups, every group's chunks run from its start state; against the oracle and the
+    sequential generic kernel, ragged last chunk, in-place streaming of the state."""
+    T = C * nch - 3
+    wl, inp = _small(widths=(d, d), B=2, T=T, H=2, C=C, io=io, seed=d + C)
+    rng = np.random.default_rng(d)
+    inp.s0 = (0.05 * rng.standard_normal(inp.theta0.shape)).astype(np.float32)
+    dev = to_device(inp)
+    log(f"case linear d={d} C={C} T={T} {io}")
+    assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == ("linear_mfma" if io == "bf16" else "linear_fp32")
+    y, thT, sT = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (1, 1), (0, 1)]
+    check_pairs(wl, y, thT, sT, pairs, oracle_seq(inp, pairs))
+    # the sequential generic kernel on the same inputs
+    monkeypatch.setenv("TITANS_MEM_LINEAR", "0")
+    assert tm.scan_path(dev["q"], wl.chunk, wl.widths).startswith(("generic", "phased"))
+    y2, t2, s2 = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("TITANS_MEM_LINEAR")
+    bar = Y_BAR[io]
+    assert y_rel_err(to_f64(y), to_f64(y2)) <= bar
+    assert state_rel_err(to_f64(thT), to_f64(t2)) <= TH_BAR[io]
+    # in place: theta_T / s_T are theta0 / s0 themselves (per batch row)
+    th = dev["theta0"].expand(2, *dev["theta0"].shape).contiguous()
+    s0 = dev["s0"].expand(2, *dev["s0"].shape).contiguous()
+    tm.scan(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["eta"], dev["beta"], th, s0,
+            wl.chunk, wl.widths, theta_T=th, s_T=s0)
+    torch.cuda.synchronize()
+    assert state_rel_err(to_f64(th), to_f64(thT)) <= 1e-6
+    assert state_rel_err(to_f64(s0), to_f64(sT)) <= 1e-6
