@@ -55,12 +55,22 @@ def alg_bytes(wl):
     return th * (4 * wl.d * io + 12) + 4 * 4 * wl.params * wl.batch * wl.heads
 
 
+# the kernels of one titans_mem_scan call, by path family
+KERNELS = {
+    "fused": "scan_mfma_kernel",
+    "generic": "scan_generic_kernel",
+    "phased": "phase_kernel",
+    "linear": "linear_summary_kernel + linear_combine_kernel + scan_generic_kernel",
+}
+
+
 def kernel_source_digest(kernel):
     """sha256 of the source file that defines the kernel (traffic is void once it changes)."""
     import hashlib
 
-    src = {"scan_mfma_kernel": "scan_mfma.hip", "scan_generic_kernel": "scan_generic.hip",
-           "phase_kernel": "scan_phased.hip"}.get(kernel, "scan_pair.hip")
+    src = ("scan_pair.hip" if "scan_pair_kernel" in kernel else
+           "scan_mfma.hip" if "scan_mfma_kernel" in kernel else
+           "scan_phased.hip" if "phase_kernel" in kernel else "scan_generic.hip")
     with open(os.path.join(ROOT, "sequence_models_amd", "csrc", src), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
@@ -267,20 +277,20 @@ def main():
         kernel = ("clear_pair_flags + pair_coef_kernel + scan_pair_kernel" if path == "fused_pair"
                   else "scan_mfma_kernel")
         bound, peak, dtype = "mfma", PEAKS["mfma_bf16"], "bf16"
-    elif path in ("generic_mfma", "phased_mfma"):  # bf16 MFMA products, fp32 accumulation
-        kernel = "scan_generic_kernel" if path == "generic_mfma" else "phase_kernel"
+    elif path.endswith("_mfma"):  # bf16 MFMA products, fp32 accumulation
+        kernel = KERNELS[path.rsplit("_", 1)[0]]
         bound, peak, dtype = "mfma", PEAKS["mfma_bf16"], "bf16"
     else:  # fp32 FMAs on the vector ALUs
-        kernel = "scan_generic_kernel" if path == "generic_fp32" else "phase_kernel"
+        kernel = KERNELS[path.rsplit("_", 1)[0]]
         bound, peak, dtype = "alu", PEAKS["valu_f32"], "f32"
     parallelism = {
-        "fused_pair": "one GPU; two workgroups (one XCD) per (batch row, head) memory",
-        "phased_mfma": "one GPU; every chunk product split into 64x64 tiles of all memories, "
-                       "4L-2 launches per chunk",
-    }.get(path, "one GPU; one workgroup per (batch row, head) memory")
-    if path == "phased_fp32":
-        parallelism = "one GPU; every chunk product split into 64x64 tiles of all memories, " \
-                      "4L-2 launches per chunk"
+        "fused": "one GPU; two workgroups (one XCD) per (batch row, head) memory",
+        "phased": "one GPU; every chunk product split into 64x64 tiles of all memories, "
+                  "4L-2 launches per chunk",
+        "linear": "one GPU; each sequence split into groups of chunks whose affine state "
+                  "maps compose in parallel",
+    }.get(path.split("_")[0] if path != "fused_mfma" else "single",
+          "one GPU; one workgroup per (batch row, head) memory")
     result = {
         "metric": METRIC,
         "value": tokens / (ms_per_step * 1e-3),

@@ -80,6 +80,10 @@ WORKLOADS = {
     # long-context streaming: 16 heads x d64, batch 1, T=2^21, C=256
     "long_h16_d64_b1_t2m": Workload("long_h16_d64_b1_t2m", 1, 16, 2097152, (64, 256, 64), 256,
                                     "bf16"),
+    # derived (not one of the pages' configurations): the long-context shape with a linear
+    # memory 64->64 (the delta-rule case) at T=2^18, for the sequence-parallel linear path
+    "linear_h16_d64_b1_t256k": Workload("linear_h16_d64_b1_t256k", 1, 16, 262144, (64, 64), 256,
+                                        "bf16"),
 }
 
 HEADLINE = "h16_d64_b8_t16k"
