@@ -246,6 +246,8 @@ static Path generic_path(const titans::ScanArgs& a) {
 static Path choose_path(const titans::ScanArgs& a) {
     const char* env = getenv("TITANS_MEM_FORCE_GENERIC");
     if (env && env[0] == '1') return generic_path(a);
+    env = getenv("TITANS_MEM_GENERIC_MODE");  // a chosen member of the generic family
+    if (env && env[0]) return generic_path(a);
     env = getenv("TITANS_MEM_LINEAR");
     if (!(env && env[0] == '0') && titans::scan_linear_supported(a)) return Path::Linear;
     env = getenv("TITANS_MEM_FUSED_SINGLE");
