@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define TITANS_MEM_ABI_VERSION 2
+#define TITANS_MEM_ABI_VERSION 3
 #define TITANS_MAX_LAYERS 4
 
 typedef enum {
@@ -192,6 +192,51 @@ const char* titans_mem_scan_surprise_path(const titans_scan_desc* desc, const ti
 /* Workspace bytes titans_mem_scan_surprise needs (SIZE_MAX if the arguments are invalid). */
 size_t titans_mem_scan_surprise_workspace_size(const titans_scan_desc* desc,
                                                const titans_mlp_desc* mlp);
+
+/* Workspace bytes titans_mem_scan_backward needs (0 if B*H = 0 or T = 0; SIZE_MAX if the
+ * arguments are invalid or unsupported): per memory, one (theta, s) checkpoint per chunk
+ * (2 P floats each) plus the chunk's intermediates. */
+size_t titans_mem_scan_backward_workspace_size(const titans_scan_desc* desc,
+                                               const titans_mlp_desc* mlp);
+
+/*
+ * Reverse-mode derivatives of titans_mem_scan: the outer loop of the two-level
+ * optimization, through which the projections and gates that produce q, k, v, alpha, eta
+ * and beta are trained (Titans explainer, the memory module and its training; lowest.today
+ * summary, "Addestramento Parallelizzato").  For output cotangents dy, dtheta_T, ds_T of
+ * the scan with the same desc / mlp / inputs, writes the cotangent of every input:
+ * dX = d<dy, y> + <dtheta_T, theta_T> + <ds_T, s_T> / dX.  The chunking and the gradients at
+ * the chunk-start weights are differentiated as they are (the chunk-start weights are not
+ * held constant: the second derivatives of the loss enter through them).
+ *
+ *   q, k, v, alpha, eta, beta, theta0, s0   the scan's inputs, as for titans_mem_scan
+ *   dy          device, io_dtype, desc->y_stride (the layout of y)
+ *   dtheta_T, ds_T  device fp32, desc->state_stride; NULL means zero
+ *   dq, dk, dv  device, io_dtype, desc->qkv_stride (the layout of q, k, v); written
+ *   dalpha, deta, dbeta  device fp32, desc->gate_stride; written
+ *   dtheta0, ds0  device fp32, desc->state_stride (not state0_stride: when theta0 / s0 are
+ *               shared over the batch, b-stride 0, the caller sums these over b); written.
+ *               dtheta0 may be exactly dtheta_T and ds0 exactly ds_T (in place)
+ *   workspace   device, >= titans_mem_scan_backward_workspace_size bytes, 256-byte aligned
+ *
+ * No output may overlap another output, an input or the workspace (apart from the two
+ * in-place pairs); TITANS_ERR_INVALID_ARGUMENT otherwise.  The call runs one forward sweep
+ * that checkpoints every chunk's start state, then the chunks in reverse order, recomputing
+ * each chunk's reads and key path; products and state in fp32 for both io dtypes.  The
+ * attentional bias is differentiated twice: TITANS_BIAS_LP needs p >= 2
+ * (TITANS_ERR_UNSUPPORTED otherwise); at |r| = delta the Huber loss takes the inner branch's
+ * second derivative.  Shape limits as for titans_mem_scan.  T = 0 copies dtheta_T -> dtheta0
+ * and ds_T -> ds0 (zero if NULL).
+ */
+titans_status titans_mem_scan_backward(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
+                                       const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* eta, const float* beta,
+                                       const float* theta0, const float* s0,
+                                       const void* dy, const float* dtheta_T, const float* ds_T,
+                                       void* dq, void* dk, void* dv,
+                                       float* dalpha, float* deta, float* dbeta,
+                                       float* dtheta0, float* ds0,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Which kernel titans_mem_retrieve runs for this problem: "fused_mfma" (bf16 MFMA, both
  * weight matrices in LDS; the 64 -> 256 -> 64 memory with bf16 q / y), "wide_mfma" (bf16

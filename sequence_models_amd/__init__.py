@@ -6,6 +6,8 @@ stream; nothing here computes.  If the library is not built this module raises
 at import time -- there is no fallback.
 
     scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths) -> (y, theta_T, s_T)
+    scan_backward(q, k, v, alpha, eta, beta, theta0, s0, dy, chunk, widths,
+                  dtheta_T=None, ds_T=None) -> cotangents of every input
     retrieve(q, theta, widths) -> y
 """
 from __future__ import annotations
@@ -15,7 +17,7 @@ import os
 
 import torch
 
-__all__ = ["scan", "retrieve", "scan_workspace_size", "scan_path", "retrieve_path", "param_count", "TitansError", "LIB_PATH",
+__all__ = ["scan", "scan_backward", "scan_backward_workspace_size", "retrieve", "scan_workspace_size", "scan_path", "retrieve_path", "param_count", "TitansError", "LIB_PATH",
            "lib", "ScanDesc", "MlpDesc", "MAX_LAYERS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtitans_mem.so")
@@ -67,6 +69,12 @@ lib.titans_mem_scan_surprise_path.argtypes = [ctypes.POINTER(ScanDesc), ctypes.P
 lib.titans_mem_scan_surprise_workspace_size.restype = ctypes.c_size_t
 lib.titans_mem_scan_surprise_workspace_size.argtypes = [ctypes.POINTER(ScanDesc),
                                                         ctypes.POINTER(MlpDesc)]
+lib.titans_mem_scan_backward_workspace_size.restype = ctypes.c_size_t
+lib.titans_mem_scan_backward_workspace_size.argtypes = [ctypes.POINTER(ScanDesc),
+                                                        ctypes.POINTER(MlpDesc)]
+lib.titans_mem_scan_backward.restype = ctypes.c_int
+lib.titans_mem_scan_backward.argtypes = ([ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)]
+                                         + [_vp] * 20 + [ctypes.c_size_t, _vp])
 lib.titans_mem_retrieve.restype = ctypes.c_int
 lib.titans_mem_retrieve.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc), _vp, _vp,
                                     _vp, _vp]
@@ -217,9 +225,7 @@ def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, *, y=None, theta_
     if s_T.stride() != theta_T.stride() or s_T.shape != theta_T.shape:
         raise ValueError("s_T must have theta_T's shape and strides")
     desc = make_desc(q, chunk, y, alpha, theta_T, theta0)
-    if bias is not None:
-        desc.bias = BIASES[bias[0]]
-        desc.bias_param = float(bias[1]) if len(bias) > 1 else 0.0
+    _set_bias(desc, bias)
     mlp = mlp_desc(widths)
     if surprise is True:
         surprise = torch.empty_like(alpha)
@@ -245,6 +251,91 @@ def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, *, y=None, theta_
                                _ptr(alpha), _ptr(eta), _ptr(beta), _ptr(theta0), _ptr(s0), _ptr(y),
                                _ptr(theta_T), _ptr(s_T), _ptr(workspace), ws_bytes, _stream()))
     return y, theta_T, s_T
+
+
+def _set_bias(desc, bias):
+    if bias is not None:
+        desc.bias = BIASES[bias[0]]
+        desc.bias_param = float(bias[1]) if len(bias) > 1 else 0.0
+
+
+def scan_backward_workspace_size(q, chunk, widths, bias=None) -> int:
+    """Workspace bytes titans_mem_scan_backward needs for q's shape."""
+    d = make_desc(q, chunk, q, None, None, None)
+    _set_bias(d, bias)
+    n = lib.titans_mem_scan_backward_workspace_size(ctypes.byref(d), ctypes.byref(mlp_desc(widths)))
+    if n == ctypes.c_size_t(-1).value:
+        raise TitansError(1, "invalid or unsupported shape, MLP widths or bias")
+    return int(n)
+
+
+BACKWARD_NAMES = ("q", "k", "v", "alpha", "eta", "beta", "theta0", "s0")
+
+
+def scan_backward(q, k, v, alpha, eta, beta, theta0, s0, dy, chunk, widths, *, dtheta_T=None,
+                  ds_T=None, bias=None, workspace=None, out=None):
+    """Cotangents of the scan's inputs (titans_mem_scan_backward) on the current stream.
+
+    Arguments as for scan, plus dy (y's shape, q's dtype) and dtheta_T / ds_T ([B,H,P]
+    float32 or None = zero).  Returns a dict keyed by BACKWARD_NAMES: dq/dk/dv with q's
+    shape, strides and dtype, gate cotangents with alpha's, state cotangents [B,H,P] (with
+    dtheta_T's strides when given; the caller sums over b when theta0 is shared by the
+    batch).  out may supply any of these tensors; passing dtheta_T / ds_T themselves as
+    out["theta0"] / out["s0"] runs in place.
+    """
+    B, T, H, dd = q.shape
+    P = param_count(widths)
+    out = dict(out or {})
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.stride() != q.stride() or t.dtype != q.dtype:
+            raise ValueError(f"{name} must have q's shape, strides and dtype")
+    if dy.shape != q.shape or dy.dtype != q.dtype:
+        raise ValueError("dy must have q's shape and dtype")
+    for name, g in (("eta", eta), ("beta", beta)):
+        if g.shape != alpha.shape or g.stride() != alpha.stride():
+            raise ValueError(f"{name} must have alpha's shape and strides")
+    state_like = dtheta_T if dtheta_T is not None else ds_T
+    for name in ("q", "k", "v"):
+        out.setdefault(name, torch.empty_strided(q.shape, q.stride(), dtype=q.dtype,
+                                                 device=q.device))
+    for name in ("alpha", "eta", "beta"):
+        out.setdefault(name, torch.empty_strided(alpha.shape, alpha.stride(),
+                                                 dtype=torch.float32, device=q.device))
+    for name in ("theta0", "s0"):
+        if state_like is not None:
+            out.setdefault(name, torch.empty_strided(state_like.shape, state_like.stride(),
+                                                     dtype=torch.float32, device=q.device))
+        else:
+            out.setdefault(name, torch.empty((B, H, P), dtype=torch.float32, device=q.device))
+    for name in ("dtheta_T", "ds_T"):
+        t = dtheta_T if name == "dtheta_T" else ds_T
+        if t is not None and (t.stride() != out["theta0"].stride() or t.dtype != torch.float32
+                              or tuple(t.shape) != (B, H, P)):
+            raise ValueError(f"{name} must be float32 [B,H,P] with the strides of dtheta0")
+    for name in ("q", "k", "v"):
+        if out[name].stride() != q.stride() or out[name].dtype != q.dtype:
+            raise ValueError(f"d{name} must have q's strides and dtype")
+    for name in ("alpha", "eta", "beta"):
+        if out[name].stride() != alpha.stride() or out[name].dtype != torch.float32:
+            raise ValueError(f"d{name} must be float32 with alpha's strides")
+    if out["s0"].stride() != out["theta0"].stride():
+        raise ValueError("ds0 must have dtheta0's strides")
+    desc = make_desc(q, chunk, dy, alpha, out["theta0"], theta0)
+    _set_bias(desc, bias)
+    mlp = mlp_desc(widths)
+    if workspace is None:
+        n = lib.titans_mem_scan_backward_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+        if n == ctypes.c_size_t(-1).value:
+            n = 0  # the call below reports the argument error
+        workspace = torch.empty(int(n), dtype=torch.uint8, device=q.device) if n else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.titans_mem_scan_backward(
+        ctypes.byref(desc), ctypes.byref(mlp), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta),
+        _ptr(beta), _ptr(theta0), _ptr(s0), _ptr(dy), _ptr(dtheta_T), _ptr(ds_T),
+        _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["alpha"]), _ptr(out["eta"]),
+        _ptr(out["beta"]), _ptr(out["theta0"]), _ptr(out["s0"]), _ptr(workspace), ws_bytes,
+        _stream()))
+    return out
 
 
 def retrieve_path(q, widths) -> str:

@@ -25,6 +25,7 @@ SOURCES = {
     "abi.hip": [],
     "scan_generic.hip": [],
     "scan_phased.hip": [],
+    "scan_backward.hip": [],
     "scan_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "scan_pair.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "retrieve_mfma.hip": [],

@@ -449,6 +449,159 @@ titans_status titans_mem_scan_surprise(const titans_scan_desc* desc, const titan
                      true, workspace, workspace_bytes, stream);
 }
 
+// ---------------------------------------------------------------- reverse pass
+
+static titans_status prepare_backward(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
+                                      titans::ScanArgs& a) {
+    titans_status st = prepare_scan(desc, mlp, a);
+    if (st) return st;
+    if (a.bias == TITANS_BIAS_LP && a.bias_param < 2.f)
+        return fail(TITANS_ERR_UNSUPPORTED,
+                    "the reverse pass needs the l_p loss twice differentiable (p=%g < 2)",
+                    (double)a.bias_param);
+    return TITANS_OK;
+}
+
+size_t titans_mem_scan_backward_workspace_size(const titans_scan_desc* desc,
+                                               const titans_mlp_desc* mlp) {
+    titans::ScanArgs a{};
+    if (prepare_backward(desc, mlp, a) != TITANS_OK) return SIZE_MAX;
+    if (a.B * a.H == 0 || a.T == 0) return 0;
+    return titans::scan_backward_workspace_bytes(a);
+}
+
+titans_status titans_mem_scan_backward(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
+                                       const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* eta, const float* beta,
+                                       const float* theta0, const float* s0, const void* dy,
+                                       const float* dtheta_T, const float* ds_T, void* dq,
+                                       void* dk, void* dv, float* dalpha, float* deta,
+                                       float* dbeta, float* dtheta0, float* ds0,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    titans::ScanArgs a{};
+    titans_status st = prepare_backward(desc, mlp, a);
+    if (st) return st;
+    const int64_t nseq = a.B * a.H;
+    const bool have_tokens = nseq > 0 && a.T > 0;
+    if (nseq > 0) {
+        if (!theta0 || !s0 || !dtheta0 || !ds0)
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "theta0, s0, dtheta0 and ds0 must be non-NULL");
+        if ((st = check_state_alignment(theta0, a.s0s, "theta0"))) return st;
+        if ((st = check_state_alignment(s0, a.s0s, "s0"))) return st;
+        if ((st = check_state_alignment(dtheta0, a.ss, "dtheta0"))) return st;
+        if ((st = check_state_alignment(ds0, a.ss, "ds0"))) return st;
+        if (dtheta_T && (st = check_state_alignment(dtheta_T, a.ss, "dtheta_T"))) return st;
+        if (ds_T && (st = check_state_alignment(ds_T, a.ss, "ds_T"))) return st;
+    }
+    if (have_tokens) {
+        if (!q || !k || !v || !alpha || !eta || !beta || !dy || !dq || !dk || !dv || !dalpha ||
+            !deta || !dbeta)
+            return fail(TITANS_ERR_INVALID_ARGUMENT,
+                        "q, k, v, the gates, dy and every token cotangent must be non-NULL");
+        const void* io_ptrs[6] = {q, k, v, dq, dk, dv};
+        const char* io_names[6] = {"q", "k", "v", "dq", "dk", "dv"};
+        for (int i = 0; i < 6; ++i)
+            if ((st = check_io_alignment(a, io_ptrs[i], a.qs, io_names[i]))) return st;
+        if ((st = check_io_alignment(a, dy, a.ys, "dy"))) return st;
+        const float* g_ptrs[3] = {dalpha, deta, dbeta};
+        for (int i = 0; i < 3; ++i)
+            if ((reinterpret_cast<uintptr_t>(g_ptrs[i]) & 3u) != 0)
+                return fail(TITANS_ERR_INVALID_ARGUMENT, "gate cotangents must be 4-byte aligned");
+    }
+    // ---- aliasing: outputs distinct from each other, from every input and the workspace;
+    // dtheta0 may be exactly dtheta_T and ds0 exactly ds_T (in place)
+    const size_t esz = a.io == TITANS_BF16 ? 2 : 4;
+    const int64_t io_sz[4] = {a.B, a.T, a.H, a.n[0]};
+    const int64_t qst[4] = {a.qs[0], a.qs[1], a.qs[2], 1};
+    const int64_t yst[4] = {a.ys[0], a.ys[1], a.ys[2], 1};
+    const int64_t g_sz[3] = {a.B, a.T, a.H};
+    const int64_t st_sz[3] = {a.B, a.H, a.P};
+    const int64_t sst[3] = {a.ss[0], a.ss[1], 1};
+    const int64_t s0st[3] = {a.s0s[0], a.s0s[1], 1};
+    if (have_tokens && !non_self_overlapping(io_sz, qst, 4))
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "q/k/v strides make distinct dq/dk/dv elements alias");
+    if (have_tokens && !non_self_overlapping(g_sz, a.gs, 3))
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "gate strides make distinct gate cotangents alias");
+    if (!non_self_overlapping(st_sz, sst, 3))
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "state strides make distinct dtheta0/ds0 elements alias");
+    Span outs[8], ins[10];
+    int nout = 0, nin = 0;
+    if (have_tokens) {
+        outs[nout++] = span_of(dq, io_sz, qst, 4, esz);
+        outs[nout++] = span_of(dk, io_sz, qst, 4, esz);
+        outs[nout++] = span_of(dv, io_sz, qst, 4, esz);
+        outs[nout++] = span_of(dalpha, g_sz, a.gs, 3, 4);
+        outs[nout++] = span_of(deta, g_sz, a.gs, 3, 4);
+        outs[nout++] = span_of(dbeta, g_sz, a.gs, 3, 4);
+        ins[nin++] = span_of(q, io_sz, qst, 4, esz);
+        ins[nin++] = span_of(k, io_sz, qst, 4, esz);
+        ins[nin++] = span_of(v, io_sz, qst, 4, esz);
+        ins[nin++] = span_of(alpha, g_sz, a.gs, 3, 4);
+        ins[nin++] = span_of(eta, g_sz, a.gs, 3, 4);
+        ins[nin++] = span_of(beta, g_sz, a.gs, 3, 4);
+        ins[nin++] = span_of(dy, io_sz, yst, 4, esz);
+    }
+    const Span sdth = span_of(dtheta0, st_sz, sst, 3, 4), sds = span_of(ds0, st_sz, sst, 3, 4);
+    const Span sdT = dtheta_T ? span_of(dtheta_T, st_sz, sst, 3, 4) : Span{};
+    const Span ssT = ds_T ? span_of(ds_T, st_sz, sst, 3, 4) : Span{};
+    outs[nout++] = sdth;
+    outs[nout++] = sds;
+    ins[nin++] = span_of(theta0, st_sz, s0st, 3, 4);
+    ins[nin++] = span_of(s0, st_sz, s0st, 3, 4);
+    for (int i = 0; i < nout; ++i) {
+        for (int j = i + 1; j < nout; ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(TITANS_ERR_INVALID_ARGUMENT, "two cotangent outputs overlap");
+        for (int j = 0; j < nin; ++j)
+            if (overlaps(outs[i], ins[j]))
+                return fail(TITANS_ERR_INVALID_ARGUMENT, "a cotangent output overlaps an input");
+    }
+    const bool th_inplace = dtheta_T == dtheta0;
+    const bool s_inplace = ds_T == ds0;
+    for (int i = 0; i < nout; ++i) {
+        const bool is_dth = i == nout - 2, is_ds = i == nout - 1;
+        if (overlaps(outs[i], sdT) && !(is_dth && th_inplace))
+            return fail(TITANS_ERR_INVALID_ARGUMENT,
+                        "dtheta_T overlaps an output without being exactly dtheta0");
+        if (overlaps(outs[i], ssT) && !(is_ds && s_inplace))
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "ds_T overlaps an output without being exactly ds0");
+    }
+    const size_t need = have_tokens ? titans::scan_backward_workspace_bytes(a) : 0;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(TITANS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+        const Span sw{reinterpret_cast<uintptr_t>(workspace),
+                      reinterpret_cast<uintptr_t>(workspace) + need};
+        for (int i = 0; i < nout; ++i)
+            if (overlaps(sw, outs[i])) return fail(TITANS_ERR_INVALID_ARGUMENT, "workspace overlaps an output");
+        for (int i = 0; i < nin; ++i)
+            if (overlaps(sw, ins[i])) return fail(TITANS_ERR_INVALID_ARGUMENT, "workspace overlaps an input");
+        if (overlaps(sw, sdT) || overlaps(sw, ssT))
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "workspace overlaps dtheta_T or ds_T");
+    }
+    if (nseq == 0) return TITANS_OK;
+    titans::BwdArgs b{};
+    a.q = q; a.k = k; a.v = v;
+    a.alpha = alpha; a.eta = eta; a.beta = beta;
+    a.theta0 = theta0; a.s0 = s0;
+    a.ws = workspace;
+    b.a = a;
+    b.dy = dy;
+    b.dthetaT = dtheta_T;
+    b.dsT = ds_T;
+    b.dq = dq; b.dk = dk; b.dv = dv;
+    b.dalpha = dalpha; b.deta = deta; b.dbeta = dbeta;
+    b.dtheta0 = dtheta0;
+    b.ds0 = ds0;
+    const hipError_t e = titans::launch_scan_backward(b, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return TITANS_OK;
+}
+
 static titans_status prepare_retrieve(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
                                       titans::ScanArgs& a) {
     titans_status st = check_desc_common(desc, a);

@@ -24,4 +24,18 @@ __device__ __forceinline__ float bias_grad(float r, int kind, float prm) {
     return 2.0f * r;
 }
 
+// The second derivative of the per-component loss (the reverse pass differentiates the
+// output-layer error once more): 2; 2 inside [-delta, delta] and 0 outside (Huber);
+// p (p - 1) |r|^(p-2) (l_p, p >= 2; 0 at r = 0 for p > 2).
+__device__ __forceinline__ float bias_grad_prime(float r, int kind, float prm) {
+    if (kind == TITANS_BIAS_HUBER) return fabsf(r) <= prm ? 2.0f : 0.0f;
+    if (kind == TITANS_BIAS_LP) {
+        if (prm == 2.0f) return 2.0f;
+        if (r == 0.0f) return 0.0f;
+        return prm * (prm - 1.0f) *
+               __builtin_amdgcn_exp2f((prm - 2.0f) * __builtin_amdgcn_logf(fabsf(r)));
+    }
+    return 2.0f;
+}
+
 }  // namespace titans

@@ -1,0 +1,639 @@
+// Reverse-mode derivatives of the chunked Titans memory scan (the outer loop of the
+// two-level optimization: the projections and gates that make q, k, v, alpha, eta, beta
+// are trained through the memory's test-time writes; Titans explainer, sections on the
+// memory module and its training, and the lowest.today summary, "Addestramento
+// Parallelizzato").  Any supported shape, fp32 products, one 256-thread workgroup per
+// (b, h) memory.
+//
+// Forward (per chunk, start weights W_l, momentum S_l, tokens t = 0..n-1):
+//   theta_t = a_t theta_c - b_t s_c - sum_{j<t} c_{t,j} g_j        (read y_t at theta_t)
+//   theta_e = a_n theta_c - b_n s_c - sum_j c_{n,j} g_j,   s_e = p_n s_c + sum_j w_{n,j} g_j
+// g_j = grad of the loss at theta_c for (k_j, v_j), layer l part Delta_l[j] Hk_{l-1}[j]^T.
+// The coefficients follow the token recurrence p_{t+1} = beta_t p_t,
+// w_{t+1,j} = beta_t w_{t,j} + (1 - beta_t)[j = t], a_{t+1} = (1 - alpha_t) a_t,
+// b_{t+1} = (1 - alpha_t) b_t + eta_t p_{t+1}, c_{t+1,j} = (1 - alpha_t) c_{t,j} + eta_t w_{t+1,j}.
+//
+// Sweep 1 runs the chunk carries forward and stores every chunk's (theta_c, s_c).  Sweep 2
+// walks the chunks backwards with the running state cotangents (Lt, Ls) = (dtheta_e,
+// ds_e), kept in the dtheta0 / ds0 outputs.  Per chunk, with rows = tokens:
+//   recompute  key path Hk_l, Zk_l, Delta_l, Gk_l = Delta_{l+1} W_{l+1}; query path Hq_l,
+//              Zq_l at the in-chunk weights; A_l = Hq_{l-1} Hk_{l-1}^T, Mq_l = Cm o A_l
+//   query adjoint  Dq_L = dY;  Bq_l = Dq_l Delta_l^T, Mb_l = Cm o Bq_l,
+//              dHq_{l-1} = diag(a) Dq_l W_l - diag(b) Dq_l S_l - Mb_l Hk_{l-1},
+//              Dq_{l-1} = dHq_{l-1} o SiLU'(Zq_{l-1}), dq = dHq_0;
+//              coefficient cotangents da_t += <Dq_l W_l, Hq_{l-1}>_row, db_t -= <Dq_l S_l,
+//              Hq_{l-1}>_row, dc_{t,j} -= Bq_l[t,j] A_l[t,j]
+//   chunk end  da_n = <Lt, theta_c>, db_n = -<Lt, s_c>, dp_n = <Ls, s_c>,
+//              dc_{n,j} = -<Delta_l, Hk_{l-1} Lt_l^T>_row, dw_{n,j} = <Delta_l, Hk_{l-1} Ls_l^T>_row
+//   second order  the cotangent U_j of g_j is -c_{n,j} Lt + w_{n,j} Ls - sum_{t>j} c_{t,j}
+//              (Dq Hq^T)_t; pushing it back through g_j = grad loss(theta_c; k_j, v_j) is a
+//              Hessian-vector product (Pearlmutter's R-operator): a tangent pass of the key
+//              path along U_j (RZ_l = RH_{l-1} W_l^T + U_l Hk_{l-1} with
+//              U_l Hk_{l-1} = -diag(c_n) Hk Lt^T + diag(w_n) Hk Ls^T - Mq_l^T Dq_l), then a
+//              tangent pass of its backward (RDelta_L = loss''(r) RZ_L,
+//              RG_l = RDelta_l W_l - diag(c_n) Delta_l Lt_l + diag(w_n) Delta_l Ls_l
+//              - Mb_l^T Hq_{l-1}, RDelta_{l-1} = RG_l o SiLU'(Zk_{l-1})
+//              + Gk_{l-1} o SiLU''(Zk_{l-1}) o RZ_{l-1}); dk = RG_1, dv = -loss''(r) RZ_L
+//   carry      Ls_l <- p_n Ls_l - b_n Lt_l - Dq_l^T diag(b) Hq_{l-1}
+//              Lt_l <- a_n Lt_l + Dq_l^T diag(a) Hq_{l-1} + RDelta_l^T Hk_{l-1} + Delta_l^T RH_{l-1}
+//   gates      the coefficient recurrence run backwards: column recurrences for the
+//              cotangents of c and w (one thread per column), one thread for those of a,
+//              b, p, then per token the gate cotangents as row sums.
+#include <hip/hip_runtime.h>
+
+#include "generic_gemm.h"
+#include "generic_util.h"
+#include "titans_internal.h"
+
+namespace titans {
+namespace {
+
+using namespace generic;
+
+constexpr int kThreads = 256;
+
+// Float offsets of the per-memory workspace regions of the reverse sweep.
+struct BwLayout {
+    int64_t ca, cb, cp;                 // a_t, b_t, p_t for t = 0..C
+    int64_t cm, wm;                     // c_{t,j}, w_{t,j}: (C + 1) x C
+    int64_t gc, gw;                     // their cotangents: (C + 1) x C
+    int64_t hk[TITANS_MAX_LAYERS];      // l = 0..L-1: C x n_l (Hk_0 = K)
+    int64_t zk[TITANS_MAX_LAYERS];      // l = 1..L-1
+    int64_t gk[TITANS_MAX_LAYERS];      // l = 1..L-1: Delta_{l+1} W_{l+1}
+    int64_t dl[TITANS_MAX_LAYERS + 1];  // l = 1..L
+    int64_t rr;                         // C x d: M(k) - v
+    int64_t hq[TITANS_MAX_LAYERS];      // l = 0..L-1 (Hq_0 = Q)
+    int64_t zq[TITANS_MAX_LAYERS];      // l = 1..L-1
+    int64_t dq[TITANS_MAX_LAYERS + 1];  // l = 1..L (Dq_L = dY)
+    int64_t rz[TITANS_MAX_LAYERS + 1];  // l = 1..L
+    int64_t rh[TITANS_MAX_LAYERS];      // l = 1..L-1
+    int64_t rd[TITANS_MAX_LAYERS + 1];  // l = 1..L
+    int64_t am[TITANS_MAX_LAYERS + 1];  // l = 1..L: C x C
+    int64_t mq[TITANS_MAX_LAYERS + 1];
+    int64_t mb[TITANS_MAX_LAYERS + 1];
+    int64_t tmp;                        // C x max width
+    int64_t per_seq;
+};
+
+__host__ __device__ inline BwLayout bw_layout(int C, int L, const int* n) {
+    auto r64 = [](int64_t x) { return (x + 63) & ~int64_t(63); };
+    BwLayout w{};
+    int maxw = 0;
+    for (int l = 0; l <= L; ++l) maxw = n[l] > maxw ? n[l] : maxw;
+    const int64_t cc = r64((int64_t)(C + 1) * C), c1 = r64(C + 1);
+    int64_t o = 0;
+    w.ca = o; o += c1;
+    w.cb = o; o += c1;
+    w.cp = o; o += c1;
+    w.cm = o; o += cc;
+    w.wm = o; o += cc;
+    w.gc = o; o += cc;
+    w.gw = o; o += cc;
+    for (int l = 0; l < L; ++l) { w.hk[l] = o; o += r64((int64_t)C * n[l]); }
+    for (int l = 1; l < L; ++l) { w.zk[l] = o; o += r64((int64_t)C * n[l]); }
+    for (int l = 1; l < L; ++l) { w.gk[l] = o; o += r64((int64_t)C * n[l]); }
+    for (int l = 1; l <= L; ++l) { w.dl[l] = o; o += r64((int64_t)C * n[l]); }
+    w.rr = o; o += r64((int64_t)C * n[L]);
+    for (int l = 0; l < L; ++l) { w.hq[l] = o; o += r64((int64_t)C * n[l]); }
+    for (int l = 1; l < L; ++l) { w.zq[l] = o; o += r64((int64_t)C * n[l]); }
+    for (int l = 1; l <= L; ++l) { w.dq[l] = o; o += r64((int64_t)C * n[l]); }
+    for (int l = 1; l <= L; ++l) { w.rz[l] = o; o += r64((int64_t)C * n[l]); }
+    for (int l = 1; l < L; ++l) { w.rh[l] = o; o += r64((int64_t)C * n[l]); }
+    for (int l = 1; l <= L; ++l) { w.rd[l] = o; o += r64((int64_t)C * n[l]); }
+    for (int l = 1; l <= L; ++l) { w.am[l] = o; o += r64((int64_t)C * C); }
+    for (int l = 1; l <= L; ++l) { w.mq[l] = o; o += r64((int64_t)C * C); }
+    for (int l = 1; l <= L; ++l) { w.mb[l] = o; o += r64((int64_t)C * C); }
+    w.tmp = o; o += r64((int64_t)C * maxw);
+    w.per_seq = o;
+    return w;
+}
+
+__device__ __forceinline__ float silu_prime(float z) {
+    const float s = sigmoidf_(z);
+    return s * (1.0f + z * (1.0f - s));
+}
+
+__device__ __forceinline__ float silu_second(float z) {
+    const float s = sigmoidf_(z);
+    return s * (1.0f - s) * (2.0f + z * (1.0f - 2.0f * s));
+}
+
+// Per-memory bases of every strided buffer.
+struct Bases {
+    int64_t b, h, q, y, g;
+};
+
+__device__ __forceinline__ Bases bases_of(const ScanArgs& a, int64_t seq) {
+    Bases r;
+    r.b = seq / a.H;
+    r.h = seq % a.H;
+    r.q = r.b * a.qs[0] + r.h * a.qs[2];
+    r.y = r.b * a.ys[0] + r.h * a.ys[2];
+    r.g = r.b * a.gs[0] + r.h * a.gs[2];
+    return r;
+}
+
+// The chunk's gates into LDS and K into Hk_0.
+__device__ __forceinline__ void stage_keys(const ScanArgs& a, const BwLayout& wl, float* ws,
+                                           const Bases& bs, int64_t c0, int n, float* s_al,
+                                           float* s_et, float* s_be) {
+    const int d = a.n[0];
+    for (int t = threadIdx.x; t < n; t += kThreads) {
+        const int64_t gi = bs.g + (c0 + t) * a.gs[1];
+        s_al[t] = a.alpha[gi];
+        s_et[t] = a.eta[gi];
+        s_be[t] = a.beta[gi];
+    }
+    float* Hk0 = ws + wl.hk[0];
+    for (int e = threadIdx.x; e < n * d; e += kThreads) {
+        const int t = e / d, c = e % d;
+        Hk0[e] = load_io(a.k, bs.q + (c0 + t) * a.qs[1] + c, a.io);
+    }
+}
+
+// Coefficients of the chunk: thread j follows column j of c and w; thread 0 also writes
+// a_t, b_t, p_t.  Rows t = 0..n of every array.
+__device__ __forceinline__ void coefficients(const BwLayout& wl, float* ws, int C, int n,
+                                             const float* s_al, const float* s_et,
+                                             const float* s_be) {
+    const int j = threadIdx.x;
+    float* ca = ws + wl.ca;
+    float* cb = ws + wl.cb;
+    float* cp = ws + wl.cp;
+    float* cm = ws + wl.cm;
+    float* wm = ws + wl.wm;
+    float wj = 0.0f, cj = 0.0f, at = 1.0f, bt = 0.0f, pt = 1.0f;
+    if (j < C) { cm[j] = 0.0f; wm[j] = 0.0f; }
+    if (j == 0) { ca[0] = 1.0f; cb[0] = 0.0f; cp[0] = 1.0f; }
+    for (int t = 0; t < n; ++t) {
+        const float al = s_al[t], et = s_et[t], be = s_be[t];
+        const float keep = 1.0f - al;
+        pt *= be;
+        wj = be * wj + ((j == t) ? 1.0f - be : 0.0f);
+        at *= keep;
+        bt = keep * bt + et * pt;
+        cj = keep * cj + et * wj;
+        if (j < C) {
+            cm[(int64_t)(t + 1) * C + j] = cj;
+            wm[(int64_t)(t + 1) * C + j] = wj;
+        }
+        if (j == 0) { ca[t + 1] = at; cb[t + 1] = bt; cp[t + 1] = pt; }
+    }
+}
+
+// Key path at the chunk-start weights: Zk, Hk, the residual r = M(k) - v, the output
+// error loss'(r) and the errors Delta_l, Gk_l of every layer.
+template <bool kMfma>
+__device__ __forceinline__ void key_path(const ScanArgs& a, const BwLayout& wl, float* ws,
+                                         const float* theta, const Bases& bs, int64_t c0, int n,
+                                         float* lds) {
+    const int L = a.L;
+    for (int l = 1; l <= L; ++l) {
+        const int nin = a.n[l - 1], nout = a.n[l];
+        const float* W = theta + a.off[l];
+        const MatA A{ws + wl.hk[l - 1], nin, 1, nullptr};
+        const MatB Bm{W, 1, nin};
+        if (l < L) {
+            float* Hout = ws + wl.hk[l];
+            float* Z = ws + wl.zk[l];
+            gemm<kMfma>(n, nout, nin, A, Bm, lds, [&](int i, int j, float z) {
+                Z[i * nout + j] = z;
+                Hout[i * nout + j] = z * sigmoidf_(z);
+            });
+        } else {
+            float* R = ws + wl.rr;
+            float* D = ws + wl.dl[L];
+            gemm<kMfma>(n, nout, nin, A, Bm, lds, [&](int i, int j, float z) {
+                const float r = z - load_io(a.v, bs.q + (c0 + i) * a.qs[1] + j, a.io);
+                R[i * nout + j] = r;
+                D[i * nout + j] = bias_grad(r, a.bias, a.bias_param);
+            });
+        }
+    }
+    for (int l = L; l >= 2; --l) {
+        const int nin = a.n[l - 1], nout = a.n[l];
+        const float* Z = ws + wl.zk[l - 1];
+        float* G = ws + wl.gk[l - 1];
+        float* Dp = ws + wl.dl[l - 1];
+        gemm<kMfma>(n, nin, nout, MatA{ws + wl.dl[l], nout, 1, nullptr},
+                    MatB{theta + a.off[l], nin, 1}, lds, [&](int i, int j, float g) {
+                        G[i * nin + j] = g;
+                        Dp[i * nin + j] = g * silu_prime(Z[i * nin + j]);
+                    });
+    }
+}
+
+// Sum of x, y, z over the workgroup (every thread gets the sums).
+__device__ __forceinline__ void block_sum3(float& x, float& y, float& z, float* red) {
+    for (int o = 32; o > 0; o >>= 1) {
+        x += __shfl_xor(x, o);
+        y += __shfl_xor(y, o);
+        z += __shfl_xor(z, o);
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { red[w] = x; red[4 + w] = y; red[8 + w] = z; }
+    __syncthreads();
+    x = red[0] + red[1] + red[2] + red[3];
+    y = red[4] + red[5] + red[6] + red[7];
+    z = red[8] + red[9] + red[10] + red[11];
+    __syncthreads();
+}
+
+// Sweep 1: every chunk's start state (theta_c, s_c) into the checkpoint area.
+template <bool kMfma>
+__global__ void __launch_bounds__(kThreads) bwd_forward_kernel(BwdArgs A, BwLayout wl,
+                                                               float* ckpt) {
+    __shared__ float lds_gemm[kGemmLds];
+    __shared__ float s_al[256], s_et[256], s_be[256];
+    const ScanArgs& a = A.a;
+    const int64_t seq = blockIdx.x;
+    const Bases bs = bases_of(a, seq);
+    const int C = a.C, L = a.L;
+    const int64_t P = a.P, nch = (a.T + C - 1) / C;
+    float* ws = static_cast<float*>(a.ws) + seq * wl.per_seq;
+    float* ck = ckpt + seq * nch * 2 * P;
+    {
+        const float* th0 = a.theta0 + bs.b * a.s0s[0] + bs.h * a.s0s[1];
+        const float* mo0 = a.s0 + bs.b * a.s0s[0] + bs.h * a.s0s[1];
+        for (int64_t i = threadIdx.x; i < P; i += kThreads) {
+            ck[i] = th0[i];
+            ck[P + i] = mo0[i];
+        }
+    }
+    __syncthreads();
+    for (int64_t ci = 0; ci + 1 < nch; ++ci) {
+        const int64_t c0 = ci * C;
+        const int n = C;  // every chunk but the last is full
+        const float* th = ck + ci * 2 * P;
+        const float* mo = th + P;
+        float* thn = ck + (ci + 1) * 2 * P;
+        float* mon = thn + P;
+        stage_keys(a, wl, ws, bs, c0, n, s_al, s_et, s_be);
+        __syncthreads();
+        coefficients(wl, ws, C, n, s_al, s_et, s_be);
+        __syncthreads();
+        key_path<kMfma>(a, wl, ws, th, bs, c0, n, lds_gemm);
+        const float an = ws[wl.ca + n], bn = ws[wl.cb + n], pn = ws[wl.cp + n];
+        const float* crow = ws + wl.cm + (int64_t)n * C;
+        const float* wrow = ws + wl.wm + (int64_t)n * C;
+        for (int l = 1; l <= L; ++l) {
+            const int nin = a.n[l - 1], nout = a.n[l];
+            const int64_t off = a.off[l];
+            const MatB Hk{ws + wl.hk[l - 1], nin, 1};
+            gemm<kMfma>(nout, nin, n, MatA{ws + wl.dl[l], 1, nout, crow}, Hk, lds_gemm,
+                        [&](int i, int j, float x) {
+                            const int64_t o = off + (int64_t)i * nin + j;
+                            thn[o] = an * th[o] - bn * mo[o] - x;
+                        });
+            gemm<kMfma>(nout, nin, n, MatA{ws + wl.dl[l], 1, nout, wrow}, Hk, lds_gemm,
+                        [&](int i, int j, float x) {
+                            const int64_t o = off + (int64_t)i * nin + j;
+                            mon[o] = pn * mo[o] + x;
+                        });
+        }
+    }
+}
+
+// Sweep 2: the chunks in reverse order.
+template <bool kMfma>
+__global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayout wl,
+                                                               const float* ckpt) {
+    __shared__ float lds_gemm[kGemmLds];
+    __shared__ float s_al[256], s_et[256], s_be[256];
+    __shared__ float s_ga[257], s_gb[257];          // cotangents of a_t, b_t (y path; t = n: chunk end)
+    __shared__ float s_gcn[256], s_gwn[256];        // of c_{n,j}, w_{n,j}
+    __shared__ float s_abar[257], s_bbar[257], s_pbar[257];
+    __shared__ float s_red[12];
+    __shared__ float s_gp;
+    const ScanArgs& a = A.a;
+    const int64_t seq = blockIdx.x;
+    const Bases bs = bases_of(a, seq);
+    const int tid = threadIdx.x;
+    const int C = a.C, L = a.L, d = a.n[0];
+    const int64_t P = a.P, nch = (a.T + C - 1) / C;
+    float* ws = static_cast<float*>(a.ws) + seq * wl.per_seq;
+    const float* ck = ckpt + seq * nch * 2 * P;
+    float* Lt = A.dtheta0 + bs.b * a.ss[0] + bs.h * a.ss[1];
+    float* Ls = A.ds0 + bs.b * a.ss[0] + bs.h * a.ss[1];
+    {
+        const float* dT = A.dthetaT ? A.dthetaT + bs.b * a.ss[0] + bs.h * a.ss[1] : nullptr;
+        const float* dS = A.dsT ? A.dsT + bs.b * a.ss[0] + bs.h * a.ss[1] : nullptr;
+        for (int64_t i = tid; i < P; i += kThreads) {
+            if (dT != Lt) Lt[i] = dT ? dT[i] : 0.0f;
+            if (dS != Ls) Ls[i] = dS ? dS[i] : 0.0f;
+        }
+    }
+    float* ca = ws + wl.ca;
+    float* cb = ws + wl.cb;
+    float* cp = ws + wl.cp;
+    float* cm = ws + wl.cm;
+    float* wm = ws + wl.wm;
+    float* gc = ws + wl.gc;
+    float* gw = ws + wl.gw;
+    float* tmp = ws + wl.tmp;
+    __syncthreads();
+
+    for (int64_t ci = nch - 1; ci >= 0; --ci) {
+        const int64_t c0 = ci * C;
+        const int n = (int)((a.T - c0) < C ? (a.T - c0) : C);
+        const float* th = ck + ci * 2 * P;
+        const float* mo = th + P;
+
+        // ---- stage: gates, K, Q, dY; clear the cotangent accumulators
+        stage_keys(a, wl, ws, bs, c0, n, s_al, s_et, s_be);
+        {
+            float* Hq0 = ws + wl.hq[0];
+            float* DqL = ws + wl.dq[L];
+            for (int e = tid; e < n * d; e += kThreads) {
+                const int t = e / d, c = e % d;
+                Hq0[e] = load_io(a.q, bs.q + (c0 + t) * a.qs[1] + c, a.io);
+                DqL[e] = load_io(A.dy, bs.y + (c0 + t) * a.ys[1] + c, a.io);
+            }
+            for (int t = tid; t <= n; t += kThreads) { s_ga[t] = 0.0f; s_gb[t] = 0.0f; }
+            for (int t = tid; t < n; t += kThreads) { s_gcn[t] = 0.0f; s_gwn[t] = 0.0f; }
+        }
+        __syncthreads();
+        coefficients(wl, ws, C, n, s_al, s_et, s_be);
+        __syncthreads();
+
+        // ---- recompute: key path, then the reads at the in-chunk weights
+        key_path<kMfma>(a, wl, ws, th, bs, c0, n, lds_gemm);
+        for (int l = 1; l <= L; ++l) {
+            const int nin = a.n[l - 1], nout = a.n[l];
+            const float* Hq = ws + wl.hq[l - 1];
+            float* Am = ws + wl.am[l];
+            float* Mq = ws + wl.mq[l];
+            gemm<kMfma>(n, n, nin, MatA{Hq, nin, 1, nullptr}, MatB{ws + wl.hk[l - 1], 1, nin},
+                        lds_gemm, [&](int i, int j, float x) {
+                            Am[i * C + j] = x;
+                            Mq[i * C + j] = (j < i) ? cm[(int64_t)i * C + j] * x : 0.0f;
+                        });
+            if (l == L) break;  // the output itself is not needed
+            float* Z = ws + wl.zq[l];
+            float* Hn = ws + wl.hq[l];
+            gemm<kMfma>(n, nout, nin, MatA{Hq, nin, 1, nullptr}, MatB{th + a.off[l], 1, nin},
+                        lds_gemm, [&](int i, int j, float x) { Z[i * nout + j] = ca[i] * x; });
+            gemm<kMfma>(n, nout, nin, MatA{Hq, nin, 1, nullptr}, MatB{mo + a.off[l], 1, nin},
+                        lds_gemm, [&](int i, int j, float x) { Z[i * nout + j] -= cb[i] * x; });
+            gemm<kMfma>(n, nout, n, MatA{Mq, C, 1, nullptr}, MatB{ws + wl.dl[l], nout, 1},
+                        lds_gemm, [&](int i, int j, float x) {
+                            const float z = Z[i * nout + j] - x;
+                            Z[i * nout + j] = z;
+                            Hn[i * nout + j] = z * sigmoidf_(z);
+                        });
+        }
+
+        // ---- query adjoint, layer L down to 1
+        for (int l = L; l >= 1; --l) {
+            const int nin = a.n[l - 1], nout = a.n[l];
+            const float* Dq = ws + wl.dq[l];
+            const float* Hq = ws + wl.hq[l - 1];
+            const float* Am = ws + wl.am[l];
+            float* Mb = ws + wl.mb[l];
+            const bool first = (l == L);
+            gemm<kMfma>(n, n, nout, MatA{Dq, nout, 1, nullptr}, MatB{ws + wl.dl[l], 1, nout},
+                        lds_gemm, [&](int i, int j, float x) {
+                            const bool low = j < i;
+                            Mb[i * C + j] = low ? cm[(int64_t)i * C + j] * x : 0.0f;
+                            const float dc = low ? -x * Am[i * C + j] : 0.0f;
+                            if (first) gc[(int64_t)i * C + j] = dc;
+                            else gc[(int64_t)i * C + j] += dc;
+                        });
+            gemm<kMfma>(n, nin, nout, MatA{Dq, nout, 1, nullptr}, MatB{th + a.off[l], nin, 1},
+                        lds_gemm, [&](int i, int j, float x) {
+                            tmp[i * nin + j] = ca[i] * x;
+                            atomicAdd(&s_ga[i], x * Hq[i * nin + j]);
+                        });
+            gemm<kMfma>(n, nin, nout, MatA{Dq, nout, 1, nullptr}, MatB{mo + a.off[l], nin, 1},
+                        lds_gemm, [&](int i, int j, float x) {
+                            tmp[i * nin + j] -= cb[i] * x;
+                            atomicAdd(&s_gb[i], -x * Hq[i * nin + j]);
+                        });
+            if (l > 1) {
+                const float* Zq = ws + wl.zq[l - 1];
+                float* Dn = ws + wl.dq[l - 1];
+                gemm<kMfma>(n, nin, n, MatA{Mb, C, 1, nullptr}, MatB{ws + wl.hk[l - 1], nin, 1},
+                            lds_gemm, [&](int i, int j, float x) {
+                                Dn[i * nin + j] = (tmp[i * nin + j] - x) * silu_prime(Zq[i * nin + j]);
+                            });
+            } else {
+                gemm<kMfma>(n, nin, n, MatA{Mb, C, 1, nullptr}, MatB{ws + wl.hk[0], nin, 1},
+                            lds_gemm, [&](int i, int j, float x) {
+                                store_io(A.dq, bs.q + (c0 + i) * a.qs[1] + j, a.io,
+                                         tmp[i * nin + j] - x);
+                            });
+            }
+        }
+
+        // ---- chunk-end cotangents of the coefficients; U_l Hk_{l-1} starts RZ_l
+        {
+            float x = 0.0f, y = 0.0f, z = 0.0f;
+            for (int64_t i = tid; i < P; i += kThreads) {
+                x = fmaf(Lt[i], th[i], x);
+                y = fmaf(Lt[i], mo[i], y);
+                z = fmaf(Ls[i], mo[i], z);
+            }
+            block_sum3(x, y, z, s_red);
+            if (tid == 0) {
+                s_ga[n] += x;
+                s_gb[n] -= y;
+                s_gp = z;
+            }
+        }
+        const float* crow = cm + (int64_t)n * C;
+        const float* wrow = wm + (int64_t)n * C;
+        for (int l = 1; l <= L; ++l) {
+            const int nin = a.n[l - 1], nout = a.n[l];
+            const float* Dl = ws + wl.dl[l];
+            float* RZ = ws + wl.rz[l];
+            const MatA Hk{ws + wl.hk[l - 1], nin, 1, nullptr};
+            gemm<kMfma>(n, nout, nin, Hk, MatB{Lt + a.off[l], 1, nin}, lds_gemm,
+                        [&](int i, int j, float x) {
+                            RZ[i * nout + j] = -crow[i] * x;
+                            atomicAdd(&s_gcn[i], -x * Dl[i * nout + j]);
+                        });
+            gemm<kMfma>(n, nout, nin, Hk, MatB{Ls + a.off[l], 1, nin}, lds_gemm,
+                        [&](int i, int j, float x) {
+                            RZ[i * nout + j] += wrow[i] * x;
+                            atomicAdd(&s_gwn[i], x * Dl[i * nout + j]);
+                        });
+        }
+
+        // ---- tangent pass of the key path along U_j
+        for (int l = 1; l <= L; ++l) {
+            const int nin = a.n[l - 1], nout = a.n[l];
+            float* RZ = ws + wl.rz[l];
+            if (l > 1)
+                gemm<kMfma>(n, nout, nin, MatA{ws + wl.rh[l - 1], nin, 1, nullptr},
+                            MatB{th + a.off[l], 1, nin}, lds_gemm,
+                            [&](int i, int j, float x) { RZ[i * nout + j] += x; });
+            const float* Zk = l < L ? ws + wl.zk[l] : nullptr;
+            float* RH = l < L ? ws + wl.rh[l] : nullptr;
+            gemm<kMfma>(n, nout, n, MatA{ws + wl.mq[l], 1, C, nullptr},
+                        MatB{ws + wl.dq[l], nout, 1}, lds_gemm, [&](int i, int j, float x) {
+                            const float rz = RZ[i * nout + j] - x;
+                            RZ[i * nout + j] = rz;
+                            if (RH) RH[i * nout + j] = rz * silu_prime(Zk[i * nout + j]);
+                        });
+        }
+
+        // ---- tangent pass of its backward; dv, dk
+        {
+            const float* R = ws + wl.rr;
+            const float* RZ = ws + wl.rz[L];
+            float* RD = ws + wl.rd[L];
+            for (int e = tid; e < n * d; e += kThreads) {
+                const int t = e / d, c = e % d;
+                const float s = bias_grad_prime(R[e], a.bias, a.bias_param) * RZ[e];
+                RD[e] = s;
+                store_io(A.dv, bs.q + (c0 + t) * a.qs[1] + c, a.io, -s);
+            }
+        }
+        __syncthreads();
+        for (int l = L; l >= 1; --l) {
+            const int nin = a.n[l - 1], nout = a.n[l];
+            const float* Dl = ws + wl.dl[l];
+            gemm<kMfma>(n, nin, nout, MatA{Dl, nout, 1, nullptr}, MatB{Lt + a.off[l], nin, 1},
+                        lds_gemm, [&](int i, int j, float x) { tmp[i * nin + j] = -crow[i] * x; });
+            gemm<kMfma>(n, nin, nout, MatA{Dl, nout, 1, nullptr}, MatB{Ls + a.off[l], nin, 1},
+                        lds_gemm, [&](int i, int j, float x) { tmp[i * nin + j] += wrow[i] * x; });
+            gemm<kMfma>(n, nin, n, MatA{ws + wl.mb[l], 1, C, nullptr},
+                        MatB{ws + wl.hq[l - 1], nin, 1}, lds_gemm,
+                        [&](int i, int j, float x) { tmp[i * nin + j] -= x; });
+            if (l > 1) {
+                const float* Zk = ws + wl.zk[l - 1];
+                const float* Gk = ws + wl.gk[l - 1];
+                const float* RZp = ws + wl.rz[l - 1];
+                float* RDp = ws + wl.rd[l - 1];
+                gemm<kMfma>(n, nin, nout, MatA{ws + wl.rd[l], nout, 1, nullptr},
+                            MatB{th + a.off[l], nin, 1}, lds_gemm, [&](int i, int j, float x) {
+                                const int o = i * nin + j;
+                                const float z = Zk[o];
+                                RDp[o] = (tmp[o] + x) * silu_prime(z) + Gk[o] * silu_second(z) * RZp[o];
+                            });
+            } else {
+                gemm<kMfma>(n, nin, nout, MatA{ws + wl.rd[1], nout, 1, nullptr},
+                            MatB{th + a.off[1], nin, 1}, lds_gemm, [&](int i, int j, float x) {
+                                store_io(A.dk, bs.q + (c0 + i) * a.qs[1] + j, a.io,
+                                         tmp[i * nin + j] + x);
+                            });
+            }
+        }
+
+        // ---- carry the state cotangents to the chunk start (Ls first: it reads the old Lt)
+        {
+            const float an = ca[n], bn = cb[n], pn = cp[n];
+            for (int l = 1; l <= L; ++l) {
+                const int nin = a.n[l - 1], nout = a.n[l];
+                float* Lt_l = Lt + a.off[l];
+                float* Ls_l = Ls + a.off[l];
+                const MatB Hq{ws + wl.hq[l - 1], nin, 1};
+                gemm<kMfma>(nout, nin, n, MatA{ws + wl.dq[l], 1, nout, cb}, Hq, lds_gemm,
+                            [&](int i, int j, float x) {
+                                const int64_t o = (int64_t)i * nin + j;
+                                Ls_l[o] = pn * Ls_l[o] - bn * Lt_l[o] - x;
+                            });
+                gemm<kMfma>(nout, nin, n, MatA{ws + wl.dq[l], 1, nout, ca}, Hq, lds_gemm,
+                            [&](int i, int j, float x) {
+                                const int64_t o = (int64_t)i * nin + j;
+                                Lt_l[o] = an * Lt_l[o] + x;
+                            });
+                gemm<kMfma>(nout, nin, n, MatA{ws + wl.rd[l], 1, nout, nullptr},
+                            MatB{ws + wl.hk[l - 1], nin, 1}, lds_gemm,
+                            [&](int i, int j, float x) { Lt_l[(int64_t)i * nin + j] += x; });
+                if (l > 1)
+                    gemm<kMfma>(nout, nin, n, MatA{ws + wl.dl[l], 1, nout, nullptr},
+                                MatB{ws + wl.rh[l - 1], nin, 1}, lds_gemm,
+                                [&](int i, int j, float x) { Lt_l[(int64_t)i * nin + j] += x; });
+            }
+        }
+
+        // ---- gates: the coefficient recurrence backwards
+        if (tid < n) {  // column j: cotangents of c_{t,j} (into gc) and w_{t,j} (into gw)
+            const int j = tid;
+            float cr = s_gcn[j], wr = s_gwn[j];
+            gc[(int64_t)n * C + j] = cr;
+            for (int t = n - 1; t >= 0; --t) {
+                wr = fmaf(s_et[t], cr, wr);                       // of w_{t+1,j}, complete
+                gw[(int64_t)(t + 1) * C + j] = wr;
+                cr = gc[(int64_t)t * C + j] + (1.0f - s_al[t]) * cr;  // of c_{t,j}
+                gc[(int64_t)t * C + j] = cr;
+                wr *= s_be[t];
+            }
+        }
+        if (tid == kThreads - 1) {  // cotangents of a_t, b_t, p_t
+            float ab = s_ga[n], bb = s_gb[n], pb = s_gp;
+            for (int t = n - 1; t >= 0; --t) {
+                pb = fmaf(s_et[t], bb, pb);
+                s_abar[t + 1] = ab;
+                s_bbar[t + 1] = bb;
+                s_pbar[t + 1] = pb;
+                const float keep = 1.0f - s_al[t];
+                ab = s_ga[t] + keep * ab;
+                bb = s_gb[t] + keep * bb;
+                pb *= s_be[t];
+            }
+        }
+        __syncthreads();
+        if (tid < n) {
+            const int t = tid;
+            const float* cn = gc + (int64_t)(t + 1) * C;
+            const float* wn = gw + (int64_t)(t + 1) * C;
+            const float* ct = cm + (int64_t)t * C;
+            const float* w1 = wm + (int64_t)(t + 1) * C;
+            const float* w0 = wm + (int64_t)t * C;
+            float sa = 0.0f, se = 0.0f, sb = 0.0f;
+            for (int j = 0; j < t; ++j) {
+                sa = fmaf(cn[j], ct[j], sa);
+                sb = fmaf(wn[j], w0[j], sb);
+            }
+            for (int j = 0; j <= t; ++j) se = fmaf(cn[j], w1[j], se);
+            const int64_t gi = bs.g + (c0 + t) * a.gs[1];
+            A.dalpha[gi] = -s_abar[t + 1] * ca[t] - s_bbar[t + 1] * cb[t] - sa;
+            A.deta[gi] = s_bbar[t + 1] * cp[t + 1] + se;
+            A.dbeta[gi] = s_pbar[t + 1] * cp[t] + sb - wn[t];
+        }
+        __syncthreads();
+    }
+}
+
+// T = 0: the state cotangents pass through.
+__global__ void bwd_copy_kernel(BwdArgs A) {
+    const ScanArgs& a = A.a;
+    const int64_t seq = blockIdx.y;
+    const int64_t b = seq / a.H, h = seq % a.H;
+    const int64_t o = b * a.ss[0] + h * a.ss[1];
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.P;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const float* dT = A.dthetaT ? A.dthetaT + o : nullptr;
+        const float* dS = A.dsT ? A.dsT + o : nullptr;
+        if (A.dtheta0 + o != dT) A.dtheta0[o + i] = dT ? dT[i] : 0.0f;
+        if (A.ds0 + o != dS) A.ds0[o + i] = dS ? dS[i] : 0.0f;
+    }
+}
+
+}  // namespace
+
+size_t scan_backward_workspace_bytes(const ScanArgs& a) {
+    const BwLayout w = bw_layout(a.C, a.L, a.n);
+    const int64_t nch = (a.T + a.C - 1) / a.C;
+    return (size_t)(a.B * a.H) * (size_t)(w.per_seq + nch * 2 * a.P) * sizeof(float);
+}
+
+hipError_t launch_scan_backward(const BwdArgs& A, hipStream_t stream) {
+    const ScanArgs& a = A.a;
+    const int64_t nseq = a.B * a.H;
+    if (nseq == 0) return hipSuccess;
+    if (a.T == 0) {
+        dim3 grid((unsigned)((a.P + 255) / 256 < 64 ? (a.P + 255) / 256 : 64), (unsigned)nseq);
+        bwd_copy_kernel<<<grid, 256, 0, stream>>>(A);
+        return hipGetLastError();
+    }
+    const BwLayout wl = bw_layout(a.C, a.L, a.n);
+    float* ckpt = static_cast<float*>(a.ws) + nseq * wl.per_seq;
+    bwd_forward_kernel<false><<<dim3((unsigned)nseq), kThreads, 0, stream>>>(A, wl, ckpt);
+    bwd_reverse_kernel<false><<<dim3((unsigned)nseq), kThreads, 0, stream>>>(A, wl, ckpt);
+    return hipGetLastError();
+}
+
+}  // namespace titans

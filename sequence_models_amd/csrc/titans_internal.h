@@ -36,6 +36,30 @@ struct ScanArgs {
     float bias_param;          // Huber delta or l_p exponent
 };
 
+// The reverse pass: the forward problem plus output cotangents and the input cotangents
+// it writes (q/k/v cotangents in q's layout and dtype, gate cotangents in the gates'
+// layout, state cotangents with the theta_T / s_T strides).
+struct BwdArgs {
+    ScanArgs a;
+    const void* dy;         // y's layout (a.ys)
+    const float* dthetaT;   // NULL: zero
+    const float* dsT;       // NULL: zero
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dalpha;
+    float* deta;
+    float* dbeta;
+    float* dtheta0;
+    float* ds0;
+};
+
+// Reverse-mode derivatives of the scan, one workgroup per (b, h): a forward sweep stores
+// every chunk's start state in the workspace, then a reverse chunk loop recomputes each
+// chunk and runs its adjoint (products on fp32 FMAs).
+size_t scan_backward_workspace_bytes(const ScanArgs& a);
+hipError_t launch_scan_backward(const BwdArgs& b, hipStream_t stream);
+
 // Generic chunked scan: any supported shape, one workgroup per (b, h), per-chunk
 // intermediates in the workspace.  Its matrix products run on bf16 MFMA (fp32
 // accumulation) for bf16 I/O and on fp32 FMAs for fp32 I/O; state is fp32 either way.

@@ -33,7 +33,7 @@ import numpy as np
 BLOCK_TOKENS = 4096
 
 # tensor ids for the stream keys
-_Q, _K, _V, _ALPHA, _ETA, _BETA, _THETA = range(7)
+_Q, _K, _V, _ALPHA, _ETA, _BETA, _THETA, _DY, _DTHETA, _DS = range(10)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -200,3 +200,35 @@ def make_inputs(wl: Workload | str, seed: int = 0, seq_len: int | None = None,
     theta0 = make_theta0(wl, seed)
     s0 = np.zeros_like(theta0)
     return Inputs(wl.with_(batch=B, seq_len=T), q, k, v, alpha, eta, beta, theta0, s0)
+
+
+@dataclasses.dataclass
+class Cotangents:
+    """Output cotangents for the reverse pass: dy like y, dtheta_T and ds_T [B,H,P]."""
+    dy: np.ndarray       # [B,T,H,d]: float32, or uint16 bf16 bits
+    dtheta_T: np.ndarray  # [B,H,P] float32
+    ds_T: np.ndarray
+
+    def dy_f32(self) -> np.ndarray:
+        return bf16_bits_to_f32(self.dy) if self.dy.dtype == np.uint16 else self.dy
+
+
+def make_cotangents(wl: Workload | str, seed: int = 0, seq_len: int | None = None,
+                    batch: int | None = None, state_scale: float = 0.1) -> Cotangents:
+    """Seeded output cotangents (the pages give none; a downstream loss's gradient stands in):
+    dy ~ N(0, 1) per element, stored like q (bf16 bits for bf16 workloads, prefix-consistent
+    in T like the inputs); dtheta_T, ds_T ~ state_scale * N(0, 1), float32."""
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    B = wl.batch if batch is None else batch
+    T = wl.seq_len if seq_len is None else seq_len
+    H, d = wl.heads, wl.d
+    dy = np.empty((B, T, H, d), dtype=np.uint16 if wl.io == "bf16" else np.float32)
+    _draw_vectors(seed, _DY, wl, B, T, False, dy)
+    P = wl.params
+    dth = np.empty((B, H, P), dtype=np.float32)
+    ds = np.empty((B, H, P), dtype=np.float32)
+    for b in range(B):
+        dth[b] = (state_scale * _rng(seed, _DTHETA, b).standard_normal((H, P))).astype(np.float32)
+        ds[b] = (state_scale * _rng(seed, _DS, b).standard_normal((H, P))).astype(np.float32)
+    return Cotangents(dy, dth, ds)

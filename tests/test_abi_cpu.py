@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_status_strings_and_param_count():
-    assert tm.lib.titans_abi_version() == 2
+    assert tm.lib.titans_abi_version() == 3
     assert tm.lib.titans_status_string(0) == b"TITANS_OK"
     assert tm.lib.titans_status_string(3) == b"TITANS_ERR_WORKSPACE"
     assert tm.param_count((64, 256, 64)) == 32768
@@ -325,3 +325,114 @@ def test_linear_memory_path_selection(monkeypatch):
         2 * 32 * (gen + summ + 2 * P) * 4
     monkeypatch.setenv("TITANS_MEM_LINEAR", "0")
     assert tm.lib.titans_mem_scan_path(ctypes.byref(long_), ctypes.byref(lin)) == b"generic_mfma"
+
+
+def test_backward_workspace_formula():
+    """Per memory: one (theta, s) checkpoint per chunk plus the reverse sweep's area --
+    coefficient rows a, b, p (C + 1 each), the (C + 1) x C matrices c, w and their
+    cotangents, the C x n_l activations, errors and tangents of both paths, three C x C
+    products per layer and one C x (max width) buffer, each rounded up to 64 floats."""
+    r64 = lambda x: (x + 63) // 64 * 64
+    widths = (16, 32, 16)
+    B, T, H, C = 2, 300, 3, 64
+    n = widths
+    L = len(n) - 1
+    P = 16 * 32 * 2
+    per = 3 * r64(C + 1) + 4 * r64((C + 1) * C)
+    per += sum(r64(C * n[l]) for l in range(L))            # Hk_0..L-1
+    per += 2 * sum(r64(C * n[l]) for l in range(1, L))     # Zk, Gk
+    per += sum(r64(C * n[l]) for l in range(1, L + 1))     # Delta
+    per += r64(C * n[L])                                   # residual
+    per += sum(r64(C * n[l]) for l in range(L))            # Hq
+    per += sum(r64(C * n[l]) for l in range(1, L))         # Zq
+    per += 2 * sum(r64(C * n[l]) for l in range(1, L + 1)) # Dq, RZ
+    per += sum(r64(C * n[l]) for l in range(1, L))         # RH
+    per += sum(r64(C * n[l]) for l in range(1, L + 1))     # RDelta
+    per += 3 * L * r64(C * C) + r64(C * 32)
+    nch = (T + C - 1) // C
+    d = _desc(B, T, H, 16, C, io=0)
+    got = tm.lib.titans_mem_scan_backward_workspace_size(ctypes.byref(d),
+                                                         ctypes.byref(tm.mlp_desc(widths)))
+    assert got == B * H * (per + nch * 2 * P) * 4
+    assert tm.lib.titans_mem_scan_backward_workspace_size(
+        ctypes.byref(_desc(T=0)), ctypes.byref(tm.mlp_desc(widths))) == 0
+    bad = ctypes.c_size_t(-1).value
+    assert tm.lib.titans_mem_scan_backward_workspace_size(
+        ctypes.byref(_desc(C=0)), ctypes.byref(tm.mlp_desc(widths))) == bad
+    lp = _desc()
+    lp.bias, lp.bias_param = 2, 1.5   # l_p below p = 2 has no second derivative at 0
+    assert tm.lib.titans_mem_scan_backward_workspace_size(
+        ctypes.byref(lp), ctypes.byref(tm.mlp_desc((64, 256, 64)))) == bad
+
+
+_BWD_IN = ("q", "k", "v", "alpha", "eta", "beta", "theta0", "s0", "dy", "dtheta_T", "ds_T")
+_BWD_OUT = ("dq", "dk", "dv", "dalpha", "deta", "dbeta", "dtheta0", "ds0")
+
+
+def _bwd(desc, mlp, ptrs, ws=None, ws_bytes=0):
+    args = [ptrs.get(n) for n in _BWD_IN + _BWD_OUT]
+    st = tm.lib.titans_mem_scan_backward(ctypes.byref(desc), ctypes.byref(mlp), *args, ws,
+                                         ws_bytes, None)
+    assert st != HIP, "validation let the call through to HIP"
+    return st, tm.lib.titans_last_error().decode()
+
+
+def _fake_bwd_ptrs(B, T, H, d, P, esz=2, base=1 << 40):
+    io = B * T * H * d * esz
+    gate = B * T * H * 4
+    state = B * H * P * 4
+    sizes = {"q": io, "k": io, "v": io, "alpha": gate, "eta": gate, "beta": gate,
+             "theta0": state, "s0": state, "dy": io, "dtheta_T": state, "ds_T": state,
+             "dq": io, "dk": io, "dv": io, "dalpha": gate, "deta": gate, "dbeta": gate,
+             "dtheta0": state, "ds0": state}
+    out, cur = {}, base
+    for n, s in sizes.items():
+        out[n] = cur
+        cur += (s + 4095) // 4096 * 4096
+    return out, cur
+
+
+def test_backward_rejects_unsupported_bias_and_null_pointers():
+    mlp = tm.mlp_desc((64, 256, 64))
+    d = _desc()
+    d.bias, d.bias_param = 2, 1.0
+    st, msg = _bwd(d, mlp, {})
+    assert st == UNSUPPORTED and "l_p" in msg
+    for bias, prm in ((0, 0.0), (1, 0.5), (2, 2.0), (2, 3.5)):
+        d = _desc()
+        d.bias, d.bias_param = bias, prm
+        st, msg = _bwd(d, mlp, {})
+        assert st == INVALID and "non-NULL" in msg, (bias, prm, msg)
+
+
+@no_fake_pointers_on_gpu
+def test_backward_validation_of_overlap_and_workspace():
+    mlp = tm.mlp_desc((64, 256, 64))
+    B, T, H, d, P = 2, 64, 4, 64, 32768
+    desc = _desc(B, T, H, d)
+    desc.state_stride[:] = (H * P, P)
+    desc.state0_stride[:] = (H * P, P)
+    ptrs, end = _fake_bwd_ptrs(B, T, H, d, P)
+    need = tm.lib.titans_mem_scan_backward_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+    assert need > 0
+    for out in _BWD_OUT:   # every output against an input and against another output
+        for other in ("q", "dy", "alpha", "theta0", "dq", "dalpha"):
+            if other == out:
+                continue
+            st, msg = _bwd(desc, mlp, dict(ptrs, **{out: ptrs[other]}), end, need)
+            assert st == INVALID, (out, other, msg)
+    # the in-place pairs are allowed up to the workspace check
+    st, msg = _bwd(desc, mlp, dict(ptrs, dtheta0=ptrs["dtheta_T"], ds0=ptrs["ds_T"]), None, 0)
+    assert st == WORKSPACE, msg
+    # dtheta_T may not feed the other state output
+    st, msg = _bwd(desc, mlp, dict(ptrs, ds0=ptrs["dtheta_T"]), end, need)
+    assert st == INVALID
+    assert _bwd(desc, mlp, dict(ptrs, dq=ptrs["dq"] + 2), end, need)[0] == INVALID
+    assert _bwd(desc, mlp, dict(ptrs, dalpha=ptrs["dalpha"] + 1), end, need)[0] == INVALID
+    assert _bwd(desc, mlp, ptrs, end, need - 1)[0] == WORKSPACE
+    assert _bwd(desc, mlp, ptrs, end + 64, need)[0] == INVALID
+    assert _bwd(desc, mlp, ptrs, ptrs["dv"], need)[0] == INVALID
+    shared = _desc(B, T, H, d)
+    shared.state_stride[:] = (0, P)   # one dtheta0 written by several batch rows
+    shared.state0_stride[:] = (0, P)
+    assert _bwd(shared, mlp, ptrs, end, need)[0] == INVALID
