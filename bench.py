@@ -18,6 +18,9 @@ batch rows, every head, all or a prefix of the tokens) on the host cores.
 retrieve: titans_mem_retrieve over the same q with the scan's final weights.
 biases: the same scan with the Huber (delta 0.5) and l_p (p 3) attentional biases.
 surprise: titans_mem_scan_surprise (the scan plus each token's gradient norm).
+backward: titans_mem_scan_backward (cotangents of every input for seeded output
+cotangents) on the same inputs, with its own roofline: the products of the checkpointing
+forward sweep and the reverse chunk loop (bwd_alg_flops_per_token_head) on fp32 FMAs.
 """
 from __future__ import annotations
 
@@ -46,6 +49,26 @@ def alg_flops_per_token_head(widths, C):
     P = sum(widths[l] * widths[l - 1] for l in range(1, len(widths)))
     lower = (C - 1) * sum(widths[l - 1] + widths[l] for l in range(1, len(widths)))
     return 12 * P - 2 * widths[1] * widths[0] + lower
+
+
+def bwd_alg_flops_per_token_head(widths, C):
+    """Products of the reverse pass per token-head, checkpointing forward sweep included.
+    Per layer l (P_l = n_l n_{l-1}), 2 P_l flops per token for each of: the sweep's key
+    forward, key backward (l >= 2) and two carries; the recompute's key forward, key backward
+    (l >= 2) and two in-chunk read products (l < L); the query adjoint's two products with
+    W_l, S_l; the chunk-end products with the two state cotangents; the key tangent
+    product (l >= 2); the tangent backward's three products; the state-cotangent carry's
+    three products plus one (l >= 2) -- 14 + 4 [l >= 2] + 2 [l < L] in all.  Plus the
+    strictly-lower C x C terms, (C - 1)(3 n_{l-1} + 2 n_l + n_l [l < L]) per token, and three
+    P-long dot products per chunk."""
+    L = len(widths) - 1
+    P = sum(widths[l] * widths[l - 1] for l in range(1, L + 1))
+    total = 6.0 * P / C
+    for l in range(1, L + 1):
+        nin, nout = widths[l - 1], widths[l]
+        units = 14 + 4 * (l >= 2) + 2 * (l < L)
+        total += units * 2 * nin * nout + (C - 1) * (3 * nin + 2 * nout + nout * (l < L))
+    return total
 
 
 def alg_bytes(wl):
@@ -193,6 +216,49 @@ def bench_surprise(tm, torch, t, wl, out, steps, warmup):
             "path": tm.surprise_path(t["q"], wl.chunk, wl.widths)}
 
 
+def bench_backward(tm, torch, t, wl, seed, steps, warmup):
+    """titans_mem_scan_backward on the same inputs with seeded output cotangents (its own
+    line): tokens/s and the fp32-FMA roofline of its two kernels (checkpointing forward
+    sweep, reverse chunk loop), timed together by HIP events around the call."""
+    import synthetic
+
+    cot = synthetic.make_cotangents(wl, seed)
+    dev = t["q"].device
+    dy = (torch.from_numpy(cot.dy.view(np.int16)).to(dev).view(torch.bfloat16)
+          if cot.dy.dtype == np.uint16 else torch.from_numpy(cot.dy).to(dev))
+    dth = torch.from_numpy(cot.dtheta_T).to(dev)
+    dsT = torch.from_numpy(cot.ds_T).to(dev)
+    n = tm.scan_backward_workspace_size(t["q"], wl.chunk, wl.widths)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    out = None
+
+    def run():
+        nonlocal out
+        out = tm.scan_backward(t["q"], t["k"], t["v"], t["alpha"], t["eta"], t["beta"],
+                               t["theta0"], t["s0"], dy, wl.chunk, wl.widths, dtheta_T=dth,
+                               ds_T=dsT, workspace=ws, out=out)
+    for _ in range(warmup):
+        run()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    B, T, H = t["q"].shape[:3]
+    flops = bwd_alg_flops_per_token_head(wl.widths, wl.chunk) * B * T * H
+    tf = flops / (ms * 1e-3) / 1e12
+    del ws
+    return {"ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "steps": steps,
+            "workspace_bytes": n, "kernels": "bwd_forward_kernel + bwd_reverse_kernel",
+            "roofline": {"bound": "alu", "achieved": tf, "peak": PEAKS["valu_f32"],
+                         "unit": "TFLOP/s", "frac": tf / PEAKS["valu_f32"],
+                         "alg_flops_per_launch": flops}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +272,7 @@ def main():
     ap.add_argument("--no-retrieve", action="store_true")
     ap.add_argument("--no-biases", action="store_true")
     ap.add_argument("--no-surprise", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -319,6 +386,8 @@ def main():
         result["biases"] = bench_biases(tm, torch, t, wl, (y, thT, sT), ws, args.steps, args.warmup)
     if not args.no_surprise:
         result["surprise"] = bench_surprise(tm, torch, t, wl, (y, thT, sT), min(args.steps, 5), 1)
+    if not args.no_backward:
+        result["backward"] = bench_backward(tm, torch, t, wl, args.seed, min(args.steps, 3), 1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_sample_rows, args.cpu_sample_tokens)
     print(json.dumps(result), flush=True)

@@ -1,6 +1,6 @@
 // Workgroup matrix products of the generic (any-shape) kernels: a 256-thread workgroup
 // computes C = A B tile by tile and hands every output element to an epilogue functor.
-// fp32 FMAs (block_gemm) or bf16 MFMA with fp32 accumulation (block_gemm_mfma).
+// fp32 FMAs (block_gemm_f32) or bf16 MFMA with fp32 accumulation (block_gemm_mfma).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,13 +11,14 @@ namespace generic {
 
 constexpr int kGemmThreads = 256;
 constexpr int kTile = 64;   // output tile edge
-constexpr int kKStep = 16;  // reduction step
-constexpr int kPad = 4;
-constexpr int kGemmLdsF32 = 2 * kKStep * (kTile + kPad);  // floats
 constexpr int kMK = 32;                                     // MFMA reduction step
 constexpr int kMLd = kMK + 8;                               // padded bf16 row of a staged tile
 constexpr int kGemmLdsMfma = 2 * kTile * kMLd / 2;          // floats (two bf16 tiles)
-constexpr int kGemmLds = kGemmLdsF32 > kGemmLdsMfma ? kGemmLdsF32 : kGemmLdsMfma;
+constexpr int kK2 = 32;                                     // fp32 reduction step
+constexpr int kLd2 = kTile + 4;                             // padded row of a staged fp32 tile
+constexpr int kGemmLdsF32v2 = 2 * 2 * kK2 * kLd2;           // floats (A and B, two buffers)
+// LDS floats a caller provides (16-byte aligned) for either product below
+constexpr int kGemmLds = kGemmLdsMfma > kGemmLdsF32v2 ? kGemmLdsMfma : kGemmLdsF32v2;
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
@@ -35,75 +36,15 @@ struct MatB {
     int64_t sk, sj;
 };
 
-// Workgroup GEMM: for every (i < M, j < N) call epi(i, j, sum_k A(i,k) B(k,j)).
-// Each output element is owned by exactly one thread.
-template <class Epi>
-__device__ void block_gemm(int M, int N, int K, MatA A, MatB B, float* lds, Epi epi) {
-    float* As = lds;                          // [kKStep][kTile + kPad]
-    float* Bs = lds + kKStep * (kTile + kPad);
-    const int tid = threadIdx.x;
-    const int tx = tid & 15, ty = tid >> 4;
-    for (int i0 = 0; i0 < M; i0 += kTile) {
-        for (int j0 = 0; j0 < N; j0 += kTile) {
-            float acc[4][4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) acc[r][c] = 0.0f;
-            for (int k0 = 0; k0 < K; k0 += kKStep) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    int e = tid + kGemmThreads * r;
-                    int ii, kk;
-                    if (A.sk == 1) { kk = e & 15; ii = e >> 4; } else { ii = e & 63; kk = e >> 6; }
-                    int gi = i0 + ii, gk = k0 + kk;
-                    float val = 0.0f;
-                    if (gi < M && gk < K) {
-                        val = A.p[gi * A.si + gk * A.sk];
-                        if (A.kscale) val *= A.kscale[gk];
-                    }
-                    As[kk * (kTile + kPad) + ii] = val;
-                    int jj;
-                    if (B.sj == 1) { jj = e & 63; kk = e >> 6; } else { kk = e & 15; jj = e >> 4; }
-                    int gj = j0 + jj;
-                    gk = k0 + kk;
-                    Bs[kk * (kTile + kPad) + jj] = (gj < N && gk < K) ? B.p[gk * B.sk + gj * B.sj] : 0.0f;
-                }
-                __syncthreads();
-#pragma unroll
-                for (int kk = 0; kk < kKStep; ++kk) {
-                    float av[4], bv[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) av[r] = As[kk * (kTile + kPad) + ty + 16 * r];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) bv[c] = Bs[kk * (kTile + kPad) + tx + 16 * c];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
-                }
-                __syncthreads();
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    int i = i0 + ty + 16 * r, j = j0 + tx + 16 * c;
-                    if (i < M && j < N) epi(i, j, acc[r][c]);
-                }
-        }
-    }
-    __syncthreads();
-}
-
-// The same workgroup GEMM on bf16 MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+// Workgroup GEMM on bf16 MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulation): for every
+// (i < M, j < N) call epi(i, j, sum_k A(i,k) B(k,j)), each output element from one thread.
 // Per 64 x 64 output tile and 32-wide reduction step, A (64 x 32) and B (32 x 64) are staged
 // in LDS as bf16 with the reduction index contiguous ([row i][k], [column j][k]); wave w
 // computes output rows 16w .. 16w+15 against the four 16-column tiles.  Operand layouts of
 // the MFMA: lane l (g = l / 16, j = l % 16) holds A[j][k] and B[k][j] for k in
 // {4g .. 4g+3, 16+4g .. 16+4g+3} and D[4g + r][j], r = 0..3.
-template <class Epi>
-__device__ void block_gemm_mfma(int M, int N, int K, MatA A, MatB B, float* lds, Epi epi) {
+template <class Pre, class Epi>
+__device__ void block_gemm_mfma(int M, int N, int K, MatA A, MatB B, float* lds, Pre pre, Epi epi) {
     __bf16* As = reinterpret_cast<__bf16*>(lds);  // [64][kMLd]
     __bf16* Bs = As + kTile * kMLd;                // [64][kMLd]
     const int tid = threadIdx.x;
@@ -176,24 +117,172 @@ __device__ void block_gemm_mfma(int M, int N, int K, MatA A, MatB B, float* lds,
                 }
                 __syncthreads();
             }
+            decltype(pre(0, 0)) pv[4][4];
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = i0 + 16 * wv + 4 * g + r, jc = j0 + 16 * tn + j;
-                    if (i < M && jc < N) epi(i, jc, acc[tn][r]);
+                    if (i < M && jc < N) pv[tn][r] = pre(i, jc);
+                }
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = i0 + 16 * wv + 4 * g + r, jc = j0 + 16 * tn + j;
+                    if (i < M && jc < N) epi(i, jc, acc[tn][r], pv[tn][r]);
                 }
         }
     }
     __syncthreads();
 }
 
+// fp32 workgroup GEMM, same contract, with 32-deep reduction steps, double-buffered in LDS:
+// the next step's global loads are in flight during the current step's FMAs, one barrier
+// per step.  Thread (ty, tx) = (tid / 16, tid % 16) owns rows 4 ty .. 4 ty + 3 and columns
+// 4 tx .. 4 tx + 3 of each 64 x 64 output tile, so every reduction index costs one 16-byte
+// LDS read per operand (A: four distinct addresses per wave, broadcast; B: 256 contiguous
+// bytes), and those reads run four reduction indices ahead of the FMAs.  Staging: eight
+// elements of A and eight of B per thread, consecutive threads on the operand's contiguous
+// dimension; out-of-range elements load a clamped in-range address and are zeroed when
+// written to LDS, so the loads carry no branches and issue back to back.
+template <class Pre, class Epi>
+__device__ void block_gemm_f32(int M, int N, int K, MatA A, MatB B, float* lds, Pre pre, Epi epi) {
+    const int tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;
+    const bool a_kc = A.sk == 1, b_jc = B.sj == 1;
+    for (int i0 = 0; i0 < M; i0 += kTile) {
+        for (int j0 = 0; j0 < N; j0 += kTile) {
+            // raw loads (clamped addresses, no branches) into registers; validity and the
+            // k-scale are applied when the step is written to LDS, after the FMAs
+            float ra[8], rb[8], rs[8];
+            const bool scaled = A.kscale != nullptr;
+            auto load = [&](int k0) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int e = tid + kGemmThreads * r;
+                    const int ii = a_kc ? e >> 5 : e & 63, ka = a_kc ? e & 31 : e >> 6;
+                    const int gi = i0 + ii, gka = k0 + ka;
+                    const int ci = gi < M ? gi : M - 1, cka = gka < K ? gka : K - 1;
+                    ra[r] = A.p[(int64_t)ci * A.si + (int64_t)cka * A.sk];
+                    if (scaled) rs[r] = A.kscale[cka];
+                    const int jj = b_jc ? e & 63 : e >> 5, kb = b_jc ? e >> 6 : e & 31;
+                    const int gj = j0 + jj, gkb = k0 + kb;
+                    const int cj = gj < N ? gj : N - 1, ckb = gkb < K ? gkb : K - 1;
+                    rb[r] = B.p[(int64_t)ckb * B.sk + (int64_t)cj * B.sj];
+                }
+            };
+            auto store = [&](int buf, int k0) {
+                float* As = lds + buf * kK2 * kLd2;
+                float* Bs = lds + (2 + buf) * kK2 * kLd2;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int e = tid + kGemmThreads * r;
+                    const int ii = a_kc ? e >> 5 : e & 63, ka = a_kc ? e & 31 : e >> 6;
+                    const float x = scaled ? ra[r] * rs[r] : ra[r];
+                    As[ka * kLd2 + ii] = (i0 + ii < M && k0 + ka < K) ? x : 0.0f;
+                    const int jj = b_jc ? e & 63 : e >> 5, kb = b_jc ? e >> 6 : e & 31;
+                    Bs[kb * kLd2 + jj] = (j0 + jj < N && k0 + kb < K) ? rb[r] : 0.0f;
+                }
+            };
+            float acc[4][4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[r][c] = 0.0f;
+            load(0);
+            store(0, 0);
+            __syncthreads();
+            int buf = 0;
+            for (int k0 = 0; k0 < K; k0 += kK2) {
+                const bool more = k0 + kK2 < K;
+                if (more) load(k0 + kK2);
+                const float* As = lds + buf * kK2 * kLd2 + 4 * ty;
+                const float* Bs = lds + (2 + buf) * kK2 * kLd2 + 4 * tx;
+                f32x4_t av[4], bv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    av[u] = *reinterpret_cast<const f32x4_t*>(As + u * kLd2);
+                    bv[u] = *reinterpret_cast<const f32x4_t*>(Bs + u * kLd2);
+                }
+#pragma unroll 2
+                for (int kb = 0; kb < kK2; kb += 4) {
+                    f32x4_t an[4], bn[4];
+                    if (kb + 4 < kK2) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            an[u] = *reinterpret_cast<const f32x4_t*>(As + (kb + 4 + u) * kLd2);
+                            bn[u] = *reinterpret_cast<const f32x4_t*>(Bs + (kb + 4 + u) * kLd2);
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+#pragma unroll
+                            for (int c = 0; c < 4; ++c)
+                                acc[r][c] = fmaf(av[u][r], bv[u][c], acc[r][c]);
+                    if (kb + 4 < kK2) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            av[u] = an[u];
+                            bv[u] = bn[u];
+                        }
+                    }
+                }
+                if (more) store(buf ^ 1, k0 + kK2);
+                __syncthreads();
+                buf ^= 1;
+            }
+            // epilogue: every element's operand loads first, then the writes
+            decltype(pre(0, 0)) pv[4][4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int i = i0 + 4 * ty + r, j = j0 + 4 * tx + c;
+                    pv[r][c] = pre(i < M ? i : M - 1, j < N ? j : N - 1);
+                }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int i = i0 + 4 * ty + r, j = j0 + 4 * tx + c;
+                    if (i < M && j < N) epi(i, j, acc[r][c], pv[r][c]);
+                }
+        }
+    }
+    __syncthreads();
+}
+
+// Epilogues in two parts: pre(i, j) loads what element (i, j) needs (any value type) and
+// runs for all of a thread's elements before any epi(i, j, sum, pre value) writes, so the
+// loads are in flight together rather than each waiting behind the previous element's
+// stores (which the compiler cannot prove do not alias them).
+template <bool kMfma, class Pre, class Epi>
+__device__ __forceinline__ void gemm2(int M, int N, int K, MatA A, MatB B, float* lds, Pre pre,
+                                      Epi epi) {
+    if constexpr (kMfma)
+        block_gemm_mfma(M, N, K, A, B, lds, pre, epi);
+    else
+        block_gemm_f32(M, N, K, A, B, lds, pre, epi);
+}
+
+struct NoPre {
+    __device__ int operator()(int, int) const { return 0; }
+};
+
+// An epilogue that loads nothing.
 template <bool kMfma, class Epi>
 __device__ __forceinline__ void gemm(int M, int N, int K, MatA A, MatB B, float* lds, Epi epi) {
-    if constexpr (kMfma)
-        block_gemm_mfma(M, N, K, A, B, lds, epi);
-    else
-        block_gemm(M, N, K, A, B, lds, epi);
+    gemm2<kMfma>(M, N, K, A, B, lds, NoPre{}, [&](int i, int j, float x, int) { epi(i, j, x); });
+}
+
+// For the linear path's fixed-size products.
+template <class Epi>
+__device__ __forceinline__ void block_gemm_f32(int M, int N, int K, MatA A, MatB B, float* lds,
+                                               Epi epi) {
+    gemm2<false>(M, N, K, A, B, lds, NoPre{}, [&](int i, int j, float x, int) { epi(i, j, x); });
 }
 
 }  // namespace generic

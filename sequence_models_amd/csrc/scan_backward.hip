@@ -52,6 +52,8 @@ using namespace generic;
 
 constexpr int kThreads = 256;
 
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f2_t;
+
 // Float offsets of the per-memory workspace regions of the reverse sweep.
 struct BwLayout {
     int64_t ca, cb, cp;                 // a_t, b_t, p_t for t = 0..C
@@ -203,11 +205,14 @@ __device__ __forceinline__ void key_path(const ScanArgs& a, const BwLayout& wl, 
         } else {
             float* R = ws + wl.rr;
             float* D = ws + wl.dl[L];
-            gemm<kMfma>(n, nout, nin, A, Bm, lds, [&](int i, int j, float z) {
-                const float r = z - load_io(a.v, bs.q + (c0 + i) * a.qs[1] + j, a.io);
-                R[i * nout + j] = r;
-                D[i * nout + j] = bias_grad(r, a.bias, a.bias_param);
-            });
+            gemm2<kMfma>(
+                n, nout, nin, A, Bm, lds,
+                [&](int i, int j) { return load_io(a.v, bs.q + (c0 + i) * a.qs[1] + j, a.io); },
+                [&](int i, int j, float z, float v) {
+                    const float r = z - v;
+                    R[i * nout + j] = r;
+                    D[i * nout + j] = bias_grad(r, a.bias, a.bias_param);
+                });
         }
     }
     for (int l = L; l >= 2; --l) {
@@ -215,11 +220,13 @@ __device__ __forceinline__ void key_path(const ScanArgs& a, const BwLayout& wl, 
         const float* Z = ws + wl.zk[l - 1];
         float* G = ws + wl.gk[l - 1];
         float* Dp = ws + wl.dl[l - 1];
-        gemm<kMfma>(n, nin, nout, MatA{ws + wl.dl[l], nout, 1, nullptr},
-                    MatB{theta + a.off[l], nin, 1}, lds, [&](int i, int j, float g) {
-                        G[i * nin + j] = g;
-                        Dp[i * nin + j] = g * silu_prime(Z[i * nin + j]);
-                    });
+        gemm2<kMfma>(n, nin, nout, MatA{ws + wl.dl[l], nout, 1, nullptr},
+                     MatB{theta + a.off[l], nin, 1}, lds,
+                     [&](int i, int j) { return Z[i * nin + j]; },
+                     [&](int i, int j, float g, float z) {
+                         G[i * nin + j] = g;
+                         Dp[i * nin + j] = g * silu_prime(z);
+                     });
     }
 }
 
@@ -243,7 +250,7 @@ __device__ __forceinline__ void block_sum3(float& x, float& y, float& z, float* 
 template <bool kMfma>
 __global__ void __launch_bounds__(kThreads) bwd_forward_kernel(BwdArgs A, BwLayout wl,
                                                                float* ckpt) {
-    __shared__ float lds_gemm[kGemmLds];
+    __shared__ __align__(16) float lds_gemm[kGemmLds];
     __shared__ float s_al[256], s_et[256], s_be[256];
     const ScanArgs& a = A.a;
     const int64_t seq = blockIdx.x;
@@ -280,16 +287,19 @@ __global__ void __launch_bounds__(kThreads) bwd_forward_kernel(BwdArgs A, BwLayo
             const int nin = a.n[l - 1], nout = a.n[l];
             const int64_t off = a.off[l];
             const MatB Hk{ws + wl.hk[l - 1], nin, 1};
-            gemm<kMfma>(nout, nin, n, MatA{ws + wl.dl[l], 1, nout, crow}, Hk, lds_gemm,
-                        [&](int i, int j, float x) {
-                            const int64_t o = off + (int64_t)i * nin + j;
-                            thn[o] = an * th[o] - bn * mo[o] - x;
-                        });
-            gemm<kMfma>(nout, nin, n, MatA{ws + wl.dl[l], 1, nout, wrow}, Hk, lds_gemm,
-                        [&](int i, int j, float x) {
-                            const int64_t o = off + (int64_t)i * nin + j;
-                            mon[o] = pn * mo[o] + x;
-                        });
+            gemm2<kMfma>(
+                nout, nin, n, MatA{ws + wl.dl[l], 1, nout, crow}, Hk, lds_gemm,
+                [&](int i, int j) {
+                    const int64_t o = off + (int64_t)i * nin + j;
+                    return f2_t{th[o], mo[o]};
+                },
+                [&](int i, int j, float x, f2_t t) {
+                    thn[off + (int64_t)i * nin + j] = an * t[0] - bn * t[1] - x;
+                });
+            gemm2<kMfma>(
+                nout, nin, n, MatA{ws + wl.dl[l], 1, nout, wrow}, Hk, lds_gemm,
+                [&](int i, int j) { return mo[off + (int64_t)i * nin + j]; },
+                [&](int i, int j, float x, float m) { mon[off + (int64_t)i * nin + j] = pn * m + x; });
         }
     }
 }
@@ -298,13 +308,14 @@ __global__ void __launch_bounds__(kThreads) bwd_forward_kernel(BwdArgs A, BwLayo
 template <bool kMfma>
 __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayout wl,
                                                                const float* ckpt) {
-    __shared__ float lds_gemm[kGemmLds];
+    __shared__ __align__(16) float lds_gemm[kGemmLds];
     __shared__ float s_al[256], s_et[256], s_be[256];
     __shared__ float s_ga[257], s_gb[257];          // cotangents of a_t, b_t (y path; t = n: chunk end)
     __shared__ float s_gcn[256], s_gwn[256];        // of c_{n,j}, w_{n,j}
     __shared__ float s_abar[257], s_bbar[257], s_pbar[257];
     __shared__ float s_red[12];
     __shared__ float s_gp;
+    __shared__ float s_ca[257], s_cb[257], s_crow[256], s_wrow[256];  // a_t, b_t, c_{n,j}, w_{n,j}
     const ScanArgs& a = A.a;
     const int64_t seq = blockIdx.x;
     const Bases bs = bases_of(a, seq);
@@ -355,6 +366,15 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayo
         __syncthreads();
         coefficients(wl, ws, C, n, s_al, s_et, s_be);
         __syncthreads();
+        for (int t = tid; t <= n; t += kThreads) {
+            s_ca[t] = ca[t];
+            s_cb[t] = cb[t];
+            if (t < n) {
+                s_crow[t] = cm[(int64_t)n * C + t];
+                s_wrow[t] = wm[(int64_t)n * C + t];
+            }
+        }
+        __syncthreads();
 
         // ---- recompute: key path, then the reads at the in-chunk weights
         key_path<kMfma>(a, wl, ws, th, bs, c0, n, lds_gemm);
@@ -363,24 +383,28 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayo
             const float* Hq = ws + wl.hq[l - 1];
             float* Am = ws + wl.am[l];
             float* Mq = ws + wl.mq[l];
-            gemm<kMfma>(n, n, nin, MatA{Hq, nin, 1, nullptr}, MatB{ws + wl.hk[l - 1], 1, nin},
-                        lds_gemm, [&](int i, int j, float x) {
-                            Am[i * C + j] = x;
-                            Mq[i * C + j] = (j < i) ? cm[(int64_t)i * C + j] * x : 0.0f;
-                        });
+            gemm2<kMfma>(n, n, nin, MatA{Hq, nin, 1, nullptr}, MatB{ws + wl.hk[l - 1], 1, nin},
+                         lds_gemm,
+                         [&](int i, int j) { return (j < i) ? cm[(int64_t)i * C + j] : 0.0f; },
+                         [&](int i, int j, float x, float c) {
+                             Am[i * C + j] = x;
+                             Mq[i * C + j] = c * x;
+                         });
             if (l == L) break;  // the output itself is not needed
             float* Z = ws + wl.zq[l];
             float* Hn = ws + wl.hq[l];
             gemm<kMfma>(n, nout, nin, MatA{Hq, nin, 1, nullptr}, MatB{th + a.off[l], 1, nin},
-                        lds_gemm, [&](int i, int j, float x) { Z[i * nout + j] = ca[i] * x; });
-            gemm<kMfma>(n, nout, nin, MatA{Hq, nin, 1, nullptr}, MatB{mo + a.off[l], 1, nin},
-                        lds_gemm, [&](int i, int j, float x) { Z[i * nout + j] -= cb[i] * x; });
-            gemm<kMfma>(n, nout, n, MatA{Mq, C, 1, nullptr}, MatB{ws + wl.dl[l], nout, 1},
-                        lds_gemm, [&](int i, int j, float x) {
-                            const float z = Z[i * nout + j] - x;
-                            Z[i * nout + j] = z;
-                            Hn[i * nout + j] = z * sigmoidf_(z);
-                        });
+                        lds_gemm, [&](int i, int j, float x) { Z[i * nout + j] = s_ca[i] * x; });
+            gemm2<kMfma>(n, nout, nin, MatA{Hq, nin, 1, nullptr}, MatB{mo + a.off[l], 1, nin},
+                         lds_gemm, [&](int i, int j) { return Z[i * nout + j]; },
+                         [&](int i, int j, float x, float z) { Z[i * nout + j] = z - s_cb[i] * x; });
+            gemm2<kMfma>(n, nout, n, MatA{Mq, C, 1, nullptr}, MatB{ws + wl.dl[l], nout, 1},
+                         lds_gemm, [&](int i, int j) { return Z[i * nout + j]; },
+                         [&](int i, int j, float x, float z0) {
+                             const float z = z0 - x;
+                             Z[i * nout + j] = z;
+                             Hn[i * nout + j] = z * sigmoidf_(z);
+                         });
         }
 
         // ---- query adjoint, layer L down to 1
@@ -391,37 +415,46 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayo
             const float* Am = ws + wl.am[l];
             float* Mb = ws + wl.mb[l];
             const bool first = (l == L);
-            gemm<kMfma>(n, n, nout, MatA{Dq, nout, 1, nullptr}, MatB{ws + wl.dl[l], 1, nout},
-                        lds_gemm, [&](int i, int j, float x) {
-                            const bool low = j < i;
-                            Mb[i * C + j] = low ? cm[(int64_t)i * C + j] * x : 0.0f;
-                            const float dc = low ? -x * Am[i * C + j] : 0.0f;
-                            if (first) gc[(int64_t)i * C + j] = dc;
-                            else gc[(int64_t)i * C + j] += dc;
-                        });
-            gemm<kMfma>(n, nin, nout, MatA{Dq, nout, 1, nullptr}, MatB{th + a.off[l], nin, 1},
-                        lds_gemm, [&](int i, int j, float x) {
-                            tmp[i * nin + j] = ca[i] * x;
-                            atomicAdd(&s_ga[i], x * Hq[i * nin + j]);
-                        });
-            gemm<kMfma>(n, nin, nout, MatA{Dq, nout, 1, nullptr}, MatB{mo + a.off[l], nin, 1},
-                        lds_gemm, [&](int i, int j, float x) {
-                            tmp[i * nin + j] -= cb[i] * x;
-                            atomicAdd(&s_gb[i], -x * Hq[i * nin + j]);
-                        });
+            gemm2<kMfma>(n, n, nout, MatA{Dq, nout, 1, nullptr}, MatB{ws + wl.dl[l], 1, nout},
+                         lds_gemm,
+                         [&](int i, int j) {
+                             const bool low = j < i;
+                             const int64_t o = (int64_t)i * C + j;
+                             return f32x4_t{low ? cm[o] : 0.0f, low ? Am[o] : 0.0f,
+                                            first ? 0.0f : gc[o], 0.0f};
+                         },
+                         [&](int i, int j, float x, f32x4_t u) {
+                             Mb[i * C + j] = u[0] * x;
+                             gc[(int64_t)i * C + j] = u[2] - x * u[1];
+                         });
+            gemm2<kMfma>(n, nin, nout, MatA{Dq, nout, 1, nullptr}, MatB{th + a.off[l], nin, 1},
+                         lds_gemm, [&](int i, int j) { return Hq[i * nin + j]; },
+                         [&](int i, int j, float x, float h) {
+                             tmp[i * nin + j] = s_ca[i] * x;
+                             atomicAdd(&s_ga[i], x * h);
+                         });
+            gemm2<kMfma>(n, nin, nout, MatA{Dq, nout, 1, nullptr}, MatB{mo + a.off[l], nin, 1},
+                         lds_gemm,
+                         [&](int i, int j) { return f2_t{tmp[i * nin + j], Hq[i * nin + j]}; },
+                         [&](int i, int j, float x, f2_t u) {
+                             tmp[i * nin + j] = u[0] - s_cb[i] * x;
+                             atomicAdd(&s_gb[i], -x * u[1]);
+                         });
             if (l > 1) {
                 const float* Zq = ws + wl.zq[l - 1];
                 float* Dn = ws + wl.dq[l - 1];
-                gemm<kMfma>(n, nin, n, MatA{Mb, C, 1, nullptr}, MatB{ws + wl.hk[l - 1], nin, 1},
-                            lds_gemm, [&](int i, int j, float x) {
-                                Dn[i * nin + j] = (tmp[i * nin + j] - x) * silu_prime(Zq[i * nin + j]);
-                            });
+                gemm2<kMfma>(n, nin, n, MatA{Mb, C, 1, nullptr}, MatB{ws + wl.hk[l - 1], nin, 1},
+                             lds_gemm,
+                             [&](int i, int j) { return f2_t{tmp[i * nin + j], Zq[i * nin + j]}; },
+                             [&](int i, int j, float x, f2_t u) {
+                                 Dn[i * nin + j] = (u[0] - x) * silu_prime(u[1]);
+                             });
             } else {
-                gemm<kMfma>(n, nin, n, MatA{Mb, C, 1, nullptr}, MatB{ws + wl.hk[0], nin, 1},
-                            lds_gemm, [&](int i, int j, float x) {
-                                store_io(A.dq, bs.q + (c0 + i) * a.qs[1] + j, a.io,
-                                         tmp[i * nin + j] - x);
-                            });
+                gemm2<kMfma>(n, nin, n, MatA{Mb, C, 1, nullptr}, MatB{ws + wl.hk[0], nin, 1},
+                             lds_gemm, [&](int i, int j) { return tmp[i * nin + j]; },
+                             [&](int i, int j, float x, float t) {
+                                 store_io(A.dq, bs.q + (c0 + i) * a.qs[1] + j, a.io, t - x);
+                             });
             }
         }
 
@@ -440,23 +473,23 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayo
                 s_gp = z;
             }
         }
-        const float* crow = cm + (int64_t)n * C;
-        const float* wrow = wm + (int64_t)n * C;
         for (int l = 1; l <= L; ++l) {
             const int nin = a.n[l - 1], nout = a.n[l];
             const float* Dl = ws + wl.dl[l];
             float* RZ = ws + wl.rz[l];
             const MatA Hk{ws + wl.hk[l - 1], nin, 1, nullptr};
-            gemm<kMfma>(n, nout, nin, Hk, MatB{Lt + a.off[l], 1, nin}, lds_gemm,
-                        [&](int i, int j, float x) {
-                            RZ[i * nout + j] = -crow[i] * x;
-                            atomicAdd(&s_gcn[i], -x * Dl[i * nout + j]);
-                        });
-            gemm<kMfma>(n, nout, nin, Hk, MatB{Ls + a.off[l], 1, nin}, lds_gemm,
-                        [&](int i, int j, float x) {
-                            RZ[i * nout + j] += wrow[i] * x;
-                            atomicAdd(&s_gwn[i], x * Dl[i * nout + j]);
-                        });
+            gemm2<kMfma>(n, nout, nin, Hk, MatB{Lt + a.off[l], 1, nin}, lds_gemm,
+                         [&](int i, int j) { return Dl[i * nout + j]; },
+                         [&](int i, int j, float x, float dl) {
+                             RZ[i * nout + j] = -s_crow[i] * x;
+                             atomicAdd(&s_gcn[i], -x * dl);
+                         });
+            gemm2<kMfma>(n, nout, nin, Hk, MatB{Ls + a.off[l], 1, nin}, lds_gemm,
+                         [&](int i, int j) { return f2_t{RZ[i * nout + j], Dl[i * nout + j]}; },
+                         [&](int i, int j, float x, f2_t u) {
+                             RZ[i * nout + j] = u[0] + s_wrow[i] * x;
+                             atomicAdd(&s_gwn[i], x * u[1]);
+                         });
         }
 
         // ---- tangent pass of the key path along U_j
@@ -464,17 +497,22 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayo
             const int nin = a.n[l - 1], nout = a.n[l];
             float* RZ = ws + wl.rz[l];
             if (l > 1)
-                gemm<kMfma>(n, nout, nin, MatA{ws + wl.rh[l - 1], nin, 1, nullptr},
-                            MatB{th + a.off[l], 1, nin}, lds_gemm,
-                            [&](int i, int j, float x) { RZ[i * nout + j] += x; });
+                gemm2<kMfma>(n, nout, nin, MatA{ws + wl.rh[l - 1], nin, 1, nullptr},
+                             MatB{th + a.off[l], 1, nin}, lds_gemm,
+                             [&](int i, int j) { return RZ[i * nout + j]; },
+                             [&](int i, int j, float x, float r) { RZ[i * nout + j] = r + x; });
             const float* Zk = l < L ? ws + wl.zk[l] : nullptr;
             float* RH = l < L ? ws + wl.rh[l] : nullptr;
-            gemm<kMfma>(n, nout, n, MatA{ws + wl.mq[l], 1, C, nullptr},
-                        MatB{ws + wl.dq[l], nout, 1}, lds_gemm, [&](int i, int j, float x) {
-                            const float rz = RZ[i * nout + j] - x;
-                            RZ[i * nout + j] = rz;
-                            if (RH) RH[i * nout + j] = rz * silu_prime(Zk[i * nout + j]);
-                        });
+            gemm2<kMfma>(n, nout, n, MatA{ws + wl.mq[l], 1, C, nullptr},
+                         MatB{ws + wl.dq[l], nout, 1}, lds_gemm,
+                         [&](int i, int j) {
+                             return f2_t{RZ[i * nout + j], Zk ? Zk[i * nout + j] : 0.0f};
+                         },
+                         [&](int i, int j, float x, f2_t u) {
+                             const float rz = u[0] - x;
+                             RZ[i * nout + j] = rz;
+                             if (RH) RH[i * nout + j] = rz * silu_prime(u[1]);
+                         });
         }
 
         // ---- tangent pass of its backward; dv, dk
@@ -494,29 +532,36 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayo
             const int nin = a.n[l - 1], nout = a.n[l];
             const float* Dl = ws + wl.dl[l];
             gemm<kMfma>(n, nin, nout, MatA{Dl, nout, 1, nullptr}, MatB{Lt + a.off[l], nin, 1},
-                        lds_gemm, [&](int i, int j, float x) { tmp[i * nin + j] = -crow[i] * x; });
-            gemm<kMfma>(n, nin, nout, MatA{Dl, nout, 1, nullptr}, MatB{Ls + a.off[l], nin, 1},
-                        lds_gemm, [&](int i, int j, float x) { tmp[i * nin + j] += wrow[i] * x; });
-            gemm<kMfma>(n, nin, n, MatA{ws + wl.mb[l], 1, C, nullptr},
-                        MatB{ws + wl.hq[l - 1], nin, 1}, lds_gemm,
-                        [&](int i, int j, float x) { tmp[i * nin + j] -= x; });
+                        lds_gemm, [&](int i, int j, float x) { tmp[i * nin + j] = -s_crow[i] * x; });
+            gemm2<kMfma>(n, nin, nout, MatA{Dl, nout, 1, nullptr}, MatB{Ls + a.off[l], nin, 1},
+                         lds_gemm, [&](int i, int j) { return tmp[i * nin + j]; },
+                         [&](int i, int j, float x, float t) { tmp[i * nin + j] = t + s_wrow[i] * x; });
+            gemm2<kMfma>(n, nin, n, MatA{ws + wl.mb[l], 1, C, nullptr},
+                         MatB{ws + wl.hq[l - 1], nin, 1}, lds_gemm,
+                         [&](int i, int j) { return tmp[i * nin + j]; },
+                         [&](int i, int j, float x, float t) { tmp[i * nin + j] = t - x; });
             if (l > 1) {
                 const float* Zk = ws + wl.zk[l - 1];
                 const float* Gk = ws + wl.gk[l - 1];
                 const float* RZp = ws + wl.rz[l - 1];
                 float* RDp = ws + wl.rd[l - 1];
-                gemm<kMfma>(n, nin, nout, MatA{ws + wl.rd[l], nout, 1, nullptr},
-                            MatB{th + a.off[l], nin, 1}, lds_gemm, [&](int i, int j, float x) {
-                                const int o = i * nin + j;
-                                const float z = Zk[o];
-                                RDp[o] = (tmp[o] + x) * silu_prime(z) + Gk[o] * silu_second(z) * RZp[o];
-                            });
+                gemm2<kMfma>(n, nin, nout, MatA{ws + wl.rd[l], nout, 1, nullptr},
+                             MatB{th + a.off[l], nin, 1}, lds_gemm,
+                             [&](int i, int j) {
+                                 const int o = i * nin + j;
+                                 return f32x4_t{tmp[o], Zk[o], Gk[o], RZp[o]};
+                             },
+                             [&](int i, int j, float x, f32x4_t u) {
+                                 RDp[i * nin + j] =
+                                     (u[0] + x) * silu_prime(u[1]) + u[2] * silu_second(u[1]) * u[3];
+                             });
             } else {
-                gemm<kMfma>(n, nin, nout, MatA{ws + wl.rd[1], nout, 1, nullptr},
-                            MatB{th + a.off[1], nin, 1}, lds_gemm, [&](int i, int j, float x) {
-                                store_io(A.dk, bs.q + (c0 + i) * a.qs[1] + j, a.io,
-                                         tmp[i * nin + j] + x);
-                            });
+                gemm2<kMfma>(n, nin, nout, MatA{ws + wl.rd[1], nout, 1, nullptr},
+                             MatB{th + a.off[1], nin, 1}, lds_gemm,
+                             [&](int i, int j) { return tmp[i * nin + j]; },
+                             [&](int i, int j, float x, float t) {
+                                 store_io(A.dk, bs.q + (c0 + i) * a.qs[1] + j, a.io, t + x);
+                             });
             }
         }
 
@@ -528,23 +573,30 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayo
                 float* Lt_l = Lt + a.off[l];
                 float* Ls_l = Ls + a.off[l];
                 const MatB Hq{ws + wl.hq[l - 1], nin, 1};
-                gemm<kMfma>(nout, nin, n, MatA{ws + wl.dq[l], 1, nout, cb}, Hq, lds_gemm,
-                            [&](int i, int j, float x) {
-                                const int64_t o = (int64_t)i * nin + j;
-                                Ls_l[o] = pn * Ls_l[o] - bn * Lt_l[o] - x;
-                            });
-                gemm<kMfma>(nout, nin, n, MatA{ws + wl.dq[l], 1, nout, ca}, Hq, lds_gemm,
-                            [&](int i, int j, float x) {
-                                const int64_t o = (int64_t)i * nin + j;
-                                Lt_l[o] = an * Lt_l[o] + x;
-                            });
-                gemm<kMfma>(nout, nin, n, MatA{ws + wl.rd[l], 1, nout, nullptr},
-                            MatB{ws + wl.hk[l - 1], nin, 1}, lds_gemm,
-                            [&](int i, int j, float x) { Lt_l[(int64_t)i * nin + j] += x; });
+                gemm2<kMfma>(nout, nin, n, MatA{ws + wl.dq[l], 1, nout, cb}, Hq, lds_gemm,
+                             [&](int i, int j) {
+                                 const int64_t o = (int64_t)i * nin + j;
+                                 return f2_t{Ls_l[o], Lt_l[o]};
+                             },
+                             [&](int i, int j, float x, f2_t u) {
+                                 Ls_l[(int64_t)i * nin + j] = pn * u[0] - bn * u[1] - x;
+                             });
+                gemm2<kMfma>(nout, nin, n, MatA{ws + wl.dq[l], 1, nout, ca}, Hq, lds_gemm,
+                             [&](int i, int j) { return Lt_l[(int64_t)i * nin + j]; },
+                             [&](int i, int j, float x, float t) {
+                                 Lt_l[(int64_t)i * nin + j] = an * t + x;
+                             });
+                gemm2<kMfma>(nout, nin, n, MatA{ws + wl.rd[l], 1, nout, nullptr},
+                             MatB{ws + wl.hk[l - 1], nin, 1}, lds_gemm,
+                             [&](int i, int j) { return Lt_l[(int64_t)i * nin + j]; },
+                             [&](int i, int j, float x, float t) { Lt_l[(int64_t)i * nin + j] = t + x; });
                 if (l > 1)
-                    gemm<kMfma>(nout, nin, n, MatA{ws + wl.dl[l], 1, nout, nullptr},
-                                MatB{ws + wl.rh[l - 1], nin, 1}, lds_gemm,
-                                [&](int i, int j, float x) { Lt_l[(int64_t)i * nin + j] += x; });
+                    gemm2<kMfma>(nout, nin, n, MatA{ws + wl.dl[l], 1, nout, nullptr},
+                                 MatB{ws + wl.rh[l - 1], nin, 1}, lds_gemm,
+                                 [&](int i, int j) { return Lt_l[(int64_t)i * nin + j]; },
+                                 [&](int i, int j, float x, float t) {
+                                     Lt_l[(int64_t)i * nin + j] = t + x;
+                                 });
             }
         }
 

@@ -79,7 +79,7 @@ struct Groups {
 template <bool kMfma>
 __global__ void __launch_bounds__(kThreads) scan_generic_kernel(ScanArgs a, WsLayout wl,
                                                                  Groups grp) {
-    __shared__ float lds_gemm[kGemmLds];
+    __shared__ __align__(16) float lds_gemm[kGemmLds];
     __shared__ float s_al[256], s_et[256], s_be[256];
 
     const int64_t wg = blockIdx.x;  // (memory, group) in group mode, else the memory
@@ -382,7 +382,7 @@ __host__ __device__ inline LinLayout lin_layout(int C, int d) {
 
 __global__ void __launch_bounds__(kThreads) linear_summary_kernel(ScanArgs a, Groups grp,
                                                                    LinLayout ll, float* sums) {
-    __shared__ float lds_gemm[kGemmLds];
+    __shared__ __align__(16) float lds_gemm[kGemmLds];
     __shared__ float s_al[256], s_et[256], s_be[256];
     __shared__ float s_tail[3];  // a_n, b_n, p of the chunk
     const int64_t wg = blockIdx.x;
@@ -448,20 +448,20 @@ __global__ void __launch_bounds__(kThreads) linear_summary_kernel(ScanArgs a, Gr
         }
         __syncthreads();
         // Gc, Gw, Hc, Hw: sums over the chunk's tokens of scaled outer products
-        block_gemm(d, d, n, MatA{Kst, 1, d, cv}, MatB{Kst, d, 1}, lds_gemm,
+        block_gemm_f32(d, d, n, MatA{Kst, 1, d, cv}, MatB{Kst, d, 1}, lds_gemm,
                    [&](int i, int j, float x) { Gc[i * d + j] = x; });
-        block_gemm(d, d, n, MatA{Kst, 1, d, wv}, MatB{Kst, d, 1}, lds_gemm,
+        block_gemm_f32(d, d, n, MatA{Kst, 1, d, wv}, MatB{Kst, d, 1}, lds_gemm,
                    [&](int i, int j, float x) { Gw[i * d + j] = x; });
-        block_gemm(d, d, n, MatA{Vst, 1, d, cv}, MatB{Kst, d, 1}, lds_gemm,
+        block_gemm_f32(d, d, n, MatA{Vst, 1, d, cv}, MatB{Kst, d, 1}, lds_gemm,
                    [&](int i, int j, float x) { Hc[i * d + j] = x; });
-        block_gemm(d, d, n, MatA{Vst, 1, d, wv}, MatB{Kst, d, 1}, lds_gemm,
+        block_gemm_f32(d, d, n, MatA{Vst, 1, d, wv}, MatB{Kst, d, 1}, lds_gemm,
                    [&](int i, int j, float x) { Hw[i * d + j] = x; });
         // the products of the composed map with this chunk's M
         const float* lhs[6] = {P11, P11, P21, P21, Q1, Q1};
         const float* rhs[6] = {Gc, Gw, Gc, Gw, Gc, Gw};
         for (int m = 0; m < 6; ++m) {
             float* Tm = z + ll.T[m];
-            block_gemm(d, d, d, MatA{lhs[m], d, 1, nullptr}, MatB{rhs[m], d, 1}, lds_gemm,
+            block_gemm_f32(d, d, d, MatA{lhs[m], d, 1, nullptr}, MatB{rhs[m], d, 1}, lds_gemm,
                        [&](int i, int j, float x) { Tm[i * d + j] = x; });
         }
         const float an = s_tail[0], bn = s_tail[1], pn = s_tail[2];
@@ -484,7 +484,7 @@ __global__ void __launch_bounds__(kThreads) linear_summary_kernel(ScanArgs a, Gr
 // X_0 = [theta0 | s0]; X_{g+1} = X_g P_g + Q_g = [W P11 + S P21 + Q1, W P12 + S P22 + Q2]
 __global__ void __launch_bounds__(kThreads) linear_combine_kernel(ScanArgs a, Groups grp,
                                                                    LinLayout ll, const float* sums) {
-    __shared__ float lds_gemm[kGemmLds];
+    __shared__ __align__(16) float lds_gemm[kGemmLds];
     const int64_t seq = blockIdx.x;
     const int64_t b = seq / a.H, h = seq % a.H;
     const int tid = threadIdx.x, d = a.n[0];
@@ -505,13 +505,13 @@ __global__ void __launch_bounds__(kThreads) linear_combine_kernel(ScanArgs a, Gr
         const float* z = sums + (seq * grp.G + g) * ll.per_group;
         const float *P11 = z + ll.P11, *P12 = z + ll.P12, *P21 = z + ll.P21, *P22 = z + ll.P22;
         const float *Q1 = z + ll.Q1, *Q2 = z + ll.Q2;
-        block_gemm(d, d, d, MatA{W, d, 1, nullptr}, MatB{P11, d, 1}, lds_gemm,
+        block_gemm_f32(d, d, d, MatA{W, d, 1, nullptr}, MatB{P11, d, 1}, lds_gemm,
                    [&](int i, int j, float x) { Wn[i * d + j] = x + Q1[i * d + j]; });
-        block_gemm(d, d, d, MatA{S, d, 1, nullptr}, MatB{P21, d, 1}, lds_gemm,
+        block_gemm_f32(d, d, d, MatA{S, d, 1, nullptr}, MatB{P21, d, 1}, lds_gemm,
                    [&](int i, int j, float x) { Wn[i * d + j] += x; });
-        block_gemm(d, d, d, MatA{W, d, 1, nullptr}, MatB{P12, d, 1}, lds_gemm,
+        block_gemm_f32(d, d, d, MatA{W, d, 1, nullptr}, MatB{P12, d, 1}, lds_gemm,
                    [&](int i, int j, float x) { Sn[i * d + j] = x + Q2[i * d + j]; });
-        block_gemm(d, d, d, MatA{S, d, 1, nullptr}, MatB{P22, d, 1}, lds_gemm,
+        block_gemm_f32(d, d, d, MatA{S, d, 1, nullptr}, MatB{P22, d, 1}, lds_gemm,
                    [&](int i, int j, float x) { Sn[i * d + j] += x; });
     }
 }

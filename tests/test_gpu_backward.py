@@ -190,10 +190,12 @@ def test_backward_empty_sequence_passes_state_cotangents_through():
 
 
 def test_backward_headline_shape_full_size_prefix_and_suffix():
-    """The 16-head, d = 64, 64-256-64, C = 64, T = 16384, batch 8 workload at full size (the
+    """The 16-head, d = 64, 64-256-64, C = 64, T = 16384, batch 8 shape at full size (the
     launch the bench times), checked through the prefix and suffix properties on sampled
-    memories."""
-    wl = synthetic.WORKLOADS["h16_d64_b8_t16k"]
+    memories; the suffix references must be far from zero for the check to mean anything."""
+    # the sustained gate mix (alpha = sigmoid(N(-7, 1))): with the workload's own gates the
+    # memory decays to ~0 long before T = 16384 and the suffix cotangents would be ~0 too
+    wl = synthetic.WORKLOADS["h16_d64_b8_t16k"].with_(alpha_mu=-7.0, name="h16_d64_b8_t16k_sustained")
     inp = synthetic.make_inputs(wl, 0)
     cot = synthetic.make_cotangents(wl, 0)
     dev = to_device(inp)
@@ -207,8 +209,18 @@ def test_backward_headline_shape_full_size_prefix_and_suffix():
     got = tm.scan_backward(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["eta"], dev["beta"],
                            dev["theta0"], dev["s0"], dy, C, wl.widths)
     torch.cuda.synchronize()
+    # one memory of this draw, (b, h) = (0, 4), diverges under the sustained gates in the
+    # fp64 oracle as well (its state overflows within the first thousand tokens); the
+    # exact-zero property is checked on every memory whose forward stays finite
+    _, thT, _ = tm.scan(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["eta"], dev["beta"],
+                        dev["theta0"], dev["s0"], C, wl.widths)
+    torch.cuda.synchronize()
+    finite = torch.isfinite(thT).all(dim=-1)  # [B, H]
+    assert all(bool(finite[b, h]) for b, h in pairs)
+    assert int(finite.sum()) >= finite.numel() - 2
     for n in NAMES[:6]:
-        assert not got[n][:, T0:].any(), n
+        past = got[n][:, T0:]
+        assert not past.transpose(1, 2)[finite].any(), n
     zero = np.zeros((1, len(pairs), wl.params))
     ref = scan_grad.scan_vjp(_gather(inp, pairs, 0, T0), C, wl.widths,
                              _gather_dy(cot, pairs, 0, T0), zero, zero)
@@ -224,6 +236,8 @@ def test_backward_headline_shape_full_size_prefix_and_suffix():
     dth = np.stack([cot.dtheta_T[b, h] for b, h in pairs])[None]
     dsT = np.stack([cot.ds_T[b, h] for b, h in pairs])[None]
     ref = scan_grad.scan_vjp(suf, C, wl.widths, _gather_dy(cot, pairs, start, T), dth, dsT)
+    for n in NAMES[:6]:
+        assert np.sqrt(np.mean(ref[n] ** 2)) > 1e-3, (n, "suffix reference has decayed")
     compare(wl, _pick(got, pairs, start, T), ref, f"suffix T1={T1}", names=NAMES[:6])
 
 
