@@ -137,122 +137,132 @@ __device__ void block_gemm_mfma(int M, int N, int K, MatA A, MatB B, float* lds,
     __syncthreads();
 }
 
-// fp32 workgroup GEMM, same contract, with 32-deep reduction steps, double-buffered in LDS:
-// the next step's global loads are in flight during the current step's FMAs, one barrier
-// per step.  Thread (ty, tx) = (tid / 16, tid % 16) owns rows 4 ty .. 4 ty + 3 and columns
-// 4 tx .. 4 tx + 3 of each 64 x 64 output tile, so every reduction index costs one 16-byte
-// LDS read per operand (A: four distinct addresses per wave, broadcast; B: 256 contiguous
-// bytes), and those reads run four reduction indices ahead of the FMAs.  Staging: eight
-// elements of A and eight of B per thread, consecutive threads on the operand's contiguous
-// dimension; out-of-range elements load a clamped in-range address and are zeroed when
-// written to LDS, so the loads carry no branches and issue back to back.
+// fp32 workgroup GEMM, same contract.  The product is one stream of steps -- every 64 x 64
+// output tile times every 32-deep slice of the reduction, tile by tile -- and each step's
+// operands are loaded two steps ahead, across tile boundaries, into registers, then written
+// to one of two LDS buffers after the current step's FMAs (one barrier per step).  An
+// output tile's epilogue operands (pre) are requested before its last step's products.  The
+// products run on the fp32 matrix cores (v_mfma_f32_16x16x4f32: fp32 operands, fp32
+// accumulation, the same precision as FMAs): wave w computes rows 16 w .. 16 w + 15 of the
+// tile against its four 16-column tiles, each lane reading one A and four B values from
+// LDS per 4-deep slice (lane l: row / column l % 16, reduction index l / 16; result rows
+// 4 (l / 16) .. + 3).  Staging: eight elements of A and eight of B per thread, consecutive
+// threads on the operand's contiguous dimension; out-of-range elements load a clamped
+// in-range address and are zeroed when written to LDS, so the loads carry no branches.
 template <class Pre, class Epi>
 __device__ void block_gemm_f32(int M, int N, int K, MatA A, MatB B, float* lds, Pre pre, Epi epi) {
     const int tid = threadIdx.x;
-    const int tx = tid & 15, ty = tid >> 4;
+    const int wv = tid >> 6, lr = tid & 15, lk = (tid & 63) >> 4;
     const bool a_kc = A.sk == 1, b_jc = B.sj == 1;
-    for (int i0 = 0; i0 < M; i0 += kTile) {
-        for (int j0 = 0; j0 < N; j0 += kTile) {
-            // raw loads (clamped addresses, no branches) into registers; validity and the
-            // k-scale are applied when the step is written to LDS, after the FMAs
-            float ra[8], rb[8], rs[8];
-            const bool scaled = A.kscale != nullptr;
-            auto load = [&](int k0) {
+    const bool scaled = A.kscale != nullptr;
+    // element offsets inside one operand (a per-memory slice, far below 2^32 elements):
+    // 32-bit arithmetic from the uniform base pointer
+    const unsigned asi = (unsigned)A.si, ask = (unsigned)A.sk, bsk = (unsigned)B.sk,
+                   bsj = (unsigned)B.sj;
+    const int tiles_n = (N + kTile - 1) / kTile;
+    const int steps = (K + kK2 - 1) / kK2;
+    const int total = ((M + kTile - 1) / kTile) * tiles_n * steps;
+    if (total == 0 || M <= 0 || N <= 0) {
+        __syncthreads();
+        return;
+    }
+    struct Stage {
+        float a[8], b[8], s[8];
+    };
+    auto origin = [&](int st, int& i0, int& j0, int& k0) {
+        const int t = st / steps;
+        k0 = (st - t * steps) * kK2;
+        i0 = (t / tiles_n) * kTile;
+        j0 = (t - (t / tiles_n) * tiles_n) * kTile;
+    };
+    auto load = [&](Stage& g, int st) {
+        int i0, j0, k0;
+        origin(st, i0, j0, k0);
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int e = tid + kGemmThreads * r;
-                    const int ii = a_kc ? e >> 5 : e & 63, ka = a_kc ? e & 31 : e >> 6;
-                    const int gi = i0 + ii, gka = k0 + ka;
-                    const int ci = gi < M ? gi : M - 1, cka = gka < K ? gka : K - 1;
-                    ra[r] = A.p[(int64_t)ci * A.si + (int64_t)cka * A.sk];
-                    if (scaled) rs[r] = A.kscale[cka];
-                    const int jj = b_jc ? e & 63 : e >> 5, kb = b_jc ? e >> 6 : e & 31;
-                    const int gj = j0 + jj, gkb = k0 + kb;
-                    const int cj = gj < N ? gj : N - 1, ckb = gkb < K ? gkb : K - 1;
-                    rb[r] = B.p[(int64_t)ckb * B.sk + (int64_t)cj * B.sj];
-                }
-            };
-            auto store = [&](int buf, int k0) {
-                float* As = lds + buf * kK2 * kLd2;
-                float* Bs = lds + (2 + buf) * kK2 * kLd2;
+        for (int r = 0; r < 8; ++r) {
+            const int e = tid + kGemmThreads * r;
+            const int ii = a_kc ? e >> 5 : e & 63, ka = a_kc ? e & 31 : e >> 6;
+            const int gi = i0 + ii, gka = k0 + ka;
+            const unsigned ci = gi < M ? gi : M - 1, cka = gka < K ? gka : K - 1;
+            g.a[r] = A.p[ci * asi + cka * ask];
+            if (scaled) g.s[r] = A.kscale[cka];
+            const int jj = b_jc ? e & 63 : e >> 5, kb = b_jc ? e >> 6 : e & 31;
+            const int gj = j0 + jj, gkb = k0 + kb;
+            const unsigned cj = gj < N ? gj : N - 1, ckb = gkb < K ? gkb : K - 1;
+            g.b[r] = B.p[ckb * bsk + cj * bsj];
+        }
+    };
+    auto store = [&](const Stage& g, int st) {
+        int i0, j0, k0;
+        origin(st, i0, j0, k0);
+        float* As = lds + (st & 1) * kK2 * kLd2;
+        float* Bs = lds + (2 + (st & 1)) * kK2 * kLd2;
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int e = tid + kGemmThreads * r;
-                    const int ii = a_kc ? e >> 5 : e & 63, ka = a_kc ? e & 31 : e >> 6;
-                    const float x = scaled ? ra[r] * rs[r] : ra[r];
-                    As[ka * kLd2 + ii] = (i0 + ii < M && k0 + ka < K) ? x : 0.0f;
-                    const int jj = b_jc ? e & 63 : e >> 5, kb = b_jc ? e >> 6 : e & 31;
-                    Bs[kb * kLd2 + jj] = (j0 + jj < N && k0 + kb < K) ? rb[r] : 0.0f;
-                }
-            };
-            float acc[4][4];
+        for (int r = 0; r < 8; ++r) {
+            const int e = tid + kGemmThreads * r;
+            const int ii = a_kc ? e >> 5 : e & 63, ka = a_kc ? e & 31 : e >> 6;
+            const float x = scaled ? g.a[r] * g.s[r] : g.a[r];
+            As[ka * kLd2 + ii] = (i0 + ii < M && k0 + ka < K) ? x : 0.0f;
+            const int jj = b_jc ? e & 63 : e >> 5, kb = b_jc ? e >> 6 : e & 31;
+            Bs[kb * kLd2 + jj] = (j0 + jj < N && k0 + kb < K) ? g.b[r] : 0.0f;
+        }
+    };
+    f32x4_t acc[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    decltype(pre(0, 0)) pv[4][4];
+    // step st: its operands are in LDS buffer st & 1; `freed` held them and now takes
+    // step st + 2's loads; `pending` holds step st + 1's, written to LDS after the FMAs
+    auto step = [&](int st, Stage& freed, Stage& pending) {
+        if (st + 2 < total) load(freed, st + 2);
+        int i0, j0, k0;
+        origin(st, i0, j0, k0);
+        const bool last = k0 + kK2 >= K;
+        if (last) {
 #pragma unroll
-                for (int c = 0; c < 4; ++c) acc[r][c] = 0.0f;
-            load(0);
-            store(0, 0);
-            __syncthreads();
-            int buf = 0;
-            for (int k0 = 0; k0 < K; k0 += kK2) {
-                const bool more = k0 + kK2 < K;
-                if (more) load(k0 + kK2);
-                const float* As = lds + buf * kK2 * kLd2 + 4 * ty;
-                const float* Bs = lds + (2 + buf) * kK2 * kLd2 + 4 * tx;
-                f32x4_t av[4], bv[4];
+            for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    av[u] = *reinterpret_cast<const f32x4_t*>(As + u * kLd2);
-                    bv[u] = *reinterpret_cast<const f32x4_t*>(Bs + u * kLd2);
-                }
-#pragma unroll 2
-                for (int kb = 0; kb < kK2; kb += 4) {
-                    f32x4_t an[4], bn[4];
-                    if (kb + 4 < kK2) {
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            an[u] = *reinterpret_cast<const f32x4_t*>(As + (kb + 4 + u) * kLd2);
-                            bn[u] = *reinterpret_cast<const f32x4_t*>(Bs + (kb + 4 + u) * kLd2);
-                        }
-                    }
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-#pragma unroll
-                            for (int c = 0; c < 4; ++c)
-                                acc[r][c] = fmaf(av[u][r], bv[u][c], acc[r][c]);
-                    if (kb + 4 < kK2) {
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            av[u] = an[u];
-                            bv[u] = bn[u];
-                        }
-                    }
-                }
-                if (more) store(buf ^ 1, k0 + kK2);
-                __syncthreads();
-                buf ^= 1;
-            }
-            // epilogue: every element's operand loads first, then the writes
-            decltype(pre(0, 0)) pv[4][4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int i = i0 + 4 * ty + r, j = j0 + 4 * tx + c;
-                    pv[r][c] = pre(i < M ? i : M - 1, j < N ? j : N - 1);
-                }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int i = i0 + 4 * ty + r, j = j0 + 4 * tx + c;
-                    if (i < M && j < N) epi(i, j, acc[r][c], pv[r][c]);
+                for (int r = 0; r < 4; ++r) {
+                    const int i = i0 + 16 * wv + 4 * lk + r, j = j0 + 16 * t + lr;
+                    pv[t][r] = pre(i < M ? i : M - 1, j < N ? j : N - 1);
                 }
         }
-    }
+        // fp32 MFMA (v_mfma_f32_16x16x4f32): wave w owns output rows 16 w .. 16 w + 15 of the
+        // tile against four 16-column tiles; per 4-deep slice lane (lr, lk) feeds
+        // A[16 w + lr][k] and B[k][16 t + lr] with k = 4 kg + lk
+        const float* As = lds + (st & 1) * kK2 * kLd2 + 16 * wv + lr;
+        const float* Bs = lds + (2 + (st & 1)) * kK2 * kLd2 + lr;
+#pragma unroll
+        for (int kg = 0; kg < kK2 / 4; ++kg) {
+            const int k = 4 * kg + lk;
+            const float a = As[k * kLd2];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Bs[k * kLd2 + 16 * t], acc[t], 0, 0, 0);
+        }
+        if (last) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = i0 + 16 * wv + 4 * lk + r, j = j0 + 16 * t + lr;
+                    if (i < M && j < N) epi(i, j, acc[t][r], pv[t][r]);
+                }
+                acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        if (st + 1 < total) store(pending, st + 1);
+        __syncthreads();
+    };
+    Stage g0, g1;
+    load(g0, 0);
+    if (total > 1) load(g1, 1);
+    store(g0, 0);
     __syncthreads();
+    for (int st = 0; st < total; st += 2) {
+        step(st, g0, g1);
+        if (st + 1 < total) step(st + 1, g1, g0);
+    }
 }
 
 // Epilogues in two parts: pre(i, j) loads what element (i, j) needs (any value type) and

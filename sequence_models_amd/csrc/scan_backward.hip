@@ -110,6 +110,9 @@ __host__ __device__ inline BwLayout bw_layout(int C, int L, const int* n) {
     return w;
 }
 
+// Floats per checkpoint half (theta or s): P rounded up to 16 bytes.
+__host__ __device__ inline int64_t ck_half(int64_t P) { return (P + 3) & ~int64_t(3); }
+
 __device__ __forceinline__ float silu_prime(float z) {
     const float s = sigmoidf_(z);
     return s * (1.0f + z * (1.0f - s));
@@ -258,23 +261,24 @@ __global__ void __launch_bounds__(kThreads) bwd_forward_kernel(BwdArgs A, BwLayo
     const int C = a.C, L = a.L;
     const int64_t P = a.P, nch = (a.T + C - 1) / C;
     float* ws = static_cast<float*>(a.ws) + seq * wl.per_seq;
-    float* ck = ckpt + seq * nch * 2 * P;
+    const int64_t PH = ck_half(P);
+    float* ck = ckpt + seq * nch * 2 * PH;
     {
         const float* th0 = a.theta0 + bs.b * a.s0s[0] + bs.h * a.s0s[1];
         const float* mo0 = a.s0 + bs.b * a.s0s[0] + bs.h * a.s0s[1];
         for (int64_t i = threadIdx.x; i < P; i += kThreads) {
             ck[i] = th0[i];
-            ck[P + i] = mo0[i];
+            ck[PH + i] = mo0[i];
         }
     }
     __syncthreads();
     for (int64_t ci = 0; ci + 1 < nch; ++ci) {
         const int64_t c0 = ci * C;
         const int n = C;  // every chunk but the last is full
-        const float* th = ck + ci * 2 * P;
-        const float* mo = th + P;
-        float* thn = ck + (ci + 1) * 2 * P;
-        float* mon = thn + P;
+        const float* th = ck + ci * 2 * PH;
+        const float* mo = th + PH;
+        float* thn = ck + (ci + 1) * 2 * PH;
+        float* mon = thn + PH;
         stage_keys(a, wl, ws, bs, c0, n, s_al, s_et, s_be);
         __syncthreads();
         coefficients(wl, ws, C, n, s_al, s_et, s_be);
@@ -323,7 +327,8 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayo
     const int C = a.C, L = a.L, d = a.n[0];
     const int64_t P = a.P, nch = (a.T + C - 1) / C;
     float* ws = static_cast<float*>(a.ws) + seq * wl.per_seq;
-    const float* ck = ckpt + seq * nch * 2 * P;
+    const int64_t PH = ck_half(P);
+    const float* ck = ckpt + seq * nch * 2 * PH;
     float* Lt = A.dtheta0 + bs.b * a.ss[0] + bs.h * a.ss[1];
     float* Ls = A.ds0 + bs.b * a.ss[0] + bs.h * a.ss[1];
     {
@@ -347,8 +352,8 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayo
     for (int64_t ci = nch - 1; ci >= 0; --ci) {
         const int64_t c0 = ci * C;
         const int n = (int)((a.T - c0) < C ? (a.T - c0) : C);
-        const float* th = ck + ci * 2 * P;
-        const float* mo = th + P;
+        const float* th = ck + ci * 2 * PH;
+        const float* mo = th + PH;
 
         // ---- stage: gates, K, Q, dY; clear the cotangent accumulators
         stage_keys(a, wl, ws, bs, c0, n, s_al, s_et, s_be);
@@ -460,8 +465,24 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayo
 
         // ---- chunk-end cotangents of the coefficients; U_l Hk_{l-1} starts RZ_l
         {
+            // 16-byte loads, four groups per thread in flight (every base is 16-byte aligned)
             float x = 0.0f, y = 0.0f, z = 0.0f;
-            for (int64_t i = tid; i < P; i += kThreads) {
+            const int64_t P4 = P >> 2;
+            const f32x4_t* Lt4 = reinterpret_cast<const f32x4_t*>(Lt);
+            const f32x4_t* Ls4 = reinterpret_cast<const f32x4_t*>(Ls);
+            const f32x4_t* th4 = reinterpret_cast<const f32x4_t*>(th);
+            const f32x4_t* mo4 = reinterpret_cast<const f32x4_t*>(mo);
+#pragma unroll 4
+            for (int64_t m = tid; m < P4; m += kThreads) {
+                const f32x4_t lt = Lt4[m], ls = Ls4[m], t = th4[m], u = mo4[m];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x = fmaf(lt[e], t[e], x);
+                    y = fmaf(lt[e], u[e], y);
+                    z = fmaf(ls[e], u[e], z);
+                }
+            }
+            for (int64_t i = 4 * P4 + tid; i < P; i += kThreads) {
                 x = fmaf(Lt[i], th[i], x);
                 y = fmaf(Lt[i], mo[i], y);
                 z = fmaf(Ls[i], mo[i], z);
@@ -669,7 +690,7 @@ __global__ void bwd_copy_kernel(BwdArgs A) {
 size_t scan_backward_workspace_bytes(const ScanArgs& a) {
     const BwLayout w = bw_layout(a.C, a.L, a.n);
     const int64_t nch = (a.T + a.C - 1) / a.C;
-    return (size_t)(a.B * a.H) * (size_t)(w.per_seq + nch * 2 * a.P) * sizeof(float);
+    return (size_t)(a.B * a.H) * (size_t)(w.per_seq + nch * 2 * ck_half(a.P)) * sizeof(float);
 }
 
 hipError_t launch_scan_backward(const BwdArgs& A, hipStream_t stream) {

@@ -328,7 +328,8 @@ def test_linear_memory_path_selection(monkeypatch):
 
 
 def test_backward_workspace_formula():
-    """Per memory: one (theta, s) checkpoint per chunk plus the reverse sweep's area --
+    """Per memory: one (theta, s) checkpoint per chunk (each half padded to 16 bytes) plus
+    the reverse sweep's area --
     coefficient rows a, b, p (C + 1 each), the (C + 1) x C matrices c, w and their
     cotangents, the C x n_l activations, errors and tangents of both paths, three C x C
     products per layer and one C x (max width) buffer, each rounded up to 64 floats."""
@@ -353,7 +354,7 @@ def test_backward_workspace_formula():
     d = _desc(B, T, H, 16, C, io=0)
     got = tm.lib.titans_mem_scan_backward_workspace_size(ctypes.byref(d),
                                                          ctypes.byref(tm.mlp_desc(widths)))
-    assert got == B * H * (per + nch * 2 * P) * 4
+    assert got == B * H * (per + nch * 2 * ((P + 3) // 4 * 4)) * 4
     assert tm.lib.titans_mem_scan_backward_workspace_size(
         ctypes.byref(_desc(T=0)), ctypes.byref(tm.mlp_desc(widths))) == 0
     bad = ctypes.c_size_t(-1).value

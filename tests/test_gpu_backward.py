@@ -93,13 +93,25 @@ def compare(wl, got, ref, label, bars=None, names=NAMES):
 
 
 @pytest.mark.parametrize("C", [1, 5, 8, 37])
-@pytest.mark.parametrize("widths", [(16, 16), (16, 32, 16), (8, 24, 12, 8)])
+@pytest.mark.parametrize("widths", [(16, 16), (16, 32, 16), (8, 24, 12, 8), (8, 5, 7, 8)])
 def test_backward_matches_oracle_fp32(widths, C):
+    """P = 131 for (8, 5, 7, 8): the state vectors end in a partial 16-byte group."""
     wl, inp, cot = _small(widths=widths, C=C)
     rng = np.random.default_rng(3)
     inp.s0 = (0.05 * rng.standard_normal(inp.theta0.shape)).astype(np.float32)
     log(f"case backward fp32 {widths} C={C}")
-    got = run_bwd(wl, to_device(inp), cot)
+    dev = to_device(inp)
+    P = wl.params
+    if P % 4:  # state rows must start 16 bytes apart: padded [.., P] views
+        pad = lambda a: torch.nn.functional.pad(torch.from_numpy(a).cuda(), (0, 4 - P % 4))[..., :P]
+        dev["theta0"], dev["s0"] = pad(inp.theta0), pad(inp.s0)
+        dth, dsT = pad(cot.dtheta_T), pad(cot.ds_T)
+        got = tm.scan_backward(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["eta"],
+                               dev["beta"], dev["theta0"], dev["s0"], _dy_dev(cot, wl.io), C,
+                               widths, dtheta_T=dth, ds_T=dsT)
+        assert got["theta0"].stride(1) % 4 == 0
+    else:
+        got = run_bwd(wl, dev, cot)
     torch.cuda.synchronize()
     ref = scan_grad.scan_vjp(_oracle_inputs(inp), C, widths, cot.dy_f32(), cot.dtheta_T,
                              cot.ds_T)
