@@ -232,14 +232,19 @@ __device__ void block_gemm_f32(int M, int N, int K, MatA A, MatB B, float* lds, 
         // A[16 w + lr][k] and B[k][16 t + lr] with k = 4 kg + lk
         const float* As = lds + (st & 1) * kK2 * kLd2 + 16 * wv + lr;
         const float* Bs = lds + (2 + (st & 1)) * kK2 * kLd2 + lr;
+        float fa[kK2 / 4], fb[kK2 / 4][4];  // the whole step's operands first: one LDS wait
 #pragma unroll
         for (int kg = 0; kg < kK2 / 4; ++kg) {
             const int k = 4 * kg + lk;
-            const float a = As[k * kLd2];
+            fa[kg] = As[k * kLd2];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) fb[kg][t] = Bs[k * kLd2 + 16 * t];
+        }
+#pragma unroll
+        for (int kg = 0; kg < kK2 / 4; ++kg)
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Bs[k * kLd2 + 16 * t], acc[t], 0, 0, 0);
-        }
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[kg], fb[kg][t], acc[t], 0, 0, 0);
         if (last) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {

@@ -138,6 +138,27 @@ __device__ __forceinline__ Bases bases_of(const ScanArgs& a, int64_t seq) {
     return r;
 }
 
+// rows c0 .. c0 + n - 1 of a [T, d] io-dtype operand (row stride rs from base) into
+// dst[n][d] as fp32; each thread issues its loads in groups of eight before storing any.
+__device__ __forceinline__ void stage_rows(float* dst, const void* src, int64_t base, int64_t rs,
+                                           int64_t c0, int n, int d, int io) {
+    const int total = n * d;
+    for (int e0 = threadIdx.x; e0 < total; e0 += 8 * kThreads) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            int e = e0 + u * kThreads;
+            e = e < total ? e : total - 1;
+            v[u] = load_io(src, base + (c0 + e / d) * rs + e % d, io);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + u * kThreads;
+            if (e < total) dst[e] = v[u];
+        }
+    }
+}
+
 // The chunk's gates into LDS and K into Hk_0.
 __device__ __forceinline__ void stage_keys(const ScanArgs& a, const BwLayout& wl, float* ws,
                                            const Bases& bs, int64_t c0, int n, float* s_al,
@@ -149,11 +170,7 @@ __device__ __forceinline__ void stage_keys(const ScanArgs& a, const BwLayout& wl
         s_et[t] = a.eta[gi];
         s_be[t] = a.beta[gi];
     }
-    float* Hk0 = ws + wl.hk[0];
-    for (int e = threadIdx.x; e < n * d; e += kThreads) {
-        const int t = e / d, c = e % d;
-        Hk0[e] = load_io(a.k, bs.q + (c0 + t) * a.qs[1] + c, a.io);
-    }
+    stage_rows(ws + wl.hk[0], a.k, bs.q, a.qs[1], c0, n, d, a.io);
 }
 
 // Coefficients of the chunk: thread j follows column j of c and w; thread 0 also writes
@@ -319,6 +336,7 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayo
     __shared__ float s_abar[257], s_bbar[257], s_pbar[257];
     __shared__ float s_red[12];
     __shared__ float s_gp;
+    __shared__ float s_dot[3];  // <Lt, theta_c>, <Lt, s_c>, <Ls, s_c> of the current chunk
     __shared__ float s_ca[257], s_cb[257], s_crow[256], s_wrow[256];  // a_t, b_t, c_{n,j}, w_{n,j}
     const ScanArgs& a = A.a;
     const int64_t seq = blockIdx.x;
@@ -348,6 +366,19 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayo
     float* gw = ws + wl.gw;
     float* tmp = ws + wl.tmp;
     __syncthreads();
+    {  // <Lt, theta_c>, <Lt, s_c>, <Ls, s_c> for the last chunk; later chunks get them
+       // from the carry that produces their (Lt, Ls)
+        const float* th = ck + (nch - 1) * 2 * PH;
+        const float* mo = th + PH;
+        float x = 0.0f, y = 0.0f, z = 0.0f;
+        for (int64_t i = tid; i < P; i += kThreads) {
+            x = fmaf(Lt[i], th[i], x);
+            y = fmaf(Lt[i], mo[i], y);
+            z = fmaf(Ls[i], mo[i], z);
+        }
+        block_sum3(x, y, z, s_red);
+        if (tid == 0) { s_dot[0] = x; s_dot[1] = y; s_dot[2] = z; }
+    }
 
     for (int64_t ci = nch - 1; ci >= 0; --ci) {
         const int64_t c0 = ci * C;
@@ -358,13 +389,8 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayo
         // ---- stage: gates, K, Q, dY; clear the cotangent accumulators
         stage_keys(a, wl, ws, bs, c0, n, s_al, s_et, s_be);
         {
-            float* Hq0 = ws + wl.hq[0];
-            float* DqL = ws + wl.dq[L];
-            for (int e = tid; e < n * d; e += kThreads) {
-                const int t = e / d, c = e % d;
-                Hq0[e] = load_io(a.q, bs.q + (c0 + t) * a.qs[1] + c, a.io);
-                DqL[e] = load_io(A.dy, bs.y + (c0 + t) * a.ys[1] + c, a.io);
-            }
+            stage_rows(ws + wl.hq[0], a.q, bs.q, a.qs[1], c0, n, d, a.io);
+            stage_rows(ws + wl.dq[L], A.dy, bs.y, a.ys[1], c0, n, d, a.io);
             for (int t = tid; t <= n; t += kThreads) { s_ga[t] = 0.0f; s_gb[t] = 0.0f; }
             for (int t = tid; t < n; t += kThreads) { s_gcn[t] = 0.0f; s_gwn[t] = 0.0f; }
         }
@@ -463,36 +489,12 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayo
             }
         }
 
-        // ---- chunk-end cotangents of the coefficients; U_l Hk_{l-1} starts RZ_l
-        {
-            // 16-byte loads, four groups per thread in flight (every base is 16-byte aligned)
-            float x = 0.0f, y = 0.0f, z = 0.0f;
-            const int64_t P4 = P >> 2;
-            const f32x4_t* Lt4 = reinterpret_cast<const f32x4_t*>(Lt);
-            const f32x4_t* Ls4 = reinterpret_cast<const f32x4_t*>(Ls);
-            const f32x4_t* th4 = reinterpret_cast<const f32x4_t*>(th);
-            const f32x4_t* mo4 = reinterpret_cast<const f32x4_t*>(mo);
-#pragma unroll 4
-            for (int64_t m = tid; m < P4; m += kThreads) {
-                const f32x4_t lt = Lt4[m], ls = Ls4[m], t = th4[m], u = mo4[m];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x = fmaf(lt[e], t[e], x);
-                    y = fmaf(lt[e], u[e], y);
-                    z = fmaf(ls[e], u[e], z);
-                }
-            }
-            for (int64_t i = 4 * P4 + tid; i < P; i += kThreads) {
-                x = fmaf(Lt[i], th[i], x);
-                y = fmaf(Lt[i], mo[i], y);
-                z = fmaf(Ls[i], mo[i], z);
-            }
-            block_sum3(x, y, z, s_red);
-            if (tid == 0) {
-                s_ga[n] += x;
-                s_gb[n] -= y;
-                s_gp = z;
-            }
+        // ---- chunk-end cotangents of the coefficients (the three state products were
+        // formed by the previous step's carry, or before the loop); U_l Hk_{l-1} starts RZ_l
+        if (tid == 0) {
+            s_ga[n] += s_dot[0];
+            s_gb[n] -= s_dot[1];
+            s_gp = s_dot[2];
         }
         for (int l = 1; l <= L; ++l) {
             const int nin = a.n[l - 1], nout = a.n[l];
@@ -587,37 +589,64 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayo
         }
 
         // ---- carry the state cotangents to the chunk start (Ls first: it reads the old Lt)
+        // the next chunk's state products ride along in the epilogues that write the final
+        // Ls and Lt values (its checkpoint is chunk ci - 1's)
         {
             const float an = ca[n], bn = cb[n], pn = cp[n];
+            const bool dots = ci > 0;
+            const float* thp = dots ? ck + (ci - 1) * 2 * PH : ck;
+            const float* mop = thp + PH;
+            float dx = 0.0f, dy = 0.0f, dz = 0.0f;
             for (int l = 1; l <= L; ++l) {
                 const int nin = a.n[l - 1], nout = a.n[l];
-                float* Lt_l = Lt + a.off[l];
-                float* Ls_l = Ls + a.off[l];
+                const int64_t off = a.off[l];
+                float* Lt_l = Lt + off;
+                float* Ls_l = Ls + off;
                 const MatB Hq{ws + wl.hq[l - 1], nin, 1};
                 gemm2<kMfma>(nout, nin, n, MatA{ws + wl.dq[l], 1, nout, cb}, Hq, lds_gemm,
                              [&](int i, int j) {
                                  const int64_t o = (int64_t)i * nin + j;
-                                 return f2_t{Ls_l[o], Lt_l[o]};
+                                 return f32x4_t{Ls_l[o], Lt_l[o], dots ? mop[off + o] : 0.0f, 0.0f};
                              },
-                             [&](int i, int j, float x, f2_t u) {
-                                 Ls_l[(int64_t)i * nin + j] = pn * u[0] - bn * u[1] - x;
+                             [&](int i, int j, float x, f32x4_t u) {
+                                 const float ls = pn * u[0] - bn * u[1] - x;
+                                 Ls_l[(int64_t)i * nin + j] = ls;
+                                 dz = fmaf(ls, u[2], dz);
                              });
                 gemm2<kMfma>(nout, nin, n, MatA{ws + wl.dq[l], 1, nout, ca}, Hq, lds_gemm,
                              [&](int i, int j) { return Lt_l[(int64_t)i * nin + j]; },
                              [&](int i, int j, float x, float t) {
                                  Lt_l[(int64_t)i * nin + j] = an * t + x;
                              });
-                gemm2<kMfma>(nout, nin, n, MatA{ws + wl.rd[l], 1, nout, nullptr},
-                             MatB{ws + wl.hk[l - 1], nin, 1}, lds_gemm,
-                             [&](int i, int j) { return Lt_l[(int64_t)i * nin + j]; },
-                             [&](int i, int j, float x, float t) { Lt_l[(int64_t)i * nin + j] = t + x; });
-                if (l > 1)
-                    gemm2<kMfma>(nout, nin, n, MatA{ws + wl.dl[l], 1, nout, nullptr},
-                                 MatB{ws + wl.rh[l - 1], nin, 1}, lds_gemm,
+                const bool fin1 = l == 1;  // the layer's last product: fold in the dots
+                auto pre_fin = [&](int i, int j) {
+                    const int64_t o = (int64_t)i * nin + j;
+                    return f32x4_t{Lt_l[o], dots ? thp[off + o] : 0.0f, dots ? mop[off + o] : 0.0f,
+                                   0.0f};
+                };
+                auto epi_fin = [&](int i, int j, float x, f32x4_t u) {
+                    const float lt = u[0] + x;
+                    Lt_l[(int64_t)i * nin + j] = lt;
+                    dx = fmaf(lt, u[1], dx);
+                    dy = fmaf(lt, u[2], dy);
+                };
+                if (fin1) {
+                    gemm2<kMfma>(nout, nin, n, MatA{ws + wl.rd[l], 1, nout, nullptr},
+                                 MatB{ws + wl.hk[l - 1], nin, 1}, lds_gemm, pre_fin, epi_fin);
+                } else {
+                    gemm2<kMfma>(nout, nin, n, MatA{ws + wl.rd[l], 1, nout, nullptr},
+                                 MatB{ws + wl.hk[l - 1], nin, 1}, lds_gemm,
                                  [&](int i, int j) { return Lt_l[(int64_t)i * nin + j]; },
                                  [&](int i, int j, float x, float t) {
                                      Lt_l[(int64_t)i * nin + j] = t + x;
                                  });
+                    gemm2<kMfma>(nout, nin, n, MatA{ws + wl.dl[l], 1, nout, nullptr},
+                                 MatB{ws + wl.rh[l - 1], nin, 1}, lds_gemm, pre_fin, epi_fin);
+                }
+            }
+            if (dots) {
+                block_sum3(dx, dy, dz, s_red);
+                if (tid == 0) { s_dot[0] = dx; s_dot[1] = dy; s_dot[2] = dz; }
             }
         }
 
@@ -626,12 +655,23 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(BwdArgs A, BwLayo
             const int j = tid;
             float cr = s_gcn[j], wr = s_gwn[j];
             gc[(int64_t)n * C + j] = cr;
-            for (int t = n - 1; t >= 0; --t) {
-                wr = fmaf(s_et[t], cr, wr);                       // of w_{t+1,j}, complete
-                gw[(int64_t)(t + 1) * C + j] = wr;
-                cr = gc[(int64_t)t * C + j] + (1.0f - s_al[t]) * cr;  // of c_{t,j}
-                gc[(int64_t)t * C + j] = cr;
-                wr *= s_be[t];
+            for (int t0 = n - 1; t0 >= 0; t0 -= 8) {
+                float yv[8];  // the y-path terms of eight rows, loaded before any store
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int t = t0 - u;
+                    yv[u] = gc[(int64_t)(t >= 0 ? t : 0) * C + j];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int t = t0 - u;
+                    if (t < 0) break;
+                    wr = fmaf(s_et[t], cr, wr);                   // of w_{t+1,j}, complete
+                    gw[(int64_t)(t + 1) * C + j] = wr;
+                    cr = yv[u] + (1.0f - s_al[t]) * cr;           // of c_{t,j}
+                    gc[(int64_t)t * C + j] = cr;
+                    wr *= s_be[t];
+                }
             }
         }
         if (tid == kThreads - 1) {  // cotangents of a_t, b_t, p_t
