@@ -20,7 +20,8 @@ biases: the same scan with the Huber (delta 0.5) and l_p (p 3) attentional biase
 surprise: titans_mem_scan_surprise (the scan plus each token's gradient norm).
 backward: titans_mem_scan_backward (cotangents of every input for seeded output
 cotangents) on the same inputs, with its own roofline: the products of the checkpointing
-forward sweep and the reverse chunk loop (bwd_alg_flops_per_token_head) on fp32 FMAs.
+forward sweep and the reverse chunk loop (bwd_alg_flops_per_token_head) on the fp32
+matrix cores.
 """
 from __future__ import annotations
 
@@ -218,8 +219,9 @@ def bench_surprise(tm, torch, t, wl, out, steps, warmup):
 
 def bench_backward(tm, torch, t, wl, seed, steps, warmup):
     """titans_mem_scan_backward on the same inputs with seeded output cotangents (its own
-    line): tokens/s and the fp32-FMA roofline of its two kernels (checkpointing forward
-    sweep, reverse chunk loop), timed together by HIP events around the call."""
+    line): tokens/s and the roofline of its two kernels (checkpointing forward sweep,
+    reverse chunk loop) against the fp32 matrix-core peak their products run on, timed
+    together by HIP events around the call."""
     import synthetic
 
     cot = synthetic.make_cotangents(wl, seed)
@@ -254,8 +256,8 @@ def bench_backward(tm, torch, t, wl, seed, steps, warmup):
     del ws
     return {"ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "steps": steps,
             "workspace_bytes": n, "kernels": "bwd_forward_kernel + bwd_reverse_kernel",
-            "roofline": {"bound": "alu", "achieved": tf, "peak": PEAKS["valu_f32"],
-                         "unit": "TFLOP/s", "frac": tf / PEAKS["valu_f32"],
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAKS["mfma_f32"],
+                         "unit": "TFLOP/s", "frac": tf / PEAKS["mfma_f32"],
                          "alg_flops_per_launch": flops}}
 
 
@@ -347,9 +349,12 @@ def main():
     elif path.endswith("_mfma"):  # bf16 MFMA products, fp32 accumulation
         kernel = KERNELS[path.rsplit("_", 1)[0]]
         bound, peak, dtype = "mfma", PEAKS["mfma_bf16"], "bf16"
-    else:  # fp32 FMAs on the vector ALUs
-        kernel = KERNELS[path.rsplit("_", 1)[0]]
+    elif path.startswith("phased"):  # fp32 FMAs on the vector ALUs
+        kernel = KERNELS["phased"]
         bound, peak, dtype = "alu", PEAKS["valu_f32"], "f32"
+    else:  # generic / linear fp32: products on the fp32 matrix cores
+        kernel = KERNELS[path.rsplit("_", 1)[0]]
+        bound, peak, dtype = "mfma", PEAKS["mfma_f32"], "f32"
     parallelism = {
         "fused": "one GPU; two workgroups (one XCD) per (batch row, head) memory",
         "phased": "one GPU; every chunk product split into 64x64 tiles of all memories, "
