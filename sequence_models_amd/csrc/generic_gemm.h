@@ -175,9 +175,28 @@ __device__ void block_gemm_f32(int M, int N, int K, MatA A, MatB B, float* lds, 
         i0 = (t / tiles_n) * kTile;
         j0 = (t - (t / tiles_n) * tiles_n) * kTile;
     };
+    // staging element r of this thread: A (ii, ka) and B (kb, jj), linear in r
+    const int a_ii0 = a_kc ? tid >> 5 : tid & 63, a_ka0 = a_kc ? tid & 31 : tid >> 6;
+    const int b_jj0 = b_jc ? tid & 63 : tid >> 5, b_kb0 = b_jc ? tid >> 6 : tid & 31;
+    const unsigned a_off0 = a_ii0 * asi + a_ka0 * ask, b_off0 = b_kb0 * bsk + b_jj0 * bsj;
+    const unsigned a_dr = a_kc ? 8 * asi : 4 * ask, b_dr = b_jc ? 4 * bsk : 8 * bsj;
+    auto interior = [&](int i0, int j0, int k0) {
+        return i0 + kTile <= M && j0 + kTile <= N && k0 + kK2 <= K;
+    };
     auto load = [&](Stage& g, int st) {
         int i0, j0, k0;
         origin(st, i0, j0, k0);
+        if (interior(i0, j0, k0)) {  // uniform: no clamps, offsets linear in r
+            const float* pa = A.p + (i0 * asi + k0 * ask + a_off0);
+            const float* pb = B.p + (k0 * bsk + j0 * bsj + b_off0);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                g.a[r] = pa[r * a_dr];
+                g.b[r] = pb[r * b_dr];
+                if (scaled) g.s[r] = A.kscale[k0 + a_ka0 + (a_kc ? 0 : 4 * r)];
+            }
+            return;
+        }
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int e = tid + kGemmThreads * r;
@@ -197,6 +216,17 @@ __device__ void block_gemm_f32(int M, int N, int K, MatA A, MatB B, float* lds, 
         origin(st, i0, j0, k0);
         float* As = lds + (st & 1) * kK2 * kLd2;
         float* Bs = lds + (2 + (st & 1)) * kK2 * kLd2;
+        if (interior(i0, j0, k0)) {
+            float* pa = As + a_ka0 * kLd2 + a_ii0;
+            float* pb = Bs + b_kb0 * kLd2 + b_jj0;
+            const int sa = a_kc ? 8 : 4 * kLd2, sb = b_jc ? 4 * kLd2 : 8;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                pa[r * sa] = scaled ? g.a[r] * g.s[r] : g.a[r];
+                pb[r * sb] = g.b[r];
+            }
+            return;
+        }
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int e = tid + kGemmThreads * r;
@@ -230,15 +260,14 @@ __device__ void block_gemm_f32(int M, int N, int K, MatA A, MatB B, float* lds, 
         // fp32 MFMA (v_mfma_f32_16x16x4f32): wave w owns output rows 16 w .. 16 w + 15 of the
         // tile against four 16-column tiles; per 4-deep slice lane (lr, lk) feeds
         // A[16 w + lr][k] and B[k][16 t + lr] with k = 4 kg + lk
-        const float* As = lds + (st & 1) * kK2 * kLd2 + 16 * wv + lr;
-        const float* Bs = lds + (2 + (st & 1)) * kK2 * kLd2 + lr;
+        const float* As = lds + (st & 1) * kK2 * kLd2 + lk * kLd2 + 16 * wv + lr;
+        const float* Bs = lds + (2 + (st & 1)) * kK2 * kLd2 + lk * kLd2 + lr;
         float fa[kK2 / 4], fb[kK2 / 4][4];  // the whole step's operands first: one LDS wait
 #pragma unroll
         for (int kg = 0; kg < kK2 / 4; ++kg) {
-            const int k = 4 * kg + lk;
-            fa[kg] = As[k * kLd2];
+            fa[kg] = As[4 * kg * kLd2];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) fb[kg][t] = Bs[k * kLd2 + 16 * t];
+            for (int t = 0; t < 4; ++t) fb[kg][t] = Bs[4 * kg * kLd2 + 16 * t];
         }
 #pragma unroll
         for (int kg = 0; kg < kK2 / 4; ++kg)

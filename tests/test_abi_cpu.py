@@ -328,33 +328,34 @@ def test_linear_memory_path_selection(monkeypatch):
 
 
 def test_backward_workspace_formula():
-    """Per memory: one (theta, s) checkpoint per chunk (each half padded to 16 bytes) plus
-    the reverse sweep's area --
-    coefficient rows a, b, p (C + 1 each), the (C + 1) x C matrices c, w and their
-    cotangents, the C x n_l activations, errors and tangents of both paths, three C x C
-    products per layer and one C x (max width) buffer, each rounded up to 64 floats."""
+    """Per memory: one (theta, s) checkpoint per chunk (each half padded to 16 bytes), then
+    for one segment of up to 64 chunks a record and a working area per chunk, and one
+    working area for the sequential part -- every region rounded up to 64 floats."""
     r64 = lambda x: (x + 63) // 64 * 64
     widths = (16, 32, 16)
     B, T, H, C = 2, 300, 3, 64
     n = widths
     L = len(n) - 1
     P = 16 * 32 * 2
-    per = 3 * r64(C + 1) + 4 * r64((C + 1) * C)
-    per += sum(r64(C * n[l]) for l in range(L))            # Hk_0..L-1
-    per += 2 * sum(r64(C * n[l]) for l in range(1, L))     # Zk, Gk
-    per += sum(r64(C * n[l]) for l in range(1, L + 1))     # Delta
-    per += r64(C * n[L])                                   # residual
-    per += sum(r64(C * n[l]) for l in range(L))            # Hq
-    per += sum(r64(C * n[l]) for l in range(1, L))         # Zq
-    per += 2 * sum(r64(C * n[l]) for l in range(1, L + 1)) # Dq, RZ
-    per += sum(r64(C * n[l]) for l in range(1, L))         # RH
-    per += sum(r64(C * n[l]) for l in range(1, L + 1))     # RDelta
-    per += 3 * L * r64(C * C) + r64(C * 32)
+    PH = (P + 3) // 4 * 4
+    maxw = max(n)
+    hid = sum(r64(C * n[l]) for l in range(1, L))          # layers 1..L-1
+    out = sum(r64(C * n[l]) for l in range(1, L + 1))      # layers 1..L
+    low = sum(r64(C * n[l]) for l in range(L))             # layers 0..L-1
+    rec = (5 * r64(C + 1) + 4 * r64((C + 1) * C) + 64 + low + 2 * hid + out
+           + r64(C * n[L]) + 2 * r64(C * n[0]) + 2 * r64(PH))
+    chunk = low + hid + out + 3 * L * r64(C * C) + out + hid + out + r64(C * maxw)
+    seq = out + hid + out + r64(C * maxw) + 64
     nch = (T + C - 1) // C
+    seg = min(nch, 64)
     d = _desc(B, T, H, 16, C, io=0)
     got = tm.lib.titans_mem_scan_backward_workspace_size(ctypes.byref(d),
                                                          ctypes.byref(tm.mlp_desc(widths)))
-    assert got == B * H * (per + nch * 2 * ((P + 3) // 4 * 4)) * 4
+    assert got == B * H * (nch * 2 * PH + seg * (rec + chunk) + seq) * 4
+    long_ = _desc(1, 64 * 200, 2, 16, C, io=0)  # 200 chunks: segments of 64
+    got = tm.lib.titans_mem_scan_backward_workspace_size(ctypes.byref(long_),
+                                                         ctypes.byref(tm.mlp_desc(widths)))
+    assert got == 2 * (200 * 2 * PH + 64 * (rec + chunk) + seq) * 4
     assert tm.lib.titans_mem_scan_backward_workspace_size(
         ctypes.byref(_desc(T=0)), ctypes.byref(tm.mlp_desc(widths))) == 0
     bad = ctypes.c_size_t(-1).value
