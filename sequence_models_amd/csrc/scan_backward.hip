@@ -39,18 +39,20 @@
 //   gates      the coefficient recurrence run backwards.
 //
 // Everything but the U^e terms, the chunk-end products and the carry's use of (Lt, Ls) is
-// independent of the later chunks, so the work is split:
-//   bwd_forward_kernel   one workgroup per memory: the chunk carries forward, storing
-//                        every chunk's start state (theta_c, s_c)
-//   bwd_chunk_kernel     one workgroup per (memory, chunk), all chunks of a segment at
-//                        once: recompute, query adjoint (dq final), the U^y halves of the
-//                        tangent passes (dk, dv partial), dLt, dLs -> a per-chunk record
-//   bwd_seq_kernel       one workgroup per memory, the segment's chunks in reverse: the
-//                        chain through (Lt, Ls) -- chunk-end products, the U^e halves
-//                        (dk, dv final), the carry
-//   bwd_gate_kernel      one workgroup per (memory, chunk): the gate cotangents
-// Segments of chunks run from the last to the first, so the records need room for one
-// segment only.
+// independent of the later chunks, so the work is split into three parts over segments of
+// chunks:
+//   chunk part   one workgroup per (memory, chunk), all chunks of a segment at once:
+//                recompute, query adjoint (dq final), the U^y halves of the tangent passes
+//                (dk, dv partial), dLt, dLs -> a per-chunk record
+//   seq part     one workgroup per memory, the segment's chunks in reverse: the chain
+//                through (Lt, Ls) -- chunk-end products, the U^e halves (dk, dv final), the
+//                carry
+//   gate part    one workgroup per (memory, chunk): the gate cotangents
+// after bwd_forward_kernel (one workgroup per memory: the chunk carries forward, storing
+// every chunk's start state).  Segments run from the last to the first; one launch of
+// bwd_step_kernel runs the seq part of segment s beside the chunk part of segment s - 1 and
+// the gate part of segment s + 1 (three record buffers), so the per-chunk work fills the
+// compute units the B*H sequential chains leave idle.
 #include <hip/hip_runtime.h>
 
 #include "generic_gemm.h"
@@ -63,7 +65,8 @@ namespace {
 using namespace generic;
 
 constexpr int kThreads = 256;
-constexpr int kSegChunks = 64;  // chunks per segment (records and scratch for this many)
+constexpr int kSegChunks = 32;  // chunks per segment
+constexpr int kRecBufs = 3;     // record buffers: the segments of the three parts of a launch
 
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f2_t;
 
@@ -177,19 +180,26 @@ __host__ __device__ inline SeqScr seq_scr(int C, int L, const int* n) {
     return w;
 }
 
-// Where everything lives in the caller's workspace, and the segment a launch works on.
+// One part's share of a launch: its segment and the workgroups that run it.
+struct Role {
+    int64_t first;         // the segment's first chunk
+    int count;             // its chunks (0: the part does not run in this launch)
+    float* rec;            // its record buffer: [nseq][seg] records
+    int64_t blk0;          // first workgroup of the part
+};
+
+// Where everything lives in the caller's workspace, and what a launch works on.
 struct Plan {
     RecLayout rl;
     ChunkScr cl;
     SeqScr sl;
     int64_t nch, seg;      // chunks per memory, chunks per segment
     float* ckpt;           // [nseq][nch][2 PH]
-    float* rec;            // [nseq][seg] records
-    float* cscr;           // [nseq][seg] chunk-kernel areas
-    float* sscr;           // [nseq] seq-kernel areas
-    int64_t first;         // this launch's first chunk
-    int count;             // and its number of chunks
-    int last_segment;      // 1: the segment holding the sequence's last chunk
+    float* recs;           // kRecBufs x [nseq][seg] records
+    float* cscr;           // [nseq][seg] chunk-part areas
+    float* sscr;           // [nseq] seq-part areas
+    Role rs, rc, rg;       // seq, chunk and gate parts
+    int last_segment;      // the seq part's segment holds the sequence's last chunk
 };
 
 inline Plan make_plan(const ScanArgs& a) {
@@ -204,16 +214,16 @@ inline Plan make_plan(const ScanArgs& a) {
 
 inline size_t plan_floats(const ScanArgs& a, const Plan& p) {
     const int64_t nseq = a.B * a.H;
-    return (size_t)nseq * (size_t)(p.nch * 2 * ck_half(a.P) + p.seg * (p.rl.per + p.cl.per) +
-                                   p.sl.per);
+    return (size_t)nseq * (size_t)(p.nch * 2 * ck_half(a.P) +
+                                   p.seg * (kRecBufs * p.rl.per + p.cl.per) + p.sl.per);
 }
 
 inline void place(const ScanArgs& a, Plan& p) {
     const int64_t nseq = a.B * a.H;
     float* base = static_cast<float*>(a.ws);
     p.ckpt = base;
-    p.rec = p.ckpt + nseq * p.nch * 2 * ck_half(a.P);
-    p.cscr = p.rec + nseq * p.seg * p.rl.per;
+    p.recs = p.ckpt + nseq * p.nch * 2 * ck_half(a.P);
+    p.cscr = p.recs + kRecBufs * nseq * p.seg * p.rl.per;
     p.sscr = p.cscr + nseq * p.seg * p.cl.per;
 }
 
@@ -380,7 +390,7 @@ __global__ void __launch_bounds__(kThreads) bwd_forward_kernel(BwdArgs A, Plan p
     const Bases bs = bases_of(a, seq);
     const int C = a.C, L = a.L, d = a.n[0];
     const int64_t P = a.P, nch = pl.nch, PH = ck_half(P);
-    float* ws = pl.rec + seq * pl.seg * rl.per;  // this memory's first record as working area
+    float* ws = pl.recs + seq * pl.seg * rl.per;  // a record of this memory as working area
     float* ck = pl.ckpt + seq * nch * 2 * PH;
     {
         const float* th0 = a.theta0 + bs.b * a.s0s[0] + bs.h * a.s0s[1];
@@ -431,17 +441,17 @@ __global__ void __launch_bounds__(kThreads) bwd_forward_kernel(BwdArgs A, Plan p
 // ---------------------------------------------------------------- per-chunk part
 
 template <bool kMfma>
-__global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(BwdArgs A, Plan pl) {
-    __shared__ __align__(16) float lds_gemm[kGemmLds];
+__device__ __forceinline__ void chunk_part(const BwdArgs& A, const Plan& pl, int64_t blk,
+                                           float* lds_gemm) {
     __shared__ float s_al[256], s_et[256], s_be[256];
     __shared__ float s_ga[257], s_gb[257];  // U^y-path cotangents of a_t, b_t
     __shared__ float s_ca[257], s_cb[257];
     const ScanArgs& a = A.a;
     const RecLayout& rl = pl.rl;
     const ChunkScr& cl = pl.cl;
-    const int64_t seq = blockIdx.x / pl.count;
-    const int cs = (int)(blockIdx.x - seq * pl.count);  // chunk within the segment
-    const int64_t ci = pl.first + cs;
+    const int64_t seq = blk / pl.rc.count;
+    const int cs = (int)(blk - seq * pl.rc.count);  // chunk within the segment
+    const int64_t ci = pl.rc.first + cs;
     const Bases bs = bases_of(a, seq);
     const int tid = threadIdx.x;
     const int C = a.C, L = a.L, d = a.n[0];
@@ -450,7 +460,7 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(BwdArgs A, Plan pl)
     const int n = (int)((a.T - c0) < C ? (a.T - c0) : C);
     const float* th = pl.ckpt + (seq * pl.nch + ci) * 2 * PH;
     const float* mo = th + PH;
-    float* rec = pl.rec + (seq * pl.seg + cs) * rl.per;
+    float* rec = pl.rc.rec + (seq * pl.seg + cs) * rl.per;
     float* ws = pl.cscr + (seq * pl.seg + cs) * cl.per;
     float* cm = rec + rl.cm;
     float* gc = rec + rl.gc;
@@ -645,8 +655,8 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(BwdArgs A, Plan pl)
 // ---------------------------------------------------------------- the chain through (Lt, Ls)
 
 template <bool kMfma>
-__global__ void __launch_bounds__(kThreads) bwd_seq_kernel(BwdArgs A, Plan pl) {
-    __shared__ __align__(16) float lds_gemm[kGemmLds];
+__device__ __forceinline__ void seq_part(const BwdArgs& A, const Plan& pl, int64_t seq,
+                                         float* lds_gemm) {
     __shared__ float s_gcn[256], s_gwn[256];     // cotangents of c_{n,j}, w_{n,j}
     __shared__ float s_crow[256], s_wrow[256];   // c_{n,j}, w_{n,j}
     __shared__ float s_red[12];
@@ -654,7 +664,6 @@ __global__ void __launch_bounds__(kThreads) bwd_seq_kernel(BwdArgs A, Plan pl) {
     const ScanArgs& a = A.a;
     const RecLayout& rl = pl.rl;
     const SeqScr& sl = pl.sl;
-    const int64_t seq = blockIdx.x;
     const Bases bs = bases_of(a, seq);
     const int tid = threadIdx.x;
     const int C = a.C, L = a.L, d = a.n[0];
@@ -687,12 +696,12 @@ __global__ void __launch_bounds__(kThreads) bwd_seq_kernel(BwdArgs A, Plan pl) {
     }
     __syncthreads();
 
-    for (int cs = pl.count - 1; cs >= 0; --cs) {
-        const int64_t ci = pl.first + cs;
+    for (int cs = pl.rs.count - 1; cs >= 0; --cs) {
+        const int64_t ci = pl.rs.first + cs;
         const int64_t c0 = ci * C;
         const int n = (int)((a.T - c0) < C ? (a.T - c0) : C);
         const float* th = ck + ci * 2 * PH;
-        float* rec = pl.rec + (seq * pl.seg + cs) * rl.per;
+        float* rec = pl.rs.rec + (seq * pl.seg + cs) * rl.per;
         for (int t = tid; t < n; t += kThreads) {
             s_gcn[t] = 0.0f;
             s_gwn[t] = 0.0f;
@@ -865,20 +874,20 @@ __global__ void __launch_bounds__(kThreads) bwd_seq_kernel(BwdArgs A, Plan pl) {
 
 // ---------------------------------------------------------------- gate cotangents
 
-__global__ void __launch_bounds__(kThreads) bwd_gate_kernel(BwdArgs A, Plan pl) {
+__device__ __forceinline__ void gate_part(const BwdArgs& A, const Plan& pl, int64_t blk) {
     __shared__ float s_al[256], s_et[256], s_be[256];
     __shared__ float s_abar[257], s_bbar[257], s_pbar[257];
     const ScanArgs& a = A.a;
     const RecLayout& rl = pl.rl;
-    const int64_t seq = blockIdx.x / pl.count;
-    const int cs = (int)(blockIdx.x - seq * pl.count);
-    const int64_t ci = pl.first + cs;
+    const int64_t seq = blk / pl.rg.count;
+    const int cs = (int)(blk - seq * pl.rg.count);
+    const int64_t ci = pl.rg.first + cs;
     const Bases bs = bases_of(a, seq);
     const int tid = threadIdx.x;
     const int C = a.C;
     const int64_t c0 = ci * C;
     const int n = (int)((a.T - c0) < C ? (a.T - c0) : C);
-    float* rec = pl.rec + (seq * pl.seg + cs) * rl.per;
+    float* rec = pl.rg.rec + (seq * pl.seg + cs) * rl.per;
     const float* ca = rec + rl.ca;
     const float* cb = rec + rl.cb;
     const float* cp = rec + rl.cp;
@@ -944,6 +953,20 @@ __global__ void __launch_bounds__(kThreads) bwd_gate_kernel(BwdArgs A, Plan pl) 
     }
 }
 
+// One launch: the seq part (workgroups 0 .. B*H - 1 when it runs) beside the chunk and gate
+// parts of other segments.  Each workgroup takes exactly one role and every role ends.
+template <bool kMfma>
+__global__ void __launch_bounds__(kThreads, 2) bwd_step_kernel(BwdArgs A, Plan pl) {
+    __shared__ __align__(16) float lds_gemm[kGemmLds];
+    const int64_t blk = blockIdx.x;
+    if (pl.rs.count > 0 && blk >= pl.rs.blk0 && blk < pl.rc.blk0)
+        seq_part<kMfma>(A, pl, blk - pl.rs.blk0, lds_gemm);
+    else if (pl.rc.count > 0 && blk >= pl.rc.blk0 && blk < pl.rg.blk0)
+        chunk_part<kMfma>(A, pl, blk - pl.rc.blk0, lds_gemm);
+    else if (pl.rg.count > 0 && blk >= pl.rg.blk0)
+        gate_part(A, pl, blk - pl.rg.blk0);
+}
+
 // T = 0: the state cotangents pass through.
 __global__ void bwd_copy_kernel(BwdArgs A) {
     const ScanArgs& a = A.a;
@@ -979,14 +1002,30 @@ hipError_t launch_scan_backward(const BwdArgs& A, hipStream_t stream) {
     place(a, p);
     bwd_forward_kernel<false><<<dim3((unsigned)nseq), kThreads, 0, stream>>>(A, p);
     const int64_t nseg = (p.nch + p.seg - 1) / p.seg;
-    for (int64_t s = nseg - 1; s >= 0; --s) {
-        p.first = s * p.seg;
-        p.count = (int)((p.nch - p.first) < p.seg ? (p.nch - p.first) : p.seg);
+    // role of segment s (count 0 outside 0 .. nseg-1); segment s keeps record buffer s % 3
+    auto role = [&](int64_t s) {
+        Role r{};
+        if (s < 0 || s >= nseg) return r;
+        r.first = s * p.seg;
+        r.count = (int)((p.nch - r.first) < p.seg ? (p.nch - r.first) : p.seg);
+        r.rec = p.recs + (s % kRecBufs) * nseq * p.seg * p.rl.per;
+        return r;
+    };
+    // launch i (i = 0 .. nseg + 1): seq part of segment nseg - i, chunk part of segment
+    // nseg - 1 - i, gate part of segment nseg + 1 - i
+    for (int64_t i = 0; i <= nseg + 1; ++i) {
+        const int64_t s = nseg - i;
+        p.rs = role(s);
+        p.rc = role(s - 1);
+        p.rg = role(s + 1);
         p.last_segment = s == nseg - 1;
-        const unsigned blocks = (unsigned)(nseq * p.count);
-        bwd_chunk_kernel<false><<<dim3(blocks), kThreads, 0, stream>>>(A, p);
-        bwd_seq_kernel<false><<<dim3((unsigned)nseq), kThreads, 0, stream>>>(A, p);
-        bwd_gate_kernel<<<dim3(blocks), kThreads, 0, stream>>>(A, p);
+        const int64_t ns = p.rs.count ? nseq : 0;
+        p.rs.blk0 = 0;
+        p.rc.blk0 = ns;
+        p.rg.blk0 = ns + nseq * p.rc.count;
+        const int64_t blocks = p.rg.blk0 + nseq * p.rg.count;
+        if (blocks == 0) continue;
+        bwd_step_kernel<false><<<dim3((unsigned)blocks), kThreads, 0, stream>>>(A, p);
     }
     return hipGetLastError();
 }

@@ -329,8 +329,8 @@ def test_linear_memory_path_selection(monkeypatch):
 
 def test_backward_workspace_formula():
     """Per memory: one (theta, s) checkpoint per chunk (each half padded to 16 bytes), then
-    for one segment of up to 64 chunks a record and a working area per chunk, and one
-    working area for the sequential part -- every region rounded up to 64 floats."""
+    for segments of up to 32 chunks three record buffers and one working area per chunk, and
+    one working area for the sequential part -- every region rounded up to 64 floats."""
     r64 = lambda x: (x + 63) // 64 * 64
     widths = (16, 32, 16)
     B, T, H, C = 2, 300, 3, 64
@@ -347,15 +347,15 @@ def test_backward_workspace_formula():
     chunk = low + hid + out + 3 * L * r64(C * C) + out + hid + out + r64(C * maxw)
     seq = out + hid + out + r64(C * maxw) + 64
     nch = (T + C - 1) // C
-    seg = min(nch, 64)
+    seg = min(nch, 32)
     d = _desc(B, T, H, 16, C, io=0)
     got = tm.lib.titans_mem_scan_backward_workspace_size(ctypes.byref(d),
                                                          ctypes.byref(tm.mlp_desc(widths)))
-    assert got == B * H * (nch * 2 * PH + seg * (rec + chunk) + seq) * 4
-    long_ = _desc(1, 64 * 200, 2, 16, C, io=0)  # 200 chunks: segments of 64
+    assert got == B * H * (nch * 2 * PH + seg * (3 * rec + chunk) + seq) * 4
+    long_ = _desc(1, 64 * 200, 2, 16, C, io=0)  # 200 chunks: segments of 32
     got = tm.lib.titans_mem_scan_backward_workspace_size(ctypes.byref(long_),
                                                          ctypes.byref(tm.mlp_desc(widths)))
-    assert got == 2 * (200 * 2 * PH + 64 * (rec + chunk) + seq) * 4
+    assert got == 2 * (200 * 2 * PH + 32 * (3 * rec + chunk) + seq) * 4
     assert tm.lib.titans_mem_scan_backward_workspace_size(
         ctypes.byref(_desc(T=0)), ctypes.byref(tm.mlp_desc(widths))) == 0
     bad = ctypes.c_size_t(-1).value
