@@ -133,6 +133,20 @@ def test_backward_matches_oracle_bf16(widths, C, T, B, H):
     compare(wl, got, ref, f"bf16 {widths} C={C} T={T}")
 
 
+@pytest.mark.parametrize("widths,C,T", [((16, 32, 16), 128, 300), ((16, 24, 16), 256, 600),
+                                        ((16, 40, 24, 32, 16), 16, 70), ((8, 16, 8), 4, 4 * 70)])
+def test_backward_long_chunks_deep_memories_and_many_segments(widths, C, T):
+    """C = 128 / 256 (partial last chunk), a four-layer memory, and 70 chunks of 4 tokens:
+    three segments of the sequential part, so its state products cross launches."""
+    wl, inp, cot = _small(widths=widths, B=1, T=T, H=2, C=C, seed=C + T)
+    log(f"case backward {widths} C={C} T={T}")
+    got = run_bwd(wl, to_device(inp), cot)
+    torch.cuda.synchronize()
+    ref = scan_grad.scan_vjp(_oracle_inputs(inp), C, widths, cot.dy_f32(), cot.dtheta_T,
+                             cot.ds_T)
+    compare(wl, got, ref, f"{widths} C={C} T={T}")
+
+
 @pytest.mark.parametrize("bias", [("huber", 0.5), ("lp", 3.0), ("lp", 2.0)])
 def test_backward_attentional_bias(bias):
     wl, inp, cot = _small(widths=(16, 32, 16), C=8, T=40, seed=11)
