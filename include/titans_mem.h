@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define TITANS_MEM_ABI_VERSION 3
+#define TITANS_MEM_ABI_VERSION 4
 #define TITANS_MAX_LAYERS 4
 
 typedef enum {
@@ -255,6 +255,71 @@ const char* titans_mem_retrieve_path(const titans_scan_desc* desc, const titans_
  */
 titans_status titans_mem_retrieve(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
                                   const void* q, const float* theta, void* y, void* stream);
+
+/*
+ * ------------------------------------------------------------------ MAG block
+ * One Titans block with the memory as a gate (the lowest.today summary, section
+ * "Varianti dell'Architettura Titans", memory as gate; the 0h-n0.github.io
+ * explainer, section "3つのアーキテクチャ変種"): sliding-window attention is the
+ * short-term branch, the neural memory the long-term branch, and the memory's
+ * read gates the attention output.  The pages fix the gate; the projections are
+ * the plainest reading.  With D = H d (d = width[0] = width[L] of the memory):
+ *
+ *   [q | k | v | g] = x W_in^T               per token; W_in [3D + 3H, D]
+ *   q, k            scaled to unit L2 norm per (token, head); v as is
+ *   alpha_h = sigmoid(g[h] + b[h]), eta_h = eta_scale sigmoid(g[H+h] + b[H+h]),
+ *   beta_h  = sigmoid(g[2H+h] + b[2H+h])
+ *   y_mem           the memory scan (titans_mem_scan, squared-error bias) of
+ *                   q, k, v, alpha, eta, beta from (theta0, s0), read before write
+ *   y_attn          per head, softmax(q.k / sqrt(d)) attention over the `window`
+ *                   most recent tokens, the token itself included (causal)
+ *   out             (sigmoid(y_mem) * y_attn) W_out^T;  W_out [D, D]
+ *
+ * Precision: x, weights, out bf16; projections, scores and sums accumulate in
+ * fp32; q, k, v, y_mem, the attention probabilities and the gated output are
+ * rounded to bf16 where they are stored; the memory state is fp32.
+ */
+typedef struct {
+    int64_t batch;      /* B >= 0 */
+    int64_t seq_len;    /* T >= 0 */
+    int64_t heads;      /* H >= 1; H d <= 65536 */
+    int32_t chunk;      /* memory chunk length C >= 1 */
+    int32_t window;     /* attention window W >= 1 (W >= T: full causal attention) */
+    float eta_scale;    /* finite, >= 0 */
+    int32_t reserved;   /* must be 0 */
+} titans_mag_desc;
+
+/* Workspace bytes titans_mag_forward needs (0 when B T = 0); SIZE_MAX if the arguments
+ * are invalid.  It holds the fp32 projection [B T, 3D + 3H (rounded up to 4)], bf16 q, k,
+ * v, y_mem and the gated output [B, T, H, d], the fp32 gates [B, T, H] and the memory
+ * scan's own workspace. */
+size_t titans_mag_workspace_size(const titans_mag_desc* desc, const titans_mlp_desc* mlp);
+
+/*
+ * Forward pass of one MAG block.  All pointers are device memory, all tensors
+ * contiguous (row-major, last dimension innermost):
+ *   x        bf16 [B, T, D]                        16-byte aligned
+ *   w_in     bf16 [3D + 3H, D] rows: q features h*d..h*d+d-1 of head h (rows 0..D-1),
+ *            then k (D..2D-1), v (2D..3D-1), then the gate logits alpha_0..alpha_{H-1},
+ *            eta_0.., beta_0..                     16-byte aligned
+ *   b_gate   fp32 [3H], the gate biases in the same order
+ *   w_out    bf16 [D, D] (out features x in features)   16-byte aligned
+ *   theta0, s0    fp32 [B, H, P] initial memory and momentum (16-byte aligned)
+ *   out      bf16 [B, T, D]                        8-byte aligned
+ *   theta_T, s_T  fp32 [B, H, P] memory and momentum after the last token
+ *   workspace     titans_mag_workspace_size bytes, 256-byte aligned (may be NULL
+ *                 when that size is 0)
+ * No output or the workspace may overlap an input or another output.  The memory
+ * must satisfy titans_mem_scan's shape limits for bf16 I/O, and d must be 32, 64
+ * or 128 (else TITANS_ERR_UNSUPPORTED).  With T = 0 the state passes through;
+ * with B = 0 nothing is done.  Zero q or k rows (before normalization) give NaN,
+ * as the norm's definition does.
+ */
+titans_status titans_mag_forward(const titans_mag_desc* desc, const titans_mlp_desc* mlp,
+                                 const void* x, const void* w_in, const float* b_gate,
+                                 const void* w_out, const float* theta0, const float* s0,
+                                 void* out, float* theta_T, float* s_T,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,8 @@ at import time -- there is no fallback.
     scan_backward(q, k, v, alpha, eta, beta, theta0, s0, dy, chunk, widths,
                   dtheta_T=None, ds_T=None) -> cotangents of every input
     retrieve(q, theta, widths) -> y
+    mag_forward(x, w_in, b_gate, w_out, theta0, s0, chunk, window, widths, eta_scale)
+                  -> (out, theta_T, s_T)    one MAG block (memory as gate)
 """
 from __future__ import annotations
 
@@ -17,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["scan", "scan_backward", "scan_backward_workspace_size", "retrieve", "scan_workspace_size", "scan_path", "retrieve_path", "param_count", "TitansError", "LIB_PATH",
+__all__ = ["mag_forward", "mag_workspace_size", "MagDesc", "scan", "scan_backward", "scan_backward_workspace_size", "retrieve", "scan_workspace_size", "scan_path", "retrieve_path", "param_count", "TitansError", "LIB_PATH",
            "lib", "ScanDesc", "MlpDesc", "MAX_LAYERS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtitans_mem.so")
@@ -39,6 +41,12 @@ class ScanDesc(ctypes.Structure):
                 ("gate_stride", ctypes.c_int64 * 3), ("state_stride", ctypes.c_int64 * 2),
                 ("state0_stride", ctypes.c_int64 * 2), ("bias", ctypes.c_int32),
                 ("bias_param", ctypes.c_float)]
+
+
+class MagDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64), ("heads", ctypes.c_int64),
+                ("chunk", ctypes.c_int32), ("window", ctypes.c_int32), ("eta_scale", ctypes.c_float),
+                ("reserved", ctypes.c_int32)]
 
 
 BIASES = {"l2": 0, "huber": 1, "lp": 2}
@@ -75,6 +83,11 @@ lib.titans_mem_scan_backward_workspace_size.argtypes = [ctypes.POINTER(ScanDesc)
 lib.titans_mem_scan_backward.restype = ctypes.c_int
 lib.titans_mem_scan_backward.argtypes = ([ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)]
                                          + [_vp] * 20 + [ctypes.c_size_t, _vp])
+lib.titans_mag_workspace_size.restype = ctypes.c_size_t
+lib.titans_mag_workspace_size.argtypes = [ctypes.POINTER(MagDesc), ctypes.POINTER(MlpDesc)]
+lib.titans_mag_forward.restype = ctypes.c_int
+lib.titans_mag_forward.argtypes = ([ctypes.POINTER(MagDesc), ctypes.POINTER(MlpDesc)] + [_vp] * 10
+                                   + [ctypes.c_size_t, _vp])
 lib.titans_mem_retrieve.restype = ctypes.c_int
 lib.titans_mem_retrieve.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc), _vp, _vp,
                                     _vp, _vp]
@@ -359,3 +372,60 @@ def retrieve(q, theta, widths, *, y=None):
     _check(lib.titans_mem_retrieve(ctypes.byref(desc), ctypes.byref(mlp_desc(widths)), _ptr(q),
                                    _ptr(theta), _ptr(y), _stream()))
     return y
+
+
+def _mag_desc(x, widths, chunk, window, eta_scale) -> MagDesc:
+    B, T, D = x.shape
+    d = widths[0]
+    if D % d:
+        raise ValueError(f"model width {D} is not a multiple of the head width {d}")
+    return MagDesc(B, T, D // d, int(chunk), int(window), float(eta_scale), 0)
+
+
+def mag_workspace_size(x, chunk, window, widths, eta_scale=1.0) -> int:
+    """Workspace bytes of mag_forward for x [B, T, D] (raises on invalid arguments)."""
+    n = lib.titans_mag_workspace_size(ctypes.byref(_mag_desc(x, widths, chunk, window, eta_scale)),
+                                      ctypes.byref(mlp_desc(widths)))
+    if n == ctypes.c_size_t(-1).value:
+        raise TitansError(-1, lib.titans_last_error().decode())
+    return int(n)
+
+
+def mag_forward(x, w_in, b_gate, w_out, theta0, s0, chunk, window, widths, eta_scale, *,
+                out=None, theta_T=None, s_T=None, workspace=None):
+    """One MAG block on the current stream (titans_mag_forward).
+
+    x [B, T, D] bf16; w_in [3D + 3H, D] bf16 (q, k, v rows, then alpha, eta, beta gate
+    rows); b_gate [3H] float32; w_out [D, D] bf16; theta0, s0 [B, H, P] float32, with
+    H = D / widths[0].  Every tensor contiguous.  Returns (out [B, T, D] bf16, theta_T,
+    s_T [B, H, P])."""
+    B, T, D = x.shape
+    d = widths[0]
+    H = D // d
+    P = param_count(widths)
+    if out is None:
+        out = torch.empty((B, T, D), dtype=torch.bfloat16, device=x.device)
+    if theta_T is None:
+        theta_T = torch.empty((B, H, P), dtype=torch.float32, device=x.device)
+    if s_T is None:
+        s_T = torch.empty((B, H, P), dtype=torch.float32, device=x.device)
+    shapes = {"x": (x, torch.bfloat16, (B, T, D)), "w_in": (w_in, torch.bfloat16, (3 * D + 3 * H, D)),
+              "b_gate": (b_gate, torch.float32, (3 * H,)), "w_out": (w_out, torch.bfloat16, (D, D)),
+              "theta0": (theta0, torch.float32, (B, H, P)), "s0": (s0, torch.float32, (B, H, P)),
+              "out": (out, torch.bfloat16, (B, T, D)), "theta_T": (theta_T, torch.float32, (B, H, P)),
+              "s_T": (s_T, torch.float32, (B, H, P))}
+    for name, (t, dt, shape) in shapes.items():
+        if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {shape}")
+    desc = _mag_desc(x, widths, chunk, window, eta_scale)
+    mlp = mlp_desc(widths)
+    if workspace is None:
+        n = lib.titans_mag_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+        if n == ctypes.c_size_t(-1).value:
+            n = 0  # the call below reports the argument error
+        workspace = torch.empty(int(n), dtype=torch.uint8, device=x.device) if n else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.titans_mag_forward(ctypes.byref(desc), ctypes.byref(mlp), _ptr(x), _ptr(w_in),
+                                  _ptr(b_gate), _ptr(w_out), _ptr(theta0), _ptr(s0), _ptr(out),
+                                  _ptr(theta_T), _ptr(s_T), _ptr(workspace), ws_bytes, _stream()))
+    return out, theta_T, s_T

@@ -668,4 +668,177 @@ titans_status titans_mem_retrieve(const titans_scan_desc* desc, const titans_mlp
     return TITANS_OK;
 }
 
+// ---------------------------------------------------------------- MAG block
+
+static Span contiguous(const void* p, size_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{lo, p ? lo + bytes : lo};
+}
+
+// The memory scan of the block: bf16 [B, T, H, d] q / k / v / y, [B, T, H] gates,
+// contiguous [B, H, P] states, the squared-error bias.
+static titans_scan_desc mag_scan_desc(const titans_mag_desc* desc, int d, int64_t P) {
+    titans_scan_desc s{};
+    const int64_t B = desc->batch, T = desc->seq_len, H = desc->heads, D = H * d;
+    s.batch = B;
+    s.seq_len = T;
+    s.heads = H;
+    s.chunk = desc->chunk;
+    s.io_dtype = TITANS_BF16;
+    s.qkv_stride[0] = s.y_stride[0] = T * D;
+    s.qkv_stride[1] = s.y_stride[1] = D;
+    s.qkv_stride[2] = s.y_stride[2] = d;
+    s.gate_stride[0] = T * H;
+    s.gate_stride[1] = H;
+    s.gate_stride[2] = 1;
+    s.state_stride[0] = s.state0_stride[0] = H * P;
+    s.state_stride[1] = s.state0_stride[1] = P;
+    s.bias = TITANS_BIAS_L2;
+    s.bias_param = 0.f;
+    return s;
+}
+
+static titans_status prepare_mag(const titans_mag_desc* desc, const titans_mlp_desc* mlp,
+                                 titans::MagArgs& g, titans_scan_desc& sd, titans::ScanArgs& a) {
+    if (!desc || !mlp) return fail(TITANS_ERR_INVALID_ARGUMENT, "desc and mlp must be non-NULL");
+    if (desc->batch < 0 || desc->seq_len < 0 || desc->heads < 1)
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "need batch >= 0, seq_len >= 0, heads >= 1");
+    if (desc->chunk < 1) return fail(TITANS_ERR_INVALID_ARGUMENT, "chunk=%d must be >= 1", desc->chunk);
+    if (desc->window < 1)
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "window=%d must be >= 1", desc->window);
+    if (!(desc->eta_scale >= 0.f && desc->eta_scale < INFINITY))
+        return fail(TITANS_ERR_INVALID_ARGUMENT, "eta_scale=%g must be finite and >= 0",
+                    (double)desc->eta_scale);
+    if (desc->reserved != 0) return fail(TITANS_ERR_INVALID_ARGUMENT, "reserved must be 0");
+    titans::ScanArgs m{};
+    titans_status st = check_mlp(mlp, m);
+    if (st) return st;
+    const int d = m.n[0];
+    if (m.n[m.L] != d)
+        return fail(TITANS_ERR_INVALID_ARGUMENT,
+                    "the memory's output width %d must equal its input width %d", m.n[m.L], d);
+    if (!titans::mag_head_dim_supported(d))
+        return fail(TITANS_ERR_UNSUPPORTED, "head width d=%d: the attention takes 32, 64 or 128", d);
+    if (desc->heads > 65536 / d)
+        return fail(TITANS_ERR_UNSUPPORTED, "heads * d = %lld exceeds 65536",
+                    (long long)(desc->heads * d));
+    const int64_t nqb = (desc->seq_len + 63) / 64;
+    const int64_t tiles_m = (desc->batch * desc->seq_len + 127) / 128;
+    const int64_t tiles_n = (3 * desc->heads * d + 3 * desc->heads + 127) / 128;
+    if (desc->batch * desc->heads * nqb > 0xffffffffLL || tiles_m * tiles_n > 0xffffffffLL ||
+        desc->batch * desc->seq_len > 0xffffffffLL)
+        return fail(TITANS_ERR_UNSUPPORTED, "batch * seq_len too large for one launch");
+    sd = mag_scan_desc(desc, d, m.P);
+    if ((st = prepare_scan(&sd, mlp, a))) return st;
+    g = titans::MagArgs{};
+    g.B = desc->batch;
+    g.T = desc->seq_len;
+    g.H = desc->heads;
+    g.d = d;
+    g.window = desc->window;
+    g.eta_scale = desc->eta_scale;
+    return TITANS_OK;
+}
+
+// The block's own pieces, then the scan's workspace (256-byte aligned offset).
+static size_t mag_own_bytes(const titans::MagArgs& g) {
+    return (titans::mag_workspace_bytes(g) + 255) / 256 * 256;
+}
+
+size_t titans_mag_workspace_size(const titans_mag_desc* desc, const titans_mlp_desc* mlp) {
+    titans::MagArgs g;
+    titans_scan_desc sd;
+    titans::ScanArgs a{};
+    if (prepare_mag(desc, mlp, g, sd, a) != TITANS_OK) return SIZE_MAX;
+    return mag_own_bytes(g) + workspace_of(a, false);
+}
+
+titans_status titans_mag_forward(const titans_mag_desc* desc, const titans_mlp_desc* mlp,
+                                 const void* x, const void* w_in, const float* b_gate,
+                                 const void* w_out, const float* theta0, const float* s0,
+                                 void* out, float* theta_T, float* s_T, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    titans::MagArgs g;
+    titans_scan_desc sd;
+    titans::ScanArgs a{};
+    titans_status st = prepare_mag(desc, mlp, g, sd, a);
+    if (st) return st;
+    const int64_t B = g.B, T = g.T, H = g.H, D = H * g.d, M = B * T, P = a.P;
+    const bool tokens = M > 0;
+    if (B > 0) {
+        if (!theta0 || !s0 || !theta_T || !s_T)
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "theta0, s0, theta_T and s_T must be non-NULL");
+        if ((st = check_state_alignment(theta0, a.s0s, "theta0"))) return st;
+        if ((st = check_state_alignment(s0, a.s0s, "s0"))) return st;
+        if ((st = check_state_alignment(theta_T, a.ss, "theta_T"))) return st;
+        if ((st = check_state_alignment(s_T, a.ss, "s_T"))) return st;
+    }
+    // x and the weights are read only when there are tokens
+    if (tokens) {
+        if (!x || !w_in || !b_gate || !w_out || !out)
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "x, w_in, b_gate, w_out and out must be non-NULL");
+        const void* a16[3] = {x, w_in, w_out};
+        const char* n16[3] = {"x", "w_in", "w_out"};
+        for (int i = 0; i < 3; ++i)
+            if (reinterpret_cast<uintptr_t>(a16[i]) & 15u)
+                return fail(TITANS_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", n16[i]);
+        if (reinterpret_cast<uintptr_t>(out) & 7u)
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "out is not 8-byte aligned");
+        if (reinterpret_cast<uintptr_t>(b_gate) & 3u)
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "b_gate is not 4-byte aligned");
+    }
+    const size_t own = tokens ? mag_own_bytes(g) : 0;
+    const size_t scan_ws = workspace_of(a, false);
+    const size_t need = tokens ? own + scan_ws : 0;
+    const size_t state_bytes = static_cast<size_t>(B * H * P) * 4;
+    const Span ins[6] = {tokens ? contiguous(x, static_cast<size_t>(M * D) * 2) : Span{},
+                         tokens ? contiguous(w_in, static_cast<size_t>((3 * D + 3 * H) * D) * 2) : Span{},
+                         tokens ? contiguous(b_gate, static_cast<size_t>(3 * H) * 4) : Span{},
+                         tokens ? contiguous(w_out, static_cast<size_t>(D * D) * 2) : Span{},
+                         contiguous(theta0, state_bytes), contiguous(s0, state_bytes)};
+    const Span outs[4] = {tokens ? contiguous(out, static_cast<size_t>(M * D) * 2) : Span{},
+                          contiguous(theta_T, state_bytes), contiguous(s_T, state_bytes),
+                          need ? contiguous(workspace, need) : Span{}};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(outs[i], ins[j]))
+                return fail(TITANS_ERR_INVALID_ARGUMENT,
+                            "out, theta_T, s_T and the workspace must not overlap an input");
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(TITANS_ERR_INVALID_ARGUMENT,
+                            "out, theta_T, s_T and the workspace must not overlap each other");
+    }
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(TITANS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+            return fail(TITANS_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    }
+    if (B == 0) return TITANS_OK;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (!tokens)  // no tokens: the memory passes through unchanged
+        return scan_impl(&sd, mlp, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, theta0, s0,
+                         nullptr, theta_T, s_T, nullptr, false, nullptr, 0, stream);
+    g.x = static_cast<const __bf16*>(x);
+    g.w_in = static_cast<const __bf16*>(w_in);
+    g.b_gate = b_gate;
+    g.w_out = static_cast<const __bf16*>(w_out);
+    g.out = static_cast<__bf16*>(out);
+    titans::mag_place(g, workspace);
+    hipError_t e = titans::launch_mag_front(g, hs);
+    if (e != hipSuccess) return hip_fail(e, "MAG front-end launch");
+    st = scan_impl(&sd, mlp, g.q, g.k, g.v, g.alpha, g.eta, g.beta, theta0, s0, g.ymem, theta_T,
+                   s_T, nullptr, false, scan_ws ? static_cast<char*>(workspace) + own : nullptr,
+                   scan_ws, stream);
+    if (st) return st;
+    if ((e = titans::launch_mag_attention(g, hs)) != hipSuccess)
+        return hip_fail(e, "MAG attention launch");
+    if ((e = titans::launch_mag_out(g, hs)) != hipSuccess)
+        return hip_fail(e, "MAG output projection launch");
+    return TITANS_OK;
+}
+
 }  // extern "C"

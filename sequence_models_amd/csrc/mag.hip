@@ -1,0 +1,427 @@
+// Titans MAG block (memory as gate) on gfx950: everything of the block except the memory
+// scan itself, which runs through the scan launchers.
+//
+// The block (Titans explainer, the three architecture variants, memory as gate; the
+// lowest.today summary, "Varianti dell'Architettura Titans"): the memory branch reads the
+// long-term memory, sliding-window attention is the short-term branch, and the memory's
+// output gates the attention output through a sigmoid, o = sigmoid(y_mem) * y_attn.  The
+// projection front end and the output projection take the plainest reading:
+//
+//   [q | k | v | g] = x W_in^T         W_in [3D + 3H, D] (out features x in features)
+//   q, k <- unit L2 norm per (token, head); v as is
+//   alpha = sigmoid(g_a + b_a), eta = eta_scale sigmoid(g_e + b_e), beta = sigmoid(g_b + b_b)
+//   y_attn = causal softmax attention over the last `window` tokens (itself included),
+//            scores q.k / sqrt(d)
+//   out = (sigmoid(y_mem) * y_attn) W_out^T                W_out [D, D]
+//
+// Kernels:
+//   gemm_nt_kernel   C = A W^T on v_mfma_f32_16x16x32_bf16, 128 x 128 tiles, 4 waves of
+//                    64 x 64, k staged 32 deep through double-buffered LDS; the front-end
+//                    projection writes fp32, the output projection bf16.
+//   prep_kernel      one workgroup per token: per-head norms of q and k (shuffle sums over
+//                    the lanes that hold one head), bf16 q, k, v, and the three gates.
+//   swa_gate_kernel  flash-style attention: 64 queries (16 per wave) against 64-key
+//                    blocks in LDS, scores computed transposed (keys x queries) so each
+//                    lane owns one query's running max and sum, probabilities fed back to
+//                    the value product straight from the score accumulators; the
+//                    epilogue gates with sigmoid(y_mem) and stores o in bf16.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "mfma_util.h"
+#include "titans_internal.h"
+
+namespace titans {
+namespace mag {
+
+using fused::bf16x4;
+using fused::bf16x8;
+using fused::f32x4;
+
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 zero8() {
+    const __bf16 z = static_cast<__bf16>(0.0f);
+    return bf16x8{z, z, z, z, z, z, z, z};
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin; when the grid divides evenly, give each
+// XCD one contiguous range of logical tiles so that tiles sharing operands share an L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nb) {
+    if (nb % 8) return bid;
+    return (bid % 8) * (nb / 8) + bid / 8;
+}
+
+// ------------------------------------------------------------------------------ GEMM
+
+constexpr int kGT = 128;       // tile extent in M and in N
+constexpr int kGK = 32;        // k per stage
+constexpr int kGP = kGK + 8;   // LDS row pitch in bf16 (80 bytes)
+
+struct StoreF32 {
+    float* p;
+    int64_t ld;
+    int n_lim;  // a multiple of 4: column groups at or beyond it are not stored
+    __device__ void operator()(int64_t m, int n, f32x4 v) const {
+        if (n < n_lim) *reinterpret_cast<f32x4*>(p + m * ld + n) = v;
+    }
+};
+struct StoreBf16 {
+    __bf16* p;
+    int64_t ld;
+    int n_lim;
+    __device__ void operator()(int64_t m, int n, f32x4 v) const {
+        if (n < n_lim) *reinterpret_cast<bf16x4*>(p + m * ld + n) = fused::bf4(v);
+    }
+};
+
+// C[m][n] = sum_k A[m][k] W[n][k] for A [M, K] (row pitch lda) and W [N, K] (row pitch K),
+// K a multiple of 8, A and W 16-byte aligned.  Workgroup tile (tm, tn) covers rows
+// 128 tm .. +127 and columns 128 tn .. +127; wave w the 64 x 64 quarter (w / 2, w % 2).
+// The product is formed transposed (W rows as the MFMA's A operand) so that a lane's
+// accumulator holds four consecutive columns of one row: lane (g, j) of block (in, im)
+// holds C[16 im + j][16 in + 4 g + r], r = 0..3.
+template <class Epi>
+__global__ __launch_bounds__(256) void gemm_nt_kernel(const __bf16* __restrict__ A, int64_t lda,
+                                                      const __bf16* __restrict__ W, int64_t M,
+                                                      int N, int K, int tiles_n, Epi epi) {
+    __shared__ __align__(16) __bf16 sa[2][kGT * kGP];
+    __shared__ __align__(16) __bf16 sw[2][kGT * kGP];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, j = lane & 15;
+    const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t m0 = (bid / tiles_n) * kGT;
+    const int n0 = static_cast<int>(bid % tiles_n) * kGT;
+    // staging: 16-byte piece c = tid + 256 i of a 128 x 32 tile is row c / 4, k (c % 4) * 8
+    const int r0 = tid >> 2, kc = (tid & 3) * 8;
+    bf16x8 ra[2], rw[2];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = r0 + 64 * i;
+            const bool kok = k0 + kc < K;
+            const int64_t m = m0 + r;
+            const int n = n0 + r;
+            ra[i] = (kok && m < M) ? *reinterpret_cast<const bf16x8*>(A + m * lda + k0 + kc) : zero8();
+            rw[i] = (kok && n < N) ? *reinterpret_cast<const bf16x8*>(W + (int64_t)n * K + k0 + kc)
+                                   : zero8();
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            *reinterpret_cast<bf16x8*>(&sa[buf][(r0 + 64 * i) * kGP + kc]) = ra[i];
+            *reinterpret_cast<bf16x8*>(&sw[buf][(r0 + 64 * i) * kGP + kc]) = rw[i];
+        }
+    };
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = fused::zero4();
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nk = (K + kGK - 1) / kGK;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int s = 0; s < nk; ++s) {
+        const int cur = s & 1;
+        if (s + 1 < nk) load((s + 1) * kGK);
+        bf16x8 fa[4], fw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            fa[i] = *reinterpret_cast<const bf16x8*>(&sa[cur][(wm * 64 + 16 * i + j) * kGP + 8 * g]);
+            fw[i] = *reinterpret_cast<const bf16x8*>(&sw[cur][(wn * 64 + 16 * i + j) * kGP + 8 * g]);
+        }
+#pragma unroll
+        for (int in = 0; in < 4; ++in)
+#pragma unroll
+            for (int im = 0; im < 4; ++im) acc[in][im] = mma(fw[in], fa[im], acc[in][im]);
+        if (s + 1 < nk) store(cur ^ 1);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int im = 0; im < 4; ++im) {
+        const int64_t m = m0 + wm * 64 + 16 * im + j;
+        if (m >= M) continue;
+#pragma unroll
+        for (int in = 0; in < 4; ++in) epi(m, n0 + wn * 64 + 16 * in + 4 * g, acc[in][im]);
+    }
+}
+
+template <class Epi>
+static hipError_t gemm_nt(const __bf16* A, int64_t lda, const __bf16* W, int64_t M, int N, int K,
+                          Epi epi, hipStream_t stream) {
+    if (M == 0 || N == 0) return hipSuccess;
+    const int tiles_n = (N + kGT - 1) / kGT;
+    const int64_t tiles = (M + kGT - 1) / kGT * tiles_n;
+    hipLaunchKernelGGL(gemm_nt_kernel<Epi>, dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
+                       stream, A, lda, W, M, N, K, tiles_n, epi);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------- front end
+
+__device__ __forceinline__ float sigm(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+// Token row m of the projection (fp32, pitch ldp): columns [0, D) q, [D, 2D) k,
+// [2D, 3D) v, [3D, 3D + 3H) the gate logits.  Thread t handles the four columns 4t .. 4t+3
+// of each 1024-column group; with d a multiple of 32 dividing 256, the d / 4 lanes
+// holding one head are consecutive lanes of one wave, and a butterfly over them leaves
+// every lane with its head's sum of squares.
+__global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ proj, int64_t ldp,
+                                                   int H, int d, float eta_scale,
+                                                   const float* __restrict__ bg,
+                                                   __bf16* __restrict__ q, __bf16* __restrict__ k,
+                                                   __bf16* __restrict__ v, float* __restrict__ alpha,
+                                                   float* __restrict__ eta, float* __restrict__ beta) {
+    const int64_t m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int D = H * d;
+    const float* row = proj + m * ldp;
+    for (int c0 = 0; c0 < D; c0 += 1024) {
+        const int c = c0 + 4 * tid;
+        const bool ok = c < D;
+        f32x4 qv = fused::zero4(), kv = fused::zero4(), vv = fused::zero4();
+        if (ok) {
+            qv = *reinterpret_cast<const f32x4*>(row + c);
+            kv = *reinterpret_cast<const f32x4*>(row + D + c);
+            vv = *reinterpret_cast<const f32x4*>(row + 2 * D + c);
+        }
+        float sq = qv[0] * qv[0] + qv[1] * qv[1] + qv[2] * qv[2] + qv[3] * qv[3];
+        float sk = kv[0] * kv[0] + kv[1] * kv[1] + kv[2] * kv[2] + kv[3] * kv[3];
+        for (int o = 1; o < d / 4; o <<= 1) {
+            sq += __shfl_xor(sq, o);
+            sk += __shfl_xor(sk, o);
+        }
+        if (ok) {
+            const float iq = 1.0f / sqrtf(sq), ik = 1.0f / sqrtf(sk);
+            *reinterpret_cast<bf16x4*>(q + m * D + c) = fused::bf4(qv * iq);
+            *reinterpret_cast<bf16x4*>(k + m * D + c) = fused::bf4(kv * ik);
+            *reinterpret_cast<bf16x4*>(v + m * D + c) = fused::bf4(vv);
+        }
+    }
+    for (int t = tid; t < 3 * H; t += 256) {
+        const float s = sigm(row[3 * D + t] + bg[t]);
+        const int which = t / H, h = t - which * H;
+        float* dst = which == 0 ? alpha : which == 1 ? eta : beta;
+        dst[m * H + h] = which == 1 ? eta_scale * s : s;
+    }
+}
+
+// ------------------------------------------------------------------------- attention
+
+constexpr int kQB = 64;  // queries per workgroup, 16 per wave
+constexpr int kKB = 64;  // keys per LDS block
+
+// One workgroup per (b, h, 64-query block).  q, k, v, y_mem and o are [B, T, H, kD] bf16
+// rows of pitch D = H kD.  Lane (g, j) of wave w owns query q0 + 16 w + j.  Per key block:
+// S^T tile t (keys 16 t .. 16 t + 15) = K Q^T, so lane (g, j) holds the scores of keys
+// 16 t + 4 g + r for its query; masked scores are -inf; the running max is shared by the
+// four lanes of a query (two xor shuffles) while each lane keeps a partial sum of its own
+// probabilities; O^T += V^T P^T takes P^T straight from the score registers (the
+// accumulator's row index, the key, is the reduction index of the value product) and V^T
+// from a transposed LDS copy.
+template <int kD>
+__global__ __launch_bounds__(256) void swa_gate_kernel(const __bf16* __restrict__ q,
+                                                       const __bf16* __restrict__ k,
+                                                       const __bf16* __restrict__ v,
+                                                       const __bf16* __restrict__ ymem,
+                                                       __bf16* __restrict__ o, int64_t T, int H,
+                                                       int window, float scale_log2, int nqb) {
+    constexpr int kKP = kD + 8;   // key rows in LDS (bf16 pitch)
+    constexpr int kVP = kKB + 8;  // transposed value rows in LDS
+    __shared__ __align__(16) __bf16 ks[kKB * kKP];
+    __shared__ __align__(16) __bf16 vt[kD * kVP];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, j = lane & 15;
+    const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int qb = static_cast<int>(bid % nqb);
+    const int64_t bh = bid / nqb;
+    const int64_t b = bh / H;
+    const int h = static_cast<int>(bh % H);
+    const int64_t D = static_cast<int64_t>(H) * kD;
+    const int64_t base = b * T * D + static_cast<int64_t>(h) * kD;  // (b, 0, h, 0)
+    const int64_t q0 = static_cast<int64_t>(qb) * kQB;
+    const int64_t qi = q0 + 16 * wave + j;
+    const bool qok = qi < T;
+
+    bf16x8 qf[kD / 32];
+#pragma unroll
+    for (int kb = 0; kb < kD / 32; ++kb)
+        qf[kb] = qok ? *reinterpret_cast<const bf16x8*>(q + base + qi * D + 32 * kb + 8 * g) : zero8();
+
+    f32x4 acc[kD / 16];
+#pragma unroll
+    for (int dt = 0; dt < kD / 16; ++dt) acc[dt] = fused::zero4();
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    const int64_t qlast = (q0 + kQB - 1 < T - 1) ? q0 + kQB - 1 : T - 1;
+    const int64_t kfirst = q0 - window + 1 > 0 ? q0 - window + 1 : 0;
+    for (int64_t kb0 = kfirst / kKB * kKB; kb0 <= qlast; kb0 += kKB) {
+        __syncthreads();  // the previous block's LDS reads are done
+        constexpr int kPieces = kKB * kD / 8;
+        for (int c = tid; c < kPieces; c += 256) {
+            const int r = c / (kD / 8), cc = (c % (kD / 8)) * 8;
+            const int64_t key = kb0 + r;
+            bf16x8 kv = zero8(), vv = zero8();
+            if (key < T) {
+                kv = *reinterpret_cast<const bf16x8*>(k + base + key * D + cc);
+                vv = *reinterpret_cast<const bf16x8*>(v + base + key * D + cc);
+            }
+            *reinterpret_cast<bf16x8*>(&ks[r * kKP + cc]) = kv;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vt[(cc + i) * kVP + r] = vv[i];
+        }
+        __syncthreads();
+
+        f32x4 s[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            s[t] = fused::zero4();
+#pragma unroll
+            for (int kb = 0; kb < kD / 32; ++kb) {
+                const bf16x8 kf =
+                    *reinterpret_cast<const bf16x8*>(&ks[(16 * t + j) * kKP + 32 * kb + 8 * g]);
+                s[t] = mma(kf, qf[kb], s[t]);
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t key = kb0 + 16 * t + 4 * g + r;
+                const bool ok = key <= qi && key > qi - window;
+                const float x = ok ? s[t][r] * scale_log2 : -INFINITY;
+                s[t][r] = x;
+                mx = fmaxf(mx, x);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float corr = exp2f(m_run - m_use);
+        m_run = m_new;
+        l_run *= corr;
+#pragma unroll
+        for (int dt = 0; dt < kD / 16; ++dt) acc[dt] *= corr;
+        bf16x4 pb[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4 p;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = exp2f(s[t][r] - m_use);
+            pb[t] = fused::bf4(p);
+            // the sum runs over the rounded probabilities, so the weights applied to the
+            // values are exactly normalized
+            const f32x4 pr = fused::f4(pb[t]);
+            l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 pf = fused::cat(pb[2 * kb], pb[2 * kb + 1]);
+#pragma unroll
+            for (int dt = 0; dt < kD / 16; ++dt) {
+                const __bf16* p = &vt[(16 * dt + j) * kVP + 32 * kb + 4 * g];
+                const bf16x8 vf = fused::cat(*reinterpret_cast<const bf16x4*>(p),
+                                             *reinterpret_cast<const bf16x4*>(p + 16));
+                acc[dt] = mma(vf, pf, acc[dt]);
+            }
+        }
+    }
+    float l = l_run;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!qok) return;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int dt = 0; dt < kD / 16; ++dt) {
+        const int64_t at = base + qi * D + 16 * dt + 4 * g;
+        const f32x4 ym = fused::f4(*reinterpret_cast<const bf16x4*>(ymem + at));
+        f32x4 out;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[r] = sigm(ym[r]) * (acc[dt][r] * inv);
+        *reinterpret_cast<bf16x4*>(o + at) = fused::bf4(out);
+    }
+}
+
+}  // namespace mag
+
+bool mag_head_dim_supported(int d) { return d == 32 || d == 64 || d == 128; }
+
+static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace: proj fp32 [M, ldp], q / k / v / y_mem / o bf16 [M, D], alpha / eta / beta
+// fp32 [M, H], each piece 256-byte aligned; the memory scan's own workspace follows.
+size_t mag_workspace_bytes(const MagArgs& g) {
+    const int64_t M = g.B * g.T, D = g.H * g.d;
+    const int64_t ldp = (3 * D + 3 * g.H + 3) / 4 * 4;
+    return static_cast<size_t>(align256(M * ldp * 4) + 5 * align256(M * D * 2) +
+                               3 * align256(M * g.H * 4));
+}
+
+void mag_place(MagArgs& g, void* ws) {
+    const int64_t M = g.B * g.T, D = g.H * g.d;
+    g.ldp = (3 * D + 3 * g.H + 3) / 4 * 4;
+    char* p = static_cast<char*>(ws);
+    g.proj = reinterpret_cast<float*>(p);
+    p += align256(M * g.ldp * 4);
+    __bf16** bufs[5] = {&g.q, &g.k, &g.v, &g.ymem, &g.o};
+    for (__bf16** b : bufs) {
+        *b = reinterpret_cast<__bf16*>(p);
+        p += align256(M * D * 2);
+    }
+    float** gates[3] = {&g.alpha, &g.eta, &g.beta};
+    for (float** a : gates) {
+        *a = reinterpret_cast<float*>(p);
+        p += align256(M * g.H * 4);
+    }
+}
+
+hipError_t launch_mag_front(const MagArgs& g, hipStream_t stream) {
+    const int64_t M = g.B * g.T;
+    const int D = static_cast<int>(g.H * g.d);
+    const int N = 3 * D + 3 * static_cast<int>(g.H);
+    hipError_t e = mag::gemm_nt(g.x, D, g.w_in, M, N, D,
+                                mag::StoreF32{g.proj, g.ldp, static_cast<int>(g.ldp)}, stream);
+    if (e != hipSuccess || M == 0) return e;
+    hipLaunchKernelGGL(mag::prep_kernel, dim3(static_cast<unsigned>(M)), dim3(256), 0, stream,
+                       g.proj, g.ldp, static_cast<int>(g.H), g.d, g.eta_scale, g.b_gate, g.q, g.k,
+                       g.v, g.alpha, g.eta, g.beta);
+    return hipGetLastError();
+}
+
+hipError_t launch_mag_attention(const MagArgs& g, hipStream_t stream) {
+    if (g.B * g.H * g.T == 0) return hipSuccess;
+    const int nqb = static_cast<int>((g.T + mag::kQB - 1) / mag::kQB);
+    const dim3 grid(static_cast<unsigned>(g.B * g.H * nqb));
+    const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(g.d));
+    const int H = static_cast<int>(g.H);
+    switch (g.d) {
+        case 32:
+            hipLaunchKernelGGL(mag::swa_gate_kernel<32>, grid, dim3(256), 0, stream, g.q, g.k, g.v,
+                               g.ymem, g.o, g.T, H, g.window, scale_log2, nqb);
+            break;
+        case 64:
+            hipLaunchKernelGGL(mag::swa_gate_kernel<64>, grid, dim3(256), 0, stream, g.q, g.k, g.v,
+                               g.ymem, g.o, g.T, H, g.window, scale_log2, nqb);
+            break;
+        case 128:
+            hipLaunchKernelGGL(mag::swa_gate_kernel<128>, grid, dim3(256), 0, stream, g.q, g.k,
+                               g.v, g.ymem, g.o, g.T, H, g.window, scale_log2, nqb);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_mag_out(const MagArgs& g, hipStream_t stream) {
+    const int64_t M = g.B * g.T;
+    const int D = static_cast<int>(g.H * g.d);
+    return mag::gemm_nt(g.o, D, g.w_out, M, D, D, mag::StoreBf16{g.out, D, D}, stream);
+}
+
+}  // namespace titans

@@ -103,4 +103,30 @@ hipError_t launch_retrieve_wide(const ScanArgs& a, hipStream_t stream);
 bool retrieve_mfma_supported(const ScanArgs& a);
 hipError_t launch_retrieve_mfma(const ScanArgs& a, hipStream_t stream);
 
+// MAG block (memory as gate): the front-end projection and gates, the gated
+// sliding-window attention and the output projection around one memory scan.  Shapes
+// are validated by the ABI layer; the pointers after b_gate/w_out are workspace pieces
+// placed by mag_place.
+struct MagArgs {
+    int64_t B, T, H;
+    int d;                 // head width (the memory's input and output width)
+    int window;            // attention window, the token itself included
+    float eta_scale;
+    const __bf16* x;       // [B, T, D], D = H d
+    const __bf16* w_in;    // [3D + 3H, D]
+    const float* b_gate;   // [3H]
+    const __bf16* w_out;   // [D, D]
+    __bf16* out;           // [B, T, D]
+    int64_t ldp;           // row pitch of proj (3D + 3H rounded up to a multiple of 4)
+    float* proj;           // [B T, ldp] fp32
+    __bf16 *q, *k, *v, *ymem, *o;  // [B, T, H, d]
+    float *alpha, *eta, *beta;     // [B, T, H]
+};
+bool mag_head_dim_supported(int d);
+size_t mag_workspace_bytes(const MagArgs& g);
+void mag_place(MagArgs& g, void* ws);
+hipError_t launch_mag_front(const MagArgs& g, hipStream_t stream);
+hipError_t launch_mag_attention(const MagArgs& g, hipStream_t stream);
+hipError_t launch_mag_out(const MagArgs& g, hipStream_t stream);
+
 }  // namespace titans

@@ -33,7 +33,7 @@ import numpy as np
 BLOCK_TOKENS = 4096
 
 # tensor ids for the stream keys
-_Q, _K, _V, _ALPHA, _ETA, _BETA, _THETA, _DY, _DTHETA, _DS = range(10)
+_Q, _K, _V, _ALPHA, _ETA, _BETA, _THETA, _DY, _DTHETA, _DS, _X, _WIN, _WOUT = range(13)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -232,3 +232,50 @@ def make_cotangents(wl: Workload | str, seed: int = 0, seq_len: int | None = Non
         dth[b] = (state_scale * _rng(seed, _DTHETA, b).standard_normal((H, P))).astype(np.float32)
         ds[b] = (state_scale * _rng(seed, _DS, b).standard_normal((H, P))).astype(np.float32)
     return Cotangents(dy, dth, ds)
+
+
+@dataclasses.dataclass
+class MagInputs:
+    """Inputs of one MAG block: x, the projection weights (out x in features, bf16 bits),
+    the gate biases and the initial memory.  The weights are drawn so the projected q, k,
+    v and gates follow the memory-scan recipe above: with x ~ N(0, 1) and weights
+    ~ N(0, 1 / D), every projected feature is ~ N(0, 1); the gate biases are
+    (alpha_mu, 0, beta_mu) per head."""
+    workload: Workload   # batch, heads, seq_len, widths, chunk, eta_scale, alpha_mu, beta_mu
+    window: int
+    x: np.ndarray        # [B,T,D] uint16 bf16 bits
+    w_in: np.ndarray     # [3D + 3H, D] uint16 bits: q, k, v rows, then alpha, eta, beta rows
+    b_gate: np.ndarray   # [3H] float32
+    w_out: np.ndarray    # [D, D] uint16 bits
+    theta0: np.ndarray   # [H,P] float32 (the same for every batch row)
+    s0: np.ndarray       # [H,P] float32
+
+    def oracle_weights(self):
+        """(Wq, Wk, Wv, Wg, bg, Wo) as float64 in the x @ W convention."""
+        D = self.x.shape[2]
+        w = bf16_bits_to_f32(self.w_in).astype(np.float64)
+        wo = bf16_bits_to_f32(self.w_out).astype(np.float64)
+        return (w[:D].T, w[D:2 * D].T, w[2 * D:3 * D].T, w[3 * D:].T,
+                self.b_gate.astype(np.float64), wo.T)
+
+
+def make_mag_inputs(wl: Workload | str, window: int, seed: int = 0, seq_len: int | None = None,
+                    batch: int | None = None) -> MagInputs:
+    """x ~ N(0, 1) per element over [B, T, D] (prefix-consistent in T), W_in and W_out rows
+    ~ N(0, 1 / D), all rounded to bf16; theta0 as make_theta0, s0 = 0."""
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    B = wl.batch if batch is None else batch
+    T = wl.seq_len if seq_len is None else seq_len
+    wl = wl.with_(batch=B, seq_len=T, io="bf16")
+    H, d = wl.heads, wl.d
+    D = H * d
+    x = np.empty((B, T, H, d), dtype=np.uint16)
+    _draw_vectors(seed, _X, wl, B, T, False, x)
+    w_in = _rng(seed, _WIN).standard_normal((3 * D + 3 * H, D)) / np.sqrt(D)
+    w_out = _rng(seed, _WOUT).standard_normal((D, D)) / np.sqrt(D)
+    b_gate = np.concatenate([np.full(H, wl.alpha_mu), np.zeros(H), np.full(H, wl.beta_mu)])
+    theta0 = make_theta0(wl, seed)
+    return MagInputs(wl, int(window), x.reshape(B, T, D),
+                     f32_to_bf16_bits(w_in.astype(np.float32)), b_gate.astype(np.float32),
+                     f32_to_bf16_bits(w_out.astype(np.float32)), theta0, np.zeros_like(theta0))

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_status_strings_and_param_count():
-    assert tm.lib.titans_abi_version() == 3
+    assert tm.lib.titans_abi_version() == 4
     assert tm.lib.titans_status_string(0) == b"TITANS_OK"
     assert tm.lib.titans_status_string(3) == b"TITANS_ERR_WORKSPACE"
     assert tm.param_count((64, 256, 64)) == 32768
@@ -438,3 +438,100 @@ def test_backward_validation_of_overlap_and_workspace():
     shared.state_stride[:] = (0, P)   # one dtheta0 written by several batch rows
     shared.state0_stride[:] = (0, P)
     assert _bwd(shared, mlp, ptrs, end, need)[0] == INVALID
+
+
+# ---------------------------------------------------------------- MAG block
+
+def _mag_desc(B=2, T=100, H=2, C=16, W=32, eta=0.1):
+    return tm.MagDesc(B, T, H, C, W, eta, 0)
+
+
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
+def test_mag_workspace_formula():
+    widths = (64, 256, 64)
+    mlp = tm.mlp_desc(widths)
+    for B, T, H, C in [(2, 100, 2, 16), (8, 16384, 16, 64), (1, 1, 3, 1)]:
+        d = widths[0]
+        D, M = H * d, B * T
+        ldp = (3 * D + 3 * H + 3) // 4 * 4
+        own = _a256(_a256(M * ldp * 4) + 5 * _a256(M * D * 2) + 3 * _a256(M * H * 4))
+        sd = _desc(B, T, H, d)
+        sd.chunk = C
+        P = tm.param_count(widths)
+        sd.qkv_stride[:] = (T * D, D, d)
+        sd.y_stride[:] = (T * D, D, d)
+        sd.gate_stride[:] = (T * H, H, 1)
+        sd.state_stride[:] = (H * P, P)
+        sd.state0_stride[:] = (H * P, P)
+        scan_ws = tm.lib.titans_mem_scan_workspace_size(ctypes.byref(sd), ctypes.byref(mlp))
+        got = tm.lib.titans_mag_workspace_size(ctypes.byref(_mag_desc(B, T, H, C)), ctypes.byref(mlp))
+        assert got == own + scan_ws, (B, T, H, C)
+    assert tm.lib.titans_mag_workspace_size(ctypes.byref(_mag_desc(0, 5, 2)), ctypes.byref(mlp)) == 0
+
+
+def test_mag_descriptor_validation():
+    big = ctypes.c_size_t(-1).value
+    ok = tm.mlp_desc((64, 256, 64))
+    size = lambda desc, mlp=ok: tm.lib.titans_mag_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+    assert size(_mag_desc()) != big
+    for bad in (_mag_desc(W=0), _mag_desc(C=0), _mag_desc(H=0), _mag_desc(B=-1),
+                _mag_desc(eta=float("nan")), _mag_desc(eta=-1.0), _mag_desc(eta=float("inf")),
+                tm.MagDesc(2, 100, 2, 16, 32, 0.1, 7)):
+        assert size(bad) == big
+    assert size(_mag_desc(), tm.mlp_desc((64, 256, 32))) == big   # output width != d
+    assert size(_mag_desc(), tm.mlp_desc((16, 32, 16))) == big     # d not 32 / 64 / 128
+    assert size(_mag_desc(H=1025)) == big                         # H d > 65536
+
+
+_MAG_ORDER = ("x", "w_in", "b_gate", "w_out", "theta0", "s0", "out", "theta_T", "s_T")
+
+
+def _fake_mag_ptrs(B, T, H, d, P):
+    D = H * d
+    sizes = {"x": B * T * D * 2, "w_in": (3 * D + 3 * H) * D * 2, "b_gate": 3 * H * 4,
+             "w_out": D * D * 2, "theta0": B * H * P * 4, "s0": B * H * P * 4,
+             "out": B * T * D * 2, "theta_T": B * H * P * 4, "s_T": B * H * P * 4}
+    base, ptrs = 1 << 40, {}
+    for n in _MAG_ORDER:
+        ptrs[n] = base
+        base = _a256(base + sizes[n] + 256)
+    return ptrs, base
+
+
+def _mag(desc, mlp, ptrs, ws, ws_bytes):
+    args = [ctypes.c_void_p(ptrs[n]) for n in _MAG_ORDER]
+    st = tm.lib.titans_mag_forward(ctypes.byref(desc), ctypes.byref(mlp), *args,
+                                   ctypes.c_void_p(ws), ws_bytes, None)
+    return st, tm.lib.titans_last_error().decode()
+
+
+@no_fake_pointers_on_gpu
+def test_mag_validation_of_pointers_overlap_and_workspace():
+    widths = (64, 256, 64)
+    mlp = tm.mlp_desc(widths)
+    B, T, H, d = 2, 100, 2, 64
+    P = tm.param_count(widths)
+    desc = _mag_desc(B, T, H)
+    ptrs, end = _fake_mag_ptrs(B, T, H, d, P)
+    need = tm.lib.titans_mag_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+    for n in _MAG_ORDER:
+        st, msg = _mag(desc, mlp, dict(ptrs, **{n: 0}), end, need)
+        assert st == INVALID and "NULL" in msg, (n, msg)
+    for n, off in (("x", 8), ("w_in", 2), ("w_out", 8), ("out", 2), ("b_gate", 2), ("theta0", 4),
+                   ("theta_T", 8)):
+        st, msg = _mag(desc, mlp, dict(ptrs, **{n: ptrs[n] + off}), end, need)
+        assert st == INVALID and "aligned" in msg, (n, msg)
+    for o in ("out", "theta_T", "s_T"):
+        for i in ("x", "w_in", "b_gate", "w_out", "theta0", "s0", "out", "theta_T", "s_T"):
+            if i == o:
+                continue
+            st, msg = _mag(desc, mlp, dict(ptrs, **{o: ptrs[i]}), end, need)
+            assert st == INVALID and "overlap" in msg, (o, i, msg)
+    assert _mag(desc, mlp, ptrs, end, need - 1)[0] == WORKSPACE
+    assert _mag(desc, mlp, ptrs, 0, need)[0] == WORKSPACE
+    assert _mag(desc, mlp, ptrs, end + 64, need)[0] == INVALID
+    st, msg = _mag(desc, mlp, ptrs, ptrs["x"], need)
+    assert st == INVALID and "overlap" in msg
