@@ -30,10 +30,24 @@ def _sigmoid(z):
     return 1.0 / (1.0 + np.exp(-z))
 
 
-def front_end(x, Wq, Wk, Wv, Wg, bg, H, eta_scale):
-    """q, k, v [B, T, H, d] and alpha, eta, beta [B, T, H] from x."""
-    B, T, D = x.shape
-    d = D // H
+def round_bf16(a):
+    """Round to the nearest bfloat16 (ties to even), through float32, by torch's CPU
+    conversion; returned as float64."""
+    import torch
+
+    t = torch.from_numpy(np.asarray(a, np.float64)).to(torch.float32).to(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def front_end(x, Wq, Wk, Wv, Wg, bg, H, eta_scale, store=None):
+    """q, k, v [B, T, H, d] and alpha, eta, beta [B, T, H] from x.
+
+    store="bf16" rounds q, k, v to bfloat16 after the normalization: the block's interface
+    keeps them in that format, so the memory and the attention both read the rounded
+    values (a long scan is sensitive enough to that rounding that its final state can
+    only be compared at the same storage precision)."""
+    B, T, _ = x.shape
+    d = np.shape(Wq)[1] // H  # the projections may cover a subset of the heads
     x = np.asarray(x, np.float64)
 
     def heads(w):
@@ -46,6 +60,10 @@ def front_end(x, Wq, Wk, Wv, Wg, bg, H, eta_scale):
     alpha = _sigmoid(g[..., :H])
     eta = eta_scale * _sigmoid(g[..., H:2 * H])
     beta = _sigmoid(g[..., 2 * H:])
+    if store == "bf16":
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    elif store is not None:
+        raise ValueError(f"store={store!r}")
     return q, k, v, alpha, eta, beta
 
 

@@ -9,7 +9,10 @@
     (y_attn / 2) Wo exactly;
   * front end: rows of x that are unit vectors pick rows of the projection matrices (q, k
     normalized), and the gates are the sigmoids of the matching Wg row plus bg;
-  * memory branch: the C oracle's scan of the front end's q, k, v, gates.
+  * memory branch: the C oracle's scan of the front end's q, k, v, gates;
+  * bf16 storage: round_bf16 agrees with an integer round-to-nearest-even on the float32
+    bit pattern (the generator's, an independent implementation) and with exhaustive
+    neighbours: no bfloat16 value lies strictly closer.
 """
 import numpy as np
 import pytest
@@ -99,3 +102,27 @@ def test_front_end_on_unit_rows_and_memory_branch():
                           th0, np.zeros((H, P)), 4, widths)
     np.testing.assert_array_equal(mid["y_mem"], y)
     np.testing.assert_allclose(mid["o"], 1 / (1 + np.exp(-y)) * mid["y_attn"], rtol=1e-15)
+
+
+def test_round_bf16_is_nearest_even():
+    import synthetic as S
+
+    rng = np.random.default_rng(4)
+    a = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-20, 20, 20000),
+                        [0.0, -0.0, 1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8)]])
+    a32 = a.astype(np.float32)
+    got = mag.round_bf16(a32)
+    ref = S.bf16_bits_to_f32(S.f32_to_bf16_bits(a32)).astype(np.float64)
+    np.testing.assert_array_equal(got, ref)
+    # ties go to the even mantissa: 1 + 2^-8 -> 1, 1 + 3 * 2^-8 -> 1 + 2^-6
+    assert got[-3] == 1.0 and got[-2] == 1.0 + 2.0 ** -6 and got[-1] == -1.0
+    # nearest: the two bf16 neighbours (one ulp, 2^-7 relative, up and down) are no closer
+    for x, y in zip(a32[:200], got[:200]):
+        ulp = 2.0 ** (np.floor(np.log2(abs(y))) - 7) if y != 0 else 0.0
+        for n in (y - ulp, y + ulp):
+            assert abs(n - x) >= abs(y - x)
+    x = np.random.default_rng(5).standard_normal((1, 4, 8))
+    W = np.eye(8)
+    q, k, v, *_ = mag.front_end(x, W, W, W, np.zeros((8, 3)), np.zeros(3), 1, 0.1, store="bf16")
+    np.testing.assert_array_equal(v, mag.round_bf16(x.reshape(1, 4, 1, 8)))
+    np.testing.assert_array_equal(q, mag.round_bf16(q))
