@@ -255,9 +255,74 @@ def bench_backward(tm, torch, t, wl, seed, steps, warmup):
     tf = flops / (ms * 1e-3) / 1e12
     del ws
     return {"ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "steps": steps,
-            "workspace_bytes": n, "kernels": "bwd_forward_kernel + bwd_reverse_kernel",
+            "workspace_bytes": n, "kernels": "bwd_forward_kernel + bwd_step_kernel",
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAKS["mfma_f32"],
                          "unit": "TFLOP/s", "frac": tf / PEAKS["mfma_f32"],
+                         "alg_flops_per_launch": flops}}
+
+
+def mag_alg_flops(B, T, H, widths, C, W):
+    """Products of one MAG block (memory as gate) by part: the front-end projection
+    x W_in^T (2 D (3D + 3H) per token), the memory scan (the scan's own count), causal
+    sliding-window attention (4 d per query-key pair: the score dot product and the value
+    accumulation; sum_t min(t + 1, W) pairs per (b, h)) and the output projection
+    (2 D^2 per token)."""
+    d = widths[0]
+    D, M = H * d, B * T
+    pairs = T * W - W * (W - 1) // 2 if T >= W else T * (T + 1) // 2
+    return {"projection": 2.0 * M * D * (3 * D + 3 * H),
+            "memory_scan": float(alg_flops_per_token_head(widths, C)) * M * H,
+            "attention": 4.0 * d * B * H * pairs,
+            "output_projection": 2.0 * M * D * D}
+
+
+def bench_mag(tm, torch, wl, window, seed, steps, warmup):
+    """One MAG block (titans_mag_forward) at the workload's shape with model width
+    D = H d: x [B, T, D] bf16, seeded weights, the sliding window `window`.  Timed by HIP
+    events around the call on its stream; the roofline is the block's algorithmic
+    products against the bf16 matrix-core peak (all four parts run on bf16 MFMA)."""
+    import synthetic
+
+    mi = synthetic.make_mag_inputs(wl, window, seed)
+    dev = "cuda"
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, w_in, w_out = bf(mi.x), bf(mi.w_in), bf(mi.w_out)
+    b_gate = torch.from_numpy(mi.b_gate).to(dev)
+    B, H = wl.batch, wl.heads
+    th0 = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(mi.theta0, (B,) + mi.theta0.shape))).to(dev)
+    s0 = torch.zeros_like(th0)
+    n = tm.mag_workspace_size(x, wl.chunk, window, wl.widths, wl.eta_scale)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    out, thT, sT = torch.empty_like(x), torch.empty_like(th0), torch.empty_like(th0)
+
+    def run():
+        tm.mag_forward(x, w_in, b_gate, w_out, th0, s0, wl.chunk, window, wl.widths,
+                       wl.eta_scale, out=out, theta_T=thT, s_T=sT, workspace=ws)
+    for _ in range(warmup):
+        run()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    parts = mag_alg_flops(B, wl.seq_len, H, wl.widths, wl.chunk, window)
+    flops = sum(parts.values())
+    tf = flops / (ms * 1e-3) / 1e12
+    del ws
+    return {"ms": ms, "tokens_per_s": B * wl.seq_len / (ms * 1e-3), "steps": steps,
+            "model_width": H * wl.d, "window": window, "workspace_bytes": n,
+            "kernels": "gemm_nt_kernel (projection) + prep_kernel + memory scan + "
+                       "swa_gate_kernel + gemm_nt_kernel (output)",
+            "alg_flops_by_part": parts,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAKS["mfma_bf16"],
+                         "unit": "TFLOP/s", "frac": tf / PEAKS["mfma_bf16"],
                          "alg_flops_per_launch": flops}}
 
 
@@ -275,6 +340,8 @@ def main():
     ap.add_argument("--no-biases", action="store_true")
     ap.add_argument("--no-surprise", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-mag", action="store_true")
+    ap.add_argument("--mag-window", type=int, default=4096)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -393,6 +460,9 @@ def main():
         result["surprise"] = bench_surprise(tm, torch, t, wl, (y, thT, sT), min(args.steps, 5), 1)
     if not args.no_backward:
         result["backward"] = bench_backward(tm, torch, t, wl, args.seed, min(args.steps, 3), 1)
+    if not args.no_mag and wl.io == "bf16" and wl.widths[0] == wl.widths[-1]:
+        result["mag_block"] = bench_mag(tm, torch, wl, args.mag_window, args.seed,
+                                        min(args.steps, 5), 1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_sample_rows, args.cpu_sample_tokens)
     print(json.dumps(result), flush=True)

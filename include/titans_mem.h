@@ -281,7 +281,7 @@ titans_status titans_mem_retrieve(const titans_scan_desc* desc, const titans_mlp
  */
 typedef struct {
     int64_t batch;      /* B >= 0 */
-    int64_t seq_len;    /* T >= 0 */
+    int64_t seq_len;    /* 0 <= T < 2^30, B T < 2^32 */
     int64_t heads;      /* H >= 1; H d <= 65536 */
     int32_t chunk;      /* memory chunk length C >= 1 */
     int32_t window;     /* attention window W >= 1 (W >= T: full causal attention) */

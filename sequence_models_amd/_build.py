@@ -30,7 +30,7 @@ SOURCES = {
     "scan_pair.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "retrieve_mfma.hip": [],
     "retrieve_wide.hip": [],
-    "mag.hip": [],
+    "mag.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -726,8 +726,9 @@ static titans_status prepare_mag(const titans_mag_desc* desc, const titans_mlp_d
     const int64_t tiles_m = (desc->batch * desc->seq_len + 127) / 128;
     const int64_t tiles_n = (3 * desc->heads * d + 3 * desc->heads + 127) / 128;
     if (desc->batch * desc->heads * nqb > 0xffffffffLL || tiles_m * tiles_n > 0xffffffffLL ||
-        desc->batch * desc->seq_len > 0xffffffffLL)
-        return fail(TITANS_ERR_UNSUPPORTED, "batch * seq_len too large for one launch");
+        desc->batch * desc->seq_len > 0xffffffffLL || desc->seq_len >= (1LL << 30))
+        return fail(TITANS_ERR_UNSUPPORTED,
+                    "seq_len >= 2^30 or batch * seq_len too large for one launch");
     sd = mag_scan_desc(desc, d, m.P);
     if ((st = prepare_scan(&sd, mlp, a))) return st;
     g = titans::MagArgs{};

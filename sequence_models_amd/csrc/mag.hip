@@ -20,11 +20,12 @@
 //                    projection writes fp32, the output projection bf16.
 //   prep_kernel      one workgroup per token: per-head norms of q and k (shuffle sums over
 //                    the lanes that hold one head), bf16 q, k, v, and the three gates.
-//   swa_gate_kernel  flash-style attention: 64 queries (16 per wave) against 64-key
-//                    blocks in LDS, scores computed transposed (keys x queries) so each
-//                    lane owns one query's running max and sum, probabilities fed back to
-//                    the value product straight from the score accumulators; the
-//                    epilogue gates with sigmoid(y_mem) and stores o in bf16.
+//   swa_gate_kernel  flash-style attention: 128 queries (32 per wave) against 64-key
+//                    blocks double-buffered in LDS, scores computed transposed (keys x
+//                    queries) so each lane owns one query's running max and sum,
+//                    probabilities fed back to the value product straight from the score
+//                    accumulators; the epilogue gates with sigmoid(y_mem) and stores o in
+//                    bf16.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -213,17 +214,23 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ pro
 
 // ------------------------------------------------------------------------- attention
 
-constexpr int kQB = 64;  // queries per workgroup, 16 per wave
-constexpr int kKB = 64;  // keys per LDS block
+constexpr int kQW = 32;         // queries per wave: two 16-query tiles
+constexpr int kQB = 4 * kQW;    // queries per workgroup
+constexpr int kKB = 64;         // keys per LDS block
+constexpr int kVP = kKB + 4;    // transposed value rows in LDS (bf16 pitch)
 
-// One workgroup per (b, h, 64-query block).  q, k, v, y_mem and o are [B, T, H, kD] bf16
-// rows of pitch D = H kD.  Lane (g, j) of wave w owns query q0 + 16 w + j.  Per key block:
-// S^T tile t (keys 16 t .. 16 t + 15) = K Q^T, so lane (g, j) holds the scores of keys
-// 16 t + 4 g + r for its query; masked scores are -inf; the running max is shared by the
-// four lanes of a query (two xor shuffles) while each lane keeps a partial sum of its own
-// probabilities; O^T += V^T P^T takes P^T straight from the score registers (the
+// One workgroup per (b, h, 128-query block); q, k, v, y_mem and o are [B, T, H, kD] bf16
+// rows of pitch D = H kD.  Wave w owns queries q0 + 32 w + 16 u + j (u = 0, 1) at lane
+// (g, j).  Per 64-key block: S^T tile (u, t) = K_t Q_u^T, so lane (g, j) holds the scores
+// of keys 16 t + 4 g + r for its query of tile u; the max is shared by the four lanes of
+// a query (two xor shuffles); O^T += V^T P^T and the row sums (ones x P^T) take P^T straight from the score registers (the
 // accumulator's row index, the key, is the reduction index of the value product) and V^T
-// from a transposed LDS copy.
+// from a transposed LDS copy.  Key and value blocks are double-buffered: the next block's
+// global loads are in flight while the current one is used.  Blocks that lie wholly
+// outside a wave's windows are skipped by that wave; masks are applied only on blocks at
+// the diagonal or the window's edge.  Exponentials are the hardware's base-2 exponential
+// (v_exp_f32): arguments are <= 0 and results below fp32's normal range flush to 0, which
+// a probability that small does not notice.
 template <int kD>
 __global__ __launch_bounds__(256) void swa_gate_kernel(const __bf16* __restrict__ q,
                                                        const __bf16* __restrict__ k,
@@ -231,10 +238,12 @@ __global__ __launch_bounds__(256) void swa_gate_kernel(const __bf16* __restrict_
                                                        const __bf16* __restrict__ ymem,
                                                        __bf16* __restrict__ o, int64_t T, int H,
                                                        int window, float scale_log2, int nqb) {
-    constexpr int kKP = kD + 8;   // key rows in LDS (bf16 pitch)
-    constexpr int kVP = kKB + 8;  // transposed value rows in LDS
-    __shared__ __align__(16) __bf16 ks[kKB * kKP];
-    __shared__ __align__(16) __bf16 vt[kD * kVP];
+    constexpr int kKP = kD + 8;                   // key rows in LDS (bf16 pitch)
+    constexpr int kKPieces = kKB * kD / 8;        // 16-byte pieces of a key block
+    constexpr int kVTasks = (kKB / 4) * (kD / 4); // 4 keys x 4 columns of a value block
+    constexpr int kNK = (kKPieces + 255) / 256, kNV = (kVTasks + 255) / 256;
+    __shared__ __align__(16) __bf16 ks[2][kKB * kKP];
+    __shared__ __align__(16) __bf16 vt[2][kD * kVP];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, j = lane & 15;
     const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -245,106 +254,193 @@ __global__ __launch_bounds__(256) void swa_gate_kernel(const __bf16* __restrict_
     const int64_t D = static_cast<int64_t>(H) * kD;
     const int64_t base = b * T * D + static_cast<int64_t>(h) * kD;  // (b, 0, h, 0)
     const int64_t q0 = static_cast<int64_t>(qb) * kQB;
-    const int64_t qi = q0 + 16 * wave + j;
-    const bool qok = qi < T;
+    const int64_t wq0 = q0 + kQW * wave, wlast = wq0 + kQW - 1;
 
-    bf16x8 qf[kD / 32];
+    bf16x8 qf[2][kD / 32];
 #pragma unroll
-    for (int kb = 0; kb < kD / 32; ++kb)
-        qf[kb] = qok ? *reinterpret_cast<const bf16x8*>(q + base + qi * D + 32 * kb + 8 * g) : zero8();
-
-    f32x4 acc[kD / 16];
+    for (int u = 0; u < 2; ++u) {
+        const int64_t qi = wq0 + 16 * u + j;
 #pragma unroll
-    for (int dt = 0; dt < kD / 16; ++dt) acc[dt] = fused::zero4();
-    float m_run = -INFINITY, l_run = 0.0f;
+        for (int kb = 0; kb < kD / 32; ++kb)
+            qf[u][kb] = qi < T ? *reinterpret_cast<const bf16x8*>(q + base + qi * D + 32 * kb + 8 * g)
+                               : zero8();
+    }
+    f32x4 acc[2][kD / 16], lsum[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        lsum[u] = fused::zero4();
+#pragma unroll
+        for (int dt = 0; dt < kD / 16; ++dt) acc[u][dt] = fused::zero4();
+    }
+    float m_ref[2] = {-INFINITY, -INFINITY};
+    const __bf16 one = static_cast<__bf16>(1.0f);
+    const bf16x8 ones = {one, one, one, one, one, one, one, one};
 
     const int64_t qlast = (q0 + kQB - 1 < T - 1) ? q0 + kQB - 1 : T - 1;
     const int64_t kfirst = q0 - window + 1 > 0 ? q0 - window + 1 : 0;
-    for (int64_t kb0 = kfirst / kKB * kKB; kb0 <= qlast; kb0 += kKB) {
-        __syncthreads();  // the previous block's LDS reads are done
-        constexpr int kPieces = kKB * kD / 8;
-        for (int c = tid; c < kPieces; c += 256) {
-            const int r = c / (kD / 8), cc = (c % (kD / 8)) * 8;
-            const int64_t key = kb0 + r;
-            bf16x8 kv = zero8(), vv = zero8();
-            if (key < T) {
-                kv = *reinterpret_cast<const bf16x8*>(k + base + key * D + cc);
-                vv = *reinterpret_cast<const bf16x8*>(v + base + key * D + cc);
-            }
-            *reinterpret_cast<bf16x8*>(&ks[r * kKP + cc]) = kv;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) vt[(cc + i) * kVP + r] = vv[i];
-        }
-        __syncthreads();
+    const int64_t kbeg = kfirst / kKB * kKB;
+    const int nblk = static_cast<int>((qlast - kbeg) / kKB) + 1;
 
-        f32x4 s[4];
+    bf16x8 rk[kNK];
+    bf16x4 rv[kNV][4];
+    // keys past T (only in the last block of a sequence) are zero
+    auto fetch = [&](int64_t kb0) {
+        const bool full = kb0 + kKB <= T;
+        const __bf16* kp = k + base + kb0 * D;
+        const __bf16* vp = v + base + kb0 * D;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            s[t] = fused::zero4();
-#pragma unroll
-            for (int kb = 0; kb < kD / 32; ++kb) {
-                const bf16x8 kf =
-                    *reinterpret_cast<const bf16x8*>(&ks[(16 * t + j) * kKP + 32 * kb + 8 * g]);
-                s[t] = mma(kf, qf[kb], s[t]);
+        for (int i = 0; i < kNK; ++i) {
+            const int c = tid + 256 * i;
+            if (c < kKPieces) {
+                const int r = c / (kD / 8);
+                rk[i] = (full || kb0 + r < T)
+                            ? *reinterpret_cast<const bf16x8*>(kp + r * D + (c % (kD / 8)) * 8)
+                            : zero8();
             }
         }
-        float mx = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int i = 0; i < kNV; ++i) {
+            const int t = tid + 256 * i;
+            if (t < kVTasks) {
+                const int cg = t % (kD / 4), kg = t / (kD / 4);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t key = kb0 + 16 * t + 4 * g + r;
-                const bool ok = key <= qi && key > qi - window;
-                const float x = ok ? s[t][r] * scale_log2 : -INFINITY;
-                s[t][r] = x;
-                mx = fmaxf(mx, x);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float corr = exp2f(m_run - m_use);
-        m_run = m_new;
-        l_run *= corr;
-#pragma unroll
-        for (int dt = 0; dt < kD / 16; ++dt) acc[dt] *= corr;
-        bf16x4 pb[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            f32x4 p;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = exp2f(s[t][r] - m_use);
-            pb[t] = fused::bf4(p);
-            // the sum runs over the rounded probabilities, so the weights applied to the
-            // values are exactly normalized
-            const f32x4 pr = fused::f4(pb[t]);
-            l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 pf = fused::cat(pb[2 * kb], pb[2 * kb + 1]);
-#pragma unroll
-            for (int dt = 0; dt < kD / 16; ++dt) {
-                const __bf16* p = &vt[(16 * dt + j) * kVP + 32 * kb + 4 * g];
-                const bf16x8 vf = fused::cat(*reinterpret_cast<const bf16x4*>(p),
-                                             *reinterpret_cast<const bf16x4*>(p + 16));
-                acc[dt] = mma(vf, pf, acc[dt]);
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * kg + e;
+                    const __bf16 z = static_cast<__bf16>(0.0f);
+                    rv[i][e] = (full || kb0 + r < T)
+                                   ? *reinterpret_cast<const bf16x4*>(vp + r * D + 4 * cg)
+                                   : bf16x4{z, z, z, z};
+                }
             }
         }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < kNK; ++i) {
+            const int c = tid + 256 * i;
+            if (c < kKPieces)
+                *reinterpret_cast<bf16x8*>(&ks[buf][(c / (kD / 8)) * kKP + (c % (kD / 8)) * 8]) = rk[i];
+        }
+#pragma unroll
+        for (int i = 0; i < kNV; ++i) {
+            const int t = tid + 256 * i;
+            if (t < kVTasks) {
+                const int cg = t % (kD / 4), kg = t / (kD / 4);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    *reinterpret_cast<bf16x4*>(&vt[buf][(4 * cg + c) * kVP + 4 * kg]) =
+                        bf16x4{rv[i][0][c], rv[i][1][c], rv[i][2][c], rv[i][3][c]};
+            }
+        }
+    };
+
+    fetch(kbeg);
+    stash(0);
+    __syncthreads();
+    for (int ib = 0; ib < nblk; ++ib) {
+        const int buf = ib & 1;
+        const int64_t kb0 = kbeg + static_cast<int64_t>(ib) * kKB;
+        const bool more = ib + 1 < nblk;
+        if (more) fetch(kb0 + kKB);
+        // some (query, key) of this wave and block with key <= query < key + window
+        const bool live = wq0 < T && kb0 <= wlast && kb0 + kKB - 1 > wq0 - window;
+        if (live) {
+            const bool edge = kb0 + kKB - 1 > wq0 || kb0 <= wlast - window;
+            f32x4 st[2][4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                bf16x8 kf[kD / 32];
+#pragma unroll
+                for (int kb = 0; kb < kD / 32; ++kb)
+                    kf[kb] = *reinterpret_cast<const bf16x8*>(&ks[buf][(16 * t + j) * kKP + 32 * kb + 8 * g]);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    st[u][t] = fused::zero4();
+#pragma unroll
+                    for (int kb = 0; kb < kD / 32; ++kb) st[u][t] = mma(kf[kb], qf[u][kb], st[u][t]);
+                }
+            }
+            bf16x8 pf[2][2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (edge) {
+                    // key - query for key kb0 (|.| < T + 2 kQB: int32 by the host's limit on T)
+                    const int rel0 = static_cast<int>(kb0 - (wq0 + 16 * u + j)) + 4 * g;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int rel = rel0 + 16 * t + r;
+                            if (!(rel <= 0 && rel > -window)) st[u][t][r] = -INFINITY;
+                        }
+                }
+                float mx = -INFINITY;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    mx = fmaxf(fmaxf(fmaxf(mx, st[u][t][0]), fmaxf(st[u][t][1], st[u][t][2])), st[u][t][3]);
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                // The exponentials are taken against a reference that moves only when the
+                // block's max exceeds it by more than 8 (a factor of 2^8), so most blocks
+                // rescale nothing; probabilities stay <= 2^8.
+                const float ms = mx * scale_log2;
+                const bool grow = ms > m_ref[u] + 8.0f;
+                if (__ballot(grow)) {
+                    // lanes that keep their reference (possibly still -inf) scale by 1
+                    const float corr = grow ? __builtin_amdgcn_exp2f(m_ref[u] - ms) : 1.0f;
+                    if (grow) m_ref[u] = ms;
+                    lsum[u] *= corr;
+#pragma unroll
+                    for (int dt = 0; dt < kD / 16; ++dt) acc[u][dt] *= corr;
+                }
+                const float m_use = m_ref[u] == -INFINITY ? 0.0f : m_ref[u];
+                bf16x4 pb[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    f32x4 p;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        p[r] = __builtin_amdgcn_exp2f(fmaf(st[u][t][r], scale_log2, -m_use));
+                    pb[t] = fused::bf4(p);
+                }
+                pf[u][0] = fused::cat(pb[0], pb[1]);
+                pf[u][1] = fused::cat(pb[2], pb[3]);
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int dt = 0; dt < kD / 16; ++dt) {
+                    const __bf16* p = &vt[buf][(16 * dt + j) * kVP + 32 * kb + 4 * g];
+                    const bf16x8 vf = fused::cat(*reinterpret_cast<const bf16x4*>(p),
+                                                 *reinterpret_cast<const bf16x4*>(p + 16));
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) acc[u][dt] = mma(vf, pf[u][kb], acc[u][dt]);
+                }
+            // row sums of the rounded probabilities on the matrix cores: every row of
+            // ones * P^T is the sum, so each lane's four results are its query's
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) lsum[u] = mma(ones, pf[u][kb], lsum[u]);
+        }
+        if (more) stash(buf ^ 1);
+        __syncthreads();
     }
-    float l = l_run;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (!qok) return;
-    const float inv = 1.0f / l;
 #pragma unroll
-    for (int dt = 0; dt < kD / 16; ++dt) {
-        const int64_t at = base + qi * D + 16 * dt + 4 * g;
-        const f32x4 ym = fused::f4(*reinterpret_cast<const bf16x4*>(ymem + at));
-        f32x4 out;
+    for (int u = 0; u < 2; ++u) {
+        const float l = lsum[u][0];
+        const int64_t qi = wq0 + 16 * u + j;
+        if (qi >= T) continue;
+        const float inv = 1.0f / l;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) out[r] = sigm(ym[r]) * (acc[dt][r] * inv);
-        *reinterpret_cast<bf16x4*>(o + at) = fused::bf4(out);
+        for (int dt = 0; dt < kD / 16; ++dt) {
+            const int64_t at = base + qi * D + 16 * dt + 4 * g;
+            const f32x4 ym = fused::f4(*reinterpret_cast<const bf16x4*>(ymem + at));
+            f32x4 out;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) out[r] = sigm(ym[r]) * (acc[u][dt][r] * inv);
+            *reinterpret_cast<bf16x4*>(o + at) = fused::bf4(out);
+        }
     }
 }
 
