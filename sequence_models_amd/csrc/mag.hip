@@ -18,6 +18,8 @@
 //   gemm_nt_kernel   C = A W^T on v_mfma_f32_16x16x32_bf16, 128 x 128 tiles, 4 waves of
 //                    64 x 64, k staged 32 deep through double-buffered LDS; the front-end
 //                    projection writes fp32, the output projection bf16.
+//                    When D is a multiple of 64 the projection's epilogue also normalizes
+//                    q and k per head and applies the gates (ProjFront); otherwise:
 //   prep_kernel      one workgroup per token: per-head norms of q and k (shuffle sums over
 //                    the lanes that hold one head), bf16 q, k, v, and the three gates.
 //   swa_gate_kernel  flash-style attention: 128 queries (32 per wave) against 64-key
@@ -61,6 +63,23 @@ constexpr int kGT = 128;       // tile extent in M and in N
 constexpr int kGK = 32;        // k per stage
 constexpr int kGP = kGK + 8;   // LDS row pitch in bf16 (80 bytes)
 
+// Epilogues see a wave's whole 64 x 64 result: acc[in][im] holds C[r0 + 16 im + j]
+// [c0 + 16 in + 4 g + r]; red is 2 KiB of LDS free for the epilogue, and every wave of the
+// workgroup calls tile() (so it may synchronize).
+template <class Store>
+struct PerElement {
+    Store st;
+    __device__ void tile(const f32x4 (&acc)[4][4], int64_t r0, int c0, int wn, int g, int j,
+                         int64_t M, float* red) const {
+#pragma unroll
+        for (int im = 0; im < 4; ++im) {
+            const int64_t m = r0 + 16 * im + j;
+            if (m >= M) continue;
+#pragma unroll
+            for (int in = 0; in < 4; ++in) st(m, c0 + 16 * in + 4 * g, acc[in][im]);
+        }
+    }
+};
 struct StoreF32 {
     float* p;
     int64_t ld;
@@ -75,6 +94,75 @@ struct StoreBf16 {
     int n_lim;
     __device__ void operator()(int64_t m, int n, f32x4 v) const {
         if (n < n_lim) *reinterpret_cast<bf16x4*>(p + m * ld + n) = fused::bf4(v);
+    }
+};
+
+__device__ __forceinline__ float sigm(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+// The front end in the projection's epilogue (D a multiple of 64, d = 32, 64 or 128): a
+// wave's 64-column strip lies in one of the q, k, v, gate sections; in q and k it holds two
+// heads (d = 32), one (64) or half of one (128, the other half in the partner wave
+// wn ^ 1, combined through LDS).  Sums of squares per row: the lane's 16 (or 8) values,
+// then xor shuffles over the four lanes g that share a row.
+struct ProjFront {
+    int D, H, d;
+    float eta_scale;
+    const float* bg;
+    __bf16 *q, *k, *v;
+    float *alpha, *eta, *beta;
+    __device__ void tile(const f32x4 (&acc)[4][4], int64_t r0, int c0, int wn, int g, int j,
+                         int64_t M, float* red) const {
+        const int sec = c0 < 3 * D ? c0 / D : 3;
+#pragma unroll
+        for (int im = 0; im < 4; ++im) {
+            const int64_t m = r0 + 16 * im + j;
+            float s0 = 0.f, s1 = 0.f;  // columns 0..31 and 32..63 of the strip
+#pragma unroll
+            for (int in = 0; in < 4; ++in) {
+                const float e = acc[in][im][0] * acc[in][im][0] + acc[in][im][1] * acc[in][im][1] +
+                                acc[in][im][2] * acc[in][im][2] + acc[in][im][3] * acc[in][im][3];
+                if (in < 2) s0 += e; else s1 += e;
+            }
+            s0 += __shfl_xor(s0, 16);
+            s0 += __shfl_xor(s0, 32);
+            s1 += __shfl_xor(s1, 16);
+            s1 += __shfl_xor(s1, 32);
+            float n0 = s0 + s1, n1 = s0 + s1;  // d = 64: one head
+            if (d == 32) {
+                n0 = s0;
+                n1 = s1;
+            } else if (d == 128) {
+                // both halves' sums meet in LDS: red[wm-local row][wn]
+                __syncthreads();
+                if (g == 0) red[(static_cast<int>(r0 & 127) + 16 * im + j) * 2 + wn] = s0 + s1;
+                __syncthreads();
+                n0 = n1 = red[(static_cast<int>(r0 & 127) + 16 * im + j) * 2] +
+                          red[(static_cast<int>(r0 & 127) + 16 * im + j) * 2 + 1];
+            }
+            if (m >= M || (sec == 3 && c0 >= 3 * D + 3 * H)) continue;
+            if (sec < 3) {
+                __bf16* dst = sec == 0 ? q : sec == 1 ? k : v;
+                const float i0 = sec == 2 ? 1.0f : 1.0f / sqrtf(n0);
+                const float i1 = sec == 2 ? 1.0f : 1.0f / sqrtf(n1);
+                const int cs = c0 - sec * D;
+#pragma unroll
+                for (int in = 0; in < 4; ++in)
+                    *reinterpret_cast<bf16x4*>(dst + m * D + cs + 16 * in + 4 * g) =
+                        fused::bf4(acc[in][im] * (in < 2 ? i0 : i1));
+            } else {
+#pragma unroll
+                for (int in = 0; in < 4; ++in)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int gc = c0 - 3 * D + 16 * in + 4 * g + r;
+                        if (gc >= 3 * H) continue;
+                        const float sgm = sigm(acc[in][im][r] + bg[gc]);
+                        const int which = gc / H, h = gc - which * H;
+                        float* dst = which == 0 ? alpha : which == 1 ? eta : beta;
+                        dst[m * H + h] = which == 1 ? eta_scale * sgm : sgm;
+                    }
+            }
+        }
     }
 };
 
@@ -143,13 +231,8 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const __bf16* __restrict__
         if (s + 1 < nk) store(cur ^ 1);
         __syncthreads();
     }
-#pragma unroll
-    for (int im = 0; im < 4; ++im) {
-        const int64_t m = m0 + wm * 64 + 16 * im + j;
-        if (m >= M) continue;
-#pragma unroll
-        for (int in = 0; in < 4; ++in) epi(m, n0 + wn * 64 + 16 * in + 4 * g, acc[in][im]);
-    }
+    // the main loop ended on a barrier: the staging buffers are free
+    epi.tile(acc, m0 + wm * 64, n0 + wn * 64, wn, g, j, M, reinterpret_cast<float*>(&sa[0][0]));
 }
 
 template <class Epi>
@@ -164,8 +247,6 @@ static hipError_t gemm_nt(const __bf16* A, int64_t lda, const __bf16* W, int64_t
 }
 
 // ------------------------------------------------------------------------- front end
-
-__device__ __forceinline__ float sigm(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 // Token row m of the projection (fp32, pitch ldp): columns [0, D) q, [D, 2D) k,
 // [2D, 3D) v, [3D, 3D + 3H) the gate logits.  Thread t handles the four columns 4t .. 4t+3
@@ -481,8 +562,14 @@ hipError_t launch_mag_front(const MagArgs& g, hipStream_t stream) {
     const int64_t M = g.B * g.T;
     const int D = static_cast<int>(g.H * g.d);
     const int N = 3 * D + 3 * static_cast<int>(g.H);
+    if (D % 64 == 0)  // normalization and gates in the GEMM's epilogue
+        return mag::gemm_nt(g.x, D, g.w_in, M, N, D,
+                            mag::ProjFront{D, static_cast<int>(g.H), g.d, g.eta_scale, g.b_gate,
+                                           g.q, g.k, g.v, g.alpha, g.eta, g.beta},
+                            stream);
     hipError_t e = mag::gemm_nt(g.x, D, g.w_in, M, N, D,
-                                mag::StoreF32{g.proj, g.ldp, static_cast<int>(g.ldp)}, stream);
+                                mag::PerElement<mag::StoreF32>{{g.proj, g.ldp, static_cast<int>(g.ldp)}},
+                                stream);
     if (e != hipSuccess || M == 0) return e;
     hipLaunchKernelGGL(mag::prep_kernel, dim3(static_cast<unsigned>(M)), dim3(256), 0, stream,
                        g.proj, g.ldp, static_cast<int>(g.H), g.d, g.eta_scale, g.b_gate, g.q, g.k,
@@ -517,7 +604,8 @@ hipError_t launch_mag_attention(const MagArgs& g, hipStream_t stream) {
 hipError_t launch_mag_out(const MagArgs& g, hipStream_t stream) {
     const int64_t M = g.B * g.T;
     const int D = static_cast<int>(g.H * g.d);
-    return mag::gemm_nt(g.o, D, g.w_out, M, D, D, mag::StoreBf16{g.out, D, D}, stream);
+    return mag::gemm_nt(g.o, D, g.w_out, M, D, D, mag::PerElement<mag::StoreBf16>{{g.out, D, D}},
+                        stream);
 }
 
 }  // namespace titans
