@@ -126,7 +126,7 @@ def test_mag_rejects_bad_arguments():
     wl = S.WORKLOADS["h16_d64_b8_t16k"].with_(heads=2)
     mi = S.make_mag_inputs(wl, 16, seed=3, seq_len=8, batch=1)
     x = _bf16(mi.x)
-    th = torch.zeros(1, 2, wl.params, device="cuda")
+    th = torch.zeros(1, 2, wl.params, dtype=torch.float32, device="cuda")
     args = (x, _bf16(mi.w_in), torch.from_numpy(mi.b_gate).cuda(), _bf16(mi.w_out), th, th.clone())
     with pytest.raises(sm.TitansError, match="window"):
         sm.mag_forward(*args, 64, 0, wl.widths, 0.1)

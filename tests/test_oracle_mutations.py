@@ -10,9 +10,19 @@ import os
 import subprocess
 
 import pytest
+import torch
 
 import oracle
 from tests import test_oracle_pins as pins
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _float64_default():
+    """The pins run with float64 as torch's default dtype (restored after this module)."""
+    prev = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(prev)
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "titans_oracle.c")
 

@@ -15,7 +15,16 @@ import torch
 import oracle
 from tests import chunk_form
 
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _float64_default():
+    """float64 as torch's default dtype for this module's tests only (restored after, so
+    it does not leak into tests collected later)."""
+    prev = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(prev)
 
 
 def _rand_theta(widths, rng, scale=1.0):
