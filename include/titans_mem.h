@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define TITANS_MEM_ABI_VERSION 4
+#define TITANS_MEM_ABI_VERSION 5
 #define TITANS_MAX_LAYERS 4
 
 typedef enum {
@@ -316,6 +316,53 @@ size_t titans_mag_workspace_size(const titans_mag_desc* desc, const titans_mlp_d
  * as the norm's definition does.
  */
 titans_status titans_mag_forward(const titans_mag_desc* desc, const titans_mlp_desc* mlp,
+                                 const void* x, const void* w_in, const float* b_gate,
+                                 const void* w_out, const float* theta0, const float* s0,
+                                 void* out, float* theta_T, float* s_T,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ------------------------------------------------------------------ MAC block
+ * One Titans block with the memory as context (the lowest.today summary, section
+ * "Varianti dell'Architettura Titans", memory as context; the 0h-n0.github.io
+ * explainer, section "3つのアーキテクチャ変種"): the sequence is processed in
+ * segments, each segment reads the long-term memory, and the reads join the
+ * attention's keys and values as a prefix.  Front end and output projection as
+ * in the MAG block (same weights and layouts).  Per segment of S tokens (from the
+ * call start; the last may be shorter):
+ *
+ *   h_t     = M_theta(q_t) for every token t of the segment, theta = the memory
+ *             state after every token before the segment
+ *   y_t     softmax(q.key / sqrt(d)) attention of q_t over the keys
+ *             [h_u, every u of the segment] then [k_u, u <= t of the segment],
+ *             values [h_u ...] then [v_u ...]
+ *   memory  the scan over the segment's k, v and gates (chunks restart at each
+ *           segment start), continuing from theta, s
+ *   out     y W_out^T
+ *
+ * Precision as in the MAG block (h stored in bf16).
+ */
+typedef struct {
+    int64_t batch;      /* B >= 0 */
+    int64_t seq_len;    /* 0 <= T < 2^30, B T < 2^32 */
+    int64_t heads;      /* H >= 1; H d <= 65536 */
+    int32_t chunk;      /* memory chunk length C >= 1 */
+    int32_t segment;    /* segment length S >= 1 */
+    float eta_scale;    /* finite, >= 0 */
+    int32_t reserved;   /* must be 0 */
+} titans_mac_desc;
+
+/* Workspace bytes titans_mac_forward needs (0 when B T = 0); SIZE_MAX if the arguments
+ * are invalid: the MAG block's pieces, the memory reads h (bf16 [B, T, H, d]) and the
+ * memory scan's workspace for one segment. */
+size_t titans_mac_workspace_size(const titans_mac_desc* desc, const titans_mlp_desc* mlp);
+
+/*
+ * Forward pass of one MAC block: the same arguments, layouts, alignment and
+ * overlap rules as titans_mag_forward.  theta_T and s_T hold the memory after the
+ * last token; they are also the running state between segments.
+ */
+titans_status titans_mac_forward(const titans_mac_desc* desc, const titans_mlp_desc* mlp,
                                  const void* x, const void* w_in, const float* b_gate,
                                  const void* w_out, const float* theta0, const float* s0,
                                  void* out, float* theta_T, float* s_T,

@@ -11,6 +11,8 @@ at import time -- there is no fallback.
     retrieve(q, theta, widths) -> y
     mag_forward(x, w_in, b_gate, w_out, theta0, s0, chunk, window, widths, eta_scale)
                   -> (out, theta_T, s_T)    one MAG block (memory as gate)
+    mac_forward(x, w_in, b_gate, w_out, theta0, s0, chunk, segment, widths, eta_scale)
+                  -> (out, theta_T, s_T)    one MAC block (memory as context)
 """
 from __future__ import annotations
 
@@ -19,7 +21,7 @@ import os
 
 import torch
 
-__all__ = ["mag_forward", "mag_workspace_size", "MagDesc", "scan", "scan_backward", "scan_backward_workspace_size", "retrieve", "scan_workspace_size", "scan_path", "retrieve_path", "param_count", "TitansError", "LIB_PATH",
+__all__ = ["mac_forward", "mac_workspace_size", "MacDesc", "mag_forward", "mag_workspace_size", "MagDesc", "scan", "scan_backward", "scan_backward_workspace_size", "retrieve", "scan_workspace_size", "scan_path", "retrieve_path", "param_count", "TitansError", "LIB_PATH",
            "lib", "ScanDesc", "MlpDesc", "MAX_LAYERS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtitans_mem.so")
@@ -46,6 +48,12 @@ class ScanDesc(ctypes.Structure):
 class MagDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64), ("heads", ctypes.c_int64),
                 ("chunk", ctypes.c_int32), ("window", ctypes.c_int32), ("eta_scale", ctypes.c_float),
+                ("reserved", ctypes.c_int32)]
+
+
+class MacDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64), ("heads", ctypes.c_int64),
+                ("chunk", ctypes.c_int32), ("segment", ctypes.c_int32), ("eta_scale", ctypes.c_float),
                 ("reserved", ctypes.c_int32)]
 
 
@@ -87,6 +95,11 @@ lib.titans_mag_workspace_size.restype = ctypes.c_size_t
 lib.titans_mag_workspace_size.argtypes = [ctypes.POINTER(MagDesc), ctypes.POINTER(MlpDesc)]
 lib.titans_mag_forward.restype = ctypes.c_int
 lib.titans_mag_forward.argtypes = ([ctypes.POINTER(MagDesc), ctypes.POINTER(MlpDesc)] + [_vp] * 10
+                                   + [ctypes.c_size_t, _vp])
+lib.titans_mac_workspace_size.restype = ctypes.c_size_t
+lib.titans_mac_workspace_size.argtypes = [ctypes.POINTER(MacDesc), ctypes.POINTER(MlpDesc)]
+lib.titans_mac_forward.restype = ctypes.c_int
+lib.titans_mac_forward.argtypes = ([ctypes.POINTER(MacDesc), ctypes.POINTER(MlpDesc)] + [_vp] * 10
                                    + [ctypes.c_size_t, _vp])
 lib.titans_mem_retrieve.restype = ctypes.c_int
 lib.titans_mem_retrieve.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc), _vp, _vp,
@@ -391,14 +404,8 @@ def mag_workspace_size(x, chunk, window, widths, eta_scale=1.0) -> int:
     return int(n)
 
 
-def mag_forward(x, w_in, b_gate, w_out, theta0, s0, chunk, window, widths, eta_scale, *,
-                out=None, theta_T=None, s_T=None, workspace=None):
-    """One MAG block on the current stream (titans_mag_forward).
-
-    x [B, T, D] bf16; w_in [3D + 3H, D] bf16 (q, k, v rows, then alpha, eta, beta gate
-    rows); b_gate [3H] float32; w_out [D, D] bf16; theta0, s0 [B, H, P] float32, with
-    H = D / widths[0].  Every tensor contiguous.  Returns (out [B, T, D] bf16, theta_T,
-    s_T [B, H, P])."""
+def _block(fn, size_fn, desc, x, w_in, b_gate, w_out, theta0, s0, widths, out, theta_T, s_T,
+           workspace):
     B, T, D = x.shape
     d = widths[0]
     H = D // d
@@ -417,15 +424,50 @@ def mag_forward(x, w_in, b_gate, w_out, theta0, s0, chunk, window, widths, eta_s
     for name, (t, dt, shape) in shapes.items():
         if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {shape}")
-    desc = _mag_desc(x, widths, chunk, window, eta_scale)
     mlp = mlp_desc(widths)
     if workspace is None:
-        n = lib.titans_mag_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+        n = size_fn(ctypes.byref(desc), ctypes.byref(mlp))
         if n == ctypes.c_size_t(-1).value:
             n = 0  # the call below reports the argument error
         workspace = torch.empty(int(n), dtype=torch.uint8, device=x.device) if n else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.titans_mag_forward(ctypes.byref(desc), ctypes.byref(mlp), _ptr(x), _ptr(w_in),
-                                  _ptr(b_gate), _ptr(w_out), _ptr(theta0), _ptr(s0), _ptr(out),
-                                  _ptr(theta_T), _ptr(s_T), _ptr(workspace), ws_bytes, _stream()))
+    _check(fn(ctypes.byref(desc), ctypes.byref(mlp), _ptr(x), _ptr(w_in), _ptr(b_gate),
+              _ptr(w_out), _ptr(theta0), _ptr(s0), _ptr(out), _ptr(theta_T), _ptr(s_T),
+              _ptr(workspace), ws_bytes, _stream()))
     return out, theta_T, s_T
+
+
+def mag_forward(x, w_in, b_gate, w_out, theta0, s0, chunk, window, widths, eta_scale, *,
+                out=None, theta_T=None, s_T=None, workspace=None):
+    """One MAG block on the current stream (titans_mag_forward).
+
+    x [B, T, D] bf16; w_in [3D + 3H, D] bf16 (q, k, v rows, then alpha, eta, beta gate
+    rows); b_gate [3H] float32; w_out [D, D] bf16; theta0, s0 [B, H, P] float32, with
+    H = D / widths[0].  Every tensor contiguous.  Returns (out [B, T, D] bf16, theta_T,
+    s_T [B, H, P])."""
+    return _block(lib.titans_mag_forward, lib.titans_mag_workspace_size,
+                  _mag_desc(x, widths, chunk, window, eta_scale), x, w_in, b_gate, w_out, theta0,
+                  s0, widths, out, theta_T, s_T, workspace)
+
+
+def _mac_desc(x, widths, chunk, segment, eta_scale) -> MacDesc:
+    m = _mag_desc(x, widths, chunk, segment, eta_scale)
+    return MacDesc(m.batch, m.seq_len, m.heads, m.chunk, m.window, m.eta_scale, 0)
+
+
+def mac_workspace_size(x, chunk, segment, widths, eta_scale=1.0) -> int:
+    """Workspace bytes of mac_forward for x [B, T, D] (raises on invalid arguments)."""
+    n = lib.titans_mac_workspace_size(ctypes.byref(_mac_desc(x, widths, chunk, segment, eta_scale)),
+                                      ctypes.byref(mlp_desc(widths)))
+    if n == ctypes.c_size_t(-1).value:
+        raise TitansError(-1, lib.titans_last_error().decode())
+    return int(n)
+
+
+def mac_forward(x, w_in, b_gate, w_out, theta0, s0, chunk, segment, widths, eta_scale, *,
+                out=None, theta_T=None, s_T=None, workspace=None):
+    """One MAC block on the current stream (titans_mac_forward): the MAG block's tensors,
+    segments of `segment` tokens whose memory reads prefix the attention's keys and values."""
+    return _block(lib.titans_mac_forward, lib.titans_mac_workspace_size,
+                  _mac_desc(x, widths, chunk, segment, eta_scale), x, w_in, b_gate, w_out, theta0,
+                  s0, widths, out, theta_T, s_T, workspace)

@@ -754,19 +754,16 @@ size_t titans_mag_workspace_size(const titans_mag_desc* desc, const titans_mlp_d
     return mag_own_bytes(g) + workspace_of(a, false);
 }
 
-titans_status titans_mag_forward(const titans_mag_desc* desc, const titans_mlp_desc* mlp,
-                                 const void* x, const void* w_in, const float* b_gate,
-                                 const void* w_out, const float* theta0, const float* s0,
-                                 void* out, float* theta_T, float* s_T, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-    g_last_error[0] = '\0';
-    titans::MagArgs g;
-    titans_scan_desc sd;
-    titans::ScanArgs a{};
-    titans_status st = prepare_mag(desc, mlp, g, sd, a);
-    if (st) return st;
-    const int64_t B = g.B, T = g.T, H = g.H, D = H * g.d, M = B * T, P = a.P;
+// Pointers, alignment, overlap and workspace of a block call (MAG or MAC): x [B, T, D],
+// W_in [3D + 3H, D], W_out [D, D] bf16, b_gate [3H], contiguous [B, H, P] states.
+static titans_status check_block_args(const titans::MagArgs& g, const titans::ScanArgs& a,
+                                      const void* x, const void* w_in, const float* b_gate,
+                                      const void* w_out, const float* theta0, const float* s0,
+                                      const void* out, const float* theta_T, const float* s_T,
+                                      const void* workspace, size_t workspace_bytes, size_t need) {
+    const int64_t B = g.B, H = g.H, D = H * g.d, M = B * g.T, P = a.P;
     const bool tokens = M > 0;
+    titans_status st;
     if (B > 0) {
         if (!theta0 || !s0 || !theta_T || !s_T)
             return fail(TITANS_ERR_INVALID_ARGUMENT, "theta0, s0, theta_T and s_T must be non-NULL");
@@ -789,9 +786,6 @@ titans_status titans_mag_forward(const titans_mag_desc* desc, const titans_mlp_d
         if (reinterpret_cast<uintptr_t>(b_gate) & 3u)
             return fail(TITANS_ERR_INVALID_ARGUMENT, "b_gate is not 4-byte aligned");
     }
-    const size_t own = tokens ? mag_own_bytes(g) : 0;
-    const size_t scan_ws = workspace_of(a, false);
-    const size_t need = tokens ? own + scan_ws : 0;
     const size_t state_bytes = static_cast<size_t>(B * H * P) * 4;
     const Span ins[6] = {tokens ? contiguous(x, static_cast<size_t>(M * D) * 2) : Span{},
                          tokens ? contiguous(w_in, static_cast<size_t>((3 * D + 3 * H) * D) * 2) : Span{},
@@ -818,7 +812,28 @@ titans_status titans_mag_forward(const titans_mag_desc* desc, const titans_mlp_d
         if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
             return fail(TITANS_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
     }
-    if (B == 0) return TITANS_OK;
+    return TITANS_OK;
+}
+
+titans_status titans_mag_forward(const titans_mag_desc* desc, const titans_mlp_desc* mlp,
+                                 const void* x, const void* w_in, const float* b_gate,
+                                 const void* w_out, const float* theta0, const float* s0,
+                                 void* out, float* theta_T, float* s_T, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    titans::MagArgs g;
+    titans_scan_desc sd;
+    titans::ScanArgs a{};
+    titans_status st = prepare_mag(desc, mlp, g, sd, a);
+    if (st) return st;
+    const bool tokens = g.B * g.T > 0;
+    const size_t own = tokens ? mag_own_bytes(g) : 0;
+    const size_t scan_ws = workspace_of(a, false);
+    const size_t need = tokens ? own + scan_ws : 0;
+    if ((st = check_block_args(g, a, x, w_in, b_gate, w_out, theta0, s0, out, theta_T, s_T,
+                               workspace, workspace_bytes, need)))
+        return st;
+    if (g.B == 0) return TITANS_OK;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (!tokens)  // no tokens: the memory passes through unchanged
         return scan_impl(&sd, mlp, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, theta0, s0,
@@ -839,6 +854,115 @@ titans_status titans_mag_forward(const titans_mag_desc* desc, const titans_mlp_d
         return hip_fail(e, "MAG attention launch");
     if ((e = titans::launch_mag_out(g, hs)) != hipSuccess)
         return hip_fail(e, "MAG output projection launch");
+    return TITANS_OK;
+}
+
+// ---------------------------------------------------------------- MAC block
+
+static titans_mag_desc mac_as_mag(const titans_mac_desc* d) {
+    titans_mag_desc m{};
+    m.batch = d->batch;
+    m.seq_len = d->seq_len;
+    m.heads = d->heads;
+    m.chunk = d->chunk;
+    m.window = d->segment;  // validated as >= 1 like a window
+    m.eta_scale = d->eta_scale;
+    m.reserved = d->reserved;
+    return m;
+}
+
+// The MAG layout, then the memory reads h (bf16 [B, T, H, d]), then the scan's workspace
+// for one segment; `seg` receives the scan descriptor of a segment of `len` tokens.
+struct MacPlan {
+    titans::MagArgs g;
+    titans_scan_desc sd;
+    titans::ScanArgs a;
+    int64_t S;
+    size_t own, scan_ws;
+};
+
+static titans_status prepare_mac(const titans_mac_desc* desc, const titans_mlp_desc* mlp,
+                                 MacPlan& p) {
+    if (!desc) return fail(TITANS_ERR_INVALID_ARGUMENT, "desc and mlp must be non-NULL");
+    const titans_mag_desc md = mac_as_mag(desc);
+    p.a = titans::ScanArgs{};
+    titans_status st = prepare_mag(&md, mlp, p.g, p.sd, p.a);
+    if (st) return st;
+    p.S = desc->segment;
+    const int64_t M = p.g.B * p.g.T, D = p.g.H * p.g.d;
+    p.own = M > 0 ? mag_own_bytes(p.g) + static_cast<size_t>((M * D * 2 + 255) / 256 * 256) : 0;
+    p.scan_ws = 0;
+    // the segments' scans (the first is the longest; the last may be shorter)
+    const int64_t T = p.g.T;
+    const int64_t lens[2] = {T < p.S ? T : p.S, T % p.S};
+    for (int i = 0; i < 2; ++i) {
+        if (lens[i] == 0) continue;
+        titans_scan_desc sdi = p.sd;
+        sdi.seq_len = lens[i];
+        titans::ScanArgs ai{};
+        if ((st = prepare_scan(&sdi, mlp, ai))) return st;
+        const size_t w = workspace_of(ai, false);
+        p.scan_ws = w > p.scan_ws ? w : p.scan_ws;
+    }
+    return TITANS_OK;
+}
+
+size_t titans_mac_workspace_size(const titans_mac_desc* desc, const titans_mlp_desc* mlp) {
+    MacPlan p;
+    if (prepare_mac(desc, mlp, p) != TITANS_OK) return SIZE_MAX;
+    return p.g.B * p.g.T > 0 ? p.own + p.scan_ws : 0;
+}
+
+titans_status titans_mac_forward(const titans_mac_desc* desc, const titans_mlp_desc* mlp,
+                                 const void* x, const void* w_in, const float* b_gate,
+                                 const void* w_out, const float* theta0, const float* s0,
+                                 void* out, float* theta_T, float* s_T, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    MacPlan p;
+    titans_status st = prepare_mac(desc, mlp, p);
+    if (st) return st;
+    titans::MagArgs& g = p.g;
+    const int64_t T = g.T, H = g.H, D = H * g.d;
+    const bool tokens = g.B * T > 0;
+    const size_t need = tokens ? p.own + p.scan_ws : 0;
+    if ((st = check_block_args(g, p.a, x, w_in, b_gate, w_out, theta0, s0, out, theta_T, s_T,
+                               workspace, workspace_bytes, need)))
+        return st;
+    if (g.B == 0) return TITANS_OK;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (!tokens)
+        return scan_impl(&p.sd, mlp, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, theta0,
+                         s0, nullptr, theta_T, s_T, nullptr, false, nullptr, 0, stream);
+    g.x = static_cast<const __bf16*>(x);
+    g.w_in = static_cast<const __bf16*>(w_in);
+    g.b_gate = b_gate;
+    g.w_out = static_cast<const __bf16*>(w_out);
+    g.out = static_cast<__bf16*>(out);
+    titans::mag_place(g, workspace);
+    __bf16* hbuf = reinterpret_cast<__bf16*>(static_cast<char*>(workspace) + mag_own_bytes(g));
+    void* scan_ws = p.scan_ws ? static_cast<char*>(workspace) + p.own : nullptr;
+    hipError_t e = titans::launch_mag_front(g, hs);
+    if (e != hipSuccess) return hip_fail(e, "MAC front-end launch");
+    for (int64_t t0 = 0; t0 < T; t0 += p.S) {
+        const int64_t len = T - t0 < p.S ? T - t0 : p.S;
+        const float* th = t0 == 0 ? theta0 : theta_T;
+        const float* sg = t0 == 0 ? s0 : s_T;
+        titans_scan_desc sdi = p.sd;
+        sdi.seq_len = len;
+        // the segment's memory reads at the state before it, then its writes (in place
+        // on theta_T / s_T after the first segment), then its attention
+        if ((st = titans_mem_retrieve(&sdi, mlp, g.q + t0 * D, th, hbuf + t0 * D, stream)))
+            return st;
+        if ((st = scan_impl(&sdi, mlp, g.q + t0 * D, g.k + t0 * D, g.v + t0 * D, g.alpha + t0 * H,
+                            g.eta + t0 * H, g.beta + t0 * H, th, sg, g.ymem + t0 * D, theta_T,
+                            s_T, nullptr, false, scan_ws, p.scan_ws, stream)))
+            return st;
+        if ((e = titans::launch_mac_attention(g, hbuf, t0, len, hs)) != hipSuccess)
+            return hip_fail(e, "MAC attention launch");
+    }
+    if ((e = titans::launch_mag_out(g, hs)) != hipSuccess)
+        return hip_fail(e, "MAC output projection launch");
     return TITANS_OK;
 }
 

@@ -1,5 +1,6 @@
-// Titans MAG block (memory as gate) on gfx950: everything of the block except the memory
-// scan itself, which runs through the scan launchers.
+// Titans MAG block (memory as gate) and MAC block (memory as context) on gfx950:
+// everything of the blocks except the memory scan and read, which run through the scan
+// and retrieve launchers.
 //
 // The block (Titans explainer, the three architecture variants, memory as gate; the
 // lowest.today summary, "Varianti dell'Architettura Titans"): the memory branch reads the
@@ -22,12 +23,13 @@
 //                    q and k per head and applies the gates (ProjFront); otherwise:
 //   prep_kernel      one workgroup per token: per-head norms of q and k (shuffle sums over
 //                    the lanes that hold one head), bf16 q, k, v, and the three gates.
-//   swa_gate_kernel  flash-style attention: 128 queries (32 per wave) against 64-key
+//   attn_kernel      flash-style attention: 128 queries (32 per wave) against 64-key
 //                    blocks double-buffered in LDS, scores computed transposed (keys x
 //                    queries) so each lane owns one query's running max and sum,
 //                    probabilities fed back to the value product straight from the score
-//                    accumulators; the epilogue gates with sigmoid(y_mem) and stores o in
-//                    bf16.
+//                    accumulators.  MAG: causal sliding window, the epilogue gates with
+//                    sigmoid(y_mem).  MAC: one segment whose memory reads form a prefix of
+//                    keys and values visible to every query, own keys causal, no gate.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -300,25 +302,41 @@ constexpr int kQB = 4 * kQW;    // queries per workgroup
 constexpr int kKB = 64;         // keys per LDS block
 constexpr int kVP = kKB + 4;    // transposed value rows in LDS (bf16 pitch)
 
-// One workgroup per (b, h, 128-query block); q, k, v, y_mem and o are [B, T, H, kD] bf16
-// rows of pitch D = H kD.  Wave w owns queries q0 + 32 w + 16 u + j (u = 0, 1) at lane
-// (g, j).  Per 64-key block: S^T tile (u, t) = K_t Q_u^T, so lane (g, j) holds the scores
-// of keys 16 t + 4 g + r for its query of tile u; the max is shared by the four lanes of
-// a query (two xor shuffles); O^T += V^T P^T and the row sums (ones x P^T) take P^T straight from the score registers (the
-// accumulator's row index, the key, is the reduction index of the value product) and V^T
-// from a transposed LDS copy.  Key and value blocks are double-buffered: the next block's
-// global loads are in flight while the current one is used.  Blocks that lie wholly
-// outside a wave's windows are skipped by that wave; masks are applied only on blocks at
-// the diagonal or the window's edge.  Exponentials are the hardware's base-2 exponential
-// (v_exp_f32): arguments are <= 0 and results below fp32's normal range flush to 0, which
-// a probability that small does not notice.
-template <int kD>
-__global__ __launch_bounds__(256) void swa_gate_kernel(const __bf16* __restrict__ q,
-                                                       const __bf16* __restrict__ k,
-                                                       const __bf16* __restrict__ v,
-                                                       const __bf16* __restrict__ ymem,
-                                                       __bf16* __restrict__ o, int64_t T, int H,
-                                                       int window, float scale_log2, int nqb) {
+// Attention over "virtual" key positions 0 .. P + Tq - 1 of one (b, h): positions below P
+// are prefix entries (MAC: the segment's memory reads, each used as key and value), the
+// rest are the tokens row0 .. row0 + Tq - 1 themselves; query i (token row0 + i) sits at
+// position P + i and sees the positions j <= P + i with j > P + i - window.  The MAG
+// block's attention is P = 0, row0 = 0, Tq = T with its sliding window; the MAC block's is
+// one segment (row0 its first token, Tq = P its length) with an unbounded window.
+struct AttnArgs {
+    const __bf16* q;
+    const __bf16* k;
+    const __bf16* v;
+    const __bf16* ymem;  // MAG: the memory read that gates the output
+    const __bf16* hpre;  // MAC: the memory reads (rows of the [B, T, H, d] buffer)
+    __bf16* o;
+    int64_t T;           // tokens per sequence of the [B, T, H, d] buffers
+    int64_t row0, Tq, P;
+    int H, window, nqb;
+    float scale_log2;
+};
+
+// One workgroup per (b, h, 128-query block); all buffers are [B, T, H, kD] bf16 rows of
+// pitch D = H kD.  Wave w owns queries q0 + 32 w + 16 u + j (u = 0, 1) at lane (g, j).
+// Per 64-key block: S^T tile (u, t) = K_t Q_u^T, so lane (g, j) holds the scores of keys
+// 16 t + 4 g + r for its query of tile u; the max is shared by the four lanes of a query
+// (two xor shuffles); O^T += V^T P^T and the row sums (ones x P^T) take P^T straight from
+// the score registers (the accumulator's row index, the key, is the reduction index of the
+// value product) and V^T from a transposed LDS copy.  Key and value blocks are
+// double-buffered: the next block's global loads are in flight while the current one is
+// used.  Blocks that lie wholly outside a wave's windows are skipped by that wave; masks
+// are applied only on blocks at the diagonal or the window's edge.  Exponentials are the
+// hardware's base-2 exponential (v_exp_f32): arguments are <= 0 and results below fp32's
+// normal range flush to 0, which a probability that small does not notice.  The softmax
+// reference moves only when a block's max exceeds it by more than 8 (a factor of 2^8), so
+// most blocks rescale nothing.
+template <int kD, bool kMac>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     constexpr int kKP = kD + 8;                   // key rows in LDS (bf16 pitch)
     constexpr int kKPieces = kKB * kD / 8;        // 16-byte pieces of a key block
     constexpr int kVTasks = (kKB / 4) * (kD / 4); // 4 keys x 4 columns of a value block
@@ -328,14 +346,17 @@ __global__ __launch_bounds__(256) void swa_gate_kernel(const __bf16* __restrict_
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, j = lane & 15;
     const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int qb = static_cast<int>(bid % nqb);
-    const int64_t bh = bid / nqb;
-    const int64_t b = bh / H;
-    const int h = static_cast<int>(bh % H);
-    const int64_t D = static_cast<int64_t>(H) * kD;
-    const int64_t base = b * T * D + static_cast<int64_t>(h) * kD;  // (b, 0, h, 0)
-    const int64_t q0 = static_cast<int64_t>(qb) * kQB;
-    const int64_t wq0 = q0 + kQW * wave, wlast = wq0 + kQW - 1;
+    const int qb = static_cast<int>(bid % a.nqb);
+    const int64_t bh = bid / a.nqb;
+    const int64_t b = bh / a.H;
+    const int h = static_cast<int>(bh % a.H);
+    const int64_t D = static_cast<int64_t>(a.H) * kD;
+    const int64_t base = b * a.T * D + static_cast<int64_t>(h) * kD;  // (b, 0, h, 0)
+    const int64_t Tq = a.Tq, P = kMac ? a.P : 0, Tk = P + Tq, row0 = kMac ? a.row0 : 0;
+    const int window = a.window;
+    const int64_t q0 = static_cast<int64_t>(qb) * kQB;          // first query of the block
+    const int64_t wq0 = q0 + kQW * wave;                         // first query of the wave
+    const int64_t wq0v = P + wq0, wlastv = wq0v + kQW - 1;       // their key positions
 
     bf16x8 qf[2][kD / 32];
 #pragma unroll
@@ -343,8 +364,9 @@ __global__ __launch_bounds__(256) void swa_gate_kernel(const __bf16* __restrict_
         const int64_t qi = wq0 + 16 * u + j;
 #pragma unroll
         for (int kb = 0; kb < kD / 32; ++kb)
-            qf[u][kb] = qi < T ? *reinterpret_cast<const bf16x8*>(q + base + qi * D + 32 * kb + 8 * g)
-                               : zero8();
+            qf[u][kb] = qi < Tq ? *reinterpret_cast<const bf16x8*>(a.q + base + (row0 + qi) * D +
+                                                                   32 * kb + 8 * g)
+                                : zero8();
     }
     f32x4 acc[2][kD / 16], lsum[2];
 #pragma unroll
@@ -357,25 +379,27 @@ __global__ __launch_bounds__(256) void swa_gate_kernel(const __bf16* __restrict_
     const __bf16 one = static_cast<__bf16>(1.0f);
     const bf16x8 ones = {one, one, one, one, one, one, one, one};
 
-    const int64_t qlast = (q0 + kQB - 1 < T - 1) ? q0 + kQB - 1 : T - 1;
-    const int64_t kfirst = q0 - window + 1 > 0 ? q0 - window + 1 : 0;
+    const int64_t qlastv = P + ((q0 + kQB - 1 < Tq - 1) ? q0 + kQB - 1 : Tq - 1);
+    const int64_t kfirst = P + q0 - window + 1 > 0 ? P + q0 - window + 1 : 0;
     const int64_t kbeg = kfirst / kKB * kKB;
-    const int nblk = static_cast<int>((qlast - kbeg) / kKB) + 1;
+    const int nblk = static_cast<int>((qlastv - kbeg) / kKB) + 1;
 
+    // row of key position kv: a prefix entry (MAC) or a token; positions past Tk are zero
+    auto key_row = [&](const __bf16* own, int64_t kv) -> const __bf16* {
+        if (kMac && kv < P) return a.hpre + base + (row0 + kv) * D;
+        return own + base + (row0 + kv - P) * D;
+    };
     bf16x8 rk[kNK];
     bf16x4 rv[kNV][4];
-    // keys past T (only in the last block of a sequence) are zero
     auto fetch = [&](int64_t kb0) {
-        const bool full = kb0 + kKB <= T;
-        const __bf16* kp = k + base + kb0 * D;
-        const __bf16* vp = v + base + kb0 * D;
+        const bool full = kb0 + kKB <= Tk;
 #pragma unroll
         for (int i = 0; i < kNK; ++i) {
             const int c = tid + 256 * i;
             if (c < kKPieces) {
-                const int r = c / (kD / 8);
-                rk[i] = (full || kb0 + r < T)
-                            ? *reinterpret_cast<const bf16x8*>(kp + r * D + (c % (kD / 8)) * 8)
+                const int64_t kv = kb0 + c / (kD / 8);
+                rk[i] = (full || kv < Tk)
+                            ? *reinterpret_cast<const bf16x8*>(key_row(a.k, kv) + (c % (kD / 8)) * 8)
                             : zero8();
             }
         }
@@ -386,10 +410,10 @@ __global__ __launch_bounds__(256) void swa_gate_kernel(const __bf16* __restrict_
                 const int cg = t % (kD / 4), kg = t / (kD / 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * kg + e;
+                    const int64_t kv = kb0 + 4 * kg + e;
                     const __bf16 z = static_cast<__bf16>(0.0f);
-                    rv[i][e] = (full || kb0 + r < T)
-                                   ? *reinterpret_cast<const bf16x4*>(vp + r * D + 4 * cg)
+                    rv[i][e] = (full || kv < Tk)
+                                   ? *reinterpret_cast<const bf16x4*>(key_row(a.v, kv) + 4 * cg)
                                    : bf16x4{z, z, z, z};
                 }
             }
@@ -424,9 +448,9 @@ __global__ __launch_bounds__(256) void swa_gate_kernel(const __bf16* __restrict_
         const bool more = ib + 1 < nblk;
         if (more) fetch(kb0 + kKB);
         // some (query, key) of this wave and block with key <= query < key + window
-        const bool live = wq0 < T && kb0 <= wlast && kb0 + kKB - 1 > wq0 - window;
+        const bool live = wq0 < Tq && kb0 <= wlastv && kb0 + kKB - 1 > wq0v - window;
         if (live) {
-            const bool edge = kb0 + kKB - 1 > wq0 || kb0 <= wlast - window;
+            const bool edge = kb0 + kKB - 1 > wq0v || kb0 <= wlastv - window;
             f32x4 st[2][4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -445,8 +469,9 @@ __global__ __launch_bounds__(256) void swa_gate_kernel(const __bf16* __restrict_
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 if (edge) {
-                    // key - query for key kb0 (|.| < T + 2 kQB: int32 by the host's limit on T)
-                    const int rel0 = static_cast<int>(kb0 - (wq0 + 16 * u + j)) + 4 * g;
+                    // key - query position for key kb0 + 4 g (|.| < P + Tq + 2 kQB: int32 by
+                    // the host's limit on T)
+                    const int rel0 = static_cast<int>(kb0 - (wq0v + 16 * u + j)) + 4 * g;
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -461,10 +486,7 @@ __global__ __launch_bounds__(256) void swa_gate_kernel(const __bf16* __restrict_
                     mx = fmaxf(fmaxf(fmaxf(mx, st[u][t][0]), fmaxf(st[u][t][1], st[u][t][2])), st[u][t][3]);
                 mx = fmaxf(mx, __shfl_xor(mx, 16));
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
-                // The exponentials are taken against a reference that moves only when the
-                // block's max exceeds it by more than 8 (a factor of 2^8), so most blocks
-                // rescale nothing; probabilities stay <= 2^8.
-                const float ms = mx * scale_log2;
+                const float ms = mx * a.scale_log2;
                 const bool grow = ms > m_ref[u] + 8.0f;
                 if (__ballot(grow)) {
                     // lanes that keep their reference (possibly still -inf) scale by 1
@@ -481,7 +503,7 @@ __global__ __launch_bounds__(256) void swa_gate_kernel(const __bf16* __restrict_
                     f32x4 p;
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        p[r] = __builtin_amdgcn_exp2f(fmaf(st[u][t][r], scale_log2, -m_use));
+                        p[r] = __builtin_amdgcn_exp2f(fmaf(st[u][t][r], a.scale_log2, -m_use));
                     pb[t] = fused::bf4(p);
                 }
                 pf[u][0] = fused::cat(pb[0], pb[1]);
@@ -511,16 +533,20 @@ __global__ __launch_bounds__(256) void swa_gate_kernel(const __bf16* __restrict_
     for (int u = 0; u < 2; ++u) {
         const float l = lsum[u][0];
         const int64_t qi = wq0 + 16 * u + j;
-        if (qi >= T) continue;
+        if (qi >= Tq) continue;
         const float inv = 1.0f / l;
 #pragma unroll
         for (int dt = 0; dt < kD / 16; ++dt) {
-            const int64_t at = base + qi * D + 16 * dt + 4 * g;
-            const f32x4 ym = fused::f4(*reinterpret_cast<const bf16x4*>(ymem + at));
+            const int64_t at = base + (row0 + qi) * D + 16 * dt + 4 * g;
             f32x4 out;
+            if (kMac) {
+                out = acc[u][dt] * inv;
+            } else {
+                const f32x4 ym = fused::f4(*reinterpret_cast<const bf16x4*>(a.ymem + at));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) out[r] = sigm(ym[r]) * (acc[u][dt][r] * inv);
-            *reinterpret_cast<bf16x4*>(o + at) = fused::bf4(out);
+                for (int r = 0; r < 4; ++r) out[r] = sigm(ym[r]) * (acc[u][dt][r] * inv);
+            }
+            *reinterpret_cast<bf16x4*>(a.o + at) = fused::bf4(out);
         }
     }
 }
@@ -577,28 +603,38 @@ hipError_t launch_mag_front(const MagArgs& g, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_mag_attention(const MagArgs& g, hipStream_t stream) {
-    if (g.B * g.H * g.T == 0) return hipSuccess;
-    const int nqb = static_cast<int>((g.T + mag::kQB - 1) / mag::kQB);
-    const dim3 grid(static_cast<unsigned>(g.B * g.H * nqb));
-    const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(g.d));
-    const int H = static_cast<int>(g.H);
-    switch (g.d) {
-        case 32:
-            hipLaunchKernelGGL(mag::swa_gate_kernel<32>, grid, dim3(256), 0, stream, g.q, g.k, g.v,
-                               g.ymem, g.o, g.T, H, g.window, scale_log2, nqb);
-            break;
-        case 64:
-            hipLaunchKernelGGL(mag::swa_gate_kernel<64>, grid, dim3(256), 0, stream, g.q, g.k, g.v,
-                               g.ymem, g.o, g.T, H, g.window, scale_log2, nqb);
-            break;
-        case 128:
-            hipLaunchKernelGGL(mag::swa_gate_kernel<128>, grid, dim3(256), 0, stream, g.q, g.k,
-                               g.v, g.ymem, g.o, g.T, H, g.window, scale_log2, nqb);
-            break;
+template <bool kMac>
+static hipError_t launch_attn(mag::AttnArgs a, int d, int64_t B, hipStream_t stream) {
+    if (B * a.H * a.Tq == 0) return hipSuccess;
+    a.nqb = static_cast<int>((a.Tq + mag::kQB - 1) / mag::kQB);
+    const dim3 grid(static_cast<unsigned>(B * a.H * a.nqb));
+    a.scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(d));
+    switch (d) {
+        case 32: hipLaunchKernelGGL((mag::attn_kernel<32, kMac>), grid, dim3(256), 0, stream, a); break;
+        case 64: hipLaunchKernelGGL((mag::attn_kernel<64, kMac>), grid, dim3(256), 0, stream, a); break;
+        case 128: hipLaunchKernelGGL((mag::attn_kernel<128, kMac>), grid, dim3(256), 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_mag_attention(const MagArgs& g, hipStream_t stream) {
+    mag::AttnArgs a{};
+    a.q = g.q; a.k = g.k; a.v = g.v; a.ymem = g.ymem; a.hpre = nullptr; a.o = g.o;
+    a.T = g.T; a.row0 = 0; a.Tq = g.T; a.P = 0;
+    a.H = static_cast<int>(g.H);
+    a.window = g.window;
+    return launch_attn<false>(a, g.d, g.B, stream);
+}
+
+hipError_t launch_mac_attention(const MagArgs& g, const __bf16* h, int64_t row0, int64_t len,
+                                hipStream_t stream) {
+    mag::AttnArgs a{};
+    a.q = g.q; a.k = g.k; a.v = g.v; a.ymem = nullptr; a.hpre = h; a.o = g.o;
+    a.T = g.T; a.row0 = row0; a.Tq = len; a.P = len;
+    a.H = static_cast<int>(g.H);
+    a.window = 0x7fffffff;
+    return launch_attn<true>(a, g.d, g.B, stream);
 }
 
 hipError_t launch_mag_out(const MagArgs& g, hipStream_t stream) {

@@ -128,5 +128,10 @@ void mag_place(MagArgs& g, void* ws);
 hipError_t launch_mag_front(const MagArgs& g, hipStream_t stream);
 hipError_t launch_mag_attention(const MagArgs& g, hipStream_t stream);
 hipError_t launch_mag_out(const MagArgs& g, hipStream_t stream);
+// MAC block attention for the segment of tokens row0 .. row0 + len - 1: every query sees
+// the segment's memory reads h (a [B, T, H, d] buffer, rows of the segment) as a prefix of
+// keys and values and its own segment's keys causally; writes g.o for those rows.
+hipError_t launch_mac_attention(const MagArgs& g, const __bf16* h, int64_t row0, int64_t len,
+                                hipStream_t stream);
 
 }  // namespace titans

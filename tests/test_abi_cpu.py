@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_status_strings_and_param_count():
-    assert tm.lib.titans_abi_version() == 4
+    assert tm.lib.titans_abi_version() == 5
     assert tm.lib.titans_status_string(0) == b"TITANS_OK"
     assert tm.lib.titans_status_string(3) == b"TITANS_ERR_WORKSPACE"
     assert tm.param_count((64, 256, 64)) == 32768
