@@ -276,11 +276,31 @@ def mag_alg_flops(B, T, H, widths, C, W):
             "output_projection": 2.0 * M * D * D}
 
 
-def bench_mag(tm, torch, wl, window, seed, steps, warmup):
-    """One MAG block (titans_mag_forward) at the workload's shape with model width
-    D = H d: x [B, T, D] bf16, seeded weights, the sliding window `window`.  Timed by HIP
-    events around the call on its stream; the roofline is the block's algorithmic
-    products against the bf16 matrix-core peak (all four parts run on bf16 MFMA)."""
+def mac_alg_flops(B, T, H, widths, C, S):
+    """Products of one MAC block (memory as context) by part: the front-end projection, the
+    memory scan, the memory reads (2 P per token-head), attention (4 d per query-key pair:
+    a query of a segment of L tokens sees the L reads and its own causal keys,
+    L^2 + L(L+1)/2 pairs per segment and (b, h)) and the output projection."""
+    d = widths[0]
+    D, M = H * d, B * T
+    P = sum(widths[l] * widths[l - 1] for l in range(1, len(widths)))
+    pairs = 0
+    for t0 in range(0, T, S):
+        L = min(S, T - t0)
+        pairs += L * L + L * (L + 1) // 2
+    return {"projection": 2.0 * M * D * (3 * D + 3 * H),
+            "memory_scan": float(alg_flops_per_token_head(widths, C)) * M * H,
+            "memory_read": 2.0 * P * M * H,
+            "attention": 4.0 * d * B * H * pairs,
+            "output_projection": 2.0 * M * D * D}
+
+
+def bench_mag(tm, torch, wl, window, seed, steps, warmup, kind="mag"):
+    """One MAG block (titans_mag_forward; kind="mac": one MAC block, titans_mac_forward,
+    with `window` as its segment length) at the workload's shape with model width
+    D = H d: x [B, T, D] bf16, seeded weights.  Timed by HIP events around the call on its
+    stream; the roofline is the block's algorithmic products against the bf16 matrix-core
+    peak (every part runs on bf16 MFMA)."""
     import synthetic
 
     mi = synthetic.make_mag_inputs(wl, window, seed)
@@ -294,13 +314,15 @@ def bench_mag(tm, torch, wl, window, seed, steps, warmup):
     B, H = wl.batch, wl.heads
     th0 = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(mi.theta0, (B,) + mi.theta0.shape))).to(dev)
     s0 = torch.zeros_like(th0)
-    n = tm.mag_workspace_size(x, wl.chunk, window, wl.widths, wl.eta_scale)
+    size_fn, fwd = ((tm.mag_workspace_size, tm.mag_forward) if kind == "mag"
+                    else (tm.mac_workspace_size, tm.mac_forward))
+    n = size_fn(x, wl.chunk, window, wl.widths, wl.eta_scale)
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     out, thT, sT = torch.empty_like(x), torch.empty_like(th0), torch.empty_like(th0)
 
     def run():
-        tm.mag_forward(x, w_in, b_gate, w_out, th0, s0, wl.chunk, window, wl.widths,
-                       wl.eta_scale, out=out, theta_T=thT, s_T=sT, workspace=ws)
+        fwd(x, w_in, b_gate, w_out, th0, s0, wl.chunk, window, wl.widths, wl.eta_scale,
+            out=out, theta_T=thT, s_T=sT, workspace=ws)
     for _ in range(warmup):
         run()
     stream = torch.cuda.current_stream()
@@ -312,14 +334,18 @@ def bench_mag(tm, torch, wl, window, seed, steps, warmup):
     b.record(stream)
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / steps
-    parts = mag_alg_flops(B, wl.seq_len, H, wl.widths, wl.chunk, window)
+    parts = (mag_alg_flops if kind == "mag" else mac_alg_flops)(B, wl.seq_len, H, wl.widths,
+                                                                  wl.chunk, window)
     flops = sum(parts.values())
     tf = flops / (ms * 1e-3) / 1e12
     del ws
+    kernels = ("gemm_nt_kernel (projection with the front end) + memory scan + attn_kernel "
+               "(sliding window, gated) + gemm_nt_kernel (output)" if kind == "mag" else
+               "gemm_nt_kernel (projection with the front end) + per segment: memory read, "
+               "memory scan, attn_kernel (read prefix) + gemm_nt_kernel (output)")
     return {"ms": ms, "tokens_per_s": B * wl.seq_len / (ms * 1e-3), "steps": steps,
-            "model_width": H * wl.d, "window": window, "workspace_bytes": n,
-            "kernels": "gemm_nt_kernel (projection) + prep_kernel + memory scan + "
-                       "swa_gate_kernel + gemm_nt_kernel (output)",
+            "model_width": H * wl.d, ("window" if kind == "mag" else "segment"): window,
+            "workspace_bytes": n, "kernels": kernels,
             "alg_flops_by_part": parts,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAKS["mfma_bf16"],
                          "unit": "TFLOP/s", "frac": tf / PEAKS["mfma_bf16"],
@@ -342,6 +368,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-mag", action="store_true")
     ap.add_argument("--mag-window", type=int, default=4096)
+    ap.add_argument("--no-mac", action="store_true")
+    ap.add_argument("--mac-segment", type=int, default=4096)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -463,6 +491,9 @@ def main():
     if not args.no_mag and wl.io == "bf16" and wl.widths[0] == wl.widths[-1]:
         result["mag_block"] = bench_mag(tm, torch, wl, args.mag_window, args.seed,
                                         min(args.steps, 5), 1)
+    if not args.no_mac and wl.io == "bf16" and wl.widths[0] == wl.widths[-1]:
+        result["mac_block"] = bench_mag(tm, torch, wl, args.mac_segment, args.seed,
+                                        min(args.steps, 5), 1, kind="mac")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_sample_rows, args.cpu_sample_tokens)
     print(json.dumps(result), flush=True)

@@ -535,3 +535,64 @@ def test_mag_validation_of_pointers_overlap_and_workspace():
     assert _mag(desc, mlp, ptrs, end + 64, need)[0] == INVALID
     st, msg = _mag(desc, mlp, ptrs, ptrs["x"], need)
     assert st == INVALID and "overlap" in msg
+
+
+# ---------------------------------------------------------------- MAC block
+
+def test_mac_workspace_formula_and_validation():
+    widths = (64, 256, 64)
+    mlp = tm.mlp_desc(widths)
+    P = tm.param_count(widths)
+    big = ctypes.c_size_t(-1).value
+    for B, T, H, C, Sg in [(2, 100, 2, 16, 48), (8, 16384, 16, 64, 4096), (1, 7, 3, 1, 1000)]:
+        d = widths[0]
+        D, M = H * d, B * T
+        ldp = (3 * D + 3 * H + 3) // 4 * 4
+        mag_own = _a256(_a256(M * ldp * 4) + 5 * _a256(M * D * 2) + 3 * _a256(M * H * 4))
+        scan_ws = 0
+        for L in (min(Sg, T), T % Sg):
+            if L == 0:
+                continue
+            sd = _desc(B, L, H, d)
+            sd.chunk = C
+            sd.qkv_stride[:] = (T * D, D, d)
+            sd.y_stride[:] = (T * D, D, d)
+            sd.gate_stride[:] = (T * H, H, 1)
+            sd.state_stride[:] = (H * P, P)
+            sd.state0_stride[:] = (H * P, P)
+            scan_ws = max(scan_ws, tm.lib.titans_mem_scan_workspace_size(ctypes.byref(sd),
+                                                                         ctypes.byref(mlp)))
+        got = tm.lib.titans_mac_workspace_size(ctypes.byref(tm.MacDesc(B, T, H, C, Sg, 0.1, 0)),
+                                               ctypes.byref(mlp))
+        assert got == mag_own + _a256(M * D * 2) + scan_ws, (B, T, H, C, Sg)
+    size = lambda desc: tm.lib.titans_mac_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+    assert size(tm.MacDesc(0, 5, 2, 16, 8, 0.1, 0)) == 0
+    for bad in (tm.MacDesc(2, 100, 2, 16, 0, 0.1, 0), tm.MacDesc(2, 100, 2, 0, 8, 0.1, 0),
+                tm.MacDesc(2, 100, 0, 16, 8, 0.1, 0), tm.MacDesc(2, 100, 2, 16, 8, -1.0, 0),
+                tm.MacDesc(2, 100, 2, 16, 8, 0.1, 1)):
+        assert size(bad) == big
+
+
+@no_fake_pointers_on_gpu
+def test_mac_validation_of_pointers_and_workspace():
+    widths = (64, 256, 64)
+    mlp = tm.mlp_desc(widths)
+    B, T, H, d = 2, 100, 2, 64
+    desc = tm.MacDesc(B, T, H, 16, 48, 0.1, 0)
+    ptrs, end = _fake_mag_ptrs(B, T, H, d, tm.param_count(widths))
+    need = tm.lib.titans_mac_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+
+    def call(p, ws, n):
+        args = [ctypes.c_void_p(p[k]) for k in _MAG_ORDER]
+        st = tm.lib.titans_mac_forward(ctypes.byref(desc), ctypes.byref(mlp), *args,
+                                       ctypes.c_void_p(ws), n, None)
+        return st, tm.lib.titans_last_error().decode()
+
+    for n in _MAG_ORDER:
+        st, msg = call(dict(ptrs, **{n: 0}), end, need)
+        assert st == INVALID and "NULL" in msg, (n, msg)
+    for o in ("out", "theta_T", "s_T"):
+        st, msg = call(dict(ptrs, **{o: ptrs["x"]}), end, need)
+        assert st == INVALID and "overlap" in msg
+    assert call(ptrs, end, need - 1)[0] == WORKSPACE
+    assert call(ptrs, end + 64, need)[0] == INVALID
