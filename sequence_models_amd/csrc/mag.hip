@@ -336,7 +336,7 @@ struct AttnArgs {
 // reference moves only when a block's max exceeds it by more than 8 (a factor of 2^8), so
 // most blocks rescale nothing.
 template <int kD, bool kMac>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 3) void attn_kernel(AttnArgs a) {
     constexpr int kKP = kD + 8;                   // key rows in LDS (bf16 pitch)
     constexpr int kKPieces = kKB * kD / 8;        // 16-byte pieces of a key block
     constexpr int kVTasks = (kKB / 4) * (kD / 4); // 4 keys x 4 columns of a value block
@@ -392,7 +392,28 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     bf16x8 rk[kNK];
     bf16x4 rv[kNV][4];
     auto fetch = [&](int64_t kb0) {
-        const bool full = kb0 + kKB <= Tk;
+        // the common case: a whole block of one source, no bound checks
+        if (kb0 + kKB <= Tk && (!kMac || kb0 + kKB <= P || kb0 >= P)) {
+            const __bf16* ksrc = key_row(a.k, kb0);
+            const __bf16* vsrc = key_row(a.v, kb0);
+#pragma unroll
+            for (int i = 0; i < kNK; ++i) {
+                const int c = tid + 256 * i;
+                if (kKPieces % 256 == 0 || c < kKPieces)
+                    rk[i] = *reinterpret_cast<const bf16x8*>(ksrc + (c / (kD / 8)) * D + (c % (kD / 8)) * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < kNV; ++i) {
+                const int t = tid + 256 * i;
+                if (kVTasks % 256 == 0 || t < kVTasks) {
+                    const __bf16* vp = vsrc + (4 * (t / (kD / 4))) * D + 4 * (t % (kD / 4));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rv[i][e] = *reinterpret_cast<const bf16x4*>(vp + e * D);
+                }
+            }
+            return;
+        }
+        const bool full = false;
 #pragma unroll
         for (int i = 0; i < kNK; ++i) {
             const int c = tid + 256 * i;
