@@ -63,7 +63,10 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nb) {
 
 constexpr int kGT = 128;       // tile extent in M and in N
 constexpr int kGK = 32;        // k per stage
-constexpr int kGP = kGK + 8;   // LDS row pitch in bf16 (80 bytes)
+constexpr int kGP = kGK + 8;   // LDS row pitch in bf16
+constexpr int kGPR = kGK / 8;                // 16-byte pieces per tile row and stage
+constexpr int kGRows = 256 / kGPR;           // tile rows one pass of 256 threads stages
+constexpr int kGIt = kGT / kGRows;           // passes per operand and stage
 
 // Epilogues see a wave's whole 64 x 64 result: acc[in][im] holds C[r0 + 16 im + j]
 // [c0 + 16 in + 4 g + r]; red is 2 KiB of LDS free for the epilogue, and every wave of the
@@ -185,13 +188,13 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const __bf16* __restrict__
     const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t m0 = (bid / tiles_n) * kGT;
     const int n0 = static_cast<int>(bid % tiles_n) * kGT;
-    // staging: 16-byte piece c = tid + 256 i of a 128 x 32 tile is row c / 4, k (c % 4) * 8
-    const int r0 = tid >> 2, kc = (tid & 3) * 8;
-    bf16x8 ra[2], rw[2];
+    // staging: thread t stages the 16-byte piece (t % kGPR) of rows t / kGPR + kGRows i
+    const int r0 = tid / kGPR, kc = (tid % kGPR) * 8;
+    bf16x8 ra[kGIt], rw[kGIt];
     auto load = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = r0 + 64 * i;
+        for (int i = 0; i < kGIt; ++i) {
+            const int r = r0 + kGRows * i;
             const bool kok = k0 + kc < K;
             const int64_t m = m0 + r;
             const int n = n0 + r;
@@ -202,9 +205,9 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const __bf16* __restrict__
     };
     auto store = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            *reinterpret_cast<bf16x8*>(&sa[buf][(r0 + 64 * i) * kGP + kc]) = ra[i];
-            *reinterpret_cast<bf16x8*>(&sw[buf][(r0 + 64 * i) * kGP + kc]) = rw[i];
+        for (int i = 0; i < kGIt; ++i) {
+            *reinterpret_cast<bf16x8*>(&sa[buf][(r0 + kGRows * i) * kGP + kc]) = ra[i];
+            *reinterpret_cast<bf16x8*>(&sw[buf][(r0 + kGRows * i) * kGP + kc]) = rw[i];
         }
     };
     f32x4 acc[4][4];
@@ -220,16 +223,19 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const __bf16* __restrict__
     for (int s = 0; s < nk; ++s) {
         const int cur = s & 1;
         if (s + 1 < nk) load((s + 1) * kGK);
-        bf16x8 fa[4], fw[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            fa[i] = *reinterpret_cast<const bf16x8*>(&sa[cur][(wm * 64 + 16 * i + j) * kGP + 8 * g]);
-            fw[i] = *reinterpret_cast<const bf16x8*>(&sw[cur][(wn * 64 + 16 * i + j) * kGP + 8 * g]);
+        for (int ks = 0; ks < kGK / 32; ++ks) {
+            bf16x8 fa[4], fw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                fa[i] = *reinterpret_cast<const bf16x8*>(&sa[cur][(wm * 64 + 16 * i + j) * kGP + 32 * ks + 8 * g]);
+                fw[i] = *reinterpret_cast<const bf16x8*>(&sw[cur][(wn * 64 + 16 * i + j) * kGP + 32 * ks + 8 * g]);
+            }
+#pragma unroll
+            for (int in = 0; in < 4; ++in)
+#pragma unroll
+                for (int im = 0; im < 4; ++im) acc[in][im] = mma(fw[in], fa[im], acc[in][im]);
         }
-#pragma unroll
-        for (int in = 0; in < 4; ++in)
-#pragma unroll
-            for (int im = 0; im < 4; ++im) acc[in][im] = mma(fw[in], fa[im], acc[in][im]);
         if (s + 1 < nk) store(cur ^ 1);
         __syncthreads();
     }
