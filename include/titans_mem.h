@@ -174,9 +174,11 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
  *   surprise   device fp32 with alpha's layout (desc->gate_stride), 4-byte aligned; must
  *              not overlap any other buffer (TITANS_ERR_INVALID_ARGUMENT)
  *   workspace  >= titans_mem_scan_surprise_workspace_size bytes
- * This call always runs the generic family ("phased_*" or "generic_*" by the width rule
- * of titans_mem_scan_path; the fused kernels do not produce the norms).  Every other
- * argument and result is as for titans_mem_scan.
+ * Shapes that titans_mem_scan runs on the pair path ("fused_pair") run there, with the
+ * norms' partial sums in the workspace and one more small kernel; every other shape runs
+ * the generic family ("phased_*" or "generic_*" by the width rule of
+ * titans_mem_scan_path; the single-workgroup fused and the linear kernels do not produce
+ * the norms).  Every other argument and result is as for titans_mem_scan.
  */
 titans_status titans_mem_scan_surprise(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
                                        const void* q, const void* k, const void* v,
@@ -185,8 +187,8 @@ titans_status titans_mem_scan_surprise(const titans_scan_desc* desc, const titan
                                        void* y, float* theta_T, float* s_T, float* surprise,
                                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Which kernel titans_mem_scan_surprise runs ("phased_*" or "generic_*"; NULL if the
- * arguments are invalid; static string). */
+/* Which kernel titans_mem_scan_surprise runs ("fused_pair", "phased_*" or "generic_*";
+ * NULL if the arguments are invalid; static string). */
 const char* titans_mem_scan_surprise_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp);
 
 /* Workspace bytes titans_mem_scan_surprise needs (SIZE_MAX if the arguments are invalid). */

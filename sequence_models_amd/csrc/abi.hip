@@ -274,15 +274,20 @@ const char* titans_mem_scan_path(const titans_scan_desc* desc, const titans_mlp_
     return path_name(choose_path(a), a);
 }
 
-// The path of a call; the per-token surprise output is computed by the generic family only.
+// The path of a call; the per-token surprise output is computed by the pair path and the
+// generic family (the single-workgroup fused and the linear paths do not produce it).
 static Path scan_path_of(const titans::ScanArgs& a, bool surprise) {
-    return surprise ? generic_path(a) : choose_path(a);
+    const Path p = choose_path(a);
+    if (!surprise || p == Path::Pair) return p;
+    return generic_path(a);
 }
 
 static size_t workspace_of(const titans::ScanArgs& a, bool surprise) {
     if (a.B * a.H == 0 || a.T == 0) return 0;
     switch (scan_path_of(a, surprise)) {
-        case Path::Pair: return titans::scan_pair_workspace_bytes(a);
+        case Path::Pair:
+            return titans::scan_pair_workspace_bytes(a) +
+                   (surprise ? titans::scan_pair_surprise_bytes(a) : 0);
         case Path::Fused: return 0;
         case Path::Phased: return titans::scan_phased_workspace_bytes(a);
         case Path::Linear: return titans::scan_linear_workspace_bytes(a);

@@ -288,7 +288,16 @@ __global__ void __launch_bounds__(kThreads) pair_coef_kernel(ScanArgs A, char* c
     }
 }
 
-template <bool kFrozen>
+// Per-token surprise (kSurp): the norm of the gradient token t writes with, at the chunk-start
+// weights.  For the 64 -> 256 -> 64 memory g_t = {E2_t Hk_t^T, D1_t k_t^T}, so
+// ||g_t||^2 = ||E2_t||^2 ||Hk_t||^2 + ||D1_t||^2 ||k_t||^2.  Each lane stores, unreduced, its
+// share of ||Hk_t||^2 and ||D1_t||^2 (its hidden unit per 16-unit tile: plain stores, nothing
+// added on the chunk's critical path); side 0 stores ||E2_t||^2; pair_surprise_kernel adds
+// the 128 shares per token (2 sides x 4 waves x 16 lanes) with ||k_t||^2 after the scan.
+// Partials per (memory, token): Hk shares [128], D1 shares [128], then ||E2||^2 apart.
+constexpr int kSurpShares = 128;
+
+template <bool kFrozen, bool kSurp>
 __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
     __shared__ std::conditional_t<kFrozen, SmemFrozen, SmemFour> sm;
     const int kSub = A.C / kC;  // sub-chunks per gradient chunk
@@ -311,6 +320,13 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
     const char* coef = static_cast<const char*>(A.ws) + ((A.B * A.H + 7) / 8 * 8) * kPairBytes +
                        seq * nchunks * kCoefBytes;
     auto yxslot = [&](int e, int s) { return xy + ((e & 1) * 2 + s) * 4 * kThreads + tid; };
+    float* const spart = kSurp ? reinterpret_cast<float*>(static_cast<char*>(A.ws) +
+                                                         ((A.B * A.H + 7) / 8 * 8) * kPairBytes +
+                                                         A.B * A.H * nchunks * kCoefBytes)
+                               : nullptr;
+    float* const shk = kSurp ? spart + seq * A.T * 2 * kSurpShares : nullptr;   // [t][2][128]
+    float* const se2 = kSurp ? spart + A.B * A.H * A.T * 2 * kSurpShares + seq * A.T : nullptr;
+    const int share = side * 64 + wv * 16 + j;  // this lane's share index
     bool bad = false;
     // test hook (debug bit 0): side 1 never posts, every wait gives up after 1024 polls
     const bool mute = (A.debug & 1) && side == 1;
@@ -456,6 +472,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
         // by an exact MFMA against the identity (D = A [I; 0] is the transpose of A's first
         // 16 x 16 tile when A is an accumulator tile in registers)
         bf16x4 Hk[4][kHt], Sp[4][kHt], HkT[kHt][4];
+        float hsq[4][4] = {};  // kSurp: this wave's share of ||Hk_t||^2, t = 16 ct + 4 g + r
         {
             const int rb = opq(j * kLd + 4 * g);
             const __bf16* ks = sm.kk + rb;
@@ -481,6 +498,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                         const float hh = z[r] * sg;
                         hk[r] = hh;
                         sp[r] = sg + hh * (1.f - sg);  // SiLU'(z) = s (1 + z (1 - s))
+                        if constexpr (kSurp) hsq[ct][r] += hh * hh;
                     }
                     Hk[ct][ht] = bf4(hk);
                     Sp[ct][ht] = bf4(sp);
@@ -488,6 +506,14 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 }
             }
         }
+        if constexpr (kSurp)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t t = c0 + 16 * ct + 4 * g + r;
+                    if (t < A.T) shk[t * 2 * kSurpShares + share] = hsq[ct][r];
+                }
         // O^T partial over this wave's hidden units: O^T[dd][c] = sum_h W2[dd][h] Hk[c][h]
         f32x4 Ot[4][4];
         {
@@ -669,6 +695,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             // in its four layouts
             const int xb = opq(rc * kLd + cl0), xt = opq(cl0 * kLd + rc);
             const float ccr = -sm.cc[rc], wr = sm.w[rc];
+            float esq = 0.f;  // kSurp: this thread's 16 columns of ||E2_rc||^2
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 f32x4 o;
@@ -680,6 +707,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 }
                 const f32x4 v4 = f4(half4(vr[q4 >> 1], q4 & 1));
                 const f32x4 e2 = bias_grad4(o - v4, A.bias, A.bias_param);
+                if constexpr (kSurp) esq += (e2[0] * e2[0] + e2[1] * e2[1]) + (e2[2] * e2[2] + e2[3] * e2[3]);
                 const bf16x4 el = bf4(e2), ec = bf4(e2 * ccr), ew = bf4(e2 * wr);
                 *reinterpret_cast<bf16x4*>(sm.e2l + xb + 4 * q4) = el;
 #pragma unroll
@@ -689,6 +717,11 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                     sm.e2c[o2] = ec[ee];
                     sm.e2w[o2] = ew[ee];
                 }
+            }
+            if constexpr (kSurp) {
+                esq += __shfl_xor(esq, 1);
+                esq += __shfl_xor(esq, 2);
+                if (side == 0 && (tid & 3) == 0 && c0 + rc < A.T) se2[c0 + rc] = esq;
             }
             if (e > 1) write_y(c0 - kC, px);
         }
@@ -701,6 +734,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
         // G = E2 W2 (rows c, cols h); D1 = G o SiLU'(Z).  The B operand W2 [dd][h] is the
         // transpose of the state tiles W2T [h][dd]: one exact identity MFMA per tile.
         bf16x4 D1[4][kHt];
+        float dsq[4][4] = {};  // kSurp: this wave's share of ||D1_t||^2
         {
             bf16x4 W2n[4][kHt];  // rows dd = 16 dt + 4g + r, cols h = 16 ht + j
 #pragma unroll
@@ -727,10 +761,22 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 for (int ct = 0; ct < 4; ++ct) {
                     f32x4 gg = mfma(frag(er, fo(ct, 0)), b0, zero4());
                     gg = mfma(frag(er, fo(ct, 1)), b1, gg);
-                    D1[ct][ht] = bf4(gg * f4(Sp[ct][ht]));
+                    const f32x4 d1 = gg * f4(Sp[ct][ht]);
+                    D1[ct][ht] = bf4(d1);
+                    if constexpr (kSurp)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) dsq[ct][r] += d1[r] * d1[r];
                 }
             }
         }
+        if constexpr (kSurp)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t t = c0 + 16 * ct + 4 * g + r;
+                    if (t < A.T) shk[t * 2 * kSurpShares + kSurpShares + share] = dsq[ct][r];
+                }
         // Zq^T += D1^T Mq^T; Hq = SiLU(Zq), also scaled by a_c and -b_c (its column c is
         // token c) for the W2 / S2 terms of Y
         bf16x4 Hq[kHt][4], Hqa[kHt][4], Hqb[kHt][4];
@@ -922,7 +968,36 @@ __global__ void clear_pair_flags(char* ws, int64_t npairs) {
 int64_t padded_pairs(const ScanArgs& a) { return (a.B * a.H + 7) / 8 * 8; }
 int64_t num_chunks(const ScanArgs& a) { return (a.T + kC - 1) / kC; }
 
+// ||g_t|| from the 128 shares of ||Hk_t||^2 and of ||D1_t||^2, ||E2_t||^2 and ||k_t||^2 read
+// from k; one wave per (memory, token): lane l adds shares 2 l and 2 l + 1 of both.
+__global__ void __launch_bounds__(256) pair_surprise_kernel(ScanArgs A, const float* part) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int l = threadIdx.x & 63;
+    if (i >= A.B * A.H * A.T) return;
+    const int64_t seq = i / A.T, t = i % A.T, b = seq / A.H, h = seq % A.H;
+    const float* p = part + i * 2 * kSurpShares;
+    float hk = p[2 * l] + p[2 * l + 1];
+    float d1 = p[kSurpShares + 2 * l] + p[kSurpShares + 2 * l + 1];
+    const __bf16* kp = static_cast<const __bf16*>(A.k) + b * A.qs[0] + t * A.qs[1] + h * A.qs[2];
+    const float kv = static_cast<float>(kp[l]);
+    float ks = kv * kv;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        hk += __shfl_xor(hk, m);
+        d1 += __shfl_xor(d1, m);
+        ks += __shfl_xor(ks, m);
+    }
+    if (l == 0) {
+        const float e2 = part[A.B * A.H * A.T * 2 * kSurpShares + i];
+        A.surprise[b * A.gs[0] + t * A.gs[1] + h * A.gs[2]] = sqrtf(e2 * hk + d1 * ks);
+    }
+}
+
 }  // namespace
+
+size_t scan_pair_surprise_bytes(const ScanArgs& a) {
+    return (size_t)(a.B * a.H) * (size_t)a.T * (2 * kSurpShares + 1) * sizeof(float);
+}
 
 bool scan_pair_supported(const ScanArgs& a) {
     return a.L == 2 && a.n[0] == kD && a.n[1] == kHid && a.n[2] == kD && a.C >= kC &&
@@ -955,11 +1030,21 @@ hipError_t launch_scan_pair(const ScanArgs& a, hipStream_t stream) {
     }
     ScanArgs args = a;
     void* kargs[] = {&args};
-    const void* fn = a.C == kC ? reinterpret_cast<const void*>(&scan_pair_kernel<false>)
-                               : reinterpret_cast<const void*>(&scan_pair_kernel<true>);
-    return hipLaunchCooperativeKernel(fn,
-                                      dim3((unsigned)(2 * npairs)), dim3(kThreads), kargs, 0,
-                                      stream);
+    const bool surp = a.surprise != nullptr;
+    const void* fn =
+        a.C == kC ? (surp ? reinterpret_cast<const void*>(&scan_pair_kernel<false, true>)
+                          : reinterpret_cast<const void*>(&scan_pair_kernel<false, false>))
+                  : (surp ? reinterpret_cast<const void*>(&scan_pair_kernel<true, true>)
+                          : reinterpret_cast<const void*>(&scan_pair_kernel<true, false>));
+    e = hipLaunchCooperativeKernel(fn, dim3((unsigned)(2 * npairs)), dim3(kThreads), kargs, 0,
+                                   stream);
+    if (e != hipSuccess || !surp) return e;
+    const float* part = reinterpret_cast<const float*>(ws + npairs * kPairBytes +
+                                                       a.B * a.H * nchunks * kCoefBytes);
+    const int64_t n = a.B * a.H * a.T;
+    if ((n + 3) / 4 > 0xffffffffLL) return hipErrorInvalidConfiguration;
+    pair_surprise_kernel<<<dim3((unsigned)((n + 3) / 4)), 256, 0, stream>>>(a, part);
+    return hipGetLastError();
 }
 
 }  // namespace titans

@@ -89,6 +89,8 @@ hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t stream);
 bool scan_pair_supported(const ScanArgs& a);
 size_t scan_pair_workspace_bytes(const ScanArgs& a);
 int64_t scan_pair_workgroups(const ScanArgs& a);
+// Extra workspace of a pair-path call that also writes the per-token surprise norms.
+size_t scan_pair_surprise_bytes(const ScanArgs& a);
 hipError_t launch_scan_pair(const ScanArgs& a, hipStream_t stream);
 
 // Generic retrieve: any supported shape, products as in the generic scan.

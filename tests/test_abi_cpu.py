@@ -256,20 +256,26 @@ def _scan_surprise(desc, mlp, ptrs, surprise, ws=None, ws_bytes=0):
     return st, tm.lib.titans_last_error().decode()
 
 
-def test_surprise_workspace_follows_the_generic_family(monkeypatch):
-    """The surprise call always runs the generic family: for the fused shape its workspace
-    is the phased path's, which TITANS_MEM_FORCE_GENERIC shows for the plain scan."""
+def test_surprise_workspace_follows_the_path(monkeypatch):
+    """The fused shape's surprise call runs on the pair path with 257 floats of partial sums
+    per token-head after the plain scan's workspace; forced onto the generic family it takes
+    the phased path's workspace, as the plain scan does there."""
     mlp = tm.mlp_desc((64, 256, 64))
     desc = _desc()
+    B, T, H = desc.batch, desc.seq_len, desc.heads
     pair = tm.lib.titans_mem_scan_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
     sur = tm.lib.titans_mem_scan_surprise_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+    assert tm.lib.titans_mem_scan_surprise_path(ctypes.byref(desc), ctypes.byref(mlp)) == b"fused_pair"
+    assert sur == pair + B * H * T * 257 * 4
     monkeypatch.setenv("TITANS_MEM_FORCE_GENERIC", "1")
     assert tm.lib.titans_mem_scan_path(ctypes.byref(desc), ctypes.byref(mlp)) == b"phased_mfma"
-    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(desc), ctypes.byref(mlp)) == sur
-    assert sur != pair
     assert tm.lib.titans_mem_scan_surprise_path(ctypes.byref(desc), ctypes.byref(mlp)) == b"phased_mfma"
+    assert tm.lib.titans_mem_scan_surprise_workspace_size(ctypes.byref(desc), ctypes.byref(mlp)) == \
+        tm.lib.titans_mem_scan_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
     monkeypatch.delenv("TITANS_MEM_FORCE_GENERIC")
+    monkeypatch.setenv("TITANS_MEM_FUSED_SINGLE", "1")   # the single-workgroup kernel has no norms
     assert tm.lib.titans_mem_scan_surprise_path(ctypes.byref(desc), ctypes.byref(mlp)) == b"phased_mfma"
+    monkeypatch.delenv("TITANS_MEM_FUSED_SINGLE")
     assert tm.lib.titans_mem_scan_surprise_path(ctypes.byref(_desc(io=0)),
                                                 ctypes.byref(tm.mlp_desc((64, 96, 64)))) == b"generic_fp32"
     bad = ctypes.c_size_t(-1).value

@@ -671,7 +671,10 @@ SURPRISE_CASES = {
     "generic_bf16": ((8, 24, 12, 8), 5, "bf16", {"TITANS_MEM_GENERIC_MODE": "single"}, "generic_mfma"),
     "phased_f32": ((32, 160, 32), 40, "f32", {}, "phased_fp32"),
     "phased_bf16": ((128, 512, 128), 128, "bf16", {}, "phased_mfma"),
-    "fused_shape": ((64, 256, 64), 64, "bf16", {}, "phased_mfma"),
+    "fused_shape": ((64, 256, 64), 64, "bf16", {}, "fused_pair"),
+    "fused_shape_c128": ((64, 256, 64), 128, "bf16", {}, "fused_pair"),
+    "fused_shape_phased": ((64, 256, 64), 64, "bf16", {"TITANS_MEM_FORCE_GENERIC": "1"},
+                           "phased_mfma"),
 }
 
 
