@@ -290,12 +290,42 @@ __global__ void __launch_bounds__(kThreads) pair_coef_kernel(ScanArgs A, char* c
 
 // Per-token surprise (kSurp): the norm of the gradient token t writes with, at the chunk-start
 // weights.  For the 64 -> 256 -> 64 memory g_t = {E2_t Hk_t^T, D1_t k_t^T}, so
-// ||g_t||^2 = ||E2_t||^2 ||Hk_t||^2 + ||D1_t||^2 ||k_t||^2.  Each lane stores, unreduced, its
-// share of ||Hk_t||^2 and ||D1_t||^2 (its hidden unit per 16-unit tile: plain stores, nothing
-// added on the chunk's critical path); side 0 stores ||E2_t||^2; pair_surprise_kernel adds
-// the 128 shares per token (2 sides x 4 waves x 16 lanes) with ||k_t||^2 after the scan.
-// Partials per (memory, token): Hk shares [128], D1 shares [128], then ||E2||^2 apart.
-constexpr int kSurpShares = 128;
+// ||g_t||^2 = ||E2_t||^2 ||Hk_t||^2 + ||D1_t||^2 ||k_t||^2.  Each lane's 16 per-token sums
+// of squares (its hidden units) are first added over its quad of lanes by two DPP steps
+// (register moves, no LDS round trip), then stored: 32 shares per token and quantity
+// (2 sides x 4 waves x 4 quads); side 0 stores ||E2_t||^2; pair_surprise_kernel adds the
+// shares with ||k_t||^2 after the scan.  Partials per (memory, token): Hk shares [32], D1
+// shares [32], then ||E2||^2 apart.
+constexpr int kSurpShares = 32;
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_quad(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xf, 0xf, true));
+}
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+
+// v[ct][r]: this lane's sums for tokens 16 ct + 4 g + r.  Returns in c[r] the sums over the
+// lane's quad (j = 4 q .. 4 q + 3) for tokens 16 p + 4 g + r, p = j & 3: each step keeps the
+// half of the entries whose ct bit matches the lane's and adds the partner's copy of it.
+__device__ __forceinline__ void quad_reduce_scatter(const float (&v)[4][4], int j, float (&c)[4]) {
+    const bool b0 = j & 1, b1 = j & 2;
+    float h[2][4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float send = b0 ? v[2 * k][r] : v[2 * k + 1][r];
+            const float keep = b0 ? v[2 * k + 1][r] : v[2 * k][r];
+            h[k][r] = keep + dpp_quad<kQuadXor1>(send);
+        }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float send = b1 ? h[0][r] : h[1][r];
+        const float keep = b1 ? h[1][r] : h[0][r];
+        c[r] = keep + dpp_quad<kQuadXor2>(send);
+    }
+}
 
 template <bool kFrozen, bool kSurp>
 __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
@@ -326,7 +356,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                                : nullptr;
     float* const shk = kSurp ? spart + seq * A.T * 2 * kSurpShares : nullptr;   // [t][2][128]
     float* const se2 = kSurp ? spart + A.B * A.H * A.T * 2 * kSurpShares + seq * A.T : nullptr;
-    const int share = side * 64 + wv * 16 + j;  // this lane's share index
+    const int share = side * 16 + wv * 4 + (j >> 2);  // this quad's share index
     bool bad = false;
     // test hook (debug bit 0): side 1 never posts, every wait gives up after 1024 polls
     const bool mute = (A.debug & 1) && side == 1;
@@ -506,14 +536,15 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 }
             }
         }
-        if constexpr (kSurp)
+        if constexpr (kSurp) {
+            float cs[4];
+            quad_reduce_scatter(hsq, j, cs);
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int64_t t = c0 + 16 * ct + 4 * g + r;
-                    if (t < A.T) shk[t * 2 * kSurpShares + share] = hsq[ct][r];
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int64_t t = c0 + 16 * (j & 3) + 4 * g + r;
+                if (t < A.T) shk[t * 2 * kSurpShares + share] = cs[r];
+            }
+        }
         // O^T partial over this wave's hidden units: O^T[dd][c] = sum_h W2[dd][h] Hk[c][h]
         f32x4 Ot[4][4];
         {
@@ -769,14 +800,15 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 }
             }
         }
-        if constexpr (kSurp)
+        if constexpr (kSurp) {
+            float cs[4];
+            quad_reduce_scatter(dsq, j, cs);
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int64_t t = c0 + 16 * ct + 4 * g + r;
-                    if (t < A.T) shk[t * 2 * kSurpShares + kSurpShares + share] = dsq[ct][r];
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int64_t t = c0 + 16 * (j & 3) + 4 * g + r;
+                if (t < A.T) shk[t * 2 * kSurpShares + kSurpShares + share] = cs[r];
+            }
+        }
         // Zq^T += D1^T Mq^T; Hq = SiLU(Zq), also scaled by a_c and -b_c (its column c is
         // token c) for the W2 / S2 terms of Y
         bf16x4 Hq[kHt][4], Hqa[kHt][4], Hqb[kHt][4];
@@ -968,28 +1000,27 @@ __global__ void clear_pair_flags(char* ws, int64_t npairs) {
 int64_t padded_pairs(const ScanArgs& a) { return (a.B * a.H + 7) / 8 * 8; }
 int64_t num_chunks(const ScanArgs& a) { return (a.T + kC - 1) / kC; }
 
-// ||g_t|| from the 128 shares of ||Hk_t||^2 and of ||D1_t||^2, ||E2_t||^2 and ||k_t||^2 read
-// from k; one wave per (memory, token): lane l adds shares 2 l and 2 l + 1 of both.
+// ||g_t|| from the 32 shares of ||Hk_t||^2 and of ||D1_t||^2, ||E2_t||^2 and ||k_t||^2 read
+// from k; one wave per (memory, token): lanes 0..31 add the Hk shares, 32..63 the D1 shares,
+// every lane one component of k.
 __global__ void __launch_bounds__(256) pair_surprise_kernel(ScanArgs A, const float* part) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     const int l = threadIdx.x & 63;
     if (i >= A.B * A.H * A.T) return;
     const int64_t seq = i / A.T, t = i % A.T, b = seq / A.H, h = seq % A.H;
-    const float* p = part + i * 2 * kSurpShares;
-    float hk = p[2 * l] + p[2 * l + 1];
-    float d1 = p[kSurpShares + 2 * l] + p[kSurpShares + 2 * l + 1];
+    float sh = part[i * 2 * kSurpShares + l];  // l < 32: Hk share l; else D1 share l - 32
     const __bf16* kp = static_cast<const __bf16*>(A.k) + b * A.qs[0] + t * A.qs[1] + h * A.qs[2];
     const float kv = static_cast<float>(kp[l]);
     float ks = kv * kv;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        hk += __shfl_xor(hk, m);
-        d1 += __shfl_xor(d1, m);
-        ks += __shfl_xor(ks, m);
-    }
+    for (int m = 16; m >= 1; m >>= 1) sh += __shfl_xor(sh, m);  // within each half
+    ks += __shfl_xor(ks, 32);
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) ks += __shfl_xor(ks, m);
+    const float d1 = __shfl(sh, 32);
     if (l == 0) {
         const float e2 = part[A.B * A.H * A.T * 2 * kSurpShares + i];
-        A.surprise[b * A.gs[0] + t * A.gs[1] + h * A.gs[2]] = sqrtf(e2 * hk + d1 * ks);
+        A.surprise[b * A.gs[0] + t * A.gs[1] + h * A.gs[2]] = sqrtf(e2 * sh + d1 * ks);
     }
 }
 

@@ -257,7 +257,7 @@ def _scan_surprise(desc, mlp, ptrs, surprise, ws=None, ws_bytes=0):
 
 
 def test_surprise_workspace_follows_the_path(monkeypatch):
-    """The fused shape's surprise call runs on the pair path with 257 floats of partial sums
+    """The fused shape's surprise call runs on the pair path with 65 floats of partial sums
     per token-head after the plain scan's workspace; forced onto the generic family it takes
     the phased path's workspace, as the plain scan does there."""
     mlp = tm.mlp_desc((64, 256, 64))
@@ -266,7 +266,7 @@ def test_surprise_workspace_follows_the_path(monkeypatch):
     pair = tm.lib.titans_mem_scan_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
     sur = tm.lib.titans_mem_scan_surprise_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
     assert tm.lib.titans_mem_scan_surprise_path(ctypes.byref(desc), ctypes.byref(mlp)) == b"fused_pair"
-    assert sur == pair + B * H * T * 257 * 4
+    assert sur == pair + B * H * T * 65 * 4
     monkeypatch.setenv("TITANS_MEM_FORCE_GENERIC", "1")
     assert tm.lib.titans_mem_scan_path(ctypes.byref(desc), ctypes.byref(mlp)) == b"phased_mfma"
     assert tm.lib.titans_mem_scan_surprise_path(ctypes.byref(desc), ctypes.byref(mlp)) == b"phased_mfma"
