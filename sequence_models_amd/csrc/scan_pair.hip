@@ -1001,23 +1001,23 @@ int64_t padded_pairs(const ScanArgs& a) { return (a.B * a.H + 7) / 8 * 8; }
 int64_t num_chunks(const ScanArgs& a) { return (a.T + kC - 1) / kC; }
 
 // ||g_t|| from the 32 shares of ||Hk_t||^2 and of ||D1_t||^2, ||E2_t||^2 and ||k_t||^2 read
-// from k; one wave per (memory, token): lanes 0..31 add the Hk shares, 32..63 the D1 shares,
-// every lane one component of k.
+// from k; 16 lanes per (memory, token): lane l adds four shares (l < 8: Hk, else D1) and
+// four components of k, then the group sums by xor shuffles inside its 16 lanes.
 __global__ void __launch_bounds__(256) pair_surprise_kernel(ScanArgs A, const float* part) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    const int l = threadIdx.x & 63;
-    if (i >= A.B * A.H * A.T) return;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+    const int l = threadIdx.x & 15;
+    if (i >= A.B * A.H * A.T) return;  // whole 16-lane groups leave together
     const int64_t seq = i / A.T, t = i % A.T, b = seq / A.H, h = seq % A.H;
-    float sh = part[i * 2 * kSurpShares + l];  // l < 32: Hk share l; else D1 share l - 32
+    const f32x4 s4 = *reinterpret_cast<const f32x4*>(part + i * 2 * kSurpShares + 4 * l);
+    float sh = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     const __bf16* kp = static_cast<const __bf16*>(A.k) + b * A.qs[0] + t * A.qs[1] + h * A.qs[2];
-    const float kv = static_cast<float>(kp[l]);
-    float ks = kv * kv;
+    const f32x4 k4 = f4(*reinterpret_cast<const bf16x4*>(kp + 4 * l));
+    float ks = (k4[0] * k4[0] + k4[1] * k4[1]) + (k4[2] * k4[2] + k4[3] * k4[3]);
 #pragma unroll
-    for (int m = 16; m >= 1; m >>= 1) sh += __shfl_xor(sh, m);  // within each half
-    ks += __shfl_xor(ks, 32);
+    for (int m = 4; m >= 1; m >>= 1) sh += __shfl_xor(sh, m);  // within each 8-lane half
 #pragma unroll
-    for (int m = 16; m >= 1; m >>= 1) ks += __shfl_xor(ks, m);
-    const float d1 = __shfl(sh, 32);
+    for (int m = 8; m >= 1; m >>= 1) ks += __shfl_xor(ks, m);
+    const float d1 = __shfl_xor(sh, 8);  // lane 0: the D1 half's sum
     if (l == 0) {
         const float e2 = part[A.B * A.H * A.T * 2 * kSurpShares + i];
         A.surprise[b * A.gs[0] + t * A.gs[1] + h * A.gs[2]] = sqrtf(e2 * sh + d1 * ks);
@@ -1073,8 +1073,8 @@ hipError_t launch_scan_pair(const ScanArgs& a, hipStream_t stream) {
     const float* part = reinterpret_cast<const float*>(ws + npairs * kPairBytes +
                                                        a.B * a.H * nchunks * kCoefBytes);
     const int64_t n = a.B * a.H * a.T;
-    if ((n + 3) / 4 > 0xffffffffLL) return hipErrorInvalidConfiguration;
-    pair_surprise_kernel<<<dim3((unsigned)((n + 3) / 4)), 256, 0, stream>>>(a, part);
+    if ((n + 15) / 16 > 0xffffffffLL) return hipErrorInvalidConfiguration;
+    pair_surprise_kernel<<<dim3((unsigned)((n + 15) / 16)), 256, 0, stream>>>(a, part);
     return hipGetLastError();
 }
 
