@@ -342,7 +342,7 @@ struct AttnArgs {
 // reference moves only when a block's max exceeds it by more than 8 (a factor of 2^8), so
 // most blocks rescale nothing.
 template <int kD, bool kMac>
-__global__ __launch_bounds__(256, 3) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, kD <= 64 ? 3 : 1) void attn_kernel(AttnArgs a) {
     constexpr int kKP = kD + 8;                   // key rows in LDS (bf16 pitch)
     constexpr int kKPieces = kKB * kD / 8;        // 16-byte pieces of a key block
     constexpr int kVTasks = (kKB / 4) * (kD / 4); // 4 keys x 4 columns of a value block
