@@ -4,13 +4,16 @@
 // (retrieve_mfma.hip) that keeps both weight matrices in LDS; wider memories (the deep
 // 128-512-512-512-128 one holds 2.6 MB of weights) do not fit, so here the weights stream.
 //
-// A workgroup (four waves) serves one (b, h) memory and 32 tokens.  The tokens'
-// activations stay in LDS as bf16 across all layers (two 32 x 512 buffers, ping-pong);
-// each layer's weights pass through LDS in 64-output x 256-input windows, double-buffered:
-// the next window's 16-byte loads are in flight while the current window's MFMAs run.
-// Per window, wave w computes outputs 16w .. 16w+15 of the window's 64 for all 32 tokens
-// (v_mfma_f32_16x16x32_bf16, A = weight rows, B = activation rows, fp32 accumulation); an
-// output tile's epilogue applies SiLU (hidden layers) and writes bf16 activations, or y.
+// A workgroup (four waves) serves one (b, h) memory and 64 tokens: every weight window
+// that streams through LDS is used by 64 tokens.  The tokens' activations stay in one LDS
+// buffer as bf16 across all layers (64 x 512); each layer's weights pass through LDS in
+// 64-output x 256-input windows, double-buffered: the next window's 16-byte loads are in
+// flight while the current window's MFMAs run.  Per window, wave w computes outputs
+// 16w .. 16w+15 of the window's 64 for all 64 tokens (v_mfma_f32_16x16x32_bf16, A = weight
+// rows, B = activation rows, fp32 accumulation).  An output tile's epilogue applies SiLU
+// and keeps the bf16 result in registers until the layer's last window is done (its inputs
+// are still being read); then every wave writes its outputs over the inputs.  The last
+// layer writes y.
 // Workgroups are numbered so that each XCD holds whole memories: all token tiles of a
 // memory then read its weights through one L2.
 #include <hip/hip_runtime.h>
@@ -24,7 +27,9 @@ namespace {
 using namespace fused;
 
 constexpr int kThreads = 256;
-constexpr int kTok = 32;          // tokens per workgroup
+constexpr int kTok = 64;          // tokens per workgroup
+constexpr int kCt = kTok / 16;    // 16-token tiles
+constexpr int kMaxTiles = 8;      // 64-output tiles of a 512-wide layer
 constexpr int kOut = 64;          // outputs per tile
 constexpr int kWin = 256;         // inputs per weight window
 constexpr int kMaxW = 512;
@@ -33,7 +38,7 @@ constexpr int kWLd = kWin + 8;    // padded weight row (bf16)
 constexpr int kGroups = kOut * kWin / 4 / kThreads;  // 16-byte groups per thread per window
 
 struct __attribute__((aligned(16))) WSmem {
-    __bf16 act[2][kTok * kActLd];  // [token][feature]
+    __bf16 act[kTok * kActLd];     // [token][feature]
     __bf16 w[2][kOut * kWLd];      // [output][input - k0]
 };
 
@@ -104,21 +109,25 @@ __global__ void __launch_bounds__(kThreads) retrieve_wide_kernel(ScanArgs A) {
     // columns past it, against zero weights, and those columns must be finite.
     Window nx;
     load_window(nx, th + A.off[1], A.n[1], A.n[0], 0, 0);
-    for (int i = tid; i < 2 * kTok * kActLd / 8; i += kThreads)
-        reinterpret_cast<bf16x8*>(&sm.act[0][0])[i] = bf16x8{};
+    for (int i = tid; i < kTok * kActLd / 8; i += kThreads)
+        reinterpret_cast<bf16x8*>(&sm.act[0])[i] = bf16x8{};
     __syncthreads();
     for (int i = tid; i < kTok * (d / 4); i += kThreads) {
         const int t = i / (d / 4), c = 4 * (i % (d / 4));
         bf16x4 v{};
         if (t0 + t < A.T)
             v = *reinterpret_cast<const bf16x4*>(qg + qbase + (t0 + t) * A.qs[1] + c);
-        *reinterpret_cast<bf16x4*>(sm.act[0] + t * kActLd + c) = v;
+        *reinterpret_cast<bf16x4*>(sm.act + t * kActLd + c) = v;
     }
     store_window(nx, sm.w[0]);
     __syncthreads();
 
-    int buf = 0, cur = 0;
-    f32x4 acc[2] = {zero4(), zero4()};
+    int buf = 0;
+    f32x4 acc[kCt];
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct) acc[ct] = zero4();
+    // SiLU outputs of the current hidden layer: tile ot, token tile ct, outputs f0 .. f0+3
+    bf16x4 stash[kMaxTiles][kCt];
     while (wl <= A.L) {
         const int nin = A.n[wl - 1], nout = A.n[wl];
         // the following window's loads go out before this one's MFMAs
@@ -132,36 +141,57 @@ __global__ void __launch_bounds__(kThreads) retrieve_wide_kernel(ScanArgs A) {
         for (int ks = 0; ks < kw; ks += 32) {
             const bf16x8 a = frag(ar, ks);
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const __bf16* br = sm.act[cur] + (16 * ct + j) * kActLd + wk + ks + 4 * g;
+            for (int ct = 0; ct < kCt; ++ct) {
+                const __bf16* br = sm.act + (16 * ct + j) * kActLd + wk + ks + 4 * g;
                 acc[ct] = mfma(a, frag(br, 0), acc[ct]);
             }
         }
         if (wk + kWin >= nin) {  // last window of this output tile: epilogue
             const int f0 = wo + 16 * wv + 4 * g;  // outputs f0 .. f0+3 of token 16 ct + j
             if (wl < A.L) {
+                bf16x4 h[kCt];
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    f32x4 h;
+                for (int ct = 0; ct < kCt; ++ct) {
+                    f32x4 x;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) h[r] = acc[ct][r] * sigmoid(acc[ct][r]);
-                    if (f0 < nout)
-                        *reinterpret_cast<bf16x4*>(sm.act[cur ^ 1] + (16 * ct + j) * kActLd + f0) =
-                            bf4(h);
+                    for (int r = 0; r < 4; ++r) x[r] = acc[ct][r] * sigmoid(acc[ct][r]);
+                    h[ct] = bf4(x);
+                }
+                // constant indices only (a switch, not a dynamic register index)
+                switch (wo / kOut) {
+#define TITANS_STASH(i) \
+    case i:             \
+        _Pragma("unroll") for (int ct = 0; ct < kCt; ++ct) stash[i][ct] = h[ct]; break;
+                    TITANS_STASH(0) TITANS_STASH(1) TITANS_STASH(2) TITANS_STASH(3)
+                    TITANS_STASH(4) TITANS_STASH(5) TITANS_STASH(6) TITANS_STASH(7)
+#undef TITANS_STASH
+                    default: break;
                 }
             } else {
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
+                for (int ct = 0; ct < kCt; ++ct) {
                     const int64_t t = t0 + 16 * ct + j;
                     if (f0 < nout && t < A.T)
                         *reinterpret_cast<bf16x4*>(yg + ybase + t * A.ys[1] + f0) = bf4(acc[ct]);
                 }
             }
-            acc[0] = acc[1] = zero4();
+#pragma unroll
+            for (int ct = 0; ct < kCt; ++ct) acc[ct] = zero4();
         }
         if (more) store_window(nx, sm.w[buf ^ 1]);
-        __syncthreads();  // the next window is in LDS; a finished layer's outputs too
-        if (more && L2 != wl) cur ^= 1;
+        __syncthreads();  // the next window is in LDS; a finished layer's inputs are read
+        if (more && L2 != wl) {
+            // hidden layer wl is done: its outputs replace its inputs
+#pragma unroll
+            for (int ot = 0; ot < kMaxTiles; ++ot) {
+                const int f0 = kOut * ot + 16 * wv + 4 * g;
+                if (kOut * ot < nout && f0 < nout)
+#pragma unroll
+                    for (int ct = 0; ct < kCt; ++ct)
+                        *reinterpret_cast<bf16x4*>(sm.act + (16 * ct + j) * kActLd + f0) = stash[ot][ct];
+            }
+            __syncthreads();
+        }
         buf ^= 1;
         wl = L2;
         wo = o2;
