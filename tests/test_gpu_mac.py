@@ -50,6 +50,8 @@ CASES = [
     ((64, 128, 64), 2, 1, 12, 1, 1),
     ((32, 64, 32), 3, 2, 130, 16, 64),
     ((128, 128, 128), 1, 2, 70, 8, 32),
+    ((64, 256, 64), 2, 1, 1, 64, 64),      # one token
+    ((64, 128, 64), 2, 1, 129, 8, 64),     # segments of one key block, a one-token last one
 ]
 
 

@@ -90,6 +90,8 @@ CASES = [
     ((32, 64, 32), 3, 2, 130, 16, 500),
     ((32, 32, 32, 32), 4, 1, 96, 32, 17),
     ((128, 128, 128), 1, 2, 70, 8, 33),
+    ((64, 256, 64), 2, 1, 1, 64, 16),      # one token
+    ((64, 128, 64), 2, 1, 129, 8, 64),     # a window of exactly one key block
 ]
 
 
