@@ -4,12 +4,12 @@
 // (retrieve_mfma.hip) that keeps both weight matrices in LDS; wider memories (the deep
 // 128-512-512-512-128 one holds 2.6 MB of weights) do not fit, so here the weights stream.
 //
-// A workgroup (four waves) serves one (b, h) memory and 64 tokens: every weight window
-// that streams through LDS is used by 64 tokens.  The tokens' activations stay in one LDS
-// buffer as bf16 across all layers (64 x 512); each layer's weights pass through LDS in
-// 64-output x 256-input windows, double-buffered: the next window's 16-byte loads are in
-// flight while the current window's MFMAs run.  Per window, wave w computes outputs
-// 16w .. 16w+15 of the window's 64 for all 64 tokens (v_mfma_f32_16x16x32_bf16, A = weight
+// A workgroup (four waves) serves one (b, h) memory and 128 tokens: every weight window
+// that streams through LDS is used by 128 tokens.  The tokens' activations stay in one LDS
+// buffer as bf16 across all layers (128 x 512, 133 KB); each layer's weights pass through
+// one LDS window of 64 outputs x 128 inputs while the next window's 16-byte loads are in
+// flight in registers (stored after a barrier).  Per window, wave w computes outputs
+// 16w .. 16w+15 of the window's 64 for all 128 tokens (v_mfma_f32_16x16x32_bf16, A = weight
 // rows, B = activation rows, fp32 accumulation).  An output tile's epilogue applies SiLU
 // and keeps the bf16 result in registers until the layer's last window is done (its inputs
 // are still being read); then every wave writes its outputs over the inputs.  The last
@@ -27,11 +27,11 @@ namespace {
 using namespace fused;
 
 constexpr int kThreads = 256;
-constexpr int kTok = 64;          // tokens per workgroup
+constexpr int kTok = 128;         // tokens per workgroup
 constexpr int kCt = kTok / 16;    // 16-token tiles
 constexpr int kMaxTiles = 8;      // 64-output tiles of a 512-wide layer
 constexpr int kOut = 64;          // outputs per tile
-constexpr int kWin = 256;         // inputs per weight window
+constexpr int kWin = 128;         // inputs per weight window
 constexpr int kMaxW = 512;
 constexpr int kActLd = kMaxW + 8; // padded activation row (bf16)
 constexpr int kWLd = kWin + 8;    // padded weight row (bf16)
@@ -39,12 +39,12 @@ constexpr int kGroups = kOut * kWin / 4 / kThreads;  // 16-byte groups per threa
 
 struct __attribute__((aligned(16))) WSmem {
     __bf16 act[kTok * kActLd];     // [token][feature]
-    __bf16 w[2][kOut * kWLd];      // [output][input - k0]
+    __bf16 w[kOut * kWLd];         // [output][input - k0]
 };
 
 // One weight window: rows o0 .. o0+63 (< nout) and columns k0 .. k0+255 (< nin) of W
-// (row-major nout x nin, fp32).  Thread t loads columns 4 (t % 64) .. +3 of rows
-// t / 64 + 4 m, m < 16: sixteen 16-byte loads (64 contiguous floats per row and wave).
+// (row-major nout x nin, fp32).  Thread t loads columns 4 (t % 32) .. +3 of rows
+// t / 32 + 8 m, m < 8: eight 16-byte loads (32 contiguous floats per row and half-wave).
 struct Window {
     f32x4 v[kGroups];
 };
@@ -52,10 +52,10 @@ struct Window {
 __device__ __forceinline__ void load_window(Window& x, const float* W, int nout, int nin, int o0,
                                             int k0) {
     const int tid = threadIdx.x;
-    const int k = k0 + 4 * (tid & 63);
+    const int k = k0 + 4 * (tid % (kWin / 4));
 #pragma unroll
     for (int m = 0; m < kGroups; ++m) {
-        const int r = o0 + (tid >> 6) + 4 * m;
+        const int r = o0 + tid / (kWin / 4) + (kThreads / (kWin / 4)) * m;
         x.v[m] = (r < nout && k < nin) ? *reinterpret_cast<const f32x4*>(W + (int64_t)r * nin + k)
                                        : zero4();
     }
@@ -63,10 +63,11 @@ __device__ __forceinline__ void load_window(Window& x, const float* W, int nout,
 
 __device__ __forceinline__ void store_window(const Window& x, __bf16* dst) {
     const int tid = threadIdx.x;
-    const int kk = 4 * (tid & 63);
+    const int kk = 4 * (tid % (kWin / 4));
 #pragma unroll
     for (int m = 0; m < kGroups; ++m)
-        *reinterpret_cast<bf16x4*>(dst + ((tid >> 6) + 4 * m) * kWLd + kk) = bf4(x.v[m]);
+        *reinterpret_cast<bf16x4*>(dst + (tid / (kWin / 4) + (kThreads / (kWin / 4)) * m) * kWLd + kk) =
+            bf4(x.v[m]);
 }
 
 __global__ void __launch_bounds__(kThreads) retrieve_wide_kernel(ScanArgs A) {
@@ -119,10 +120,9 @@ __global__ void __launch_bounds__(kThreads) retrieve_wide_kernel(ScanArgs A) {
             v = *reinterpret_cast<const bf16x4*>(qg + qbase + (t0 + t) * A.qs[1] + c);
         *reinterpret_cast<bf16x4*>(sm.act + t * kActLd + c) = v;
     }
-    store_window(nx, sm.w[0]);
+    store_window(nx, sm.w);
     __syncthreads();
 
-    int buf = 0;
     f32x4 acc[kCt];
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) acc[ct] = zero4();
@@ -137,7 +137,7 @@ __global__ void __launch_bounds__(kThreads) retrieve_wide_kernel(ScanArgs A) {
         if (more) load_window(nx, th + A.off[L2], A.n[L2], A.n[L2 - 1], o2, k2);
 
         const int kw = (nin - wk) < kWin ? (nin - wk) : kWin;  // a multiple of 16
-        const __bf16* ar = sm.w[buf] + (16 * wv + j) * kWLd + 4 * g;
+        const __bf16* ar = sm.w + (16 * wv + j) * kWLd + 4 * g;
         for (int ks = 0; ks < kw; ks += 32) {
             const bf16x8 a = frag(ar, ks);
 #pragma unroll
@@ -178,8 +178,8 @@ __global__ void __launch_bounds__(kThreads) retrieve_wide_kernel(ScanArgs A) {
 #pragma unroll
             for (int ct = 0; ct < kCt; ++ct) acc[ct] = zero4();
         }
-        if (more) store_window(nx, sm.w[buf ^ 1]);
-        __syncthreads();  // the next window is in LDS; a finished layer's inputs are read
+        __syncthreads();  // this window and, at a layer's end, the layer's inputs are read
+        if (more) store_window(nx, sm.w);
         if (more && L2 != wl) {
             // hidden layer wl is done: its outputs replace its inputs
 #pragma unroll
@@ -190,9 +190,8 @@ __global__ void __launch_bounds__(kThreads) retrieve_wide_kernel(ScanArgs A) {
                     for (int ct = 0; ct < kCt; ++ct)
                         *reinterpret_cast<bf16x4*>(sm.act + (16 * ct + j) * kActLd + f0) = stash[ot][ct];
             }
-            __syncthreads();
         }
-        buf ^= 1;
+        __syncthreads();  // the next window (and a finished layer's outputs) are in LDS
         wl = L2;
         wo = o2;
         wk = k2;
