@@ -375,7 +375,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the B*H memories are "
+        print(json.dumps({"error": "bench.py runs on one GPU only: the B*H memories are "
                                    "independent and are not sharded across GPUs; run with --gpus 1"}))
         sys.exit(2)
 
