@@ -130,3 +130,37 @@ def test_mac_full_size_sampled_rows_and_state():
                                        np.zeros((1, P)), wl.chunk, wl.widths)
         _check_state(th[b, h], th_ref.reshape(-1), f"theta_T[{b},{h}]")
         _check_state(s[b, h], s_ref.reshape(-1), f"s_T[{b},{h}]")
+
+
+def test_mac_full_size_zero_memory_late_segments():
+    """theta0 = 0 keeps the memory at zero (a bias-free MLP reads 0 and its gradient at 0
+    vanishes), so every segment's reads are zero and a query of segment i at offset u sees
+    L zero entries plus its own keys: y = sum_{u' <= u} e^{s} v / (L + sum e^{s}).  Rows of
+    the last three segments are checked with the storage-only bars."""
+    Sg = 4096
+    wl = S.WORKLOADS["h16_d64_b8_t16k"]
+    mi = S.make_mag_inputs(wl, 0, seed=4)
+    zero = np.zeros_like(mi.theta0)
+    import sequence_models_amd as sm
+
+    B = wl.batch
+    th0 = torch.zeros((B,) + zero.shape, dtype=torch.float32, device="cuda")
+    print("mac_forward zero memory, full size", flush=True)
+    out, th, _ = sm.mac_forward(_bf16(mi.x), _bf16(mi.w_in), torch.from_numpy(mi.b_gate).cuda(),
+                                _bf16(mi.w_out), th0, torch.zeros_like(th0), wl.chunk, Sg,
+                                wl.widths, wl.eta_scale)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(th).item() == 0
+    out = out.float().cpu().numpy()
+    Wq, Wk, Wv, Wg, bg, Wo = mi.oracle_weights()
+    H, d = wl.heads, wl.d
+    got, ref = [], []
+    for b, t in ((0, 4096), (1, 6000), (3, 8191), (4, 8192), (6, 12345), (7, 16383)):
+        seg0 = t // Sg * Sg
+        x = S.bf16_bits_to_f32(mi.x[b:b + 1, seg0:t + 1]).astype(np.float64)
+        q, k, v, *_ = omag.front_end(x, Wq, Wk, Wv, Wg, bg, H, 0.0)
+        e = np.exp(np.einsum("hd,jhd->hj", q[0, -1], k[0]) / np.sqrt(d))
+        y = np.einsum("hj,jhd->hd", e, v[0]) / (Sg + e.sum(axis=1))[:, None]
+        ref.append(y.reshape(-1) @ Wo)
+        got.append(out[b, t])
+    _check_out(np.array(got), np.array(ref))
