@@ -43,6 +43,7 @@ PEAKS = {  # MI355X published dense peaks
     "mfma_f32": 157.3,
     "valu_f32": 157.3,
     "hbm": 8000.0,         # GB/s
+    "valu_slots": 39.32,   # T lane-slots/s: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, scalar fp32
 }
 
 
@@ -162,8 +163,21 @@ def bench_retrieve(tm, torch, q, theta, wl, steps, warmup):
     else:
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAKS["hbm"], "unit": "GB/s",
                 "frac": gbs / PEAKS["hbm"], "alg_bytes_per_launch": nbytes}
-    return {"path": tm.retrieve_path(q, wl.widths), "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
-            "roofline": roof, "mfma_tflops": tflops}
+    out = {"path": tm.retrieve_path(q, wl.widths), "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+           "roofline": roof, "mfma_tflops": tflops}
+    # The SiLU of every hidden unit is vector-ALU work the matrix cores do not share: one
+    # exp2 and one reciprocal (transcendental, a quarter of the issue rate: 4 slots each), an
+    # add, a multiply and half a packed bf16 conversion -> 10.5 lane slots per hidden unit
+    # and token-head, against 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T slots/s of
+    # scalar fp32 issue (packed fp32 is not used).
+    hidden = sum(wl.widths[1:-1])
+    if hidden:
+        slots = 10.5 * hidden * B * T * H
+        rate = slots / (ms * 1e-3) / 1e12
+        out["alu_roofline"] = {"bound": "alu", "achieved": rate, "peak": PEAKS["valu_slots"],
+                               "unit": "T lane-slots/s", "frac": rate / PEAKS["valu_slots"],
+                               "alg_slots_per_launch": slots}
+    return out
 
 
 def bench_biases(tm, torch, t, wl, out, ws, steps, warmup):
