@@ -60,3 +60,26 @@ def test_workload_table():
     assert w["deep_h8_d128_b2_t32k"].n_layers == 4 and w["deep_h8_d128_b2_t32k"].params == 655360
     assert w["long_h16_d64_b1_t2m"].seq_len == 1 << 21 and w["long_h16_d64_b1_t2m"].chunk == 256
     assert w["tiny_f32_h1_t512"].io == "f32" and w["tiny_f32_h1_t512"].chunk == 16
+
+
+def test_mag_inputs_prefix_consistent_and_distributed_as_the_recipe():
+    import synthetic as S
+
+    wl = S.WORKLOADS[S.HEADLINE].with_(heads=4)
+    a = S.make_mag_inputs(wl, 64, seed=2, seq_len=300, batch=2)
+    b = S.make_mag_inputs(wl, 64, seed=2, seq_len=100, batch=2)
+    assert np.array_equal(a.x[:, :100], b.x)
+    for n in ("w_in", "w_out", "b_gate", "theta0"):
+        assert np.array_equal(getattr(a, n), getattr(b, n))
+    D = wl.heads * wl.d
+    assert a.x.shape == (2, 300, D) and a.w_in.shape == (3 * D + 3 * wl.heads, D)
+    assert a.w_out.shape == (D, D) and a.b_gate.shape == (3 * wl.heads,)
+    # every projected feature of x is ~ N(0, 1); the gate biases are (mu_alpha, 0, mu_beta)
+    Wq, Wk, Wv, Wg, bg, Wo = a.oracle_weights()
+    x = S.bf16_bits_to_f32(a.x).astype(np.float64).reshape(-1, D)
+    for W in (Wq, Wv, Wg):
+        f = x @ W
+        assert abs(f.mean()) < 0.05 and abs(f.std() - 1.0) < 0.05
+    np.testing.assert_array_equal(bg, np.repeat([wl.alpha_mu, 0.0, wl.beta_mu], wl.heads))
+    c = S.make_mag_inputs(wl, 64, seed=3, seq_len=100, batch=2)
+    assert not np.array_equal(c.x, b.x) and not np.array_equal(c.w_in, b.w_in)
