@@ -493,6 +493,13 @@ def main():
                      "kernel": kernel, "kernel_ms": kernel_ms,
                      "alg_flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes(wl)},
     }
+    # fp64 checksums of the final memory per (b, h): its sum and Frobenius norm, listed when
+    # there are at most 16 memories (the long-context workload), else summarised
+    th64 = thT.double().reshape(B * H, -1)
+    sums, fros = th64.sum(dim=1).cpu().tolist(), th64.norm(dim=1).cpu().tolist()
+    result["state_checksum"] = ({"sum": sums, "fro": fros} if B * H <= 16 else
+                                {"memories": B * H, "sum_total": float(np.sum(sums)),
+                                 "fro_min": float(np.min(fros)), "fro_max": float(np.max(fros))})
     if not args.no_retrieve:
         result["retrieve"] = bench_retrieve(tm, torch, t["q"], thT, wl, args.steps, args.warmup)
     if not args.no_biases:
