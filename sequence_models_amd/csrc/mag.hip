@@ -52,6 +52,17 @@ __device__ __forceinline__ bf16x8 zero8() {
     return bf16x8{z, z, z, z, z, z, z, z};
 }
 
+// Max over the lane pairs l, l ^ 16 and l, l ^ 32 by the permlane swaps (register moves,
+// no LDS round trip): each swap returns the pair's two values, in some order, to both lanes.
+__device__ __forceinline__ float max_pair16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_pair32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Workgroups are dealt to the 8 XCDs round-robin; when the grid divides evenly, give each
 // XCD one contiguous range of logical tiles so that tiles sharing operands share an L2.
 __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nb) {
@@ -331,7 +342,7 @@ struct AttnArgs {
 // pitch D = H kD.  Wave w owns queries q0 + 32 w + 16 u + j (u = 0, 1) at lane (g, j).
 // Per 64-key block: S^T tile (u, t) = K_t Q_u^T, so lane (g, j) holds the scores of keys
 // 16 t + 4 g + r for its query of tile u; the max is shared by the four lanes of a query
-// (two xor shuffles); O^T += V^T P^T and the row sums (ones x P^T) take P^T straight from
+// (two permlane swaps); O^T += V^T P^T and the row sums (ones x P^T) take P^T straight from
 // the score registers (the accumulator's row index, the key, is the reduction index of the
 // value product) and V^T from a transposed LDS copy.  Key and value blocks are
 // double-buffered: the next block's global loads are in flight while the current one is
@@ -511,8 +522,7 @@ __global__ __launch_bounds__(256, kD <= 64 ? 3 : 1) void attn_kernel(AttnArgs a)
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
                     mx = fmaxf(fmaxf(fmaxf(mx, st[u][t][0]), fmaxf(st[u][t][1], st[u][t][2])), st[u][t][3]);
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                mx = max_pair32(max_pair16(mx));
                 const float ms = mx * a.scale_log2;
                 const bool grow = ms > m_ref[u] + 8.0f;
                 if (__ballot(grow)) {
