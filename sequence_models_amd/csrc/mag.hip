@@ -16,9 +16,10 @@
 //   out = (sigmoid(y_mem) * y_attn) W_out^T                W_out [D, D]
 //
 // Kernels:
-//   gemm_nt_kernel   C = A W^T on v_mfma_f32_16x16x32_bf16, 128 x 128 tiles, 4 waves of
+//   gemm_nt_kernel   C = A W^T on v_mfma_f32_16x16x32_bf16, 256 x 128 tiles, 8 waves of
 //                    64 x 64, k staged 32 deep through double-buffered LDS; the front-end
-//                    projection writes fp32, the output projection bf16.
+//                    projection normalizes and gates in its epilogue, the output
+//                    projection writes bf16.
 //                    When D is a multiple of 64 the projection's epilogue also normalizes
 //                    q and k per head and applies the gates (ProjFront); otherwise:
 //   prep_kernel      one workgroup per token: per-head norms of q and k (shuffle sums over
@@ -72,12 +73,14 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nb) {
 
 // ------------------------------------------------------------------------------ GEMM
 
-constexpr int kGT = 128;       // tile extent in M and in N
+constexpr int kGT = 128;       // tile extent in N
+constexpr int kGM = 256;       // tile extent in M (8 waves: 4 x 2 of 64 x 64)
 constexpr int kGK = 32;        // k per stage
 constexpr int kGP = kGK + 8;   // LDS row pitch in bf16
 constexpr int kGPR = kGK / 8;                // 16-byte pieces per tile row and stage
-constexpr int kGRows = 256 / kGPR;           // tile rows one pass of 256 threads stages
-constexpr int kGIt = kGT / kGRows;           // passes per operand and stage
+constexpr int kGRows = 512 / kGPR;           // tile rows one pass of 512 threads stages
+constexpr int kGItA = kGM / kGRows;          // passes per stage: A (256 rows), W (128 rows)
+constexpr int kGItW = kGT / kGRows;
 
 // Epilogues see a wave's whole 64 x 64 result: acc[in][im] holds C[r0 + 16 im + j]
 // [c0 + 16 in + 4 g + r]; red is 2 KiB of LDS free for the epilogue, and every wave of the
@@ -150,10 +153,10 @@ struct ProjFront {
             } else if (d == 128) {
                 // both halves' sums meet in LDS: red[wm-local row][wn]
                 __syncthreads();
-                if (g == 0) red[(static_cast<int>(r0 & 127) + 16 * im + j) * 2 + wn] = s0 + s1;
+                if (g == 0) red[(static_cast<int>(r0 % kGM) + 16 * im + j) * 2 + wn] = s0 + s1;
                 __syncthreads();
-                n0 = n1 = red[(static_cast<int>(r0 & 127) + 16 * im + j) * 2] +
-                          red[(static_cast<int>(r0 & 127) + 16 * im + j) * 2 + 1];
+                n0 = n1 = red[(static_cast<int>(r0 % kGM) + 16 * im + j) * 2] +
+                          red[(static_cast<int>(r0 % kGM) + 16 * im + j) * 2 + 1];
             }
             if (m >= M || (sec == 3 && c0 >= 3 * D + 3 * H)) continue;
             if (sec < 3) {
@@ -184,49 +187,52 @@ struct ProjFront {
 
 // C[m][n] = sum_k A[m][k] W[n][k] for A [M, K] (row pitch lda) and W [N, K] (row pitch K),
 // K a multiple of 8, A and W 16-byte aligned.  Workgroup tile (tm, tn) covers rows
-// 128 tm .. +127 and columns 128 tn .. +127; wave w the 64 x 64 quarter (w / 2, w % 2).
+// 256 tm .. +255 and columns 128 tn .. +127; wave w the 64 x 64 block (w / 2, w % 2).
 // The product is formed transposed (W rows as the MFMA's A operand) so that a lane's
 // accumulator holds four consecutive columns of one row: lane (g, j) of block (in, im)
 // holds C[16 im + j][16 in + 4 g + r], r = 0..3.
 template <class Epi>
-__global__ __launch_bounds__(256) void gemm_nt_kernel(const __bf16* __restrict__ A, int64_t lda,
+__global__ __launch_bounds__(512) void gemm_nt_kernel(const __bf16* __restrict__ A, int64_t lda,
                                                       const __bf16* __restrict__ W, int64_t M,
                                                       int N, int K, int tiles_n, Epi epi) {
-    __shared__ __align__(16) __bf16 sa[2][kGT * kGP];
+    __shared__ __align__(16) __bf16 sa[2][kGM * kGP];
     __shared__ __align__(16) __bf16 sw[2][kGT * kGP];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, j = lane & 15;
     const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int64_t m0 = (bid / tiles_n) * kGT;
+    const int64_t m0 = (bid / tiles_n) * kGM;
     const int n0 = static_cast<int>(bid % tiles_n) * kGT;
     // staging: thread t stages the 16-byte piece (t % kGPR) of rows t / kGPR + kGRows i
     const int r0 = tid / kGPR, kc = (tid % kGPR) * 8;
-    bf16x8 ra[kGIt], rw[kGIt];
+    bf16x8 ra[kGItA], rw[kGItW];
     auto load = [&](int k0) {
+        const bool kok = k0 + kc < K;
 #pragma unroll
-        for (int i = 0; i < kGIt; ++i) {
-            const int r = r0 + kGRows * i;
-            const bool kok = k0 + kc < K;
-            const int64_t m = m0 + r;
-            const int n = n0 + r;
+        for (int i = 0; i < kGItA; ++i) {
+            const int64_t m = m0 + r0 + kGRows * i;
             ra[i] = (kok && m < M) ? *reinterpret_cast<const bf16x8*>(A + m * lda + k0 + kc) : zero8();
+        }
+#pragma unroll
+        for (int i = 0; i < kGItW; ++i) {
+            const int n = n0 + r0 + kGRows * i;
             rw[i] = (kok && n < N) ? *reinterpret_cast<const bf16x8*>(W + (int64_t)n * K + k0 + kc)
                                    : zero8();
         }
     };
     auto store = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < kGIt; ++i) {
+        for (int i = 0; i < kGItA; ++i)
             *reinterpret_cast<bf16x8*>(&sa[buf][(r0 + kGRows * i) * kGP + kc]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < kGItW; ++i)
             *reinterpret_cast<bf16x8*>(&sw[buf][(r0 + kGRows * i) * kGP + kc]) = rw[i];
-        }
     };
     f32x4 acc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = fused::zero4();
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 1, wn = wave & 1;  // wm 0..3
     const int nk = (K + kGK - 1) / kGK;
     load(0);
     store(0);
@@ -259,8 +265,8 @@ static hipError_t gemm_nt(const __bf16* A, int64_t lda, const __bf16* W, int64_t
                           Epi epi, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     const int tiles_n = (N + kGT - 1) / kGT;
-    const int64_t tiles = (M + kGT - 1) / kGT * tiles_n;
-    hipLaunchKernelGGL(gemm_nt_kernel<Epi>, dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
+    const int64_t tiles = (M + kGM - 1) / kGM * tiles_n;
+    hipLaunchKernelGGL(gemm_nt_kernel<Epi>, dim3(static_cast<unsigned>(tiles)), dim3(512), 0,
                        stream, A, lda, W, M, N, K, tiles_n, epi);
     return hipGetLastError();
 }
