@@ -114,29 +114,87 @@ def measured_traffic(kernel, workload):
     return rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"]
 
 
-def cpu_baseline(inp, wl, sample_rows, sample_tokens):
+def cpu_baseline(inp, wl, sample_rows, sample_tokens, single_tokens=1024):
+    """The fp64 oracle on a bounded sample of the workload: the first `sample_rows` batch rows
+    x every head over the first `sample_tokens` tokens on every usable host core, then one
+    memory over `single_tokens` tokens on one thread.  Rates are workload tokens/s (a token
+    is one batch row's position, all heads)."""
     import oracle
 
-    threads = len(os.sched_getaffinity(0))
+    usable = len(os.sched_getaffinity(0))
     T = min(sample_tokens, wl.seq_len)
     rows = min(sample_rows, wl.batch)
     sl = (slice(0, rows), slice(0, T))
     q, k, v = (inp.qkv_f32(n)[sl] for n in ("q", "k", "v"))
     g = [getattr(inp, n)[sl] for n in ("alpha", "eta", "beta")]
     t0 = time.perf_counter()
-    oracle.scan(q, k, v, *g, inp.theta0, inp.s0, wl.chunk, wl.widths, nthreads=threads)
+    oracle.scan(q, k, v, *g, inp.theta0, inp.s0, wl.chunk, wl.widths, nthreads=usable)
     dt = time.perf_counter() - t0
-    used = min(threads, rows * wl.heads)
+    used = min(usable, rows * wl.heads)
+    # one thread, one memory (batch row 0, head 0): memory-tokens/s, / H for workload tokens/s
+    T1 = min(single_tokens, wl.seq_len)
+    one = (slice(0, 1), slice(0, T1), slice(0, 1))
+    q1, k1, v1 = (inp.qkv_f32(n)[one] for n in ("q", "k", "v"))
+    g1 = [getattr(inp, n)[one] for n in ("alpha", "eta", "beta")]
+    t1 = time.perf_counter()
+    oracle.scan(q1, k1, v1, *g1, inp.theta0[:1], inp.s0[:1], wl.chunk, wl.widths, nthreads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": rows * T / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "host_cores": os.cpu_count(), "usable_cores": usable,
+            "single_thread_value": T1 / dt1 / wl.heads,
             "sample": f"fp64 oracle, batch rows 0..{rows - 1} x all {wl.heads} heads "
                       f"({rows * wl.heads} memories), first {T} of {wl.seq_len} tokens "
-                      f"({dt:.1f} s on {used} threads of {threads} host cores)"}
+                      f"({dt:.1f} s on {used} threads; {usable} usable of {os.cpu_count()} host "
+                      f"cores); single thread: 1 memory x {T1} tokens in {dt1:.2f} s"}
+
+
+def time_calls(torch, fn, steps, warmup):
+    """Mean ms of fn() over `steps` calls after `warmup`, from HIP events on torch's current
+    stream (the stream the library launches on)."""
+    for _ in range(warmup):
+        fn()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def bench_sustained(tm, torch, t, wl, seed, out, ws, steps, warmup, peak):
+    """The same scan (same q, k, v, shapes and launch) with the sustained gate mix, which
+    keeps every memory O(1) to the end (with the specified gates the memory decays to its
+    zero fixed point within a few thousand tokens, so most chunks of the headline step
+    multiply zero state).  Returns the object and the final weights (a live memory)."""
+    import synthetic
+
+    swl = synthetic.sustained(wl)
+    B, T, H = t["q"].shape[:3]
+    gates = synthetic.make_gates(swl, seed, T, B)
+    ts = dict(t)
+    for n, g in zip(("alpha", "eta", "beta"), gates):
+        ts[n] = torch.from_numpy(g).to(t["q"].device)
+    y, thT, sT = out
+
+    def run():
+        tm.scan(ts["q"], ts["k"], ts["v"], ts["alpha"], ts["eta"], ts["beta"], ts["theta0"],
+                ts["s0"], wl.chunk, wl.widths, y=y, theta_T=thT, s_T=sT, workspace=ws)
+    ms = time_calls(torch, run, steps, warmup)
+    flops = alg_flops_per_token_head(wl.widths, wl.chunk) * B * T * H
+    tf = flops / (ms * 1e-3) / 1e12
+    fro = thT.double().reshape(B * H, -1).norm(dim=1)
+    return {"ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "alpha_mu": swl.alpha_mu,
+            "eta_scale": swl.eta_scale, "frac": tf / peak, "achieved": tf,
+            "state_fro_min": float(fro.min()), "state_fro_max": float(fro.max())}, thT.clone()
 
 
 def bench_retrieve(tm, torch, q, theta, wl, steps, warmup):
-    """titans_mem_retrieve (fixed-weight read) over the same q with the scan's final
-    weights [B, H, P]: its own line, not part of the scan step.  Algorithmic bytes: q and y
-    once, theta once per memory; flops 2 P per token-head."""
+    """titans_mem_retrieve (fixed-weight read) over the same q with live weights [B, H, P]
+    (the sustained scan's final weights, else theta0): its own line, not part of the scan
+    step.  Algorithmic bytes: q and y once, theta once per memory; flops 2 P per token-head."""
     y = torch.empty_like(q)
     for _ in range(warmup):
         tm.retrieve(q, theta, wl.widths, y=y)
@@ -376,6 +434,7 @@ def main():
     ap.add_argument("--cpu-sample-rows", type=int, default=8)
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sustained", action="store_true")
     ap.add_argument("--no-retrieve", action="store_true")
     ap.add_argument("--no-biases", action="store_true")
     ap.add_argument("--no-surprise", action="store_true")
@@ -500,10 +559,16 @@ def main():
     result["state_checksum"] = ({"sum": sums, "fro": fros} if B * H <= 16 else
                                 {"memories": B * H, "sum_total": float(np.sum(sums)),
                                  "fro_min": float(np.min(fros)), "fro_max": float(np.max(fros))})
+    import synthetic as _syn
+    live = None
+    if not args.no_sustained and wl.name in _syn.SUSTAINED:
+        result["sustained"], live = bench_sustained(tm, torch, t, wl, args.seed, (y, thT, sT), ws,
+                                                    args.steps, args.warmup, peak)
     if not args.no_retrieve:
-        result["retrieve"] = bench_retrieve(tm, torch, t["q"], thT, wl, args.steps, args.warmup)
+        if live is None:
+            live = t["theta0"].expand(B, -1, -1).contiguous()
+        result["retrieve"] = bench_retrieve(tm, torch, t["q"], live, wl, args.steps, args.warmup)
     if not args.no_biases:
-        # after the retrieve: it reads the squared-error scan's final weights
         result["biases"] = bench_biases(tm, torch, t, wl, (y, thT, sT), ws, args.steps, args.warmup)
     if not args.no_surprise:
         result["surprise"] = bench_surprise(tm, torch, t, wl, (y, thT, sT), min(args.steps, 5), 1)

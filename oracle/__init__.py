@@ -18,19 +18,22 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "titans_oracle.c")
-_LIB = os.path.join(_HERE, "libtitans_oracle.so")
+# TITANS_ORACLE_LIB points the loader at another build of the same source (the tests'
+# sanitizer build); build() always writes the default path.
+_DEFAULT_LIB = os.path.join(_HERE, "libtitans_oracle.so")
+_LIB = os.environ.get("TITANS_ORACLE_LIB") or _DEFAULT_LIB
 _lib = None
 
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (-O2, OpenMP over independent sequences)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
+    if force or not os.path.exists(_DEFAULT_LIB):
+        tmp = _DEFAULT_LIB + ".tmp"
         subprocess.check_call(
             ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall",
              "-Wno-unused-variable", _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, _DEFAULT_LIB)
+    return _DEFAULT_LIB
 
 
 def _load():

@@ -24,7 +24,10 @@ import torch
 __all__ = ["mac_forward", "mac_workspace_size", "MacDesc", "mag_forward", "mag_workspace_size", "MagDesc", "scan", "scan_backward", "scan_backward_workspace_size", "retrieve", "scan_workspace_size", "scan_path", "retrieve_path", "param_count", "TitansError", "LIB_PATH",
            "lib", "ScanDesc", "MlpDesc", "MAX_LAYERS"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtitans_mem.so")
+# TITANS_MEM_LIB loads another build of the same sources instead (the tests' host-only
+# sanitizer build of the validation layer); there is no fallback either way.
+LIB_PATH = os.environ.get("TITANS_MEM_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libtitans_mem.so")
 MAX_LAYERS = 4
 F32, BF16 = 0, 1
 

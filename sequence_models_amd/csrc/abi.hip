@@ -224,11 +224,23 @@ static int64_t device_cus() {
 
 enum class Path { Generic, Phased, Fused, Pair, Linear };
 
+// Testing overrides.  The TITANS_MEM_* switches below (kernel family, generic member,
+// linear path, fused kernel, the pair path's failure hook) are read only while
+// TITANS_MEM_DEBUG=1 is set as well, so a stray variable cannot move production calls
+// onto another path; titans_mem_scan_path reports the path a call would take, overrides
+// included.
+static const char* debug_env(const char* name) {
+    const char* on = getenv("TITANS_MEM_DEBUG");
+    if (!on || on[0] != '1') return nullptr;
+    return getenv(name);
+}
+
 // Within the generic family: the chain of GPU-wide launches for memories with a layer of
 // 128 or more units (their chunk products span several 64 x 64 tiles), else one workgroup
-// per memory.  TITANS_MEM_GENERIC_MODE=single / phased picks one for testing.
+// per memory.  TITANS_MEM_GENERIC_MODE=single / phased picks one for testing (with
+// TITANS_MEM_DEBUG=1).
 static Path generic_path(const titans::ScanArgs& a) {
-    const char* env = getenv("TITANS_MEM_GENERIC_MODE");
+    const char* env = debug_env("TITANS_MEM_GENERIC_MODE");
     if (env && strcmp(env, "single") == 0) return Path::Generic;
     if (env && strcmp(env, "phased") == 0) return Path::Phased;
     int maxw = 0;
@@ -240,17 +252,18 @@ static Path generic_path(const titans::ScanArgs& a) {
 // workgroups (any chunk length that is a multiple of 64) while the pairs fit the device at
 // one workgroup per compute unit, else on one workgroup per memory (C = 64 only).  A linear
 // memory (L = 1) with the squared-error bias and enough chunks takes the sequence-parallel
-// linear path.  Debugging switches: TITANS_MEM_FORCE_GENERIC=1 routes every call through
-// the generic family, TITANS_MEM_LINEAR=0 keeps linear memories on it too,
-// TITANS_MEM_FUSED_SINGLE=1 keeps the fused shape on one workgroup per memory.
+// linear path.  Testing switches (read with TITANS_MEM_DEBUG=1 only):
+// TITANS_MEM_FORCE_GENERIC=1 routes every call through the generic family,
+// TITANS_MEM_LINEAR=0 keeps linear memories on it too, TITANS_MEM_FUSED_SINGLE=1 keeps the
+// fused shape on one workgroup per memory.
 static Path choose_path(const titans::ScanArgs& a) {
-    const char* env = getenv("TITANS_MEM_FORCE_GENERIC");
+    const char* env = debug_env("TITANS_MEM_FORCE_GENERIC");
     if (env && env[0] == '1') return generic_path(a);
-    env = getenv("TITANS_MEM_GENERIC_MODE");  // a chosen member of the generic family
+    env = debug_env("TITANS_MEM_GENERIC_MODE");  // a chosen member of the generic family
     if (env && env[0]) return generic_path(a);
-    env = getenv("TITANS_MEM_LINEAR");
+    env = debug_env("TITANS_MEM_LINEAR");
     if (!(env && env[0] == '0') && titans::scan_linear_supported(a)) return Path::Linear;
-    env = getenv("TITANS_MEM_FUSED_SINGLE");
+    env = debug_env("TITANS_MEM_FUSED_SINGLE");
     const bool single = env && env[0] == '1';
     if (!single && titans::scan_pair_supported(a) &&
         titans::scan_pair_workgroups(a) <= device_cus())
@@ -422,7 +435,7 @@ static titans_status scan_impl(const titans_scan_desc* desc, const titans_mlp_de
     // Test hook for the pair path's failure handling: side 1 of every pair never posts its
     // exchange flags and every wait gives up after a few polls, so side 0 times out (its
     // slice of theta_T / s_T comes out NaN) while every kernel still ends normally.
-    const char* hook = getenv("TITANS_MEM_TEST_PAIR_TIMEOUT");
+    const char* hook = debug_env("TITANS_MEM_TEST_PAIR_TIMEOUT");
     a.debug = (hook && hook[0] == '1') ? 1 : 0;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const Path path = a.T > 0 ? scan_path_of(a, want_surprise) : Path::Generic;
@@ -619,9 +632,10 @@ enum class RPath { Fused, Wide, Generic };
 
 // The 64-256-64 bf16 memory keeps its weights in LDS ("fused_mfma"); other bf16 memories
 // with widths that are multiples of 16 stream them ("wide_mfma"); the rest, and fp32 I/O,
-// take the generic kernel.  TITANS_MEM_FORCE_GENERIC=1 forces the generic kernel.
+// take the generic kernel.  TITANS_MEM_FORCE_GENERIC=1 (with TITANS_MEM_DEBUG=1) forces
+// the generic kernel.
 static RPath retrieve_path_of(const titans::ScanArgs& a) {
-    const char* env = getenv("TITANS_MEM_FORCE_GENERIC");
+    const char* env = debug_env("TITANS_MEM_FORCE_GENERIC");
     if (env && env[0] == '1') return RPath::Generic;
     if (titans::retrieve_mfma_supported(a)) return RPath::Fused;
     return titans::retrieve_wide_supported(a) ? RPath::Wide : RPath::Generic;

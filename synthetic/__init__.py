@@ -88,6 +88,22 @@ WORKLOADS = {
 
 HEADLINE = "h16_d64_b8_t16k"
 
+# Gate mixes that keep every memory O(1) to the end of its sequence.  With the specified
+# gates and i.i.d. q/k/v the memory decays to its zero fixed point within a few thousand
+# tokens, so each full shape is also run with alpha_t = sigmoid(N(mu, 1)) for a lower mu
+# (and, with C = 256, a smaller eta scale: there eta = 0.1 sigmoid(.) diverges in the fp64
+# recurrence itself).  (alpha_mu, eta_scale) per workload.
+SUSTAINED = {"h8_d64_b4_t4k": (-7.0, 0.1), "h16_d64_b8_t16k": (-7.0, 0.1),
+             "deep_h8_d128_b2_t32k": (-8.0, 0.05), "long_h16_d64_b1_t2m": (-10.0, 0.02)}
+
+
+def sustained(wl: "Workload | str") -> "Workload":
+    """The workload with its sustained gate mix (name suffixed "_sustained")."""
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    mu, es = SUSTAINED[wl.name]
+    return wl.with_(alpha_mu=mu, eta_scale=es, name=wl.name + "_sustained")
+
 
 @dataclasses.dataclass
 class Inputs:
@@ -179,6 +195,14 @@ def make_theta0(wl: Workload, seed: int) -> np.ndarray:
     return th
 
 
+def make_gates(wl: Workload, seed: int, T: int, B: int):
+    """alpha, eta, beta [B, T, H] float32 (the same streams as make_inputs draws)."""
+    alpha = _draw_gate(seed, _ALPHA, wl, B, T, lambda z: _sigmoid(z + wl.alpha_mu))
+    eta = _draw_gate(seed, _ETA, wl, B, T, lambda z: wl.eta_scale * _sigmoid(z))
+    beta = _draw_gate(seed, _BETA, wl, B, T, lambda z: _sigmoid(z + wl.beta_mu))
+    return alpha, eta, beta
+
+
 def make_inputs(wl: Workload | str, seed: int = 0, seq_len: int | None = None,
                 batch: int | None = None) -> Inputs:
     """Draw the workload's inputs.  seq_len / batch override T / B (prefix-consistent)."""
@@ -194,9 +218,7 @@ def make_inputs(wl: Workload | str, seed: int = 0, seq_len: int | None = None,
     _draw_vectors(seed, _Q, wl, B, T, True, q)
     _draw_vectors(seed, _K, wl, B, T, True, k)
     _draw_vectors(seed, _V, wl, B, T, False, v)
-    alpha = _draw_gate(seed, _ALPHA, wl, B, T, lambda z: _sigmoid(z + wl.alpha_mu))
-    eta = _draw_gate(seed, _ETA, wl, B, T, lambda z: wl.eta_scale * _sigmoid(z))
-    beta = _draw_gate(seed, _BETA, wl, B, T, lambda z: _sigmoid(z + wl.beta_mu))
+    alpha, eta, beta = make_gates(wl, seed, T, B)
     theta0 = make_theta0(wl, seed)
     s0 = np.zeros_like(theta0)
     return Inputs(wl.with_(batch=B, seq_len=T), q, k, v, alpha, eta, beta, theta0, s0)

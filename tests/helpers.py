@@ -29,6 +29,11 @@ def to_f64(t) -> np.ndarray:
 
 F32_MIN_NORMAL = 2.0 ** -126
 
+# A reference state below this norm has decayed out of float32's range in practice (the
+# memory's zero fixed point): its relative error carries no information, so the state
+# checks skip it (and say so) instead of passing against a floor.
+DECAYED_STATE = 1e-20
+
 
 def rel_err_slices(x, ref, axes):
     """max over slices of ||x - ref||_F / max(||ref||_F, floor); `axes` are reduced.
@@ -54,3 +59,27 @@ def y_rel_err(y, y_ref):
 def state_rel_err(th, th_ref):
     """theta: [B,H,P]; per-(b,h) relative error, max over (b,h)."""
     return rel_err_slices(th, th_ref, axes=(2,))
+
+
+def token_errors(y, y_ref, chunk, floor=2.0 ** -96):
+    """Per-token error of one sequence, y and y_ref [T, d].
+
+    e_t = ||y_t - ref_t|| / s_t, with s_t the RMS of the reference rows' norms over the
+    chunk that holds token t (a local scale: an element of y_t is a sum over the hidden
+    units, so its rounding error follows the size of the chunk's reads, not the size of
+    y_t itself, which can cancel).  Chunks whose scale is below `floor` (a memory decayed
+    to its zero fixed point, out of float32's relative precision) are left out.
+    Returns (max e_t, 99th percentile, index of the worst token, tokens left out)."""
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(y_ref, np.float64)
+    T = ref.shape[0]
+    err = np.sqrt(np.sum((y - ref) ** 2, axis=-1))
+    nrm2 = np.sum(ref ** 2, axis=-1)
+    nch = (T + chunk - 1) // chunk
+    padded = np.concatenate([nrm2, np.full(nch * chunk - T, np.nan)]).reshape(nch, chunk)
+    s = np.repeat(np.sqrt(np.nanmean(padded, axis=1)), chunk)[:T]
+    keep = s > floor
+    if not keep.any():
+        return 0.0, 0.0, -1, T
+    e = np.where(keep, err / np.where(keep, s, 1.0), 0.0)
+    return float(e.max()), float(np.percentile(e[keep], 99)), int(e.argmax()), int(T - keep.sum())

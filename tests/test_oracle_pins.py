@@ -527,3 +527,32 @@ def test_surprise_of_a_linear_memory_closed_form():
             assert sur[0, t, 0] == pytest.approx(2 * np.linalg.norm(r) * np.linalg.norm(k[0, t, 0]),
                                                  rel=1e-12)
             W = W - 2 * eta[0, t, 0] * np.outer(r, k[0, t, 0])
+
+
+def test_state_conditioning_is_a_property_of_the_method():
+    """The GPU tests' state bars are a multiple of how far theta_T moves when k and v carry
+    one bf16 rounding (each element times 1 + 2^-9 u, u ~ U(-1, 1)).  That sensitivity must
+    be the recurrence's, not an artefact of one implementation: the sequential oracle and the
+    independent NumPy chunk-form restatement give the same figure on the same perturbation,
+    and it is far above float64 rounding (a bf16-operand kernel cannot do better than a
+    multiple of it)."""
+    import synthetic
+
+    wl = synthetic.sustained("h16_d64_b8_t16k").with_(batch=1, heads=1, seq_len=1024)
+    inp = synthetic.make_inputs(wl, 0)
+    q, k, v = (inp.qkv_f32(n).astype(np.float64) for n in ("q", "k", "v"))
+    g = [getattr(inp, n).astype(np.float64) for n in ("alpha", "eta", "beta")]
+    rng = np.random.default_rng(7)
+    pk = k * (1.0 + 2.0 ** -9 * rng.uniform(-1, 1, k.shape))
+    pv = v * (1.0 + 2.0 ** -9 * rng.uniform(-1, 1, v.shape))
+    th0, s0 = inp.theta0.astype(np.float64), inp.s0.astype(np.float64)
+
+    def kappa(fn):
+        _, t, _ = fn(q, k, v, *g, th0, s0, wl.chunk, wl.widths)
+        _, tp, _ = fn(q, pk, pv, *g, th0, s0, wl.chunk, wl.widths)
+        return np.linalg.norm(tp - t) / np.linalg.norm(t)
+
+    k_oracle = kappa(oracle.scan)
+    k_chunk = kappa(chunk_form.chunk_scan)
+    assert 1e-3 < k_oracle < 2e-2
+    assert abs(k_oracle - k_chunk) <= 1e-3 * k_oracle
