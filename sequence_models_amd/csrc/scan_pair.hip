@@ -36,8 +36,10 @@
 // the parity of the chunk; a wave posts e + 1 only after its reads of exchange e have
 // returned, which is what lets the partner reuse a buffer two exchanges later.  The
 // launch is cooperative, so both workgroups of a pair are resident together.  A wait that
-// exceeds its bound (never expected) stops all further waits of that wave and the
-// memory's theta_T and s_T come out as NaN.
+// exceeds its bound (never expected) stops all further waits of that wave, and from then on
+// the wave sends NaN in place of its O and y partials and writes NaN y rows: the partner's
+// E2 turns NaN at the next exchange, so both halves of the memory end with NaN y rows and
+// a NaN theta_T / s_T, never with finite values built from a missing partial.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -159,10 +161,14 @@ __device__ __forceinline__ float* yslot(Smem& sm, int w) {
 //   p = prod_m beta_m,  w_j = (1 - beta_j) prod_{j<m<C} beta_m
 //   c_{t,j} = sum_{j<=i<t} L1[t][i] L2[i][j]          (strictly lower, t = 0..C)
 //     L1[t][i] = prod_{i<m<t} (1 - alpha_m),  L2[i][j] = eta_i (1 - beta_j) prod_{j<m<=i} beta_m
-// Each L1 / L2 entry is exp2 of a difference of log2 prefix sums (positive factors only;
-// a zero factor enters as log2 = -1024 and comes out as exactly zero); the C x C sum is one
-// bf16 MFMA product, row C of it is c_C.  Tokens past the sequence end are padding: no
-// decay, no write, momentum kept (alpha = eta = 0, beta = 1).
+// The carry's coefficients (the chunk-end row c_C and w) are scans of plain fp32 products
+// (suffix scans: the lane order reversed by a lane permutation): S_j = sum_{i>=j} L1[C][i]
+// eta_i prod_{j<m<=i} beta_m satisfies S_j = eta_j L1[C][j] + beta_{j+1} S_{j+1}, and
+// c_C[j] = (1 - beta_j) S_j.  The in-chunk matrix Cm (the reads only) is one bf16 MFMA
+// product of L1 and L2 entries, each exp2 of a difference of log2 prefix sums (positive
+// factors only; a zero factor enters as log2 = -1024 and comes out as exactly zero).
+// Tokens past the sequence end are padding: no decay, no write, momentum kept (alpha = eta
+// = 0, beta = 1).
 //
 // Record of one chunk (bytes): Cm [t][j] bf16 64 x 64 | a[0..63] | b[0..63] | c_C[0..63] |
 // w[0..63] (fp32) | a_C, b_C, p, 0.
@@ -208,6 +214,11 @@ __device__ __forceinline__ bf16x8 l2_frag(const CoefSmem& cs, float lbj, float o
     return f;
 }
 
+// Value of lane 63 - l (the wave's lane order reversed).
+__device__ __forceinline__ float lane_rev(float x, int l) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((63 - l) << 2, __float_as_int(x)));
+}
+
 __global__ void __launch_bounds__(kThreads) pair_coef_kernel(ScanArgs A, char* coef, int64_t nchunks) {
     __shared__ CoefSmem csm[kWaves];
     const int wv = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, j = l & 15;
@@ -234,16 +245,23 @@ __global__ void __launch_bounds__(kThreads) pair_coef_kernel(ScanArgs A, char* c
     const float lb = wave_scan_add(be_l > 0.f ? __log2f(be_l) : -1024.f);
     float mk = keep, mc = et_l * pbl;        // affine maps x -> keep_t x + eta_t p_t, composed
     wave_scan_affine(mk, mc);
-    const float la2C = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lk), 63));
-    const float lbL = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lb), 63));
+    // suffix products and the suffix affine scan, on the reversed lane order (lane
+    // r = 63 - j holds token j): L1[C][j] = prod_{j<m<C} (1 - alpha_m), prod_{j<m<C} beta_m,
+    // S_j = eta_j L1[C][j] + beta_{j+1} S_{j+1}
+    const float keep_r = lane_rev(keep, l), be_r = lane_rev(be_l, l), et_r = lane_rev(et_l, l);
+    const float l1c_r = lane_prev(wave_scan_mul(keep_r), 1.f);
+    const float pw_r = lane_prev(wave_scan_mul(be_r), 1.f);
+    float sk = lane_prev(be_r, 1.f), sc = et_r * l1c_r;
+    wave_scan_affine(sk, sc);
     cs.la2i[l] = lk;
     cs.la2x[l] = lane_prev(lk, 0.f);
     cs.lb2[l] = lb;
     cs.et[l] = et_l;
     cs.omb[l] = 1.f - be_l;
-    rv[l] = lane_prev(pa, 1.f);                                            // a_l
-    rv[kC + l] = lane_prev(mc, 0.f);                                       // b_l
-    rv[3 * kC + l] = (1.f - be_l) * __builtin_amdgcn_exp2f(lbL - lb);      // w_l
+    rv[l] = lane_prev(pa, 1.f);                       // a_l
+    rv[kC + l] = lane_prev(mc, 0.f);                  // b_l
+    rv[2 * kC + l] = (1.f - be_l) * lane_rev(sc, l);  // c_C[l]
+    rv[3 * kC + l] = (1.f - be_l) * lane_rev(pw_r, l);  // w_l
     if (l == 63) {
         rv[4 * kC + 0] = pa;
         rv[4 * kC + 1] = mc;
@@ -251,8 +269,7 @@ __global__ void __launch_bounds__(kThreads) pair_coef_kernel(ScanArgs A, char* c
         rv[4 * kC + 3] = 0.f;
     }
     wave_lds_sync();
-    // Cm^T[j][t] = sum_i L2^T[j][i] L1^T[i][t], tiles (j-block jt, t-block tb), jt <= tb;
-    // c_C[j] = sum_i L2^T[j][i] L1[C][i] with L1[C][i] broadcast to every column
+    // Cm^T[j][t] = sum_i L2^T[j][i] L1^T[i][t], tiles (j-block jt, t-block tb), jt <= tb
     bf16x8 l2f[4][2];
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
@@ -275,15 +292,6 @@ __global__ void __launch_bounds__(kThreads) pair_coef_kernel(ScanArgs A, char* c
                 x = mfma(l2f[jt][1], b1, x);
             }
             *reinterpret_cast<bf16x4*>(cmg + tr * kC + 16 * jt + 4 * g) = bf4(x);
-        }
-    }
-    {
-        const bf16x8 c0 = l1_frag(cs, la2C, kC, 0, g), c1 = l1_frag(cs, la2C, kC, 1, g);
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            f32x4 x = mfma(l2f[jt][0], c0, zero4());
-            x = mfma(l2f[jt][1], c1, x);
-            if (j == 0) *reinterpret_cast<f32x4*>(rv + 2 * kC + 16 * jt + 4 * g) = x;  // c_C
         }
     }
 }
@@ -436,8 +444,8 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
         bf16x8 out;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            out[2 * i] = (__bf16)(yown[2 * i] + lo32(px[i]));
-            out[2 * i + 1] = (__bf16)(yown[2 * i + 1] + hi32(px[i]));
+            out[2 * i] = (__bf16)(bad ? __builtin_nanf("") : yown[2 * i] + lo32(px[i]));
+            out[2 * i + 1] = (__bf16)(bad ? __builtin_nanf("") : yown[2 * i + 1] + hi32(px[i]));
         }
         if (t < A.T) *reinterpret_cast<bf16x8*>(yg + ybase + t * A.ys[1] + yd0) = out;
     };
@@ -647,7 +655,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                     o = *reinterpret_cast<const f32x4*>(sm.r[0] + xb + 4 * q4) +
                         *reinterpret_cast<const f32x4*>(sm.r[1] + xb + 4 * q4);
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) oo[4 * q4 + e4] = o[e4];
+                for (int e4 = 0; e4 < 4; ++e4) oo[4 * q4 + e4] = bad ? __builtin_nanf("") : o[e4];
             }
             // the O words go out now; the flag follows once they have landed (below)
             uint64_t* dst = oslot(e, side);
@@ -904,7 +912,9 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             for (int k = 0; k < 8; ++k) yown[k] = ys[0][k];
             uint64_t* dst = yxslot(e, side);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xstore(dst + i * kThreads, pack2(ys[1][2 * i], ys[1][2 * i + 1]));
+            for (int i = 0; i < 4; ++i)
+                xstore(dst + i * kThreads, pack2(bad ? __builtin_nanf("") : ys[1][2 * i],
+                                                 bad ? __builtin_nanf("") : ys[1][2 * i + 1]));
         }
         if (c0 + kC < A.T) commit_qc();  // every wave is past B6: Q and Cm are no longer read
         {
