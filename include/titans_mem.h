@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define TITANS_MEM_ABI_VERSION 5
+#define TITANS_MEM_ABI_VERSION 6
 #define TITANS_MAX_LAYERS 4
 
 typedef enum {
@@ -163,6 +163,26 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
                               const float* theta0, const float* s0,
                               void* y, float* theta_T, float* s_T,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * titans_mem_scan for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments
+ * without the workspace.  Serves the shapes titans_mem_scan runs on the pair path
+ * ("fused_pair" in titans_mem_scan_path); any other shape is TITANS_ERR_UNSUPPORTED.  Its
+ * scratch (exchange areas and chunk coefficient records) is a 64 MiB static device array
+ * that every GPU the library runs on holds until the process ends; the call enqueues the
+ * pair path over segments of the sequence that fit it, continuing in place through
+ * theta_T / s_T, and calls no hipMalloc, hipFree or other allocating routine.  Results are
+ * bitwise those of titans_mem_scan.  The array is shared by every call on one GPU: calls
+ * that overlap on a GPU (on different streams, or from several threads) race and must be
+ * serialized by the caller.  Errors as for titans_mem_scan; TITANS_ERR_UNSUPPORTED also
+ * when one chunk's scratch would exceed the array (not reachable on the pair path).
+ */
+titans_status titans_mem_scan_noalloc(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
+                                      const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* eta, const float* beta,
+                                      const float* theta0, const float* s0,
+                                      void* y, float* theta_T, float* s_T, void* stream);
 
 /*
  * The same scan, also writing each token's momentary surprise: surprise[b, t, h] =

@@ -21,7 +21,7 @@ import os
 
 import torch
 
-__all__ = ["mac_forward", "mac_workspace_size", "MacDesc", "mag_forward", "mag_workspace_size", "MagDesc", "scan", "scan_backward", "scan_backward_workspace_size", "retrieve", "scan_workspace_size", "scan_path", "retrieve_path", "param_count", "TitansError", "LIB_PATH",
+__all__ = ["scan_noalloc", "mac_forward", "mac_workspace_size", "MacDesc", "mag_forward", "mag_workspace_size", "MagDesc", "scan", "scan_backward", "scan_backward_workspace_size", "retrieve", "scan_workspace_size", "scan_path", "retrieve_path", "param_count", "TitansError", "LIB_PATH",
            "lib", "ScanDesc", "MlpDesc", "MAX_LAYERS"]
 
 # TITANS_MEM_LIB loads another build of the same sources instead (the tests' host-only
@@ -77,6 +77,8 @@ lib.titans_mem_scan_path.restype = ctypes.c_char_p
 lib.titans_mem_scan_path.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)]
 lib.titans_mem_retrieve_path.restype = ctypes.c_char_p
 lib.titans_mem_retrieve_path.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)]
+lib.titans_mem_scan_noalloc.restype = ctypes.c_int
+lib.titans_mem_scan_noalloc.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)] + [_vp] * 12
 lib.titans_mem_scan.restype = ctypes.c_int
 lib.titans_mem_scan.argtypes = ([ctypes.POINTER(ScanDesc), ctypes.POINTER(MlpDesc)] + [_vp] * 12
                                 + [ctypes.c_size_t, _vp])
@@ -279,6 +281,35 @@ def scan(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, *, y=None, theta_
     _check(lib.titans_mem_scan(ctypes.byref(desc), ctypes.byref(mlp), _ptr(q), _ptr(k), _ptr(v),
                                _ptr(alpha), _ptr(eta), _ptr(beta), _ptr(theta0), _ptr(s0), _ptr(y),
                                _ptr(theta_T), _ptr(s_T), _ptr(workspace), ws_bytes, _stream()))
+    return y, theta_T, s_T
+
+
+def scan_noalloc(q, k, v, alpha, eta, beta, theta0, s0, chunk, widths, *, y, theta_T, s_T,
+                 bias=None):
+    """titans_mem_scan_noalloc on the current stream: the scan with no workspace (the pair
+    path's shapes only; its scratch is the library's static device array).  The outputs
+    y [B,T,H,d], theta_T and s_T [B,H,P] are passed in (nothing is allocated here either);
+    arguments otherwise as for scan().  Returns (y, theta_T, s_T)."""
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.stride() != q.stride() or t.dtype != q.dtype:
+            raise ValueError(f"{name} must have q's shape, strides and dtype")
+    for name, g in (("eta", eta), ("beta", beta)):
+        if g.shape != alpha.shape or g.stride() != alpha.stride():
+            raise ValueError(f"{name} must have alpha's shape and strides")
+    for name, t in (("alpha", alpha), ("eta", eta), ("beta", beta), ("theta0", theta0), ("s0", s0),
+                    ("theta_T", theta_T), ("s_T", s_T)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if s0.stride() != theta0.stride() or s0.shape != theta0.shape:
+        raise ValueError("s0 must have theta0's shape and strides")
+    if s_T.stride() != theta_T.stride() or s_T.shape != theta_T.shape:
+        raise ValueError("s_T must have theta_T's shape and strides")
+    desc = make_desc(q, chunk, y, alpha, theta_T, theta0)
+    _set_bias(desc, bias)
+    mlp = mlp_desc(widths)
+    _check(lib.titans_mem_scan_noalloc(ctypes.byref(desc), ctypes.byref(mlp), _ptr(q), _ptr(k),
+                                       _ptr(v), _ptr(alpha), _ptr(eta), _ptr(beta), _ptr(theta0),
+                                       _ptr(s0), _ptr(y), _ptr(theta_T), _ptr(s_T), _stream()))
     return y, theta_T, s_T
 
 

@@ -327,12 +327,54 @@ size_t titans_mem_scan_surprise_workspace_size(const titans_scan_desc* desc,
     return workspace_of(a, true);
 }
 
+// The pair path run as a chain of calls over segments of the sequence, each within the
+// static scratch array (no caller workspace, nothing allocated): segment 1 reads theta0 /
+// s0, every later one continues in place from theta_T / s_T.  Segments are whole gradient
+// chunks, so the chain equals one call bitwise (calls chain exactly).
+static titans_status scan_pair_noalloc(titans::ScanArgs a, hipStream_t hs) {
+    const size_t cap = titans::scan_pair_scratch_capacity();
+    const size_t fixed = titans::scan_pair_scratch_exchange_bytes(a);
+    const size_t per_chunk = titans::scan_pair_scratch_chunk_bytes(a);
+    if (fixed + per_chunk > cap)
+        return fail(TITANS_ERR_UNSUPPORTED,
+                    "titans_mem_scan_noalloc: B*H=%lld with C=%d needs %zu bytes of scratch for one "
+                    "chunk, more than the %zu-byte static array",
+                    (long long)(a.B * a.H), a.C, fixed + per_chunk, cap);
+    void* ws = nullptr;
+    hipError_t e = titans::scan_pair_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "scratch address (hipGetSymbolAddress)");
+    const int64_t seg = (int64_t)((cap - fixed) / per_chunk) * a.C;  // tokens per segment
+    const size_t esz = a.io == TITANS_BF16 ? 2 : 4;
+    titans::ScanArgs s = a;
+    s.ws = ws;
+    for (int64_t t0 = 0; t0 < a.T; t0 += seg) {
+        s.T = a.T - t0 < seg ? a.T - t0 : seg;
+        const size_t qo = (size_t)(t0 * a.qs[1]) * esz, yo = (size_t)(t0 * a.ys[1]) * esz;
+        s.q = static_cast<const char*>(a.q) + qo;
+        s.k = static_cast<const char*>(a.k) + qo;
+        s.v = static_cast<const char*>(a.v) + qo;
+        s.y = static_cast<char*>(a.y) + yo;
+        s.alpha = a.alpha + t0 * a.gs[1];
+        s.eta = a.eta + t0 * a.gs[1];
+        s.beta = a.beta + t0 * a.gs[1];
+        if (t0 > 0) {  // continue from the previous segment's state, in place
+            s.theta0 = a.thetaT;
+            s.s0 = a.sT;
+            s.s0s[0] = a.ss[0];
+            s.s0s[1] = a.ss[1];
+        }
+        e = titans::launch_scan_pair(s, hs);
+        if (e != hipSuccess) return hip_fail(e, "scan launch");
+    }
+    return TITANS_OK;
+}
+
 static titans_status scan_impl(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
                                const void* q, const void* k, const void* v, const float* alpha,
                                const float* eta, const float* beta, const float* theta0,
                                const float* s0, void* y, float* theta_T, float* s_T,
                                float* surprise, bool want_surprise, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               size_t workspace_bytes, void* stream, bool noalloc = false) {
     g_last_error[0] = '\0';
     titans::ScanArgs a{};
     titans_status st = prepare_scan(desc, mlp, a);
@@ -410,8 +452,15 @@ static titans_status scan_impl(const titans_scan_desc* desc, const titans_mlp_de
         return fail(TITANS_ERR_INVALID_ARGUMENT, "s_T overlaps theta0/s0 without being exactly s0");
     if (theta_inplace && overlaps(sth, ss0) && !s_inplace)
         return fail(TITANS_ERR_INVALID_ARGUMENT, "theta_T overlaps s0");
-    // ---- workspace
-    size_t need = workspace_of(a, want_surprise);
+    // ---- workspace (the allocation-free call has none: the pair path only, see below)
+    if (noalloc && a.T > 0 && nseq > 0 && scan_path_of(a, false) != Path::Pair)
+        return fail(TITANS_ERR_UNSUPPORTED,
+                    "titans_mem_scan_noalloc serves the shapes titans_mem_scan runs on the pair path "
+                    "(\"fused_pair\": the 64-256-64 memory, bf16 I/O, C a multiple of 64, "
+                    "2*ceil(B*H/8)*8 workgroups within the device's compute units); this one takes "
+                    "\"%s\"",
+                    path_name(scan_path_of(a, false), a));
+    size_t need = noalloc ? 0 : workspace_of(a, want_surprise);
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
             return fail(TITANS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -438,6 +487,7 @@ static titans_status scan_impl(const titans_scan_desc* desc, const titans_mlp_de
     const char* hook = debug_env("TITANS_MEM_TEST_PAIR_TIMEOUT");
     a.debug = (hook && hook[0] == '1') ? 1 : 0;
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (noalloc && a.T > 0) return scan_pair_noalloc(a, hs);
     const Path path = a.T > 0 ? scan_path_of(a, want_surprise) : Path::Generic;
     hipError_t e = path == Path::Pair    ? titans::launch_scan_pair(a, hs)
                    : path == Path::Fused ? titans::launch_scan_mfma(a, hs)
@@ -455,6 +505,15 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
                               void* workspace, size_t workspace_bytes, void* stream) {
     return scan_impl(desc, mlp, q, k, v, alpha, eta, beta, theta0, s0, y, theta_T, s_T, nullptr,
                      false, workspace, workspace_bytes, stream);
+}
+
+titans_status titans_mem_scan_noalloc(const titans_scan_desc* desc, const titans_mlp_desc* mlp,
+                                      const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* eta, const float* beta,
+                                      const float* theta0, const float* s0, void* y,
+                                      float* theta_T, float* s_T, void* stream) {
+    return scan_impl(desc, mlp, q, k, v, alpha, eta, beta, theta0, s0, y, theta_T, s_T, nullptr,
+                     false, nullptr, 0, stream, true);
 }
 
 titans_status titans_mem_scan_surprise(const titans_scan_desc* desc, const titans_mlp_desc* mlp,

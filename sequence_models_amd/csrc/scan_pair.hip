@@ -43,6 +43,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "mfma_util.h"
@@ -1034,7 +1035,47 @@ __global__ void __launch_bounds__(256) pair_surprise_kernel(ScanArgs A, const fl
     }
 }
 
+// Scratch of the allocation-free entry point (titans_mem_scan_noalloc): the pair path's
+// exchange areas and chunk coefficient records in one static device array, which every
+// GPU the library runs on holds from the library's first use on it until the process
+// ends.  Host code reaches it only through the address hipGetSymbolAddress returns for the
+// current device (the array's name is a host-side stand-in, not a device address).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
 }  // namespace
+
+size_t scan_pair_scratch_capacity() { return kScratchBytes; }
+
+hipError_t scan_pair_scratch(void** ptr) {
+    *ptr = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        // once per device, with that device current: this GPU's copy of the array
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = p;
+    }
+    *ptr = g_scratch[dev];
+    return hipSuccess;
+}
+
+size_t scan_pair_scratch_exchange_bytes(const ScanArgs& a) {
+    return (size_t)padded_pairs(a) * (size_t)kPairBytes;
+}
+
+size_t scan_pair_scratch_chunk_bytes(const ScanArgs& a) {
+    return (size_t)(a.B * a.H) * (size_t)(a.C / kC) * (size_t)kCoefBytes;
+}
 
 size_t scan_pair_surprise_bytes(const ScanArgs& a) {
     return (size_t)(a.B * a.H) * (size_t)a.T * (2 * kSurpShares + 1) * sizeof(float);

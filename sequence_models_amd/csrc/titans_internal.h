@@ -92,6 +92,15 @@ int64_t scan_pair_workgroups(const ScanArgs& a);
 // Extra workspace of a pair-path call that also writes the per-token surprise norms.
 size_t scan_pair_surprise_bytes(const ScanArgs& a);
 hipError_t launch_scan_pair(const ScanArgs& a, hipStream_t stream);
+// The pair path without a caller workspace: a static device array of
+// scan_pair_scratch_capacity() bytes per GPU (scan_pair_scratch: its address on the current
+// device, looked up once per device).  A call needs scan_pair_scratch_exchange_bytes for the
+// exchange areas plus scan_pair_scratch_chunk_bytes per gradient chunk of C tokens it
+// covers (the coefficient records).
+size_t scan_pair_scratch_capacity();
+hipError_t scan_pair_scratch(void** ptr);
+size_t scan_pair_scratch_exchange_bytes(const ScanArgs& a);
+size_t scan_pair_scratch_chunk_bytes(const ScanArgs& a);
 
 // Generic retrieve: any supported shape, products as in the generic scan.
 hipError_t launch_retrieve_generic(const ScanArgs& a, hipStream_t stream);
