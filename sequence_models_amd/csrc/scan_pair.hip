@@ -144,6 +144,12 @@ struct __attribute__((aligned(16))) SmemFour : Smem {
 };
 static_assert(sizeof(SmemFour) <= 160 * 1024, "LDS budget");
 
+// bf16 operand fragment from a k-contiguous fp32 LDS row (as frag(), rounding each element).
+__device__ __forceinline__ bf16x8 frag32(const float* p, int off) {
+    return cat(bf4(*reinterpret_cast<const f32x4*>(p + off)),
+               bf4(*reinterpret_cast<const f32x4*>(p + off + 16)));
+}
+
 __device__ __forceinline__ float* yslot(Smem& sm, int w) {
     switch (w) {
         case 0: return sm.r[0];
@@ -734,6 +740,11 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             // E2 = loss'(O - V) (2 (O - V) for the squared error), O = O_side0 + O_side1,
             // in its four layouts
             const int xb = opq(rc * kLd + cl0), xt = opq(cl0 * kLd + rc);
+            // gradient chunks longer than 64 tokens: E2's low part E2 - bf16(E2) (exact in
+            // fp32) for the product G below, fp32 [c][dd] in O partial slot 0, which is dead
+            // from the O sum to the Y partials; each thread writes exactly the elements it
+            // read in the O sum, so the write needs no barrier before it
+            float* const elw = sm.r[0] + xb;
             const float ccr = -sm.cc[rc], wr = sm.w[rc];
             float esq = 0.f;  // kSurp: this thread's 16 columns of ||E2_rc||^2
 #pragma unroll
@@ -750,6 +761,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 if constexpr (kSurp) esq += (e2[0] * e2[0] + e2[1] * e2[1]) + (e2[2] * e2[2] + e2[3] * e2[3]);
                 const bf16x4 el = bf4(e2), ec = bf4(e2 * ccr), ew = bf4(e2 * wr);
                 *reinterpret_cast<bf16x4*>(sm.e2l + xb + 4 * q4) = el;
+                if constexpr (kFrozen) *reinterpret_cast<f32x4*>(elw + 4 * q4) = e2 - f4(el);
 #pragma unroll
                 for (int ee = 0; ee < 4; ++ee) {
                     const int o2 = xt + (4 * q4 + ee) * kLd;
@@ -791,16 +803,38 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                         tile = bf4(W2T[ht][dt]);
                     W2n[dt][ht] = bf4(mfma(cat(tile, bf16x4{}), eye, zero4()));
                 }
+            // With gradient chunks longer than 64 tokens (the long-context configurations)
+            // E2 enters as bf16 high + low parts, two products each: of the kernel's bf16
+            // rounding points this is the one that moves long runs furthest from the exact
+            // recurrence (emulated point by point over 256K tokens of a slowly forgetting
+            // memory, C = 256: alone it moves single reads by up to 20 %, all the others
+            // together by 3 %; at 2M tokens it takes y from 4.9e-3 to 3.1e-2 of the exact
+            // result).  With C = 64 one product is kept (it costs 5 % there, and on the
+            // 16K-token workload the split changes the error by nothing measurable).
             const int rb = opq(j * kLd + 4 * g);
             const __bf16* er = sm.e2l + rb;
+            const float* erl = sm.r[0] + rb;
 #pragma unroll
-            for (int ht = 0; ht < kHt; ++ht) {
-                const bf16x8 b0 = cat(W2n[0][ht], W2n[1][ht]);
-                const bf16x8 b1 = cat(W2n[2][ht], W2n[3][ht]);
+            for (int ct = 0; ct < 4; ++ct) {
+                const bf16x8 a0 = frag(er, fo(ct, 0)), a1 = frag(er, fo(ct, 1));
+                bf16x8 l0{}, l1{};
+                if constexpr (kFrozen) {
+                    l0 = frag32(erl, fo(ct, 0));
+                    l1 = frag32(erl, fo(ct, 1));
+                }
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) {
-                    f32x4 gg = mfma(frag(er, fo(ct, 0)), b0, zero4());
-                    gg = mfma(frag(er, fo(ct, 1)), b1, gg);
+                for (int ht = 0; ht < kHt; ++ht) {
+                    const bf16x8 b0 = cat(W2n[0][ht], W2n[1][ht]);
+                    const bf16x8 b1 = cat(W2n[2][ht], W2n[3][ht]);
+                    f32x4 gg = mfma(a0, b0, zero4());
+                    if constexpr (kFrozen) {
+                        f32x4 gl = mfma(l0, b0, zero4());
+                        gg = mfma(a1, b1, gg);
+                        gl = mfma(l1, b1, gl);
+                        gg += gl;
+                    } else {
+                        gg = mfma(a1, b1, gg);
+                    }
                     const f32x4 d1 = gg * f4(Sp[ct][ht]);
                     D1[ct][ht] = bf4(d1);
                     if constexpr (kSurp)

@@ -15,9 +15,11 @@ to ~0):
     |out - ref| <= 3e-2 RMS_row(ref); per row RMS(out - ref) <= 1e-2 RMS_row(ref).  (A CPU
     model of exactly these roundings reaches 1.5e-2 and 4.4e-3 on the cases below, as the
     kernels do.)
-  * theta_T, s_T: the memory scan's own bf16 bar (relative Frobenius error <= 1e-1): its
-    kernels round products' operands to bf16, and here q, k, v are also rounded to bf16
-    before the scan; in fp64 alone that rounding moves theta_T after 16K tokens by 2-4%.
+  * theta_T, s_T: the memory scan's own bf16 bars (relative Frobenius error): 1e-1 on the
+    short cases; at full size 5x the method's own sensitivity, measured by running the fp64
+    scan again with k and v perturbed by one bf16 rounding (at least 2e-2), as the scan's
+    full-length tests do -- the scan kernels round about seven operands of that size per
+    chunk, which add in quadrature to about 3x that sensitivity.
 """
 import numpy as np
 import pytest
@@ -75,10 +77,13 @@ def _check_out(got, ref, bar_max=None, bar_rms=None):
     assert erms <= (BAR_OUT_RMS if bar_rms is None else bar_rms)
 
 
-def _check_state(got, ref, name):
+def _check_state(got, ref, name, bar=BAR_STATE):
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
-    print(f"{name}: relative error {rel:.3e}", flush=True)
-    assert rel <= BAR_STATE
+    print(f"{name}: relative error {rel:.3e} (bar {bar:.2e})", flush=True)
+    assert rel <= bar
+
+
+SENSITIVITY_FACTOR = 5.0
 
 
 CASES = [
@@ -196,7 +201,23 @@ def test_mag_full_size_prefix_and_final_state(headline):
         q, k, v, al, et, be = omag.front_end(x, Wq[:, cols], Wk[:, cols], Wv[:, cols],
                                              Wg[:, gcols], bg[gcols], 1, wl.eta_scale,
                                              store="bf16")
-        _, th_ref, s_ref = oracle.scan(q, k, v, al, et, be, mi.theta0[h:h + 1].astype(np.float64),
-                                       np.zeros((1, wl.params)), wl.chunk, wl.widths)
-        _check_state(th[b, h], th_ref.reshape(-1), f"theta_T[{b},{h}]")
-        _check_state(s[b, h], s_ref.reshape(-1), f"s_T[{b},{h}]")
+        # and once more on k, v perturbed by one bf16 rounding: the method's own sensitivity
+        rng = np.random.default_rng(4321 + h)
+        pk, pv = (a * (1.0 + 2.0 ** -9 * rng.uniform(-1.0, 1.0, a.shape)) for a in (k, v))
+
+        def two(a, b_):
+            return np.concatenate([a, b_], axis=2)
+
+        th0 = mi.theta0[h:h + 1].astype(np.float64)
+        _, th_ref, s_ref = oracle.scan(two(q, q), two(k, pk), two(v, pv), two(al, al),
+                                       two(et, et), two(be, be), np.concatenate([th0, th0]),
+                                       np.zeros((2, wl.params)), wl.chunk, wl.widths)
+
+        def rel(a, r):
+            return np.linalg.norm(a - r) / np.linalg.norm(r)
+
+        kappa = max(rel(th_ref[0, 1], th_ref[0, 0]), rel(s_ref[0, 1], s_ref[0, 0]))
+        bar = max(2e-2, SENSITIVITY_FACTOR * kappa)
+        print(f"({b},{h}) oracle sensitivity to one bf16 rounding of k, v: {kappa:.2e}", flush=True)
+        _check_state(th[b, h], th_ref[0, 0], f"theta_T[{b},{h}]", bar)
+        _check_state(s[b, h], s_ref[0, 0], f"s_T[{b},{h}]", bar)

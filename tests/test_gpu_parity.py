@@ -53,12 +53,15 @@ def run_gpu(dev, wl, **kw):
                    dev["theta0"], dev["s0"], wl.chunk, wl.widths, **kw)
 
 
-def oracle_seq(inp, pairs, T=None, theta0=None, s0=None, bias=None, t0=0, perturb=False):
+def oracle_seq(inp, pairs, T=None, theta0=None, s0=None, bias=None, t0=0, perturb=False,
+               ptheta0=None, ps0=None):
     """Oracle on the (b, h) pairs over tokens t0 .. t0+T-1 (default: the whole sequence),
     all pairs in one OpenMP-parallel call.  theta0 / s0: None (the head's initial state),
     or one start state per pair [n, P] (a window that starts from a GPU state).  With
     perturb=True the oracle also runs on k and v perturbed by one bf16 rounding (each
-    element times 1 + 2^-9 u, u ~ U(-1, 1), seeded): the method's own sensitivity.
+    element times 1 + 2^-9 u, u ~ U(-1, 1), seeded by t0): the method's own sensitivity;
+    that copy starts from ptheta0 / ps0 when given (a perturbed run continued over
+    consecutive windows), else from the same state.
     Returns a list of (y [T,d], theta_T [P], s_T [P]) (and the perturbed list)."""
     wl = inp.workload
     T = wl.seq_len - t0 if T is None else T
@@ -83,7 +86,9 @@ def oracle_seq(inp, pairs, T=None, theta0=None, s0=None, bias=None, t0=0, pertur
         qkv = [np.concatenate([qkv[0], qkv[0]], axis=2), np.concatenate([qkv[1], pk], axis=2),
                np.concatenate([qkv[2], pv], axis=2)]
         gates = [np.concatenate([g, g], axis=2) for g in gates]
-        th0, sg0 = np.concatenate([th0, th0]), np.concatenate([sg0, sg0])
+        pth0 = th0 if ptheta0 is None else np.asarray(ptheta0)
+        psg0 = sg0 if ps0 is None else np.asarray(ps0)
+        th0, sg0 = np.concatenate([th0, pth0]), np.concatenate([sg0, psg0])
     y, th, s = oracle.scan(*qkv, *gates, th0, sg0, wl.chunk, wl.widths, bias=bias)
     out = [(y[0, :, i], th[0, i], s[0, i]) for i in range(n)]
     if not perturb:
@@ -109,13 +114,19 @@ def state_bar(refs, prefs, floor):
     return bar
 
 
-def check_pairs(wl, y, thT, sT, pairs, refs, prefs=None, T=None, check_state=True, t0=0):
+def check_pairs(wl, y, thT, sT, pairs, refs, prefs=None, T=None, check_state=True, t0=0,
+                drift=False):
     """Each (b, h) sequence against its oracle reference (y [n, d] for tokens t0 .. t0+n-1,
     theta_T, s_T): y per sequence (Frobenius, Y_BAR) and per token; the state unless it has
     decayed out of float32's range.  With `prefs` (the oracle on k, v perturbed by one bf16
     rounding, oracle_seq(perturb=True)) the per-token and state bars are SENSITIVITY_FACTOR
     times the recurrence's own change under that perturbation (at least Y_TOKEN_BAR / 2e-2);
-    without, Y_TOKEN_BAR and TH_BAR.  Returns the worst (y, per-token y, state) errors."""
+    without, Y_TOKEN_BAR and TH_BAR.  drift=True (a comparison more than 2^18 tokens from
+    the common start): the errors are logged beside the perturbed run's, not asserted --
+    there they measure how far two roundings of the same chaotic recurrence have drifted
+    apart (the perturbed exact recurrence drifts too), not whether a token was computed
+    right, which the windows started from the GPU's own state assert.  Returns the worst
+    (y, per-token y, state) errors."""
     tg = to_f64(thT)
     sg = to_f64(sT)
     if wl.io == "f32":  # fp32 I/O keeps the fixed 1e-4 bars
@@ -129,10 +140,14 @@ def check_pairs(wl, y, thT, sT, pairs, refs, prefs=None, T=None, check_state=Tru
         emax, e99, iw, left = token_errors(yb, yr, wl.chunk)
         tbar = Y_TOKEN_BAR[wl.io]
         if prefs is not None:
-            kmax = token_errors(prefs[i][0], yr, wl.chunk)[0]
+            kmax, k99 = token_errors(prefs[i][0], yr, wl.chunk)[:2]
             tbar = max(tbar, SENSITIVITY_FACTOR * kmax)
+            ky = y_rel_err(prefs[i][0][None, :, None], yr[None, :, None])
         msg = (f"{wl.name} (b={b},h={h}) tokens {t0}..{t0 + Tn - 1}: y rel err {ey:.2e}, "
-               f"per token max {emax:.2e} (token {t0 + iw}) p99 {e99:.2e} (bar {tbar:.1e})"
+               f"per token max {emax:.2e} (token {t0 + iw}) p99 {e99:.2e} "
+               + (f"(drift, logged: the perturbed run's y rel err {ky:.2e}, per token max "
+                  f"{kmax:.2e} p99 {k99:.2e})" if drift and prefs is not None
+                  else "(drift, logged)" if drift else f"(bar {tbar:.1e})")
                + (f", {left} decayed tokens left out" if left else ""))
         worst[0], worst[1] = max(worst[0], ey), max(worst[1], emax)
         decayed = check_state and np.linalg.norm(tr) < DECAYED_STATE
@@ -140,13 +155,15 @@ def check_pairs(wl, y, thT, sT, pairs, refs, prefs=None, T=None, check_state=Tru
             et = state_rel_err(tg[b:b + 1, h:h + 1], tr[None, None])
             es = state_rel_err(sg[b:b + 1, h:h + 1], sr[None, None])
             worst[2] = max(worst[2], et, es)
-            msg += f", theta_T {et:.2e}, s_T {es:.2e} (bar {bar:.1e})"
+            msg += f", theta_T {et:.2e}, s_T {es:.2e} " + (
+                f"(drift, logged; 5x the perturbed run's change: {bar:.1e})" if drift
+                else f"(bar {bar:.1e})")
         elif decayed:
             msg += f", state decayed to |theta_T| = {np.linalg.norm(tr):.1e}: not compared"
         log(msg)
-        assert ey <= Y_BAR[wl.io], msg
-        assert emax <= tbar, msg
-        if check_state and not decayed:
+        assert drift or ey <= Y_BAR[wl.io], msg
+        assert drift or emax <= tbar, msg
+        if check_state and not decayed and not drift:
             assert et <= bar, msg
             assert es <= bar, msg
     return worst
@@ -260,7 +277,7 @@ def test_long_context_prefix_64k(sustained):
     check_pairs(inp.workload, y, thT, sT, pairs, refs, prefs=prefs)
 
 
-@pytest.mark.timeout(900)
+@pytest.mark.timeout(1200)
 def test_long_context_full_length_windows():
     """The 2M-token workload (sustained gates, every head kept O(1) to the end) in the
     bench's launch: one call over all 2,097,152 tokens.  The same sequence is then run again
@@ -269,7 +286,15 @@ def test_long_context_full_length_windows():
     states at the cuts.  Windows of 4096 tokens -- at the start, in the middle, past
     2^31 bytes into q, k, v and y (token 2^20 onwards), and the last 4096 tokens -- are then
     checked against the oracle started from the GPU's state at the window start: y of
-    every token of the window and the state at its end."""
+    every token of the window and the state at its end.  Last, the whole sequence against
+    one oracle run from the initial state over all 2,097,152 tokens (continued segment by
+    segment, which is exact at chunk multiples): the first 2^18 tokens -- y, per token and
+    the state at their end -- at the usual bars; after that the errors of every segment
+    and of the final state are logged beside the perturbed run's.  Over millions of tokens
+    two roundings of this recurrence drift apart: the exact recurrence on k, v rounded
+    once more (the perturbed run) moves theta_T by up to 7 % and single reads by up to
+    10 %, and the kernel's own rounding points (about seven per chunk) by a few times
+    that, which no fixed bar separates from an error."""
     wl = _workload("long_h16_d64_b1_t2m", True)
     T, N = wl.seq_len, 4096
     log(f"case {wl.name} full length, windows of {N}")
@@ -278,7 +303,8 @@ def test_long_context_full_length_windows():
     y, thT, sT = run_gpu(dev, wl)
     torch.cuda.synchronize()
     starts = [0, 1 << 19, (1 << 20) + (1 << 19), T - N]
-    cuts = sorted(set([0, T] + starts + [s_ + N for s_ in starts]))
+    span = 1 << 18  # the whole-sequence comparison's segments
+    cuts = sorted(set([0, T, span] + starts + [s_ + N for s_ in starts]))
     B, H = wl.batch, wl.heads
     th = dev["theta0"].expand(B, -1, -1).contiguous()
     s = dev["s0"].expand(B, -1, -1).contiguous()
@@ -303,6 +329,23 @@ def test_long_context_full_length_windows():
         the = torch.from_numpy(states[t0 + N][0]).float()
         she = torch.from_numpy(states[t0 + N][1]).float()
         check_pairs(wl, y, the, she, pairs, refs, prefs=prefs, t0=t0)
+    # the whole sequence: the oracle (and its perturbed copy) from theta0 over all tokens
+    assert span % wl.chunk == 0 and T % span == 0
+    th1 = torch.from_numpy(states[span][0]).float()
+    s1 = torch.from_numpy(states[span][1]).float()
+    del states, th, s
+    ref_st = pref_st = (None, None)
+    for t0 in range(0, T, span):
+        refs, prefs = oracle_seq(inp, pairs, T=span, theta0=ref_st[0], s0=ref_st[1], t0=t0,
+                                 perturb=True, ptheta0=pref_st[0], ps0=pref_st[1])
+        log(f"  oracle from token 0 through token {t0 + span - 1}")
+        if t0 == 0:
+            check_pairs(wl, y, th1, s1, pairs, refs, prefs=prefs, t0=t0)
+        else:
+            check_pairs(wl, y, thT, sT, pairs, refs, prefs=prefs, t0=t0,
+                        check_state=t0 + span == T, drift=True)
+        ref_st = (np.stack([r[1] for r in refs]), np.stack([r[2] for r in refs]))
+        pref_st = (np.stack([r[1] for r in prefs]), np.stack([r[2] for r in prefs]))
 
 
 # -------------------------------------------------------------- edge cases
