@@ -513,11 +513,11 @@ def main():
     flops = alg_flops_per_token_head(wl.widths, wl.chunk) * B * T * H
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     path = tm.scan_path(t["q"], wl.chunk, wl.widths)
-    if path in ("fused_pair", "fused_mfma"):  # bf16 MFMA contractions with fp32 accumulation
-        # the pair path is three launches (flag clear, chunk-coefficient pass, scan); the
-        # events bracket the whole call, so kernel_ms is their sum
-        kernel = ("clear_pair_flags + pair_coef_kernel + scan_pair_kernel" if path == "fused_pair"
-                  else "scan_mfma_kernel")
+    if path in ("fused_pair", "fused_quad", "fused_mfma"):  # bf16 MFMA, fp32 accumulation
+        # the pair path (pairs or quads) is three launches (flag clear, chunk-coefficient
+        # pass, scan); the events bracket the whole call, so kernel_ms is their sum
+        kernel = ("scan_mfma_kernel" if path == "fused_mfma"
+                  else "clear_pair_flags + pair_coef_kernel + scan_pair_kernel")
         bound, peak, dtype = "mfma", PEAKS["mfma_bf16"], "bf16"
     elif path.endswith("_mfma"):  # bf16 MFMA products, fp32 accumulation
         kernel = KERNELS[path.rsplit("_", 1)[0]]
@@ -529,12 +529,13 @@ def main():
         kernel = KERNELS[path.rsplit("_", 1)[0]]
         bound, peak, dtype = "mfma", PEAKS["mfma_f32"], "f32"
     parallelism = {
-        "fused": "one GPU; two workgroups (one XCD) per (batch row, head) memory",
+        "fused_pair": "one GPU; two workgroups (one XCD) per (batch row, head) memory",
+        "fused_quad": "one GPU; four workgroups (one XCD) per (batch row, head) memory",
         "phased": "one GPU; every chunk product split into 64x64 tiles of all memories, "
                   "4L-2 launches per chunk",
         "linear": "one GPU; each sequence split into groups of chunks whose affine state "
                   "maps compose in parallel",
-    }.get(path.split("_")[0] if path != "fused_mfma" else "single",
+    }.get(path if path.startswith("fused") else path.split("_")[0],
           "one GPU; one workgroup per (batch row, head) memory")
     result = {
         "metric": METRIC,

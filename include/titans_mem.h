@@ -118,8 +118,9 @@ int64_t titans_mem_param_count(const titans_mlp_desc* mlp);
 
 /* Which kernel titans_mem_scan runs for this problem on the current device (a 256-CU
  * MI355X is assumed when no device is visible).  For the 64 -> 256 -> 64 memory with bf16
- * I/O: "fused_pair" (bf16 MFMA, state resident on chip, two workgroups per memory; C a
- * multiple of 64; chosen while 2 * ceil(B*H / 8) * 8 workgroups fit one per compute unit),
+ * I/O: "fused_quad" (bf16 MFMA, state resident on chip, four workgroups per memory; C a
+ * multiple of 64; chosen while 4 * ceil(B*H / 8) * 8 workgroups fit one per compute unit),
+ * "fused_pair" (the same with two workgroups per memory, while 2 * ceil(B*H / 8) * 8 fit),
  * else "fused_mfma" (one workgroup per memory; C = 64).  Every other supported shape runs the
  * generic family: "phased_mfma" / "phased_fp32" when a layer has 128 or more units (each
  * chunk step's products spread as 64 x 64 tiles over the whole GPU, one launch per step),
@@ -168,7 +169,8 @@ titans_status titans_mem_scan(const titans_scan_desc* desc, const titans_mlp_des
  * titans_mem_scan for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments
  * without the workspace.  Serves the shapes titans_mem_scan runs on the pair path
- * ("fused_pair" in titans_mem_scan_path); any other shape is TITANS_ERR_UNSUPPORTED.  Its
+ * ("fused_pair" or "fused_quad" in titans_mem_scan_path); any other shape is
+ * TITANS_ERR_UNSUPPORTED.  Its
  * scratch (exchange areas and chunk coefficient records) is a 64 MiB static device array
  * that every GPU the library runs on holds until the process ends; the call enqueues the
  * pair path over segments of the sequence that fit it, continuing in place through
@@ -194,8 +196,9 @@ titans_status titans_mem_scan_noalloc(const titans_scan_desc* desc, const titans
  *   surprise   device fp32 with alpha's layout (desc->gate_stride), 4-byte aligned; must
  *              not overlap any other buffer (TITANS_ERR_INVALID_ARGUMENT)
  *   workspace  >= titans_mem_scan_surprise_workspace_size bytes
- * Shapes that titans_mem_scan runs on the pair path ("fused_pair") run there, with the
- * norms' partial sums in the workspace and one more small kernel; every other shape runs
+ * Shapes that titans_mem_scan runs on the pair path ("fused_pair" or "fused_quad") run
+ * there with two workgroups per memory ("fused_pair"), with the norms' partial sums in the
+ * workspace and one more small kernel; every other shape runs
  * the generic family ("phased_*" or "generic_*" by the width rule of
  * titans_mem_scan_path; the single-workgroup fused and the linear kernels do not produce
  * the norms).  Every other argument and result is as for titans_mem_scan.

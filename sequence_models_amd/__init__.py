@@ -200,7 +200,7 @@ def scan_workspace_size(q, chunk, widths) -> int:
 
 
 def scan_path(q, chunk, widths) -> str:
-    """Name of the kernel that serves this shape: "fused_pair", "fused_mfma", "phased_mfma" /
+    """Name of the kernel that serves this shape: "fused_quad", "fused_pair", "fused_mfma", "phased_mfma" /
     "phased_fp32" (layers of 128+ units; bf16 / fp32 I/O) or "generic_mfma" / "generic_fp32"."""
     d = make_desc(q, chunk, q, None, None, None)
     r = lib.titans_mem_scan_path(ctypes.byref(d), ctypes.byref(mlp_desc(widths)))

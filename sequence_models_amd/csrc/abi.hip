@@ -271,9 +271,21 @@ static Path choose_path(const titans::ScanArgs& a) {
     return titans::scan_mfma_supported(a) ? Path::Fused : generic_path(a);
 }
 
-static const char* path_name(Path p, const titans::ScanArgs& a) {
+// Workgroups per memory on the pair path: quads (four workgroups per memory, 16 hidden
+// units per wave) while 4 * ceil(B*H/8) * 8 of them fit the device at one per compute unit
+// and no per-token surprise is asked for (its shares are laid out for pairs), else pairs.
+// TITANS_MEM_PAIR_SIDES=2 keeps pairs (a testing switch, with TITANS_MEM_DEBUG=1).
+static int pair_sides(const titans::ScanArgs& a, bool surprise) {
+    const char* env = debug_env("TITANS_MEM_PAIR_SIDES");
+    if (surprise || (env && env[0] == '2')) return 2;
+    titans::ScanArgs b = a;
+    b.sides = 4;
+    return titans::scan_pair_workgroups(b) <= device_cus() ? 4 : 2;
+}
+
+static const char* path_name(Path p, const titans::ScanArgs& a, bool surprise = false) {
     switch (p) {
-        case Path::Pair: return "fused_pair";
+        case Path::Pair: return pair_sides(a, surprise) == 4 ? "fused_quad" : "fused_pair";
         case Path::Fused: return "fused_mfma";
         case Path::Phased: return a.io == TITANS_BF16 ? "phased_mfma" : "phased_fp32";
         case Path::Linear: return a.io == TITANS_BF16 ? "linear_mfma" : "linear_fp32";
@@ -298,9 +310,12 @@ static Path scan_path_of(const titans::ScanArgs& a, bool surprise) {
 static size_t workspace_of(const titans::ScanArgs& a, bool surprise) {
     if (a.B * a.H == 0 || a.T == 0) return 0;
     switch (scan_path_of(a, surprise)) {
-        case Path::Pair:
-            return titans::scan_pair_workspace_bytes(a) +
-                   (surprise ? titans::scan_pair_surprise_bytes(a) : 0);
+        case Path::Pair: {
+            titans::ScanArgs b = a;
+            b.sides = pair_sides(a, surprise);
+            return titans::scan_pair_workspace_bytes(b) +
+                   (surprise ? titans::scan_pair_surprise_bytes(b) : 0);
+        }
         case Path::Fused: return 0;
         case Path::Phased: return titans::scan_phased_workspace_bytes(a);
         case Path::Linear: return titans::scan_linear_workspace_bytes(a);
@@ -317,7 +332,7 @@ size_t titans_mem_scan_workspace_size(const titans_scan_desc* desc, const titans
 const char* titans_mem_scan_surprise_path(const titans_scan_desc* desc, const titans_mlp_desc* mlp) {
     titans::ScanArgs a{};
     if (prepare_scan(desc, mlp, a) != TITANS_OK) return nullptr;
-    return path_name(scan_path_of(a, true), a);
+    return path_name(scan_path_of(a, true), a, true);
 }
 
 size_t titans_mem_scan_surprise_workspace_size(const titans_scan_desc* desc,
@@ -456,10 +471,11 @@ static titans_status scan_impl(const titans_scan_desc* desc, const titans_mlp_de
     if (noalloc && a.T > 0 && nseq > 0 && scan_path_of(a, false) != Path::Pair)
         return fail(TITANS_ERR_UNSUPPORTED,
                     "titans_mem_scan_noalloc serves the shapes titans_mem_scan runs on the pair path "
-                    "(\"fused_pair\": the 64-256-64 memory, bf16 I/O, C a multiple of 64, "
-                    "2*ceil(B*H/8)*8 workgroups within the device's compute units); this one takes "
-                    "\"%s\"",
+                    "(\"fused_pair\" / \"fused_quad\": the 64-256-64 memory, bf16 I/O, C a multiple "
+                    "of 64, 2*ceil(B*H/8)*8 workgroups within the device's compute units); this one "
+                    "takes \"%s\"",
                     path_name(scan_path_of(a, false), a));
+    a.sides = pair_sides(a, want_surprise);
     size_t need = noalloc ? 0 : workspace_of(a, want_surprise);
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
@@ -481,9 +497,10 @@ static titans_status scan_impl(const titans_scan_desc* desc, const titans_mlp_de
     a.y = y; a.thetaT = theta_T; a.sT = s_T;
     a.surprise = want_surprise ? surprise : nullptr;
     a.ws = workspace;
-    // Test hook for the pair path's failure handling: side 1 of every pair never posts its
-    // exchange flags and every wait gives up after a few polls, so side 0 times out (its
-    // slice of theta_T / s_T comes out NaN) while every kernel still ends normally.
+    // Test hook for the pair path's failure handling: side 1 of every memory never posts
+    // its exchange flags and every wait gives up after a few polls, so the other sides time
+    // out and every output of the memory comes out NaN while every kernel still ends
+    // normally.
     const char* hook = debug_env("TITANS_MEM_TEST_PAIR_TIMEOUT");
     a.debug = (hook && hook[0] == '1') ? 1 : 0;
     hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -59,20 +59,43 @@ constexpr int kHid = 256;                // hidden width of the memory MLP
 constexpr int kC = 64;                   // chunk length
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kHidSide = kHid / 2;       // hidden units per workgroup
-constexpr int kHidW = kHidSide / kWaves; // hidden units per wave (32)
-constexpr int kHt = kHidW / 16;          // 16-wide hidden tiles per wave (2)
 constexpr int kMat = kC * kLd;           // elements of one padded 64 x 64 matrix
 constexpr int kMaxSpin = 1 << 21;        // flag polls before a wait gives up (about 2 s)
 
-// Exchange area of one pair (byte offsets): flags [side][wave] 128 bytes apart, then
-// O words [slot 2][side 2][i 8][thread], then Y words [slot 2][side 2][i 4][thread];
-// a word is two fp32 values.
-constexpr int64_t kFlagBytes = 2 * kWaves * 128;
-constexpr int64_t kOWords = 2 * 2 * 8 * kThreads;
-constexpr int64_t kYWords = 2 * 2 * 4 * kThreads;
-constexpr int64_t kPairBytes = kFlagBytes + 8 * (kOWords + kYWords);
-static_assert(kPairBytes % 256 == 0, "pair areas stay 256-byte aligned");
+// A memory split over kS workgroups ("sides": 2 for pairs, 4 for quads).  Side s owns hidden
+// units kHidSide s .. kHidSide (s + 1) - 1, a wave kHidW of them, and y rows kYRows s ..
+// kYRows (s + 1) - 1 of every chunk.
+//
+// Exchange area of one memory (byte offsets): flags [side][wave] 128 bytes apart, then
+// O words [slot 2][side][i 8][thread], then Y words [slot 2][source side][destination
+// d][i][thread], destination side (source + 1 + d) mod kS; a word is two fp32 values.
+template <int kS>
+struct Split {
+    static_assert(kS == 2 || kS == 4, "pairs or quads");
+    static constexpr int kHidSide = kHid / kS;        // hidden units per workgroup
+    static constexpr int kHidW = kHidSide / kWaves;   // hidden units per wave (32, 16)
+    static constexpr int kHt = kHidW / 16;            // 16-wide hidden tiles per wave (2, 1)
+    static constexpr int kLd2 = kHidSide + 8;         // padded row of the frozen W2 slice
+    static constexpr int kYRows = kC / kS;            // y rows a side owns per chunk
+    static constexpr int kYE = kYRows * kD / kThreads;  // y elements per thread and side
+    static constexpr int kYW = kYE / 2;               // ... in exchange words
+    static constexpr int64_t kFlagBytes = kS * kWaves * 128;
+    static constexpr int64_t kOWords = 2 * kS * 8 * kThreads;
+    static constexpr int64_t kYWords = 2 * kS * (kS - 1) * kYW * kThreads;
+    static constexpr int64_t kBytes = kFlagBytes + 8 * (kOWords + kYWords);
+    static_assert(kBytes % 256 == 0, "exchange areas stay 256-byte aligned");
+};
+
+// Sum of one value per side, own = this side's, p[d] = side (this side ^ (d + 1))'s:
+// (own + p0) for pairs, (own + p0) + (p1 + p2) for quads.  fp32 addition is commutative, so
+// every side gets bitwise (v0 + v1) resp. (v0 + v1) + (v2 + v3), side order.
+template <int kS>
+__device__ __forceinline__ float sum_sides(float own, const float (&p)[kS - 1]) {
+    if constexpr (kS == 2)
+        return own + p[0];
+    else
+        return (own + p[0]) + (p[1] + p[2]);
+}
 
 __device__ __forceinline__ uint64_t pack2(float a, float b) {
     return (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
@@ -130,12 +153,12 @@ static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
 // every sub-chunk are taken at the weights of the chunk start, kept here in bf16 (the
 // precision every product reads them in) and refreshed at each chunk start; the reads and
 // the carry use the running weights in registers as for C = 64.
-constexpr int kLd2 = kHidSide + 8;  // padded row of the frozen W2 slice
+template <int kS>
 struct __attribute__((aligned(16))) SmemFrozen : Smem {
-    __bf16 w1c[kHidSide * kLd];  // W1 at the chunk start [h][d], this side's 128 rows
-    __bf16 w2c[kD * kLd2];       // W2 at the chunk start [dd][h], this side's 128 columns
+    __bf16 w1c[Split<kS>::kHidSide * kLd];  // W1 at the chunk start [h][d], this side's rows
+    __bf16 w2c[kD * Split<kS>::kLd2];       // W2 at the chunk start [dd][h], this side's columns
 };
-static_assert(sizeof(SmemFrozen) <= 160 * 1024, "LDS budget");
+static_assert(sizeof(SmemFrozen<2>) <= 160 * 1024, "LDS budget");
 
 // C = 64: the LDS the frozen copy would take holds two more O partial slots instead, so all
 // four waves store their partials at once and the sum needs no second stage or barrier.
@@ -143,6 +166,15 @@ struct __attribute__((aligned(16))) SmemFour : Smem {
     float o2[2][kMat];  // O partials of waves 2, 3
 };
 static_assert(sizeof(SmemFour) <= 160 * 1024, "LDS budget");
+
+// k operand over a wave's hidden units: its two 16-wide tiles, or its one tile and zeros.
+template <int kHt>
+__device__ __forceinline__ bf16x8 hcat(const bf16x4 (&x)[kHt][4], int i) {
+    if constexpr (kHt == 2)
+        return cat(x[0][i], x[1][i]);
+    else
+        return cat(x[0][i], bf16x4{});
+}
 
 // bf16 operand fragment from a k-contiguous fp32 LDS row (as frag(), rounding each element).
 __device__ __forceinline__ bf16x8 frag32(const float* p, int off) {
@@ -342,31 +374,41 @@ __device__ __forceinline__ void quad_reduce_scatter(const float (&v)[4][4], int 
     }
 }
 
-template <bool kFrozen, bool kSurp>
+template <int kS, bool kFrozen, bool kSurp>
 __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
-    __shared__ std::conditional_t<kFrozen, SmemFrozen, SmemFour> sm;
+    static_assert(!kSurp || kS == 2, "the surprise shares are laid out for pairs");
+    using SX = Split<kS>;
+    constexpr int kHidSide = SX::kHidSide, kHidW = SX::kHidW, kHt = SX::kHt;
+    constexpr int kYRows = SX::kYRows, kYE = SX::kYE, kYW = SX::kYW;
+    __shared__ std::conditional_t<kFrozen, SmemFrozen<kS>, SmemFour> sm;
     const int kSub = A.C / kC;  // sub-chunks per gradient chunk
     const int tid = threadIdx.x;
     const int wv = tid >> 6, l = tid & 63, g = l >> 4, j = l & 15;
-    // workgroups i and i ^ 8 form pair 8 (i / 16) + i % 8
+    // workgroups i + 8 s, s < kS (i % 8 = x, one XCD), serve memory 8 (i / (8 kS)) + x
     const int bid = blockIdx.x;
-    const int side = (bid >> 3) & 1;
-    const int64_t seq = 8 * (int64_t)(bid >> 4) + (bid & 7);
-    if (seq >= A.B * A.H) return;  // both workgroups of a padding pair leave together
+    const int side = (bid >> 3) % kS;
+    const int64_t seq = 8 * (int64_t)(bid / (8 * kS)) + (bid & 7);
+    if (seq >= A.B * A.H) return;  // all workgroups of a padding memory leave together
     const int64_t bi = seq / A.H, hi = seq % A.H;
 
-    char* pbase = static_cast<char*>(A.ws) + seq * kPairBytes;
+    char* pbase = static_cast<char*>(A.ws) + seq * SX::kBytes;
     int* myflag = reinterpret_cast<int*>(pbase) + (side * kWaves + wv) * 32;
-    int* otflag = reinterpret_cast<int*>(pbase) + ((1 - side) * kWaves + wv) * 32;
-    uint64_t* xo = reinterpret_cast<uint64_t*>(pbase + kFlagBytes);
-    uint64_t* xy = xo + kOWords;
-    auto oslot = [&](int e, int s) { return xo + ((e & 1) * 2 + s) * 8 * kThreads + tid; };
+    // the other sides: other(d) = side ^ (d + 1), d < kS - 1
+    auto other = [&](int d) { return side ^ (d + 1); };
+    auto flag_of = [&](int s) { return reinterpret_cast<int*>(pbase) + (s * kWaves + wv) * 32; };
+    uint64_t* xo = reinterpret_cast<uint64_t*>(pbase + SX::kFlagBytes);
+    uint64_t* xy = xo + SX::kOWords;
+    auto oslot = [&](int e, int s) { return xo + ((e & 1) * kS + s) * 8 * kThreads + tid; };
     const int64_t nchunks = (A.T + kC - 1) / kC;
-    const char* coef = static_cast<const char*>(A.ws) + ((A.B * A.H + 7) / 8 * 8) * kPairBytes +
+    const char* coef = static_cast<const char*>(A.ws) + ((A.B * A.H + 7) / 8 * 8) * SX::kBytes +
                        seq * nchunks * kCoefBytes;
-    auto yxslot = [&](int e, int s) { return xy + ((e & 1) * 2 + s) * 4 * kThreads + tid; };
+    // the y words side `src` posts for side `dst` (dst != src)
+    auto yxslot = [&](int e, int src, int dst) {
+        const int d = (src ^ dst) - 1;
+        return xy + (((e & 1) * kS + src) * (kS - 1) + d) * kYW * kThreads + tid;
+    };
     float* const spart = kSurp ? reinterpret_cast<float*>(static_cast<char*>(A.ws) +
-                                                         ((A.B * A.H + 7) / 8 * 8) * kPairBytes +
+                                                         ((A.B * A.H + 7) / 8 * 8) * SX::kBytes +
                                                          A.B * A.H * nchunks * kCoefBytes)
                                : nullptr;
     float* const shk = kSurp ? spart + seq * A.T * 2 * kSurpShares : nullptr;   // [t][2][128]
@@ -410,11 +452,10 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
     const int64_t ybase = bi * A.ys[0] + hi * A.ys[2];
     // this thread's slice of a chunk's 64 x 64 token tiles: row rc, columns cl0 .. cl0+15
     const int rc = tid >> 2, cl0 = 16 * (tid & 3);
-    // this thread's y elements: row yr of this side's half (own) and of the partner's
-    // half, columns yd0 .. yd0+7
-    const int yr = tid >> 3, yd0 = 8 * (tid & 7);
-    const int yrow_own = 32 * side + yr, yrow_oth = 32 * (1 - side) + yr;
-    float yown[8];
+    // this thread's y elements: row yr of each side's kYRows rows, columns yd0 .. yd0 + kYE - 1
+    const int yr = tid / (kD / kYE), yd0 = kYE * (tid % (kD / kYE));
+    const int yrow_own = kYRows * side + yr;
+    float yown[kYE];
 
     // B = [I16; 0] and [0; I16] in the MFMA k order (lane (g, j) slot v < 4 is row 4g + v of
     // the block's first 16 rows, slot v >= 4 row 4g + v - 4 of its second 16)
@@ -445,16 +486,27 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             kpre[0] = kpre[1] = qpre[0] = qpre[1] = bf16x8{};
         }
     };
-    // y for this side's rows of the chunk starting at token t0, own partial + partner's
-    auto write_y = [&](int64_t t0, const uint64_t* px) {
+    // y for this side's rows of the chunk starting at token t0: the sum of every side's
+    // partial in side order (px[d]: the words of side other(d))
+    auto write_y = [&](int64_t t0, const uint64_t (&px)[kS - 1][kYW]) {
         const int64_t t = t0 + yrow_own;
-        bf16x8 out;
+        __bf16 out[kYE];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            out[2 * i] = (__bf16)(bad ? __builtin_nanf("") : yown[2 * i] + lo32(px[i]));
-            out[2 * i + 1] = (__bf16)(bad ? __builtin_nanf("") : yown[2 * i + 1] + hi32(px[i]));
+        for (int i = 0; i < kYW; ++i)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                float pv[kS - 1];
+#pragma unroll
+                for (int d = 0; d < kS - 1; ++d) pv[d] = h2 ? hi32(px[d][i]) : lo32(px[d][i]);
+                out[2 * i + h2] = (__bf16)(bad ? __builtin_nanf("") : sum_sides<kS>(yown[2 * i + h2], pv));
+            }
+        if (t < A.T) {
+            __bf16* dst = yg + ybase + t * A.ys[1] + yd0;
+            if constexpr (kYE == 8)
+                *reinterpret_cast<bf16x8*>(dst) = bf16x8{out[0], out[1], out[2], out[3], out[4], out[5], out[6], out[7]};
+            else
+                *reinterpret_cast<bf16x4*>(dst) = bf16x4{out[0], out[1], out[2], out[3]};
         }
-        if (t < A.T) *reinterpret_cast<bf16x8*>(yg + ybase + t * A.ys[1] + yd0) = out;
     };
     // the prefetched chunk's Q and Cm into LDS (both dead once the Y partials are stored)
     auto commit_qc = [&]() {
@@ -491,10 +543,10 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
                     for (int ht = 0; ht < kHt; ++ht) {
-                        *reinterpret_cast<bf16x4*>(sm.w1c + (32 * wv + 16 * ht + j) * kLd + 16 * dt +
-                                                   4 * g) = bf4(W1T[dt][ht]);
-                        *reinterpret_cast<bf16x4*>(sm.w2c + (16 * dt + j) * kLd2 + 32 * wv + 16 * ht +
-                                                   4 * g) = bf4(W2T[ht][dt]);
+                        *reinterpret_cast<bf16x4*>(sm.w1c + (kHidW * wv + 16 * ht + j) * kLd +
+                                                   16 * dt + 4 * g) = bf4(W1T[dt][ht]);
+                        *reinterpret_cast<bf16x4*>(sm.w2c + (16 * dt + j) * SX::kLd2 + kHidW * wv +
+                                                   16 * ht + 4 * g) = bf4(W2T[ht][dt]);
                     }
             }
         }
@@ -513,7 +565,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
         __syncthreads();  // B1
 
         // ================= P1: key forward and O partials
-        // Z = K W1^T (rows c, cols h) for this wave's 32 hidden units; Hk^T (rows h, cols c)
+        // Z = K W1^T (rows c, cols h) for this wave's hidden units; Hk^T (rows h, cols c)
         // by an exact MFMA against the identity (D = A [I; 0] is the transpose of A's first
         // 16 x 16 tile when A is an accumulator tile in registers)
         bf16x4 Hk[4][kHt], Sp[4][kHt], HkT[kHt][4];
@@ -525,7 +577,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             for (int ht = 0; ht < kHt; ++ht) {
                 bf16x8 bw0, bw1;
                 if constexpr (kFrozen) {
-                    const __bf16* wr = sm.w1c + (32 * wv + 16 * ht + j) * kLd + 4 * g;
+                    const __bf16* wr = sm.w1c + (kHidW * wv + 16 * ht + j) * kLd + 4 * g;
                     bw0 = frag(wr, 0);
                     bw1 = frag(wr, 32);
                 } else {
@@ -566,14 +618,20 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             const int rb = opq(j * kLd + 4 * g);
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
+                // k = this wave's hidden units (16 of them: the upper k half is zero)
                 bf16x8 a0;
-                if constexpr (kFrozen)
-                    a0 = frag(sm.w2c + (16 * dt + j) * kLd2 + 32 * wv + 4 * g, 0);
-                else
+                const __bf16* w2r = nullptr;
+                if constexpr (kFrozen) w2r = sm.w2c + (16 * dt + j) * SX::kLd2 + kHidW * wv + 4 * g;
+                if constexpr (kFrozen && kHt == 2)
+                    a0 = frag(w2r, 0);
+                else if constexpr (kFrozen)
+                    a0 = cat(*reinterpret_cast<const bf16x4*>(w2r), bf16x4{});
+                else if constexpr (kHt == 2)
                     a0 = state_frag(W2T[0][dt], W2T[1][dt]);
+                else
+                    a0 = state_frag(W2T[0][dt], zero4());
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct)
-                    Ot[dt][ct] = mfma(a0, cat(HkT[0][ct], HkT[1][ct]), zero4());
+                for (int ct = 0; ct < 4; ++ct) Ot[dt][ct] = mfma(a0, hcat(HkT, ct), zero4());
             }
             // deterministic reduction, fixed order (w0 + w2) + (w1 + w3):
             //   C = 64: every wave stores its partial in its own slot;
@@ -724,21 +782,29 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                     S1T[dt][ht] = pC * S1T[dt][ht];
                 }
         }
-        wait_flag(otflag, e, bad, max_spin);
+#pragma unroll
+        for (int d = 0; d < kS - 1; ++d) wait_flag(flag_of(other(d)), e, bad, max_spin);
         {
-            // the partner's O partial of this chunk and its partial of this side's y rows of
-            // the previous chunk, all loads issued together (one round trip)
-            uint64_t po[8], px[4];
-            const uint64_t* src = oslot(e, 1 - side);
+            // the other sides' O partials of this chunk and their partials of this side's y
+            // rows of the previous chunk, all loads issued together (one round trip)
+            uint64_t po[kS - 1][8], px[kS - 1][kYW];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) po[i] = xload(const_cast<uint64_t*>(src + i * kThreads));
-            if (e > 1) {
-                const uint64_t* srcy = yxslot(e - 1, 1 - side);
+            for (int d = 0; d < kS - 1; ++d) {
+                const uint64_t* src = oslot(e, other(d));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) px[i] = xload(const_cast<uint64_t*>(srcy + i * kThreads));
+                for (int i = 0; i < 8; ++i) po[d][i] = xload(const_cast<uint64_t*>(src + i * kThreads));
             }
-            // E2 = loss'(O - V) (2 (O - V) for the squared error), O = O_side0 + O_side1,
-            // in its four layouts
+            if (e > 1) {
+#pragma unroll
+                for (int d = 0; d < kS - 1; ++d) {
+                    const uint64_t* srcy = yxslot(e - 1, other(d), side);
+#pragma unroll
+                    for (int i = 0; i < kYW; ++i)
+                        px[d][i] = xload(const_cast<uint64_t*>(srcy + i * kThreads));
+                }
+            }
+            // E2 = loss'(O - V) (2 (O - V) for the squared error), O = the sides' partials
+            // summed in side order (bitwise the same O on every side), in its four layouts
             const int xb = opq(rc * kLd + cl0), xt = opq(cl0 * kLd + rc);
             // gradient chunks longer than 64 tokens: E2's low part E2 - bf16(E2) (exact in
             // fp32) for the product G below, fp32 [c][dd] in O partial slot 0, which is dead
@@ -753,8 +819,11 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) {
                     const int k = 4 * q4 + e4;
-                    const float op = (k & 1) ? hi32(po[k >> 1]) : lo32(po[k >> 1]);
-                    o[e4] = side == 0 ? oo[k] + op : op + oo[k];
+                    float op[kS - 1];
+#pragma unroll
+                    for (int d = 0; d < kS - 1; ++d)
+                        op[d] = (k & 1) ? hi32(po[d][k >> 1]) : lo32(po[d][k >> 1]);
+                    o[e4] = sum_sides<kS>(oo[k], op);
                 }
                 const f32x4 v4 = f4(half4(vr[q4 >> 1], q4 & 1));
                 const f32x4 e2 = bias_grad4(o - v4, A.bias, A.bias_param);
@@ -797,8 +866,8 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                     // gradient is taken at (operand A of the identity product)
                     bf16x4 tile;
                     if constexpr (kFrozen)
-                        tile = *reinterpret_cast<const bf16x4*>(sm.w2c + (16 * dt + j) * kLd2 +
-                                                                 32 * wv + 16 * ht + 4 * g);
+                        tile = *reinterpret_cast<const bf16x4*>(sm.w2c + (16 * dt + j) * SX::kLd2 +
+                                                                 kHidW * wv + 16 * ht + 4 * g);
                     else
                         tile = bf4(W2T[ht][dt]);
                     W2n[dt][ht] = bf4(mfma(cat(tile, bf16x4{}), eye, zero4()));
@@ -892,12 +961,12 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 const __bf16* cmr = sm.cm + rb;
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
-                    const bf16x8 bq = cat(Hq[0][ct], Hq[1][ct]);
+                    const bf16x8 bq = hcat(Hq, ct);
 #pragma unroll
                     for (int ctp = 0; ctp < 4; ++ctp) {
                         f32x4 pt = zero4();
                         if (ctp <= ct) {
-                            pt = mfma(cat(HkT[0][ctp], HkT[1][ctp]), bq, pt);
+                            pt = mfma(hcat(HkT, ctp), bq, pt);
                             const f32x4 cmv =
                                 f4(*reinterpret_cast<const bf16x4*>(cmr + 16 * ct * kLd + 16 * ctp));
                             pt = -(pt * cmv);
@@ -910,14 +979,20 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
             const __bf16* etr = sm.e2t + rb;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                const bf16x8 aw = state_frag(W2T[0][dt], W2T[1][dt]);
-                const bf16x8 as = state_frag(S2T[0][dt], S2T[1][dt]);
+                bf16x8 aw, as;
+                if constexpr (kHt == 2) {
+                    aw = state_frag(W2T[0][dt], W2T[1][dt]);
+                    as = state_frag(S2T[0][dt], S2T[1][dt]);
+                } else {
+                    aw = state_frag(W2T[0][dt], zero4());
+                    as = state_frag(S2T[0][dt], zero4());
+                }
                 const bf16x8 e0 = frag(etr, fo(dt, 0));
                 const bf16x8 e1 = frag(etr, fo(dt, 1));
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
-                    f32x4 yt = mfma(aw, cat(Hqa[0][ct], Hqa[1][ct]), zero4());
-                    yt = mfma(as, cat(Hqb[0][ct], Hqb[1][ct]), yt);
+                    f32x4 yt = mfma(aw, hcat(Hqa, ct), zero4());
+                    yt = mfma(as, hcat(Hqb, ct), yt);
                     yt = mfma(e0, cat(pm[ct][0], pm[ct][1]), yt);
                     if (ct >= 2) yt = mfma(e1, cat(pm[ct][2], pm[ct][3]), yt);
                     *reinterpret_cast<f32x4*>(slot + 16 * ct * kLd + 16 * dt) = yt;
@@ -926,14 +1001,15 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
         }
         __syncthreads();  // B6: all Y partials stored
 
-        // ================= P5: this side's Y; post the partner's rows; carry
+        // ================= P5: this side's Y; post the other sides' rows; carry
         {
-            float ys[2][8];
+            // hlf 0: this side's rows; hlf d + 1: side other(d)'s rows
+            float ys[kS][kYE];
 #pragma unroll
-            for (int hlf = 0; hlf < 2; ++hlf) {
-                const int e0 = (hlf == 0 ? yrow_own : yrow_oth) * kLd + yd0;
+            for (int hlf = 0; hlf < kS; ++hlf) {
+                const int e0 = (kYRows * (hlf == 0 ? side : other(hlf - 1)) + yr) * kLd + yd0;
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
+                for (int q = 0; q < kYE / 4; ++q) {
                     const int e4 = e0 + 4 * q;
                     const f32x4 yv = (*reinterpret_cast<const f32x4*>(yslot(sm, 0) + e4) +
                                       *reinterpret_cast<const f32x4*>(yslot(sm, 1) + e4)) +
@@ -944,12 +1020,15 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                 }
             }
 #pragma unroll
-            for (int k = 0; k < 8; ++k) yown[k] = ys[0][k];
-            uint64_t* dst = yxslot(e, side);
+            for (int k = 0; k < kYE; ++k) yown[k] = ys[0][k];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                xstore(dst + i * kThreads, pack2(bad ? __builtin_nanf("") : ys[1][2 * i],
-                                                 bad ? __builtin_nanf("") : ys[1][2 * i + 1]));
+            for (int d = 0; d < kS - 1; ++d) {
+                uint64_t* dst = yxslot(e, side, other(d));
+#pragma unroll
+                for (int i = 0; i < kYW; ++i)
+                    xstore(dst + i * kThreads, pack2(bad ? __builtin_nanf("") : ys[d + 1][2 * i],
+                                                     bad ? __builtin_nanf("") : ys[d + 1][2 * i + 1]));
+            }
         }
         if (c0 + kC < A.T) commit_qc();  // every wave is past B6: Q and Cm are no longer read
         {
@@ -1005,11 +1084,15 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
     {
         const int ef = e + 1;
         if (!mute) post_flag(myflag, ef, l);
-        wait_flag(otflag, ef, bad, max_spin);
-        uint64_t px[4];
-        const uint64_t* src = yxslot(e, 1 - side);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) px[i] = xload(const_cast<uint64_t*>(src + i * kThreads));
+        for (int d = 0; d < kS - 1; ++d) wait_flag(flag_of(other(d)), ef, bad, max_spin);
+        uint64_t px[kS - 1][kYW];
+#pragma unroll
+        for (int d = 0; d < kS - 1; ++d) {
+            const uint64_t* src = yxslot(e, other(d), side);
+#pragma unroll
+            for (int i = 0; i < kYW; ++i) px[d][i] = xload(const_cast<uint64_t*>(src + i * kThreads));
+        }
         write_y((int64_t)(e - 1) * kC, px);
     }
     if (bad) sm.fail = 1;
@@ -1034,14 +1117,20 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
         }
 }
 
-// Clears the flags of every pair before a launch (exchange numbers restart at 1).
-__global__ void clear_pair_flags(char* ws, int64_t npairs) {
-    const int64_t pair = blockIdx.x;
-    if (pair >= npairs) return;
-    int* f = reinterpret_cast<int*>(ws + pair * kPairBytes);
-    for (int i = threadIdx.x; i < (int)(kFlagBytes / 4); i += blockDim.x) f[i] = 0;
+// Clears the flags of every memory's exchange area before a launch (exchange numbers
+// restart at 1).
+__global__ void clear_pair_flags(char* ws, int64_t nmem, int64_t area_bytes, int flag_bytes) {
+    const int64_t m = blockIdx.x;
+    if (m >= nmem) return;
+    int* f = reinterpret_cast<int*>(ws + m * area_bytes);
+    for (int i = threadIdx.x; i < flag_bytes / 4; i += blockDim.x) f[i] = 0;
 }
 
+// Workgroups per memory of a call (ScanArgs::sides, 2 unless the dispatcher chose 4).
+int sides_of(const ScanArgs& a) { return a.sides == 4 ? 4 : 2; }
+int64_t area_bytes(const ScanArgs& a) {
+    return sides_of(a) == 4 ? Split<4>::kBytes : Split<2>::kBytes;
+}
 int64_t padded_pairs(const ScanArgs& a) { return (a.B * a.H + 7) / 8 * 8; }
 int64_t num_chunks(const ScanArgs& a) { return (a.T + kC - 1) / kC; }
 
@@ -1104,7 +1193,7 @@ hipError_t scan_pair_scratch(void** ptr) {
 }
 
 size_t scan_pair_scratch_exchange_bytes(const ScanArgs& a) {
-    return (size_t)padded_pairs(a) * (size_t)kPairBytes;
+    return (size_t)padded_pairs(a) * (size_t)area_bytes(a);
 }
 
 size_t scan_pair_scratch_chunk_bytes(const ScanArgs& a) {
@@ -1121,17 +1210,22 @@ bool scan_pair_supported(const ScanArgs& a) {
 }
 
 size_t scan_pair_workspace_bytes(const ScanArgs& a) {
-    return (size_t)padded_pairs(a) * (size_t)kPairBytes +
+    return (size_t)padded_pairs(a) * (size_t)area_bytes(a) +
            (size_t)(a.B * a.H) * (size_t)num_chunks(a) * (size_t)kCoefBytes;
 }
 
-int64_t scan_pair_workgroups(const ScanArgs& a) { return 2 * padded_pairs(a); }
+int64_t scan_pair_workgroups(const ScanArgs& a) { return sides_of(a) * padded_pairs(a); }
 
 hipError_t launch_scan_pair(const ScanArgs& a, hipStream_t stream) {
-    const int64_t npairs = padded_pairs(a);
-    if (npairs == 0) return hipSuccess;
+    const int64_t nmem = padded_pairs(a);
+    if (nmem == 0) return hipSuccess;
+    const int S = sides_of(a);
+    const bool surp = a.surprise != nullptr;
+    if (surp && S != 2) return hipErrorInvalidValue;  // surprise shares: pairs only
     char* ws = static_cast<char*>(a.ws);
-    clear_pair_flags<<<dim3((unsigned)npairs), 256, 0, stream>>>(ws, npairs);
+    const int64_t area = area_bytes(a);
+    clear_pair_flags<<<dim3((unsigned)nmem), 256, 0, stream>>>(
+        ws, nmem, area, (int)(S == 4 ? Split<4>::kFlagBytes : Split<2>::kFlagBytes));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nchunks = num_chunks(a);
@@ -1139,23 +1233,28 @@ hipError_t launch_scan_pair(const ScanArgs& a, hipStream_t stream) {
     if (ntasks > 0) {
         const int64_t blocks = (ntasks + kWaves - 1) / kWaves;
         if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-        pair_coef_kernel<<<dim3((unsigned)blocks), kThreads, 0, stream>>>(
-            a, ws + npairs * kPairBytes, nchunks);
+        pair_coef_kernel<<<dim3((unsigned)blocks), kThreads, 0, stream>>>(a, ws + nmem * area,
+                                                                         nchunks);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     ScanArgs args = a;
     void* kargs[] = {&args};
-    const bool surp = a.surprise != nullptr;
-    const void* fn =
-        a.C == kC ? (surp ? reinterpret_cast<const void*>(&scan_pair_kernel<false, true>)
-                          : reinterpret_cast<const void*>(&scan_pair_kernel<false, false>))
-                  : (surp ? reinterpret_cast<const void*>(&scan_pair_kernel<true, true>)
-                          : reinterpret_cast<const void*>(&scan_pair_kernel<true, false>));
-    e = hipLaunchCooperativeKernel(fn, dim3((unsigned)(2 * npairs)), dim3(kThreads), kargs, 0,
+    const bool frozen = a.C != kC;
+    const void* fn;
+    if (S == 4)
+        fn = frozen ? reinterpret_cast<const void*>(&scan_pair_kernel<4, true, false>)
+                    : reinterpret_cast<const void*>(&scan_pair_kernel<4, false, false>);
+    else if (frozen)
+        fn = surp ? reinterpret_cast<const void*>(&scan_pair_kernel<2, true, true>)
+                  : reinterpret_cast<const void*>(&scan_pair_kernel<2, true, false>);
+    else
+        fn = surp ? reinterpret_cast<const void*>(&scan_pair_kernel<2, false, true>)
+                  : reinterpret_cast<const void*>(&scan_pair_kernel<2, false, false>);
+    e = hipLaunchCooperativeKernel(fn, dim3((unsigned)(S * nmem)), dim3(kThreads), kargs, 0,
                                    stream);
     if (e != hipSuccess || !surp) return e;
-    const float* part = reinterpret_cast<const float*>(ws + npairs * kPairBytes +
+    const float* part = reinterpret_cast<const float*>(ws + nmem * area +
                                                        a.B * a.H * nchunks * kCoefBytes);
     const int64_t n = a.B * a.H * a.T;
     if ((n + 15) / 16 > 0xffffffffLL) return hipErrorInvalidConfiguration;

@@ -32,6 +32,7 @@ struct ScanArgs {
     float* sT;
     void* ws;
     int debug;                 // test hooks (0 in normal use), see abi.hip
+    int sides;                 // pair path: workgroups per memory (4, else 2), set by the dispatcher
     int bias;                  // titans_bias of the writes
     float bias_param;          // Huber delta or l_p exponent
 };
@@ -83,9 +84,10 @@ hipError_t launch_scan_phased(const ScanArgs& a, hipStream_t stream);
 bool scan_mfma_supported(const ScanArgs& a);
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t stream);
 
-// Fused MFMA scan split over pairs of workgroups (same shape as above): each (b, h)
-// memory is served by two workgroups on one XCD that exchange partial sums through the
-// workspace; cooperative launch of scan_pair_workgroups(a) workgroups.
+// Fused MFMA scan split over pairs (a.sides = 2) or quads (a.sides = 4) of workgroups
+// (same shape as above): each (b, h) memory is served by that many workgroups on one XCD
+// that exchange partial sums through the workspace; cooperative launch of
+// scan_pair_workgroups(a) workgroups.  The per-token surprise needs pairs.
 bool scan_pair_supported(const ScanArgs& a);
 size_t scan_pair_workspace_bytes(const ScanArgs& a);
 int64_t scan_pair_workgroups(const ScanArgs& a);

@@ -57,17 +57,31 @@ def _desc(B=2, T=64, H=4, d=64, C=64, io=1):
 
 def test_workspace_size_query(monkeypatch):
     mlp = tm.mlp_desc((64, 256, 64))
-    # the fused shape (64-256-64, C=64, bf16) runs on pairs of workgroups that exchange
-    # partial sums through the workspace (one 97 KiB area per pair, pairs padded to 8),
-    # after a pass that writes every chunk's gate coefficients (9472 bytes per chunk)
+    # the fused shape (64-256-64, C=64, bf16) runs on groups of workgroups that exchange
+    # partial sums through the workspace, after a pass that writes every chunk's gate
+    # coefficients (9472 bytes per chunk): quads (a 226 KiB area per memory, memories padded
+    # to 8) while four workgroups per memory fit the 256 compute units (B*H <= 64), pairs (a
+    # 97 KiB area per memory) up to B*H = 128
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc()), ctypes.byref(mlp)) == b"fused_quad"
+    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc()),
+                                                 ctypes.byref(mlp)) == 8 * 231424 + 8 * 1 * 9472
+    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(B=3, T=130, H=3)),
+                                                 ctypes.byref(mlp)) == 16 * 231424 + 9 * 3 * 9472
+    for B, H, path, area in ((4, 16, b"fused_quad", 231424), (5, 13, b"fused_pair", 99328),
+                             (8, 16, b"fused_pair", 99328)):
+        d = _desc(B=B, H=H)
+        assert tm.lib.titans_mem_scan_path(ctypes.byref(d), ctypes.byref(mlp)) == path
+        npad = (B * H + 7) // 8 * 8
+        assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(d), ctypes.byref(mlp)) == \
+            npad * area + B * H * 9472
+    monkeypatch.setenv("TITANS_MEM_PAIR_SIDES", "2")  # keeps pairs (testing switch)
     assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc()), ctypes.byref(mlp)) == b"fused_pair"
     assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc()),
                                                  ctypes.byref(mlp)) == 8 * 99328 + 8 * 1 * 9472
-    assert tm.lib.titans_mem_scan_workspace_size(ctypes.byref(_desc(B=3, T=130, H=3)),
-                                                 ctypes.byref(mlp)) == 16 * 99328 + 9 * 3 * 9472
+    monkeypatch.delenv("TITANS_MEM_PAIR_SIDES")
     # chunks that are multiples of 64 run on the pair path too (64-token sub-chunks whose
     # gradients share the chunk-start weights); other lengths on the generic kernel
-    for C, path in ((128, b"fused_pair"), (256, b"fused_pair"), (96, b"phased_mfma"),
+    for C, path in ((128, b"fused_quad"), (256, b"fused_quad"), (96, b"phased_mfma"),
                     (32, b"phased_mfma")):
         assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(C=C)), ctypes.byref(mlp)) == path
     assert tm.lib.titans_mem_scan_path(ctypes.byref(_desc(B=64, H=16, C=256)),
@@ -221,7 +235,7 @@ def test_pair_path_workspace_validation():
     desc = _desc(B, T, H)
     desc.state_stride[:] = (H * P, P)
     desc.state0_stride[:] = (0, P)
-    assert tm.lib.titans_mem_scan_path(ctypes.byref(desc), ctypes.byref(mlp)) == b"fused_pair"
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(desc), ctypes.byref(mlp)) == b"fused_quad"
     ptrs, end = _fake_ptrs()
     need = tm.lib.titans_mem_scan_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
     assert need > 0
@@ -257,15 +271,19 @@ def _scan_surprise(desc, mlp, ptrs, surprise, ws=None, ws_bytes=0):
 
 
 def test_surprise_workspace_follows_the_path(monkeypatch):
-    """The fused shape's surprise call runs on the pair path with 65 floats of partial sums
-    per token-head after the plain scan's workspace; forced onto the generic family it takes
-    the phased path's workspace, as the plain scan does there."""
+    """The fused shape's surprise call runs on pairs (where the plain scan of this small
+    shape takes quads) with 65 floats of partial sums per token-head after the pairs'
+    workspace; forced onto the generic family it takes the phased path's workspace, as the
+    plain scan does there."""
     mlp = tm.mlp_desc((64, 256, 64))
     desc = _desc()
     B, T, H = desc.batch, desc.seq_len, desc.heads
-    pair = tm.lib.titans_mem_scan_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+    assert tm.lib.titans_mem_scan_path(ctypes.byref(desc), ctypes.byref(mlp)) == b"fused_quad"
     sur = tm.lib.titans_mem_scan_surprise_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
     assert tm.lib.titans_mem_scan_surprise_path(ctypes.byref(desc), ctypes.byref(mlp)) == b"fused_pair"
+    monkeypatch.setenv("TITANS_MEM_PAIR_SIDES", "2")
+    pair = tm.lib.titans_mem_scan_workspace_size(ctypes.byref(desc), ctypes.byref(mlp))
+    monkeypatch.delenv("TITANS_MEM_PAIR_SIDES")
     assert sur == pair + B * H * T * 65 * 4
     monkeypatch.setenv("TITANS_MEM_FORCE_GENERIC", "1")
     assert tm.lib.titans_mem_scan_path(ctypes.byref(desc), ctypes.byref(mlp)) == b"phased_mfma"

@@ -586,15 +586,21 @@ def test_retrieve_headline_shape_sampled():
 
 # ----------------------------------------------------------- fused kernels
 #
-# The 64-256-64, C=64, bf16 shape runs on the pair kernel (two workgroups per memory)
-# while the pairs fit the GPU, else on the single-workgroup kernel; both are tested.
+# The 64-256-64, C=64, bf16 shape runs on the pair kernel with four workgroups per memory
+# (quads) while they fit the GPU, with two (pairs) while those fit, else on the
+# single-workgroup kernel; all three are tested (TITANS_MEM_PAIR_SIDES=2 keeps a small
+# shape on pairs, TITANS_MEM_FUSED_SINGLE=1 on one workgroup per memory).
 
-FUSED = ["pair", "single"]
+FUSED = ["quad", "pair", "single"]
 
 
 def _use(kernel, monkeypatch):
     monkeypatch.setenv("TITANS_MEM_FUSED_SINGLE", "1" if kernel == "single" else "0")
-    return "fused_pair" if kernel == "pair" else "fused_mfma"
+    if kernel == "pair":
+        monkeypatch.setenv("TITANS_MEM_PAIR_SIDES", "2")
+    else:
+        monkeypatch.delenv("TITANS_MEM_PAIR_SIDES", raising=False)
+    return {"quad": "fused_quad", "pair": "fused_pair", "single": "fused_mfma"}[kernel]
 
 
 @pytest.mark.parametrize("kernel", FUSED)
@@ -684,14 +690,15 @@ def test_fused_strided_inputs_nonzero_momentum(kernel, monkeypatch):
     check_pairs(wl, y, thT, sT, pairs, refs)
 
 
+@pytest.mark.parametrize("kernel", ["quad", "pair"])
 @pytest.mark.parametrize("C,T", [(128, 300), (192, 385), (256, 600), (256, 100)])
-def test_pair_long_chunks_match_oracle(C, T, monkeypatch):
-    """Chunks of 128..256 tokens on the pair path: 64-token sub-chunks whose gradients are
-    all taken at the chunk-start weights."""
+def test_pair_long_chunks_match_oracle(C, T, kernel, monkeypatch):
+    """Chunks of 128..256 tokens on the pair path (quads and pairs): 64-token sub-chunks
+    whose gradients are all taken at the chunk-start weights."""
     wl, inp = _small(widths=(64, 256, 64), B=2, T=T, H=3, C=C, io="bf16", seed=C + T)
     dev = to_device(inp)
-    log(f"case pair path C={C} T={T}")
-    expected = _use("pair", monkeypatch)
+    log(f"case {kernel} path C={C} T={T}")
+    expected = _use(kernel, monkeypatch)
     assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == expected
     y, thT, sT = run_gpu(dev, wl)
     y2, thT2, sT2 = run_gpu(dev, wl)
@@ -726,16 +733,17 @@ def test_scan_and_retrieve_on_a_side_stream():
     assert torch.equal(r0, r1)
 
 
-def test_pair_wait_bound_ends_the_kernel(monkeypatch):
-    """Failure handling of the pair exchange, forced from the host: one side of every pair
-    never sends (test hook) and the waits give up after a few polls.  The kernel must end;
-    the side that timed out poisons what it sends from then on, so every output of the
-    memory -- both halves of theta_T and s_T and every y row of both sides -- comes out NaN
-    (no finite value built from missing partials); the next normal call is exact again."""
+@pytest.mark.parametrize("kernel", ["quad", "pair"])
+def test_pair_wait_bound_ends_the_kernel(kernel, monkeypatch):
+    """Failure handling of the exchange, forced from the host: side 1 of every memory never
+    sends (test hook) and the waits give up after a few polls.  The kernel must end; a side
+    that timed out poisons what it sends from then on, so every output of the memory --
+    every side's slice of theta_T and s_T and every y row -- comes out NaN (no finite value
+    built from missing partials); the next normal call is exact again."""
     wl, inp = _small(widths=(64, 256, 64), B=1, T=200, H=2, C=64, io="bf16", seed=41)
     dev = to_device(inp)
-    log("case pair wait bound (forced timeout)")
-    _use("pair", monkeypatch)
+    log(f"case {kernel} wait bound (forced timeout)")
+    _use(kernel, monkeypatch)
     y0, t0, s0 = run_gpu(dev, wl)
     monkeypatch.setenv("TITANS_MEM_TEST_PAIR_TIMEOUT", "1")
     y1, t1, s1 = run_gpu(dev, wl)
@@ -748,13 +756,14 @@ def test_pair_wait_bound_ends_the_kernel(monkeypatch):
     assert torch.equal(y2, y0) and torch.equal(t2, t0) and torch.equal(s2, s0)
 
 
-def test_pair_kernel_matches_single_kernel(monkeypatch):
-    """The two fused kernels round at the same points and differ only in summation order."""
+@pytest.mark.parametrize("kernel", ["quad", "pair"])
+def test_pair_kernel_matches_single_kernel(kernel, monkeypatch):
+    """The fused kernels round at the same points and differ only in summation order."""
     wl = _workload("h8_d64_b4_t4k", True)
     inp = synthetic.make_inputs(wl, 5)
     dev = to_device(inp)
-    log("case pair vs single fused kernel, h8 T=4096 sustained")
-    _use("pair", monkeypatch)
+    log(f"case {kernel} vs single fused kernel, h8 T=4096 sustained")
+    assert _use(kernel, monkeypatch) == tm.scan_path(dev["q"], wl.chunk, wl.widths)
     y1, t1, s1 = run_gpu(dev, wl)
     _use("single", monkeypatch)
     y2, t2, s2 = run_gpu(dev, wl)
@@ -762,16 +771,22 @@ def test_pair_kernel_matches_single_kernel(monkeypatch):
     ey = y_rel_err(to_f64(y1), to_f64(y2))
     et = state_rel_err(to_f64(t1), to_f64(t2))
     es = state_rel_err(to_f64(s1), to_f64(s2))
-    log(f"  pair vs single: y {ey:.2e} theta_T {et:.2e} s_T {es:.2e}")
+    log(f"  {kernel} vs single: y {ey:.2e} theta_T {et:.2e} s_T {es:.2e}")
     assert ey <= 2e-2 and et <= 1e-1 and es <= 1e-1
 
 
 def test_fused_path_switch_at_the_compute_unit_limit(monkeypatch):
-    """More memories than pairs of compute units: the fused shape runs one workgroup per
-    memory (and still matches the oracle)."""
+    """Quads while four workgroups per memory fit the compute units, then pairs; more
+    memories than pairs of compute units: the fused shape runs one workgroup per memory
+    (and still matches the oracle)."""
     monkeypatch.delenv("TITANS_MEM_FUSED_SINGLE", raising=False)
+    monkeypatch.delenv("TITANS_MEM_PAIR_SIDES", raising=False)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     H = 8
+    Bq = cus // (4 * H)  # 4 * ceil(B*H / 8) * 8 <= cus
+    for Bx, path in ((Bq, "fused_quad"), (Bq + 1, "fused_pair")):
+        x = _small(widths=(64, 256, 64), B=Bx, T=70, H=H, C=64, io="bf16", seed=31)[1]
+        assert tm.scan_path(to_device(x)["q"], 64, (64, 256, 64)) == path
     B = cus // (2 * H) + 1  # 2 * ceil(B*H / 8) * 8 > cus
     wl, inp = _small(widths=(64, 256, 64), B=B, T=130, H=H, C=64, io="bf16", seed=31)
     dev = to_device(inp)
@@ -805,8 +820,10 @@ BIAS_PATHS = {
     "generic_bf16": ((16, 32, 16), 5, "bf16", {"TITANS_MEM_GENERIC_MODE": "single"}, "generic_mfma"),
     "phased_f32": ((32, 160, 32), 40, "f32", {}, "phased_fp32"),
     "phased_bf16": ((32, 160, 32), 40, "bf16", {}, "phased_mfma"),
-    "pair": ((64, 256, 64), 64, "bf16", {}, "fused_pair"),
-    "pair_c128": ((64, 256, 64), 128, "bf16", {}, "fused_pair"),
+    "quad": ((64, 256, 64), 64, "bf16", {}, "fused_quad"),
+    "quad_c128": ((64, 256, 64), 128, "bf16", {}, "fused_quad"),
+    "pair": ((64, 256, 64), 64, "bf16", {"TITANS_MEM_PAIR_SIDES": "2"}, "fused_pair"),
+    "pair_c128": ((64, 256, 64), 128, "bf16", {"TITANS_MEM_PAIR_SIDES": "2"}, "fused_pair"),
     "single": ((64, 256, 64), 64, "bf16", {"TITANS_MEM_FUSED_SINGLE": "1"}, "fused_mfma"),
 }
 
