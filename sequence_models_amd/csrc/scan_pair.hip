@@ -113,14 +113,22 @@ __device__ __forceinline__ void post_flag(int* flag, int e, int lane) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     if (lane == 0) __hip_atomic_store(flag, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Wave-uniform bounded wait for the partner wave's flag to reach e.  `bad` latches a
-// timeout; a wave that has timed out does not wait again.
-__device__ __forceinline__ void wait_flag(int* flag, int e, bool& bad, int max_spin) {
+// Wave-uniform bounded wait for the partner waves' flags (one per other side) to reach e:
+// every poll loads all of them at once, so partners that post at different times cost one
+// round trip per poll, not one per partner.  `bad` latches a timeout; a wave that has timed
+// out does not wait again.
+template <int N>
+__device__ __forceinline__ void wait_flags(int* const (&flag)[N], int e, bool& bad, int max_spin) {
     if (bad) return;
     for (int s = 0; s < max_spin; ++s) {
-        const int v = __builtin_amdgcn_readfirstlane(
-            __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        if (v >= e) {
+        int v[N];
+#pragma unroll
+        for (int d = 0; d < N; ++d)
+            v[d] = __hip_atomic_load(flag[d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int m = __builtin_amdgcn_readfirstlane(v[0]);
+#pragma unroll
+        for (int d = 1; d < N; ++d) m = min(m, __builtin_amdgcn_readfirstlane(v[d]));
+        if (m >= e) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // no load moves above
             return;
         }
@@ -396,6 +404,9 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
     // the other sides: other(d) = side ^ (d + 1), d < kS - 1
     auto other = [&](int d) { return side ^ (d + 1); };
     auto flag_of = [&](int s) { return reinterpret_cast<int*>(pbase) + (s * kWaves + wv) * 32; };
+    int* pflag[kS - 1];  // the same wave's flag on every other side
+#pragma unroll
+    for (int d = 0; d < kS - 1; ++d) pflag[d] = flag_of(other(d));
     uint64_t* xo = reinterpret_cast<uint64_t*>(pbase + SX::kFlagBytes);
     uint64_t* xy = xo + SX::kOWords;
     auto oslot = [&](int e, int s) { return xo + ((e & 1) * kS + s) * 8 * kThreads + tid; };
@@ -782,8 +793,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
                     S1T[dt][ht] = pC * S1T[dt][ht];
                 }
         }
-#pragma unroll
-        for (int d = 0; d < kS - 1; ++d) wait_flag(flag_of(other(d)), e, bad, max_spin);
+        wait_flags(pflag, e, bad, max_spin);
         {
             // the other sides' O partials of this chunk and their partials of this side's y
             // rows of the previous chunk, all loads issued together (one round trip)
@@ -1084,8 +1094,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_pair_kernel(ScanArgs A) {
     {
         const int ef = e + 1;
         if (!mute) post_flag(myflag, ef, l);
-#pragma unroll
-        for (int d = 0; d < kS - 1; ++d) wait_flag(flag_of(other(d)), ef, bad, max_spin);
+        wait_flags(pflag, ef, bad, max_spin);
         uint64_t px[kS - 1][kYW];
 #pragma unroll
         for (int d = 0; d < kS - 1; ++d) {
