@@ -1,45 +1,49 @@
-// Fused chunked Titans memory scan with each memory split over a PAIR of workgroups,
-// for the 64 -> 256 -> 64 SiLU memory with chunks of 64 tokens and bf16 q/k/v/y
-// (fp32 gates and state).
+// Fused chunked Titans memory scan with each memory split over a PAIR (or a QUAD) of
+// workgroups, for the 64 -> 256 -> 64 SiLU memory with chunks of 64 tokens and bf16
+// q/k/v/y (fp32 gates and state).
 //
-// Why a pair: one (b, h) memory per workgroup leaves half of the GPU's compute units
-// idle when there are fewer memories than compute units, and its 256 KB of fp32 state
-// fills the register file of one CU.  Here side s (0, 1) of a pair owns hidden units
-// 128 s .. 128 s + 127; wave w of a side owns 32 of them (rows of W1 / S1, columns of
-// W2 / S2), held in registers as MFMA accumulators for the whole sequence.
+// Why split: one (b, h) memory per workgroup leaves most of the GPU's compute units idle
+// when there are fewer memories than compute units, and its 256 KB of fp32 state fills the
+// register file of one CU.  Here side s of kS = 2 (pairs) or 4 (quads) owns hidden units
+// kHidSide s .. kHidSide (s + 1) - 1 (kHidSide = 256 / kS); wave w of a side owns 32 (pairs)
+// or 16 (quads) of them (rows of W1 / S1, columns of W2 / S2), held in registers as MFMA
+// accumulators for the whole sequence.  Quads serve small B*H (four workgroups per memory
+// fit the compute units); pairs the rest.
 //
 // Per chunk the algebra is that of the single-workgroup kernel (the unrolled momentum /
 // forget-gated write rule of the Titans pages with gradients frozen at the chunk start,
 // each gradient an outer product delta h^T).  What depends on the gates only (the
 // coefficient vectors and Cm) comes from a pass over all chunks before the scan
 // (pair_coef_kernel); the rest that does not depend on the hidden units (scaled Q / K
-// copies, Cm o Q K^T, E2 layouts) is formed by both sides; every sum over hidden units
+// copies, Cm o Q K^T, E2 layouts) is formed by every side; every sum over hidden units
 // is computed per side:
-//   O = Hk W2^T      both sides need the full O for E2 = 2 (O - V): each side posts its
-//                    partial (64 x 64 fp32) to the partner and adds the partner's;
-//   Y                each side writes y for its half of the chunk's tokens (side s: rows
-//                    32 s .. 32 s + 31) and posts its partial of the other half to the
-//                    partner, which adds it one chunk later (off the critical path).
-// O = O_0 + O_1 and y = Y_0 + Y_1 are formed in that order on both sides (fp32 addition
-// is commutative), so both sides hold bitwise the same E2 and the result is
-// reproducible.
+//   O = Hk W2^T      every side needs the full O for E2 = 2 (O - V): each side posts its
+//                    partial (64 x 64 fp32) and adds the other sides';
+//   Y                each side writes y for its 64 / kS rows of the chunk's tokens and
+//                    posts its partials of the other rows to their owners, which add them
+//                    one chunk later (off the critical path).
+// The sides' partials are added in side order ((O_0 + O_1) for pairs, (O_0 + O_1) +
+// (O_2 + O_3) for quads; each side forms it as (own + side^1) + (side^2 + side^3), equal
+// bit for bit since fp32 addition is commutative), so every side holds bitwise the same
+// E2 and the result is reproducible.
 //
-// Exchange protocol.  The two workgroups of a pair are blockIdx i and i ^ 8 (the
-// dispatcher places both on one XCD).  Every word of the exchange area is written and
+// Exchange protocol.  The workgroups of a memory are blockIdx x + 8 s, s < kS (the
+// dispatcher places them on one XCD).  Every word of the exchange area is written and
 // read only with agent-scope relaxed atomics: per-instruction coherent loads and stores
 // that meet beyond the per-XCD L2s, so no L2 writeback or invalidate is ever issued.
 // Thread t of wave w writes its own words, the wave waits for its stores to complete
 // (s_waitcnt vmcnt(0)), then lane 0 stores the wave's flag = exchange number e.  The
-// partner's wave w polls that flag (bounded), then thread t reads exactly the words the
-// partner's thread t wrote.  Exchange e (one per chunk, plus one after the last) carries
-// chunk e's O partial and chunk e-1's y partial.  O and Y areas are double-buffered by
-// the parity of the chunk; a wave posts e + 1 only after its reads of exchange e have
-// returned, which is what lets the partner reuse a buffer two exchanges later.  The
-// launch is cooperative, so both workgroups of a pair are resident together.  A wait that
-// exceeds its bound (never expected) stops all further waits of that wave, and from then on
-// the wave sends NaN in place of its O and y partials and writes NaN y rows: the partner's
-// E2 turns NaN at the next exchange, so both halves of the memory end with NaN y rows and
-// a NaN theta_T / s_T, never with finite values built from a missing partial.
+// other sides' waves w poll those flags (all in one bounded loop), then thread t reads
+// exactly the words the other sides' threads t wrote.  Exchange e (one per chunk, plus
+// one after the last) carries chunk e's O partial and chunk e-1's y partials.  O and Y
+// areas are double-buffered by the parity of the chunk; a wave posts e + 1 only after its
+// reads of exchange e have returned, which is what lets the writer reuse a buffer two
+// exchanges later.  The launch is cooperative, so all workgroups of a memory are resident
+// together.  A wait that exceeds its bound (never expected) stops all further waits of that
+// wave, and from then on the wave sends NaN in place of its O and y partials and writes NaN
+// y rows: the other sides' E2 turns NaN at the next exchange, so every side of the memory
+// ends with NaN y rows and a NaN theta_T / s_T, never with finite values built from a
+// missing partial.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
