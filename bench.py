@@ -43,7 +43,8 @@ PEAKS = {  # MI355X published dense peaks
     "mfma_f32": 157.3,
     "valu_f32": 157.3,
     "hbm": 8000.0,         # GB/s
-    "valu_slots": 39.32,   # T lane-slots/s: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, scalar fp32
+    "valu_slots": 78.64,   # T lane-slots/s: 256 CUs x 4 SIMDs x 32 fp32 lanes x 2.4 GHz
+                           # (157.3 TFLOP/s counts an FMA as two flops)
 }
 
 
@@ -228,18 +229,22 @@ def bench_retrieve(tm, torch, q, theta, wl, steps, warmup):
                 "frac": gbs / PEAKS["hbm"], "alg_bytes_per_launch": nbytes}
     out = {"path": tm.retrieve_path(q, wl.widths), "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
            "roofline": roof, "mfma_tflops": tflops}
-    # The SiLU of every hidden unit is vector-ALU work the matrix cores do not share: one
-    # exp2 and one reciprocal (transcendental, a quarter of the issue rate: 4 slots each), an
-    # add, a multiply and half a packed bf16 conversion -> 10.5 lane slots per hidden unit
-    # and token-head, against 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T slots/s of
-    # scalar fp32 issue (packed fp32 is not used).
+    # The SiLU of every hidden unit is vector-ALU work: one exp2 and one reciprocal, an add,
+    # a multiply and half a packed bf16 conversion.  Priced at the issue costs measured on
+    # MI355X relative to an fp32 add (1 slot; exp2 and reciprocal 3.5 each, the packed
+    # conversion 1.7) that is 9.85 lane slots per hidden unit and token-head, against
+    # 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz = 78.6 T slots/s.  Transcendental VALU work and
+    # MFMA work of the waves on one SIMD were measured to overlap little, so the floor of
+    # this read is the sum of the two: serial_floor_ms.
     hidden = sum(wl.widths[1:-1])
     if hidden:
-        slots = 10.5 * hidden * B * T * H
+        slots = 9.85 * hidden * B * T * H
         rate = slots / (ms * 1e-3) / 1e12
+        floor = (slots / (PEAKS["valu_slots"] * 1e12) + flops / (PEAKS["mfma_bf16"] * 1e12)) * 1e3
         out["alu_roofline"] = {"bound": "alu", "achieved": rate, "peak": PEAKS["valu_slots"],
                                "unit": "T lane-slots/s", "frac": rate / PEAKS["valu_slots"],
-                               "alg_slots_per_launch": slots}
+                               "alg_slots_per_launch": slots, "serial_floor_ms": floor,
+                               "serial_frac": floor / ms}
     return out
 
 

@@ -756,7 +756,7 @@ titans_status titans_mem_retrieve(const titans_scan_desc* desc, const titans_mlp
     a.y = y;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const RPath rp = retrieve_path_of(a);
-    hipError_t e = rp == RPath::Fused  ? titans::launch_retrieve_mfma(a, hs)
+    hipError_t e = rp == RPath::Fused  ? titans::launch_retrieve_mfma(a, device_cus(), hs)
                    : rp == RPath::Wide ? titans::launch_retrieve_wide(a, hs)
                                        : titans::launch_retrieve_generic(a, hs);
     if (e != hipSuccess) return hip_fail(e, "retrieve launch");

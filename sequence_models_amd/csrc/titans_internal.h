@@ -112,9 +112,11 @@ hipError_t launch_retrieve_generic(const ScanArgs& a, hipStream_t stream);
 bool retrieve_wide_supported(const ScanArgs& a);
 hipError_t launch_retrieve_wide(const ScanArgs& a, hipStream_t stream);
 
-// MFMA retrieve for the 64 -> 256 -> 64 memory with bf16 q / y.
+// MFMA retrieve for the 64 -> 256 -> 64 memory with bf16 q / y; cus = compute units of
+// the device (sets the tokens per workgroup).
 bool retrieve_mfma_supported(const ScanArgs& a);
-hipError_t launch_retrieve_mfma(const ScanArgs& a, hipStream_t stream);
+int retrieve_mfma_tiles(const ScanArgs& a, int64_t cus);
+hipError_t launch_retrieve_mfma(const ScanArgs& a, int64_t cus, hipStream_t stream);
 
 // MAG block (memory as gate): the front-end projection and gates, the gated
 // sliding-window attention and the output projection around one memory scan.  Shapes

@@ -573,6 +573,31 @@ def test_retrieve_wide_matches_oracle(widths, T):
     assert err <= 2e-2
 
 
+@pytest.mark.parametrize("B,H,T", [(4, 16, 8192), (4, 16, 16383)])
+def test_retrieve_mfma_block_sizes(B, H, T, monkeypatch):
+    """The fused retrieve picks its tokens per workgroup from the grid (4 and 8 wave tiles
+    per wave on 256 compute units at these shapes; the small cases above take 2, the
+    headline 16): full comparison with the generic kernel, sampled tokens and the last
+    one against the oracle."""
+    wl = synthetic.Workload("retrieve_blocks", batch=B, heads=H, seq_len=T, widths=(64, 256, 64), chunk=64, io="bf16")
+    inp = synthetic.make_inputs(wl, 5)
+    dev = to_device(inp)
+    log(f"case retrieve mfma blocks B={B} H={H} T={T}")
+    rng = np.random.default_rng(T)
+    theta = torch.from_numpy((rng.standard_normal((B, H, wl.params)) / 8).astype(np.float32)).cuda()
+    assert tm.retrieve_path(dev["q"], wl.widths) == "fused_mfma"
+    y = tm.retrieve(dev["q"], theta, wl.widths)
+    monkeypatch.setenv("TITANS_MEM_FORCE_GENERIC", "1")
+    y2 = tm.retrieve(dev["q"], theta, wl.widths)
+    torch.cuda.synchronize()
+    idx = np.r_[np.arange(0, T, 97), T - 1]
+    yr = oracle.retrieve(inp.qkv_f32("q")[:, idx], to_f64(theta), wl.widths)
+    e1 = y_rel_err(to_f64(y[:, idx]), yr)
+    e2 = y_rel_err(to_f64(y), to_f64(y2))
+    log(f"  mfma vs oracle {e1:.2e}, mfma vs generic {e2:.2e}")
+    assert e1 <= 2e-2 and e2 <= 2e-2
+
+
 def test_retrieve_headline_shape_sampled():
     wl = synthetic.WORKLOADS[synthetic.HEADLINE]
     inp = synthetic.make_inputs(wl, 0)
