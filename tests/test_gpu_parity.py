@@ -836,8 +836,9 @@ def test_headline_sampled_single_kernel(sustained, monkeypatch):
 #
 # The Huber and l_p attentional biases replace the output-layer error 2 (O - V) by the
 # derivative of the per-component loss in every scan kernel.  Each path against the
-# oracle with the same bias (l_1 only with fp32 I/O: its gradient jumps at r = 0, where
-# bf16 rounding of the residual flips signs).
+# oracle with the same bias.  l_1's gradient jumps at r = 0, where bf16 rounding of a
+# near-zero residual flips its sign; with bf16 I/O it is therefore checked on inputs whose
+# residuals stay away from zero (test_l1_bias_bf16_separated_residuals).
 
 BIAS_PATHS = {
     # name: (widths, C, io, env, expected path)
@@ -858,7 +859,8 @@ BIAS_PATHS = {
 def test_attentional_bias_matches_oracle(path, bias, monkeypatch):
     widths, C, io, env, expected = BIAS_PATHS[path]
     if bias == ("lp", 1.0) and io == "bf16":
-        pytest.skip("l_1 flips the sign of near-zero residuals under bf16 rounding")
+        pytest.skip("l_1 on bf16: residuals near zero flip sign under bf16 rounding; "
+                    "covered by test_l1_bias_bf16_separated_residuals")
     for k_, v_ in env.items():
         monkeypatch.setenv(k_, v_)
     wl, inp = _small(widths=widths, B=2, T=200, H=2, C=C, io=io, seed=C + 7)
@@ -872,6 +874,42 @@ def test_attentional_bias_matches_oracle(path, bias, monkeypatch):
     check_pairs(wl, y, thT, sT, pairs, refs, prefs)
     # the bias changes the memory (else the test would not see a kernel that ignores it)
     y0, t0, _ = run_gpu(dev, wl)
+    torch.cuda.synchronize()
+    assert state_rel_err(to_f64(t0[:1, 1:2]), refs[0][1][None, None]) > 0.3
+
+
+@pytest.mark.parametrize("path", sorted(p for p, v in BIAS_PATHS.items() if v[2] == "bf16"))
+def test_l1_bias_bf16_separated_residuals(path, monkeypatch):
+    """l_1 (l_p with p = 1) on every bf16 path, on inputs where no residual is near its
+    jump: every value component has |v| >= 2 (both signs) while the memory's outputs at
+    the chunk-start weights stay below 1 in magnitude (checked here with the oracle), so
+    sign(M(k) - v) = -sign(v) is decided with a margin no bf16 rounding can cross."""
+    widths, C, io, env, expected = BIAS_PATHS[path]
+    for k_, v_ in env.items():
+        monkeypatch.setenv(k_, v_)
+    bias = ("lp", 1.0)
+    wl, inp = _small(widths=widths, B=2, T=200, H=2, C=C, io=io, seed=C + 7)
+    v = synthetic.bf16_bits_to_f32(inp.v)
+    v = np.where(v < 0, -1.0, 1.0) * (2.0 + np.abs(v))
+    inp.v = synthetic.f32_to_bf16_bits(v.astype(np.float32))
+    dev = to_device(inp)
+    log(f"case l1 separated on {path}")
+    assert tm.scan_path(dev["q"], wl.chunk, wl.widths) == expected
+    pairs = [(0, 1), (1, 0)]
+    k32 = inp.qkv_f32("k")
+    out = 0.0
+    for tc in range(0, wl.seq_len, C):
+        th = (inp.theta0[[h for _, h in pairs]] if tc == 0 else
+              np.stack([r[1] for r in oracle_seq(inp, pairs, T=tc, bias=bias)]))
+        kk = np.stack([k32[b, tc:tc + C, h] for b, h in pairs], axis=1)[None]
+        out = max(out, float(np.abs(oracle.retrieve(kk, th[None], wl.widths)).max()))
+    log(f"  max |M(k)| at chunk-start weights {out:.3f}, min |v| 2")
+    assert out < 1.0
+    y, thT, sT = run_gpu(dev, wl, bias=bias)
+    torch.cuda.synchronize()
+    refs, prefs = oracle_seq(inp, pairs, bias=bias, perturb=True)
+    check_pairs(wl, y, thT, sT, pairs, refs, prefs)
+    y0, t0, _ = run_gpu(dev, wl)  # the squared loss lands elsewhere
     torch.cuda.synchronize()
     assert state_rel_err(to_f64(t0[:1, 1:2]), refs[0][1][None, None]) > 0.3
 
