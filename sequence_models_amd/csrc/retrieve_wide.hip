@@ -4,16 +4,18 @@
 // (retrieve_mfma.hip) that keeps both weight matrices in LDS; wider memories (the deep
 // 128-512-512-512-128 one holds 2.6 MB of weights) do not fit, so here the weights stream.
 //
-// A workgroup (four waves) serves one (b, h) memory and 128 tokens: every weight window
-// that streams through LDS is used by 128 tokens.  The tokens' activations stay in one LDS
-// buffer as bf16 across all layers (128 x 512, 133 KB); each layer's weights pass through
-// one LDS window of 64 outputs x 128 inputs while the next window's 16-byte loads are in
-// flight in registers (stored after a barrier).  Per window, wave w computes outputs
-// 16w .. 16w+15 of the window's 64 for all 128 tokens (v_mfma_f32_16x16x32_bf16, A = weight
-// rows, B = activation rows, fp32 accumulation).  An output tile's epilogue applies SiLU
-// and keeps the bf16 result in registers until the layer's last window is done (its inputs
-// are still being read); then every wave writes its outputs over the inputs.  The last
-// layer writes y.
+// A workgroup (eight waves, two per SIMD) serves one (b, h) memory and 128 tokens: every
+// weight window that streams through LDS is used by 128 tokens.  The tokens' activations
+// stay in one LDS buffer as bf16 across all layers (128 x 512, 133 KB); each layer's
+// weights pass through one LDS window of 256 outputs x 32 inputs while the next window's
+// 16-byte loads are in flight in registers (stored after a barrier).  Per window, wave
+// (o, q) computes outputs 128 o .. 128 o + 127 of the window's 256 for tokens
+// 32 q .. 32 q + 31 (v_mfma_f32_16x16x32_bf16, A = weight rows, B = activation rows, fp32
+// accumulation): of the splits of a window over eight waves, the one that reads the least
+// from LDS (80 KB per window; LDS reads, not the matrix cores, set the pace here).  An
+// output tile's epilogue applies SiLU and keeps the bf16 result in registers until the
+// layer's last window is done (its inputs are still being read); then every wave writes
+// its outputs over the inputs.  The last layer writes y.
 // Workgroups are numbered so that each XCD holds whole memories: all token tiles of a
 // memory then read its weights through one L2.
 #include <hip/hip_runtime.h>
@@ -26,12 +28,14 @@ namespace {
 
 using namespace fused;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kTok = 128;         // tokens per workgroup
-constexpr int kCt = kTok / 16;    // 16-token tiles
-constexpr int kMaxTiles = 8;      // 64-output tiles of a 512-wide layer
-constexpr int kOut = 64;          // outputs per tile
-constexpr int kWin = 128;         // inputs per weight window
+constexpr int kQuarters = 4;      // token quarters: waves 2q, 2q+1 take quarter q
+constexpr int kCt = kTok / 16 / kQuarters;  // 16-token tiles per wave
+constexpr int kTw = 8;            // 16-output tiles per wave (of a window's sixteen)
+constexpr int kMaxTiles = 2;      // 256-output tiles of a 512-wide layer
+constexpr int kOut = 256;         // outputs per tile
+constexpr int kWin = 32;          // inputs per weight window (one MFMA step)
 constexpr int kMaxW = 512;
 constexpr int kActLd = kMaxW + 8; // padded activation row (bf16)
 constexpr int kWLd = kWin + 8;    // padded weight row (bf16)
@@ -42,9 +46,9 @@ struct __attribute__((aligned(16))) WSmem {
     __bf16 w[kOut * kWLd];         // [output][input - k0]
 };
 
-// One weight window: rows o0 .. o0+63 (< nout) and columns k0 .. k0+255 (< nin) of W
-// (row-major nout x nin, fp32).  Thread t loads columns 4 (t % 32) .. +3 of rows
-// t / 32 + 8 m, m < 8: eight 16-byte loads (32 contiguous floats per row and half-wave).
+// One weight window: rows o0 .. o0+255 (< nout) and columns k0 .. k0+31 (< nin) of W
+// (row-major nout x nin, fp32; zero outside).  Thread t loads columns 4 (t % 8) .. +3 of
+// rows t / 8 + 64 m, m < 4: four 16-byte loads (a row's 32 floats from 8 threads).
 struct Window {
     f32x4 v[kGroups];
 };
@@ -70,10 +74,11 @@ __device__ __forceinline__ void store_window(const Window& x, __bf16* dst) {
             bf4(x.v[m]);
 }
 
-__global__ void __launch_bounds__(kThreads) retrieve_wide_kernel(ScanArgs A) {
+__global__ void __launch_bounds__(kThreads, 2) retrieve_wide_kernel(ScanArgs A) {
     __shared__ WSmem sm;
     const int tid = threadIdx.x;
-    const int wv = tid >> 6, g = (tid & 63) >> 4, j = tid & 15;
+    const int wo2 = (tid >> 6) & 1, quarter = tid >> 7, g = (tid & 63) >> 4, j = tid & 15;
+    const int tb = 32 * quarter;  // the wave's first token in the block
 
     // XCD-contiguous numbering of (memory, token tile)
     const int64_t ntiles = (A.T + kTok - 1) / kTok;
@@ -105,7 +110,7 @@ __global__ void __launch_bounds__(kThreads) retrieve_wide_kernel(ScanArgs A) {
         }
     };
 
-    // first window in flight while q lands in LDS.  Both activation buffers start at zero:
+    // first window in flight while q lands in LDS.  The activation buffer starts at zero:
     // a 32-wide MFMA step over a width that is a multiple of 16 only reads up to 16
     // columns past it, against zero weights, and those columns must be finite.
     Window nx;
@@ -123,11 +128,14 @@ __global__ void __launch_bounds__(kThreads) retrieve_wide_kernel(ScanArgs A) {
     store_window(nx, sm.w);
     __syncthreads();
 
-    f32x4 acc[kCt];
+    f32x4 acc[kTw][kCt];
 #pragma unroll
-    for (int ct = 0; ct < kCt; ++ct) acc[ct] = zero4();
-    // SiLU outputs of the current hidden layer: tile ot, token tile ct, outputs f0 .. f0+3
-    bf16x4 stash[kMaxTiles][kCt];
+    for (int tw = 0; tw < kTw; ++tw)
+#pragma unroll
+        for (int ct = 0; ct < kCt; ++ct) acc[tw][ct] = zero4();
+    // SiLU outputs of the current hidden layer: window ot, the wave's output tile tw, token
+    // tile ct (outputs f0 .. f0+3 of the lane's token)
+    bf16x4 stash[kMaxTiles][kTw][kCt];
     while (wl <= A.L) {
         const int nin = A.n[wl - 1], nout = A.n[wl];
         // the following window's loads go out before this one's MFMAs
@@ -136,60 +144,66 @@ __global__ void __launch_bounds__(kThreads) retrieve_wide_kernel(ScanArgs A) {
         const bool more = L2 <= A.L;
         if (more) load_window(nx, th + A.off[L2], A.n[L2], A.n[L2 - 1], o2, k2);
 
-        const int kw = (nin - wk) < kWin ? (nin - wk) : kWin;  // a multiple of 16
-        const __bf16* ar = sm.w + (16 * wv + j) * kWLd + 4 * g;
-        for (int ks = 0; ks < kw; ks += 32) {
-            const bf16x8 a = frag(ar, ks);
+        // every operand of the window's products is read before the first of them (one
+        // LDS wait); past a width that is a multiple of 16 the step reads zero weights
+        const __bf16* ar = sm.w + (128 * wo2 + j) * kWLd + 4 * g;
+        bf16x8 a[kTw], b[kCt];
 #pragma unroll
-            for (int ct = 0; ct < kCt; ++ct) {
-                const __bf16* br = sm.act + (16 * ct + j) * kActLd + wk + ks + 4 * g;
-                acc[ct] = mfma(a, frag(br, 0), acc[ct]);
-            }
-        }
+        for (int tw = 0; tw < kTw; ++tw) a[tw] = frag(ar + 16 * tw * kWLd, 0);
+#pragma unroll
+        for (int ct = 0; ct < kCt; ++ct) b[ct] = frag(sm.act + (tb + 16 * ct + j) * kActLd + wk + 4 * g, 0);
+#pragma unroll
+        for (int tw = 0; tw < kTw; ++tw)
+#pragma unroll
+            for (int ct = 0; ct < kCt; ++ct) acc[tw][ct] = mfma(a[tw], b[ct], acc[tw][ct]);
         if (wk + kWin >= nin) {  // last window of this output tile: epilogue
-            const int f0 = wo + 16 * wv + 4 * g;  // outputs f0 .. f0+3 of token 16 ct + j
-            if (wl < A.L) {
-                bf16x4 h[kCt];
 #pragma unroll
-                for (int ct = 0; ct < kCt; ++ct) {
-                    f32x4 x;
+            for (int tw = 0; tw < kTw; ++tw) {
+                const int f0 = wo + 128 * wo2 + 16 * tw + 4 * g;  // outputs f0 .. f0+3 of token tb + 16 ct + j
+                if (wl < A.L) {
+                    bf16x4 h[kCt];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) x[r] = acc[ct][r] * sigmoid(acc[ct][r]);
-                    h[ct] = bf4(x);
-                }
-                // constant indices only (a switch, not a dynamic register index)
-                switch (wo / kOut) {
+                    for (int ct = 0; ct < kCt; ++ct) {
+                        f32x4 x;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) x[r] = acc[tw][ct][r] * sigmoid(acc[tw][ct][r]);
+                        h[ct] = bf4(x);
+                    }
+                    // constant indices only (a switch, not a dynamic register index)
+                    switch (wo / kOut) {
 #define TITANS_STASH(i) \
     case i:             \
-        _Pragma("unroll") for (int ct = 0; ct < kCt; ++ct) stash[i][ct] = h[ct]; break;
-                    TITANS_STASH(0) TITANS_STASH(1) TITANS_STASH(2) TITANS_STASH(3)
-                    TITANS_STASH(4) TITANS_STASH(5) TITANS_STASH(6) TITANS_STASH(7)
+        _Pragma("unroll") for (int ct = 0; ct < kCt; ++ct) stash[i][tw][ct] = h[ct]; break;
+                        TITANS_STASH(0) TITANS_STASH(1)
 #undef TITANS_STASH
-                    default: break;
-                }
-            } else {
+                        default: break;
+                    }
+                } else {
 #pragma unroll
-                for (int ct = 0; ct < kCt; ++ct) {
-                    const int64_t t = t0 + 16 * ct + j;
-                    if (f0 < nout && t < A.T)
-                        *reinterpret_cast<bf16x4*>(yg + ybase + t * A.ys[1] + f0) = bf4(acc[ct]);
+                    for (int ct = 0; ct < kCt; ++ct) {
+                        const int64_t t = t0 + tb + 16 * ct + j;
+                        if (f0 < nout && t < A.T)
+                            *reinterpret_cast<bf16x4*>(yg + ybase + t * A.ys[1] + f0) = bf4(acc[tw][ct]);
+                    }
                 }
+#pragma unroll
+                for (int ct = 0; ct < kCt; ++ct) acc[tw][ct] = zero4();
             }
-#pragma unroll
-            for (int ct = 0; ct < kCt; ++ct) acc[ct] = zero4();
         }
         __syncthreads();  // this window and, at a layer's end, the layer's inputs are read
         if (more) store_window(nx, sm.w);
         if (more && L2 != wl) {
             // hidden layer wl is done: its outputs replace its inputs
 #pragma unroll
-            for (int ot = 0; ot < kMaxTiles; ++ot) {
-                const int f0 = kOut * ot + 16 * wv + 4 * g;
-                if (kOut * ot < nout && f0 < nout)
+            for (int ot = 0; ot < kMaxTiles; ++ot)
 #pragma unroll
-                    for (int ct = 0; ct < kCt; ++ct)
-                        *reinterpret_cast<bf16x4*>(sm.act + (16 * ct + j) * kActLd + f0) = stash[ot][ct];
-            }
+                for (int tw = 0; tw < kTw; ++tw) {
+                    const int f0 = kOut * ot + 128 * wo2 + 16 * tw + 4 * g;
+                    if (kOut * ot < nout && f0 < nout)
+#pragma unroll
+                        for (int ct = 0; ct < kCt; ++ct)
+                            *reinterpret_cast<bf16x4*>(sm.act + (tb + 16 * ct + j) * kActLd + f0) = stash[ot][tw][ct];
+                }
         }
         __syncthreads();  // the next window (and a finished layer's outputs) are in LDS
         wl = L2;
