@@ -337,13 +337,59 @@ __device__ __forceinline__ void tile_mfma(int i0, int j0, int M, int N, int K, O
     __syncthreads();  // the LDS tiles may be restaged by the next product
 }
 
+// The same product for an epilogue that also reads one value per element from global
+// memory: pre(i, j) for each of the thread's sixteen elements is loaded before the
+// operands are staged, so those loads overlap the staging instead of following the
+// products one element at a time; epi(i, j, out, pre(i, j)).
+template <int kSl = 8, class Pre, class Epi>
+__device__ __forceinline__ void tile_mfma_pre(int i0, int j0, int M, int N, int K, Opnd A, Opnd B,
+                                              __bf16* lds, Pre pre, Epi epi) {
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6, g = (tid & 63) >> 4, j = tid & 15;
+    float pv[4][4];
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 16 * wv + 4 * g + r, jc = j0 + 16 * tn + j;
+            pv[tn][r] = (i < M && jc < N) ? pre(i, jc) : 0.f;
+        }
+    const int Kp = (K + 31) & ~31, ld = Kp + 8;
+    __bf16* const dst[2] = {lds, lds + kTile * ld};
+    const Opnd X[2] = {A, B};
+    const int r0[2] = {i0, j0}, R[2] = {M, N};
+    stage<2, kSl>(dst, X, r0, R, 0, Kp, K, ld);
+    __syncthreads();
+    f32x4_t acc[4];
+    zero_acc(acc);
+    mfma_tile(dst[0], dst[1], Kp, ld, acc);
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 16 * wv + 4 * g + r, jc = j0 + 16 * tn + j;
+            if (i < M && jc < N) epi(i, jc, acc[tn][r], pv[tn][r]);
+        }
+    __syncthreads();  // the LDS tiles may be restaged by the next product
+}
+
 constexpr int kWin3 = 128;  // k window of a three-operand staging round (52 KB of LDS)
 
 // out1 = A B1^T and out2 = A B2^T: A, B1, B2 staged together in k windows of 128 (A is
-// loaded once); epi(i, j, out1, out2).
-template <class Epi>
+// loaded once); epi(i, j, out1, out2, pre(i)), with pre(i) (two floats of row i) loaded
+// before the staging.
+template <class Pre, class Epi>
 __device__ __forceinline__ void tile_mfma_shared_a(int i0, int j0, int M, int N, int K, Opnd A,
-                                                   Opnd B1, Opnd B2, __bf16* lds, Epi epi) {
+                                                   Opnd B1, Opnd B2, __bf16* lds, Pre pre, Epi epi) {
+    float2 pr[4];
+    {
+        const int wv0 = threadIdx.x >> 6, g0 = (threadIdx.x & 63) >> 4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 16 * wv0 + 4 * g0 + r;
+            pr[r] = i < M ? pre(i) : float2{0.f, 0.f};
+        }
+    }
     const int Kw = K < kWin3 ? K : kWin3;
     const int Kwp = (Kw + 31) & ~31, ld = Kwp + 8;
     __bf16* const dst[3] = {lds, lds + kTile * ld, lds + 2 * kTile * ld};
@@ -368,7 +414,7 @@ __device__ __forceinline__ void tile_mfma_shared_a(int i0, int j0, int M, int N,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = i0 + 16 * wv + 4 * g + r, jc = j0 + 16 * tn + j;
-            if (i < M && jc < N) epi(i, jc, acc1[tn][r], acc2[tn][r]);
+            if (i < M && jc < N) epi(i, jc, acc1[tn][r], acc2[tn][r], pr[r]);
         }
 }
 
@@ -494,6 +540,17 @@ __device__ __forceinline__ void tile(int i0, int j0, int M, int N, int K, Opnd A
         tile_mfma<kSl>(i0, j0, M, N, K, A, B, static_cast<__bf16*>(lds), epi);
     else
         tile_f32(i0, j0, M, N, K, A, B, static_cast<float*>(lds), epi);
+}
+
+// tile() for an epilogue epi(i, j, out, pre(i, j)) that reads one global value per element.
+template <bool kMfma, int kSl = 8, class Pre, class Epi>
+__device__ __forceinline__ void tile_pre(int i0, int j0, int M, int N, int K, Opnd A, Opnd B,
+                                         void* lds, Pre pre, Epi epi) {
+    if constexpr (kMfma)
+        tile_mfma_pre<kSl>(i0, j0, M, N, K, A, B, static_cast<__bf16*>(lds), pre, epi);
+    else
+        tile_f32(i0, j0, M, N, K, A, B, static_cast<float*>(lds),
+                 [&](int i, int jj, float x) { epi(i, jj, x, pre(i, jj)); });
 }
 
 // Float offsets of the per-memory workspace regions.
@@ -702,10 +759,12 @@ __global__ void __launch_bounds__(kThreads, kTasks == kSetLast ? 2 : 1) phase_ke
                     Sp[i * nout + jj] = sg_ * (1.0f + z * (1.0f - sg_));
                 });
             } else {
-                tile<kMfma>(i0, j0, n, nout, nin, A, Bo, lds, [&](int i, int jj, float z) {
-                    const float vv = load_io(a.v, qbase + (c0 + i) * a.qs[1] + jj, a.io);
-                    Dl[i * nout + jj] = bias_grad(z - vv, a.bias, a.bias_param);
-                });
+                tile_pre<kMfma>(
+                    i0, j0, n, nout, nin, A, Bo, lds,
+                    [&](int i, int jj) { return load_io(a.v, qbase + (c0 + i) * a.qs[1] + jj, a.io); },
+                    [&](int i, int jj, float z, float vv) {
+                        Dl[i * nout + jj] = bias_grad(z - vv, a.bias, a.bias_param);
+                    });
             }
             break;
         }
@@ -713,15 +772,16 @@ __global__ void __launch_bounds__(kThreads, kTasks == kSetLast ? 2 : 1) phase_ke
             if constexpr (!(kTasks & bit(kBwd))) break;
             float* Dp = ws + wl.dl[l - 1];
             const float* Sp = ws + wl.sp[l - 1];
-            tile<kMfma>(i0, j0, n, nin, nout, Opnd{Dl, nout, 1, nullptr}, Opnd{W, 1, nin, nullptr},
-                        lds, [&](int i, int jj, float x) { Dp[i * nin + jj] = x * Sp[i * nin + jj]; });
+            tile_pre<kMfma>(i0, j0, n, nin, nout, Opnd{Dl, nout, 1, nullptr}, Opnd{W, 1, nin, nullptr},
+                            lds, [&](int i, int jj) { return Sp[i * nin + jj]; },
+                            [&](int i, int jj, float x, float sp) { Dp[i * nin + jj] = x * sp; });
             break;
         }
         case kMq: {  // Mq = Cm o (Hq_{l-1} Hk_{l-1}^T), strictly lower triangular
             if constexpr (!(kTasks & bit(kMq))) break;
-            tile<kMfma>(i0, j0, n, n, nin, hq_rows, hk_rows, lds, [&](int i, int jj, float x) {
-                            Mq[i * C + jj] = (jj < i) ? Cm[(int64_t)i * C + jj] * x : 0.0f;
-                        });
+            tile_pre<kMfma>(i0, j0, n, n, nin, hq_rows, hk_rows, lds,
+                            [&](int i, int jj) { return (jj < i) ? Cm[(int64_t)i * C + jj] : 0.0f; },
+                            [&](int i, int jj, float x, float cm) { Mq[i * C + jj] = (jj < i) ? cm * x : 0.0f; });
             break;
         }
         case kU: {  // U_l = diag(a) Hq W_l^T - diag(b) Hq S_l^T
@@ -729,8 +789,10 @@ __global__ void __launch_bounds__(kThreads, kTasks == kSetLast ? 2 : 1) phase_ke
             if constexpr (kMfma) {  // both products from one staging of Hq, W, S
                 tile_mfma_shared_a(i0, j0, n, nout, nin, hq_rows,
                                    Opnd{W, nin, 1, nullptr}, Opnd{S, nin, 1, nullptr},
-                                   static_cast<__bf16*>(lds), [&](int i, int jj, float xw, float xs) {
-                                       U[i * nout + jj] = coef_a[i] * xw - coef_b[i] * xs;
+                                   static_cast<__bf16*>(lds),
+                                   [&](int i) { return float2{coef_a[i], coef_b[i]}; },
+                                   [&](int i, int jj, float xw, float xs, float2 ab) {
+                                       U[i * nout + jj] = ab.x * xw - ab.y * xs;
                                    });
             } else {
                 const Opnd A = hq_rows;
@@ -745,14 +807,18 @@ __global__ void __launch_bounds__(kThreads, kTasks == kSetLast ? 2 : 1) phase_ke
             if constexpr (!(kTasks & bit(kQb))) break;
             const Opnd A{Mq, C, 1, nullptr}, Bo{Dl, 1, nout, nullptr};
             if (l < L) {
-                tile<kMfma, 4>(i0, j0, n, nout, n, A, Bo, lds, [&](int i, int jj, float x) {
-                    const float u = U[i * nout + jj] - x;
-                    U[i * nout + jj] = u * sigm<kMfma>(u);
-                });
+                tile_pre<kMfma, 4>(i0, j0, n, nout, n, A, Bo, lds,
+                                   [&](int i, int jj) { return U[i * nout + jj]; },
+                                   [&](int i, int jj, float x, float u0) {
+                                       const float u = u0 - x;
+                                       U[i * nout + jj] = u * sigm<kMfma>(u);
+                                   });
             } else {
-                tile<kMfma, 4>(i0, j0, n, nout, n, A, Bo, lds, [&](int i, int jj, float x) {
-                    store_io(a.y, ybase + (c0 + i) * a.ys[1] + jj, a.io, U[i * nout + jj] - x);
-                });
+                tile_pre<kMfma, 4>(i0, j0, n, nout, n, A, Bo, lds,
+                                   [&](int i, int jj) { return U[i * nout + jj]; },
+                                   [&](int i, int jj, float x, float u0) {
+                                       store_io(a.y, ybase + (c0 + i) * a.ys[1] + jj, a.io, u0 - x);
+                                   });
             }
             break;
         }
