@@ -202,7 +202,10 @@ def bench_retrieve(tm, torch, q, theta, wl, steps, warmup):
     (the sustained scan's final weights, else theta0): its own line, not part of the scan
     step.  Algorithmic bytes: q and y once, theta once per memory; flops 2 P per token-head."""
     y = torch.empty_like(q)
-    for _ in range(warmup):
+    # the read is short (a fraction of a millisecond at the headline): at least 100 calls,
+    # so that clock ramps after the scan's runs average out
+    steps = max(steps, 100)
+    for _ in range(max(warmup, 5)):
         tm.retrieve(q, theta, wl.widths, y=y)
     stream = torch.cuda.current_stream()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -227,7 +230,7 @@ def bench_retrieve(tm, torch, q, theta, wl, steps, warmup):
     else:
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAKS["hbm"], "unit": "GB/s",
                 "frac": gbs / PEAKS["hbm"], "alg_bytes_per_launch": nbytes}
-    out = {"path": tm.retrieve_path(q, wl.widths), "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+    out = {"path": tm.retrieve_path(q, wl.widths), "ms": ms, "calls": steps, "tokens_per_s": B * T / (ms * 1e-3),
            "roofline": roof, "mfma_tflops": tflops}
     # The SiLU of every hidden unit is vector-ALU work: one exp2 and one reciprocal, an add,
     # a multiply and half a packed bf16 conversion.  Priced at the issue costs measured on
