@@ -598,6 +598,55 @@ def test_retrieve_mfma_block_sizes(B, H, T, monkeypatch):
     assert e1 <= 2e-2 and e2 <= 2e-2
 
 
+def test_retrieve_deep_shape_sampled():
+    """The wide retrieve at the deep workload's full shape (B=2, T=32768, H=8,
+    128-512-512-512-128), in the configuration the bench times, against the oracle on every
+    257th token and the last one."""
+    wl = synthetic.WORKLOADS["deep_h8_d128_b2_t32k"]
+    inp = synthetic.make_inputs(wl, 0)
+    dev = to_device(inp)
+    log("case retrieve deep shape")
+    B, H, W = wl.batch, wl.heads, wl.widths
+    rng = np.random.default_rng(11)
+    theta = np.concatenate([rng.standard_normal((B, H, W[l + 1] * W[l])) / np.sqrt(W[l])
+                            for l in range(len(W) - 1)], axis=2).astype(np.float32)
+    assert tm.retrieve_path(dev["q"], W) == "wide_mfma"
+    y = tm.retrieve(dev["q"], torch.from_numpy(theta).cuda(), W)
+    torch.cuda.synchronize()
+    idx = np.r_[np.arange(0, wl.seq_len, 257), wl.seq_len - 1]
+    yr = oracle.retrieve(inp.qkv_f32("q")[:, idx], theta, W)
+    err = y_rel_err(to_f64(y[:, idx]), yr)
+    log(f"  deep retrieve vs oracle {err:.2e}")
+    assert err <= 2e-2
+
+
+def test_retrieve_long_context_sampled():
+    """The 64-256-64 retrieve over 2^21 tokens x 16 heads (q and y are 4 GiB each, so the
+    sampled rows near the end sit past 2^31 bytes) against the oracle on every 4099th token
+    and the last one."""
+    B, T, H, d = 1, 1 << 21, 16, 64
+    widths = (64, 256, 64)
+    log("case retrieve long context")
+    g = torch.Generator(device="cuda").manual_seed(21)
+    q = torch.empty(B, T, H, d, dtype=torch.bfloat16, device="cuda")
+    for t0 in range(0, T, 1 << 18):  # in slabs: the fp32 draw of the whole q would be 8 GiB
+        x = torch.randn(B, 1 << 18, H, d, device="cuda", generator=g)
+        q[:, t0:t0 + (1 << 18)] = (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    P = 2 * d * widths[1]
+    theta = (torch.randn(B, H, P, device="cuda", generator=g) / 8).contiguous()
+    assert tm.retrieve_path(q, widths) == "fused_mfma"
+    y = tm.retrieve(q, theta, widths)
+    torch.cuda.synchronize()
+    idx = np.r_[np.arange(0, T, 4099), T - 1]
+    qs = q[:, idx].float().cpu().numpy()
+    yr = oracle.retrieve(qs, theta.cpu().numpy().astype(np.float64), widths)
+    err = y_rel_err(to_f64(y[:, idx]), yr)
+    log(f"  long-context retrieve vs oracle {err:.2e} ({len(idx)} tokens, last byte offset "
+        f"{(T - 1) * H * d * 2})")
+    assert err <= 2e-2
+    del q, y
+
+
 def test_retrieve_headline_shape_sampled():
     wl = synthetic.WORKLOADS[synthetic.HEADLINE]
     inp = synthetic.make_inputs(wl, 0)
